@@ -1,0 +1,20 @@
+"""CPU oracle of the SwitchFFN forward pass -- test infrastructure only.
+
+Only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg may import
+this package.  The HIP product path never does.
+"""
+from .switchffn_oracle import (  # noqa: F401
+    aux_loss,
+    bf16_bits,
+    capacity,
+    dispatch,
+    expert_ffn,
+    forward,
+    near_tie_tokens,
+    round_to_bf16,
+    round_to_dtype,
+    router,
+    router_logits,
+    softmax,
+    top1,
+)

@@ -1,0 +1,235 @@
+"""CPU oracle for the SwitchFFN forward pass (float64, numpy).
+
+TEST INFRASTRUCTURE ONLY.  Only tests/, __graft_entry__.smoke() and the
+cpu_baseline leg of bench.py may import this module.  It shares no code with
+the HIP path; the two meet only in the seeded inputs of switchffn_synth.
+
+Every step below is the plain definition the pages give, written out in the
+pages' order, with a library matmul as the only primitive.  Sources:
+  [Switch summary] "Switch Transformers: Scaling to Trillion Parameter Models
+      with Simple and Efficient Sparsity" (paper-graph-ui summary), section 3.4
+      "Detailed, Sentence-Based Technical Breakdown" and section 3.2
+      "Big-Picture Architecture (Diagram in Words)".
+  [Paper note] "Switch Transformer" (eightmm.github.io note), sections
+      "Router", "Expert FFN Layer", "Capacity Factor", "Load-Balancing Loss",
+      "Implementation Notes".
+  [Explainer] "Switch Transformer, explained." (vibeengines.com), the nine-step
+      recipe (steps 2-5).
+  [Math-LLMs card] "Chapter 8 - Attention and Transformers" companion reader,
+      card 08 "Penalize uneven expert traffic".
+
+Readings where the pages are silent or disagree (each also listed in the
+design notes): capacity C = floor(CF*T/N) in IEEE double; the first C tokens of
+an expert in flattened token order are accepted; argmax ties go to the lowest
+expert index and the decision is taken on fp32 logits (the router precision);
+f_i counts the argmax before capacity; P_i averages over all T tokens; the
+aux loss is returned without the alpha factor; y = x + g*E(x) for accepted
+tokens and y = x for dropped ones; b2 sits inside the gate scaling.
+
+Pins (tests/test_oracle_pins.py): the worked aux-loss example of the
+Math-LLMs card (1.15), the uniform-routing closed forms (aux = 1), the
+one-expert limit (aux -> N, closed form), N = 1 dense-FFN reduction, the x = 0
+and Wr = 0 closed forms, a hand-computed FFN example, capacity edge cases and
+a brute-force per-token loop on tiny inputs.  End-to-end y at the measured
+workload shapes, beyond those special cases, is parity unpinned: the pages
+print no values of a full forward pass.
+"""
+from __future__ import annotations
+
+import math
+from typing import Callable, Iterable, Optional
+
+import numpy as np
+
+
+# ----------------------------------------------------------------------------
+# Capacity ([Switch summary] 3.4 "Distributed Implementation and Expert
+# Capacity", expert capacity formula; [Paper note] "Capacity Factor";
+# [Explainer] step 3).  The three pages round differently; the reading used
+# here is floor((CF * T) / N) evaluated in IEEE double in that order.
+# ----------------------------------------------------------------------------
+def capacity(T: int, N: int, CF: float) -> int:
+    if T < 0 or N <= 0 or not math.isfinite(CF) or CF < 0:
+        raise ValueError("capacity needs T >= 0, N > 0 and a finite CF >= 0")
+    return int(math.floor((float(CF) * float(T)) / float(N)))
+
+
+# ----------------------------------------------------------------------------
+# Router ([Switch summary] 3.4 "Switch Routing: The k=1 Simplification":
+# h(x) = W_r . x, p_i(x) = softmax, selected expert = argmax_i p_i(x), gate
+# p_{i*}(x); [Paper note] "Router"; [Explainer] step 2 and [Switch summary]
+# 3.4 "Selective Precision Training": the router works in float32).
+# ----------------------------------------------------------------------------
+def router_logits(x: np.ndarray, Wr: np.ndarray) -> np.ndarray:
+    """z[t, i] = sum_k x[t, k] * Wr[i, k]  (Wr stored [N, d]), in float64."""
+    return np.asarray(x, np.float64) @ np.asarray(Wr, np.float64).T
+
+
+def softmax(z: np.ndarray) -> np.ndarray:
+    """p[t, i] = exp(z[t, i] - m_t) / sum_j exp(z[t, j] - m_t), m_t = max_i z[t, i]."""
+    m = z.max(axis=1, keepdims=True)
+    e = np.exp(z - m)
+    return e / e.sum(axis=1, keepdims=True)
+
+
+def top1(z: np.ndarray) -> np.ndarray:
+    """Lowest expert index among the largest fp32 logits of each token."""
+    z32 = z.astype(np.float32)
+    return np.argmax(z32, axis=1).astype(np.int64)  # argmax returns the first maximum
+
+
+def router(x: np.ndarray, Wr: np.ndarray) -> dict:
+    z = router_logits(x, Wr)
+    probs = softmax(z)
+    expert_idx = top1(z)
+    gate = probs[np.arange(z.shape[0]), expert_idx]
+    return {"logits": z, "probs": probs, "expert_idx": expert_idx, "gate": gate}
+
+
+# ----------------------------------------------------------------------------
+# Dispatch with the capacity mask ([Switch summary] 3.4 "Distributed
+# Implementation and Expert Capacity": a running count per expert column gives
+# each token its position; positions past the capacity are masked out and the
+# token overflows).  Token order is the flattened order t = b*L + l
+# ([Paper note] "Implementation Notes -- Batch and Sequence Shape").
+# ----------------------------------------------------------------------------
+def dispatch(expert_idx: np.ndarray, N: int, C: int) -> dict:
+    T = len(expert_idx)
+    count = np.zeros(N, dtype=np.int64)
+    rank = np.empty(T, dtype=np.int64)
+    for t in range(T):
+        e = int(expert_idx[t])
+        rank[t] = count[e]          # tokens of expert e seen before t
+        count[e] += 1
+    slot = np.where(rank < C, rank, -1)
+    accepted = np.minimum(count, C)
+    offset = np.zeros(N + 1, dtype=np.int64)
+    offset[1:] = np.cumsum(accepted)
+    row2tok = np.empty(int(offset[-1]), dtype=np.int64)
+    for t in range(T):
+        if slot[t] >= 0:
+            row2tok[offset[int(expert_idx[t])] + slot[t]] = t
+    return {"hist": count, "rank": rank, "slot": slot, "accepted": accepted,
+            "offset": offset, "row2tok": row2tok}
+
+
+# ----------------------------------------------------------------------------
+# Load-balancing auxiliary loss ([Switch summary] 3.4 "The Load-Balancing
+# Auxiliary Loss": f_i = (1/T) sum_x 1{argmax p(x) = i}, P_i = (1/T) sum_x
+# p_i(x), loss = alpha * N * sum_i f_i P_i; [Math-LLMs card] card 08).  Returned
+# without alpha.
+# ----------------------------------------------------------------------------
+def aux_loss(expert_idx: np.ndarray, probs: np.ndarray) -> float:
+    T, N = probs.shape
+    f = np.bincount(expert_idx, minlength=N).astype(np.float64) / T
+    P = probs.sum(axis=0) / T
+    return float(N * np.dot(f, P))
+
+
+# ----------------------------------------------------------------------------
+# Expert FFN ([Paper note] "Expert FFN Layer": E_i(x) = W_{2,i} sigma(W_{1,i} x
+# + b_{1,i}) + b_{2,i}; sigma = ReLU, [Switch summary] 3.2 "Expert FFNs").
+# W1 is stored [F, d] and W2 [d, F] per expert.
+# ----------------------------------------------------------------------------
+def expert_ffn(xe: np.ndarray, W1e: np.ndarray, b1e, W2e: np.ndarray, b2e) -> np.ndarray:
+    a = xe @ np.asarray(W1e, np.float64).T
+    if b1e is not None:
+        a = a + np.asarray(b1e, np.float64)
+    h = np.maximum(a, 0.0)
+    o = h @ np.asarray(W2e, np.float64).T
+    if b2e is not None:
+        o = o + np.asarray(b2e, np.float64)
+    return o
+
+
+# ----------------------------------------------------------------------------
+# Rounding of the layer output to the storage type (once, from float64).
+# ----------------------------------------------------------------------------
+def round_to_bf16(v: np.ndarray) -> np.ndarray:
+    """Nearest bfloat16 value (ties to even) of each float64, returned as float64."""
+    v = np.asarray(v, np.float64)
+    m, e = np.frexp(v)                 # v = m * 2^e, 0.5 <= |m| < 1
+    q = np.rint(m * 256.0)             # 8 significant bits, round half to even
+    return np.ldexp(q, e - 8)
+
+
+def bf16_bits(v: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns of values that are already bf16-representable."""
+    return (np.asarray(v, np.float64).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def round_to_dtype(v: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == "fp32":
+        return np.asarray(v, np.float64).astype(np.float32).astype(np.float64)
+    if dtype == "bf16":
+        return round_to_bf16(v)
+    raise ValueError(dtype)
+
+
+# ----------------------------------------------------------------------------
+# The whole layer ([Switch summary] 3.2 "Information flow through a Switch
+# layer": route, dispatch, expert, scale by the gate, add on the residual;
+# overflow tokens bypass the expert and pass through unchanged; [Explainer]
+# step 4).
+# ----------------------------------------------------------------------------
+ExpertSource = Callable[[int], tuple]
+
+
+def forward(x, Wr, experts, CF: float, dtype: str = "fp32", *, no_residual: bool = False,
+            expert_idx: Optional[np.ndarray] = None,
+            only_experts: Optional[Iterable[int]] = None) -> dict:
+    """Run the layer on float64 inputs.
+
+    experts: (W1 [N,F,d], b1 [N,F] | None, W2 [N,d,F], b2 [N,d] | None), or a
+        callable e -> (W1e, b1e, W2e, b2e) for weights drawn one expert at a time.
+    expert_idx: replay a given routing instead of the oracle's own top-1 (the
+        probabilities, gate and aux loss still come from the oracle's logits).
+    only_experts: compute expert outputs for these experts only; the y rows of
+        other experts' accepted tokens are NaN.
+    no_residual: y = g * E(x) for accepted tokens and 0 for dropped ones.
+    """
+    x = np.asarray(x, np.float64)
+    T = x.shape[0]
+    N = np.asarray(Wr).shape[0]
+    C = capacity(T, N, CF)
+    r = router(x, Wr)
+    eidx = r["expert_idx"] if expert_idx is None else np.asarray(expert_idx, np.int64)
+    gate = r["probs"][np.arange(T), eidx]
+    dp = dispatch(eidx, N, C)
+    aux = aux_loss(eidx, r["probs"])
+
+    if callable(experts):
+        get = experts
+    else:
+        W1, b1, W2, b2 = experts
+        def get(e):
+            return (W1[e], None if b1 is None else b1[e], W2[e], None if b2 is None else b2[e])
+
+    y = np.zeros_like(x) if no_residual else x.copy()
+    todo = range(N) if only_experts is None else sorted(set(int(e) for e in only_experts))
+    if only_experts is not None:
+        for e in range(N):
+            if e not in todo:
+                y[dp["row2tok"][dp["offset"][e]:dp["offset"][e + 1]]] = np.nan
+    for e in todo:
+        rows = dp["row2tok"][dp["offset"][e]:dp["offset"][e + 1]]
+        if len(rows) == 0:
+            continue
+        W1e, b1e, W2e, b2e = get(e)
+        o = expert_ffn(x[rows], W1e, b1e, W2e, b2e)
+        contrib = gate[rows, None] * o
+        y[rows] = contrib if no_residual else x[rows] + contrib
+
+    return {
+        "C": C, "logits": r["logits"], "probs": r["probs"], "expert_idx": eidx,
+        "router_expert_idx": r["expert_idx"], "gate": gate, "aux_loss": aux,
+        "y64": y, "y": round_to_dtype(y, dtype), **dp,
+    }
+
+
+def near_tie_tokens(logits: np.ndarray, tol: float = 1e-5) -> np.ndarray:
+    """Tokens whose top-1 and top-2 logits differ by at most tol (float64 logits)."""
+    if logits.shape[1] < 2:
+        return np.zeros(logits.shape[0], dtype=bool)
+    part = np.partition(logits, -2, axis=1)
+    return (part[:, -1] - part[:, -2]) <= tol

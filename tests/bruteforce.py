@@ -1,0 +1,72 @@
+"""Brute-force SwitchFFN forward: pure Python, one token at a time.
+
+An independent second reading of the layer for tiny inputs, used to pin the
+oracle.  It shares nothing with the oracle: no numpy, a token's rank is found
+by scanning every earlier token, each dot product is an exactly rounded
+math.fsum, and the fp32 rounding of a logit goes through struct.
+"""
+from __future__ import annotations
+
+import math
+import struct
+
+
+def to_f32(v: float) -> float:
+    return struct.unpack("<f", struct.pack("<f", v))[0]
+
+
+def dot(a, b) -> float:
+    return math.fsum(ai * bi for ai, bi in zip(a, b))
+
+
+def brute_forward(x, Wr, W1, b1, W2, b2, CF, no_residual=False):
+    """All arguments are nested lists of floats (b1/b2 may be None)."""
+    T = len(x)
+    N = len(Wr)
+    d = len(x[0]) if T else len(Wr[0])
+    F = len(W1[0])
+    C = math.floor(CF * T / N)
+
+    choice, probs = [], []
+    for t in range(T):
+        z = [dot(x[t], Wr[i]) for i in range(N)]
+        z32 = [to_f32(v) for v in z]
+        best = 0
+        for i in range(1, N):
+            if z32[i] > z32[best]:
+                best = i
+        m = max(z)
+        ex = [math.exp(v - m) for v in z]
+        s = math.fsum(ex)
+        choice.append(best)
+        probs.append([v / s for v in ex])
+
+    slot, y = [], []
+    for t in range(T):
+        e = choice[t]
+        rank = sum(1 for s_ in range(t) if choice[s_] == e)
+        accepted = rank < C
+        slot.append(rank if accepted else -1)
+        if not accepted:
+            y.append([0.0] * d if no_residual else list(x[t]))
+            continue
+        g = probs[t][e]
+        h = []
+        for j in range(F):
+            a = dot(W1[e][j], x[t]) + (b1[e][j] if b1 is not None else 0.0)
+            h.append(a if a > 0.0 else 0.0)
+        row = []
+        for i in range(d):
+            o = dot(W2[e][i], h) + (b2[e][i] if b2 is not None else 0.0)
+            row.append(g * o if no_residual else x[t][i] + g * o)
+        y.append(row)
+
+    aux = 0.0
+    for i in range(N):
+        f_i = sum(1 for t in range(T) if choice[t] == i) / T
+        P_i = math.fsum(probs[t][i] for t in range(T)) / T
+        aux += f_i * P_i
+    aux *= N
+    gate = [probs[t][choice[t]] for t in range(T)]
+    return {"C": C, "expert_idx": choice, "slot": slot, "gate": gate, "aux_loss": aux, "y": y,
+            "probs": probs}

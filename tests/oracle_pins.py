@@ -1,0 +1,264 @@
+"""Pins of the CPU oracle: facts fixed by the pages or by the mathematics.
+
+Each pin is a plain function that raises AssertionError on failure, so the
+same set can be run against the oracle as written (test_oracle_pins.py) and
+against deliberately broken copies of it (test_oracle_mutations.py).
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+
+import oracle.switchffn_oracle as O
+from bruteforce import brute_forward
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _f32(a):
+    return np.asarray(a, np.float32).astype(np.float64)
+
+
+def random_case(seed, T, d, F, N, bias=False, wscale=0.3):
+    rng = np.random.default_rng(seed)
+    x = _f32(rng.standard_normal((T, d)))
+    Wr = _f32(rng.standard_normal((N, d)) * wscale)
+    W1 = _f32(rng.standard_normal((N, F, d)) * wscale)
+    W2 = _f32(rng.standard_normal((N, d, F)) * wscale)
+    b1 = _f32(rng.standard_normal((N, F)) * wscale) if bias else None
+    b2 = _f32(rng.standard_normal((N, d)) * wscale) if bias else None
+    return x, Wr, W1, b1, W2, b2
+
+
+def _tolist(a):
+    return None if a is None else np.asarray(a).tolist()
+
+
+def _close(a, b, tol):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    assert a.shape == b.shape, (a.shape, b.shape)
+    assert np.all(np.abs(a - b) <= tol * (1.0 + np.abs(b))), float(np.max(np.abs(a - b)))
+
+
+def _zero_ffn(N, F, d):
+    return (np.zeros((N, F, d)), None, np.zeros((N, d, F)), None)
+
+
+# ---------------------------------------------------------------------------
+# Aux loss: the worked example of the Math-LLMs card 08 and its closed forms.
+# ---------------------------------------------------------------------------
+def pin_aux_worked_example():
+    g = json.load(open(os.path.join(GOLDEN, "aux_worked_example.json")))
+    rows = np.array(g["book_batch_rows"], np.float64)
+    N = g["book_batch"]["experts"]
+    assert rows.shape == (g["book_batch"]["tokens"], N)
+    x = np.log(rows)
+    Wr = np.eye(N)
+    r = O.forward(x, Wr, _zero_ffn(N, 4, N), CF=2.0)
+    T = rows.shape[0]
+    f = np.bincount(r["expert_idx"], minlength=N) / T
+    _close(f, g["book_batch"]["f"], 1e-15)
+    _close(r["probs"].mean(axis=0), g["book_batch"]["p"], 1e-12)
+    assert abs(r["aux_loss"] - g["book_batch"]["loss"]) < 1e-12, r["aux_loss"]
+
+    rows = np.array(g["check_question_rows"], np.float64)
+    r = O.forward(np.log(rows), np.eye(4), _zero_ffn(4, 4, 4), CF=2.0)
+    f = np.bincount(r["expert_idx"], minlength=4) / rows.shape[0]
+    _close(f, g["check_question"]["f"], 1e-15)
+    assert abs(r["aux_loss"] - g["check_question"]["loss"]) < 1e-12, r["aux_loss"]
+
+
+def pin_aux_uniform_probs():
+    # Wr = 0: every logit is 0, p is uniform, and the aux loss is 1 whatever f is
+    # (all tokens tie and go to expert 0).
+    for N in (1, 3, 8):
+        x, _, W1, b1, W2, b2 = random_case(1, 20, 6, 5, N)
+        r = O.forward(x, np.zeros((N, 6)), (W1, b1, W2, b2), CF=1.0)
+        assert np.all(r["expert_idx"] == 0)
+        _close(r["gate"], np.full(20, 1.0 / N), 1e-15)
+        assert abs(r["aux_loss"] - 1.0) < 1e-12
+
+
+def pin_aux_uniform_f():
+    # x_t = s * e_{t mod N}, Wr = I: each expert gets T/N tokens, sum_i P_i = 1, aux = 1.
+    N, T, s = 4, 12, 3.0
+    x = np.zeros((T, N))
+    x[np.arange(T), np.arange(T) % N] = s
+    r = O.forward(x, np.eye(N), _zero_ffn(N, 2, N), CF=1.0)
+    assert np.all(np.bincount(r["expert_idx"], minlength=N) == T // N)
+    assert abs(r["aux_loss"] - 1.0) < 1e-12
+
+
+def pin_aux_one_expert_limit():
+    # Every token prefers expert 0 by a margin s: p_0 = 1 / (1 + (N-1) e^-s), so
+    # aux = N * 1 * p_0, which tends to N as s grows.
+    N, T = 6, 10
+    for s in (1.0, 5.0, 40.0):
+        x = np.zeros((T, N))
+        x[:, 0] = s
+        r = O.forward(x, np.eye(N), _zero_ffn(N, 2, N), CF=float(N))
+        expect = N / (1.0 + (N - 1) * math.exp(-s))
+        assert abs(r["aux_loss"] - expect) < 1e-12 * N, (r["aux_loss"], expect)
+
+
+def pin_aux_can_fall_below_one():
+    # The inner sum is not bounded below by 1/N for arbitrary routings: with
+    # p rows (.51,.49), (.51,.49), (.01,.99): f = (2/3, 1/3), P = (1.03/3, 1.97/3),
+    # aux = 2 * (2.06 + 1.97) / 9 = 8.06 / 9.
+    rows = np.array([[0.51, 0.49], [0.51, 0.49], [0.01, 0.99]])
+    r = O.forward(np.log(rows), np.eye(2), _zero_ffn(2, 2, 2), CF=2.0)
+    assert abs(r["aux_loss"] - 8.06 / 9.0) < 1e-12, r["aux_loss"]
+
+
+# ---------------------------------------------------------------------------
+# Capacity and dispatch.
+# ---------------------------------------------------------------------------
+def pin_capacity_values():
+    assert O.capacity(64, 4, 1.0) == 16
+    assert O.capacity(8192, 64, 1.25) == 160
+    assert O.capacity(16384, 128, 1.0) == 128
+    assert O.capacity(32768, 128, 1.25) == 320
+    assert O.capacity(65536, 2048, 1.0) == 32
+    assert O.capacity(10, 4, 1.0) == 2       # 2.5 rounds down
+    assert O.capacity(10, 4, 1.25) == 3      # 3.125
+    assert O.capacity(7, 3, 1.0) == 2
+    assert O.capacity(7, 3, 0.0) == 0
+    assert O.capacity(7, 3, 3.0) == 7        # CF = N admits every token
+    assert O.capacity(0, 3, 1.0) == 0
+    for bad in ((5, 0, 1.0), (5, 2, -0.5), (5, 2, float("nan")), (5, 2, float("inf"))):
+        try:
+            O.capacity(*bad)
+        except ValueError:
+            continue
+        raise AssertionError(f"capacity{bad} accepted")
+
+
+def pin_dispatch_bruteforce():
+    rng = np.random.default_rng(7)
+    for T, N, C in ((1, 1, 0), (1, 1, 1), (50, 3, 10), (200, 7, 20), (64, 4, 64), (33, 5, 0)):
+        skew = rng.dirichlet(np.ones(N) * 0.5)
+        eidx = rng.choice(N, size=T, p=skew)
+        dp = O.dispatch(eidx, N, C)
+        for t in range(T):
+            rank = sum(1 for s in range(t) if eidx[s] == eidx[t])
+            assert dp["rank"][t] == rank
+            assert dp["slot"][t] == (rank if rank < C else -1)
+        hist = np.bincount(eidx, minlength=N)
+        assert np.array_equal(dp["hist"], hist)
+        assert np.array_equal(dp["accepted"], np.minimum(hist, C))
+        assert int(dp["offset"][-1]) + int(np.sum(dp["slot"] < 0)) == T
+        for e in range(N):
+            toks = dp["row2tok"][dp["offset"][e]:dp["offset"][e + 1]]
+            assert np.all(eidx[toks] == e)
+            assert np.array_equal(dp["slot"][toks], np.arange(len(toks)))
+            assert np.all(np.diff(toks) > 0)
+
+
+def pin_capacity_special_cases():
+    x, Wr, W1, b1, W2, b2 = random_case(3, 40, 6, 7, 4, bias=True)
+    r = O.forward(x, Wr, (W1, b1, W2, b2), CF=0.0)          # C = 0: all dropped
+    assert r["C"] == 0 and np.all(r["slot"] == -1)
+    assert np.array_equal(r["y64"], x)
+    r = O.forward(x, Wr, (W1, b1, W2, b2), CF=4.0)          # CF = N: none dropped
+    assert np.all(r["slot"] >= 0)
+    r = O.forward(x, np.zeros_like(Wr), (W1, b1, W2, b2), CF=1.0)   # Wr = 0
+    assert r["C"] == 10
+    assert np.array_equal(r["slot"][:10], np.arange(10)) and np.all(r["slot"][10:] == -1)
+    assert np.array_equal(r["y64"][10:], x[10:])
+
+
+# ---------------------------------------------------------------------------
+# Expert FFN, gate and combine.
+# ---------------------------------------------------------------------------
+def pin_ffn_hand_example():
+    # One expert (gate 1), d = 2, F = 3, worked by hand:
+    #   a = W1 x + b1 = (1*2 - 1*1 + 0.5, 0*2 + 2*1 - 3, -1*2 + 0*1 + 4) = (1.5, -1, 2)
+    #   h = ReLU(a) = (1.5, 0, 2)
+    #   o = W2 h + b2 = (1*1.5 + 5*0 - 1*2 + 0.25, 2*1.5 + 0*0 + 0.5*2 - 1) = (-0.25, 3)
+    #   y = x + o = (1.75, 4)
+    x = np.array([[2.0, 1.0]])
+    W1 = np.array([[[1.0, -1.0], [0.0, 2.0], [-1.0, 0.0]]])
+    b1 = np.array([[0.5, -3.0, 4.0]])
+    W2 = np.array([[[1.0, 5.0, -1.0], [2.0, 0.0, 0.5]]])
+    b2 = np.array([[0.25, -1.0]])
+    r = O.forward(x, np.zeros((1, 2)), (W1, b1, W2, b2), CF=1.0)
+    assert r["gate"][0] == 1.0 and r["expert_idx"][0] == 0
+    assert np.array_equal(r["y64"], np.array([[1.75, 4.0]]))
+    r = O.forward(x, np.zeros((1, 2)), (W1, b1, W2, b2), CF=1.0, no_residual=True)
+    assert np.array_equal(r["y64"], np.array([[-0.25, 3.0]]))
+
+
+def pin_dense_ffn_n1():
+    # N = 1 and CF >= 1: every token goes to the one expert with gate exactly 1 and
+    # the layer is x + FFN(x), the dense baseline of the paper note.
+    x, Wr, W1, b1, W2, b2 = random_case(11, 9, 5, 7, 1, bias=True)
+    r = O.forward(x, Wr, (W1, b1, W2, b2), CF=1.0)
+    assert np.all(r["gate"] == 1.0) and np.all(r["slot"] == np.arange(9))
+    for t in range(9):
+        h = [max(0.0, math.fsum(W1[0, j, k] * x[t, k] for k in range(5)) + b1[0, j]) for j in range(7)]
+        for i in range(5):
+            o = math.fsum(W2[0, i, j] * h[j] for j in range(7)) + b2[0, i]
+            assert abs(r["y64"][t, i] - (x[t, i] + o)) < 1e-12
+
+
+def pin_x_zero_closed_form():
+    # x = 0: all logits tie at 0, every token goes to expert 0 with gate 1/N and
+    # the accepted ones get y = (W2_0 ReLU(b1_0) + b2_0) / N; the rest stay 0.
+    N, T, d, F = 4, 16, 3, 5
+    _, _, W1, b1, W2, b2 = random_case(5, T, d, F, N, bias=True)
+    _, Wr, _, _, _, _ = random_case(6, T, d, F, N)
+    r = O.forward(np.zeros((T, d)), Wr, (W1, b1, W2, b2), CF=1.0)
+    C = r["C"]
+    h = [max(0.0, b1[0, j]) for j in range(F)]
+    o = [math.fsum(W2[0, i, j] * h[j] for j in range(F)) + b2[0, i] for i in range(d)]
+    for t in range(T):
+        want = [v / N for v in o] if t < C else [0.0] * d
+        _close(r["y64"][t], want, 1e-14)
+
+
+def pin_bruteforce_agreement():
+    cases = [
+        dict(seed=21, T=1, d=3, F=4, N=1, CF=1.0, bias=False),
+        dict(seed=22, T=7, d=5, F=6, N=3, CF=1.0, bias=True),
+        dict(seed=23, T=64, d=8, F=12, N=4, CF=1.0, bias=False),
+        dict(seed=24, T=100, d=6, F=9, N=8, CF=0.5, bias=True),
+        dict(seed=25, T=40, d=4, F=3, N=3, CF=1.25, bias=True),
+        dict(seed=26, T=30, d=7, F=5, N=5, CF=2.0, bias=False),
+        dict(seed=27, T=25, d=3, F=2, N=4, CF=4.0, bias=True),
+    ]
+    for c in cases:
+        x, Wr, W1, b1, W2, b2 = random_case(c["seed"], c["T"], c["d"], c["F"], c["N"], c["bias"])
+        for nr in (False, True):
+            r = O.forward(x, Wr, (W1, b1, W2, b2), CF=c["CF"], no_residual=nr)
+            b = brute_forward(_tolist(x), _tolist(Wr), _tolist(W1), _tolist(b1), _tolist(W2),
+                              _tolist(b2), c["CF"], no_residual=nr)
+            assert r["C"] == b["C"]
+            assert list(r["expert_idx"]) == b["expert_idx"]
+            assert list(r["slot"]) == b["slot"]
+            _close(r["gate"], b["gate"], 1e-12)
+            _close(r["probs"], b["probs"], 1e-12)
+            assert abs(r["aux_loss"] - b["aux_loss"]) < 1e-12
+            _close(r["y64"], b["y"], 1e-12)
+
+
+def pin_ties_lowest_index():
+    # Logit ties (exact in fp32) go to the lowest expert index.
+    x = np.array([[1.0, 1.0, 0.0], [0.0, 2.0, 2.0], [3.0, 3.0, 3.0], [0.0, 0.0, 5.0]])
+    r = O.forward(x, np.eye(3), _zero_ffn(3, 2, 3), CF=3.0)
+    assert list(r["expert_idx"]) == [0, 1, 0, 2]
+
+
+def pin_round_to_bf16():
+    ulp = 2.0 ** -7
+    vals = np.array([1.0, 1.0 + ulp / 2, 1.0 + 1.5 * ulp, 1.0 + 0.75 * ulp, -1.0 - ulp / 2,
+                     3.0 + 0.3 * 2 * ulp, 0.0, 255.5, 256.5, 1.0 + 2.0 ** -30])
+    want = np.array([1.0, 1.0, 1.0 + 2 * ulp, 1.0 + ulp, -1.0, 3.0, 0.0, 256.0, 256.0, 1.0])
+    got = O.round_to_bf16(vals)
+    assert np.array_equal(got, want), got
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

@@ -1,0 +1,192 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check that the pins catch each.
+
+A pin set that a dropped term, a wrong sign or index, or a transposed operand
+slips through would not pin the oracle; every mutant below must make at least
+one pin fail.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle.switchffn_oracle as O
+from oracle_pins import ALL_PINS
+
+_orig = {name: getattr(O, name) for name in
+         ("capacity", "router_logits", "softmax", "top1", "dispatch", "aux_loss", "expert_ffn",
+          "round_to_bf16", "forward")}
+
+
+def _ffn_no_b2(xe, W1e, b1e, W2e, b2e):
+    return _orig["expert_ffn"](xe, W1e, b1e, W2e, None)
+
+
+def _ffn_no_b1(xe, W1e, b1e, W2e, b2e):
+    return _orig["expert_ffn"](xe, W1e, None, W2e, b2e)
+
+
+def _ffn_no_relu(xe, W1e, b1e, W2e, b2e):
+    a = xe @ np.asarray(W1e).T + (0 if b1e is None else b1e)
+    return a @ np.asarray(W2e).T + (0 if b2e is None else b2e)
+
+
+def _ffn_relu_after(xe, W1e, b1e, W2e, b2e):
+    return np.maximum(_ffn_no_relu(xe, W1e, b1e, W2e, b2e), 0.0)
+
+
+def _ffn_transposed_w1(xe, W1e, b1e, W2e, b2e):
+    W1e = np.asarray(W1e)
+    return _orig["expert_ffn"](xe, W1e.reshape(W1e.shape[::-1]), b1e, W2e, b2e)
+
+
+def _logits_sign(x, Wr):
+    return -_orig["router_logits"](x, Wr)
+
+
+def _logits_untransposed(x, Wr):
+    Wr = np.asarray(Wr, np.float64)
+    return np.asarray(x, np.float64) @ Wr.reshape(Wr.shape[::-1])
+
+
+def _softmax_axis0(z):
+    m = z.max(axis=0, keepdims=True)
+    e = np.exp(z - m)
+    return e / e.sum(axis=0, keepdims=True)
+
+
+def _softmax_no_norm(z):
+    return np.exp(z - z.max(axis=1, keepdims=True))
+
+
+def _top1_last_tie(z):
+    z32 = z.astype(np.float32)[:, ::-1]
+    return (z.shape[1] - 1 - np.argmax(z32, axis=1)).astype(np.int64)
+
+
+def _top1_argmin(z):
+    return np.argmin(z.astype(np.float32), axis=1).astype(np.int64)
+
+
+def _dispatch_one_based(eidx, N, C):
+    dp = _orig["dispatch"](eidx, N, C)
+    rank = dp["rank"] + 1
+    dp["rank"] = rank
+    dp["slot"] = np.where(rank < C, rank, -1)
+    return dp
+
+
+def _dispatch_le(eidx, N, C):
+    return _orig["dispatch"](eidx, N, C + 1)
+
+
+def _dispatch_reverse_order(eidx, N, C):
+    T = len(eidx)
+    dp = _orig["dispatch"](np.asarray(eidx)[::-1], N, C)
+    out = dict(dp)
+    for k in ("rank", "slot"):
+        out[k] = dp[k][::-1]
+    out["row2tok"] = T - 1 - dp["row2tok"]
+    return out
+
+
+def _aux_no_n(eidx, probs):
+    return _orig["aux_loss"](eidx, probs) / probs.shape[1]
+
+
+def _aux_gate_only(eidx, probs):
+    T, N = probs.shape
+    onehot = np.zeros_like(probs)
+    onehot[np.arange(T), eidx] = probs[np.arange(T), eidx]
+    return _orig["aux_loss"](eidx, onehot)
+
+
+def _aux_f_squared(eidx, probs):
+    T, N = probs.shape
+    f = np.bincount(eidx, minlength=N) / T
+    return float(N * np.dot(f, f))
+
+
+def _capacity_ceil(T, N, CF):
+    _orig["capacity"](T, N, CF)
+    return int(math.ceil(CF * T / N))
+
+
+def _capacity_floor_first(T, N, CF):
+    _orig["capacity"](T, N, CF)
+    return int(math.floor(T / N) * CF)
+
+
+def _bf16_truncate(v):
+    m, e = np.frexp(np.asarray(v, np.float64))
+    return np.ldexp(np.trunc(m * 256.0), e - 8)
+
+
+def _forward_no_residual(*a, **k):
+    k = dict(k)
+    r = _orig["forward"](*a, **k)
+    if not k.get("no_residual"):
+        x = np.asarray(a[0], np.float64)
+        acc = r["slot"] >= 0
+        r["y64"] = r["y64"].copy()
+        r["y64"][acc] -= x[acc]
+    return r
+
+
+def _forward_dropped_zero(*a, **k):
+    r = _orig["forward"](*a, **k)
+    r["y64"] = r["y64"].copy()
+    r["y64"][r["slot"] < 0] = 0.0
+    return r
+
+
+def _forward_gate_outside_b2(*a, **k):
+    # y = x + g * (W2 h) + b2 instead of x + g * (W2 h + b2)
+    r = _orig["forward"](*a, **k)
+    experts = a[2] if len(a) > 2 else k["experts"]
+    b2 = experts[3] if not callable(experts) else None
+    if b2 is not None:
+        r["y64"] = r["y64"].copy()
+        for t in np.nonzero(r["slot"] >= 0)[0]:
+            e = r["expert_idx"][t]
+            r["y64"][t] += (1.0 - r["gate"][t]) * b2[e]
+    return r
+
+
+MUTANTS = {
+    "ffn_drops_b2": ("expert_ffn", _ffn_no_b2),
+    "ffn_drops_b1": ("expert_ffn", _ffn_no_b1),
+    "ffn_no_relu": ("expert_ffn", _ffn_no_relu),
+    "ffn_relu_after_w2": ("expert_ffn", _ffn_relu_after),
+    "ffn_w1_transposed": ("expert_ffn", _ffn_transposed_w1),
+    "logits_sign_flip": ("router_logits", _logits_sign),
+    "logits_wr_untransposed": ("router_logits", _logits_untransposed),
+    "softmax_wrong_axis": ("softmax", _softmax_axis0),
+    "softmax_unnormalised": ("softmax", _softmax_no_norm),
+    "top1_ties_to_highest": ("top1", _top1_last_tie),
+    "top1_argmin": ("top1", _top1_argmin),
+    "dispatch_one_based_rank": ("dispatch", _dispatch_one_based),
+    "dispatch_capacity_off_by_one": ("dispatch", _dispatch_le),
+    "dispatch_reverse_token_order": ("dispatch", _dispatch_reverse_order),
+    "aux_missing_n": ("aux_loss", _aux_no_n),
+    "aux_gate_only": ("aux_loss", _aux_gate_only),
+    "aux_f_times_f": ("aux_loss", _aux_f_squared),
+    "capacity_ceil": ("capacity", _capacity_ceil),
+    "capacity_floor_then_scale": ("capacity", _capacity_floor_first),
+    "bf16_truncates": ("round_to_bf16", _bf16_truncate),
+    "combine_no_residual": ("forward", _forward_no_residual),
+    "dropped_rows_zeroed": ("forward", _forward_dropped_zero),
+    "gate_outside_b2": ("forward", _forward_gate_outside_b2),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, monkeypatch):
+    attr, fn = MUTANTS[name]
+    monkeypatch.setattr(O, attr, fn)
+    caught = []
+    for pin in ALL_PINS:
+        try:
+            pin()
+        except Exception as exc:  # noqa: BLE001 -- any failure of a pin counts
+            caught.append(f"{pin.__name__}: {type(exc).__name__}")
+    assert caught, f"mutant {name} passed every pin"
