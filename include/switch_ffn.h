@@ -1,0 +1,141 @@
+/*
+ * switch_ffn.h -- C-ABI of the SwitchFFN forward pass on one MI355X (gfx950).
+ *
+ * The layer (one Switch layer's sparse FFN, forward only):
+ *   router   z[t,i] = sum_k x[t,k] Wr[i,k] in fp32; p[t,:] = softmax(z[t,:]);
+ *            e_t = argmax_i z[t,i] (ties -> lowest index); gate g_t = p[t,e_t]
+ *            ("Switch Transformers: Scaling to Trillion Parameter Models with
+ *            Simple and Efficient Sparsity", section 3.4, "Switch Routing: The
+ *            k=1 Simplification"; float32 router per "Selective Precision
+ *            Training" in the same section).
+ *   capacity C = floor(CF * T / N) (same page, "Distributed Implementation and
+ *            Expert Capacity"; the pages round differently, this is the reading
+ *            used throughout).  The first C tokens of an expert in token order
+ *            are accepted; the rest are dropped (that section's overflow
+ *            handling: a running count per expert, positions past C masked out).
+ *   experts  E_e(v) = W2[e] ReLU(W1[e] v + b1[e]) + b2[e] ("Switch Transformer"
+ *            paper note, section "Expert FFN Layer").
+ *   combine  y_t = x_t + g_t E_{e_t}(x_t) for accepted tokens, y_t = x_t for
+ *            dropped ones (section 3.2 "Big-Picture Architecture", information
+ *            flow: scaled by the gate, added through the residual; overflow
+ *            tokens pass through unchanged).
+ *   aux      aux = N sum_i f_i P_i with f_i = #{t : e_t = i}/T (before capacity)
+ *            and P_i = (1/T) sum_t p[t,i] (section 3.4, "The Load-Balancing
+ *            Auxiliary Loss"); returned without the alpha factor.
+ *
+ * Layouts (row-major, all device memory):
+ *   x [T, d]   Wr [N, d] (fp32)   W1 [N, F, d]   b1 [N, F]   W2 [N, d, F]
+ *   b2 [N, d]  y [T, d]  expert_idx [T] (int32)  slot [T] (int32)
+ *   gate [T] (fp32)  aux_loss [1] (fp32)
+ * x, W1, b1, W2, b2 and y share `dtype` (SFFN_FP32 or SFFN_BF16); Wr, gate and
+ * aux_loss are always fp32.  Every GEMM operand is contiguous along its
+ * reduction axis.  b1 and b2 may be NULL (zero bias).
+ *
+ * Outputs for a dropped token t: expert_idx[t] = its routed expert,
+ * slot[t] = -1, gate[t] = p[t, e_t], y[t] = x[t].  Accepted tokens have
+ * slot[t] in [0, C): their position in the expert's buffer.
+ *
+ * Ownership and ordering: every pointer is owned by the caller.  The library
+ * allocates nothing, keeps no state between calls (apart from loading its code
+ * object once) and enqueues all work on `stream` (a hipStream_t; NULL = the
+ * default stream) without synchronising the host: outputs are valid once the
+ * stream reaches the end of the call, and inputs must stay unchanged until
+ * then.  Calls on different streams are independent when each has its own
+ * workspace and outputs.
+ *
+ * Errors: arguments are validated before anything is enqueued; on an error
+ * nothing is launched and no output is touched.  NaN/Inf inputs are not
+ * checked (undefined results).  SFFN_EHIP reports a launch failure; the HIP
+ * error text is then available from switch_ffn_status_string(SFFN_EHIP) on
+ * the same thread.
+ */
+#ifndef SWITCH_FFN_H
+#define SWITCH_FFN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define SFFN_OK 0
+#define SFFN_EINVAL (-1)       /* null required pointer, T/d/F/N <= 0, CF < 0 or not finite */
+#define SFFN_EDTYPE (-2)       /* dtype is neither SFFN_FP32 nor SFFN_BF16 */
+#define SFFN_EWORKSPACE (-3)   /* workspace NULL or smaller than switch_ffn_workspace_bytes() */
+#define SFFN_EUNSUPPORTED (-4) /* shape or alignment outside this build's limits (see below) */
+#define SFFN_EHIP (-5)         /* a HIP launch failed */
+
+/* Element types of x, W1, b1, W2, b2 and y. */
+#define SFFN_FP32 0
+#define SFFN_BF16 1
+
+/* forward_ex flags. */
+#define SFFN_NO_RESIDUAL 1u /* y = g*E(x) for accepted tokens and 0 for dropped ones */
+
+/* Limits of this build (SFFN_EUNSUPPORTED beyond them):
+ *   N <= 4096;  T * max(N, d, F) < 2^31;
+ *   SFFN_BF16: d % 8 == 0, F % 8 == 0, and x, W1, W2, y 16-byte aligned. */
+#define SFFN_MAX_EXPERTS 4096
+
+/* Optional routing statistics of forward_ex (each pointer device memory, nullable):
+ *   expert_count[N]   tokens whose top-1 is expert i (before capacity)
+ *   accepted_count[N] tokens expert i processes: min(expert_count[i], C)
+ *   n_dropped[1]      tokens dropped by the capacity limit */
+typedef struct sffn_stats {
+  int32_t* expert_count;
+  int32_t* accepted_count;
+  int32_t* n_dropped;
+} sffn_stats;
+
+/* Expert capacity C = floor((CF * T) / N), evaluated in IEEE double in that
+ * order.  Returns -1 if T < 0, N <= 0, or CF is negative or not finite.
+ * Host only; touches no device. */
+int64_t switch_ffn_capacity(int64_t T, int64_t N, double CF);
+
+/* Bytes of device workspace switch_ffn_forward needs for this shape (0 on bad
+ * arguments).  Host only.  The workspace holds fp32 router logits [T, N],
+ * per-block probability sums, dispatch counts and offsets, the row-to-token
+ * map and the expert hidden activations [min(T, N*C), F]. */
+size_t switch_ffn_workspace_bytes(int64_t T, int64_t d, int64_t F, int64_t N, double CF,
+                                  int dtype);
+
+/* The SwitchFFN forward pass (see the top of this file).  `workspace` is a
+ * device buffer of at least switch_ffn_workspace_bytes() bytes, 256-byte
+ * aligned; its contents on entry do not matter and are garbage afterwards.
+ * `stream` is a hipStream_t.  Returns SFFN_OK or a negative status. */
+int switch_ffn_forward(const void* x, const float* Wr, const void* W1, const void* b1,
+                       const void* W2, const void* b2, int64_t T, int64_t d, int64_t F,
+                       int64_t N, double CF, int dtype, void* y, int32_t* expert_idx,
+                       int32_t* slot, float* gate, float* aux_loss, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+/* switch_ffn_forward plus:
+ *   flags         0 or SFFN_NO_RESIDUAL (a diagnostic: the bare expert term)
+ *   stats         optional routing statistics (NULL = none)
+ *   stage_events  optional host array of switch_ffn_num_stages()+1 hipEvent_t
+ *                 handles (created by the caller); event i is recorded on
+ *                 `stream` before stage i and the last one after the final
+ *                 stage, so the caller can time each stage.  NULL = none. */
+int switch_ffn_forward_ex(const void* x, const float* Wr, const void* W1, const void* b1,
+                          const void* W2, const void* b2, int64_t T, int64_t d, int64_t F,
+                          int64_t N, double CF, int dtype, void* y, int32_t* expert_idx,
+                          int32_t* slot, float* gate, float* aux_loss, void* workspace,
+                          size_t workspace_bytes, void* stream, uint32_t flags,
+                          const sffn_stats* stats, void* const* stage_events);
+
+/* Number of stages forward_ex reports events around, and their names
+ * ("router_logits", "softmax_route", ...); NULL for an index out of range. */
+int switch_ffn_num_stages(void);
+const char* switch_ffn_stage_name(int stage);
+
+/* Static description of a status code; for SFFN_EHIP, the text of the last
+ * HIP error seen on this thread. */
+const char* switch_ffn_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SWITCH_FFN_H */

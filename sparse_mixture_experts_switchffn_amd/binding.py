@@ -1,0 +1,171 @@
+"""ctypes binding of libswitchffn.so: the C-ABI names, argument marshalling only.
+
+Tensors are torch tensors in device memory (torch provides the allocations
+and the stream); every step of the layer runs in the library's HIP kernels.
+The library must be built (``__graft_entry__.build()``); loading fails loudly
+when it is missing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libswitchffn.so")
+HEADER = os.path.join(os.path.dirname(_HERE), "include", "switch_ffn.h")
+
+SFFN_OK = 0
+SFFN_EINVAL = -1
+SFFN_EDTYPE = -2
+SFFN_EWORKSPACE = -3
+SFFN_EUNSUPPORTED = -4
+SFFN_EHIP = -5
+SFFN_FP32 = 0
+SFFN_BF16 = 1
+SFFN_NO_RESIDUAL = 1
+
+
+class sffn_stats(ctypes.Structure):
+    _fields_ = [("expert_count", ctypes.c_void_p), ("accepted_count", ctypes.c_void_p),
+                ("n_dropped", ctypes.c_void_p)]
+
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_FWD_ARGS = [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, ctypes.c_double, ctypes.c_int,
+             _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+
+_lib = None
+
+
+def lib():
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: the HIP library must be built "
+                               "(__graft_entry__.build()); there is no fallback path")
+        L = ctypes.CDLL(LIB_PATH)
+        L.switch_ffn_capacity.restype = ctypes.c_int64
+        L.switch_ffn_capacity.argtypes = [_I64, _I64, ctypes.c_double]
+        L.switch_ffn_workspace_bytes.restype = ctypes.c_size_t
+        L.switch_ffn_workspace_bytes.argtypes = [_I64, _I64, _I64, _I64, ctypes.c_double,
+                                                 ctypes.c_int]
+        L.switch_ffn_forward.restype = ctypes.c_int
+        L.switch_ffn_forward.argtypes = _FWD_ARGS
+        L.switch_ffn_forward_ex.restype = ctypes.c_int
+        L.switch_ffn_forward_ex.argtypes = _FWD_ARGS + [ctypes.c_uint32,
+                                                        ctypes.POINTER(sffn_stats), _P]
+        L.switch_ffn_num_stages.restype = ctypes.c_int
+        L.switch_ffn_num_stages.argtypes = []
+        L.switch_ffn_stage_name.restype = ctypes.c_char_p
+        L.switch_ffn_stage_name.argtypes = [ctypes.c_int]
+        L.switch_ffn_status_string.restype = ctypes.c_char_p
+        L.switch_ffn_status_string.argtypes = [ctypes.c_int]
+        _lib = L
+    return _lib
+
+
+def header_functions() -> list:
+    """Names of the functions include/switch_ffn.h declares."""
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(switch_ffn_\w+)\s*\(", text)))
+
+
+def switch_ffn_capacity(T: int, N: int, CF: float) -> int:
+    return lib().switch_ffn_capacity(T, N, CF)
+
+
+def switch_ffn_workspace_bytes(T, d, F, N, CF, dtype) -> int:
+    return lib().switch_ffn_workspace_bytes(T, d, F, N, CF, dtype)
+
+
+def switch_ffn_num_stages() -> int:
+    return lib().switch_ffn_num_stages()
+
+
+def switch_ffn_stage_name(i: int):
+    s = lib().switch_ffn_stage_name(i)
+    return None if s is None else s.decode()
+
+
+def switch_ffn_status_string(status: int) -> str:
+    return lib().switch_ffn_status_string(status).decode()
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return SFFN_BF16
+    if t.dtype == torch.float32:
+        return SFFN_FP32
+    raise TypeError(f"x must be float32 or bfloat16, not {t.dtype}")
+
+
+def switch_ffn_forward(x, Wr, W1, b1, W2, b2, CF: float, *, y=None, expert_idx=None, slot=None,
+                       gate=None, aux_loss=None, workspace=None, stream=None, flags: int = 0,
+                       stats=None, stage_events=None, check: bool = True) -> dict:
+    """Run the layer on device tensors; returns the output tensors (allocated when not given).
+
+    x [T, d], Wr [N, d] fp32, W1 [N, F, d], b1 [N, F] | None, W2 [N, d, F], b2 [N, d] | None.
+    stats: optional dict of int32 device tensors 'expert_count' [N], 'accepted_count' [N],
+    'n_dropped' [1].  stage_events: optional list of torch.cuda.Event (already recorded once
+    so that the handle exists), switch_ffn_num_stages()+1 of them.
+    """
+    import torch
+
+    T, d = x.shape
+    N = Wr.shape[0]
+    F = W1.shape[1]
+    dt = _dtype_code(x)
+    dev = x.device
+    if y is None:
+        y = torch.empty_like(x)
+    if expert_idx is None:
+        expert_idx = torch.empty(T, dtype=torch.int32, device=dev)
+    if slot is None:
+        slot = torch.empty(T, dtype=torch.int32, device=dev)
+    if gate is None:
+        gate = torch.empty(T, dtype=torch.float32, device=dev)
+    if aux_loss is None:
+        aux_loss = torch.empty(1, dtype=torch.float32, device=dev)
+    nbytes = switch_ffn_workspace_bytes(T, d, F, N, CF, dt)
+    if workspace is None and nbytes > 0:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    st = None
+    if stats is not None:
+        st = sffn_stats(_ptr(stats.get("expert_count")), _ptr(stats.get("accepted_count")),
+                        _ptr(stats.get("n_dropped")))
+    ev = None
+    if stage_events is not None:
+        handles = [e.cuda_event for e in stage_events]
+        if any(h == 0 for h in handles):
+            raise ValueError("stage events must be recorded once before use (handle is null)")
+        ev = (ctypes.c_void_p * len(handles))(*handles)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    args = (_ptr(x), _ptr(Wr), _ptr(W1), _ptr(b1), _ptr(W2), _ptr(b2), T, d, F, N, CF, dt,
+            _ptr(y), _ptr(expert_idx), _ptr(slot), _ptr(gate), _ptr(aux_loss), _ptr(workspace),
+            ws_bytes, stream)
+    if flags == 0 and st is None and ev is None:
+        name = "switch_ffn_forward"
+        rc = lib().switch_ffn_forward(*args)
+    else:
+        name = "switch_ffn_forward_ex"
+        rc = lib().switch_ffn_forward_ex(*args, flags, None if st is None else ctypes.byref(st),
+                                         None if ev is None else ctypes.cast(ev, ctypes.c_void_p))
+    if check and rc != SFFN_OK:
+        raise RuntimeError(f"{name} failed ({rc}): {switch_ffn_status_string(rc)}")
+    return {"status": rc, "y": y, "expert_idx": expert_idx, "slot": slot, "gate": gate,
+            "aux_loss": aux_loss, "workspace": workspace}
+
+
+# forward_ex's extra arguments are keyword arguments of switch_ffn_forward.
+switch_ffn_forward_ex = switch_ffn_forward

@@ -1,0 +1,187 @@
+// C-ABI entry points of the SwitchFFN library: argument checks, capacity,
+// workspace carve-up and the launch sequence (all on the caller's stream).
+#include <math.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "sffn_internal.h"
+#include "../../include/switch_ffn.h"
+
+namespace {
+
+thread_local char g_hip_error[256] = "no HIP error recorded";
+
+const char* const kStageNames[] = {"router_logits", "softmax_route", "dispatch_scan",
+                                   "dispatch_scatter", "ffn1", "ffn2"};
+constexpr int kNumStages = (int)(sizeof(kStageNames) / sizeof(kStageNames[0]));
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+bool aligned16(const void* p) { return p == nullptr || ((uintptr_t)p & 15) == 0; }
+
+int record_hip_error(hipError_t e, const char* what) {
+  snprintf(g_hip_error, sizeof(g_hip_error), "%s: %s", what, hipGetErrorString(e));
+  return SFFN_EHIP;
+}
+
+}  // namespace
+
+namespace sffn {
+
+size_t workspace_layout(const Shape& s, Workspace* ws, char* base) {
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    char* p = base ? base + off : nullptr;
+    off += align256(bytes);
+    return p;
+  };
+  const size_t T = (size_t)s.T, N = (size_t)s.N, nb = (size_t)s.n_route_blocks;
+  const size_t esize = s.dtype == SFFN_BF16 ? 2 : 4;
+  Workspace w;
+  w.logits = (float*)take(T * N * sizeof(float));
+  w.ppart = (float*)take(nb * N * sizeof(float));
+  w.cnt = (int*)take(nb * N * sizeof(int));
+  w.base = (int*)take(nb * N * sizeof(int));
+  w.lrank = (int*)take(T * sizeof(int));
+  w.hist = (int*)take(N * sizeof(int));
+  w.acc = (int*)take(N * sizeof(int));
+  w.offset = (int*)take((N + 1) * sizeof(int));
+  w.psum = (double*)take(N * sizeof(double));
+  w.row2tok = (int*)take((size_t)s.max_rows * sizeof(int) + 4);
+  w.H = (void*)take((size_t)s.max_rows * (size_t)s.F * esize + 16);
+  if (ws) *ws = w;
+  return off;
+}
+
+}  // namespace sffn
+
+// Shape checks shared by workspace sizing and the forward pass.
+static int make_shape(int64_t T, int64_t d, int64_t F, int64_t N, double CF, int dtype,
+                      sffn::Shape* s) {
+  if (T <= 0 || d <= 0 || F <= 0 || N <= 0 || !isfinite(CF) || CF < 0) return SFFN_EINVAL;
+  if (dtype != SFFN_FP32 && dtype != SFFN_BF16) return SFFN_EDTYPE;
+  if (N > SFFN_MAX_EXPERTS) return SFFN_EUNSUPPORTED;
+  const int64_t widest = N > d ? (N > F ? N : F) : (d > F ? d : F);
+  if (T > ((int64_t)1 << 31) / widest - 1) return SFFN_EUNSUPPORTED;
+  if (dtype == SFFN_BF16 && ((d % 8) != 0 || (F % 8) != 0)) return SFFN_EUNSUPPORTED;
+  const int64_t C = switch_ffn_capacity(T, N, CF);
+  const int64_t Ce = C < T ? C : T;  // a rank never reaches T
+  s->T = (int)T;
+  s->d = (int)d;
+  s->F = (int)F;
+  s->N = (int)N;
+  s->C = (int)Ce;
+  s->dtype = dtype;
+  s->n_route_blocks = (int)((T + sffn::kRouteTokens - 1) / sffn::kRouteTokens);
+  const int64_t cap_rows = N * Ce;
+  s->max_rows = (int)(cap_rows < T ? cap_rows : T);
+  return SFFN_OK;
+}
+
+extern "C" {
+
+int64_t switch_ffn_capacity(int64_t T, int64_t N, double CF) {
+  if (T < 0 || N <= 0 || !isfinite(CF) || CF < 0) return -1;
+  const double c = floor((CF * (double)T) / (double)N);
+  if (c >= 9.2e18) return INT64_MAX;
+  return (int64_t)c;
+}
+
+size_t switch_ffn_workspace_bytes(int64_t T, int64_t d, int64_t F, int64_t N, double CF,
+                                  int dtype) {
+  sffn::Shape s;
+  if (make_shape(T, d, F, N, CF, dtype, &s) != SFFN_OK) return 0;
+  return sffn::workspace_layout(s, nullptr, nullptr);
+}
+
+int switch_ffn_num_stages(void) { return kNumStages; }
+
+const char* switch_ffn_stage_name(int stage) {
+  return (stage >= 0 && stage < kNumStages) ? kStageNames[stage] : nullptr;
+}
+
+const char* switch_ffn_status_string(int status) {
+  switch (status) {
+    case SFFN_OK: return "ok";
+    case SFFN_EINVAL: return "invalid argument (null pointer, non-positive size, or bad CF)";
+    case SFFN_EDTYPE: return "unknown dtype (expected SFFN_FP32 or SFFN_BF16)";
+    case SFFN_EWORKSPACE: return "workspace missing or smaller than switch_ffn_workspace_bytes()";
+    case SFFN_EUNSUPPORTED:
+      return "unsupported shape or alignment (N <= 4096, T*max(N,d,F) < 2^31; bf16 needs d, F "
+             "multiples of 8 and 16-byte aligned x, Wr, W1, W2, y; workspace 256-byte aligned)";
+    case SFFN_EHIP: return g_hip_error;
+    default: return "unknown status";
+  }
+}
+
+int switch_ffn_forward_ex(const void* x, const float* Wr, const void* W1, const void* b1,
+                          const void* W2, const void* b2, int64_t T, int64_t d, int64_t F,
+                          int64_t N, double CF, int dtype, void* y, int32_t* expert_idx,
+                          int32_t* slot, float* gate, float* aux_loss, void* workspace,
+                          size_t workspace_bytes, void* stream, uint32_t flags,
+                          const sffn_stats* stats, void* const* stage_events) {
+  if (!x || !Wr || !W1 || !W2 || !y || !expert_idx || !slot || !gate || !aux_loss)
+    return SFFN_EINVAL;
+  if (flags & ~(uint32_t)SFFN_NO_RESIDUAL) return SFFN_EINVAL;
+  sffn::Shape s;
+  const int rc = make_shape(T, d, F, N, CF, dtype, &s);
+  if (rc != SFFN_OK) return rc;
+  if (dtype == SFFN_BF16 &&
+      !(aligned16(x) && aligned16(Wr) && aligned16(W1) && aligned16(W2) && aligned16(y)))
+    return SFFN_EUNSUPPORTED;
+  const size_t need = sffn::workspace_layout(s, nullptr, nullptr);
+  if (!workspace || workspace_bytes < need) return SFFN_EWORKSPACE;
+  if (((uintptr_t)workspace & 255) != 0) return SFFN_EUNSUPPORTED;
+
+  sffn::Workspace ws;
+  sffn::workspace_layout(s, &ws, (char*)workspace);
+  const sffn::Inputs in{x, Wr, W1, b1, W2, b2};
+  const sffn::Outputs out{y,
+                          expert_idx,
+                          slot,
+                          gate,
+                          aux_loss,
+                          stats ? stats->expert_count : nullptr,
+                          stats ? stats->accepted_count : nullptr,
+                          stats ? stats->n_dropped : nullptr};
+  const bool no_res = (flags & SFFN_NO_RESIDUAL) != 0;
+  hipStream_t st = (hipStream_t)stream;
+
+  auto mark = [&](int i) -> hipError_t {
+    if (!stage_events) return hipSuccess;
+    return hipEventRecord((hipEvent_t)stage_events[i], st);
+  };
+  hipError_t e;
+  if ((e = mark(0)) != hipSuccess) return record_hip_error(e, "event record");
+  if ((e = sffn::launch_router_logits(s, in, ws, st)) != hipSuccess)
+    return record_hip_error(e, kStageNames[0]);
+  if ((e = mark(1)) != hipSuccess) return record_hip_error(e, "event record");
+  if ((e = sffn::launch_softmax_route(s, ws, out, st)) != hipSuccess)
+    return record_hip_error(e, kStageNames[1]);
+  if ((e = mark(2)) != hipSuccess) return record_hip_error(e, "event record");
+  if ((e = sffn::launch_dispatch_scan(s, ws, st)) != hipSuccess)
+    return record_hip_error(e, kStageNames[2]);
+  if ((e = mark(3)) != hipSuccess) return record_hip_error(e, "event record");
+  if ((e = sffn::launch_dispatch_scatter(s, in, ws, out, no_res, st)) != hipSuccess)
+    return record_hip_error(e, kStageNames[3]);
+  if ((e = mark(4)) != hipSuccess) return record_hip_error(e, "event record");
+  if ((e = sffn::launch_ffn1(s, in, ws, st)) != hipSuccess)
+    return record_hip_error(e, kStageNames[4]);
+  if ((e = mark(5)) != hipSuccess) return record_hip_error(e, "event record");
+  if ((e = sffn::launch_ffn2(s, in, ws, out, no_res, st)) != hipSuccess)
+    return record_hip_error(e, kStageNames[5]);
+  if ((e = mark(6)) != hipSuccess) return record_hip_error(e, "event record");
+  return SFFN_OK;
+}
+
+int switch_ffn_forward(const void* x, const float* Wr, const void* W1, const void* b1,
+                       const void* W2, const void* b2, int64_t T, int64_t d, int64_t F,
+                       int64_t N, double CF, int dtype, void* y, int32_t* expert_idx,
+                       int32_t* slot, float* gate, float* aux_loss, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  return switch_ffn_forward_ex(x, Wr, W1, b1, W2, b2, T, d, F, N, CF, dtype, y, expert_idx, slot,
+                               gate, aux_loss, workspace, workspace_bytes, stream, 0u, nullptr,
+                               nullptr);
+}
+
+}  // extern "C"

@@ -1,0 +1,208 @@
+// Capacity-limited dispatch of the Switch layer and its aux loss.
+//
+// "Switch Transformers: Scaling to Trillion Parameter Models with Simple and
+// Efficient Sparsity", section 3.4, "Distributed Implementation and Expert
+// Capacity": a running count down each expert's column gives every token its
+// position in that expert's buffer; positions at or past the capacity C are
+// masked out and the token overflows, bypassing the expert on the residual
+// path.  Here the running count is an exact integer rank in flattened token
+// order: rank_t = (tokens of e_t in earlier routing blocks) + (tokens of e_t
+// earlier in t's own block).  No step depends on the order in which blocks
+// run, so slots are bitwise reproducible.
+//
+// Same section, "The Load-Balancing Auxiliary Loss": aux = N sum_i f_i P_i with
+// f_i the top-1 share before capacity and P_i the mean router probability.
+#include "sffn_device.h"
+#include "sffn_internal.h"
+#include "../../include/switch_ffn.h"
+
+namespace sffn {
+
+// ---------------------------------------------------------------------------
+// Column scan over routing blocks.  Block = 32 experts x 8 segments of routing
+// blocks.  Outputs base[b][e] (tokens of e in blocks < b), hist[e], acc[e] =
+// min(hist[e], C) and psum[e] = sum_b ppart[b][e] (float64, fixed order).
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256)
+dispatch_scan_kernel(const int* __restrict__ cnt, const float* __restrict__ ppart, int nblk,
+                     int N, int C, int* __restrict__ base, int* __restrict__ hist,
+                     int* __restrict__ acc, double* __restrict__ psum) {
+  __shared__ int part[8][32];
+  __shared__ double ppart_s[8][32];
+  const int el = threadIdx.x & 31;
+  const int seg = threadIdx.x >> 5;
+  const int e = blockIdx.x * 32 + el;
+  const int per = (nblk + 7) / 8;
+  const int c0 = min(nblk, seg * per);
+  const int c1 = min(nblk, c0 + per);
+  int s = 0;
+  double ps = 0.0;
+  if (e < N) {
+    for (int c = c0; c < c1; ++c) {
+      s += cnt[(size_t)c * N + e];
+      ps += (double)ppart[(size_t)c * N + e];
+    }
+  }
+  part[seg][el] = s;
+  ppart_s[seg][el] = ps;
+  __syncthreads();
+  if (e >= N) return;
+  int run = 0;
+  for (int q = 0; q < seg; ++q) run += part[q][el];
+  for (int c = c0; c < c1; ++c) {
+    base[(size_t)c * N + e] = run;
+    run += cnt[(size_t)c * N + e];
+  }
+  if (seg == 0) {
+    int total = 0;
+    double ptot = 0.0;
+    for (int q = 0; q < 8; ++q) {
+      total += part[q][el];
+      ptot += ppart_s[q][el];
+    }
+    hist[e] = total;
+    acc[e] = min(total, C);
+    psum[e] = ptot;
+  }
+}
+
+hipError_t launch_dispatch_scan(const Shape& s, const Workspace& ws, hipStream_t st) {
+  const dim3 grid((unsigned)((s.N + 31) / 32)), block(256);
+  hipLaunchKernelGGL(dispatch_scan_kernel, grid, block, 0, st, ws.cnt, ws.ppart,
+                     s.n_route_blocks, s.N, s.C, ws.base, ws.hist, ws.acc, ws.psum);
+  return hipGetLastError();
+}
+
+// Exclusive scan of acc[0..N) into off_s[0..N] by one 256-thread block.
+__device__ void block_offsets(const int* __restrict__ acc, int N, int* off_s, int* tsum) {
+  const int per = (N + 255) / 256;
+  const int i0 = min(N, (int)threadIdx.x * per);
+  const int i1 = min(N, i0 + per);
+  int s = 0;
+  for (int i = i0; i < i1; ++i) s += acc[i];
+  tsum[threadIdx.x] = s;
+  __syncthreads();
+  if (threadIdx.x < 64) {  // one wave scans the 256 thread sums, 4 per lane
+    const int l = threadIdx.x;
+    int v[4], run = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) { v[q] = tsum[4 * l + q]; run += v[q]; }
+    int incl = run;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int o = __shfl_up(incl, off);
+      if (l >= off) incl += o;
+    }
+    int ex = incl - run;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) { tsum[4 * l + q] = ex; ex += v[q]; }
+  }
+  __syncthreads();
+  int run = tsum[threadIdx.x];
+  for (int i = i0; i < i1; ++i) {
+    off_s[i] = run;
+    run += acc[i];
+  }
+  if (threadIdx.x == 255) off_s[N] = run;
+  __syncthreads();
+}
+
+// ---------------------------------------------------------------------------
+// Slots, the row-to-token map and the residual pass-through of dropped tokens.
+// Block b handles routing block b (kRouteTokens tokens).  Block 0 also writes
+// the expert offsets, the aux loss and the optional statistics.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256)
+dispatch_scatter_kernel(const int32_t* __restrict__ expert_idx, const int* __restrict__ base,
+                        const int* __restrict__ lrank, const int* __restrict__ hist,
+                        const int* __restrict__ acc, const double* __restrict__ psum, int T, int N,
+                        int C, int d, int esize, const void* __restrict__ x, void* __restrict__ y,
+                        int no_residual, int32_t* __restrict__ slot, int* __restrict__ row2tok,
+                        int* __restrict__ offset, float* __restrict__ aux_loss,
+                        int32_t* __restrict__ stat_count, int32_t* __restrict__ stat_accepted,
+                        int32_t* __restrict__ stat_dropped) {
+  __shared__ int off_s[SFFN_MAX_EXPERTS + 1];
+  __shared__ int tsum[256];
+  __shared__ int dropped_s[kRouteTokens];
+  __shared__ double red[256];
+
+  block_offsets(acc, N, off_s, tsum);
+
+  const int b = blockIdx.x;
+  const int tb = b * kRouteTokens;
+  if (threadIdx.x < kRouteTokens) {
+    const int t = tb + threadIdx.x;
+    int dropped = 0;
+    if (t < T) {
+      const int e = expert_idx[t];
+      const int r = base[(size_t)b * N + e] + lrank[t];
+      if (r < C) {
+        slot[t] = r;
+        row2tok[off_s[e] + r] = t;
+      } else {
+        slot[t] = -1;
+        dropped = 1;
+      }
+    }
+    dropped_s[threadIdx.x] = dropped;
+  }
+  __syncthreads();
+
+  // Dropped tokens leave the layer unchanged (or as zero in the no-residual view).
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const size_t row_bytes = (size_t)d * esize;
+  for (int j = wave; j < kRouteTokens; j += 4) {
+    if (!dropped_s[j]) continue;
+    const size_t t = (size_t)(tb + j);
+    char* dst = (char*)y + t * row_bytes;
+    const char* src = (const char*)x + t * row_bytes;
+    if (((row_bytes | (size_t)x | (size_t)y) & 15) == 0) {
+      for (size_t c = (size_t)lane * 16; c < row_bytes; c += 64 * 16)
+        store16(dst + c, no_residual ? u32x4{0, 0, 0, 0} : load16(src + c));
+    } else {
+      for (size_t c = (size_t)lane * 4; c < row_bytes; c += 64 * 4)
+        *(uint32_t*)(dst + c) = no_residual ? 0u : *(const uint32_t*)(src + c);
+    }
+  }
+
+  if (b != 0) return;
+  for (int i = threadIdx.x; i <= N; i += 256) offset[i] = off_s[i];
+  // aux = N * sum_i (hist_i / T) * (psum_i / T), summed in a fixed tree order.
+  double part = 0.0;
+  int accepted = 0;
+  for (int i = threadIdx.x; i < N; i += 256) {
+    part += (double)hist[i] * psum[i];
+    accepted += acc[i];
+    if (stat_count) stat_count[i] = hist[i];
+    if (stat_accepted) stat_accepted[i] = acc[i];
+  }
+  red[threadIdx.x] = part;
+  tsum[threadIdx.x] = accepted;
+  __syncthreads();
+  for (int w = 128; w >= 1; w >>= 1) {
+    if (threadIdx.x < w) {
+      red[threadIdx.x] += red[threadIdx.x + w];
+      tsum[threadIdx.x] += tsum[threadIdx.x + w];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const double Td = (double)T;
+    aux_loss[0] = (float)((double)N * red[0] / (Td * Td));
+    if (stat_dropped) stat_dropped[0] = T - tsum[0];
+  }
+}
+
+hipError_t launch_dispatch_scatter(const Shape& s, const Inputs& in, const Workspace& ws,
+                                   const Outputs& out, bool no_residual, hipStream_t st) {
+  const dim3 grid((unsigned)s.n_route_blocks), block(256);
+  const int esize = s.dtype == SFFN_BF16 ? 2 : 4;
+  hipLaunchKernelGGL(dispatch_scatter_kernel, grid, block, 0, st, out.expert_idx, ws.base,
+                     ws.lrank, ws.hist, ws.acc, ws.psum, s.T, s.N, s.C, s.d, esize, in.x, out.y,
+                     no_residual ? 1 : 0, out.slot, ws.row2tok, ws.offset, out.aux_loss,
+                     out.stat_count, out.stat_accepted, out.stat_dropped);
+  return hipGetLastError();
+}
+
+}  // namespace sffn

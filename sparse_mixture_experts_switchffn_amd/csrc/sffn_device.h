@@ -1,0 +1,55 @@
+// Device-side helpers shared by the SwitchFFN kernels (gfx950 / CDNA4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sffn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr int kXcds = 8;  // MI355X: 8 accelerator complex dies, blocks dealt round-robin
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) {
+  return __uint_as_float(h << 16);
+}
+
+// fp32 -> bf16 bits, round to nearest, ties to even (finite values).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// D = A(32x16) * B(16x32) + C on the matrix cores.  Lane l supplies
+// A[l%32][8*(l/32) + 0..7] and B[8*(l/32) + 0..7][l%32]; the 16 results of
+// lane l are C[8*(v/4) + 4*(l/32) + v%4][l%32], v = 0..15.
+__device__ __forceinline__ f32x16 mfma_32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Map the hardware block id to a logical tile id so that each XCD receives a
+// contiguous range of logical tiles (blocks are dealt to XCDs round-robin).
+// Tiles that share operands then share one XCD's L2.
+__device__ __forceinline__ int xcd_contiguous_tile(int bid, int nblocks) {
+  const int xcd = bid % kXcds;
+  const int local = bid / kXcds;
+  const int q = nblocks / kXcds;
+  const int r = nblocks % kXcds;
+  return (xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q) + local;
+}
+
+__device__ __forceinline__ u32x4 load16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+__device__ __forceinline__ void store16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+}  // namespace sffn

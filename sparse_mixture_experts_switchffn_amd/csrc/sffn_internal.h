@@ -1,0 +1,71 @@
+// Internal interfaces of the SwitchFFN library: workspace carve-up and the
+// kernel launchers each stage file provides.  Not part of the C-ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sffn {
+
+// Tokens per routing block: one softmax/route block handles this many tokens
+// and produces one row of per-expert probability sums and counts.
+constexpr int kRouteTokens = 64;
+
+struct Shape {
+  int T, d, F, N, C;
+  int dtype;            // SFFN_FP32 / SFFN_BF16
+  int n_route_blocks;   // ceil(T / kRouteTokens)
+  int max_rows;         // min(T, N*C): rows the expert buffers can hold
+};
+
+struct Workspace {
+  float* logits;   // [T, N] fp32 router logits
+  float* ppart;    // [n_route_blocks, N] sum of p[t,i] over a block's tokens
+  int* cnt;        // [n_route_blocks, N] top-1 counts per block
+  int* base;       // [n_route_blocks, N] tokens of expert i in earlier blocks
+  int* lrank;      // [T] rank of a token among its block's tokens of the same expert
+  int* hist;       // [N] top-1 counts (before capacity)
+  int* acc;        // [N] accepted counts min(hist, C)
+  int* offset;     // [N+1] exclusive scan of acc: start row of each expert
+  double* psum;    // [N] sum over all tokens of p[t,i]
+  int* row2tok;    // [max_rows] token of each expert-buffer row
+  void* H;         // [max_rows, F] expert hidden activations (dtype)
+};
+
+// Bytes of each region, in order, 256-byte aligned; returns the total.
+size_t workspace_layout(const Shape& s, Workspace* ws, char* base);
+
+struct Inputs {
+  const void* x;
+  const float* Wr;
+  const void* W1;
+  const void* b1;
+  const void* W2;
+  const void* b2;
+};
+
+struct Outputs {
+  void* y;
+  int32_t* expert_idx;
+  int32_t* slot;
+  float* gate;
+  float* aux_loss;
+  int32_t* stat_count;
+  int32_t* stat_accepted;
+  int32_t* stat_dropped;
+};
+
+// Stage launchers (each enqueues on `st` and returns hipGetLastError()).
+hipError_t launch_router_logits(const Shape& s, const Inputs& in, const Workspace& ws,
+                                hipStream_t st);
+hipError_t launch_softmax_route(const Shape& s, const Workspace& ws, const Outputs& out,
+                                hipStream_t st);
+hipError_t launch_dispatch_scan(const Shape& s, const Workspace& ws, hipStream_t st);
+hipError_t launch_dispatch_scatter(const Shape& s, const Inputs& in, const Workspace& ws,
+                                   const Outputs& out, bool no_residual, hipStream_t st);
+hipError_t launch_ffn1(const Shape& s, const Inputs& in, const Workspace& ws, hipStream_t st);
+hipError_t launch_ffn2(const Shape& s, const Inputs& in, const Workspace& ws, const Outputs& out,
+                       bool no_residual, hipStream_t st);
+
+}  // namespace sffn

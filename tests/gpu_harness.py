@@ -1,0 +1,126 @@
+"""Shared helpers of the GPU parity tests: run the C-ABI path, run the oracle on the
+same seeded inputs, compare by the parity rules."""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+import switchffn_synth as synth
+
+TIE_TOL = 1e-5      # top-1 / top-2 logit gap below which the routing choice is ambiguous
+GATE_TOL = 1e-6
+AUX_TOL = 1e-5
+Y_TOL = {"bf16": 2e-2, "fp32": 1e-5}
+
+
+def announce(msg: str) -> None:
+    print(f"[case] {msg}", flush=True)
+
+
+def run_gpu(w, dev_in, flags: int = 0):
+    import torch
+
+    import sparse_mixture_experts_switchffn_amd as sffn
+
+    dev = dev_in["x"].device
+    stats = {"expert_count": torch.full((w.N,), -7, dtype=torch.int32, device=dev),
+             "accepted_count": torch.full((w.N,), -7, dtype=torch.int32, device=dev),
+             "n_dropped": torch.full((1,), -7, dtype=torch.int32, device=dev)}
+    out = sffn.switch_ffn_forward(dev_in["x"], dev_in["Wr"], dev_in["W1"], dev_in["b1"],
+                                  dev_in["W2"], dev_in["b2"], w.CF, flags=flags, stats=stats)
+    torch.cuda.synchronize(dev)
+    y = out["y"]
+    if y.dtype == torch.bfloat16:
+        y_bits = y.view(torch.int16).cpu().numpy().view(np.uint16)
+        y64 = synth.bf16_bits_to_f32(y_bits).astype(np.float64)
+    else:
+        y_bits = y.view(torch.int32).cpu().numpy().view(np.uint32)
+        y64 = y_bits.view(np.float32).astype(np.float64)
+    return {
+        "expert_idx": out["expert_idx"].cpu().numpy().astype(np.int64),
+        "slot": out["slot"].cpu().numpy().astype(np.int64),
+        "gate": out["gate"].cpu().numpy().astype(np.float64),
+        "aux_loss": float(out["aux_loss"].cpu()[0]),
+        "y": y64,
+        "y_bits": y_bits,
+        "expert_count": stats["expert_count"].cpu().numpy(),
+        "accepted_count": stats["accepted_count"].cpu().numpy(),
+        "n_dropped": int(stats["n_dropped"].cpu()[0]),
+        "raw": out,
+    }
+
+
+def host_x(w):
+    return synth.host_array(w, "x").reshape(w.T, w.d)
+
+
+def oracle_ref(w, x_raw, Wr_raw, expert_idx, only_experts=None, no_residual=False,
+               experts=None):
+    """The oracle on the same inputs, replaying the GPU's routing for dispatch and y."""
+    x64 = synth.decode(x_raw)
+    Wr64 = synth.decode(Wr_raw)
+    if experts is None:
+        def experts(e):
+            ew = synth.expert_weights_host(w, e)
+            return (synth.decode(ew["W1"]), synth.decode(ew["b1"]), synth.decode(ew["W2"]),
+                    synth.decode(ew["b2"]))
+    return oracle.forward(x64, Wr64, experts, w.CF, w.dtype, no_residual=no_residual,
+                          expert_idx=expert_idx, only_experts=only_experts)
+
+
+def rel_l2(a, b):
+    nb = np.linalg.norm(b)
+    return float(np.linalg.norm(a - b) / (nb if nb > 0 else 1.0))
+
+
+def check_routing(gpu, ref):
+    """expert_idx, slot, gate, aux and stats.  Returns the near-tie count."""
+    z = ref["logits"]
+    tie = oracle.near_tie_tokens(z, TIE_TOL)
+    eg = gpu["expert_idx"]
+    bad = np.nonzero((eg != ref["router_expert_idx"]) & ~tie)[0]
+    assert bad.size == 0, f"expert_idx differs at {bad[:10]} (outside near-ties)"
+    if tie.any():
+        t = np.nonzero(tie)[0]
+        zmax = z[t].max(axis=1)
+        assert np.all(z[t, eg[t]] >= zmax - TIE_TOL), "near-tie choice not within tolerance"
+    assert np.array_equal(gpu["slot"], ref["slot"]), \
+        f"slot differs at {np.nonzero(gpu['slot'] != ref['slot'])[0][:10]}"
+    gerr = np.max(np.abs(gpu["gate"] - ref["gate"]))
+    assert gerr <= GATE_TOL, f"gate error {gerr:.3e}"
+    assert abs(gpu["aux_loss"] - ref["aux_loss"]) <= AUX_TOL, (gpu["aux_loss"], ref["aux_loss"])
+    assert np.array_equal(gpu["expert_count"], ref["hist"])
+    assert np.array_equal(gpu["accepted_count"], ref["accepted"])
+    assert gpu["n_dropped"] == int(np.sum(ref["slot"] < 0))
+    return int(tie.sum())
+
+
+def check_y(w, gpu, ref, x_bits, rows=None, no_residual=False):
+    """Dropped rows bit-exact (x, or 0 without the residual); accepted rows to tolerance."""
+    dropped = ref["slot"] < 0
+    if no_residual:
+        assert np.all(gpu["y"][dropped] == 0.0), "dropped rows not zero"
+    else:
+        xb = x_bits if x_bits.dtype != np.float32 else x_bits.view(np.uint32)
+        assert np.array_equal(gpu["y_bits"][dropped], xb[dropped]), "dropped rows differ from x"
+    acc_rows = np.nonzero(~dropped)[0] if rows is None else np.asarray(rows)
+    if acc_rows.size == 0:
+        return 0.0
+    err = rel_l2(gpu["y"][acc_rows], ref["y64"][acc_rows])
+    assert err <= Y_TOL[w.dtype], f"y rel-L2 {err:.3e} over {acc_rows.size} rows"
+    return err
+
+
+def sample_experts(ref, k: int, seed: int = 0):
+    """A few experts with accepted tokens: the first, the last, the busiest and random ones."""
+    acc = ref["accepted"]
+    live = np.nonzero(acc > 0)[0]
+    pick = {int(live[0]), int(live[-1]), int(np.argmax(acc))}
+    rng = np.random.default_rng(seed)
+    while len(pick) < min(k, live.size):
+        pick.add(int(rng.choice(live)))
+    return sorted(pick)
+
+
+def rows_of(ref, experts):
+    return np.concatenate([ref["row2tok"][ref["offset"][e]:ref["offset"][e + 1]] for e in experts])

@@ -1,0 +1,158 @@
+"""GPU parity: the HIP path (through the C-ABI) against the CPU oracle on the same
+seeded inputs.  Routing, slots and the drop mask bit-exact outside near-ties of the
+top-2 logits (gap <= 1e-5), gate within 1e-6, aux within 1e-5, y within rel-L2 2e-2
+(bf16 experts) or 1e-5 (fp32), dropped rows bit-exact."""
+import numpy as np
+import pytest
+
+import oracle
+import switchffn_synth as synth
+from gpu_harness import (announce, check_routing, check_y, host_x, oracle_ref, rows_of, run_gpu,
+                         sample_experts)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _full_case(w, mutate=None, no_residual_too=True):
+    """Small shapes: the oracle computes every row."""
+    announce(w.describe())
+    dev_in = synth.device_inputs(w, DEV)
+    x_raw = host_x(w)
+    Wr_raw = synth.host_array(w, "Wr").reshape(w.N, w.d)
+    if mutate is not None:
+        x_raw, Wr_raw = mutate(dev_in, x_raw, Wr_raw)
+    gpu = run_gpu(w, dev_in)
+    ref = oracle_ref(w, x_raw, Wr_raw, gpu["expert_idx"])
+    ties = check_routing(gpu, ref)
+    err = check_y(w, gpu, ref, x_raw)
+    out = {"ties": ties, "y_err": err, "dropped": int(np.sum(ref["slot"] < 0)), "ref": ref}
+    if no_residual_too:
+        from sparse_mixture_experts_switchffn_amd import SFFN_NO_RESIDUAL
+        gnr = run_gpu(w, dev_in, flags=SFFN_NO_RESIDUAL)
+        assert np.array_equal(gnr["slot"], gpu["slot"])
+        rnr = oracle_ref(w, x_raw, Wr_raw, gnr["expert_idx"], no_residual=True)
+        out["y_err_nr"] = check_y(w, gnr, rnr, x_raw, no_residual=True)
+    print(f"  ties={ties} dropped={out['dropped']} y_err={err:.2e} "
+          f"y_err_nr={out.get('y_err_nr', float('nan')):.2e}", flush=True)
+    return out
+
+
+def test_device_filler_matches_host_filler():
+    import torch
+    w = synth.workload("switch_base").replace(T=512, N=4, bias_sigma=0.02)
+    announce("device filler vs host filler " + w.describe())
+    dev_in = synth.device_inputs(w, DEV)
+    for name in ("x", "W1", "b1", "W2", "b2"):
+        t = dev_in[name]
+        got = t.view(torch.int16).cpu().numpy().view(np.uint16).ravel()
+        assert np.array_equal(got, synth.host_array(w, name)), name
+    wf = w.replace(dtype="fp32")
+    t = synth.device_inputs(wf, DEV)["W2"]
+    assert np.array_equal(t.cpu().numpy().ravel(), synth.host_array(wf, "W2"))
+
+
+def test_tiny_fp32():
+    r = _full_case(synth.workload("tiny"))
+    assert r["y_err"] <= 1e-6
+
+
+@pytest.mark.parametrize("case", [
+    dict(T=300, d=72, F=136, N=6, CF=1.0, bias_sigma=0.02),      # ragged T, K tail, column tail
+    dict(T=257, d=64, F=128, N=1, CF=1.0, bias_sigma=0.02),      # one expert: dense FFN, gate 1
+    dict(T=200, d=32, F=64, N=5, CF=0.0),                        # C = 0: every token dropped
+    dict(T=199, d=40, F=48, N=3, CF=3.0, bias_sigma=0.02),       # CF = N: nothing dropped
+    dict(T=1, d=16, F=24, N=3, CF=1.0),                          # a single token (C = 0)
+    dict(T=2, d=16, F=24, N=2, CF=2.0, bias_sigma=0.02),         # two tokens, C = 2
+    dict(T=2048, d=64, F=96, N=4, CF=1.0),                       # C = 512: two row chunks
+    dict(T=1000, d=128, F=256, N=130, CF=1.5),                   # N > 128: partial expert tile
+    dict(T=700, d=2080, F=64, N=7, CF=1.0),                      # d = 2080 (32 x 65) K tail
+    dict(T=640, d=256, F=512, N=16, CF=0.5, bias_sigma=0.05),    # heavy dropping
+])
+def test_bf16_edge_shapes(case):
+    w = synth.workload("switch_base").replace(**case)
+    _full_case(w)
+
+
+@pytest.mark.parametrize("case", [
+    dict(T=100, d=5, F=7, N=3, CF=1.0, bias_sigma=0.1),
+    dict(T=333, d=33, F=65, N=9, CF=1.25, bias_sigma=0.02),
+    dict(T=64, d=32, F=64, N=4, CF=0.0),
+])
+def test_fp32_edge_shapes(case):
+    w = synth.workload("tiny").replace(**case)
+    r = _full_case(w)
+    assert r["y_err"] <= 1e-5
+
+
+def test_router_zero_all_ties():
+    """Wr = 0: every logit ties at 0, all tokens go to expert 0 with gate 1/N and only the
+    first C tokens are accepted."""
+    import torch
+    w = synth.workload("switch_base").replace(T=320, d=64, F=128, N=8, CF=2.0, bias_sigma=0.02)
+
+    def mutate(dev_in, x_raw, Wr_raw):
+        dev_in["Wr"].zero_()
+        torch.cuda.synchronize()
+        return x_raw, np.zeros_like(Wr_raw)
+
+    r = _full_case(w, mutate)
+    ref = r["ref"]
+    assert np.all(ref["expert_idx"] == 0)
+    C = ref["C"]
+    assert np.array_equal(ref["slot"][:C], np.arange(C)) and np.all(ref["slot"][C:] == -1)
+
+
+def test_zero_tokens_closed_form():
+    """x = 0: all tokens tie into expert 0; accepted rows are (W2_0 ReLU(b1_0) + b2_0) / N."""
+    import torch
+    w = synth.workload("switch_base").replace(T=256, d=64, F=128, N=4, CF=1.0, bias_sigma=0.05)
+
+    def mutate(dev_in, x_raw, Wr_raw):
+        dev_in["x"].zero_()
+        torch.cuda.synchronize()
+        return np.zeros_like(x_raw), Wr_raw
+
+    _full_case(w, mutate)
+
+
+@pytest.mark.parametrize("name", ["switch_base", "skewed", "switch_large", "many_expert"])
+def test_measured_workloads(name):
+    """The full-size workloads, in the launch configuration the benchmark times: routing,
+    slots, gate, aux and the drop mask for every token; y for every dropped row (bit-exact)
+    and for all accepted rows of sampled experts."""
+    import torch
+    w = synth.workload(name)
+    announce(w.describe())
+    dev_in = synth.device_inputs(w, DEV)
+    gpu = run_gpu(w, dev_in)
+    x_raw = host_x(w)
+    Wr_raw = synth.host_array(w, "Wr").reshape(w.N, w.d)
+    C = oracle.capacity(w.T, w.N, w.CF)
+    experts = sample_experts(oracle.dispatch(gpu["expert_idx"], w.N, C), 8)
+    ref = oracle_ref(w, x_raw, Wr_raw, gpu["expert_idx"], only_experts=experts)
+    ties = check_routing(gpu, ref)
+    rows = rows_of(ref, experts)
+    err = check_y(w, gpu, ref, x_raw, rows=rows)
+    from sparse_mixture_experts_switchffn_amd import SFFN_NO_RESIDUAL
+    gnr = run_gpu(w, dev_in, flags=SFFN_NO_RESIDUAL)
+    rnr = oracle_ref(w, x_raw, Wr_raw, gnr["expert_idx"], only_experts=experts, no_residual=True)
+    err_nr = check_y(w, gnr, rnr, x_raw, rows=rows, no_residual=True)
+    hist = ref["hist"]
+    print(f"  ties={ties} dropped={int(np.sum(ref['slot'] < 0))} accepted={int(ref['offset'][-1])}"
+          f" hist[min,max]=({hist.min()},{hist.max()}) aux={gpu['aux_loss']:.6f}"
+          f" y_err={err:.2e} y_err_nr={err_nr:.2e} experts={experts}", flush=True)
+    del dev_in
+    torch.cuda.empty_cache()
+
+
+def test_deterministic():
+    w = synth.workload("switch_base")
+    announce("determinism " + w.describe())
+    dev_in = synth.device_inputs(w, DEV)
+    a = run_gpu(w, dev_in)
+    b = run_gpu(w, dev_in)
+    for k in ("expert_idx", "slot", "gate", "y_bits"):
+        assert np.array_equal(a[k], b[k]), k
+    assert a["aux_loss"] == b["aux_loss"]
