@@ -1,0 +1,237 @@
+#!/usr/bin/env python3
+"""SwitchFFN forward benchmark on one MI355X.
+
+One step = one switch_ffn_forward call over one batch of the workload (router,
+softmax/top-1, dispatch, both expert GEMMs with the combine, aux loss), with
+inputs already resident in HBM.  Prints ONE JSON line:
+  value       tokens/s over the K timed steps (HIP events around the timed region)
+  roofline    the dominant kernel's algorithmic HBM bytes per launch / its average
+              duration (per-stage HIP events recorded on the launch stream inside
+              the timed region) against the 8 TB/s HBM peak; `traffic` is the HBM
+              byte count rocprofv3 measured for that kernel (profiles/), or null
+              when the kernel source changed since it was measured
+  cpu_baseline the CPU oracle (float64 numpy) timed on this host on a bounded
+              sample of the same workload
+Default workload: Switch-Base-like (T=8192 tokens, d_model 768, d_ff 3072, 64
+experts, CF 1.25, bf16 experts, fp32 router).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+KERNEL_SOURCES = {"ffn1": "ffn.hip", "ffn2": "ffn.hip", "router_logits": "router.hip",
+                  "softmax_route": "router.hip", "dispatch_scan": "dispatch.hip",
+                  "dispatch_scatter": "dispatch.hip"}
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--config", default="switch_base",
+                   help="workload: tiny, switch_base, skewed, switch_large, many_expert")
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="CPU work budget of the oracle baseline (0 = skip)")
+    p.add_argument("--quiet", action="store_true", help="only the JSON line on stdout")
+    return p.parse_args()
+
+
+def log(args, msg):
+    if not args.quiet:
+        print(msg, file=sys.stderr, flush=True)
+
+
+def source_digest(fname: str) -> str:
+    path = os.path.join(ROOT, "sparse_mixture_experts_switchffn_amd", "csrc", fname)
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if still valid."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if "=" in line and not line.lstrip().startswith("#"):
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_sha256_16") != source_digest(KERNEL_SOURCES[kernel]):
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def algorithmic_bytes(w, stage, accepted, active, esize):
+    """Bytes a stage must move at minimum, from what it reads and writes once.
+
+    ffn1: W1 of every expert with accepted tokens + the gathered x rows + the H rows
+          written + b1 + the row-to-token map.
+    ffn2: W2 of active experts + H rows + the x rows of the residual + the y rows
+          written + b2 + gate and row-to-token entries.
+    """
+    A = accepted
+    wbytes = active * w.F * w.d * esize
+    bias1 = active * w.F * esize if w.has_bias else 0
+    bias2 = active * w.d * esize if w.has_bias else 0
+    if stage == "ffn1":
+        return wbytes + A * w.d * esize + A * w.F * esize + bias1 + A * 4
+    if stage == "ffn2":
+        return wbytes + A * w.F * esize + 2 * A * w.d * esize + bias2 + A * 8
+    if stage == "router_logits":
+        return w.T * w.d * esize + w.N * w.d * 4 + w.T * w.N * 4
+    if stage == "softmax_route":
+        nb = (w.T + 63) // 64
+        return w.T * w.N * 4 + w.T * 12 + 2 * nb * w.N * 4
+    return None
+
+
+def cpu_baseline(w, budget_s, args):
+    """The oracle as it stands on this host: full forward passes until the budget is used."""
+    import numpy as np
+
+    import oracle
+    import switchffn_synth as synth
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = int(os.environ.get("OMP_NUM_THREADS", "1"))
+    log(args, f"cpu_baseline: drawing inputs for {w.name}")
+    host = synth.host_inputs(w, max_elems=1 << 31)
+    dec = {k: synth.decode(v) for k, v in host.items()}
+    experts = (dec["W1"], dec["b1"], dec["W2"], dec["b2"])
+    passes, t0 = 0, time.perf_counter()
+    while True:
+        oracle.forward(dec["x"], dec["Wr"], experts, w.CF, w.dtype)
+        passes += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or passes >= 1000:
+            break
+    log(args, f"cpu_baseline: {passes} passes in {el:.2f} s")
+    return {"value": w.T * passes / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{passes} full forward pass(es) of the {w.name} workload "
+                      f"(T={w.T}) in float64 numpy, {el:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1",
+                          "n_gpus_requested": args.gpus}))
+        sys.stderr.write("bench.py: multi-GPU runs are not part of this build (one GPU only)\n")
+        return 2
+
+    import torch
+
+    import sparse_mixture_experts_switchffn_amd as sffn
+    import switchffn_synth as synth
+
+    w = synth.workload(args.config)
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    log(args, f"bench: {w.describe()}")
+    inp = synth.device_inputs(w, dev)
+    T, N = w.T, w.N
+    esize = 2 if w.dtype == "bf16" else 4
+    stats = {"expert_count": torch.zeros(N, dtype=torch.int32, device=dev),
+             "accepted_count": torch.zeros(N, dtype=torch.int32, device=dev),
+             "n_dropped": torch.zeros(1, dtype=torch.int32, device=dev)}
+    out = sffn.switch_ffn_forward(inp["x"], inp["Wr"], inp["W1"], inp["b1"], inp["W2"], inp["b2"],
+                                  w.CF, stats=stats)
+    bufs = {k: out[k] for k in ("y", "expert_idx", "slot", "gate", "aux_loss", "workspace")}
+    nst = sffn.switch_ffn_num_stages()
+    names = [sffn.switch_ffn_stage_name(i) for i in range(nst)]
+    stream = torch.cuda.current_stream(dev)
+
+    def step(events=None):
+        sffn.switch_ffn_forward(inp["x"], inp["Wr"], inp["W1"], inp["b1"], inp["W2"], inp["b2"],
+                                w.CF, stats=stats, stage_events=events, **bufs)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize(dev)
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nst + 1)] for _ in range(args.steps)]
+    for row in evs:  # create the underlying handles
+        for e in row:
+            e.record(stream)
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize(dev)
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for k in range(args.steps):
+        step(evs[k])
+    t_end.record(stream)
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - wall0
+    total_ms = t_start.elapsed_time(t_end)
+    ms_per_step = total_ms / args.steps
+    stage_ms = {names[i]: sum(evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(args.steps))
+                / args.steps for i in range(nst)}
+
+    acc = stats["accepted_count"].cpu()
+    accepted = int(acc.sum())
+    active = int((acc > 0).sum())
+    dropped = int(stats["n_dropped"].cpu()[0])
+    dominant = max(stage_ms, key=stage_ms.get)
+    alg = algorithmic_bytes(w, dominant, accepted, active, esize)
+    achieved = alg / (stage_ms[dominant] * 1e-3) / 1e9 if alg else None
+    gemm_flops = 4.0 * accepted * w.d * w.F
+    gemm_ms = stage_ms.get("ffn1", 0.0) + stage_ms.get("ffn2", 0.0)
+    traffic = measured_traffic(dominant, w.name)
+
+    result = {
+        "metric": "SwitchFFN fwd tokens/s",
+        "value": T / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded counter-based generator; x ~ N(0,1), W ~ N(0,0.02^2))",
+        "config": {"workload": w.name, "tokens": T, "d_model": w.d, "d_ff": w.F, "experts": N,
+                   "capacity_factor": w.CF, "capacity": sffn.switch_ffn_capacity(T, N, w.CF),
+                   "router_dtype": "fp32", "accepted_tokens": accepted, "dropped_tokens": dropped,
+                   "active_experts": active, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": dominant, "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": (achieved / HBM_PEAK_GBS) if achieved else None,
+                     "traffic": traffic, "algorithmic_bytes": alg},
+        "stages_ms": stage_ms,
+        "expert_gemm": {"tflops": gemm_flops / (gemm_ms * 1e-3) / 1e12 if gemm_ms else None,
+                        "frac_of_bf16_mfma_peak": (gemm_flops / (gemm_ms * 1e-3) / 1e12
+                                                   / MFMA_BF16_PEAK_TFLOPS) if gemm_ms else None},
+        "wall_s_timed_region": wall,
+    }
+    del inp, bufs, out
+    torch.cuda.empty_cache()
+    if args.cpu_seconds > 0 and w.name != "many_expert":
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, args)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -75,7 +75,7 @@ extern "C" {
 #define SFFN_NO_RESIDUAL 1u /* y = g*E(x) for accepted tokens and 0 for dropped ones */
 
 /* Limits of this build (SFFN_EUNSUPPORTED beyond them):
- *   N <= 4096;  T * max(N, d, F) < 2^31;
+ *   N <= 4096;  T * max(N, d, F) < 2^30;  d * F < 2^30;
  *   SFFN_BF16: d % 8 == 0, F % 8 == 0, and x, W1, W2, y 16-byte aligned. */
 #define SFFN_MAX_EXPERTS 4096
 

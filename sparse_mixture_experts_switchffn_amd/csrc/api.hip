@@ -62,7 +62,9 @@ static int make_shape(int64_t T, int64_t d, int64_t F, int64_t N, double CF, int
   if (dtype != SFFN_FP32 && dtype != SFFN_BF16) return SFFN_EDTYPE;
   if (N > SFFN_MAX_EXPERTS) return SFFN_EUNSUPPORTED;
   const int64_t widest = N > d ? (N > F ? N : F) : (d > F ? d : F);
-  if (T > ((int64_t)1 << 31) / widest - 1) return SFFN_EUNSUPPORTED;
+  // Element offsets of every tensor, and byte offsets of the bf16 ones, stay below 2^31.
+  if (T > ((int64_t)1 << 30) / widest - 1) return SFFN_EUNSUPPORTED;
+  if (d * F >= ((int64_t)1 << 30)) return SFFN_EUNSUPPORTED;
   if (dtype == SFFN_BF16 && ((d % 8) != 0 || (F % 8) != 0)) return SFFN_EUNSUPPORTED;
   const int64_t C = switch_ffn_capacity(T, N, CF);
   const int64_t Ce = C < T ? C : T;  // a rank never reaches T
@@ -107,7 +109,8 @@ const char* switch_ffn_status_string(int status) {
     case SFFN_EDTYPE: return "unknown dtype (expected SFFN_FP32 or SFFN_BF16)";
     case SFFN_EWORKSPACE: return "workspace missing or smaller than switch_ffn_workspace_bytes()";
     case SFFN_EUNSUPPORTED:
-      return "unsupported shape or alignment (N <= 4096, T*max(N,d,F) < 2^31; bf16 needs d, F "
+      return "unsupported shape or alignment (N <= 4096, T*max(N,d,F) < 2^30, d*F < 2^30; bf16 "
+             "needs d, F "
              "multiples of 8 and 16-byte aligned x, Wr, W1, W2, y; workspace 256-byte aligned)";
     case SFFN_EHIP: return g_hip_error;
     default: return "unknown status";

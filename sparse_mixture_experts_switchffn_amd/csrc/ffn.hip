@@ -19,32 +19,40 @@ namespace sffn {
 // ---------------------------------------------------------------------------
 // bf16 grouped GEMM on the matrix cores (v_mfma_f32_32x32x16_bf16).
 //
-// A block owns up to MT*32 rows of one expert and FW*32 output columns.  The
-// weights are the streamed operand: each lane loads 32 consecutive k of one
-// weight row (64 bytes) straight from HBM into registers, two k-steps ahead,
-// and every weight byte is fetched once per row chunk.  The activations are
-// the reused operand: the block gathers its rows (token rows of x for FFN1,
-// rows of H for FFN2) into LDS, 64 k per step, double-buffered, and all four
-// waves read them from there.  Within a k-step, the 64 k are permuted
-// identically on both operands (lane half h, MFMA q covers k = 32h + 8q + i),
-// which leaves the dot products unchanged.
+// A block owns up to MT*32 rows of one expert and FW*32 output columns (32 per
+// wave).  The weights are the streamed operand: every weight byte is fetched
+// once per row chunk, straight from HBM into registers, eight lanes per
+// 128-byte line (one k-step of one weight row), so each load instruction covers
+// eight whole lines.  Each wave then passes its 32 x 64 weight tile through a
+// small private LDS slot to put it in the matrix-core operand layout.  The
+// activations are the reused operand: the block gathers its rows (token rows of
+// x for FFN1, rows of H for FFN2) into LDS, 64 k per step, and all four waves
+// read them from there.  Both operands are fetched FP steps ahead into
+// registers (buffer loads: out-of-range rows and k return zero, so the loop has
+// no branches), and the activations pass through a double-buffered LDS tile one
+// step ahead of use.  Within a k-step the 64 k are permuted identically on both
+// operands (lane half h, MFMA q covers k = 32h + 8q + i), which leaves the dot
+// products unchanged.
 // ---------------------------------------------------------------------------
 constexpr int FW = 4;           // waves per block
 constexpr int FBK = 64;         // k per step
-constexpr int FLDS = FBK + 8;   // bf16 per LDS row (144 B)
+constexpr int FLDS = FBK + 8;   // bf16 per LDS row (144 B): rows start 4 banks apart
+constexpr int FP = 3;           // k-steps in flight per operand
 
 template <int MT, bool SECOND>
 __global__ void __launch_bounds__(FW * 64)
-ffn_bf16_kernel(const uint16_t* __restrict__ act, const uint16_t* __restrict__ W,
-                const uint16_t* __restrict__ bias, const int* __restrict__ offset,
-                const int* __restrict__ row2tok, const float* __restrict__ gate,
-                const uint16_t* __restrict__ xres, uint16_t* __restrict__ out, int K, int Nout,
-                int n_mchunks, int d_model, int no_residual) {
+ffn_bf16_kernel(const uint16_t* __restrict__ act, uint32_t act_bytes,
+                const uint16_t* __restrict__ W, const uint16_t* __restrict__ bias,
+                const int* __restrict__ offset, const int* __restrict__ row2tok,
+                const float* __restrict__ gate, const uint16_t* __restrict__ xres,
+                uint16_t* __restrict__ out, int K, int Nout, int n_mchunks, int d_model,
+                int no_residual) {
   constexpr int ROWS = MT * 32;
   constexpr int NTHR = FW * 64;
   constexpr int RPP = NTHR / 8;        // rows per pass of the A loader (8 chunks of 16 B a row)
   constexpr int A_LOADS = ROWS / RPP;  // == MT
   __shared__ __attribute__((aligned(16))) uint16_t As[2][ROWS * FLDS];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[FW][32 * FLDS];
   __shared__ int tok_s[ROWS];
   __shared__ float gate_s[ROWS];
 
@@ -68,95 +76,106 @@ ffn_bf16_kernel(const uint16_t* __restrict__ act, const uint16_t* __restrict__ W
     tok_s[r] = t;
     if (SECOND) gate_s[r] = t >= 0 ? gate[t] : 0.f;
   }
-  __syncthreads();
+  lds_barrier();
 
+  // Activation rows this thread stages: byte offset of (row, chunk) at k = 0.
+  const __amdgpu_buffer_rsrc_t ra_src = make_rsrc(act, act_bytes);
   const int chunk = tid & 7;
-  const uint16_t* a_src[A_LOADS];
+  uint32_t a_off[A_LOADS];
+  bool a_ok[A_LOADS];
 #pragma unroll
   for (int i = 0; i < A_LOADS; ++i) {
     const int r = (tid >> 3) + i * RPP;
-    a_src[i] = nullptr;
-    if (r < nrows)
-      a_src[i] = SECOND ? act + (size_t)(rbeg + r) * K : act + (size_t)tok_s[r] * K;
+    a_ok[i] = r < nrows;
+    const uint32_t row = a_ok[i] ? (SECOND ? (uint32_t)(rbeg + r) : (uint32_t)tok_s[r]) : 0u;
+    a_off[i] = (row * (uint32_t)K + (uint32_t)chunk * 8u) * 2u;
   }
-  const int n = nt * (FW * 32) + wave * 32 + (lane & 31);
-  const uint16_t* b_src = n < Nout ? W + ((size_t)e * Nout + n) * K + khalf * 32 : nullptr;
+  // The wave's 32 weight rows (expert e's block of Nout rows of K): load i of a
+  // step brings rows 8i + lane/8, 16-byte chunk lane%8, of the k-step.
+  const int n0 = nt * (FW * 32) + wave * 32;
+  const __amdgpu_buffer_rsrc_t rb_src =
+      make_rsrc(W + (size_t)e * Nout * K, (uint32_t)((size_t)Nout * K * 2));
+  uint32_t b_off[4];
+  bool b_ok[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int nr = n0 + i * 8 + (lane >> 3);
+    b_ok[i] = nr < Nout;
+    b_off[i] = ((uint32_t)(b_ok[i] ? nr : 0) * (uint32_t)K + (uint32_t)(lane & 7) * 8u) * 2u;
+  }
+  const int n = n0 + (lane & 31);  // output column of this lane in the MFMA result layout
 
   f32x16 acc[MT];
 #pragma unroll
   for (int m = 0; m < MT; ++m) acc[m] = f32x16{};
-  const int n_active = (nrows + 31) / 32;
-  const int nk = (K + FBK - 1) / FBK;
+  // Steps rounded up to whole pipeline rounds: the loop body is then free of
+  // branches (extra steps load zeros), which keeps the load-wait counts exact.
+  const int nk = ((K + FBK - 1) / FBK + FP - 1) / FP * FP;
 
-  u32x4 ra[A_LOADS];
-  u32x4 rb0[4], rb1[4];
-
-  auto load_a = [&](int k0) {
-    const int k = k0 + chunk * 8;
+  auto load_a = [&](u32x4 (&ra)[A_LOADS], int ks) {
+    const bool kin = ks * FBK + chunk * 8 < K;
 #pragma unroll
     for (int i = 0; i < A_LOADS; ++i)
-      ra[i] = (a_src[i] && k < K) ? load16(a_src[i] + k) : u32x4{0, 0, 0, 0};
+      ra[i] = buffer_load16(ra_src, (a_ok[i] && kin) ? a_off[i] + (uint32_t)ks * (FBK * 2) : kOob);
   };
-  auto load_b = [&](u32x4 (&rb)[4], int k0) {
+  auto load_b = [&](u32x4 (&rb)[4], int ks) {
+    const bool kin = ks * FBK + (lane & 7) * 8 < K;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int k = k0 + khalf * 32 + q * 8;
-      rb[q] = (b_src && k < K) ? load16(b_src + k0 + q * 8) : u32x4{0, 0, 0, 0};
-    }
+    for (int i = 0; i < 4; ++i)
+      rb[i] = buffer_load16(rb_src, (b_ok[i] && kin) ? b_off[i] + (uint32_t)ks * (FBK * 2) : kOob);
   };
-  auto store_a = [&](int buf) {
+  auto store_a = [&](int buf, const u32x4 (&ra)[A_LOADS]) {
 #pragma unroll
     for (int i = 0; i < A_LOADS; ++i) {
       const int r = (tid >> 3) + i * RPP;
       store16(&As[buf][r * FLDS + chunk * 8], ra[i]);
     }
   };
+  uint16_t* bslot = &Bs[wave][0];
   auto compute = [&](int buf, const u32x4 (&rb)[4]) {
+    // Weight tile into the wave's LDS slot (row-major), back out in operand layout.
+    // LDS accesses of one wave complete in order, so no barrier is needed.
+#pragma unroll
+    for (int i = 0; i < 4; ++i) store16(bslot + (i * 8 + (lane >> 3)) * FLDS + (lane & 7) * 8, rb[i]);
+    const uint16_t* base = &As[buf][(lane & 31) * FLDS + khalf * 32];
+    const uint16_t* bbase = bslot + (lane & 31) * FLDS + khalf * 32;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const bf16x8 b = as_bf16x8(rb[q]);
+      const bf16x8 b = as_bf16x8(load16(bbase + q * 8));
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
-        if (m < n_active) {
-          const bf16x8 a =
-              as_bf16x8(load16(&As[buf][(m * 32 + (lane & 31)) * FLDS + khalf * 32 + q * 8]));
-          acc[m] = mfma_32x32x16(a, b, acc[m]);
-        }
+        const bf16x8 a = as_bf16x8(load16(base + m * 32 * FLDS + q * 8));
+        acc[m] = mfma_32x32x16(a, b, acc[m]);
       }
     }
   };
 
-  load_b(rb0, 0);
-  load_a(0);
-  store_a(0);
-  if (nk > 1) {
-    load_b(rb1, FBK);
-    load_a(FBK);
+  u32x4 ra[FP][A_LOADS];
+  u32x4 rb[FP][4];
+#pragma unroll
+  for (int s = 0; s < FP; ++s) {
+    load_a(ra[s], s);
+    load_b(rb[s], s);
   }
-  __syncthreads();
-  for (int ks = 0; ks < nk; ks += 2) {
-    compute(0, rb0);
-    if (ks + 1 < nk) store_a(1);
-    if (ks + 2 < nk) {
-      load_b(rb0, (ks + 2) * FBK);
-      load_a((ks + 2) * FBK);
+  store_a(0, ra[0]);
+  lds_barrier();
+  for (int ks = 0; ks < nk; ks += FP) {
+#pragma unroll
+    for (int j = 0; j < FP; ++j) {
+      const int k = ks + j;
+      compute(k & 1, rb[j]);
+      store_a((k + 1) & 1, ra[(j + 1) % FP]);   // A(k+1), fetched FP-1 steps ago
+      load_a(ra[j], k + FP);                      // zero past the end of K
+      load_b(rb[j], k + FP);
+      lds_barrier();
     }
-    __syncthreads();
-    if (ks + 1 >= nk) break;
-    compute(1, rb1);
-    if (ks + 2 < nk) store_a(0);
-    if (ks + 3 < nk) {
-      load_b(rb1, (ks + 3) * FBK);
-      load_a((ks + 3) * FBK);
-    }
-    __syncthreads();
   }
 
   if (n >= Nout) return;
   const float bv = bias ? bf16_bits_to_f32(bias[(size_t)e * Nout + n]) : 0.f;
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
-    if (m >= n_active) continue;
+    if (m * 32 >= nrows) continue;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int r = m * 32 + (v >> 2) * 8 + khalf * 4 + (v & 3);
@@ -176,13 +195,15 @@ ffn_bf16_kernel(const uint16_t* __restrict__ act, const uint16_t* __restrict__ W
 
 template <bool SECOND>
 static void launch_ffn_bf16(int mt, dim3 grid, hipStream_t st, const uint16_t* act,
-                            const uint16_t* W, const uint16_t* bias, const int* offset,
+                            uint32_t act_bytes, const uint16_t* W, const uint16_t* bias,
+                            const int* offset,
                             const int* row2tok, const float* gate, const uint16_t* xres,
                             uint16_t* out, int K, int Nout, int n_mchunks, int d_model,
                             int no_residual) {
 #define SFFN_FFN(M)                                                                              \
-  hipLaunchKernelGGL((ffn_bf16_kernel<M, SECOND>), grid, dim3(FW * 64), 0, st, act, W, bias,     \
-                     offset, row2tok, gate, xres, out, K, Nout, n_mchunks, d_model, no_residual)
+  hipLaunchKernelGGL((ffn_bf16_kernel<M, SECOND>), grid, dim3(FW * 64), 0, st, act, act_bytes,    \
+                     W, bias, offset, row2tok, gate, xres, out, K, Nout, n_mchunks, d_model,         \
+                     no_residual)
   switch (mt) {
     case 1: SFFN_FFN(1); break;
     case 2: SFFN_FFN(2); break;
@@ -196,7 +217,13 @@ static void launch_ffn_bf16(int mt, dim3 grid, hipStream_t st, const uint16_t* a
 #undef SFFN_FFN
 }
 
-static int rows_tiles(int C) { return C <= 0 ? 1 : min(8, (C + 31) / 32); }
+// Row tiles per block: the capacity's 32-row tiles split into as few chunks of at
+// most 8 tiles as possible, evenly.
+static int rows_tiles(int C) {
+  const int tiles = C <= 0 ? 1 : (C + 31) / 32;
+  const int chunks = (tiles + 7) / 8;
+  return (tiles + chunks - 1) / chunks;
+}
 
 // ---------------------------------------------------------------------------
 // fp32 experts: one thread per output element, fp32 FMA in k order.  Used for
@@ -245,7 +272,8 @@ hipError_t launch_ffn1(const Shape& s, const Inputs& in, const Workspace& ws, hi
   const int n_mchunks = (s.C + mt * 32 - 1) / (mt * 32);
   const int n_ntiles = (s.F + FW * 32 - 1) / (FW * 32);
   const dim3 grid((unsigned)((long)n_ntiles * n_mchunks * s.N));
-  launch_ffn_bf16<false>(mt, grid, st, (const uint16_t*)in.x, (const uint16_t*)in.W1,
+  launch_ffn_bf16<false>(mt, grid, st, (const uint16_t*)in.x,
+                         (uint32_t)((size_t)s.T * s.d * 2), (const uint16_t*)in.W1,
                          (const uint16_t*)in.b1, ws.offset, ws.row2tok, nullptr, nullptr,
                          (uint16_t*)ws.H, s.d, s.F, n_mchunks, s.d, 0);
   return hipGetLastError();
@@ -265,7 +293,8 @@ hipError_t launch_ffn2(const Shape& s, const Inputs& in, const Workspace& ws, co
   const int n_mchunks = (s.C + mt * 32 - 1) / (mt * 32);
   const int n_ntiles = (s.d + FW * 32 - 1) / (FW * 32);
   const dim3 grid((unsigned)((long)n_ntiles * n_mchunks * s.N));
-  launch_ffn_bf16<true>(mt, grid, st, (const uint16_t*)ws.H, (const uint16_t*)in.W2,
+  launch_ffn_bf16<true>(mt, grid, st, (const uint16_t*)ws.H,
+                        (uint32_t)((size_t)s.max_rows * s.F * 2), (const uint16_t*)in.W2,
                         (const uint16_t*)in.b2, ws.offset, ws.row2tok, out.gate,
                         (const uint16_t*)in.x, (uint16_t*)out.y, s.F, s.d, n_mchunks, s.d,
                         no_residual ? 1 : 0);

@@ -78,7 +78,7 @@ def _call(**over):
     (dict(N=0), S.SFFN_EINVAL), (dict(CF=-1.0), S.SFFN_EINVAL), (dict(CF=math.nan), S.SFFN_EINVAL),
     (dict(flags=8), S.SFFN_EINVAL), (dict(dtype=3), S.SFFN_EDTYPE),
     (dict(N=5000), S.SFFN_EUNSUPPORTED), (dict(d=36), S.SFFN_EUNSUPPORTED),
-    (dict(F=70), S.SFFN_EUNSUPPORTED), (dict(T=1 << 26, d=64), S.SFFN_EUNSUPPORTED),
+    (dict(F=70), S.SFFN_EUNSUPPORTED), (dict(T=1 << 25, d=64), S.SFFN_EUNSUPPORTED), (dict(d=32768, F=32768), S.SFFN_EUNSUPPORTED),
     (dict(x=0x100004), S.SFFN_EUNSUPPORTED), (dict(ws=None), S.SFFN_EWORKSPACE),
     (dict(ws_bytes=1000), S.SFFN_EWORKSPACE), (dict(ws=0x100010), S.SFFN_EUNSUPPORTED),
 ])
