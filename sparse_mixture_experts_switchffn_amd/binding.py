@@ -39,31 +39,36 @@ _FWD_ARGS = [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, ctypes.c_double, ct
 _lib = None
 
 
+def load_library(path: str = LIB_PATH):
+    """ctypes handle of a libswitchffn build with argument types set."""
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: the HIP library must be built "
+                           "(__graft_entry__.build()); there is no fallback path")
+    L = ctypes.CDLL(path)
+    L.switch_ffn_capacity.restype = ctypes.c_int64
+    L.switch_ffn_capacity.argtypes = [_I64, _I64, ctypes.c_double]
+    L.switch_ffn_workspace_bytes.restype = ctypes.c_size_t
+    L.switch_ffn_workspace_bytes.argtypes = [_I64, _I64, _I64, _I64, ctypes.c_double,
+                                             ctypes.c_int]
+    L.switch_ffn_forward.restype = ctypes.c_int
+    L.switch_ffn_forward.argtypes = _FWD_ARGS
+    L.switch_ffn_forward_ex.restype = ctypes.c_int
+    L.switch_ffn_forward_ex.argtypes = _FWD_ARGS + [ctypes.c_uint32, ctypes.POINTER(sffn_stats),
+                                                    _P]
+    L.switch_ffn_num_stages.restype = ctypes.c_int
+    L.switch_ffn_num_stages.argtypes = []
+    L.switch_ffn_stage_name.restype = ctypes.c_char_p
+    L.switch_ffn_stage_name.argtypes = [ctypes.c_int]
+    L.switch_ffn_status_string.restype = ctypes.c_char_p
+    L.switch_ffn_status_string.argtypes = [ctypes.c_int]
+    return L
+
+
 def lib():
     """The loaded library (raises if it has not been built)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise RuntimeError(f"{LIB_PATH} is missing: the HIP library must be built "
-                               "(__graft_entry__.build()); there is no fallback path")
-        L = ctypes.CDLL(LIB_PATH)
-        L.switch_ffn_capacity.restype = ctypes.c_int64
-        L.switch_ffn_capacity.argtypes = [_I64, _I64, ctypes.c_double]
-        L.switch_ffn_workspace_bytes.restype = ctypes.c_size_t
-        L.switch_ffn_workspace_bytes.argtypes = [_I64, _I64, _I64, _I64, ctypes.c_double,
-                                                 ctypes.c_int]
-        L.switch_ffn_forward.restype = ctypes.c_int
-        L.switch_ffn_forward.argtypes = _FWD_ARGS
-        L.switch_ffn_forward_ex.restype = ctypes.c_int
-        L.switch_ffn_forward_ex.argtypes = _FWD_ARGS + [ctypes.c_uint32,
-                                                        ctypes.POINTER(sffn_stats), _P]
-        L.switch_ffn_num_stages.restype = ctypes.c_int
-        L.switch_ffn_num_stages.argtypes = []
-        L.switch_ffn_stage_name.restype = ctypes.c_char_p
-        L.switch_ffn_stage_name.argtypes = [ctypes.c_int]
-        L.switch_ffn_status_string.restype = ctypes.c_char_p
-        L.switch_ffn_status_string.argtypes = [ctypes.c_int]
-        _lib = L
+        _lib = load_library(LIB_PATH)
     return _lib
 
 

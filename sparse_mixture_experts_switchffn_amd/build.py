@@ -26,12 +26,15 @@ def _run(cmd):
     return out
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, out: str = LIB, build_dir: str = BUILD, defines=(),
+          csrc: str = CSRC) -> str:
+    """Compile and link the library (defines: extra -D options for tuning builds)."""
+    os.makedirs(build_dir, exist_ok=True)
     jobs = []
     for src in SOURCES:
-        obj = os.path.join(BUILD, src.replace(".hip", ".o"))
-        jobs.append(([HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj], obj))
+        obj = os.path.join(build_dir, src.replace(".hip", ".o"))
+        jobs.append(([HIPCC, *FLAGS, *[f"-D{d}" for d in defines], "-c",
+                      os.path.join(csrc, src), "-o", obj], obj))
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
         outs = list(ex.map(lambda j: _run(j[0]), jobs))
     if verbose:
@@ -39,9 +42,9 @@ def build(verbose: bool = False) -> str:
             if o.strip():
                 print(o)
     _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *[o for _, o in jobs],
-          "-o", LIB + ".tmp"])
-    os.replace(LIB + ".tmp", LIB)
-    return LIB
+          "-o", out + ".tmp"])
+    os.replace(out + ".tmp", out)
+    return out
 
 
 if __name__ == "__main__":

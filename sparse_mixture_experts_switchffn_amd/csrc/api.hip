@@ -49,6 +49,7 @@ size_t workspace_layout(const Shape& s, Workspace* ws, char* base) {
   w.psum = (double*)take(N * sizeof(double));
   w.row2tok = (int*)take((size_t)s.max_rows * sizeof(int) + 4);
   w.H = (void*)take((size_t)s.max_rows * (size_t)s.F * esize + 16);
+  w.planes = (uint16_t*)take(sffn::router_planes_bytes(s));
   if (ws) *ws = w;
   return off;
 }
@@ -159,7 +160,7 @@ int switch_ffn_forward_ex(const void* x, const float* Wr, const void* W1, const 
   if ((e = sffn::launch_router_logits(s, in, ws, st)) != hipSuccess)
     return record_hip_error(e, kStageNames[0]);
   if ((e = mark(1)) != hipSuccess) return record_hip_error(e, "event record");
-  if ((e = sffn::launch_softmax_route(s, ws, out, st)) != hipSuccess)
+  if ((e = sffn::launch_softmax_route(s, in, ws, out, st)) != hipSuccess)
     return record_hip_error(e, kStageNames[1]);
   if ((e = mark(2)) != hipSuccess) return record_hip_error(e, "event record");
   if ((e = sffn::launch_dispatch_scan(s, ws, st)) != hipSuccess)

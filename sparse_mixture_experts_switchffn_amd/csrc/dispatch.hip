@@ -19,25 +19,29 @@
 namespace sffn {
 
 // ---------------------------------------------------------------------------
-// Column scan over routing blocks.  Block = 32 experts x 8 segments of routing
-// blocks.  Outputs base[b][e] (tokens of e in blocks < b), hist[e], acc[e] =
-// min(hist[e], C) and psum[e] = sum_b ppart[b][e] (float64, fixed order).
+// Column scan over routing blocks.  Block = 32 experts x 32 segments of routing
+// blocks (1024 threads).  Outputs base[b][e] (tokens of e in blocks < b),
+// hist[e], acc[e] = min(hist[e], C) and psum[e] = sum_b ppart[b][e] (float64,
+// segment partial sums combined in segment order).
 // ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(256)
+constexpr int kScanSegs = 32;
+
+__global__ void __launch_bounds__(32 * kScanSegs)
 dispatch_scan_kernel(const int* __restrict__ cnt, const float* __restrict__ ppart, int nblk,
                      int N, int C, int* __restrict__ base, int* __restrict__ hist,
                      int* __restrict__ acc, double* __restrict__ psum) {
-  __shared__ int part[8][32];
-  __shared__ double ppart_s[8][32];
+  __shared__ int part[kScanSegs][33];
+  __shared__ double ppart_s[kScanSegs][33];
   const int el = threadIdx.x & 31;
   const int seg = threadIdx.x >> 5;
   const int e = blockIdx.x * 32 + el;
-  const int per = (nblk + 7) / 8;
+  const int per = (nblk + kScanSegs - 1) / kScanSegs;
   const int c0 = min(nblk, seg * per);
   const int c1 = min(nblk, c0 + per);
   int s = 0;
   double ps = 0.0;
   if (e < N) {
+#pragma unroll 4
     for (int c = c0; c < c1; ++c) {
       s += cnt[(size_t)c * N + e];
       ps += (double)ppart[(size_t)c * N + e];
@@ -49,14 +53,16 @@ dispatch_scan_kernel(const int* __restrict__ cnt, const float* __restrict__ ppar
   if (e >= N) return;
   int run = 0;
   for (int q = 0; q < seg; ++q) run += part[q][el];
+#pragma unroll 4
   for (int c = c0; c < c1; ++c) {
+    const int v = cnt[(size_t)c * N + e];
     base[(size_t)c * N + e] = run;
-    run += cnt[(size_t)c * N + e];
+    run += v;
   }
   if (seg == 0) {
     int total = 0;
     double ptot = 0.0;
-    for (int q = 0; q < 8; ++q) {
+    for (int q = 0; q < kScanSegs; ++q) {
       total += part[q][el];
       ptot += ppart_s[q][el];
     }
@@ -67,7 +73,7 @@ dispatch_scan_kernel(const int* __restrict__ cnt, const float* __restrict__ ppar
 }
 
 hipError_t launch_dispatch_scan(const Shape& s, const Workspace& ws, hipStream_t st) {
-  const dim3 grid((unsigned)((s.N + 31) / 32)), block(256);
+  const dim3 grid((unsigned)((s.N + 31) / 32)), block(32 * kScanSegs);
   hipLaunchKernelGGL(dispatch_scan_kernel, grid, block, 0, st, ws.cnt, ws.ppart,
                      s.n_route_blocks, s.N, s.C, ws.base, ws.hist, ws.acc, ws.psum);
   return hipGetLastError();

@@ -34,10 +34,16 @@ namespace sffn {
 // operands (lane half h, MFMA q covers k = 32h + 8q + i), which leaves the dot
 // products unchanged.
 // ---------------------------------------------------------------------------
-constexpr int FW = 4;           // waves per block
-constexpr int FBK = 64;         // k per step
-constexpr int FLDS = FBK + 8;   // bf16 per LDS row (144 B): rows start 4 banks apart
-constexpr int FP = 3;           // k-steps in flight per operand
+#ifndef SFFN_FFN_WAVES
+#define SFFN_FFN_WAVES 4
+#endif
+#ifndef SFFN_FFN_STAGES
+#define SFFN_FFN_STAGES 3
+#endif
+constexpr int FW = SFFN_FFN_WAVES;   // waves per block
+constexpr int FBK = 64;              // k per step
+constexpr int FLDS = FBK + 8;        // bf16 per LDS row (144 B): rows start 4 banks apart
+constexpr int FP = SFFN_FFN_STAGES;  // k-steps in flight per operand
 
 template <int MT, bool SECOND>
 __global__ void __launch_bounds__(FW * 64)
@@ -49,8 +55,8 @@ ffn_bf16_kernel(const uint16_t* __restrict__ act, uint32_t act_bytes,
                 int no_residual) {
   constexpr int ROWS = MT * 32;
   constexpr int NTHR = FW * 64;
-  constexpr int RPP = NTHR / 8;        // rows per pass of the A loader (8 chunks of 16 B a row)
-  constexpr int A_LOADS = ROWS / RPP;  // == MT
+  constexpr int RPP = NTHR / 8;                    // rows per pass of the A loader (8 chunks a row)
+  constexpr int A_LOADS = (ROWS + RPP - 1) / RPP;
   __shared__ __attribute__((aligned(16))) uint16_t As[2][ROWS * FLDS];
   __shared__ __attribute__((aligned(16))) uint16_t Bs[FW][32 * FLDS];
   __shared__ int tok_s[ROWS];
@@ -71,6 +77,34 @@ ffn_bf16_kernel(const uint16_t* __restrict__ act, uint32_t act_bytes,
   const int wave = tid >> 6;
   const int khalf = lane >> 5;
 
+  // The wave's 32 weight rows (expert e's block of Nout rows of K): load i of a
+  // step brings rows 8i + lane/8, 16-byte chunk lane%8, of the k-step.
+  const int n0 = nt * (FW * 32) + wave * 32;
+  const __amdgpu_buffer_rsrc_t rb_src =
+      make_rsrc(W + (size_t)e * Nout * K, (uint32_t)((size_t)Nout * K * 2));
+  uint32_t b_off[4];
+  bool b_ok[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int nr = n0 + i * 8 + (lane >> 3);
+    b_ok[i] = nr < Nout;
+    b_off[i] = ((uint32_t)(b_ok[i] ? nr : 0) * (uint32_t)K + (uint32_t)(lane & 7) * 8u) * 2u;
+  }
+  const int n = n0 + (lane & 31);  // output column of this lane in the MFMA result layout
+  auto load_b = [&](u32x4 (&rb)[4], int ks) {
+    const bool kin = ks * FBK + (lane & 7) * 8 < K;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      rb[i] = buffer_load16(rb_src, (b_ok[i] && kin) ? b_off[i] + (uint32_t)ks * (FBK * 2) : kOob);
+  };
+  // Weights do not depend on the routing: start streaming them before the row lookups.
+  u32x4 rb[FP][4];
+#pragma unroll
+  for (int s = 0; s < FP; ++s) {
+    load_b(rb[s], s);
+    __builtin_amdgcn_sched_barrier(0);  // keep the prologue in step order
+  }
+
   for (int r = tid; r < ROWS; r += NTHR) {
     const int t = r < nrows ? row2tok[rbeg + r] : -1;
     tok_s[r] = t;
@@ -90,20 +124,6 @@ ffn_bf16_kernel(const uint16_t* __restrict__ act, uint32_t act_bytes,
     const uint32_t row = a_ok[i] ? (SECOND ? (uint32_t)(rbeg + r) : (uint32_t)tok_s[r]) : 0u;
     a_off[i] = (row * (uint32_t)K + (uint32_t)chunk * 8u) * 2u;
   }
-  // The wave's 32 weight rows (expert e's block of Nout rows of K): load i of a
-  // step brings rows 8i + lane/8, 16-byte chunk lane%8, of the k-step.
-  const int n0 = nt * (FW * 32) + wave * 32;
-  const __amdgpu_buffer_rsrc_t rb_src =
-      make_rsrc(W + (size_t)e * Nout * K, (uint32_t)((size_t)Nout * K * 2));
-  uint32_t b_off[4];
-  bool b_ok[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int nr = n0 + i * 8 + (lane >> 3);
-    b_ok[i] = nr < Nout;
-    b_off[i] = ((uint32_t)(b_ok[i] ? nr : 0) * (uint32_t)K + (uint32_t)(lane & 7) * 8u) * 2u;
-  }
-  const int n = n0 + (lane & 31);  // output column of this lane in the MFMA result layout
 
   f32x16 acc[MT];
 #pragma unroll
@@ -118,17 +138,11 @@ ffn_bf16_kernel(const uint16_t* __restrict__ act, uint32_t act_bytes,
     for (int i = 0; i < A_LOADS; ++i)
       ra[i] = buffer_load16(ra_src, (a_ok[i] && kin) ? a_off[i] + (uint32_t)ks * (FBK * 2) : kOob);
   };
-  auto load_b = [&](u32x4 (&rb)[4], int ks) {
-    const bool kin = ks * FBK + (lane & 7) * 8 < K;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      rb[i] = buffer_load16(rb_src, (b_ok[i] && kin) ? b_off[i] + (uint32_t)ks * (FBK * 2) : kOob);
-  };
   auto store_a = [&](int buf, const u32x4 (&ra)[A_LOADS]) {
 #pragma unroll
     for (int i = 0; i < A_LOADS; ++i) {
       const int r = (tid >> 3) + i * RPP;
-      store16(&As[buf][r * FLDS + chunk * 8], ra[i]);
+      if (ROWS % RPP == 0 || r < ROWS) store16(&As[buf][r * FLDS + chunk * 8], ra[i]);
     }
   };
   uint16_t* bslot = &Bs[wave][0];
@@ -151,11 +165,10 @@ ffn_bf16_kernel(const uint16_t* __restrict__ act, uint32_t act_bytes,
   };
 
   u32x4 ra[FP][A_LOADS];
-  u32x4 rb[FP][4];
 #pragma unroll
   for (int s = 0; s < FP; ++s) {
     load_a(ra[s], s);
-    load_b(rb[s], s);
+    __builtin_amdgcn_sched_barrier(0);
   }
   store_a(0, ra[0]);
   lds_barrier();
@@ -171,24 +184,71 @@ ffn_bf16_kernel(const uint16_t* __restrict__ act, uint32_t act_bytes,
     }
   }
 
-  if (n >= Nout) return;
-  const float bv = bias ? bf16_bits_to_f32(bias[(size_t)e * Nout + n]) : 0.f;
+  // Epilogue: the block's result tile goes through LDS (the activation buffers
+  // are free after the loop's last barrier) and leaves in 16-byte row chunks.
+  const float bv = (bias && n < Nout) ? bf16_bits_to_f32(bias[(size_t)e * Nout + n]) : 0.f;
+  const int ccol = wave * 32 + (lane & 31);  // this lane's column within the block tile
+  if (!SECOND) {
+    // H rows: bias, ReLU, one rounding to bf16.
+    constexpr int CST = FW * 32 + 8;  // bf16 per staged row
+    static_assert(ROWS * CST <= 2 * ROWS * FLDS, "staging tile exceeds the LDS buffers");
+    uint16_t* Cs = &As[0][0];
 #pragma unroll
-  for (int m = 0; m < MT; ++m) {
-    if (m * 32 >= nrows) continue;
+    for (int m = 0; m < MT; ++m) {
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int r = m * 32 + (v >> 2) * 8 + khalf * 4 + (v & 3);
-      if (r >= nrows) continue;
-      const float val = acc[m][v] + bv;
-      if (!SECOND) {
-        out[(size_t)(rbeg + r) * Nout + n] = (uint16_t)f32_to_bf16_bits(fmaxf(val, 0.f));
-      } else {
-        const size_t o = (size_t)tok_s[r] * d_model + n;
-        float yv = gate_s[r] * val;
-        if (!no_residual) yv += bf16_bits_to_f32(xres[o]);
-        out[o] = (uint16_t)f32_to_bf16_bits(yv);
+      for (int v = 0; v < 16; ++v) {
+        const int r = m * 32 + (v >> 2) * 8 + khalf * 4 + (v & 3);
+        Cs[r * CST + ccol] = (uint16_t)f32_to_bf16_bits(fmaxf(acc[m][v] + bv, 0.f));
       }
+    }
+    lds_barrier();
+    constexpr int CPR = FW * 32 / 8;  // 16-byte chunks per staged row
+    for (int idx = tid; idx < nrows * CPR; idx += NTHR) {
+      const int r = idx / CPR, c = idx % CPR;
+      const int col = nt * (FW * 32) + c * 8;
+      if (col < Nout) store16(out + (size_t)(rbeg + r) * Nout + col, load16(&Cs[r * CST + c * 8]));
+    }
+  } else {
+    // y rows: (acc + b2) * gate + x, one rounding to bf16; fp32 staging, half the
+    // columns at a time.
+    constexpr int HALF = FW * 16;     // columns per half
+    constexpr int CST = HALF + 4;     // fp32 per staged row
+    static_assert(ROWS * CST * 4 <= 2 * ROWS * FLDS * 2, "staging tile exceeds the LDS buffers");
+    float* Cs = reinterpret_cast<float*>(&As[0][0]);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if (ccol / HALF == h) {
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int r = m * 32 + (v >> 2) * 8 + khalf * 4 + (v & 3);
+            Cs[r * CST + (ccol - h * HALF)] = acc[m][v] + bv;
+          }
+        }
+      }
+      lds_barrier();
+      constexpr int CPR = HALF / 8;
+      for (int idx = tid; idx < nrows * CPR; idx += NTHR) {
+        const int r = idx / CPR, c = idx % CPR;
+        const int col = nt * (FW * 32) + h * HALF + c * 8;
+        if (col >= Nout) continue;
+        const size_t o = (size_t)tok_s[r] * d_model + col;
+        const float g = gate_s[r];
+        const f32x4 v0 = *reinterpret_cast<const f32x4*>(&Cs[r * CST + c * 8]);
+        const f32x4 v1 = *reinterpret_cast<const f32x4*>(&Cs[r * CST + c * 8 + 4]);
+        const float val[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+        u32x4 xr = no_residual ? u32x4{0, 0, 0, 0} : load16(xres + o);
+        u32x4 yr;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float lo = g * val[2 * j] + bf16_bits_to_f32(xr[j] & 0xffffu);
+          const float hi = g * val[2 * j + 1] + bf16_bits_to_f32(xr[j] >> 16);
+          yr[j] = f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+        }
+        store16(out + o, yr);
+      }
+      lds_barrier();
     }
   }
 }

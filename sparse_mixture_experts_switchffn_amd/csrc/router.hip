@@ -174,6 +174,237 @@ router_logits_bf16_kernel(const uint16_t* __restrict__ x, const float* __restric
   }
 }
 
+// ---------------------------------------------------------------------------
+// Router planes: the exact three-way bf16 split of Wr (w = hi + mid + lo, each
+// term the round-to-nearest of what remains), written in matrix-core fragment
+// order so that a wave loads each 32x16 operand fragment as one contiguous
+// 1 KB block:  planes[ks][p][m][q][lane][8] = plane p of
+//   Wr[32 m + lane%32][32 ks + 16 (lane/32) + 8 q + 0..7],
+// zero outside [0, N) x [0, d).
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256)
+router_planes_kernel(const float* __restrict__ Wr, int d, int N, int MT, int nks,
+                     uint16_t* __restrict__ planes) {
+  const int g = blockIdx.x * 256 + threadIdx.x;   // one (ks, m, q, lane) group of 8 weights
+  const int total = nks * MT * 2 * 64;
+  if (g >= total) return;
+  const int lane = g & 63;
+  const int q = (g >> 6) & 1;
+  const int m = (g >> 7) % MT;
+  const int ks = (g >> 7) / MT;
+  const int row = 32 * m + (lane & 31);
+  const int k0 = 32 * ks + 16 * (lane >> 5) + 8 * q;
+  uint32_t hi[8], mid[8], lo[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const float w = (row < N && k0 + c < d) ? Wr[(size_t)row * d + k0 + c] : 0.f;
+    hi[c] = f32_to_bf16_bits(w);
+    const float r1 = w - bf16_bits_to_f32(hi[c]);
+    mid[c] = f32_to_bf16_bits(r1);
+    lo[c] = f32_to_bf16_bits(r1 - bf16_bits_to_f32(mid[c]));
+  }
+  auto pack = [](const uint32_t* v) {
+    return u32x4{v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16), v[6] | (v[7] << 16)};
+  };
+  const size_t frag = 64 * 8;  // bf16 per fragment
+  uint16_t* base = planes + ((((size_t)ks * 3) * MT + m) * 2 + q) * frag + (size_t)lane * 8;
+  store16(base, pack(hi));
+  store16(base + (size_t)MT * 2 * frag, pack(mid));
+  store16(base + (size_t)2 * MT * 2 * frag, pack(lo));
+}
+
+// ---------------------------------------------------------------------------
+// Router with softmax, top-1 and the per-block statistics fused into the GEMM
+// epilogue, for N <= 128 experts.  A block of four waves routes one routing
+// block of kRouteTokens (32) tokens and computes all N logits, so the logits
+// never leave the chip.  The reduction over k is split across the waves (wave w
+// takes k-steps w, w+4, ...), which spreads the token stream over four times as
+// many blocks; the four partial logit tiles are summed in LDS in wave order.
+//
+// GEMM: rows = experts (the router planes, one coalesced fragment load each,
+// L2-resident), columns = tokens (four lanes per 64-byte row segment,
+// re-laid out through a private LDS slot into the operand layout).  32 k per
+// step, operands fetched 2-3 steps ahead.
+// Epilogue (wave 0): lane l holds the logits of token l%32 for the experts of
+// its lane half; the halves meet through one cross-lane exchange:
+//   m = max z, e = lowest index with z = m, S = sum exp(z - m), gate = 1/S;
+//   ppart[b, i] = sum over the block's tokens of exp(z_i - m)/S (butterfly in a
+//   fixed order), cnt[b, i] = tokens of the block whose top-1 is i,
+//   lrank[t] = tokens of the block before t with the same top-1.
+// ---------------------------------------------------------------------------
+constexpr int FR_BK = 32;
+constexpr int FR_LD = FR_BK + 8;  // bf16 per LDS row of the token slot (80 B)
+constexpr int FR_KSPLIT = 4;      // waves per block, each a quarter of the k-steps
+static_assert(kRouteTokens == 32, "one block routes 32 tokens");
+
+template <int MT>
+__global__ void __launch_bounds__(64 * FR_KSPLIT)
+router_fused_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ planes,
+                    uint32_t planes_bytes, int T, int d, int N, int32_t* __restrict__ expert_idx,
+                    float* __restrict__ gate, float* __restrict__ ppart, int* __restrict__ cnt,
+                    int* __restrict__ lrank) {
+  __shared__ __attribute__((aligned(16))) uint16_t Xs[FR_KSPLIT][32 * FR_LD];
+  __shared__ __attribute__((aligned(16))) float Ps[FR_KSPLIT - 1][MT * 16][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int b = blockIdx.x;
+  const int t0 = b * kRouteTokens;
+  const int khalf = lane >> 5;
+
+  const __amdgpu_buffer_rsrc_t rp_src = make_rsrc(planes, planes_bytes);
+  const __amdgpu_buffer_rsrc_t rx_src = make_rsrc(x, (uint32_t)((size_t)T * d * 2));
+  uint32_t x_off[2];
+  bool x_ok[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int t = t0 + i * 16 + (lane >> 2);
+    x_ok[i] = t < T;
+    x_off[i] = ((uint32_t)(x_ok[i] ? t : 0) * (uint32_t)d + (uint32_t)(lane & 3) * 8u) * 2u;
+  }
+  constexpr int RFP = MT <= 2 ? 3 : 2;  // k-steps in flight (register budget)
+  const int nks = (d + FR_BK - 1) / FR_BK;
+  const int nmine = (nks + FR_KSPLIT - 1) / FR_KSPLIT;      // this wave's steps, padded
+  const int nk = (nmine + RFP - 1) / RFP * RFP;
+  const uint32_t step_bytes = 3u * MT * 2u * 1024u;
+
+  // Local step j of this wave is global k-step wave + 4 j.
+  auto load_a = [&](u32x4 (&ra)[3 * MT * 2], int j) {
+    const int ks = wave + FR_KSPLIT * j;
+    const bool kin = ks < nks;
+#pragma unroll
+    for (int f = 0; f < 3 * MT * 2; ++f)
+      ra[f] = buffer_load16(rp_src, kin ? (uint32_t)ks * step_bytes + (uint32_t)f * 1024u +
+                                              (uint32_t)lane * 16u : kOob);
+  };
+  auto load_x = [&](u32x4 (&rx)[2], int j) {
+    const int ks = wave + FR_KSPLIT * j;
+    const bool kin = ks * FR_BK + (lane & 3) * 8 < d;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      rx[i] = buffer_load16(rx_src, (x_ok[i] && kin) ? x_off[i] + (uint32_t)ks * (FR_BK * 2) : kOob);
+  };
+  uint16_t* xslot = &Xs[wave][0];
+  f32x16 acc[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) acc[m] = f32x16{};
+  auto compute = [&](const u32x4 (&ra)[3 * MT * 2], const u32x4 (&rx)[2]) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) store16(xslot + (i * 16 + (lane >> 2)) * FR_LD + (lane & 3) * 8, rx[i]);
+    const uint16_t* xbase = xslot + (lane & 31) * FR_LD + khalf * 16;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const bf16x8 bv = as_bf16x8(load16(xbase + q * 8));
+#pragma unroll
+      for (int p = 0; p < 3; ++p)
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+          acc[m] = mfma_32x32x16(as_bf16x8(ra[(p * MT + m) * 2 + q]), bv, acc[m]);
+    }
+  };
+
+  u32x4 ra[RFP][3 * MT * 2];
+  u32x4 rx[RFP][2];
+#pragma unroll
+  for (int st = 0; st < RFP; ++st) {
+    load_a(ra[st], st);
+    load_x(rx[st], st);
+    __builtin_amdgcn_sched_barrier(0);  // keep the prologue in step order
+  }
+  for (int js = 0; js < nk; js += RFP) {
+#pragma unroll
+    for (int j = 0; j < RFP; ++j) {
+      compute(ra[j], rx[j]);
+      load_a(ra[j], js + j + RFP);
+      load_x(rx[j], js + j + RFP);
+    }
+  }
+
+  // ---- sum of the partial logit tiles, waves in order ----
+  if (wave > 0) {
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) Ps[wave - 1][m * 16 + v][lane] = acc[m][v];
+  }
+  lds_barrier();
+  if (wave > 0) return;
+#pragma unroll
+  for (int w = 0; w < FR_KSPLIT - 1; ++w)
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[m][v] += Ps[w][m * 16 + v][lane];
+
+  // ---- softmax, top-1 and gate for token t ----
+  const int tl = lane & 31;
+  const int t = t0 + tl;
+  const bool live = t < T;
+  float mx = -INFINITY;
+  int arg = 0x7fffffff;
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int e = m * 32 + (v >> 2) * 8 + khalf * 4 + (v & 3);
+      const float z = acc[m][v];
+      if (e < N && (z > mx || (z == mx && e < arg))) {
+        mx = z;
+        arg = e;
+      }
+    }
+  }
+  {
+    const float om = __shfl_xor(mx, 32);
+    const int oa = __shfl_xor(arg, 32);
+    if (om > mx || (om == mx && oa < arg)) {
+      mx = om;
+      arg = oa;
+    }
+  }
+  float ssum = 0.f;
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int e = m * 32 + (v >> 2) * 8 + khalf * 4 + (v & 3);
+      acc[m][v] = e < N ? expf(acc[m][v] - mx) : 0.f;
+      ssum += acc[m][v];
+    }
+  }
+  ssum += __shfl_xor(ssum, 32);
+  const float inv = 1.0f / ssum;
+  if (khalf == 0 && live) {
+    expert_idx[t] = arg;
+    gate[t] = inv;
+  }
+
+  // ---- block sums of p over the 32 tokens (butterfly over lane bits 0..4) ----
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      float pv = live ? acc[m][v] * inv : 0.f;
+#pragma unroll
+      for (int off = 1; off < 32; off <<= 1) pv += __shfl_xor(pv, off);
+      const int e = m * 32 + (v >> 2) * 8 + khalf * 4 + (v & 3);
+      if (tl == 0 && e < N) ppart[(size_t)b * N + e] = pv;
+    }
+  }
+
+  // ---- top-1 counts and in-block ranks (every lane joins every shuffle) ----
+  const int my_e = live ? arg : -1;
+  int r = 0, c0 = 0, c1 = 0;
+  for (int j = 0; j < 32; ++j) {
+    const int ej = __shfl(my_e, j);
+    r += (j < tl && ej == my_e);
+    c0 += (ej == lane);
+    c1 += (ej == lane + 64);
+  }
+  if (khalf == 0 && live) lrank[t] = r;
+  if (lane < N) cnt[(size_t)b * N + lane] = c0;
+  if (lane + 64 < N) cnt[(size_t)b * N + lane + 64] = c1;
+}
+
 // Logits for fp32 token states: one thread per (token, expert), fp32 FMA in k order.
 __global__ void __launch_bounds__(256)
 router_logits_f32_kernel(const float* __restrict__ x, const float* __restrict__ Wr,
@@ -189,6 +420,8 @@ router_logits_f32_kernel(const float* __restrict__ x, const float* __restrict__ 
   logits[idx] = s;
 }
 
+bool router_is_fused(const Shape& s) { return s.dtype == SFFN_BF16 && s.N <= 128; }
+
 hipError_t launch_router_logits(const Shape& s, const Inputs& in, const Workspace& ws,
                                 hipStream_t st) {
   if (s.dtype == SFFN_FP32) {
@@ -198,6 +431,7 @@ hipError_t launch_router_logits(const Shape& s, const Inputs& in, const Workspac
                        (const float*)in.x, in.Wr, ws.logits, s.T, s.d, s.N);
     return hipGetLastError();
   }
+  if (router_is_fused(s)) return hipSuccess;  // done by launch_softmax_route
   const int ttiles = (s.T + RW_WAVES * 32 - 1) / (RW_WAVES * 32);
   const int rm = s.N >= 128 ? 4 : (s.N + 31) / 32;
   const int etiles = (s.N + rm * 32 - 1) / (rm * 32);
@@ -243,20 +477,38 @@ softmax_route_kernel(const float* __restrict__ logits, int T, int N,
 #pragma unroll
   for (int q = 0; q < NPL; ++q) acc[q] = 0.f;
 
+  // Each wave takes every 4th token of the block; up to N = 2048 the next
+  // token's logits are fetched while the current one is reduced.
+  constexpr bool kPrefetch = NPL <= 32;
+  float vn[NPL];
+  auto fetch = [&](int j, float (&v)[NPL]) {
+    const int t = tb + j;
+#pragma unroll
+    for (int q = 0; q < NPL; ++q) {
+      const int i = lane + 64 * q;
+      v[q] = (t < T && i < N) ? logits[(size_t)t * N + i] : -INFINITY;
+    }
+  };
+  if (kPrefetch) fetch(wave, vn);
   for (int j = wave; j < kRouteTokens; j += WAVES) {
     const int t = tb + j;
+    float v[NPL];
+    if (kPrefetch) {
+#pragma unroll
+      for (int q = 0; q < NPL; ++q) v[q] = vn[q];
+      if (j + WAVES < kRouteTokens) fetch(j + WAVES, vn);
+    } else {
+      fetch(j, v);
+    }
     if (t >= T) {
       if (lane == 0) eid_s[j] = -1;
       continue;
     }
-    const float* z = logits + (size_t)t * N;
-    float v[NPL];
     float m = -INFINITY;
     int arg = 0x7fffffff;
 #pragma unroll
     for (int q = 0; q < NPL; ++q) {
       const int i = lane + 64 * q;
-      v[q] = (i < N) ? z[i] : -INFINITY;
       if (i < N && (v[q] > m || (v[q] == m && i < arg))) {
         m = v[q];
         arg = i;
@@ -312,8 +564,42 @@ softmax_route_kernel(const float* __restrict__ logits, int T, int N,
   for (int i = threadIdx.x; i < N; i += 256) cnt[(size_t)b * N + i] = cnt_s[i];
 }
 
-hipError_t launch_softmax_route(const Shape& s, const Workspace& ws, const Outputs& out,
-                                hipStream_t st) {
+int router_plane_tiles(int N) { return (N + 31) / 32; }
+
+size_t router_planes_bytes(const Shape& s) {
+  if (!router_is_fused(s)) return 0;
+  const size_t nks = (size_t)(s.d + FR_BK - 1) / FR_BK;
+  return nks * 3 * (size_t)router_plane_tiles(s.N) * 2 * 1024;
+}
+
+hipError_t launch_router_fused(const Shape& s, const Inputs& in, const Workspace& ws,
+                               const Outputs& out, hipStream_t st) {
+  const int mt = router_plane_tiles(s.N);
+  const int nks = (s.d + FR_BK - 1) / FR_BK;
+  const int groups = nks * mt * 2 * 64;
+  hipLaunchKernelGGL(router_planes_kernel, dim3((unsigned)((groups + 255) / 256)), dim3(256), 0,
+                     st, in.Wr, s.d, s.N, mt, nks, ws.planes);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 grid((unsigned)s.n_route_blocks), block(256);
+  const uint16_t* x = (const uint16_t*)in.x;
+  const uint32_t pbytes = (uint32_t)router_planes_bytes(s);
+#define SFFN_FUSED(M)                                                                            \
+  hipLaunchKernelGGL(router_fused_kernel<M>, grid, block, 0, st, x, ws.planes, pbytes, s.T, s.d, \
+                     s.N, out.expert_idx, out.gate, ws.ppart, ws.cnt, ws.lrank)
+  switch (mt) {
+    case 1: SFFN_FUSED(1); break;
+    case 2: SFFN_FUSED(2); break;
+    case 3: SFFN_FUSED(3); break;
+    default: SFFN_FUSED(4); break;
+  }
+#undef SFFN_FUSED
+  return hipGetLastError();
+}
+
+hipError_t launch_softmax_route(const Shape& s, const Inputs& in, const Workspace& ws,
+                                const Outputs& out, hipStream_t st) {
+  if (router_is_fused(s)) return launch_router_fused(s, in, ws, out, st);
   const dim3 grid((unsigned)s.n_route_blocks), block(256);
   const int npl = (s.N + 63) / 64;
 #define SFFN_SOFTMAX(K)                                                                          \

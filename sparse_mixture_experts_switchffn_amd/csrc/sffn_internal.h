@@ -10,7 +10,7 @@ namespace sffn {
 
 // Tokens per routing block: one softmax/route block handles this many tokens
 // and produces one row of per-expert probability sums and counts.
-constexpr int kRouteTokens = 64;
+constexpr int kRouteTokens = 32;
 
 struct Shape {
   int T, d, F, N, C;
@@ -31,6 +31,7 @@ struct Workspace {
   double* psum;    // [N] sum over all tokens of p[t,i]
   int* row2tok;    // [max_rows] token of each expert-buffer row
   void* H;         // [max_rows, F] expert hidden activations (dtype)
+  uint16_t* planes;  // router weights split into three bf16 planes, fragment order (fused router)
 };
 
 // Bytes of each region, in order, 256-byte aligned; returns the total.
@@ -59,8 +60,12 @@ struct Outputs {
 // Stage launchers (each enqueues on `st` and returns hipGetLastError()).
 hipError_t launch_router_logits(const Shape& s, const Inputs& in, const Workspace& ws,
                                 hipStream_t st);
-hipError_t launch_softmax_route(const Shape& s, const Workspace& ws, const Outputs& out,
-                                hipStream_t st);
+// Softmax, top-1 and per-block statistics; for bf16 with N <= 128 this also
+// computes the logits (fused) and launch_router_logits does nothing.
+hipError_t launch_softmax_route(const Shape& s, const Inputs& in, const Workspace& ws,
+                                const Outputs& out, hipStream_t st);
+bool router_is_fused(const Shape& s);
+size_t router_planes_bytes(const Shape& s);
 hipError_t launch_dispatch_scan(const Shape& s, const Workspace& ws, hipStream_t st);
 hipError_t launch_dispatch_scatter(const Shape& s, const Inputs& in, const Workspace& ws,
                                    const Outputs& out, bool no_residual, hipStream_t st);
