@@ -26,26 +26,23 @@ namespace sffn {
 // eight whole lines.  Each wave then passes its 32 x 64 weight tile through a
 // small private LDS slot to put it in the matrix-core operand layout.  The
 // activations are the reused operand: the block gathers its rows (token rows of
-// x for FFN1, rows of H for FFN2) into LDS, 64 k per step, and all four waves
-// read them from there.  Both operands are fetched FP steps ahead into
-// registers (buffer loads: out-of-range rows and k return zero, so the loop has
-// no branches), and the activations pass through a double-buffered LDS tile one
-// step ahead of use.  Within a k-step the 64 k are permuted identically on both
-// operands (lane half h, MFMA q covers k = 32h + 8q + i), which leaves the dot
-// products unchanged.
+// x for FFN1, rows of H for FFN2) into LDS, 64 k per step, and all waves read
+// them from there; the activation bytes a block moves per weight byte are
+// MT*32 / (FW*32), so wider blocks (FW up to 8) move fewer.  Both operands are
+// fetched FP steps ahead into registers (buffer loads: out-of-range rows and k
+// return zero, so the loop has no branches), and the activations pass through a
+// double-buffered LDS tile one step ahead of use.  Within a k-step the 64 k are
+// permuted identically on both operands (lane half h, MFMA q covers
+// k = 32h + 8q + i), which leaves the dot products unchanged.
 // ---------------------------------------------------------------------------
-#ifndef SFFN_FFN_WAVES
-#define SFFN_FFN_WAVES 4
-#endif
 #ifndef SFFN_FFN_STAGES
 #define SFFN_FFN_STAGES 3
 #endif
-constexpr int FW = SFFN_FFN_WAVES;   // waves per block
 constexpr int FBK = 64;              // k per step
 constexpr int FLDS = FBK + 8;        // bf16 per LDS row (144 B): rows start 4 banks apart
 constexpr int FP = SFFN_FFN_STAGES;  // k-steps in flight per operand
 
-template <int MT, bool SECOND>
+template <int MT, int FW, bool SECOND>
 __global__ void __launch_bounds__(FW * 64)
 ffn_bf16_kernel(const uint16_t* __restrict__ act, uint32_t act_bytes,
                 const uint16_t* __restrict__ W, const uint16_t* __restrict__ bias,
@@ -55,10 +52,18 @@ ffn_bf16_kernel(const uint16_t* __restrict__ act, uint32_t act_bytes,
                 int no_residual) {
   constexpr int ROWS = MT * 32;
   constexpr int NTHR = FW * 64;
+  static_assert(ROWS <= NTHR, "one thread per row for the row lookups");
   constexpr int RPP = NTHR / 8;                    // rows per pass of the A loader (8 chunks a row)
   constexpr int A_LOADS = (ROWS + RPP - 1) / RPP;
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][ROWS * FLDS];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[FW][32 * FLDS];
+  // One LDS buffer: [A tiles x2 | wave weight slots] in the k-loop, the result
+  // staging tile in the epilogue.
+  constexpr int AS_ELEMS = ROWS * FLDS;
+  constexpr int LOOP_BYTES = (2 * AS_ELEMS + FW * 32 * FLDS) * 2;
+  constexpr int STAGE_BYTES = SECOND ? ROWS * (FW * 16 + 4) * 4 : ROWS * (FW * 32 + 8) * 2;
+  constexpr int SMEM_BYTES = LOOP_BYTES > STAGE_BYTES ? LOOP_BYTES : STAGE_BYTES;
+  __shared__ __attribute__((aligned(16))) char smem[SMEM_BYTES];
+  uint16_t* const As0 = reinterpret_cast<uint16_t*>(smem);
+  uint16_t* const Bs0 = As0 + 2 * AS_ELEMS;
   __shared__ int tok_s[ROWS];
   __shared__ float gate_s[ROWS];
 
@@ -97,7 +102,7 @@ ffn_bf16_kernel(const uint16_t* __restrict__ act, uint32_t act_bytes,
     for (int i = 0; i < 4; ++i)
       rb[i] = buffer_load16(rb_src, (b_ok[i] && kin) ? b_off[i] + (uint32_t)ks * (FBK * 2) : kOob);
   };
-  // Weights do not depend on the routing: start streaming them before the row lookups.
+  // Weights do not depend on the routing: start streaming them first.
   u32x4 rb[FP][4];
 #pragma unroll
   for (int s = 0; s < FP; ++s) {
@@ -105,12 +110,14 @@ ffn_bf16_kernel(const uint16_t* __restrict__ act, uint32_t act_bytes,
     __builtin_amdgcn_sched_barrier(0);  // keep the prologue in step order
   }
 
-  for (int r = tid; r < ROWS; r += NTHR) {
-    const int t = r < nrows ? row2tok[rbeg + r] : -1;
-    tok_s[r] = t;
-    if (SECOND) gate_s[r] = t >= 0 ? gate[t] : 0.f;
+  // Token of each row (one thread per row).  FFN1 needs it to find its
+  // activation rows; FFN2 only in the epilogue, so there the load stays in
+  // flight through the k-loop.
+  const int my_tok = tid < nrows ? row2tok[rbeg + tid] : -1;
+  if (!SECOND) {
+    if (tid < ROWS) tok_s[tid] = my_tok;
+    lds_barrier();
   }
-  lds_barrier();
 
   // Activation rows this thread stages: byte offset of (row, chunk) at k = 0.
   const __amdgpu_buffer_rsrc_t ra_src = make_rsrc(act, act_bytes);
@@ -142,16 +149,16 @@ ffn_bf16_kernel(const uint16_t* __restrict__ act, uint32_t act_bytes,
 #pragma unroll
     for (int i = 0; i < A_LOADS; ++i) {
       const int r = (tid >> 3) + i * RPP;
-      if (ROWS % RPP == 0 || r < ROWS) store16(&As[buf][r * FLDS + chunk * 8], ra[i]);
+      if (ROWS % RPP == 0 || r < ROWS) store16(As0 + buf * AS_ELEMS + r * FLDS + chunk * 8, ra[i]);
     }
   };
-  uint16_t* bslot = &Bs[wave][0];
+  uint16_t* bslot = Bs0 + wave * 32 * FLDS;
   auto compute = [&](int buf, const u32x4 (&rb)[4]) {
     // Weight tile into the wave's LDS slot (row-major), back out in operand layout.
     // LDS accesses of one wave complete in order, so no barrier is needed.
 #pragma unroll
     for (int i = 0; i < 4; ++i) store16(bslot + (i * 8 + (lane >> 3)) * FLDS + (lane & 7) * 8, rb[i]);
-    const uint16_t* base = &As[buf][(lane & 31) * FLDS + khalf * 32];
+    const uint16_t* base = As0 + buf * AS_ELEMS + (lane & 31) * FLDS + khalf * 32;
     const uint16_t* bbase = bslot + (lane & 31) * FLDS + khalf * 32;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -191,8 +198,7 @@ ffn_bf16_kernel(const uint16_t* __restrict__ act, uint32_t act_bytes,
   if (!SECOND) {
     // H rows: bias, ReLU, one rounding to bf16.
     constexpr int CST = FW * 32 + 8;  // bf16 per staged row
-    static_assert(ROWS * CST <= 2 * ROWS * FLDS, "staging tile exceeds the LDS buffers");
-    uint16_t* Cs = &As[0][0];
+    uint16_t* Cs = As0;
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
 #pragma unroll
@@ -210,11 +216,30 @@ ffn_bf16_kernel(const uint16_t* __restrict__ act, uint32_t act_bytes,
     }
   } else {
     // y rows: (acc + b2) * gate + x, one rounding to bf16; fp32 staging, half the
-    // columns at a time.
-    constexpr int HALF = FW * 16;     // columns per half
-    constexpr int CST = HALF + 4;     // fp32 per staged row
-    static_assert(ROWS * CST * 4 <= 2 * ROWS * FLDS * 2, "staging tile exceeds the LDS buffers");
-    float* Cs = reinterpret_cast<float*>(&As[0][0]);
+    // block's columns at a time.  The gate and residual loads go out first.
+    constexpr int HALF = FW * 16;                       // columns per half
+    constexpr int CST = HALF + 4;                       // fp32 per staged row
+    constexpr int CPR = HALF / 8;                       // 16-byte output chunks per row and half
+    constexpr int XPT = (ROWS * CPR + NTHR - 1) / NTHR; // chunks per thread and half
+    if (tid < ROWS) {
+      tok_s[tid] = my_tok;
+      gate_s[tid] = my_tok >= 0 ? gate[my_tok] : 0.f;
+    }
+    lds_barrier();
+    u32x4 xr[2][XPT];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int i = 0; i < XPT; ++i) {
+        const int idx = tid + i * NTHR;
+        const int r = idx / CPR, c = idx % CPR;
+        const int col = nt * (FW * 32) + h * HALF + c * 8;
+        xr[h][i] = u32x4{0, 0, 0, 0};
+        if (!no_residual && r < nrows && col < Nout)
+          xr[h][i] = load16(xres + (size_t)tok_s[r] * d_model + col);
+      }
+    }
+    float* Cs = reinterpret_cast<float*>(smem);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       if (ccol / HALF == h) {
@@ -228,42 +253,40 @@ ffn_bf16_kernel(const uint16_t* __restrict__ act, uint32_t act_bytes,
         }
       }
       lds_barrier();
-      constexpr int CPR = HALF / 8;
-      for (int idx = tid; idx < nrows * CPR; idx += NTHR) {
+#pragma unroll
+      for (int i = 0; i < XPT; ++i) {
+        const int idx = tid + i * NTHR;
         const int r = idx / CPR, c = idx % CPR;
         const int col = nt * (FW * 32) + h * HALF + c * 8;
-        if (col >= Nout) continue;
-        const size_t o = (size_t)tok_s[r] * d_model + col;
+        if (r >= nrows || col >= Nout) continue;
         const float g = gate_s[r];
         const f32x4 v0 = *reinterpret_cast<const f32x4*>(&Cs[r * CST + c * 8]);
         const f32x4 v1 = *reinterpret_cast<const f32x4*>(&Cs[r * CST + c * 8 + 4]);
         const float val[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-        u32x4 xr = no_residual ? u32x4{0, 0, 0, 0} : load16(xres + o);
         u32x4 yr;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float lo = g * val[2 * j] + bf16_bits_to_f32(xr[j] & 0xffffu);
-          const float hi = g * val[2 * j + 1] + bf16_bits_to_f32(xr[j] >> 16);
+          const float lo = g * val[2 * j] + bf16_bits_to_f32(xr[h][i][j] & 0xffffu);
+          const float hi = g * val[2 * j + 1] + bf16_bits_to_f32(xr[h][i][j] >> 16);
           yr[j] = f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
         }
-        store16(out + o, yr);
+        store16(out + (size_t)tok_s[r] * d_model + col, yr);
       }
       lds_barrier();
     }
   }
 }
 
-template <bool SECOND>
-static void launch_ffn_bf16(int mt, dim3 grid, hipStream_t st, const uint16_t* act,
-                            uint32_t act_bytes, const uint16_t* W, const uint16_t* bias,
-                            const int* offset,
-                            const int* row2tok, const float* gate, const uint16_t* xres,
-                            uint16_t* out, int K, int Nout, int n_mchunks, int d_model,
-                            int no_residual) {
+template <int FW, bool SECOND>
+static void launch_ffn_bf16_fw(int mt, dim3 grid, hipStream_t st, const uint16_t* act,
+                               uint32_t act_bytes, const uint16_t* W, const uint16_t* bias,
+                               const int* offset, const int* row2tok, const float* gate,
+                               const uint16_t* xres, uint16_t* out, int K, int Nout,
+                               int n_mchunks, int d_model, int no_residual) {
 #define SFFN_FFN(M)                                                                              \
-  hipLaunchKernelGGL((ffn_bf16_kernel<M, SECOND>), grid, dim3(FW * 64), 0, st, act, act_bytes,    \
-                     W, bias, offset, row2tok, gate, xres, out, K, Nout, n_mchunks, d_model,         \
-                     no_residual)
+  hipLaunchKernelGGL((ffn_bf16_kernel<M, FW, SECOND>), grid, dim3(FW * 64), 0, st, act,          \
+                     act_bytes, W, bias, offset, row2tok, gate, xres, out, K, Nout, n_mchunks,   \
+                     d_model, no_residual)
   switch (mt) {
     case 1: SFFN_FFN(1); break;
     case 2: SFFN_FFN(2); break;
@@ -318,6 +341,39 @@ ffn_f32_kernel(const float* __restrict__ act, const float* __restrict__ W,
   }
 }
 
+// Waves per block: the widest of 8, 6, 4 that still gives every CU a block
+// (row chunks of 7-8 tiles keep 4 waves: wider blocks would spill registers).
+static int pick_waves(int Nout, int mt, int n_mchunks, int N) {
+  if (mt >= 7) return 4;
+  const int fws[3] = {8, 6, 4};
+  for (int fw : fws) {
+    const long blocks = (long)((Nout + fw * 32 - 1) / (fw * 32)) * n_mchunks * N;
+    if (blocks >= 256) return fw;
+  }
+  return 4;
+}
+
+template <bool SECOND>
+static void launch_ffn_bf16(int Nout, const Shape& s, hipStream_t st, const uint16_t* act,
+                            uint32_t act_bytes, const uint16_t* W, const uint16_t* bias,
+                            const int* offset, const int* row2tok, const float* gate,
+                            const uint16_t* xres, uint16_t* out, int K, int no_residual) {
+  const int mt = rows_tiles(s.C);
+  const int n_mchunks = (s.C + mt * 32 - 1) / (mt * 32);
+  const int fw = pick_waves(Nout, mt, n_mchunks, s.N);
+  const int n_ntiles = (Nout + fw * 32 - 1) / (fw * 32);
+  const dim3 grid((unsigned)((long)n_ntiles * n_mchunks * s.N));
+  if (fw == 8)
+    launch_ffn_bf16_fw<8, SECOND>(mt, grid, st, act, act_bytes, W, bias, offset, row2tok, gate,
+                                  xres, out, K, Nout, n_mchunks, s.d, no_residual);
+  else if (fw == 6)
+    launch_ffn_bf16_fw<6, SECOND>(mt, grid, st, act, act_bytes, W, bias, offset, row2tok, gate,
+                                  xres, out, K, Nout, n_mchunks, s.d, no_residual);
+  else
+    launch_ffn_bf16_fw<4, SECOND>(mt, grid, st, act, act_bytes, W, bias, offset, row2tok, gate,
+                                  xres, out, K, Nout, n_mchunks, s.d, no_residual);
+}
+
 hipError_t launch_ffn1(const Shape& s, const Inputs& in, const Workspace& ws, hipStream_t st) {
   if (s.C <= 0) return hipSuccess;
   if (s.dtype == SFFN_FP32) {
@@ -328,14 +384,9 @@ hipError_t launch_ffn1(const Shape& s, const Inputs& in, const Workspace& ws, hi
                        0);
     return hipGetLastError();
   }
-  const int mt = rows_tiles(s.C);
-  const int n_mchunks = (s.C + mt * 32 - 1) / (mt * 32);
-  const int n_ntiles = (s.F + FW * 32 - 1) / (FW * 32);
-  const dim3 grid((unsigned)((long)n_ntiles * n_mchunks * s.N));
-  launch_ffn_bf16<false>(mt, grid, st, (const uint16_t*)in.x,
-                         (uint32_t)((size_t)s.T * s.d * 2), (const uint16_t*)in.W1,
-                         (const uint16_t*)in.b1, ws.offset, ws.row2tok, nullptr, nullptr,
-                         (uint16_t*)ws.H, s.d, s.F, n_mchunks, s.d, 0);
+  launch_ffn_bf16<false>(s.F, s, st, (const uint16_t*)in.x, (uint32_t)((size_t)s.T * s.d * 2),
+                         (const uint16_t*)in.W1, (const uint16_t*)in.b1, ws.offset, ws.row2tok,
+                         nullptr, nullptr, (uint16_t*)ws.H, s.d, 0);
   return hipGetLastError();
 }
 
@@ -349,15 +400,10 @@ hipError_t launch_ffn2(const Shape& s, const Inputs& in, const Workspace& ws, co
                        (const float*)in.x, (float*)out.y, s.F, s.d, s.d, no_residual ? 1 : 0);
     return hipGetLastError();
   }
-  const int mt = rows_tiles(s.C);
-  const int n_mchunks = (s.C + mt * 32 - 1) / (mt * 32);
-  const int n_ntiles = (s.d + FW * 32 - 1) / (FW * 32);
-  const dim3 grid((unsigned)((long)n_ntiles * n_mchunks * s.N));
-  launch_ffn_bf16<true>(mt, grid, st, (const uint16_t*)ws.H,
+  launch_ffn_bf16<true>(s.d, s, st, (const uint16_t*)ws.H,
                         (uint32_t)((size_t)s.max_rows * s.F * 2), (const uint16_t*)in.W2,
                         (const uint16_t*)in.b2, ws.offset, ws.row2tok, out.gate,
-                        (const uint16_t*)in.x, (uint16_t*)out.y, s.F, s.d, n_mchunks, s.d,
-                        no_residual ? 1 : 0);
+                        (const uint16_t*)in.x, (uint16_t*)out.y, s.F, no_residual ? 1 : 0);
   return hipGetLastError();
 }
 
