@@ -30,9 +30,11 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
-KERNEL_SOURCES = {"ffn1": "ffn.hip", "ffn2": "ffn.hip", "router_logits": "router.hip",
-                  "softmax_route": "router.hip", "dispatch_scan": "dispatch.hip",
-                  "dispatch_scatter": "dispatch.hip"}
+KERNEL_SOURCES = {"ffn1": ("ffn.hip", "sffn_device.h"), "ffn2": ("ffn.hip", "sffn_device.h"),
+                  "router_logits": ("router.hip", "sffn_device.h"),
+                  "softmax_route": ("router.hip", "sffn_device.h"),
+                  "dispatch_scan": ("dispatch.hip", "sffn_device.h"),
+                  "dispatch_scatter": ("dispatch.hip", "sffn_device.h")}
 
 
 def parse():
@@ -45,7 +47,23 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="CPU work budget of the oracle baseline (0 = skip)")
     p.add_argument("--quiet", action="store_true", help="only the JSON line on stdout")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="run only a plain device copy of 1 GiB three times (calibrates the "
+                        "rocprofv3 FETCH_SIZE / WRITE_SIZE counters) and exit")
     return p.parse_args()
+
+
+def copy_calibration():
+    """A plain copy of known size: 1 GiB read and 1 GiB written per launch."""
+    import torch
+    n = 1 << 29  # bf16 elements = 1 GiB
+    src = torch.ones(n, dtype=torch.bfloat16, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read_per_launch": n * 2,
+                      "copy_calibration_bytes_written_per_launch": n * 2, "launches": 3}))
 
 
 def log(args, msg):
@@ -53,9 +71,13 @@ def log(args, msg):
         print(msg, file=sys.stderr, flush=True)
 
 
-def source_digest(fname: str) -> str:
-    path = os.path.join(ROOT, "sparse_mixture_experts_switchffn_amd", "csrc", fname)
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+def source_digest(fnames) -> str:
+    """First 16 hex digits of the sha256 over the kernel's source files, in order."""
+    h = hashlib.sha256()
+    for fname in fnames:
+        path = os.path.join(ROOT, "sparse_mixture_experts_switchffn_amd", "csrc", fname)
+        h.update(open(path, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(kernel: str, workload: str):
@@ -131,10 +153,13 @@ def cpu_baseline(w, budget_s, args):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return 0
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1",
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; --gpus must be 1",
                           "n_gpus_requested": args.gpus}))
-        sys.stderr.write("bench.py: multi-GPU runs are not part of this build (one GPU only)\n")
+        sys.stderr.write("bench.py: multi-GPU runs are not supported (one GPU only)\n")
         return 2
 
     import torch

@@ -64,7 +64,7 @@ extern "C" {
 #define SFFN_EINVAL (-1)       /* null required pointer, T/d/F/N <= 0, CF < 0 or not finite */
 #define SFFN_EDTYPE (-2)       /* dtype is neither SFFN_FP32 nor SFFN_BF16 */
 #define SFFN_EWORKSPACE (-3)   /* workspace NULL or smaller than switch_ffn_workspace_bytes() */
-#define SFFN_EUNSUPPORTED (-4) /* shape or alignment outside this build's limits (see below) */
+#define SFFN_EUNSUPPORTED (-4) /* shape or alignment outside this library's limits (see below) */
 #define SFFN_EHIP (-5)         /* a HIP launch failed */
 
 /* Element types of x, W1, b1, W2, b2 and y. */
@@ -74,7 +74,7 @@ extern "C" {
 /* forward_ex flags. */
 #define SFFN_NO_RESIDUAL 1u /* y = g*E(x) for accepted tokens and 0 for dropped ones */
 
-/* Limits of this build (SFFN_EUNSUPPORTED beyond them):
+/* Limits of this library (SFFN_EUNSUPPORTED beyond them):
  *   N <= 4096;  T * max(N, d, F) < 2^30;  d * F < 2^30;
  *   SFFN_BF16: d % 8 == 0, F % 8 == 0, and x, W1, W2, y 16-byte aligned. */
 #define SFFN_MAX_EXPERTS 4096
