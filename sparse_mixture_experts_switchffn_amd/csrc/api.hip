@@ -48,6 +48,7 @@ size_t workspace_layout(const Shape& s, Workspace* ws, char* base) {
   w.offset = (int*)take((N + 1) * sizeof(int));
   w.psum = (double*)take(N * sizeof(double));
   w.row2tok = (int*)take((size_t)s.max_rows * sizeof(int) + 4);
+  w.rowgate = (float*)take((size_t)s.max_rows * sizeof(float) + 4);
   w.H = (void*)take((size_t)s.max_rows * (size_t)s.F * esize + 16);
   w.planes = (uint16_t*)take(sffn::router_planes_bytes(s));
   if (ws) *ws = w;

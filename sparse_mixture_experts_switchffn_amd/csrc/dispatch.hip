@@ -123,8 +123,9 @@ dispatch_scatter_kernel(const int32_t* __restrict__ expert_idx, const int* __res
                         const int* __restrict__ lrank, const int* __restrict__ hist,
                         const int* __restrict__ acc, const double* __restrict__ psum, int T, int N,
                         int C, int d, int esize, const void* __restrict__ x, void* __restrict__ y,
-                        int no_residual, int32_t* __restrict__ slot, int* __restrict__ row2tok,
-                        int* __restrict__ offset, float* __restrict__ aux_loss,
+                        int no_residual, const float* __restrict__ gate,
+                        int32_t* __restrict__ slot, int* __restrict__ row2tok,
+                        float* __restrict__ rowgate, int* __restrict__ offset, float* __restrict__ aux_loss,
                         int32_t* __restrict__ stat_count, int32_t* __restrict__ stat_accepted,
                         int32_t* __restrict__ stat_dropped) {
   __shared__ int off_s[SFFN_MAX_EXPERTS + 1];
@@ -145,6 +146,7 @@ dispatch_scatter_kernel(const int32_t* __restrict__ expert_idx, const int* __res
       if (r < C) {
         slot[t] = r;
         row2tok[off_s[e] + r] = t;
+        rowgate[off_s[e] + r] = gate[t];
       } else {
         slot[t] = -1;
         dropped = 1;
@@ -206,7 +208,8 @@ hipError_t launch_dispatch_scatter(const Shape& s, const Inputs& in, const Works
   const int esize = s.dtype == SFFN_BF16 ? 2 : 4;
   hipLaunchKernelGGL(dispatch_scatter_kernel, grid, block, 0, st, out.expert_idx, ws.base,
                      ws.lrank, ws.hist, ws.acc, ws.psum, s.T, s.N, s.C, s.d, esize, in.x, out.y,
-                     no_residual ? 1 : 0, out.slot, ws.row2tok, ws.offset, out.aux_loss,
+                     no_residual ? 1 : 0, out.gate, out.slot, ws.row2tok, ws.rowgate,
+                     ws.offset, out.aux_loss,
                      out.stat_count, out.stat_accepted, out.stat_dropped);
   return hipGetLastError();
 }

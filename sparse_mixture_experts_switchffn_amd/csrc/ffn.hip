@@ -19,285 +19,561 @@ namespace sffn {
 // ---------------------------------------------------------------------------
 // bf16 grouped GEMM on the matrix cores (v_mfma_f32_32x32x16_bf16).
 //
-// A block owns up to MT*32 rows of one expert and FW*32 output columns (32 per
-// wave).  The weights are the streamed operand: every weight byte is fetched
-// once per row chunk, straight from HBM into registers, eight lanes per
-// 128-byte line (one k-step of one weight row), so each load instruction covers
-// eight whole lines.  Each wave then passes its 32 x 64 weight tile through a
-// small private LDS slot to put it in the matrix-core operand layout.  The
-// activations are the reused operand: the block gathers its rows (token rows of
-// x for FFN1, rows of H for FFN2) into LDS, 64 k per step, and all waves read
-// them from there; the activation bytes a block moves per weight byte are
-// MT*32 / (FW*32), so wider blocks (FW up to 8) move fewer.  Both operands are
-// fetched FP steps ahead into registers (buffer loads: out-of-range rows and k
-// return zero, so the loop has no branches), and the activations pass through a
-// double-buffered LDS tile one step ahead of use.  Within a k-step the 64 k are
-// permuted identically on both operands (lane half h, MFMA q covers
+// A tile is up to MT*32 rows of one expert against FW*32 output columns (32
+// per wave), computed over k-steps of 64.
+//
+// Weights (the streamed operand) go from HBM straight into registers, eight
+// lanes per 128-byte line (one k-step of one weight row), so each load
+// instruction covers eight whole lines; each wave then passes its 32 x 64
+// weight tile through a small private LDS slot to put it in the matrix-core
+// operand layout.
+//
+// Activations (the reused operand: token rows of x for FFN1, rows of H for
+// FFN2) go from memory straight into LDS with buffer loads that write LDS
+// (one instruction moves 8 rows x 128 bytes), into a ring of FP+1 tiles; all
+// waves read them from there.  Within a row the eight 16-byte chunks are
+// stored XOR-swizzled by the row's low bits, so the matrix-core operand reads
+// (32 rows, same chunk) spread over all LDS banks.  The activation bytes a
+// block moves per weight byte are MT*32 / (FW*32).
+//
+// Both operands run FP steps ahead.  Out-of-range rows and k read as zero
+// (buffer range checks), so the k-loop has no branches.  The LDS-writing loads
+// are not tracked by the compiler's wait insertion: each step waits for them
+// explicitly with a vector-memory count derived from the fixed issue order
+// below (loads of all kinds complete in issue order on this target), then a
+// barrier makes every wave's part of the tile visible.  Within a k-step the 64
+// k are permuted identically on both operands (lane half h, MFMA q covers
 // k = 32h + 8q + i), which leaves the dot products unchanged.
+//
+// The grid is persistent: one block per resident slot, each walking the tiles
+// t = b, b + G, b + 2G, ... (b its XCD-contiguous index, G the grid size; tiles
+// ordered by expert, then row chunk, then column tile, so the blocks running at
+// one time on one XCD share an expert's activations in its L2).  The step
+// stream runs on across tiles: the last round of a tile already fetches the
+// next tile's first FP steps, and the next tile's row tokens, gates and bias
+// are fetched while the tile runs, so tile starts and epilogues hide under
+// loads in flight.
 // ---------------------------------------------------------------------------
 #ifndef SFFN_FFN_STAGES
 #define SFFN_FFN_STAGES 3
 #endif
-constexpr int FBK = 64;              // k per step
-constexpr int FLDS = FBK + 8;        // bf16 per LDS row (144 B): rows start 4 banks apart
-constexpr int FP = SFFN_FFN_STAGES;  // k-steps in flight per operand
+// Cache policy of the weight loads (gfx950 buffer-load cache bits; the
+// weights are read once per row chunk).
+#ifndef SFFN_WEIGHT_CPOL
+#define SFFN_WEIGHT_CPOL 0
+#endif
+constexpr int FBK = 64;              // k per step (one 128-byte chunk row)
+constexpr int FLDS = FBK + 8;        // bf16 per row of a weight slot (144 B: rows 4 banks apart)
+constexpr int FP = SFFN_FFN_STAGES;  // k-steps in flight
+constexpr int FNB = FP + 1;          // activation tiles in the LDS ring
+constexpr int kLdsBytes = 160 * 1024;
+
+// Kinds of pipeline round (FP steps): the first of a tile, a middle one, and
+// the last (whose loads fetch the next tile; it may also be the first).
+enum : int { kRoundFirst = 0, kRoundMid = 1, kRoundLast = 2 };
+
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding
+// (gfx9 encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt left at
+// their maxima, i.e. not waited for).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  constexpr int n = N < 0 ? 0 : (N > 63 ? 63 : N);
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int MT, int FW, bool SECOND>
+struct FfnGeom {
+  static constexpr int ROWS = MT * 32;
+  static constexpr int NTHR = FW * 64;
+  static constexpr int GROUPS = ROWS / 8;             // 8-row groups: one LDS-writing load each
+  static constexpr int AL = (GROUPS + FW - 1) / FW;   // such loads per wave and step
+  static constexpr int A_BYTES = ROWS * 128;          // one activation tile
+  static constexpr int B_BYTES = FW * 32 * FLDS * 2;  // the waves' weight slots
+  static constexpr int FREE = A_BYTES + B_BYTES;      // LDS the epilogue may use
+  static constexpr int part_bytes(int wpp) {
+    return SECOND ? ROWS * (wpp * 32 + 4) * 4 : ROWS * (wpp * 32 + 8) * 2;
+  }
+  static constexpr int pick_wpp() {
+    for (int w = FW; w > 1; --w)
+      if (FW % w == 0 && part_bytes(w) <= FREE) return w;
+    return 1;
+  }
+  // Epilogue: the result leaves through LDS in column parts of WPP waves.
+  static constexpr int WPP = pick_wpp();
+  static constexpr int NPARTS = FW / WPP;
+  static constexpr int PCOLS = WPP * 32;
+  static constexpr int CPR = PCOLS / 8;                           // 16-byte chunks per part row
+  static constexpr int CST = SECOND ? PCOLS + 4 : PCOLS + 8;      // staged elements per row
+  static constexpr int XPT = (ROWS * CPR + NTHR - 1) / NTHR;      // chunks per thread and part
+  // Vector-memory operations per thread, in issue order:
+  static constexpr int G = AL + 4;                  // per step of a first/middle round
+  static constexpr int S = NPARTS * XPT;            // epilogue stores
+  static constexpr int T1 = SECOND ? 3 : 2;         // next tile's token, bias (and gate)
+  // FFN2 holds its residual rows in registers through the epilogue; it then
+  // fetches the next tile's weights after the epilogue instead of during the
+  // last round (its activations still go out before the epilogue).
+  static constexpr bool LATE_B = SECOND;
+  static constexpr int EXTRA = SECOND ? S : 0;      // FFN2 residual loads (last round, step 0)
+  static constexpr int SMEM = FNB * A_BYTES + B_BYTES + 1024;
+  static constexpr bool fits = SMEM + ROWS * 8 <= kLdsBytes && part_bytes(1) <= FREE;
+
+  // Operations this wave issued after the activation loads of step j of a
+  // round of kind KIND, when that step starts; the step waits until no more
+  // than this many are outstanding.  Tile start: the tile's FP activation
+  // steps were the last activation loads, followed by S stores (the previous
+  // epilogue, or as many placeholder loads before the first tile), with
+  // LATE_B the FP weight steps, and the T1 lookups.
+  template <int KIND, int J>
+  static constexpr int step_wait() {
+    constexpr int start = (FP - 1 - J) * AL + S + (LATE_B ? 4 * FP : 0) + T1;
+    constexpr int extra = (LATE_B && J >= 1) ? EXTRA : 0;
+    constexpr int last_b = LATE_B ? 0 : J * 4;
+    if constexpr (KIND == kRoundFirst) return start + J * G;
+    else if constexpr (KIND == kRoundMid) return (FP - 1) * G;
+    else {
+      // A tile's final round runs one code path whether or not it is also
+      // its first (K <= FP*64): the smaller count serves both.
+      constexpr int after_mid = (FP - 1 - J) * G + extra + last_b;
+      constexpr int after_start = start + extra + last_b;
+      return after_mid < after_start ? after_mid : after_start;
+    }
+  }
+};
+
+// Rows rbeg .. rbeg+nrows-1 of expert e's buffer against column tile nt.
+struct FfnTile {
+  int e, nt, rbeg, nrows;
+};
+
+// The first non-empty tile of t, t + stride, ...; n_tiles if there is none.
+// Everything here is uniform across the block (scalar loads of the offsets).
+template <int ROWS>
+__device__ __forceinline__ int find_tile(int t, int stride, int n_tiles, int n_ntiles,
+                                         int n_mchunks, const int* __restrict__ offset,
+                                         FfnTile& d) {
+  for (; t < n_tiles; t += stride) {
+    const int nt = t % n_ntiles;
+    const int rest = t / n_ntiles;
+    const int mc = rest % n_mchunks;
+    const int e = rest / n_mchunks;
+    const int rbeg = offset[e] + mc * ROWS;
+    const int nrows = min(offset[e + 1] - rbeg, ROWS);
+    if (nrows > 0) {
+      d = FfnTile{e, nt, rbeg, nrows};
+      return t;
+    }
+  }
+  return n_tiles;
+}
+
+#define SFFN_LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
+
+// Workgroup barrier of the grouped GEMM.  An LDS fence would make the
+// compiler wait for every load still writing LDS (all FP steps in flight);
+// those are waited for explicitly instead, so this only completes the wave's
+// own LDS accesses and meets the other waves.  The memory clobber keeps the
+// compiler from moving any memory access across it.
+__device__ __forceinline__ void ffn_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 template <int MT, int FW, bool SECOND>
 __global__ void __launch_bounds__(FW * 64)
 ffn_bf16_kernel(const uint16_t* __restrict__ act, uint32_t act_bytes,
                 const uint16_t* __restrict__ W, const uint16_t* __restrict__ bias,
                 const int* __restrict__ offset, const int* __restrict__ row2tok,
-                const float* __restrict__ gate, const uint16_t* __restrict__ xres,
-                uint16_t* __restrict__ out, int K, int Nout, int n_mchunks, int d_model,
+                const float* __restrict__ rowgate, const uint16_t* __restrict__ xres,
+                uint16_t* __restrict__ out, uint32_t out_bytes, int K, int Nout,
+                int n_mchunks, int n_experts, int max_rows, int T, int d_model,
                 int no_residual) {
-  constexpr int ROWS = MT * 32;
-  constexpr int NTHR = FW * 64;
+  using Geo = FfnGeom<MT, FW, SECOND>;
+  constexpr int ROWS = Geo::ROWS, NTHR = Geo::NTHR, AL = Geo::AL, A_BYTES = Geo::A_BYTES;
+  constexpr int NPARTS = Geo::NPARTS, WPP = Geo::WPP, PCOLS = Geo::PCOLS, CPR = Geo::CPR;
+  constexpr int CST = Geo::CST, XPT = Geo::XPT;
   static_assert(ROWS <= NTHR, "one thread per row for the row lookups");
-  constexpr int RPP = NTHR / 8;                    // rows per pass of the A loader (8 chunks a row)
-  constexpr int A_LOADS = (ROWS + RPP - 1) / RPP;
-  // One LDS buffer: [A tiles x2 | wave weight slots] in the k-loop, the result
-  // staging tile in the epilogue.
-  constexpr int AS_ELEMS = ROWS * FLDS;
-  constexpr int LOOP_BYTES = (2 * AS_ELEMS + FW * 32 * FLDS) * 2;
-  constexpr int STAGE_BYTES = SECOND ? ROWS * (FW * 16 + 4) * 4 : ROWS * (FW * 32 + 8) * 2;
-  constexpr int SMEM_BYTES = LOOP_BYTES > STAGE_BYTES ? LOOP_BYTES : STAGE_BYTES;
-  __shared__ __attribute__((aligned(16))) char smem[SMEM_BYTES];
-  uint16_t* const As0 = reinterpret_cast<uint16_t*>(smem);
-  uint16_t* const Bs0 = As0 + 2 * AS_ELEMS;
+  static_assert(Geo::fits, "LDS budget");
+  // [activation ring (FNB tiles) | weight slots | 1 KB sink for idle loads].
+  // The epilogue stages its result over [ring tile FP | weight slots].
+  __shared__ __attribute__((aligned(1024))) char smem[Geo::SMEM];
   __shared__ int tok_s[ROWS];
   __shared__ float gate_s[ROWS];
+  char* const As = smem;
+  uint16_t* const Bs = reinterpret_cast<uint16_t*>(smem + FNB * A_BYTES);
+  char* const sink = smem + FNB * A_BYTES + Geo::B_BYTES;
+  char* const stage = smem + FP * A_BYTES;
 
   const int n_ntiles = (Nout + FW * 32 - 1) / (FW * 32);
-  const int tile = xcd_contiguous_tile(blockIdx.x, gridDim.x);
-  const int nt = tile % n_ntiles;
-  const int rest = tile / n_ntiles;
-  const int mc = rest % n_mchunks;
-  const int e = rest / n_mchunks;
-  const int rbeg = offset[e] + mc * ROWS;
-  const int nrows = min(offset[e + 1] - rbeg, ROWS);
-  if (nrows <= 0) return;
+  const int n_tiles = n_ntiles * n_mchunks * n_experts;
+  const int stride = gridDim.x;
+  FfnTile cur;
+  int t = find_tile<ROWS>(xcd_contiguous_tile(blockIdx.x, gridDim.x), stride, n_tiles, n_ntiles,
+                          n_mchunks, offset, cur);
+  if (t >= n_tiles) return;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int khalf = lane >> 5;
+  const int ccol = wave * 32 + (lane & 31);  // this lane's column within the tile
+  // Steps rounded up to whole pipeline rounds: the loop body is then free of
+  // branches (extra steps load zeros).
+  const int nk = ((K + FBK - 1) / FBK + FP - 1) / FP * FP;
 
-  // The wave's 32 weight rows (expert e's block of Nout rows of K): load i of a
-  // step brings rows 8i + lane/8, 16-byte chunk lane%8, of the k-step.
-  const int n0 = nt * (FW * 32) + wave * 32;
-  const __amdgpu_buffer_rsrc_t rb_src =
-      make_rsrc(W + (size_t)e * Nout * K, (uint32_t)((size_t)Nout * K * 2));
-  uint32_t b_off[4];
-  bool b_ok[4];
+  const __amdgpu_buffer_rsrc_t ra_src = make_rsrc(act, act_bytes);
+  const __amdgpu_buffer_rsrc_t tok_src = make_rsrc(row2tok, (uint32_t)max_rows * 4u);
+  const __amdgpu_buffer_rsrc_t gate_src = make_rsrc(rowgate, SECOND ? (uint32_t)max_rows * 4u : 0u);
+  const __amdgpu_buffer_rsrc_t out_src = make_rsrc(out, out_bytes);
+  const __amdgpu_buffer_rsrc_t x_src =
+      make_rsrc(xres, (SECOND && !no_residual) ? (uint32_t)T * (uint32_t)d_model * 2u : 0u);
+
+  // Per-tile lookups: row token and gate (thread r: row r) and the bias of
+  // this lane's output column.
+  auto load_tok = [&](const FfnTile& dt) -> int {
+    return (int)buffer_load4(tok_src, tid < dt.nrows ? (uint32_t)(dt.rbeg + tid) * 4u : kOob);
+  };
+  auto load_gate = [&](const FfnTile& dt) -> float {
+    return __uint_as_float(
+        buffer_load4(gate_src, tid < dt.nrows ? (uint32_t)(dt.rbeg + tid) * 4u : kOob));
+  };
+  auto load_bias = [&](const FfnTile& dt) -> uint32_t {
+    const int n = dt.nt * (FW * 32) + ccol;
+    const __amdgpu_buffer_rsrc_t src =
+        make_rsrc(bias ? bias + (size_t)dt.e * Nout : bias, bias ? (uint32_t)Nout * 2u : 0u);
+    return buffer_load2(src, (dt.nrows > 0 && n < Nout) ? (uint32_t)n * 2u : kOob);
+  };
+  // Weights: load i of a step brings rows 8i + lane/8 of the wave's 32,
+  // 16-byte chunk lane%8 of the k-step.
+  auto setup_b = [&](const FfnTile& dt, __amdgpu_buffer_rsrc_t& src, uint32_t (&off)[4]) {
+    src = make_rsrc(W + (size_t)dt.e * Nout * K, (uint32_t)((size_t)Nout * K * 2));
+    const int n0 = dt.nt * (FW * 32) + wave * 32;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int nr = n0 + i * 8 + (lane >> 3);
-    b_ok[i] = nr < Nout;
-    b_off[i] = ((uint32_t)(b_ok[i] ? nr : 0) * (uint32_t)K + (uint32_t)(lane & 7) * 8u) * 2u;
-  }
-  const int n = n0 + (lane & 31);  // output column of this lane in the MFMA result layout
-  auto load_b = [&](u32x4 (&rb)[4], int ks) {
+    for (int i = 0; i < 4; ++i) {
+      const int nr = n0 + i * 8 + (lane >> 3);
+      off[i] = (dt.nrows > 0 && nr < Nout)
+                   ? ((uint32_t)nr * (uint32_t)K + (uint32_t)(lane & 7) * 8u) * 2u : kOob;
+    }
+  };
+  auto load_b = [&](u32x4 (&rb)[4], const __amdgpu_buffer_rsrc_t& src, const uint32_t (&off)[4],
+                    int ks) {
     const bool kin = ks * FBK + (lane & 7) * 8 < K;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      rb[i] = buffer_load16(rb_src, (b_ok[i] && kin) ? b_off[i] + (uint32_t)ks * (FBK * 2) : kOob);
+      rb[i] = __builtin_amdgcn_raw_buffer_load_b128(
+          src, (int)(kin ? off[i] + (uint32_t)ks * (FBK * 2) : kOob), 0, SFFN_WEIGHT_CPOL);
   };
-  // Weights do not depend on the routing: start streaming them first.
-  u32x4 rb[FP][4];
+  // Activations: load i of a step fills row group g = wave + i*FW (rows 8g ..
+  // 8g+7); lane l writes LDS chunk l%8 of row 8g + l/8, which holds logical
+  // chunk (l%8) ^ swizzle(row).  Groups past the tile go to the sink.
+  static_assert(FW % 2 == 0, "row groups of one wave share their swizzle parity");
+  uint32_t a_off[AL];
+  const int a_c8 = (((lane & 7) ^ (lane >> 3) ^ (wave & 1)) & 7) * 8;  // 8 x logical chunk
+  auto setup_a = [&](const FfnTile& dt) {
 #pragma unroll
-  for (int s = 0; s < FP; ++s) {
-    load_b(rb[s], s);
-    __builtin_amdgcn_sched_barrier(0);  // keep the prologue in step order
-  }
-
-  // Token of each row (one thread per row).  FFN1 needs it to find its
-  // activation rows; FFN2 only in the epilogue, so there the load stays in
-  // flight through the k-loop.
-  const int my_tok = tid < nrows ? row2tok[rbeg + tid] : -1;
-  if (!SECOND) {
-    if (tid < ROWS) tok_s[tid] = my_tok;
-    lds_barrier();
-  }
-
-  // Activation rows this thread stages: byte offset of (row, chunk) at k = 0.
-  const __amdgpu_buffer_rsrc_t ra_src = make_rsrc(act, act_bytes);
-  const int chunk = tid & 7;
-  uint32_t a_off[A_LOADS];
-  bool a_ok[A_LOADS];
-#pragma unroll
-  for (int i = 0; i < A_LOADS; ++i) {
-    const int r = (tid >> 3) + i * RPP;
-    a_ok[i] = r < nrows;
-    const uint32_t row = a_ok[i] ? (SECOND ? (uint32_t)(rbeg + r) : (uint32_t)tok_s[r]) : 0u;
-    a_off[i] = (row * (uint32_t)K + (uint32_t)chunk * 8u) * 2u;
-  }
-
-  f32x16 acc[MT];
-#pragma unroll
-  for (int m = 0; m < MT; ++m) acc[m] = f32x16{};
-  // Steps rounded up to whole pipeline rounds: the loop body is then free of
-  // branches (extra steps load zeros), which keeps the load-wait counts exact.
-  const int nk = ((K + FBK - 1) / FBK + FP - 1) / FP * FP;
-
-  auto load_a = [&](u32x4 (&ra)[A_LOADS], int ks) {
-    const bool kin = ks * FBK + chunk * 8 < K;
-#pragma unroll
-    for (int i = 0; i < A_LOADS; ++i)
-      ra[i] = buffer_load16(ra_src, (a_ok[i] && kin) ? a_off[i] + (uint32_t)ks * (FBK * 2) : kOob);
-  };
-  auto store_a = [&](int buf, const u32x4 (&ra)[A_LOADS]) {
-#pragma unroll
-    for (int i = 0; i < A_LOADS; ++i) {
-      const int r = (tid >> 3) + i * RPP;
-      if (ROWS % RPP == 0 || r < ROWS) store16(As0 + buf * AS_ELEMS + r * FLDS + chunk * 8, ra[i]);
+    for (int i = 0; i < AL; ++i) {
+      const int r = (wave + i * FW) * 8 + (lane >> 3);
+      const bool ok = r < dt.nrows;
+      const uint32_t row = SECOND ? (uint32_t)(dt.rbeg + r) : (uint32_t)tok_s[ok ? r : 0];
+      a_off[i] = ok ? (row * (uint32_t)K + (uint32_t)a_c8) * 2u : kOob;
     }
   };
-  uint16_t* bslot = Bs0 + wave * 32 * FLDS;
+  auto dma_a = [&](int buf, int ks) {
+#pragma unroll
+    for (int i = 0; i < AL; ++i) {
+      const int g = wave + i * FW;
+      char* dst = g < Geo::GROUPS ? As + buf * A_BYTES + g * 1024 : sink;
+      const bool kin = ks * FBK + a_c8 < K;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          ra_src, SFFN_LDS_PTR(dst), 16, (int)(kin ? a_off[i] + (uint32_t)ks * (FBK * 2) : kOob),
+          0, 0, 0);
+    }
+  };
+  // Matrix-core operand reads of the activation tile: lane l, MFMA q reads
+  // row m*32 + l%32, logical chunk 4*khalf + q, stored at chunk
+  // (4*khalf + q) ^ swizzle; the q term only flips address bits 4-5.
+  const int rsw = (lane & 7) ^ ((lane >> 3) & 1);  // swizzle of rows with these low bits
+  const uint32_t a_rd = (uint32_t)(lane & 31) * 128u + (uint32_t)(((khalf * 4) ^ rsw) * 16);
+  f32x16 acc[MT];
+  uint16_t* bslot = Bs + wave * 32 * FLDS;
   auto compute = [&](int buf, const u32x4 (&rb)[4]) {
     // Weight tile into the wave's LDS slot (row-major), back out in operand layout.
     // LDS accesses of one wave complete in order, so no barrier is needed.
 #pragma unroll
     for (int i = 0; i < 4; ++i) store16(bslot + (i * 8 + (lane >> 3)) * FLDS + (lane & 7) * 8, rb[i]);
-    const uint16_t* base = As0 + buf * AS_ELEMS + (lane & 31) * FLDS + khalf * 32;
+    const char* abase = As + buf * A_BYTES;
     const uint16_t* bbase = bslot + (lane & 31) * FLDS + khalf * 32;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const bf16x8 b = as_bf16x8(load16(bbase + q * 8));
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
-        const bf16x8 a = as_bf16x8(load16(base + m * 32 * FLDS + q * 8));
+        const bf16x8 a = as_bf16x8(load16(abase + ((a_rd ^ (uint32_t)(q * 16)) + m * 32 * 128)));
         acc[m] = mfma_32x32x16(a, b, acc[m]);
       }
     }
   };
 
-  u32x4 ra[FP][A_LOADS];
+  // First tile: its lookups, then the weights (independent of the routing)
+  // and the activation rows (FFN1 needs the tokens for them), in the order a
+  // tile start inside the loop sees them.
+  __amdgpu_buffer_rsrc_t rb_src;
+  uint32_t b_off[4];
+  u32x4 rb[FP][4];
+  int my_tok = load_tok(cur);
+  uint32_t my_bias = load_bias(cur);
+  float my_gate = SECOND ? load_gate(cur) : 0.f;
+  setup_b(cur, rb_src, b_off);
+  auto prologue_b = [&]() {
+#pragma unroll
+    for (int s = 0; s < FP; ++s) {
+      load_b(rb[s], rb_src, b_off, s);
+      __builtin_amdgcn_sched_barrier(0);  // keep the prologue in step order
+    }
+  };
+  if (!Geo::LATE_B) prologue_b();
+  if (!SECOND) {
+    if (tid < ROWS) tok_s[tid] = my_tok;
+    ffn_barrier();
+  }
+  setup_a(cur);
 #pragma unroll
   for (int s = 0; s < FP; ++s) {
-    load_a(ra[s], s);
+    dma_a(s, s);
     __builtin_amdgcn_sched_barrier(0);
   }
-  store_a(0, ra[0]);
-  lds_barrier();
-  for (int ks = 0; ks < nk; ks += FP) {
+  // Placeholders for the epilogue stores that precede a tile start inside the
+  // loop: stores at distinct offsets past the output's range, which the
+  // range check drops.  Every tile then starts with the same sequence of
+  // outstanding operations.
 #pragma unroll
-    for (int j = 0; j < FP; ++j) {
-      const int k = ks + j;
-      compute(k & 1, rb[j]);
-      store_a((k + 1) & 1, ra[(j + 1) % FP]);   // A(k+1), fetched FP-1 steps ago
-      load_a(ra[j], k + FP);                      // zero past the end of K
-      load_b(rb[j], k + FP);
-      lds_barrier();
-    }
-  }
+  for (int i = 0; i < Geo::S; ++i) buffer_store16(out_src, kOob + 16u * (uint32_t)i, u32x4{0, 0, 0, 0});
+  __builtin_amdgcn_sched_barrier(0);
+  if (Geo::LATE_B) prologue_b();
 
-  // Epilogue: the block's result tile goes through LDS (the activation buffers
-  // are free after the loop's last barrier) and leaves in 16-byte row chunks.
-  const float bv = (bias && n < Nout) ? bf16_bits_to_f32(bias[(size_t)e * Nout + n]) : 0.f;
-  const int ccol = wave * 32 + (lane & 31);  // this lane's column within the block tile
-  if (!SECOND) {
-    // H rows: bias, ReLU, one rounding to bf16.
-    constexpr int CST = FW * 32 + 8;  // bf16 per staged row
-    uint16_t* Cs = As0;
+  for (;;) {
+    // Tile start: steps 0 .. FP-1 are in flight (weights in rb, activations
+    // into ring tiles 0 .. FP-1).  The epilogue's index arithmetic derives from
+    // an opaque copy of the thread index so that it is recomputed per tile
+    // rather than hoisted out of the tile loop, where it would hold registers.
+    int etid = tid;
+    asm volatile("" : "+v"(etid));
 #pragma unroll
-    for (int m = 0; m < MT; ++m) {
+    for (int m = 0; m < MT; ++m) acc[m] = f32x16{};
+    if (SECOND && tid < ROWS) {
+      tok_s[tid] = my_tok;  // visible after the first step's barrier
+      gate_s[tid] = my_gate;
+    }
+    // The next tile and its lookups, in flight through this tile.
+    FfnTile nxt{cur.e, cur.nt, 0, 0};
+    const int tn = find_tile<ROWS>(t + stride, stride, n_tiles, n_ntiles, n_mchunks, offset, nxt);
+    const int tok_n = load_tok(nxt);
+    const uint32_t bias_n = load_bias(nxt);
+    const float gate_n = SECOND ? load_gate(nxt) : 0.f;
+    __amdgpu_buffer_rsrc_t rb_src_n;
+    uint32_t b_off_n[4];
+
+    u32x4 xr[NPARTS][SECOND ? XPT : 1];
+    auto load_residual = [&]() {
+      if constexpr (SECOND) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int r = m * 32 + (v >> 2) * 8 + khalf * 4 + (v & 3);
-        Cs[r * CST + ccol] = (uint16_t)f32_to_bf16_bits(fmaxf(acc[m][v] + bv, 0.f));
+        for (int p = 0; p < NPARTS; ++p) {
+#pragma unroll
+          for (int i = 0; i < XPT; ++i) {
+            const int idx = etid + i * NTHR;
+            const int r = idx / CPR, c = idx % CPR;
+            const int col = cur.nt * (FW * 32) + p * PCOLS + c * 8;
+            const bool ok = r < cur.nrows && col < Nout;
+            xr[p][i] = buffer_load16(
+                x_src, ok ? ((uint32_t)tok_s[ok ? r : 0] * (uint32_t)d_model + (uint32_t)col) * 2u
+                          : kOob);
+          }
+        }
       }
-    }
-    lds_barrier();
-    constexpr int CPR = FW * 32 / 8;  // 16-byte chunks per staged row
-    for (int idx = tid; idx < nrows * CPR; idx += NTHR) {
-      const int r = idx / CPR, c = idx % CPR;
-      const int col = nt * (FW * 32) + c * 8;
-      if (col < Nout) store16(out + (size_t)(rbeg + r) * Nout + col, load16(&Cs[r * CST + c * 8]));
-    }
-  } else {
-    // y rows: (acc + b2) * gate + x, one rounding to bf16; fp32 staging, half the
-    // block's columns at a time.  The gate and residual loads go out first.
-    constexpr int HALF = FW * 16;                       // columns per half
-    constexpr int CST = HALF + 4;                       // fp32 per staged row
-    constexpr int CPR = HALF / 8;                       // 16-byte output chunks per row and half
-    constexpr int XPT = (ROWS * CPR + NTHR - 1) / NTHR; // chunks per thread and half
-    if (tid < ROWS) {
-      tok_s[tid] = my_tok;
-      gate_s[tid] = my_tok >= 0 ? gate[my_tok] : 0.f;
-    }
-    lds_barrier();
-    u32x4 xr[2][XPT];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-#pragma unroll
-      for (int i = 0; i < XPT; ++i) {
-        const int idx = tid + i * NTHR;
-        const int r = idx / CPR, c = idx % CPR;
-        const int col = nt * (FW * 32) + h * HALF + c * 8;
-        xr[h][i] = u32x4{0, 0, 0, 0};
-        if (!no_residual && r < nrows && col < Nout)
-          xr[h][i] = load16(xres + (size_t)tok_s[r] * d_model + col);
+    };
+    auto step = [&](auto kind_c, auto j_c, int ks) {
+      constexpr int KIND = decltype(kind_c)::value;
+      constexpr int J = decltype(j_c)::value;
+      const int k = ks + J;
+      wait_vmcnt<Geo::template step_wait<KIND, J>()>();  // this wave's A(k) is in LDS
+      ffn_barrier();                                      // everyone's; ring tile k-1 is free
+      compute(k % FNB, rb[J]);
+      if constexpr (KIND == kRoundFirst || KIND == kRoundMid) {
+        dma_a((k + FP) % FNB, k + FP);  // zero past the end of K
+        load_b(rb[J], rb_src, b_off, k + FP);
+      } else if constexpr (Geo::LATE_B) {
+        if (J == 0) {  // FFN2's residual rows; tok_s is visible since the first step
+          __builtin_amdgcn_sched_barrier(0);  // not into the compute above
+          load_residual();
+        }
+      } else {
+        load_b(rb[J], rb_src_n, b_off_n, J);
       }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    auto round = [&](auto kind_c, int ks) {
+      static_for<0, FP>([&](auto j_c) { step(kind_c, j_c, ks); });
+    };
+    if (nk > FP) {
+      round(std::integral_constant<int, kRoundFirst>{}, 0);
+      for (int ks = FP; ks < nk - FP; ks += FP) round(std::integral_constant<int, kRoundMid>{}, ks);
     }
-    float* Cs = reinterpret_cast<float*>(smem);
+    if (!Geo::LATE_B) setup_b(nxt, rb_src_n, b_off_n);
+    round(std::integral_constant<int, kRoundLast>{}, nk - FP);
+
+    // The next tile's activation rows (ring tiles 0 .. FP-1), once every wave
+    // is past its last read of the ring.
+    if (!SECOND && tid < ROWS) tok_s[tid] = tok_n;
+    ffn_barrier();
+    setup_a(nxt);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      if (ccol / HALF == h) {
+    for (int s = 0; s < FP; ++s) {
+      dma_a(s, s);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // Epilogue: the result goes through LDS in column parts and leaves in
+    // 16-byte row chunks.
+    const float bv = bf16_bits_to_f32(my_bias);
+#pragma unroll
+    for (int p = 0; p < NPARTS; ++p) {
+      if (wave / WPP == p) {
+        const int pc = ccol - p * PCOLS;
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
             const int r = m * 32 + (v >> 2) * 8 + khalf * 4 + (v & 3);
-            Cs[r * CST + (ccol - h * HALF)] = acc[m][v] + bv;
+            if (SECOND)
+              reinterpret_cast<float*>(stage)[r * CST + pc] = acc[m][v] + bv;
+            else  // H: bias, ReLU, one rounding to bf16
+              reinterpret_cast<uint16_t*>(stage)[r * CST + pc] =
+                  (uint16_t)f32_to_bf16_bits(fmaxf(acc[m][v] + bv, 0.f));
           }
         }
       }
-      lds_barrier();
+      ffn_barrier();
 #pragma unroll
       for (int i = 0; i < XPT; ++i) {
-        const int idx = tid + i * NTHR;
+        const int idx = etid + i * NTHR;
         const int r = idx / CPR, c = idx % CPR;
-        const int col = nt * (FW * 32) + h * HALF + c * 8;
-        if (r >= nrows || col >= Nout) continue;
-        const float g = gate_s[r];
-        const f32x4 v0 = *reinterpret_cast<const f32x4*>(&Cs[r * CST + c * 8]);
-        const f32x4 v1 = *reinterpret_cast<const f32x4*>(&Cs[r * CST + c * 8 + 4]);
-        const float val[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-        u32x4 yr;
+        const int col = cur.nt * (FW * 32) + p * PCOLS + c * 8;
+        const bool ok = r < cur.nrows && col < Nout;
+        const int rr = ok ? r : 0;
+        if (!SECOND) {
+          const u32x4 v = load16(reinterpret_cast<const uint16_t*>(stage) + rr * CST + c * 8);
+          buffer_store16(out_src,
+                         ok ? ((uint32_t)(cur.rbeg + r) * (uint32_t)Nout + (uint32_t)col) * 2u : kOob, v);
+        } else {
+          // y = (acc + b2) * gate + x, one rounding to bf16.
+          const float* srow = reinterpret_cast<const float*>(stage) + rr * CST + c * 8;
+          const f32x4 v0 = *reinterpret_cast<const f32x4*>(srow);
+          const f32x4 v1 = *reinterpret_cast<const f32x4*>(srow + 4);
+          const float val[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+          const float g = gate_s[rr];
+          u32x4 yr;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float lo = g * val[2 * j] + bf16_bits_to_f32(xr[h][i][j] & 0xffffu);
-          const float hi = g * val[2 * j + 1] + bf16_bits_to_f32(xr[h][i][j] >> 16);
-          yr[j] = f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+          for (int j = 0; j < 4; ++j) {
+            const float lo = g * val[2 * j] + bf16_bits_to_f32(xr[p][i][j] & 0xffffu);
+            const float hi = g * val[2 * j + 1] + bf16_bits_to_f32(xr[p][i][j] >> 16);
+            yr[j] = f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+          }
+          buffer_store16(out_src,
+                         ok ? ((uint32_t)tok_s[rr] * (uint32_t)d_model + (uint32_t)col) * 2u : kOob, yr);
         }
-        store16(out + (size_t)tok_s[r] * d_model + col, yr);
       }
-      lds_barrier();
+      ffn_barrier();
     }
+
+    if (tn >= n_tiles) break;
+    if (Geo::LATE_B) {
+      setup_b(nxt, rb_src_n, b_off_n);
+#pragma unroll
+      for (int s = 0; s < FP; ++s) {
+        load_b(rb[s], rb_src_n, b_off_n, s);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    cur = nxt;
+    t = tn;
+    my_tok = tok_n;
+    my_bias = bias_n;
+    my_gate = gate_n;
+    rb_src = rb_src_n;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) b_off[i] = b_off_n[i];
+  }
+  // The last activation loads (range-checked to nothing) still write LDS:
+  // let them land before the block's LDS is released.
+  wait_vmcnt<0>();
+}
+
+#undef SFFN_LDS_PTR
+
+template <int MT, int FW, bool SECOND>
+static int ffn_resident_blocks() {
+  // Blocks of this kernel the device holds at once (a persistent grid's size).
+  static const int n = [] {
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, ffn_bf16_kernel<MT, FW, SECOND>,
+                                                     FW * 64, 0) != hipSuccess)
+      return 256;
+    return (cus > 0 ? cus : 256) * (per_cu > 0 ? per_cu : 1);
+  }();
+  return n;
+}
+
+struct FfnArgs {
+  const uint16_t* act;
+  uint32_t act_bytes;
+  const uint16_t* W;
+  const uint16_t* bias;
+  const int* offset;
+  const int* row2tok;
+  const float* rowgate;
+  const uint16_t* xres;
+  uint16_t* out;
+  uint32_t out_bytes;
+  int K, Nout, n_mchunks, n_experts, max_rows, T, d_model, no_residual;
+};
+
+template <int MT, int FW, bool SECOND>
+static void launch_ffn_bf16_t(const FfnArgs& a, hipStream_t st) {
+  if constexpr (!FfnGeom<MT, FW, SECOND>::fits) {
+    launch_ffn_bf16_t<MT, 4, SECOND>(a, st);  // narrower blocks need less LDS
+  } else {
+    const long n_tiles = (long)((a.Nout + FW * 32 - 1) / (FW * 32)) * a.n_mchunks * a.n_experts;
+    const long resident = ffn_resident_blocks<MT, FW, SECOND>();
+    const dim3 grid((unsigned)(n_tiles < resident ? n_tiles : resident));
+    hipLaunchKernelGGL((ffn_bf16_kernel<MT, FW, SECOND>), grid, dim3(FW * 64), 0, st, a.act,
+                       a.act_bytes, a.W, a.bias, a.offset, a.row2tok, a.rowgate, a.xres, a.out,
+                       a.out_bytes, a.K, a.Nout, a.n_mchunks, a.n_experts, a.max_rows, a.T,
+                       a.d_model, a.no_residual);
   }
 }
 
 template <int FW, bool SECOND>
-static void launch_ffn_bf16_fw(int mt, dim3 grid, hipStream_t st, const uint16_t* act,
-                               uint32_t act_bytes, const uint16_t* W, const uint16_t* bias,
-                               const int* offset, const int* row2tok, const float* gate,
-                               const uint16_t* xres, uint16_t* out, int K, int Nout,
-                               int n_mchunks, int d_model, int no_residual) {
-#define SFFN_FFN(M)                                                                              \
-  hipLaunchKernelGGL((ffn_bf16_kernel<M, FW, SECOND>), grid, dim3(FW * 64), 0, st, act,          \
-                     act_bytes, W, bias, offset, row2tok, gate, xres, out, K, Nout, n_mchunks,   \
-                     d_model, no_residual)
+static void launch_ffn_bf16_fw(int mt, const FfnArgs& a, hipStream_t st) {
   switch (mt) {
-    case 1: SFFN_FFN(1); break;
-    case 2: SFFN_FFN(2); break;
-    case 3: SFFN_FFN(3); break;
-    case 4: SFFN_FFN(4); break;
-    case 5: SFFN_FFN(5); break;
-    case 6: SFFN_FFN(6); break;
-    case 7: SFFN_FFN(7); break;
-    default: SFFN_FFN(8); break;
+    case 1: launch_ffn_bf16_t<1, FW, SECOND>(a, st); break;
+    case 2: launch_ffn_bf16_t<2, FW, SECOND>(a, st); break;
+    case 3: launch_ffn_bf16_t<3, FW, SECOND>(a, st); break;
+    case 4: launch_ffn_bf16_t<4, FW, SECOND>(a, st); break;
+    case 5: launch_ffn_bf16_t<5, FW, SECOND>(a, st); break;
+    case 6: launch_ffn_bf16_t<6, FW, SECOND>(a, st); break;
+    case 7: launch_ffn_bf16_t<7, FW, SECOND>(a, st); break;
+    default: launch_ffn_bf16_t<8, FW, SECOND>(a, st); break;
   }
-#undef SFFN_FFN
 }
 
 // Row tiles per block: the capacity's 32-row tiles split into as few chunks of at
@@ -342,9 +618,9 @@ ffn_f32_kernel(const float* __restrict__ act, const float* __restrict__ W,
 }
 
 // Waves per block: the widest of 8, 6, 4 that still gives every CU a block
-// (row chunks of 7-8 tiles keep 4 waves: wider blocks would spill registers).
+// (row chunks of 6-8 tiles keep 4 waves: wider blocks would spill registers).
 static int pick_waves(int Nout, int mt, int n_mchunks, int N) {
-  if (mt >= 7) return 4;
+  if (mt >= 6) return 4;
   const int fws[3] = {8, 6, 4};
   for (int fw : fws) {
     const long blocks = (long)((Nout + fw * 32 - 1) / (fw * 32)) * n_mchunks * N;
@@ -354,24 +630,20 @@ static int pick_waves(int Nout, int mt, int n_mchunks, int N) {
 }
 
 template <bool SECOND>
-static void launch_ffn_bf16(int Nout, const Shape& s, hipStream_t st, const uint16_t* act,
-                            uint32_t act_bytes, const uint16_t* W, const uint16_t* bias,
-                            const int* offset, const int* row2tok, const float* gate,
-                            const uint16_t* xres, uint16_t* out, int K, int no_residual) {
+static void launch_ffn_bf16(FfnArgs a, const Shape& s, hipStream_t st) {
   const int mt = rows_tiles(s.C);
-  const int n_mchunks = (s.C + mt * 32 - 1) / (mt * 32);
-  const int fw = pick_waves(Nout, mt, n_mchunks, s.N);
-  const int n_ntiles = (Nout + fw * 32 - 1) / (fw * 32);
-  const dim3 grid((unsigned)((long)n_ntiles * n_mchunks * s.N));
+  a.n_mchunks = (s.C + mt * 32 - 1) / (mt * 32);
+  a.n_experts = s.N;
+  a.max_rows = s.max_rows;
+  a.T = s.T;
+  a.d_model = s.d;
+  const int fw = pick_waves(a.Nout, mt, a.n_mchunks, s.N);
   if (fw == 8)
-    launch_ffn_bf16_fw<8, SECOND>(mt, grid, st, act, act_bytes, W, bias, offset, row2tok, gate,
-                                  xres, out, K, Nout, n_mchunks, s.d, no_residual);
+    launch_ffn_bf16_fw<8, SECOND>(mt, a, st);
   else if (fw == 6)
-    launch_ffn_bf16_fw<6, SECOND>(mt, grid, st, act, act_bytes, W, bias, offset, row2tok, gate,
-                                  xres, out, K, Nout, n_mchunks, s.d, no_residual);
+    launch_ffn_bf16_fw<6, SECOND>(mt, a, st);
   else
-    launch_ffn_bf16_fw<4, SECOND>(mt, grid, st, act, act_bytes, W, bias, offset, row2tok, gate,
-                                  xres, out, K, Nout, n_mchunks, s.d, no_residual);
+    launch_ffn_bf16_fw<4, SECOND>(mt, a, st);
 }
 
 hipError_t launch_ffn1(const Shape& s, const Inputs& in, const Workspace& ws, hipStream_t st) {
@@ -384,9 +656,18 @@ hipError_t launch_ffn1(const Shape& s, const Inputs& in, const Workspace& ws, hi
                        0);
     return hipGetLastError();
   }
-  launch_ffn_bf16<false>(s.F, s, st, (const uint16_t*)in.x, (uint32_t)((size_t)s.T * s.d * 2),
-                         (const uint16_t*)in.W1, (const uint16_t*)in.b1, ws.offset, ws.row2tok,
-                         nullptr, nullptr, (uint16_t*)ws.H, s.d, 0);
+  FfnArgs a{};
+  a.act = (const uint16_t*)in.x;
+  a.act_bytes = (uint32_t)((size_t)s.T * s.d * 2);
+  a.W = (const uint16_t*)in.W1;
+  a.bias = (const uint16_t*)in.b1;
+  a.offset = ws.offset;
+  a.row2tok = ws.row2tok;
+  a.out = (uint16_t*)ws.H;
+  a.out_bytes = (uint32_t)((size_t)s.max_rows * s.F * 2);
+  a.K = s.d;
+  a.Nout = s.F;
+  launch_ffn_bf16<false>(a, s, st);
   return hipGetLastError();
 }
 
@@ -400,10 +681,21 @@ hipError_t launch_ffn2(const Shape& s, const Inputs& in, const Workspace& ws, co
                        (const float*)in.x, (float*)out.y, s.F, s.d, s.d, no_residual ? 1 : 0);
     return hipGetLastError();
   }
-  launch_ffn_bf16<true>(s.d, s, st, (const uint16_t*)ws.H,
-                        (uint32_t)((size_t)s.max_rows * s.F * 2), (const uint16_t*)in.W2,
-                        (const uint16_t*)in.b2, ws.offset, ws.row2tok, out.gate,
-                        (const uint16_t*)in.x, (uint16_t*)out.y, s.F, no_residual ? 1 : 0);
+  FfnArgs a{};
+  a.act = (const uint16_t*)ws.H;
+  a.act_bytes = (uint32_t)((size_t)s.max_rows * s.F * 2);
+  a.W = (const uint16_t*)in.W2;
+  a.bias = (const uint16_t*)in.b2;
+  a.offset = ws.offset;
+  a.row2tok = ws.row2tok;
+  a.rowgate = ws.rowgate;
+  a.xres = (const uint16_t*)in.x;
+  a.out = (uint16_t*)out.y;
+  a.out_bytes = (uint32_t)((size_t)s.T * s.d * 2);
+  a.K = s.F;
+  a.Nout = s.d;
+  a.no_residual = no_residual ? 1 : 0;
+  launch_ffn_bf16<true>(a, s, st);
   return hipGetLastError();
 }
 

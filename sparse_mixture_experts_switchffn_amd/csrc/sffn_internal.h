@@ -30,6 +30,7 @@ struct Workspace {
   int* offset;     // [N+1] exclusive scan of acc: start row of each expert
   double* psum;    // [N] sum over all tokens of p[t,i]
   int* row2tok;    // [max_rows] token of each expert-buffer row
+  float* rowgate;  // [max_rows] gate of each expert-buffer row's token
   void* H;         // [max_rows, F] expert hidden activations (dtype)
   uint16_t* planes;  // router weights split into three bf16 planes, fragment order (fused router)
 };
