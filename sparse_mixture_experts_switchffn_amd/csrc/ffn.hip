@@ -57,11 +57,12 @@ namespace sffn {
 #ifndef SFFN_FFN_STAGES
 #define SFFN_FFN_STAGES 3
 #endif
-// Cache policy of the weight loads (gfx950 buffer-load cache bits; the
-// weights are read once per row chunk).
-#ifndef SFFN_WEIGHT_CPOL
-#define SFFN_WEIGHT_CPOL 0
-#endif
+// Cache policy bits of gfx950 buffer accesses: non-temporal (streamed,
+// not kept in the caches).  The results are stored non-temporal (FFN2 reads
+// H back, but keeping the dirty lines in L2 costs more than re-reading them);
+// the weights are loaded non-temporal when each weight byte is read once (one
+// row chunk per expert), and cached when row chunks re-read them.
+constexpr int kCpolNonTemporal = 2;
 constexpr int FBK = 64;              // k per step (one 128-byte chunk row)
 constexpr int FLDS = FBK + 8;        // bf16 per row of a weight slot (144 B: rows 4 banks apart)
 constexpr int FP = SFFN_FFN_STAGES;  // k-steps in flight
@@ -91,17 +92,20 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int MT, int FW, bool SECOND>
+template <int MT, int FW, int WN, bool SECOND>
 struct FfnGeom {
   static constexpr int ROWS = MT * 32;
   static constexpr int NTHR = FW * 64;
+  static constexpr int WCOLS = WN * 32;               // output columns per wave
+  static constexpr int COLS = FW * WCOLS;             // output columns per tile
   static constexpr int GROUPS = ROWS / 8;             // 8-row groups: one LDS-writing load each
   static constexpr int AL = (GROUPS + FW - 1) / FW;   // such loads per wave and step
+  static constexpr int BL = 4 * WN;                   // weight loads per wave and step
   static constexpr int A_BYTES = ROWS * 128;          // one activation tile
-  static constexpr int B_BYTES = FW * 32 * FLDS * 2;  // the waves' weight slots
+  static constexpr int B_BYTES = COLS * FLDS * 2;     // the waves' weight slots
   static constexpr int FREE = A_BYTES + B_BYTES;      // LDS the epilogue may use
   static constexpr int part_bytes(int wpp) {
-    return SECOND ? ROWS * (wpp * 32 + 4) * 4 : ROWS * (wpp * 32 + 8) * 2;
+    return SECOND ? ROWS * (wpp * WCOLS + 4) * 4 : ROWS * (wpp * WCOLS + 8) * 2;
   }
   static constexpr int pick_wpp() {
     for (int w = FW; w > 1; --w)
@@ -111,14 +115,14 @@ struct FfnGeom {
   // Epilogue: the result leaves through LDS in column parts of WPP waves.
   static constexpr int WPP = pick_wpp();
   static constexpr int NPARTS = FW / WPP;
-  static constexpr int PCOLS = WPP * 32;
+  static constexpr int PCOLS = WPP * WCOLS;
   static constexpr int CPR = PCOLS / 8;                           // 16-byte chunks per part row
   static constexpr int CST = SECOND ? PCOLS + 4 : PCOLS + 8;      // staged elements per row
   static constexpr int XPT = (ROWS * CPR + NTHR - 1) / NTHR;      // chunks per thread and part
   // Vector-memory operations per thread, in issue order:
-  static constexpr int G = AL + 4;                  // per step of a first/middle round
+  static constexpr int G = AL + BL;                 // per step of a first/middle round
   static constexpr int S = NPARTS * XPT;            // epilogue stores
-  static constexpr int T1 = SECOND ? 3 : 2;         // next tile's token, bias (and gate)
+  static constexpr int T1 = 1 + WN + (SECOND ? 1 : 0);  // next tile's token, bias (and gate)
   // FFN2 holds its residual rows in registers through the epilogue; it then
   // fetches the next tile's weights after the epilogue instead of during the
   // last round (its activations still go out before the epilogue).
@@ -131,13 +135,13 @@ struct FfnGeom {
   // round of kind KIND, when that step starts; the step waits until no more
   // than this many are outstanding.  Tile start: the tile's FP activation
   // steps were the last activation loads, followed by S stores (the previous
-  // epilogue, or as many placeholder loads before the first tile), with
+  // epilogue, or as many placeholder stores before the first tile), with
   // LATE_B the FP weight steps, and the T1 lookups.
   template <int KIND, int J>
   static constexpr int step_wait() {
-    constexpr int start = (FP - 1 - J) * AL + S + (LATE_B ? 4 * FP : 0) + T1;
+    constexpr int start = (FP - 1 - J) * AL + S + (LATE_B ? BL * FP : 0) + T1;
     constexpr int extra = (LATE_B && J >= 1) ? EXTRA : 0;
-    constexpr int last_b = LATE_B ? 0 : J * 4;
+    constexpr int last_b = LATE_B ? 0 : J * BL;
     if constexpr (KIND == kRoundFirst) return start + J * G;
     else if constexpr (KIND == kRoundMid) return (FP - 1) * G;
     else {
@@ -187,7 +191,7 @@ __device__ __forceinline__ void ffn_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-template <int MT, int FW, bool SECOND>
+template <int MT, int FW, int WN, bool SECOND, int WPOL>
 __global__ void __launch_bounds__(FW * 64)
 ffn_bf16_kernel(const uint16_t* __restrict__ act, uint32_t act_bytes,
                 const uint16_t* __restrict__ W, const uint16_t* __restrict__ bias,
@@ -196,10 +200,11 @@ ffn_bf16_kernel(const uint16_t* __restrict__ act, uint32_t act_bytes,
                 uint16_t* __restrict__ out, uint32_t out_bytes, int K, int Nout,
                 int n_mchunks, int n_experts, int max_rows, int T, int d_model,
                 int no_residual) {
-  using Geo = FfnGeom<MT, FW, SECOND>;
+  using Geo = FfnGeom<MT, FW, WN, SECOND>;
   constexpr int ROWS = Geo::ROWS, NTHR = Geo::NTHR, AL = Geo::AL, A_BYTES = Geo::A_BYTES;
   constexpr int NPARTS = Geo::NPARTS, WPP = Geo::WPP, PCOLS = Geo::PCOLS, CPR = Geo::CPR;
-  constexpr int CST = Geo::CST, XPT = Geo::XPT;
+  constexpr int CST = Geo::CST, XPT = Geo::XPT, BL = Geo::BL, WCOLS = Geo::WCOLS;
+  constexpr int COLS = Geo::COLS;
   static_assert(ROWS <= NTHR, "one thread per row for the row lookups");
   static_assert(Geo::fits, "LDS budget");
   // [activation ring (FNB tiles) | weight slots | 1 KB sink for idle loads].
@@ -212,7 +217,7 @@ ffn_bf16_kernel(const uint16_t* __restrict__ act, uint32_t act_bytes,
   char* const sink = smem + FNB * A_BYTES + Geo::B_BYTES;
   char* const stage = smem + FP * A_BYTES;
 
-  const int n_ntiles = (Nout + FW * 32 - 1) / (FW * 32);
+  const int n_ntiles = (Nout + COLS - 1) / COLS;
   const int n_tiles = n_ntiles * n_mchunks * n_experts;
   const int stride = gridDim.x;
   FfnTile cur;
@@ -224,7 +229,9 @@ ffn_bf16_kernel(const uint16_t* __restrict__ act, uint32_t act_bytes,
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int khalf = lane >> 5;
-  const int ccol = wave * 32 + (lane & 31);  // this lane's column within the tile
+  // This lane's column within the tile in column tile w of its wave:
+  // wave * WCOLS + w * 32 + lane % 32.
+  const int ccol0 = wave * WCOLS + (lane & 31);
   // Steps rounded up to whole pipeline rounds: the loop body is then free of
   // branches (extra steps load zeros).
   const int nk = ((K + FBK - 1) / FBK + FP - 1) / FP * FP;
@@ -245,45 +252,50 @@ ffn_bf16_kernel(const uint16_t* __restrict__ act, uint32_t act_bytes,
     return __uint_as_float(
         buffer_load4(gate_src, tid < dt.nrows ? (uint32_t)(dt.rbeg + tid) * 4u : kOob));
   };
-  auto load_bias = [&](const FfnTile& dt) -> uint32_t {
-    const int n = dt.nt * (FW * 32) + ccol;
+  auto load_bias = [&](const FfnTile& dt, uint32_t (&bv)[WN]) {
     const __amdgpu_buffer_rsrc_t src =
         make_rsrc(bias ? bias + (size_t)dt.e * Nout : bias, bias ? (uint32_t)Nout * 2u : 0u);
-    return buffer_load2(src, (dt.nrows > 0 && n < Nout) ? (uint32_t)n * 2u : kOob);
-  };
-  // Weights: load i of a step brings rows 8i + lane/8 of the wave's 32,
-  // 16-byte chunk lane%8 of the k-step.
-  auto setup_b = [&](const FfnTile& dt, __amdgpu_buffer_rsrc_t& src, uint32_t (&off)[4]) {
-    src = make_rsrc(W + (size_t)dt.e * Nout * K, (uint32_t)((size_t)Nout * K * 2));
-    const int n0 = dt.nt * (FW * 32) + wave * 32;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int w = 0; w < WN; ++w) {
+      const int n = dt.nt * COLS + ccol0 + w * 32;
+      bv[w] = buffer_load2(src, (dt.nrows > 0 && n < Nout) ? (uint32_t)n * 2u : kOob);
+    }
+  };
+  // Weights: load i of a step brings rows 8i + lane/8 of the wave's WCOLS,
+  // 16-byte chunk lane%8 of the k-step.
+  auto setup_b = [&](const FfnTile& dt, __amdgpu_buffer_rsrc_t& src, uint32_t (&off)[BL]) {
+    src = make_rsrc(W + (size_t)dt.e * Nout * K, (uint32_t)((size_t)Nout * K * 2));
+    const int n0 = dt.nt * COLS + wave * WCOLS;
+#pragma unroll
+    for (int i = 0; i < BL; ++i) {
       const int nr = n0 + i * 8 + (lane >> 3);
       off[i] = (dt.nrows > 0 && nr < Nout)
                    ? ((uint32_t)nr * (uint32_t)K + (uint32_t)(lane & 7) * 8u) * 2u : kOob;
     }
   };
-  auto load_b = [&](u32x4 (&rb)[4], const __amdgpu_buffer_rsrc_t& src, const uint32_t (&off)[4],
+  auto load_b = [&](u32x4 (&rb)[BL], const __amdgpu_buffer_rsrc_t& src, const uint32_t (&off)[BL],
                     int ks) {
     const bool kin = ks * FBK + (lane & 7) * 8 < K;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < BL; ++i)
       rb[i] = __builtin_amdgcn_raw_buffer_load_b128(
-          src, (int)(kin ? off[i] + (uint32_t)ks * (FBK * 2) : kOob), 0, SFFN_WEIGHT_CPOL);
+          src, (int)(kin ? off[i] + (uint32_t)ks * (FBK * 2) : kOob), 0, WPOL);
   };
   // Activations: load i of a step fills row group g = wave + i*FW (rows 8g ..
   // 8g+7); lane l writes LDS chunk l%8 of row 8g + l/8, which holds logical
   // chunk (l%8) ^ swizzle(row).  Groups past the tile go to the sink.
-  static_assert(FW % 2 == 0, "row groups of one wave share their swizzle parity");
   uint32_t a_off[AL];
-  const int a_c8 = (((lane & 7) ^ (lane >> 3) ^ (wave & 1)) & 7) * 8;  // 8 x logical chunk
+  int a_c8[AL];  // 8 x the logical chunk this lane loads (the swizzle parity follows the group)
+#pragma unroll
+  for (int i = 0; i < AL; ++i)
+    a_c8[i] = (((lane & 7) ^ (lane >> 3) ^ ((wave + i * FW) & 1)) & 7) * 8;
   auto setup_a = [&](const FfnTile& dt) {
 #pragma unroll
     for (int i = 0; i < AL; ++i) {
       const int r = (wave + i * FW) * 8 + (lane >> 3);
       const bool ok = r < dt.nrows;
       const uint32_t row = SECOND ? (uint32_t)(dt.rbeg + r) : (uint32_t)tok_s[ok ? r : 0];
-      a_off[i] = ok ? (row * (uint32_t)K + (uint32_t)a_c8) * 2u : kOob;
+      a_off[i] = ok ? (row * (uint32_t)K + (uint32_t)a_c8[i]) * 2u : kOob;
     }
   };
   auto dma_a = [&](int buf, int ks) {
@@ -291,7 +303,7 @@ ffn_bf16_kernel(const uint16_t* __restrict__ act, uint32_t act_bytes,
     for (int i = 0; i < AL; ++i) {
       const int g = wave + i * FW;
       char* dst = g < Geo::GROUPS ? As + buf * A_BYTES + g * 1024 : sink;
-      const bool kin = ks * FBK + a_c8 < K;
+      const bool kin = ks * FBK + a_c8[i] < K;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           ra_src, SFFN_LDS_PTR(dst), 16, (int)(kin ? a_off[i] + (uint32_t)ks * (FBK * 2) : kOob),
           0, 0, 0);
@@ -302,23 +314,37 @@ ffn_bf16_kernel(const uint16_t* __restrict__ act, uint32_t act_bytes,
   // (4*khalf + q) ^ swizzle; the q term only flips address bits 4-5.
   const int rsw = (lane & 7) ^ ((lane >> 3) & 1);  // swizzle of rows with these low bits
   const uint32_t a_rd = (uint32_t)(lane & 31) * 128u + (uint32_t)(((khalf * 4) ^ rsw) * 16);
-  f32x16 acc[MT];
-  uint16_t* bslot = Bs + wave * 32 * FLDS;
-  auto compute = [&](int buf, const u32x4 (&rb)[4]) {
+  f32x16 acc[MT * WN];
+  uint16_t* bslot = Bs + wave * WCOLS * FLDS;
+  auto compute = [&](int buf, const u32x4 (&rb)[BL]) {
     // Weight tile into the wave's LDS slot (row-major), back out in operand layout.
     // LDS accesses of one wave complete in order, so no barrier is needed.
 #pragma unroll
-    for (int i = 0; i < 4; ++i) store16(bslot + (i * 8 + (lane >> 3)) * FLDS + (lane & 7) * 8, rb[i]);
+    for (int i = 0; i < BL; ++i) store16(bslot + (i * 8 + (lane >> 3)) * FLDS + (lane & 7) * 8, rb[i]);
     const char* abase = As + buf * A_BYTES;
     const uint16_t* bbase = bslot + (lane & 31) * FLDS + khalf * 32;
+    // Operand fragments of sub-step q (16 k): read one sub-step ahead of the
+    // matrix-core ops that use them; the scheduling fence per sub-step keeps
+    // the compiler from hoisting all of a step's reads (registers).
+    bf16x8 fa[2][MT], fb[2][WN];
+    auto read_frags = [&](int q, bf16x8 (&a)[MT], bf16x8 (&b)[WN]) {
+#pragma unroll
+      for (int w = 0; w < WN; ++w) b[w] = as_bf16x8(load16(bbase + w * 32 * FLDS + q * 8));
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+        a[m] = as_bf16x8(load16(abase + ((a_rd ^ (uint32_t)(q * 16)) + m * 32 * 128)));
+    };
+    read_frags(0, fa[0], fb[0]);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const bf16x8 b = as_bf16x8(load16(bbase + q * 8));
+      if (q < 3) read_frags(q + 1, fa[(q + 1) & 1], fb[(q + 1) & 1]);
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
-        const bf16x8 a = as_bf16x8(load16(abase + ((a_rd ^ (uint32_t)(q * 16)) + m * 32 * 128)));
-        acc[m] = mfma_32x32x16(a, b, acc[m]);
+#pragma unroll
+        for (int w = 0; w < WN; ++w)
+          acc[m * WN + w] = mfma_32x32x16(fa[q & 1][m], fb[q & 1][w], acc[m * WN + w]);
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
@@ -326,10 +352,11 @@ ffn_bf16_kernel(const uint16_t* __restrict__ act, uint32_t act_bytes,
   // and the activation rows (FFN1 needs the tokens for them), in the order a
   // tile start inside the loop sees them.
   __amdgpu_buffer_rsrc_t rb_src;
-  uint32_t b_off[4];
-  u32x4 rb[FP][4];
+  uint32_t b_off[BL];
+  u32x4 rb[FP][BL];
   int my_tok = load_tok(cur);
-  uint32_t my_bias = load_bias(cur);
+  uint32_t my_bias[WN];
+  load_bias(cur, my_bias);
   float my_gate = SECOND ? load_gate(cur) : 0.f;
   setup_b(cur, rb_src, b_off);
   auto prologue_b = [&]() {
@@ -367,7 +394,7 @@ ffn_bf16_kernel(const uint16_t* __restrict__ act, uint32_t act_bytes,
     int etid = tid;
     asm volatile("" : "+v"(etid));
 #pragma unroll
-    for (int m = 0; m < MT; ++m) acc[m] = f32x16{};
+    for (int m = 0; m < MT * WN; ++m) acc[m] = f32x16{};
     if (SECOND && tid < ROWS) {
       tok_s[tid] = my_tok;  // visible after the first step's barrier
       gate_s[tid] = my_gate;
@@ -376,10 +403,11 @@ ffn_bf16_kernel(const uint16_t* __restrict__ act, uint32_t act_bytes,
     FfnTile nxt{cur.e, cur.nt, 0, 0};
     const int tn = find_tile<ROWS>(t + stride, stride, n_tiles, n_ntiles, n_mchunks, offset, nxt);
     const int tok_n = load_tok(nxt);
-    const uint32_t bias_n = load_bias(nxt);
+    uint32_t bias_n[WN];
+    load_bias(nxt, bias_n);
     const float gate_n = SECOND ? load_gate(nxt) : 0.f;
     __amdgpu_buffer_rsrc_t rb_src_n;
-    uint32_t b_off_n[4];
+    uint32_t b_off_n[BL];
 
     u32x4 xr[NPARTS][SECOND ? XPT : 1];
     auto load_residual = [&]() {
@@ -390,7 +418,7 @@ ffn_bf16_kernel(const uint16_t* __restrict__ act, uint32_t act_bytes,
           for (int i = 0; i < XPT; ++i) {
             const int idx = etid + i * NTHR;
             const int r = idx / CPR, c = idx % CPR;
-            const int col = cur.nt * (FW * 32) + p * PCOLS + c * 8;
+            const int col = cur.nt * COLS + p * PCOLS + c * 8;
             const bool ok = r < cur.nrows && col < Nout;
             xr[p][i] = buffer_load16(
                 x_src, ok ? ((uint32_t)tok_s[ok ? r : 0] * (uint32_t)d_model + (uint32_t)col) * 2u
@@ -442,21 +470,28 @@ ffn_bf16_kernel(const uint16_t* __restrict__ act, uint32_t act_bytes,
 
     // Epilogue: the result goes through LDS in column parts and leaves in
     // 16-byte row chunks.
-    const float bv = bf16_bits_to_f32(my_bias);
 #pragma unroll
     for (int p = 0; p < NPARTS; ++p) {
       if (wave / WPP == p) {
-        const int pc = ccol - p * PCOLS;
+        // Lane geometry from the opaque index: per-element staging addresses
+        // stay immediates off one per-tile base instead of hoisted registers.
+        const int elane = etid & 63;
+        const int ekh = elane >> 5;
 #pragma unroll
-        for (int m = 0; m < MT; ++m) {
+        for (int w = 0; w < WN; ++w) {
+          const float bv = bf16_bits_to_f32(my_bias[w]);
+          const int pc = wave * WCOLS + (elane & 31) + w * 32 - p * PCOLS;
 #pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int r = m * 32 + (v >> 2) * 8 + khalf * 4 + (v & 3);
-            if (SECOND)
-              reinterpret_cast<float*>(stage)[r * CST + pc] = acc[m][v] + bv;
-            else  // H: bias, ReLU, one rounding to bf16
-              reinterpret_cast<uint16_t*>(stage)[r * CST + pc] =
-                  (uint16_t)f32_to_bf16_bits(fmaxf(acc[m][v] + bv, 0.f));
+          for (int m = 0; m < MT; ++m) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const int r = m * 32 + (v >> 2) * 8 + ekh * 4 + (v & 3);
+              if (SECOND)
+                reinterpret_cast<float*>(stage)[r * CST + pc] = acc[m * WN + w][v] + bv;
+              else  // H: bias, ReLU, one rounding to bf16
+                reinterpret_cast<uint16_t*>(stage)[r * CST + pc] =
+                    (uint16_t)f32_to_bf16_bits(fmaxf(acc[m * WN + w][v] + bv, 0.f));
+            }
           }
         }
       }
@@ -465,13 +500,15 @@ ffn_bf16_kernel(const uint16_t* __restrict__ act, uint32_t act_bytes,
       for (int i = 0; i < XPT; ++i) {
         const int idx = etid + i * NTHR;
         const int r = idx / CPR, c = idx % CPR;
-        const int col = cur.nt * (FW * 32) + p * PCOLS + c * 8;
+        const int col = cur.nt * COLS + p * PCOLS + c * 8;
         const bool ok = r < cur.nrows && col < Nout;
         const int rr = ok ? r : 0;
         if (!SECOND) {
           const u32x4 v = load16(reinterpret_cast<const uint16_t*>(stage) + rr * CST + c * 8);
-          buffer_store16(out_src,
-                         ok ? ((uint32_t)(cur.rbeg + r) * (uint32_t)Nout + (uint32_t)col) * 2u : kOob, v);
+          __builtin_amdgcn_raw_buffer_store_b128(
+              v, out_src,
+              (int)(ok ? ((uint32_t)(cur.rbeg + r) * (uint32_t)Nout + (uint32_t)col) * 2u : kOob), 0,
+              kCpolNonTemporal);
         } else {
           // y = (acc + b2) * gate + x, one rounding to bf16.
           const float* srow = reinterpret_cast<const float*>(stage) + rr * CST + c * 8;
@@ -486,8 +523,10 @@ ffn_bf16_kernel(const uint16_t* __restrict__ act, uint32_t act_bytes,
             const float hi = g * val[2 * j + 1] + bf16_bits_to_f32(xr[p][i][j] >> 16);
             yr[j] = f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
           }
-          buffer_store16(out_src,
-                         ok ? ((uint32_t)tok_s[rr] * (uint32_t)d_model + (uint32_t)col) * 2u : kOob, yr);
+          __builtin_amdgcn_raw_buffer_store_b128(
+              yr, out_src,
+              (int)(ok ? ((uint32_t)tok_s[rr] * (uint32_t)d_model + (uint32_t)col) * 2u : kOob), 0,
+              kCpolNonTemporal);
         }
       }
       ffn_barrier();
@@ -505,11 +544,12 @@ ffn_bf16_kernel(const uint16_t* __restrict__ act, uint32_t act_bytes,
     cur = nxt;
     t = tn;
     my_tok = tok_n;
-    my_bias = bias_n;
+#pragma unroll
+    for (int w = 0; w < WN; ++w) my_bias[w] = bias_n[w];
     my_gate = gate_n;
     rb_src = rb_src_n;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) b_off[i] = b_off_n[i];
+    for (int i = 0; i < BL; ++i) b_off[i] = b_off_n[i];
   }
   // The last activation loads (range-checked to nothing) still write LDS:
   // let them land before the block's LDS is released.
@@ -518,14 +558,14 @@ ffn_bf16_kernel(const uint16_t* __restrict__ act, uint32_t act_bytes,
 
 #undef SFFN_LDS_PTR
 
-template <int MT, int FW, bool SECOND>
+template <int MT, int FW, int WN, bool SECOND>
 static int ffn_resident_blocks() {
   // Blocks of this kernel the device holds at once (a persistent grid's size).
   static const int n = [] {
     int dev = 0, cus = 0, per_cu = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, ffn_bf16_kernel<MT, FW, SECOND>,
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, ffn_bf16_kernel<MT, FW, WN, SECOND, 0>,
                                                      FW * 64, 0) != hipSuccess)
       return 256;
     return (cus > 0 ? cus : 256) * (per_cu > 0 ? per_cu : 1);
@@ -547,33 +587,101 @@ struct FfnArgs {
   int K, Nout, n_mchunks, n_experts, max_rows, T, d_model, no_residual;
 };
 
-template <int MT, int FW, bool SECOND>
+// Block shapes (waves, 32-column tiles per wave) the launcher chooses from.
+struct FfnShape {
+  int fw, wn;
+};
+constexpr FfnShape kFfnShapes[] = {{4, 2}, {3, 2}, {8, 1}, {6, 1}, {4, 1}};
+
+template <int MT, int FW, int WN, bool SECOND>
+static constexpr bool ffn_shape_ok() {
+  // Two column tiles per wave only for up to 2 row tiles: beyond that the
+  // registers allow one wave per SIMD, which leaves too little latency
+  // hiding.  Blocks of more than 4 waves (2 per SIMD) only up to 6 row tiles
+  // (registers).  One thread per row for the row lookups; the LDS budget holds.
+  return (WN == 1 || MT <= 2) && (FW <= 4 || MT <= 6) && MT * 32 <= FW * 64 &&
+         FfnGeom<MT, FW, WN, SECOND>::fits;
+}
+
+template <int MT, int FW, int WN, bool SECOND>
+static long ffn_resident_if_ok() {
+  if constexpr (ffn_shape_ok<MT, FW, WN, SECOND>()) return ffn_resident_blocks<MT, FW, WN, SECOND>();
+  else return 0;
+}
+
+template <int MT, int FW, int WN, bool SECOND>
+static long ffn_grid(const FfnArgs& a) {
+  const long cols = FW * WN * 32;
+  const long n_tiles = (a.Nout + cols - 1) / cols * a.n_mchunks * a.n_experts;
+  const long resident = ffn_resident_blocks<MT, FW, WN, SECOND>();
+  return n_tiles < resident ? n_tiles : resident;
+}
+
+template <int MT, int FW, int WN, bool SECOND>
 static void launch_ffn_bf16_t(const FfnArgs& a, hipStream_t st) {
-  if constexpr (!FfnGeom<MT, FW, SECOND>::fits) {
-    launch_ffn_bf16_t<MT, 4, SECOND>(a, st);  // narrower blocks need less LDS
-  } else {
-    const long n_tiles = (long)((a.Nout + FW * 32 - 1) / (FW * 32)) * a.n_mchunks * a.n_experts;
-    const long resident = ffn_resident_blocks<MT, FW, SECOND>();
-    const dim3 grid((unsigned)(n_tiles < resident ? n_tiles : resident));
-    hipLaunchKernelGGL((ffn_bf16_kernel<MT, FW, SECOND>), grid, dim3(FW * 64), 0, st, a.act,
-                       a.act_bytes, a.W, a.bias, a.offset, a.row2tok, a.rowgate, a.xres, a.out,
-                       a.out_bytes, a.K, a.Nout, a.n_mchunks, a.n_experts, a.max_rows, a.T,
-                       a.d_model, a.no_residual);
+  if constexpr (ffn_shape_ok<MT, FW, WN, SECOND>()) {
+    const dim3 grid((unsigned)ffn_grid<MT, FW, WN, SECOND>(a)), block(FW * 64);
+    // Weights are streamed past the caches when no other row chunk re-reads
+    // them; single-row-tile blocks keep them cached (measured faster there).
+    if (a.n_mchunks == 1 && MT >= 2)
+      hipLaunchKernelGGL((ffn_bf16_kernel<MT, FW, WN, SECOND, kCpolNonTemporal>), grid, block, 0, st,
+                         a.act, a.act_bytes, a.W, a.bias, a.offset, a.row2tok, a.rowgate, a.xres,
+                         a.out, a.out_bytes, a.K, a.Nout, a.n_mchunks, a.n_experts, a.max_rows,
+                         a.T, a.d_model, a.no_residual);
+    else
+      hipLaunchKernelGGL((ffn_bf16_kernel<MT, FW, WN, SECOND, 0>), grid, block, 0, st, a.act,
+                         a.act_bytes, a.W, a.bias, a.offset, a.row2tok, a.rowgate, a.xres, a.out,
+                         a.out_bytes, a.K, a.Nout, a.n_mchunks, a.n_experts, a.max_rows, a.T,
+                         a.d_model, a.no_residual);
   }
 }
 
-template <int FW, bool SECOND>
-static void launch_ffn_bf16_fw(int mt, const FfnArgs& a, hipStream_t st) {
-  switch (mt) {
-    case 1: launch_ffn_bf16_t<1, FW, SECOND>(a, st); break;
-    case 2: launch_ffn_bf16_t<2, FW, SECOND>(a, st); break;
-    case 3: launch_ffn_bf16_t<3, FW, SECOND>(a, st); break;
-    case 4: launch_ffn_bf16_t<4, FW, SECOND>(a, st); break;
-    case 5: launch_ffn_bf16_t<5, FW, SECOND>(a, st); break;
-    case 6: launch_ffn_bf16_t<6, FW, SECOND>(a, st); break;
-    case 7: launch_ffn_bf16_t<7, FW, SECOND>(a, st); break;
-    default: launch_ffn_bf16_t<8, FW, SECOND>(a, st); break;
+// Estimated time of one launch with a block shape, in units of one row of K
+// streamed through a CU: each tile streams its COLS weight rows and re-reads
+// its activation rows (mostly L2 hits, weighted 0.6); tiles run in rounds of
+// the resident grid.  Returns a huge cost for shapes that cannot run.
+template <int MT, bool SECOND>
+static double ffn_shape_cost(const FfnArgs& a, FfnShape sh, int cus) {
+  long resident = 0;
+  if (sh.fw == 4 && sh.wn == 2) resident = ffn_resident_if_ok<MT, 4, 2, SECOND>();
+  if (sh.fw == 3 && sh.wn == 2) resident = ffn_resident_if_ok<MT, 3, 2, SECOND>();
+  if (sh.fw == 8 && sh.wn == 1) resident = ffn_resident_if_ok<MT, 8, 1, SECOND>();
+  if (sh.fw == 6 && sh.wn == 1) resident = ffn_resident_if_ok<MT, 6, 1, SECOND>();
+  if (sh.fw == 4 && sh.wn == 1) resident = ffn_resident_if_ok<MT, 4, 1, SECOND>();
+  if (resident <= 0) return 1e300;
+  const long cols = sh.fw * sh.wn * 32;
+  const long n_tiles = (a.Nout + cols - 1) / cols * a.n_mchunks * a.n_experts;
+  const long rounds = (n_tiles + resident - 1) / resident;
+  const double tile = (double)cols + 0.6 * MT * 32;
+  return (double)rounds * (double)resident / (double)cus * tile;
+}
+
+template <int MT, bool SECOND>
+static void launch_ffn_bf16_mt(const FfnArgs& a, hipStream_t st) {
+  static const int cus = [] {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      return 256;
+    return n;
+  }();
+  FfnShape best = kFfnShapes[0];
+  double best_cost = 1e301;
+  for (const FfnShape& sh : kFfnShapes) {  // first of equal cost wins (fewer LDS reads)
+#ifdef SFFN_FFN_ONLY_WN  // tuning builds: restrict the choice to one wave width
+    if (sh.wn != SFFN_FFN_ONLY_WN) continue;
+#endif
+    const double c = ffn_shape_cost<MT, SECOND>(a, sh, cus);
+    if (c < best_cost) {
+      best_cost = c;
+      best = sh;
+    }
   }
+  if (best.fw == 4 && best.wn == 2) launch_ffn_bf16_t<MT, 4, 2, SECOND>(a, st);
+  else if (best.fw == 3 && best.wn == 2) launch_ffn_bf16_t<MT, 3, 2, SECOND>(a, st);
+  else if (best.fw == 8) launch_ffn_bf16_t<MT, 8, 1, SECOND>(a, st);
+  else if (best.fw == 6) launch_ffn_bf16_t<MT, 6, 1, SECOND>(a, st);
+  else launch_ffn_bf16_t<MT, 4, 1, SECOND>(a, st);
 }
 
 // Row tiles per block: the capacity's 32-row tiles split into as few chunks of at
@@ -617,18 +725,6 @@ ffn_f32_kernel(const float* __restrict__ act, const float* __restrict__ W,
   }
 }
 
-// Waves per block: the widest of 8, 6, 4 that still gives every CU a block
-// (row chunks of 6-8 tiles keep 4 waves: wider blocks would spill registers).
-static int pick_waves(int Nout, int mt, int n_mchunks, int N) {
-  if (mt >= 6) return 4;
-  const int fws[3] = {8, 6, 4};
-  for (int fw : fws) {
-    const long blocks = (long)((Nout + fw * 32 - 1) / (fw * 32)) * n_mchunks * N;
-    if (blocks >= 256) return fw;
-  }
-  return 4;
-}
-
 template <bool SECOND>
 static void launch_ffn_bf16(FfnArgs a, const Shape& s, hipStream_t st) {
   const int mt = rows_tiles(s.C);
@@ -637,13 +733,16 @@ static void launch_ffn_bf16(FfnArgs a, const Shape& s, hipStream_t st) {
   a.max_rows = s.max_rows;
   a.T = s.T;
   a.d_model = s.d;
-  const int fw = pick_waves(a.Nout, mt, a.n_mchunks, s.N);
-  if (fw == 8)
-    launch_ffn_bf16_fw<8, SECOND>(mt, a, st);
-  else if (fw == 6)
-    launch_ffn_bf16_fw<6, SECOND>(mt, a, st);
-  else
-    launch_ffn_bf16_fw<4, SECOND>(mt, a, st);
+  switch (mt) {
+    case 1: launch_ffn_bf16_mt<1, SECOND>(a, st); break;
+    case 2: launch_ffn_bf16_mt<2, SECOND>(a, st); break;
+    case 3: launch_ffn_bf16_mt<3, SECOND>(a, st); break;
+    case 4: launch_ffn_bf16_mt<4, SECOND>(a, st); break;
+    case 5: launch_ffn_bf16_mt<5, SECOND>(a, st); break;
+    case 6: launch_ffn_bf16_mt<6, SECOND>(a, st); break;
+    case 7: launch_ffn_bf16_mt<7, SECOND>(a, st); break;
+    default: launch_ffn_bf16_mt<8, SECOND>(a, st); break;
+  }
 }
 
 hipError_t launch_ffn1(const Shape& s, const Inputs& in, const Workspace& ws, hipStream_t st) {
