@@ -225,12 +225,13 @@ router_planes_kernel(const float* __restrict__ Wr, int d, int N, int MT, int nks
 // L2-resident), columns = tokens (four lanes per 64-byte row segment,
 // re-laid out through a private LDS slot into the operand layout).  32 k per
 // step, operands fetched 2-3 steps ahead.
-// Epilogue (wave 0): lane l holds the logits of token l%32 for the experts of
-// its lane half; the halves meet through one cross-lane exchange:
-//   m = max z, e = lowest index with z = m, S = sum exp(z - m), gate = 1/S;
-//   ppart[b, i] = sum over the block's tokens of exp(z_i - m)/S (butterfly in a
-//   fixed order), cnt[b, i] = tokens of the block whose top-1 is i,
-//   lrank[t] = tokens of the block before t with the same top-1.
+// Epilogue (all four waves): the partial logit tiles meet in LDS and are
+// summed in wave order; eight threads per token then take
+//   m = max z, e = lowest index with z = m, S = sum exp(z - m), gate = 1/S,
+// each over an eighth of the experts, combined by three cross-lane steps;
+// finally one thread per expert sums p over the block's tokens in token order
+// (ppart[b, i]) and counts the tokens whose top-1 is i (cnt[b, i]), and one
+// thread per token counts the earlier tokens with its top-1 (lrank[t]).
 // ---------------------------------------------------------------------------
 constexpr int FR_BK = 32;
 constexpr int FR_LD = FR_BK + 8;  // bf16 per LDS row of the token slot (80 B)
@@ -243,8 +244,12 @@ router_fused_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__
                     uint32_t planes_bytes, int T, int d, int N, int32_t* __restrict__ expert_idx,
                     float* __restrict__ gate, float* __restrict__ ppart, int* __restrict__ cnt,
                     int* __restrict__ lrank) {
+  constexpr int NE = MT * 32;       // expert rows of the tile
+  constexpr int PST = 33;           // floats per staged expert row (32 tokens + 1: banks)
+  constexpr int EPT = NE / 8;       // experts per thread in the softmax (8 threads a token)
   __shared__ __attribute__((aligned(16))) uint16_t Xs[FR_KSPLIT][32 * FR_LD];
-  __shared__ __attribute__((aligned(16))) float Ps[FR_KSPLIT - 1][MT * 16][64];
+  __shared__ float Ps[FR_KSPLIT][NE * PST];  // partial logits; then Ps[0] holds p
+  __shared__ int ids_s[32];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int b = blockIdx.x;
@@ -319,43 +324,37 @@ router_fused_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__
     }
   }
 
-  // ---- sum of the partial logit tiles, waves in order ----
-  if (wave > 0) {
-#pragma unroll
-    for (int m = 0; m < MT; ++m)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) Ps[wave - 1][m * 16 + v][lane] = acc[m][v];
-  }
-  lds_barrier();
-  if (wave > 0) return;
-#pragma unroll
-  for (int w = 0; w < FR_KSPLIT - 1; ++w)
-#pragma unroll
-    for (int m = 0; m < MT; ++m)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[m][v] += Ps[w][m * 16 + v][lane];
-
-  // ---- softmax, top-1 and gate for token t ----
+  // ---- partial logit tiles to LDS: Ps[w][e][t] ----
   const int tl = lane & 31;
-  const int t = t0 + tl;
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int v = 0; v < 16; ++v)
+      Ps[wave][(m * 32 + (v >> 2) * 8 + khalf * 4 + (v & 3)) * PST + tl] = acc[m][v];
+  lds_barrier();
+
+  // ---- softmax, top-1 and gate: token tt, experts g + 8 i ----
+  const int tt = threadIdx.x >> 3;
+  const int g = threadIdx.x & 7;
+  const int t = t0 + tt;
   const bool live = t < T;
+  float z[EPT];
   float mx = -INFINITY;
   int arg = 0x7fffffff;
 #pragma unroll
-  for (int m = 0; m < MT; ++m) {
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int e = m * 32 + (v >> 2) * 8 + khalf * 4 + (v & 3);
-      const float z = acc[m][v];
-      if (e < N && (z > mx || (z == mx && e < arg))) {
-        mx = z;
-        arg = e;
-      }
+  for (int i = 0; i < EPT; ++i) {
+    const int e = g + 8 * i;
+    const int o = e * PST + tt;
+    z[i] = ((Ps[0][o] + Ps[1][o]) + Ps[2][o]) + Ps[3][o];  // waves in order
+    if (e < N && z[i] > mx) {  // e rises with i: the first maximum is the lowest index
+      mx = z[i];
+      arg = e;
     }
   }
-  {
-    const float om = __shfl_xor(mx, 32);
-    const int oa = __shfl_xor(arg, 32);
+#pragma unroll
+  for (int off = 1; off < 8; off <<= 1) {
+    const float om = __shfl_xor(mx, off);
+    const int oa = __shfl_xor(arg, off);
     if (om > mx || (om == mx && oa < arg)) {
       mx = om;
       arg = oa;
@@ -363,46 +362,43 @@ router_fused_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__
   }
   float ssum = 0.f;
 #pragma unroll
-  for (int m = 0; m < MT; ++m) {
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int e = m * 32 + (v >> 2) * 8 + khalf * 4 + (v & 3);
-      acc[m][v] = e < N ? expf(acc[m][v] - mx) : 0.f;
-      ssum += acc[m][v];
-    }
+  for (int i = 0; i < EPT; ++i) {
+    z[i] = (g + 8 * i) < N ? expf(z[i] - mx) : 0.f;
+    ssum += z[i];
   }
-  ssum += __shfl_xor(ssum, 32);
+#pragma unroll
+  for (int off = 1; off < 8; off <<= 1) ssum += __shfl_xor(ssum, off);
   const float inv = 1.0f / ssum;
-  if (khalf == 0 && live) {
-    expert_idx[t] = arg;
-    gate[t] = inv;
-  }
-
-  // ---- block sums of p over the 32 tokens (butterfly over lane bits 0..4) ----
-#pragma unroll
-  for (int m = 0; m < MT; ++m) {
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      float pv = live ? acc[m][v] * inv : 0.f;
-#pragma unroll
-      for (int off = 1; off < 32; off <<= 1) pv += __shfl_xor(pv, off);
-      const int e = m * 32 + (v >> 2) * 8 + khalf * 4 + (v & 3);
-      if (tl == 0 && e < N) ppart[(size_t)b * N + e] = pv;
+  if (g == 0) {
+    ids_s[tt] = live ? arg : -1;
+    if (live) {
+      expert_idx[t] = arg;
+      gate[t] = inv;
     }
   }
+  lds_barrier();  // every wave is past its reads of the partial tiles
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) Ps[0][(g + 8 * i) * PST + tt] = live ? z[i] * inv : 0.f;
+  lds_barrier();
 
-  // ---- top-1 counts and in-block ranks (every lane joins every shuffle) ----
-  const int my_e = live ? arg : -1;
-  int r = 0, c0 = 0, c1 = 0;
-  for (int j = 0; j < 32; ++j) {
-    const int ej = __shfl(my_e, j);
-    r += (j < tl && ej == my_e);
-    c0 += (ej == lane);
-    c1 += (ej == lane + 64);
+  // ---- per expert: block sum of p (token order) and top-1 count ----
+  for (int e = threadIdx.x; e < N; e += 64 * FR_KSPLIT) {
+    float ps = 0.f;
+    int c = 0;
+    for (int j = 0; j < 32; ++j) {
+      ps += Ps[0][e * PST + j];
+      c += ids_s[j] == e;
+    }
+    ppart[(size_t)b * N + e] = ps;
+    cnt[(size_t)b * N + e] = c;
   }
-  if (khalf == 0 && live) lrank[t] = r;
-  if (lane < N) cnt[(size_t)b * N + lane] = c0;
-  if (lane + 64 < N) cnt[(size_t)b * N + lane + 64] = c1;
+  // ---- per token: earlier tokens of the block with the same top-1 ----
+  if (threadIdx.x < 32 && t0 + (int)threadIdx.x < T) {
+    const int me = ids_s[threadIdx.x];
+    int r = 0;
+    for (int j = 0; j < (int)threadIdx.x; ++j) r += ids_s[j] == me;
+    lrank[t0 + threadIdx.x] = r;
+  }
 }
 
 // Logits for fp32 token states: one thread per (token, expert), fp32 FMA in k order.
