@@ -59,6 +59,41 @@ def parse():
     return p.parse_args()
 
 
+def measured_peaks(dev):
+    """This GPU's own reference points, beside the published peaks: a plain device copy
+    (read + write bytes per second) and a large bf16 GEMM through torch (hipBLASLt)."""
+    import torch
+    out = {"hbm_spec_GBps": HBM_PEAK_GBS, "bf16_mfma_spec_TFLOPs": MFMA_BF16_PEAK_TFLOPS}
+    try:
+        n = 1 << 29  # 1 GiB of bf16
+        src = torch.ones(n, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize(dev)
+        out["copy_GBps"] = 5 * 2 * n * 2 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+        del src, dst
+        m = 8192
+        a = torch.randn(m, m, device=dev).to(torch.bfloat16)
+        b = torch.randn(m, m, device=dev).to(torch.bfloat16)
+        c = a @ b
+        e0.record()
+        for _ in range(5):
+            c = a @ b
+        e1.record()
+        torch.cuda.synchronize(dev)
+        out["bf16_gemm_8192_TFLOPs"] = 5 * 2.0 * m ** 3 / (e0.elapsed_time(e1) * 1e-3) / 1e12
+        del a, b, c
+        torch.cuda.empty_cache()
+    except Exception as exc:  # a reference only; never fails the benchmark
+        out["error"] = str(exc)[:200]
+    return out
+
+
 def copy_calibration():
     """A plain copy of known size: 1 GiB read and 1 GiB written per launch."""
     import torch
@@ -104,15 +139,26 @@ def measured_traffic(kernel: str, workload: str):
         return None
 
 
-def algorithmic_bytes(w, stage, accepted, active, esize):
+def algorithmic_bytes(w, stage, accepted, active, esize, dropped=0):
     """Bytes a stage must move at minimum, from what it reads and writes once.
 
+    router_logits: fused router (bf16, N <= 128): Wr read + its three bf16 planes
+          written; otherwise x + Wr read and the fp32 logits written.
+    softmax_route: fused: x + the planes read, expert/gate/rank per token and the
+          per-block p sums and counts written; otherwise the logits read instead of x.
+    dispatch_scan: per-block counts and p sums read, per-block bases written, and the
+          per-expert counts / accepted / p totals.
+    dispatch_scatter: expert, rank, block base and gate per token read; slot per token,
+          the row-to-token and row-to-gate maps, and the dropped rows (read + write).
     ffn1: W1 of every expert with accepted tokens + the gathered x rows + the H rows
           written + b1 + the row-to-token map.
     ffn2: W2 of active experts + H rows + the x rows of the residual + the y rows
           written + b2 + gate and row-to-token entries.
     """
     A = accepted
+    T, N, d = w.T, w.N, w.d
+    nblk = (T + 31) // 32
+    fused = w.dtype == "bf16" and N <= 128
     wbytes = active * w.F * w.d * esize
     bias1 = active * w.F * esize if w.has_bias else 0
     bias2 = active * w.d * esize if w.has_bias else 0
@@ -121,10 +167,14 @@ def algorithmic_bytes(w, stage, accepted, active, esize):
     if stage == "ffn2":
         return wbytes + A * w.F * esize + 2 * A * w.d * esize + bias2 + A * 8
     if stage == "router_logits":
-        return w.T * w.d * esize + w.N * w.d * 4 + w.T * w.N * 4
+        return N * d * 4 + 3 * N * d * 2 if fused else T * d * esize + N * d * 4 + T * N * 4
     if stage == "softmax_route":
-        nb = (w.T + 63) // 64
-        return w.T * w.N * 4 + w.T * 12 + 2 * nb * w.N * 4
+        src = T * d * 2 + 3 * N * d * 2 if fused else T * N * 4
+        return src + T * 12 + nblk * N * 8
+    if stage == "dispatch_scan":
+        return nblk * N * 12 + N * 16
+    if stage == "dispatch_scatter":
+        return T * 20 + A * 8 + 2 * dropped * d * esize
     return None
 
 
@@ -268,12 +318,31 @@ def main():
     stage_ms = {names[i]: sum(evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(args.steps))
                 / args.steps for i in range(nst)}
 
+    # Per-call wall time on the stream: an event between consecutive eager calls.
+    cev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize(dev)
+    cev[0].record(stream)
+    for k in range(args.steps):
+        step()
+        cev[k + 1].record(stream)
+    torch.cuda.synchronize(dev)
+    per_call = sorted(cev[k].elapsed_time(cev[k + 1]) for k in range(args.steps))
+
+    def pct(q):
+        return per_call[min(len(per_call) - 1, int(round(q * (len(per_call) - 1))))]
+
     acc = stats["accepted_count"].cpu()
     accepted = int(acc.sum())
     active = int((acc > 0).sum())
     dropped = int(stats["n_dropped"].cpu()[0])
     dominant = max(stage_ms, key=stage_ms.get)
-    alg = algorithmic_bytes(w, dominant, accepted, active, esize)
+    alg = algorithmic_bytes(w, dominant, accepted, active, esize, dropped)
+    stage_table = {}
+    for name, ms in stage_ms.items():
+        b = algorithmic_bytes(w, name, accepted, active, esize, dropped)
+        gbs = b / (ms * 1e-3) / 1e9 if (b and ms > 0) else None
+        stage_table[name] = {"ms": ms, "algorithmic_bytes": b, "GB_per_s": gbs,
+                             "hbm_frac": gbs / HBM_PEAK_GBS if gbs else None}
     achieved = alg / (stage_ms[dominant] * 1e-3) / 1e9 if alg else None
     gemm_flops = 4.0 * accepted * w.d * w.F
     gemm_ms = stage_ms.get("ffn1", 0.0) + stage_ms.get("ffn2", 0.0)
@@ -301,6 +370,11 @@ def main():
                      "frac": (achieved / HBM_PEAK_GBS) if achieved else None,
                      "traffic": traffic, "algorithmic_bytes": alg},
         "stages_ms": stage_ms,
+        "stages": stage_table,
+        "per_call_ms": {"median": pct(0.5), "p10": pct(0.1), "p90": pct(0.9),
+                        "note": "eager calls with an event between consecutive calls"},
+        "accepted_tokens_per_s": accepted / (ms_per_step * 1e-3),
+        "measured_peaks": measured_peaks(dev),
         "expert_gemm": {"tflops": gemm_flops / (gemm_ms * 1e-3) / 1e12 if gemm_ms else None,
                         "frac_of_bf16_mfma_peak": (gemm_flops / (gemm_ms * 1e-3) / 1e12
                                                    / MFMA_BF16_PEAK_TFLOPS) if gemm_ms else None},
