@@ -122,14 +122,14 @@ struct FfnGeom {
   // Vector-memory operations per thread, in issue order:
   static constexpr int G = AL + BL;                 // per step of a first/middle round
   static constexpr int S = NPARTS * XPT;            // epilogue stores
-  static constexpr int T1 = 1 + WN + (SECOND ? 1 : 0);  // next tile's token, bias (and gate)
+  static constexpr int T1 = SECOND ? 3 : 2;         // next tile's token, bias chunk (and gate)
   // FFN2 holds its residual rows in registers through the epilogue; it then
   // fetches the next tile's weights after the epilogue instead of during the
   // last round (its activations still go out before the epilogue).
   static constexpr bool LATE_B = SECOND;
   static constexpr int EXTRA = SECOND ? S : 0;      // FFN2 residual loads (last round, step 0)
   static constexpr int SMEM = FNB * A_BYTES + B_BYTES + 1024;
-  static constexpr bool fits = SMEM + ROWS * 8 <= kLdsBytes && part_bytes(1) <= FREE;
+  static constexpr bool fits = SMEM + ROWS * 8 + COLS * 2 <= kLdsBytes && part_bytes(1) <= FREE;
 
   // Operations this wave issued after the activation loads of step j of a
   // round of kind KIND, when that step starts; the step waits until no more
@@ -212,6 +212,7 @@ ffn_bf16_kernel(const uint16_t* __restrict__ act, uint32_t act_bytes,
   __shared__ __attribute__((aligned(1024))) char smem[Geo::SMEM];
   __shared__ int tok_s[ROWS];
   __shared__ float gate_s[ROWS];
+  __shared__ __attribute__((aligned(16))) uint16_t bias_s[COLS];
   char* const As = smem;
   uint16_t* const Bs = reinterpret_cast<uint16_t*>(smem + FNB * A_BYTES);
   char* const sink = smem + FNB * A_BYTES + Geo::B_BYTES;
@@ -229,9 +230,6 @@ ffn_bf16_kernel(const uint16_t* __restrict__ act, uint32_t act_bytes,
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int khalf = lane >> 5;
-  // This lane's column within the tile in column tile w of its wave:
-  // wave * WCOLS + w * 32 + lane % 32.
-  const int ccol0 = wave * WCOLS + (lane & 31);
   // Steps rounded up to whole pipeline rounds: the loop body is then free of
   // branches (extra steps load zeros).
   const int nk = ((K + FBK - 1) / FBK + FP - 1) / FP * FP;
@@ -243,8 +241,8 @@ ffn_bf16_kernel(const uint16_t* __restrict__ act, uint32_t act_bytes,
   const __amdgpu_buffer_rsrc_t x_src =
       make_rsrc(xres, (SECOND && !no_residual) ? (uint32_t)T * (uint32_t)d_model * 2u : 0u);
 
-  // Per-tile lookups: row token and gate (thread r: row r) and the bias of
-  // this lane's output column.
+  // Per-tile lookups: row token and gate (thread r: row r) and the tile's
+  // bias (thread i: 16-byte chunk i, staged in LDS for the epilogue).
   auto load_tok = [&](const FfnTile& dt) -> int {
     return (int)buffer_load4(tok_src, tid < dt.nrows ? (uint32_t)(dt.rbeg + tid) * 4u : kOob);
   };
@@ -252,14 +250,11 @@ ffn_bf16_kernel(const uint16_t* __restrict__ act, uint32_t act_bytes,
     return __uint_as_float(
         buffer_load4(gate_src, tid < dt.nrows ? (uint32_t)(dt.rbeg + tid) * 4u : kOob));
   };
-  auto load_bias = [&](const FfnTile& dt, uint32_t (&bv)[WN]) {
+  auto load_bias = [&](const FfnTile& dt) -> u32x4 {
     const __amdgpu_buffer_rsrc_t src =
         make_rsrc(bias ? bias + (size_t)dt.e * Nout : bias, bias ? (uint32_t)Nout * 2u : 0u);
-#pragma unroll
-    for (int w = 0; w < WN; ++w) {
-      const int n = dt.nt * COLS + ccol0 + w * 32;
-      bv[w] = buffer_load2(src, (dt.nrows > 0 && n < Nout) ? (uint32_t)n * 2u : kOob);
-    }
+    const int n = dt.nt * COLS + tid * 8;  // Nout % 8 == 0: a chunk is all in or all out
+    return buffer_load16(src, (dt.nrows > 0 && tid < COLS / 8 && n < Nout) ? (uint32_t)n * 2u : kOob);
   };
   // Weights: load i of a step brings rows 8i + lane/8 of the wave's WCOLS,
   // 16-byte chunk lane%8 of the k-step.
@@ -342,7 +337,7 @@ ffn_bf16_kernel(const uint16_t* __restrict__ act, uint32_t act_bytes,
       for (int m = 0; m < MT; ++m) {
 #pragma unroll
         for (int w = 0; w < WN; ++w)
-          acc[m * WN + w] = mfma_32x32x16(fa[q & 1][m], fb[q & 1][w], acc[m * WN + w]);
+          acc[m * WN + w] = mfma_32x32x16(fb[q & 1][w], fa[q & 1][m], acc[m * WN + w]);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -355,8 +350,7 @@ ffn_bf16_kernel(const uint16_t* __restrict__ act, uint32_t act_bytes,
   uint32_t b_off[BL];
   u32x4 rb[FP][BL];
   int my_tok = load_tok(cur);
-  uint32_t my_bias[WN];
-  load_bias(cur, my_bias);
+  u32x4 my_bias = load_bias(cur);
   float my_gate = SECOND ? load_gate(cur) : 0.f;
   setup_b(cur, rb_src, b_off);
   auto prologue_b = [&]() {
@@ -399,12 +393,12 @@ ffn_bf16_kernel(const uint16_t* __restrict__ act, uint32_t act_bytes,
       tok_s[tid] = my_tok;  // visible after the first step's barrier
       gate_s[tid] = my_gate;
     }
+    if (tid < COLS / 8) store16(bias_s + tid * 8, my_bias);
     // The next tile and its lookups, in flight through this tile.
     FfnTile nxt{cur.e, cur.nt, 0, 0};
     const int tn = find_tile<ROWS>(t + stride, stride, n_tiles, n_ntiles, n_mchunks, offset, nxt);
     const int tok_n = load_tok(nxt);
-    uint32_t bias_n[WN];
-    load_bias(nxt, bias_n);
+    const u32x4 bias_n = load_bias(nxt);
     const float gate_n = SECOND ? load_gate(nxt) : 0.f;
     __amdgpu_buffer_rsrc_t rb_src_n;
     uint32_t b_off_n[BL];
@@ -473,24 +467,35 @@ ffn_bf16_kernel(const uint16_t* __restrict__ act, uint32_t act_bytes,
 #pragma unroll
     for (int p = 0; p < NPARTS; ++p) {
       if (wave / WPP == p) {
-        // Lane geometry from the opaque index: per-element staging addresses
-        // stay immediates off one per-tile base instead of hoisted registers.
+        // The matrix-core result is C^T: lane l holds row l%32 of row tile m
+        // and, for value 4g + j, column 8g + 4*(l/32) + j of column tile w --
+        // four consecutive columns per g, staged as one 8- or 16-byte write.
+        // Lane geometry from the opaque index keeps the staging addresses
+        // immediates off one per-tile base.
         const int elane = etid & 63;
         const int ekh = elane >> 5;
+        const int er = elane & 31;
 #pragma unroll
         for (int w = 0; w < WN; ++w) {
-          const float bv = bf16_bits_to_f32(my_bias[w]);
-          const int pc = wave * WCOLS + (elane & 31) + w * 32 - p * PCOLS;
 #pragma unroll
-          for (int m = 0; m < MT; ++m) {
+          for (int g = 0; g < 4; ++g) {
+            const int cw = wave * WCOLS + w * 32 + 8 * g + 4 * ekh;  // column within the tile
+            const u32x2 bb = *reinterpret_cast<const u32x2*>(bias_s + cw);
+            const float b0 = bf16_bits_to_f32(bb[0] & 0xffffu), b1 = bf16_bits_to_f32(bb[0] >> 16);
+            const float b2 = bf16_bits_to_f32(bb[1] & 0xffffu), b3 = bf16_bits_to_f32(bb[1] >> 16);
+            const int pc = cw - p * PCOLS;
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-              const int r = m * 32 + (v >> 2) * 8 + ekh * 4 + (v & 3);
-              if (SECOND)
-                reinterpret_cast<float*>(stage)[r * CST + pc] = acc[m * WN + w][v] + bv;
-              else  // H: bias, ReLU, one rounding to bf16
-                reinterpret_cast<uint16_t*>(stage)[r * CST + pc] =
-                    (uint16_t)f32_to_bf16_bits(fmaxf(acc[m * WN + w][v] + bv, 0.f));
+            for (int m = 0; m < MT; ++m) {
+              const f32x16& a = acc[m * WN + w];
+              const int r = m * 32 + er;
+              if (SECOND) {
+                *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(stage) + r * CST + pc) =
+                    f32x4{a[4 * g] + b0, a[4 * g + 1] + b1, a[4 * g + 2] + b2, a[4 * g + 3] + b3};
+              } else {  // H: bias, ReLU, one rounding to bf16
+                *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(stage) + r * CST + pc) =
+                    u32x2{pack_bf16x2(fmaxf(a[4 * g] + b0, 0.f), fmaxf(a[4 * g + 1] + b1, 0.f)),
+                          pack_bf16x2(fmaxf(a[4 * g + 2] + b2, 0.f), fmaxf(a[4 * g + 3] + b3, 0.f))};
+              }
             }
           }
         }
@@ -521,7 +526,7 @@ ffn_bf16_kernel(const uint16_t* __restrict__ act, uint32_t act_bytes,
           for (int j = 0; j < 4; ++j) {
             const float lo = g * val[2 * j] + bf16_bits_to_f32(xr[p][i][j] & 0xffffu);
             const float hi = g * val[2 * j + 1] + bf16_bits_to_f32(xr[p][i][j] >> 16);
-            yr[j] = f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+            yr[j] = pack_bf16x2(lo, hi);
           }
           __builtin_amdgcn_raw_buffer_store_b128(
               yr, out_src,
@@ -544,8 +549,7 @@ ffn_bf16_kernel(const uint16_t* __restrict__ act, uint32_t act_bytes,
     cur = nxt;
     t = tn;
     my_tok = tok_n;
-#pragma unroll
-    for (int w = 0; w < WN; ++w) my_bias[w] = bias_n[w];
+    my_bias = bias_n;
     my_gate = gate_n;
     rb_src = rb_src_n;
 #pragma unroll

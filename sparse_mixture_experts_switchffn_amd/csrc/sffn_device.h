@@ -30,6 +30,15 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> bf16 (round to nearest, ties to even; one v_cvt_pk_bf16_f32),
+// lo in the low half.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+}
+
 // D = A(32x16) * B(16x32) + C on the matrix cores.  Lane l supplies
 // A[l%32][8*(l/32) + 0..7] and B[8*(l/32) + 0..7][l%32]; the 16 results of
 // lane l are C[8*(v/4) + 4*(l/32) + v%4][l%32], v = 0..15.
