@@ -73,25 +73,6 @@ constexpr int kLdsBytes = 160 * 1024;
 // the last (whose loads fetch the next tile; it may also be the first).
 enum : int { kRoundFirst = 0, kRoundMid = 1, kRoundLast = 2 };
 
-template <int I, int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (I < N) {
-    f(std::integral_constant<int, I>{});
-    static_for<I + 1, N>(f);
-  }
-}
-
-// Wait until at most N vector-memory operations of this wave are outstanding
-// (gfx9 encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt left at
-// their maxima, i.e. not waited for).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  constexpr int n = N < 0 ? 0 : (N > 63 ? 63 : N);
-  __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
-  __builtin_amdgcn_sched_barrier(0);
-}
-
 template <int MT, int FW, int WN, bool SECOND>
 struct FfnGeom {
   static constexpr int ROWS = MT * 32;
@@ -181,15 +162,6 @@ __device__ __forceinline__ int find_tile(int t, int stride, int n_tiles, int n_n
 }
 
 #define SFFN_LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
-
-// Workgroup barrier of the grouped GEMM.  An LDS fence would make the
-// compiler wait for every load still writing LDS (all FP steps in flight);
-// those are waited for explicitly instead, so this only completes the wave's
-// own LDS accesses and meets the other waves.  The memory clobber keeps the
-// compiler from moving any memory access across it.
-__device__ __forceinline__ void ffn_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
 
 template <int MT, int FW, int WN, bool SECOND, int WPOL>
 __global__ void __launch_bounds__(FW * 64)
@@ -363,7 +335,7 @@ ffn_bf16_kernel(const uint16_t* __restrict__ act, uint32_t act_bytes,
   if (!Geo::LATE_B) prologue_b();
   if (!SECOND) {
     if (tid < ROWS) tok_s[tid] = my_tok;
-    ffn_barrier();
+    dma_barrier();
   }
   setup_a(cur);
 #pragma unroll
@@ -426,7 +398,7 @@ ffn_bf16_kernel(const uint16_t* __restrict__ act, uint32_t act_bytes,
       constexpr int J = decltype(j_c)::value;
       const int k = ks + J;
       wait_vmcnt<Geo::template step_wait<KIND, J>()>();  // this wave's A(k) is in LDS
-      ffn_barrier();                                      // everyone's; ring tile k-1 is free
+      dma_barrier();                                      // everyone's; ring tile k-1 is free
       compute(k % FNB, rb[J]);
       if constexpr (KIND == kRoundFirst || KIND == kRoundMid) {
         dma_a((k + FP) % FNB, k + FP);  // zero past the end of K
@@ -454,7 +426,7 @@ ffn_bf16_kernel(const uint16_t* __restrict__ act, uint32_t act_bytes,
     // The next tile's activation rows (ring tiles 0 .. FP-1), once every wave
     // is past its last read of the ring.
     if (!SECOND && tid < ROWS) tok_s[tid] = tok_n;
-    ffn_barrier();
+    dma_barrier();
     setup_a(nxt);
 #pragma unroll
     for (int s = 0; s < FP; ++s) {
@@ -500,7 +472,7 @@ ffn_bf16_kernel(const uint16_t* __restrict__ act, uint32_t act_bytes,
           }
         }
       }
-      ffn_barrier();
+      dma_barrier();
 #pragma unroll
       for (int i = 0; i < XPT; ++i) {
         const int idx = etid + i * NTHR;
@@ -534,7 +506,7 @@ ffn_bf16_kernel(const uint16_t* __restrict__ act, uint32_t act_bytes,
               kCpolNonTemporal);
         }
       }
-      ffn_barrier();
+      dma_barrier();
     }
 
     if (tn >= n_tiles) break;

@@ -401,6 +401,170 @@ router_fused_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__
   }
 }
 
+// ---------------------------------------------------------------------------
+// Logits for many experts (N > 128, N % 4 == 0), bf16 token states: the same
+// exact three-plane product, tiled for the matrix cores.
+//
+// A block of 8 waves computes 128 experts x 384 tokens; wave w takes expert
+// half w%2 (two 32-expert tiles) and token quarter w/2 (three 32-token tiles),
+// so each 16-k sub-step is 18 matrix-core ops on 6 plane and 3 token
+// fragments.  Both operands go from memory straight into LDS rings with
+// buffer loads that write LDS, 32 k per step:
+//   * planes (fragment order, from router_planes_kernel): 24 KB a step, one
+//     1 KB fragment per instruction; each lane reads back the 16 bytes it
+//     loaded, so the reads need no swizzle.
+//   * token rows: 384 x 64 B a step, 16 rows per instruction; the four 16-byte
+//     chunks of row r are stored XOR-swizzled by (r/4)%4 so the operand reads
+//     (32 rows, one chunk) spread over the banks.
+// Three ring slots each: step k computes, then issues the loads of step k+2,
+// so at its start everything but the loads of step k+1 must have landed: a
+// fixed wait, then a barrier that completes LDS accesses only (the loads are
+// issued after the step's LDS reads, which keeps the compiler from waiting
+// for them there).
+// Blocks are ordered token tile -> expert group with XCD-contiguous ids: the
+// blocks running together on one XCD share their token tiles in its L2.
+// ---------------------------------------------------------------------------
+constexpr int RL_WAVES = 8;
+constexpr int RL_TOK = 384;                   // tokens per block
+constexpr int RL_TN = RL_TOK / 128;           // 32-token tiles per wave
+constexpr int RL_EXP = 128;                   // experts per block
+constexpr int RL_PSLOT = 24 * 1024;           // plane bytes per step: 3 planes x 4 tiles x 2 q
+constexpr int RL_XSLOT = RL_TOK * 64;         // token bytes per step
+constexpr int RL_NB = 3;                      // ring slots (two steps in flight)
+constexpr int RL_PLD = 24 / RL_WAVES;         // plane loads per wave per step
+constexpr int RL_XLD = RL_TOK / 16 / RL_WAVES;  // token loads per wave per step
+
+__global__ void __launch_bounds__(RL_WAVES * 64)
+router_logits_mfma_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ planes,
+                          uint32_t planes_bytes, int T, int d, int N, int MTp, int nks,
+                          float* __restrict__ logits) {
+  // One LDS object for both rings (the compiler then leaves the waits for the
+  // loads that write it to the explicit ones below).
+  __shared__ __attribute__((aligned(1024))) char ring[RL_NB * (RL_PSLOT + RL_XSLOT)];
+  char* const pring = ring;
+  char* const xring = ring + RL_NB * RL_PSLOT;
+  const int n_eg = MTp / 4;
+  const int tile = xcd_contiguous_tile(blockIdx.x, gridDim.x);
+  const int eg = tile % n_eg;  // expert group fastest: the blocks of one token tile sit together
+  const int tt = tile / n_eg;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int khalf = lane >> 5;
+  const int t0 = tt * RL_TOK;
+
+  const __amdgpu_buffer_rsrc_t rp = make_rsrc(planes, planes_bytes);
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, (uint32_t)((size_t)T * d * 2));
+  const __amdgpu_buffer_rsrc_t rz = make_rsrc(logits, (uint32_t)((size_t)T * N * 4));
+
+  // Plane loads: fragment f = wave*PLD + i of a step is (plane f/8, tile
+  // (f/2)%4, q f%2) and sits at f KB of the slot.
+  const uint32_t pstep = (uint32_t)(3 * MTp * 2) * 1024u;
+  uint32_t p_off[RL_PLD];
+#pragma unroll
+  for (int i = 0; i < RL_PLD; ++i) {
+    const int f = wave * RL_PLD + i;
+    p_off[i] = (uint32_t)(((f / 8) * MTp + 4 * eg + (f / 2) % 4) * 2 + f % 2) * 1024u + (uint32_t)lane * 16u;
+  }
+  // Token loads: instruction j = wave*XLD + i of a step covers rows 16 j ..
+  // 16 j + 15; lane l fills row 16 j + l/4, stored chunk l%4, which holds
+  // logical chunk (l%4) ^ ((row/4)%4) = k 8c .. 8c+7 of the step.  Rows past
+  // T are pushed past the end of x (offsets stay below 2^32).
+  uint32_t x_row[RL_XLD];
+  int x_k[RL_XLD];
+#pragma unroll
+  for (int i = 0; i < RL_XLD; ++i) {
+    const int r = 16 * (wave * RL_XLD + i) + (lane >> 2);
+    const int t = t0 + r;
+    x_row[i] = t < T ? (uint32_t)t * (uint32_t)d * 2u : kOob;
+    x_k[i] = 8 * ((lane & 3) ^ ((r >> 2) & 3));
+  }
+  auto dma_p = [&](int k) {
+    char* slot = pring + (k % RL_NB) * RL_PSLOT;
+#pragma unroll
+    for (int i = 0; i < RL_PLD; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rp, (__attribute__((address_space(3))) void*)(slot + (wave * RL_PLD + i) * 1024), 16,
+          (int)((uint32_t)k * pstep + p_off[i]), 0, 0, 0);
+  };
+  auto dma_x = [&](int k) {
+    char* slot = xring + (k % RL_NB) * RL_XSLOT;
+#pragma unroll
+    for (int i = 0; i < RL_XLD; ++i) {
+      const int kk = 32 * k + x_k[i];
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rx, (__attribute__((address_space(3))) void*)(slot + (wave * RL_XLD + i) * 1024), 16,
+          (int)(kk < d ? x_row[i] + (uint32_t)kk * 2u : kOob), 0, 0, 0);
+    }
+  };
+
+  // Operand reads: planes of tiles 2 (w%2) + m, tokens of tiles 3 (w/2) + n;
+  // sub-step q (k = 16 khalf + 8 q + 0..7 of the step in lane half khalf).
+  const int we = wave & 1, wt = wave >> 1;
+  const uint32_t p_rd = (uint32_t)lane * 16u;
+  const uint32_t x_rd = (uint32_t)(wt * RL_TN * 32 + (lane & 31)) * 64u;
+  const int xsw = (lane >> 2) & 3;  // (row/4)%4 of every row this lane reads
+  f32x16 acc[2][RL_TN];
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int n = 0; n < RL_TN; ++n) acc[m][n] = f32x16{};
+  auto compute = [&](int k) {
+    const char* ps = pring + (k % RL_NB) * RL_PSLOT + p_rd;
+    const char* xs = xring + (k % RL_NB) * RL_XSLOT + x_rd;
+    bf16x8 pf[3][2], xf[RL_TN];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+#pragma unroll
+      for (int p = 0; p < 3; ++p)
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+          pf[p][m] = as_bf16x8(load16(ps + ((p * 4 + 2 * we + m) * 2 + q) * 1024));
+      const int xc = ((2 * khalf + q) ^ xsw) * 16;
+#pragma unroll
+      for (int n = 0; n < RL_TN; ++n) xf[n] = as_bf16x8(load16(xs + n * 32 * 64 + xc));
+#pragma unroll
+      for (int p = 0; p < 3; ++p)
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+          for (int n = 0; n < RL_TN; ++n) acc[m][n] = mfma_32x32x16(pf[p][m], xf[n], acc[m][n]);
+    }
+  };
+
+  dma_x(0);
+  dma_p(0);
+  dma_x(1);
+  dma_p(1);
+  for (int k = 0; k < nks; ++k) {
+    wait_vmcnt<RL_XLD + RL_PLD>();  // all but the loads of step k+1 have landed
+    dma_barrier();                  // everyone's; the slots of step k-1 are free
+    compute(k);
+    dma_x(k + 2);  // zero past the end of d
+    dma_p(k + 2);
+  }
+
+  // Logits: lane holds, for tiles (m, n), token t0 + 96 (w/2) + 32 n + lane%32
+  // and experts 128 eg + 64 (w%2) + 32 m + 8 g + 4 khalf + 0..3 in values 4g..4g+3.
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int n = 0; n < RL_TN; ++n) {
+      const int t = t0 + wt * RL_TN * 32 + 32 * n + (lane & 31);
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int e = eg * RL_EXP + we * 64 + 32 * m + 8 * g + 4 * khalf;
+        const f32x4 v = f32x4{acc[m][n][4 * g], acc[m][n][4 * g + 1], acc[m][n][4 * g + 2],
+                              acc[m][n][4 * g + 3]};
+        __builtin_amdgcn_raw_buffer_store_b128(
+            __builtin_bit_cast(u32x4, v), rz,
+            (int)(((t < T) & (e < N)) ? ((uint32_t)t * (uint32_t)N + (uint32_t)e) * 4u : kOob), 0, 0);
+      }
+    }
+  // The last ring loads (zeros past the end of d) still write LDS.
+  wait_vmcnt<0>();
+}
+
+// ---------------------------------------------------------------------------
 // Logits for fp32 token states: one thread per (token, expert), fp32 FMA in k order.
 __global__ void __launch_bounds__(256)
 router_logits_f32_kernel(const float* __restrict__ x, const float* __restrict__ Wr,
@@ -418,6 +582,24 @@ router_logits_f32_kernel(const float* __restrict__ x, const float* __restrict__ 
 
 bool router_is_fused(const Shape& s) { return s.dtype == SFFN_BF16 && s.N <= 128; }
 
+// Many-expert logits on the matrix cores: planes for 64-k steps and 64-expert
+// groups (zero-padded), offsets of the staged logits and of the planes below
+// 2^31 so that the range-checked placeholder offset stays out of range.
+static size_t tiled_planes_bytes(const Shape& s) {
+  const size_t nks = (size_t)(s.d + 31) / 32;
+  const size_t mtp = 4 * (size_t)((s.N + RL_EXP - 1) / RL_EXP);
+  return nks * 3 * mtp * 2 * 1024;
+}
+
+static bool logits_fit_offsets(const Shape& s) {
+  return (size_t)s.T * (size_t)s.N * 4 < ((size_t)1 << 31);
+}
+
+static bool router_is_tiled(const Shape& s) {
+  return s.dtype == SFFN_BF16 && s.N > 128 && s.N % 4 == 0 && logits_fit_offsets(s) &&
+         tiled_planes_bytes(s) < ((size_t)1 << 31) - ((size_t)8 << 20);
+}
+
 hipError_t launch_router_logits(const Shape& s, const Inputs& in, const Workspace& ws,
                                 hipStream_t st) {
   if (s.dtype == SFFN_FP32) {
@@ -428,11 +610,25 @@ hipError_t launch_router_logits(const Shape& s, const Inputs& in, const Workspac
     return hipGetLastError();
   }
   if (router_is_fused(s)) return hipSuccess;  // done by launch_softmax_route
+  const uint16_t* x = (const uint16_t*)in.x;
+  if (router_is_tiled(s)) {
+    const int mtp = 4 * ((s.N + RL_EXP - 1) / RL_EXP);
+    const int nks = (s.d + 31) / 32;
+    const int groups = nks * mtp * 2 * 64;
+    hipLaunchKernelGGL(router_planes_kernel, dim3((unsigned)((groups + 255) / 256)), dim3(256), 0,
+                       st, in.Wr, s.d, s.N, mtp, nks, ws.planes);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int n_tt = (s.T + RL_TOK - 1) / RL_TOK;
+    hipLaunchKernelGGL(router_logits_mfma_kernel, dim3((unsigned)(n_tt * (mtp / 4))),
+                       dim3(RL_WAVES * 64), 0, st, x, ws.planes, (uint32_t)tiled_planes_bytes(s),
+                       s.T, s.d, s.N, mtp, nks, ws.logits);
+    return hipGetLastError();
+  }
   const int ttiles = (s.T + RW_WAVES * 32 - 1) / (RW_WAVES * 32);
   const int rm = s.N >= 128 ? 4 : (s.N + 31) / 32;
   const int etiles = (s.N + rm * 32 - 1) / (rm * 32);
   const dim3 grid((unsigned)(ttiles * etiles));
-  const uint16_t* x = (const uint16_t*)in.x;
   switch (rm) {
     case 1: hipLaunchKernelGGL(router_logits_bf16_kernel<1>, grid, dim3(RW_WAVES * 64), 0, st, x, in.Wr, ws.logits, s.T, s.d, s.N); break;
     case 2: hipLaunchKernelGGL(router_logits_bf16_kernel<2>, grid, dim3(RW_WAVES * 64), 0, st, x, in.Wr, ws.logits, s.T, s.d, s.N); break;
@@ -560,9 +756,129 @@ softmax_route_kernel(const float* __restrict__ logits, int T, int N,
   for (int i = threadIdx.x; i < N; i += 256) cnt[(size_t)b * N + i] = cnt_s[i];
 }
 
+// ---------------------------------------------------------------------------
+// The same for N % 4 == 0 with 16-byte loads: lane l of a wave holds experts
+// 4 (64 q + l) + c, c = 0..3, q = 0..NQ-1, so one load instruction of a wave
+// covers 1 KB of a logit row.  A wave routes every 4th token of the block and
+// has the next one's row in flight; the expert order within a lane rises with
+// (q, c), so the first strict maximum is the lowest index of the lane's maxima.
+// Sums: per lane in (q, c) order, then a fixed butterfly across the wave; p
+// sums over the block: per lane in token order, then the four waves in order.
+// ---------------------------------------------------------------------------
+template <int NQ>
+__global__ void __launch_bounds__(256)
+softmax_route_vec_kernel(const float* __restrict__ logits, int T, int N,
+                         int32_t* __restrict__ expert_idx, float* __restrict__ gate,
+                         float* __restrict__ ppart, int* __restrict__ cnt, int* __restrict__ lrank) {
+  constexpr int WAVES = 4;
+  __shared__ __attribute__((aligned(16))) float pacc[WAVES][NQ * 256];
+  __shared__ int eid_s[kRouteTokens];
+  __shared__ int cnt_s[NQ * 256];
+
+  const int b = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int tb = b * kRouteTokens;
+  const __amdgpu_buffer_rsrc_t src = make_rsrc(logits, (uint32_t)((size_t)T * N * 4));
+
+  for (int i = threadIdx.x; i < NQ * 256; i += 256) cnt_s[i] = 0;
+
+  f32x4 acc[NQ];
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto fetch = [&](int j, u32x4 (&v)[NQ]) {
+    const int t = tb + j;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const int i = 4 * (64 * q + lane);
+      v[q] = buffer_load16(src, (t < T && i < N) ? ((uint32_t)t * (uint32_t)N + (uint32_t)i) * 4u : kOob);
+    }
+  };
+  u32x4 vn[NQ];
+  fetch(wave, vn);
+  for (int j = wave; j < kRouteTokens; j += WAVES) {
+    const int t = tb + j;
+    f32x4 v[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) v[q] = __builtin_bit_cast(f32x4, vn[q]);
+    if (j + WAVES < kRouteTokens) fetch(j + WAVES, vn);
+    if (t >= T) {
+      if (lane == 0) eid_s[j] = -1;
+      continue;
+    }
+    float m = -INFINITY;
+    int arg = 0x7fffffff;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int i = 4 * (64 * q + lane) + c;
+        if (i < N && v[q][c] > m) {
+          m = v[q][c];
+          arg = i;
+        }
+      }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float om = __shfl_xor(m, off);
+      const int oa = __shfl_xor(arg, off);
+      if (om > m || (om == m && oa < arg)) {
+        m = om;
+        arg = oa;
+      }
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        v[q][c] = (4 * (64 * q + lane) + c < N) ? expf(v[q][c] - m) : 0.f;
+        s += v[q][c];
+      }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+    const float inv = 1.0f / s;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc[q][c] += v[q][c] * inv;
+    if (lane == 0) {
+      expert_idx[t] = arg;
+      gate[t] = inv;
+      eid_s[j] = arg;
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < NQ; ++q)
+    *reinterpret_cast<f32x4*>(&pacc[wave][4 * (64 * q + lane)]) = acc[q];
+  __syncthreads();
+
+  for (int i4 = threadIdx.x; 4 * i4 < N; i4 += 256) {
+    const int i = 4 * i4;
+    f32x4 p = *reinterpret_cast<const f32x4*>(&pacc[0][i]);
+#pragma unroll
+    for (int w = 1; w < WAVES; ++w) p += *reinterpret_cast<const f32x4*>(&pacc[w][i]);
+    *reinterpret_cast<f32x4*>(ppart + (size_t)b * N + i) = p;
+  }
+  if (threadIdx.x < kRouteTokens) {
+    const int j = threadIdx.x;
+    const int e = eid_s[j];
+    if (e >= 0) {
+      int r = 0;
+      for (int s2 = 0; s2 < j; ++s2) r += (eid_s[s2] == e);
+      lrank[tb + j] = r;
+      atomicAdd(&cnt_s[e], 1);
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < N; i += 256) cnt[(size_t)b * N + i] = cnt_s[i];
+}
+
 int router_plane_tiles(int N) { return (N + 31) / 32; }
 
 size_t router_planes_bytes(const Shape& s) {
+  if (router_is_tiled(s)) return tiled_planes_bytes(s);
   if (!router_is_fused(s)) return 0;
   const size_t nks = (size_t)(s.d + FR_BK - 1) / FR_BK;
   return nks * 3 * (size_t)router_plane_tiles(s.N) * 2 * 1024;
@@ -597,8 +913,21 @@ hipError_t launch_softmax_route(const Shape& s, const Inputs& in, const Workspac
                                 const Outputs& out, hipStream_t st) {
   if (router_is_fused(s)) return launch_router_fused(s, in, ws, out, st);
   const dim3 grid((unsigned)s.n_route_blocks), block(256);
+  if (s.N % 4 == 0 && logits_fit_offsets(s)) {
+    const int nq = (s.N + 255) / 256;
+#define SFFN_SOFTMAX_VEC(K)                                                                      \
+  hipLaunchKernelGGL(softmax_route_vec_kernel<K>, grid, block, 0, st, ws.logits, s.T, s.N,       \
+                     out.expert_idx, out.gate, ws.ppart, ws.cnt, ws.lrank)
+    if (nq <= 1) SFFN_SOFTMAX_VEC(1);
+    else if (nq <= 2) SFFN_SOFTMAX_VEC(2);
+    else if (nq <= 4) SFFN_SOFTMAX_VEC(4);
+    else if (nq <= 8) SFFN_SOFTMAX_VEC(8);
+    else SFFN_SOFTMAX_VEC(16);
+#undef SFFN_SOFTMAX_VEC
+    return hipGetLastError();
+  }
   const int npl = (s.N + 63) / 64;
-#define SFFN_SOFTMAX(K)                                                                          \
+#define SFFN_SOFTMAX(K)                                                                         \
   hipLaunchKernelGGL(softmax_route_kernel<K>, grid, block, 0, st, ws.logits, s.T, s.N,           \
                      out.expert_idx, out.gate, ws.ppart, ws.cnt, ws.lrank)
   if (npl <= 1) SFFN_SOFTMAX(1);

@@ -92,6 +92,35 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding
+// (gfx9 encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt left at
+// their maxima, i.e. not waited for).  Loads that write LDS are not tracked
+// by the compiler's wait insertion; kernels that issue them wait with this.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  constexpr int n = N < 0 ? 0 : (N > 63 ? 63 : N);
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Workgroup barrier for kernels with loads that write LDS in flight.  An LDS
+// fence would make the compiler wait for every such load (all pipeline steps
+// in flight); those are waited for explicitly instead, so this only completes
+// the wave's own LDS accesses and meets the other waves.  The memory clobber
+// keeps the compiler from moving any memory access across it.
+__device__ __forceinline__ void dma_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 __device__ __forceinline__ u32x4 load16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }

@@ -66,7 +66,10 @@ def test_tiny_fp32():
     dict(T=1, d=16, F=24, N=3, CF=1.0),                          # a single token (C = 0)
     dict(T=2, d=16, F=24, N=2, CF=2.0, bias_sigma=0.02),         # two tokens, C = 2
     dict(T=2048, d=64, F=96, N=4, CF=1.0),                       # C = 512: two row chunks
-    dict(T=1000, d=128, F=256, N=130, CF=1.5),                   # N > 128: partial expert tile
+    dict(T=1000, d=128, F=256, N=130, CF=1.5),                   # N > 128, N % 4 != 0: scalar path
+    dict(T=1100, d=200, F=64, N=260, CF=2.0, bias_sigma=0.02),   # tiled logits: partial group, k tail
+    dict(T=530, d=2080, F=32, N=132, CF=4.0),                    # tiled logits: odd step count, ragged T
+    dict(T=300, d=72, F=16, N=4096, CF=16.0),                    # the most experts: widest softmax
     dict(T=700, d=2080, F=64, N=7, CF=1.0),                      # d = 2080 (32 x 65) K tail
     dict(T=640, d=256, F=512, N=16, CF=0.5, bias_sigma=0.05),    # heavy dropping
 ])
