@@ -61,7 +61,9 @@ namespace sffn {
 // not kept in the caches).  The results are stored non-temporal (FFN2 reads
 // H back, but keeping the dirty lines in L2 costs more than re-reading them);
 // the weights are loaded non-temporal when each weight byte is read once (one
-// row chunk per expert), and cached when row chunks re-read them.
+// row chunk per expert) and every weight row starts on a 128-byte line, and
+// cached otherwise: row chunks re-read them, and with rows off the line grid
+// a k-step reads half of a line whose other half the next step reads.
 constexpr int kCpolNonTemporal = 2;
 constexpr int FBK = 64;              // k per step (one 128-byte chunk row)
 constexpr int FLDS = FBK + 8;        // bf16 per row of a weight slot (144 B: rows 4 banks apart)
@@ -597,9 +599,8 @@ template <int MT, int FW, int WN, bool SECOND>
 static void launch_ffn_bf16_t(const FfnArgs& a, hipStream_t st) {
   if constexpr (ffn_shape_ok<MT, FW, WN, SECOND>()) {
     const dim3 grid((unsigned)ffn_grid<MT, FW, WN, SECOND>(a)), block(FW * 64);
-    // Weights are streamed past the caches when no other row chunk re-reads
-    // them; single-row-tile blocks keep them cached (measured faster there).
-    if (a.n_mchunks == 1 && MT >= 2)
+    // Weights are streamed past the caches when nothing re-reads their lines.
+    if (a.n_mchunks == 1 && (a.K * 2) % 128 == 0)
       hipLaunchKernelGGL((ffn_bf16_kernel<MT, FW, WN, SECOND, kCpolNonTemporal>), grid, block, 0, st,
                          a.act, a.act_bytes, a.W, a.bias, a.offset, a.row2tok, a.rowgate, a.xres,
                          a.out, a.out_bytes, a.K, a.Nout, a.n_mchunks, a.n_experts, a.max_rows,

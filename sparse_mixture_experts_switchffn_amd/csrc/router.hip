@@ -421,8 +421,9 @@ router_fused_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__
 // fixed wait, then a barrier that completes LDS accesses only (the loads are
 // issued after the step's LDS reads, which keeps the compiler from waiting
 // for them there).
-// Blocks are ordered token tile -> expert group with XCD-contiguous ids: the
-// blocks running together on one XCD share their token tiles in its L2.
+// Block order: tiles are grouped in runs of 8 token tiles x 4 expert groups
+// (expert group fastest, XCD-contiguous ids), so the blocks running together
+// on one XCD share both their token rows and their planes in its L2.
 // ---------------------------------------------------------------------------
 constexpr int RL_WAVES = 8;
 constexpr int RL_TOK = 384;                   // tokens per block
@@ -444,9 +445,17 @@ router_logits_mfma_kernel(const uint16_t* __restrict__ x, const uint16_t* __rest
   char* const pring = ring;
   char* const xring = ring + RL_NB * RL_PSLOT;
   const int n_eg = MTp / 4;
-  const int tile = xcd_contiguous_tile(blockIdx.x, gridDim.x);
-  const int eg = tile % n_eg;  // expert group fastest: the blocks of one token tile sit together
-  const int tt = tile / n_eg;
+  const int n_tt = (T + RL_TOK - 1) / RL_TOK;
+  const int egc = (n_eg % 4 == 0) ? 4 : (n_eg % 2 == 0 ? 2 : 1);  // expert groups per run
+  int tt, eg;
+  {
+    const int tile = xcd_contiguous_tile(blockIdx.x, gridDim.x);
+    const int row = tile / (8 * n_eg), rem = tile % (8 * n_eg);
+    const int rows = min(8, n_tt - row * 8);
+    const int chunk = rem / (rows * egc), inner = rem % (rows * egc);
+    tt = row * 8 + inner / egc;
+    eg = chunk * egc + inner % egc;
+  }
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int khalf = lane >> 5;
