@@ -405,15 +405,16 @@ router_fused_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__
 // Logits for many experts (N > 128, N % 4 == 0), bf16 token states: the same
 // exact three-plane product, tiled for the matrix cores.
 //
-// A block of 8 waves computes 128 experts x 384 tokens; wave w takes expert
-// half w%2 (two 32-expert tiles) and token quarter w/2 (three 32-token tiles),
-// so each 16-k sub-step is 18 matrix-core ops on 6 plane and 3 token
-// fragments.  Both operands go from memory straight into LDS rings with
+// A block of 8 waves computes 128 experts x 128 TN tokens; wave w takes
+// expert half w%2 (two 32-expert tiles) and token quarter w/2 (TN 32-token
+// tiles), so each 16-k sub-step is 6 TN matrix-core ops on 6 plane and TN
+// token fragments (TN = 3 for many experts, 1 for 128 experts, where fewer
+// tokens per block keep every CU busy).  Both operands go from memory straight into LDS rings with
 // buffer loads that write LDS, 32 k per step:
 //   * planes (fragment order, from router_planes_kernel): 24 KB a step, one
 //     1 KB fragment per instruction; each lane reads back the 16 bytes it
 //     loaded, so the reads need no swizzle.
-//   * token rows: 384 x 64 B a step, 16 rows per instruction; the four 16-byte
+//   * token rows: 128 TN x 64 B a step, 16 rows per instruction; the four 16-byte
 //     chunks of row r are stored XOR-swizzled by (r/4)%4 so the operand reads
 //     (32 rows, one chunk) spread over the banks.
 // Three ring slots each: step k computes, then issues the loads of step k+2,
@@ -426,19 +427,20 @@ router_fused_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__
 // on one XCD share both their token rows and their planes in its L2.
 // ---------------------------------------------------------------------------
 constexpr int RL_WAVES = 8;
-constexpr int RL_TOK = 384;                   // tokens per block
-constexpr int RL_TN = RL_TOK / 128;           // 32-token tiles per wave
 constexpr int RL_EXP = 128;                   // experts per block
 constexpr int RL_PSLOT = 24 * 1024;           // plane bytes per step: 3 planes x 4 tiles x 2 q
-constexpr int RL_XSLOT = RL_TOK * 64;         // token bytes per step
 constexpr int RL_NB = 3;                      // ring slots (two steps in flight)
 constexpr int RL_PLD = 24 / RL_WAVES;         // plane loads per wave per step
-constexpr int RL_XLD = RL_TOK / 16 / RL_WAVES;  // token loads per wave per step
 
+template <int TN>
 __global__ void __launch_bounds__(RL_WAVES * 64)
 router_logits_mfma_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ planes,
                           uint32_t planes_bytes, int T, int d, int N, int MTp, int nks,
                           float* __restrict__ logits) {
+  constexpr int RL_TOK = 128 * TN;                // tokens per block
+  constexpr int RL_TN = TN;                       // 32-token tiles per wave
+  constexpr int RL_XSLOT = RL_TOK * 64;           // token bytes per step
+  constexpr int RL_XLD = RL_TOK / 16 / RL_WAVES;  // token loads per wave per step
   // One LDS object for both rings (the compiler then leaves the waits for the
   // loads that write it to the explicit ones below).
   __shared__ __attribute__((aligned(1024))) char ring[RL_NB * (RL_PSLOT + RL_XSLOT)];
@@ -552,7 +554,7 @@ router_logits_mfma_kernel(const uint16_t* __restrict__ x, const uint16_t* __rest
     dma_p(k + 2);
   }
 
-  // Logits: lane holds, for tiles (m, n), token t0 + 96 (w/2) + 32 n + lane%32
+  // Logits: lane holds, for tiles (m, n), token t0 + 32 TN (w/2) + 32 n + lane%32
   // and experts 128 eg + 64 (w%2) + 32 m + 8 g + 4 khalf + 0..3 in values 4g..4g+3.
 #pragma unroll
   for (int m = 0; m < 2; ++m)
@@ -589,9 +591,7 @@ router_logits_f32_kernel(const float* __restrict__ x, const float* __restrict__ 
   logits[idx] = s;
 }
 
-bool router_is_fused(const Shape& s) { return s.dtype == SFFN_BF16 && s.N <= 128; }
-
-// Many-expert logits on the matrix cores: planes for 64-k steps and 64-expert
+// Many-expert logits on the matrix cores: planes for 32-k steps and 128-expert
 // groups (zero-padded), offsets of the staged logits and of the planes below
 // 2^31 so that the range-checked placeholder offset stays out of range.
 static size_t tiled_planes_bytes(const Shape& s) {
@@ -604,9 +604,18 @@ static bool logits_fit_offsets(const Shape& s) {
   return (size_t)s.T * (size_t)s.N * 4 < ((size_t)1 << 31);
 }
 
+// The tiled router (logits staged in HBM, then the softmax pass) for many
+// experts, and for 128-expert-scale layers with enough tokens to give every
+// CU a 128-token block, where the fused router would fetch the planes once
+// per 32 tokens.
 static bool router_is_tiled(const Shape& s) {
-  return s.dtype == SFFN_BF16 && s.N > 128 && s.N % 4 == 0 && logits_fit_offsets(s) &&
-         tiled_planes_bytes(s) < ((size_t)1 << 31) - ((size_t)8 << 20);
+  return s.dtype == SFFN_BF16 && s.N % 4 == 0 && logits_fit_offsets(s) &&
+         tiled_planes_bytes(s) < ((size_t)1 << 31) - ((size_t)8 << 20) &&
+         (s.N > 128 || (s.N > 64 && s.T >= 256 * 128));
+}
+
+bool router_is_fused(const Shape& s) {
+  return s.dtype == SFFN_BF16 && s.N <= 128 && !router_is_tiled(s);
 }
 
 hipError_t launch_router_logits(const Shape& s, const Inputs& in, const Workspace& ws,
@@ -628,10 +637,18 @@ hipError_t launch_router_logits(const Shape& s, const Inputs& in, const Workspac
                        st, in.Wr, s.d, s.N, mtp, nks, ws.planes);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int n_tt = (s.T + RL_TOK - 1) / RL_TOK;
-    hipLaunchKernelGGL(router_logits_mfma_kernel, dim3((unsigned)(n_tt * (mtp / 4))),
-                       dim3(RL_WAVES * 64), 0, st, x, ws.planes, (uint32_t)tiled_planes_bytes(s),
-                       s.T, s.d, s.N, mtp, nks, ws.logits);
+    const uint32_t pbytes = (uint32_t)tiled_planes_bytes(s);
+    if (s.N > 128) {
+      const int n_tt = (s.T + 383) / 384;
+      hipLaunchKernelGGL(router_logits_mfma_kernel<3>, dim3((unsigned)(n_tt * (mtp / 4))),
+                         dim3(RL_WAVES * 64), 0, st, x, ws.planes, pbytes, s.T, s.d, s.N, mtp,
+                         nks, ws.logits);
+    } else {
+      const int n_tt = (s.T + 127) / 128;
+      hipLaunchKernelGGL(router_logits_mfma_kernel<1>, dim3((unsigned)(n_tt * (mtp / 4))),
+                         dim3(RL_WAVES * 64), 0, st, x, ws.planes, pbytes, s.T, s.d, s.N, mtp,
+                         nks, ws.logits);
+    }
     return hipGetLastError();
   }
   const int ttiles = (s.T + RW_WAVES * 32 - 1) / (RW_WAVES * 32);

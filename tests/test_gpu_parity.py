@@ -70,6 +70,8 @@ def test_tiny_fp32():
     dict(T=1100, d=200, F=64, N=260, CF=2.0, bias_sigma=0.02),   # tiled logits: partial group, k tail
     dict(T=530, d=2080, F=32, N=132, CF=4.0),                    # tiled logits: odd step count, ragged T
     dict(T=300, d=72, F=16, N=4096, CF=16.0),                    # the most experts: widest softmax
+    dict(T=33000, d=64, F=32, N=128, CF=1.0, bias_sigma=0.02),   # tiled logits, 128-token blocks, ragged T
+    dict(T=33000, d=40, F=16, N=68, CF=1.0),                     # tiled logits, partial expert group
     dict(T=700, d=2080, F=64, N=7, CF=1.0),                      # d = 2080 (32 x 65) K tail
     dict(T=640, d=256, F=512, N=16, CF=0.5, bias_sigma=0.05),    # heavy dropping
 ])
