@@ -142,10 +142,14 @@ def measured_traffic(kernel: str, workload: str):
 def algorithmic_bytes(w, stage, accepted, active, esize, dropped=0):
     """Bytes a stage must move at minimum, from what it reads and writes once.
 
-    router_logits: fused router (bf16, N <= 128): Wr read + its three bf16 planes
-          written; otherwise x + Wr read and the fp32 logits written.
-    softmax_route: fused: x + the planes read, expert/gate/rank per token and the
-          per-block p sums and counts written; otherwise the logits read instead of x.
+    The router runs one of two ways (the library's choice, mirrored here):
+    fused (bf16, N <= 128, fewer than 32768 tokens when N > 64): the whole
+          router is in the softmax_route stage (router_logits launches nothing):
+          Wr read, its three bf16 planes written and read once, x read, and
+          expert/gate/rank per token and the per-block p sums and counts written;
+    tiled / staged (otherwise): router_logits reads x and Wr (and, tiled, writes
+          and reads the planes once) and writes the fp32 logits; softmax_route
+          reads the logits and writes the same per-token and per-block outputs.
     dispatch_scan: per-block counts and p sums read, per-block bases written, and the
           per-expert counts / accepted / p totals.
     dispatch_scatter: expert, rank, block base and gate per token read; slot per token,
@@ -158,19 +162,25 @@ def algorithmic_bytes(w, stage, accepted, active, esize, dropped=0):
     A = accepted
     T, N, d = w.T, w.N, w.d
     nblk = (T + 31) // 32
-    fused = w.dtype == "bf16" and N <= 128
+    bf16 = w.dtype == "bf16"
+    tiled = bf16 and N % 4 == 0 and (N > 128 or (N > 64 and T >= 256 * 128))
+    fused = bf16 and N <= 128 and not tiled
     wbytes = active * w.F * w.d * esize
     bias1 = active * w.F * esize if w.has_bias else 0
     bias2 = active * w.d * esize if w.has_bias else 0
+    outs = T * 12 + nblk * N * 8
     if stage == "ffn1":
         return wbytes + A * w.d * esize + A * w.F * esize + bias1 + A * 4
     if stage == "ffn2":
         return wbytes + A * w.F * esize + 2 * A * w.d * esize + bias2 + A * 8
     if stage == "router_logits":
-        return N * d * 4 + 3 * N * d * 2 if fused else T * d * esize + N * d * 4 + T * N * 4
+        if fused:
+            return None
+        return T * d * esize + N * d * 4 + (12 * N * d if tiled else 0) + T * N * 4
     if stage == "softmax_route":
-        src = T * d * 2 + 3 * N * d * 2 if fused else T * N * 4
-        return src + T * 12 + nblk * N * 8
+        if fused:
+            return T * d * 2 + N * d * 4 + 12 * N * d + outs
+        return T * N * 4 + outs
     if stage == "dispatch_scan":
         return nblk * N * 12 + N * 16
     if stage == "dispatch_scatter":

@@ -65,6 +65,12 @@ namespace sffn {
 // cached otherwise: row chunks re-read them, and with rows off the line grid
 // a k-step reads half of a line whose other half the next step reads.
 constexpr int kCpolNonTemporal = 2;
+// Weight policy for rows of an odd number of 64-byte halves (K % 64 == 32):
+// every other row then starts mid-line.  The loads are grouped by row parity
+// (load i of a step takes rows of parity i%2): rows on the line grid stream
+// past the caches, the others stay cached for the next k-step, which reads
+// the other half of their last line.
+constexpr int kCpolSplitRows = -1;
 constexpr int FBK = 64;              // k per step (one 128-byte chunk row)
 constexpr int FLDS = FBK + 8;        // bf16 per row of a weight slot (144 B: rows 4 banks apart)
 constexpr int FP = SFFN_FFN_STAGES;  // k-steps in flight
@@ -230,14 +236,18 @@ ffn_bf16_kernel(const uint16_t* __restrict__ act, uint32_t act_bytes,
     const int n = dt.nt * COLS + tid * 8;  // Nout % 8 == 0: a chunk is all in or all out
     return buffer_load16(src, (dt.nrows > 0 && tid < COLS / 8 && n < Nout) ? (uint32_t)n * 2u : kOob);
   };
-  // Weights: load i of a step brings rows 8i + lane/8 of the wave's WCOLS,
-  // 16-byte chunk lane%8 of the k-step.
+  // Weights: load i of a step brings rows wrow(i) of the wave's WCOLS (8i +
+  // lane/8, or grouped by parity for kCpolSplitRows), 16-byte chunk lane%8 of
+  // the k-step.
+  auto wrow = [&](int i) {
+    return WPOL == kCpolSplitRows ? 2 * (8 * (i / 2) + (lane >> 3)) + (i & 1) : i * 8 + (lane >> 3);
+  };
   auto setup_b = [&](const FfnTile& dt, __amdgpu_buffer_rsrc_t& src, uint32_t (&off)[BL]) {
     src = make_rsrc(W + (size_t)dt.e * Nout * K, (uint32_t)((size_t)Nout * K * 2));
     const int n0 = dt.nt * COLS + wave * WCOLS;
 #pragma unroll
     for (int i = 0; i < BL; ++i) {
-      const int nr = n0 + i * 8 + (lane >> 3);
+      const int nr = n0 + wrow(i);
       off[i] = (dt.nrows > 0 && nr < Nout)
                    ? ((uint32_t)nr * (uint32_t)K + (uint32_t)(lane & 7) * 8u) * 2u : kOob;
     }
@@ -245,11 +255,19 @@ ffn_bf16_kernel(const uint16_t* __restrict__ act, uint32_t act_bytes,
   auto load_b = [&](u32x4 (&rb)[BL], const __amdgpu_buffer_rsrc_t& src, const uint32_t (&off)[BL],
                     int ks) {
     const bool kin = ks * FBK + (lane & 7) * 8 < K;
+    constexpr int P0 = WPOL == kCpolSplitRows ? kCpolNonTemporal : WPOL;  // even loads
+    constexpr int P1 = WPOL == kCpolSplitRows ? 0 : WPOL;                 // odd loads
 #pragma unroll
-    for (int i = 0; i < BL; ++i)
-      rb[i] = __builtin_amdgcn_raw_buffer_load_b128(
-          src, (int)(kin ? off[i] + (uint32_t)ks * (FBK * 2) : kOob), 0, WPOL);
+    for (int i = 0; i < BL; ++i) {
+      if (i & 1)
+        rb[i] = __builtin_amdgcn_raw_buffer_load_b128(
+            src, (int)(kin ? off[i] + (uint32_t)ks * (FBK * 2) : kOob), 0, P1);
+      else
+        rb[i] = __builtin_amdgcn_raw_buffer_load_b128(
+            src, (int)(kin ? off[i] + (uint32_t)ks * (FBK * 2) : kOob), 0, P0);
+    }
   };
+
   // Activations: load i of a step fills row group g = wave + i*FW (rows 8g ..
   // 8g+7); lane l writes LDS chunk l%8 of row 8g + l/8, which holds logical
   // chunk (l%8) ^ swizzle(row).  Groups past the tile go to the sink.
@@ -289,7 +307,7 @@ ffn_bf16_kernel(const uint16_t* __restrict__ act, uint32_t act_bytes,
     // Weight tile into the wave's LDS slot (row-major), back out in operand layout.
     // LDS accesses of one wave complete in order, so no barrier is needed.
 #pragma unroll
-    for (int i = 0; i < BL; ++i) store16(bslot + (i * 8 + (lane >> 3)) * FLDS + (lane & 7) * 8, rb[i]);
+    for (int i = 0; i < BL; ++i) store16(bslot + wrow(i) * FLDS + (lane & 7) * 8, rb[i]);
     const char* abase = As + buf * A_BYTES;
     const uint16_t* bbase = bslot + (lane & 31) * FLDS + khalf * 32;
     // Operand fragments of sub-step q (16 k): read one sub-step ahead of the
@@ -599,8 +617,14 @@ template <int MT, int FW, int WN, bool SECOND>
 static void launch_ffn_bf16_t(const FfnArgs& a, hipStream_t st) {
   if constexpr (ffn_shape_ok<MT, FW, WN, SECOND>()) {
     const dim3 grid((unsigned)ffn_grid<MT, FW, WN, SECOND>(a)), block(FW * 64);
-    // Weights are streamed past the caches when nothing re-reads their lines.
-    if (a.n_mchunks == 1 && (a.K * 2) % 128 == 0)
+    // Weights are streamed past the caches when nothing re-reads their lines
+    // (with rows off the line grid: only the rows on it).
+    if (a.n_mchunks == 1 && (a.K * 2) % 128 == 64 && ((size_t)a.W & 127) == 0 && a.Nout % 2 == 0)
+      hipLaunchKernelGGL((ffn_bf16_kernel<MT, FW, WN, SECOND, kCpolSplitRows>), grid, block, 0, st,
+                         a.act, a.act_bytes, a.W, a.bias, a.offset, a.row2tok, a.rowgate, a.xres,
+                         a.out, a.out_bytes, a.K, a.Nout, a.n_mchunks, a.n_experts, a.max_rows,
+                         a.T, a.d_model, a.no_residual);
+    else if (a.n_mchunks == 1 && (a.K * 2) % 128 == 0)
       hipLaunchKernelGGL((ffn_bf16_kernel<MT, FW, WN, SECOND, kCpolNonTemporal>), grid, block, 0, st,
                          a.act, a.act_bytes, a.W, a.bias, a.offset, a.row2tok, a.rowgate, a.xres,
                          a.out, a.out_bytes, a.K, a.Nout, a.n_mchunks, a.n_experts, a.max_rows,
