@@ -159,8 +159,14 @@ __device__ __forceinline__ int find_tile(int t, int stride, int n_tiles, int n_n
     const int rest = t / n_ntiles;
     const int mc = rest % n_mchunks;
     const int e = rest / n_mchunks;
-    const int rbeg = offset[e] + mc * ROWS;
-    const int nrows = min(offset[e + 1] - rbeg, ROWS);
+    // The expert's rows split evenly over the chunks it needs, so that its
+    // chunks (which read the same weights, at the same time on one XCD) stream
+    // in step and the second reader of a weight line finds it in L2.
+    const int n_e = offset[e + 1] - offset[e];
+    const int used = (n_e + ROWS - 1) / ROWS;
+    const int per = used > 0 ? (n_e + used - 1) / used : 0;
+    const int rbeg = offset[e] + mc * per;
+    const int nrows = mc < used ? min(n_e - mc * per, per) : 0;
     if (nrows > 0) {
       d = FfnTile{e, nt, rbeg, nrows};
       return t;
