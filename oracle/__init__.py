@@ -8,6 +8,7 @@ from .switchffn_oracle import (  # noqa: F401
     bf16_bits,
     capacity,
     dispatch,
+    dispatch_topk,
     expert_ffn,
     forward,
     near_tie_tokens,
@@ -15,6 +16,7 @@ from .switchffn_oracle import (  # noqa: F401
     round_to_dtype,
     router,
     router_logits,
+    second_choice,
     softmax,
     top1,
 )

@@ -26,6 +26,16 @@ f_i counts the argmax before capacity; P_i averages over all T tokens; the
 aux loss is returned without the alpha factor; y = x + g*E(x) for accepted
 tokens and y = x for dropped ones; b2 sits inside the gate scaling.
 
+Top-2 routing (the MoE baseline the Switch summary contrasts with, section
+"Why Top-1 Routing Matters" and the routing formula before "Switch uses"):
+y = x + sum over the two largest p_{t,i} of p_{t,i} E_i(x), raw (not
+renormalised) gates; the second choice is the largest of the remaining fp32
+logits, ties to the lowest index; the capacity is floor(CF * (k*T) / N)
+([Switch summary] 3.4, k x tokens per batch / N x capacity factor); each
+expert column is filled in token order (a token holds at most one position
+per expert, so both choices of a token are ranked by token); f_i of the aux
+loss stays the top-1 (argmax) share.
+
 Pins (tests/test_oracle_pins.py): the worked aux-loss example of the
 Math-LLMs card (1.15), the uniform-routing closed forms (aux = 1), the
 one-expert limit (aux -> N, closed form), N = 1 dense-FFN reduction, the x = 0
@@ -113,6 +123,44 @@ def dispatch(expert_idx: np.ndarray, N: int, C: int) -> dict:
             "offset": offset, "row2tok": row2tok}
 
 
+def second_choice(z: np.ndarray, first: np.ndarray) -> np.ndarray:
+    """Lowest expert index among the largest fp32 logits other than the first choice."""
+    z32 = z.astype(np.float32).copy()
+    z32[np.arange(z.shape[0]), first] = -np.inf
+    return np.argmax(z32, axis=1).astype(np.int64)
+
+
+def topk_gates(probs: np.ndarray, choices: np.ndarray) -> np.ndarray:
+    """Raw gates p[t, e_{t,c}] of the chosen experts (not renormalised)."""
+    return probs[np.arange(probs.shape[0])[:, None], choices]
+
+
+def dispatch_topk(choices: np.ndarray, N: int, C: int) -> dict:
+    """Dispatch of k choices per token: each expert column is filled in token order."""
+    T, k = choices.shape
+    count = np.zeros(N, dtype=np.int64)
+    rank = np.empty((T, k), dtype=np.int64)
+    for t in range(T):
+        for c in range(k):
+            e = int(choices[t, c])
+            rank[t, c] = count[e]   # tokens holding a choice of e before t
+            count[e] += 1
+    slot = np.where(rank < C, rank, -1)
+    accepted = np.minimum(count, C)
+    offset = np.zeros(N + 1, dtype=np.int64)
+    offset[1:] = np.cumsum(accepted)
+    row2tok = np.empty(int(offset[-1]), dtype=np.int64)
+    row2choice = np.empty(int(offset[-1]), dtype=np.int64)
+    for t in range(T):
+        for c in range(k):
+            if slot[t, c] >= 0:
+                row = offset[int(choices[t, c])] + slot[t, c]
+                row2tok[row] = t
+                row2choice[row] = c
+    return {"hist": count, "rank": rank, "slot": slot, "accepted": accepted,
+            "offset": offset, "row2tok": row2tok, "row2choice": row2choice}
+
+
 # ----------------------------------------------------------------------------
 # Load-balancing auxiliary loss ([Switch summary] 3.4 "The Load-Balancing
 # Auxiliary Loss": f_i = (1/T) sum_x 1{argmax p(x) = i}, P_i = (1/T) sum_x
@@ -177,8 +225,11 @@ ExpertSource = Callable[[int], tuple]
 
 def forward(x, Wr, experts, CF: float, dtype: str = "fp32", *, no_residual: bool = False,
             expert_idx: Optional[np.ndarray] = None,
-            only_experts: Optional[Iterable[int]] = None) -> dict:
+            only_experts: Optional[Iterable[int]] = None, k: int = 1) -> dict:
     """Run the layer on float64 inputs.
+
+    k: experts per token, 1 (Switch routing) or 2 (top-2 routing; expert_idx,
+        slot, gate and rank are then [T, 2], choice minor).
 
     experts: (W1 [N,F,d], b1 [N,F] | None, W2 [N,d,F], b2 [N,d] | None), or a
         callable e -> (W1e, b1e, W2e, b2e) for weights drawn one expert at a time.
@@ -188,6 +239,11 @@ def forward(x, Wr, experts, CF: float, dtype: str = "fp32", *, no_residual: bool
         other experts' accepted tokens are NaN.
     no_residual: y = g * E(x) for accepted tokens and 0 for dropped ones.
     """
+    if k == 2:
+        return _forward_top2(x, Wr, experts, CF, dtype, no_residual=no_residual,
+                             expert_idx=expert_idx, only_experts=only_experts)
+    if k != 1:
+        raise ValueError("k must be 1 or 2")
     x = np.asarray(x, np.float64)
     T = x.shape[0]
     N = np.asarray(Wr).shape[0]
@@ -223,6 +279,51 @@ def forward(x, Wr, experts, CF: float, dtype: str = "fp32", *, no_residual: bool
     return {
         "C": C, "logits": r["logits"], "probs": r["probs"], "expert_idx": eidx,
         "router_expert_idx": r["expert_idx"], "gate": gate, "aux_loss": aux,
+        "y64": y, "y": round_to_dtype(y, dtype), **dp,
+    }
+
+
+def _forward_top2(x, Wr, experts, CF, dtype, *, no_residual, expert_idx, only_experts) -> dict:
+    """Top-2 routing: y_t = x_t + sum_c [accepted] p_{t,e_c} E_{e_c}(x_t) (see the header)."""
+    x = np.asarray(x, np.float64)
+    T = x.shape[0]
+    N = np.asarray(Wr).shape[0]
+    if N < 2:
+        raise ValueError("top-2 routing needs N >= 2")
+    C = capacity(2 * T, N, CF)
+    r = router(x, Wr)
+    first = r["expert_idx"]
+    own = np.stack([first, second_choice(r["logits"], first)], axis=1)
+    choices = own if expert_idx is None else np.asarray(expert_idx, np.int64).reshape(T, 2)
+    gate = topk_gates(r["probs"], choices)
+    dp = dispatch_topk(choices, N, C)
+    aux = aux_loss(choices[:, 0], r["probs"])
+
+    if callable(experts):
+        get = experts
+    else:
+        W1, b1, W2, b2 = experts
+        def get(e):
+            return (W1[e], None if b1 is None else b1[e], W2[e], None if b2 is None else b2[e])
+
+    y = np.zeros_like(x) if no_residual else x.copy()
+    todo = range(N) if only_experts is None else sorted(set(int(e) for e in only_experts))
+    if only_experts is not None:
+        for e in range(N):
+            if e not in todo:
+                y[dp["row2tok"][dp["offset"][e]:dp["offset"][e + 1]]] = np.nan
+    for e in todo:
+        lo, hi = dp["offset"][e], dp["offset"][e + 1]
+        rows = dp["row2tok"][lo:hi]
+        if len(rows) == 0:
+            continue
+        W1e, b1e, W2e, b2e = get(e)
+        o = expert_ffn(x[rows], W1e, b1e, W2e, b2e)
+        y[rows] += gate[rows, dp["row2choice"][lo:hi], None] * o   # distinct rows per expert
+
+    return {
+        "C": C, "logits": r["logits"], "probs": r["probs"], "expert_idx": choices,
+        "router_expert_idx": own, "gate": gate, "aux_loss": aux,
         "y64": y, "y": round_to_dtype(y, dtype), **dp,
     }
 

@@ -70,3 +70,63 @@ def brute_forward(x, Wr, W1, b1, W2, b2, CF, no_residual=False):
     gate = [probs[t][choice[t]] for t in range(T)]
     return {"C": C, "expert_idx": choice, "slot": slot, "gate": gate, "aux_loss": aux, "y": y,
             "probs": probs}
+
+
+def brute_forward_top2(x, Wr, W1, b1, W2, b2, CF, no_residual=False):
+    """Top-2 routing, one token at a time: the two largest fp32 logits (ties to the
+    lowest index), raw gates, capacity floor(CF * 2T / N), expert columns filled in
+    token order, y = x + the gated outputs of the accepted choices."""
+    T = len(x)
+    N = len(Wr)
+    d = len(x[0]) if T else len(Wr[0])
+    F = len(W1[0])
+    C = math.floor(CF * (2 * T) / N)
+
+    choices, probs = [], []
+    for t in range(T):
+        z = [dot(x[t], Wr[i]) for i in range(N)]
+        z32 = [to_f32(v) for v in z]
+        first = 0
+        for i in range(1, N):
+            if z32[i] > z32[first]:
+                first = i
+        second = 1 if first == 0 else 0
+        for i in range(N):
+            if i != first and z32[i] > z32[second]:
+                second = i
+        m = max(z)
+        ex = [math.exp(v - m) for v in z]
+        s = math.fsum(ex)
+        choices.append((first, second))
+        probs.append([v / s for v in ex])
+
+    slot, gate, y = [], [], []
+    for t in range(T):
+        row = [0.0] * d if no_residual else list(x[t])
+        slots, gates = [], []
+        for e in choices[t]:
+            rank = sum(1 for s_ in range(t) if e in choices[s_])
+            g = probs[t][e]
+            gates.append(g)
+            if rank >= C:
+                slots.append(-1)
+                continue
+            slots.append(rank)
+            h = []
+            for j in range(F):
+                a = dot(W1[e][j], x[t]) + (b1[e][j] if b1 is not None else 0.0)
+                h.append(a if a > 0.0 else 0.0)
+            for i in range(d):
+                row[i] += g * (dot(W2[e][i], h) + (b2[e][i] if b2 is not None else 0.0))
+        slot.append(slots)
+        gate.append(gates)
+        y.append(row)
+
+    aux = 0.0
+    for i in range(N):
+        f_i = sum(1 for t in range(T) if choices[t][0] == i) / T
+        P_i = math.fsum(probs[t][i] for t in range(T)) / T
+        aux += f_i * P_i
+    aux *= N
+    return {"C": C, "expert_idx": [list(c) for c in choices], "slot": slot, "gate": gate,
+            "aux_loss": aux, "y": y, "probs": probs}

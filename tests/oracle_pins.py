@@ -13,7 +13,7 @@ import os
 import numpy as np
 
 import oracle.switchffn_oracle as O
-from bruteforce import brute_forward
+from bruteforce import brute_forward, brute_forward_top2
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
@@ -259,6 +259,94 @@ def pin_round_to_bf16():
     want = np.array([1.0, 1.0, 1.0 + 2 * ulp, 1.0 + ulp, -1.0, 3.0, 0.0, 256.0, 256.0, 1.0])
     got = O.round_to_bf16(vals)
     assert np.array_equal(got, want), got
+
+
+# ---------------------------------------------------------------------------
+# Top-2 routing (the MoE baseline: y = x + sum over the two largest p of p E(x)).
+# ---------------------------------------------------------------------------
+def pin_top2_bruteforce_agreement():
+    cases = [
+        dict(seed=31, T=1, d=3, F=4, N=2, CF=1.0, bias=False),
+        dict(seed=32, T=9, d=5, F=6, N=3, CF=1.0, bias=True),
+        dict(seed=33, T=48, d=6, F=7, N=5, CF=0.5, bias=True),
+        dict(seed=34, T=40, d=4, F=3, N=4, CF=1.25, bias=False),
+        dict(seed=35, T=30, d=7, F=5, N=6, CF=3.0, bias=True),
+    ]
+    for c in cases:
+        x, Wr, W1, b1, W2, b2 = random_case(c["seed"], c["T"], c["d"], c["F"], c["N"], c["bias"])
+        for nr in (False, True):
+            r = O.forward(x, Wr, (W1, b1, W2, b2), CF=c["CF"], no_residual=nr, k=2)
+            b = brute_forward_top2(_tolist(x), _tolist(Wr), _tolist(W1), _tolist(b1), _tolist(W2),
+                                   _tolist(b2), c["CF"], no_residual=nr)
+            assert r["C"] == b["C"]
+            assert r["expert_idx"].tolist() == b["expert_idx"]
+            assert r["slot"].tolist() == b["slot"]
+            _close(r["gate"], b["gate"], 1e-12)
+            assert abs(r["aux_loss"] - b["aux_loss"]) < 1e-12
+            _close(r["y64"], b["y"], 1e-12)
+
+
+def pin_top2_two_experts_is_dense_mixture():
+    # N = k = 2 and C >= T: every token visits both experts and the layer is the
+    # soft mixture x + sum_i p_i E_i(x) (p = softmax of the logits), written here
+    # with scipy's softmax and one plain matmul chain per expert.
+    from scipy.special import softmax as sp_softmax
+    x, Wr, W1, b1, W2, b2 = random_case(41, 25, 6, 8, 2, bias=True)
+    r = O.forward(x, Wr, (W1, b1, W2, b2), CF=1.0, k=2)
+    assert r["C"] == 25 and np.all(r["slot"] >= 0)
+    p = sp_softmax(x @ Wr.T, axis=1)
+    want = x.copy()
+    for e in range(2):
+        want += p[:, e:e + 1] * (np.maximum(x @ W1[e].T + b1[e], 0.0) @ W2[e].T + b2[e])
+    _close(r["y64"], want, 1e-12)
+    _close(np.sort(r["gate"], axis=1), np.sort(p, axis=1), 1e-12)
+
+
+def pin_top2_router_zero_ties():
+    # Wr = 0: all logits tie, so every token picks experts 0 then 1 with gates 1/N,
+    # C = floor(CF 2T / N), and tokens 0..C-1 get x + (E_0(x) + E_1(x)) / N.
+    N, T = 4, 20
+    x, _, W1, b1, W2, b2 = random_case(43, T, 5, 6, N, bias=True)
+    r = O.forward(x, np.zeros((N, 5)), (W1, b1, W2, b2), CF=1.0, k=2)
+    C = r["C"]
+    assert C == 10
+    assert np.all(r["expert_idx"] == np.array([0, 1]))
+    _close(r["gate"], np.full((T, 2), 1.0 / N), 1e-15)
+    for t in range(T):
+        want = x[t].copy()
+        if t < C:
+            for e in (0, 1):
+                want += (np.maximum(W1[e] @ x[t] + b1[e], 0.0) @ W2[e].T + b2[e]) / N
+            assert np.all(r["slot"][t] == t)
+        else:
+            assert np.all(r["slot"][t] == -1)
+        _close(r["y64"][t], want, 1e-13)
+
+
+def pin_top2_second_choice_ties():
+    # Second choices with exact ties go to the lowest remaining index.
+    x = np.array([[1.0, 1.0, 0.0], [0.0, 2.0, 2.0], [3.0, 3.0, 3.0], [0.0, 0.0, 5.0],
+                  [4.0, 0.0, 4.0]])
+    r = O.forward(x, np.eye(3), _zero_ffn(3, 2, 3), CF=3.0, k=2)
+    assert r["expert_idx"].tolist() == [[0, 1], [1, 2], [0, 1], [2, 0], [0, 2]]
+
+
+def pin_top2_capacity_and_aux():
+    # Capacity counts k choices per token; aux keeps the top-1 share f_i, so it
+    # equals the top-1 layer's on the same inputs; CF = 0 drops every choice.
+    assert O.capacity(2 * 8192, 64, 1.25) == 320
+    assert O.capacity(2 * 10, 4, 1.0) == 5
+    x, Wr, W1, b1, W2, b2 = random_case(45, 36, 6, 5, 4, bias=True)
+    r1 = O.forward(x, Wr, (W1, b1, W2, b2), CF=1.0)
+    r2 = O.forward(x, Wr, (W1, b1, W2, b2), CF=1.0, k=2)
+    assert r2["C"] == 2 * r1["C"] == 18
+    assert abs(r1["aux_loss"] - r2["aux_loss"]) < 1e-15
+    assert np.array_equal(r2["expert_idx"][:, 0], r1["expert_idx"])
+    assert np.all(r2["expert_idx"][:, 0] != r2["expert_idx"][:, 1])
+    acc = np.bincount(r2["expert_idx"][r2["slot"] >= 0], minlength=4)
+    assert np.array_equal(acc, np.minimum(r2["hist"], 18))
+    r0 = O.forward(x, Wr, (W1, b1, W2, b2), CF=0.0, k=2)
+    assert np.all(r0["slot"] == -1) and np.array_equal(r0["y64"], x)
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

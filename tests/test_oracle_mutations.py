@@ -14,7 +14,7 @@ from oracle_pins import ALL_PINS
 
 _orig = {name: getattr(O, name) for name in
          ("capacity", "router_logits", "softmax", "top1", "dispatch", "aux_loss", "expert_ffn",
-          "round_to_bf16", "forward")}
+          "round_to_bf16", "forward", "second_choice", "topk_gates", "dispatch_topk")}
 
 
 def _ffn_no_b2(xe, W1e, b1e, W2e, b2e):
@@ -152,6 +152,38 @@ def _forward_gate_outside_b2(*a, **k):
     return r
 
 
+def _second_ties_to_highest(z, first):
+    z32 = z.astype(np.float32).copy()
+    z32[np.arange(z.shape[0]), first] = -np.inf
+    return (z.shape[1] - 1 - np.argmax(z32[:, ::-1], axis=1)).astype(np.int64)
+
+
+def _gates_renormalised(probs, choices):
+    g = _orig["topk_gates"](probs, choices)
+    return g / g.sum(axis=1, keepdims=True)
+
+
+def _dispatch_first_choices_first(choices, N, C):
+    # All first choices in token order, then all second choices (a different
+    # priority rule from filling each expert column in token order).
+    T, k = choices.shape
+    count = np.zeros(N, dtype=np.int64)
+    rank = np.empty((T, k), dtype=np.int64)
+    for c in range(k):
+        for t in range(T):
+            e = int(choices[t, c])
+            rank[t, c] = count[e]
+            count[e] += 1
+    dp = _orig["dispatch_topk"](choices, N, C)
+    slot = np.where(rank < C, rank, -1)
+    dp.update(rank=rank, slot=slot)
+    return dp
+
+
+def _dispatch_topk_capacity_without_k(choices, N, C):
+    return _orig["dispatch_topk"](choices, N, C // 2)
+
+
 MUTANTS = {
     "ffn_drops_b2": ("expert_ffn", _ffn_no_b2),
     "ffn_drops_b1": ("expert_ffn", _ffn_no_b1),
@@ -176,6 +208,10 @@ MUTANTS = {
     "combine_no_residual": ("forward", _forward_no_residual),
     "dropped_rows_zeroed": ("forward", _forward_dropped_zero),
     "gate_outside_b2": ("forward", _forward_gate_outside_b2),
+    "top2_second_ties_to_highest": ("second_choice", _second_ties_to_highest),
+    "top2_gates_renormalised": ("topk_gates", _gates_renormalised),
+    "top2_first_choices_first": ("dispatch_topk", _dispatch_first_choices_first),
+    "top2_capacity_without_k": ("dispatch_topk", _dispatch_topk_capacity_without_k),
 }
 
 
