@@ -125,6 +125,35 @@ int switch_ffn_forward_ex(const void* x, const float* Wr, const void* W1, const 
                           size_t workspace_bytes, void* stream, uint32_t flags,
                           const sffn_stats* stats, void* const* stage_events);
 
+/* Top-k routing, k = 1 or 2 (k = 2: the MoE top-2 baseline the Switch summary
+ * contrasts with, section "Why Top-1 Routing Matters" and its top-2 routing
+ * formula y = sum over the two largest p[t,i] of p[t,i] E_i(x); section 3.4
+ * gives the capacity k x tokens / N x capacity factor).  With k = 2:
+ *   choices  e[t,0] = argmax_i z[t,i], e[t,1] = argmax over i != e[t,0]
+ *            (fp32 logits, ties -> lowest index)
+ *   gates    gate[t,c] = p[t, e[t,c]] (raw, not renormalised)
+ *   capacity C = floor(CF * (k*T) / N) = switch_ffn_capacity(k*T, N, CF); each
+ *            expert's buffer is filled in token order (a token holds at most
+ *            one position per expert), the first C accepted, the rest dropped
+ *   combine  y_t = x_t + sum over t's accepted choices of gate[t,c] E_{e[t,c]}(x_t)
+ *            (y_t = x_t when both are dropped); SFFN_NO_RESIDUAL drops the x_t term
+ *   aux      as for k = 1: f_i counts the top-1 choices
+ *   outputs  expert_idx, slot, gate are [T, k], row-major (choice minor);
+ *            stats: expert_count[i] = tokens with i among their k choices,
+ *            accepted_count = min(expert_count, C), n_dropped = dropped choices.
+ * k = 1 is exactly switch_ffn_forward_ex.  k = 2 needs N >= 2 and
+ * min(2T, N*C) * max(d, F) * 4 < 2^31 (else SFFN_EUNSUPPORTED); k outside
+ * {1, 2} or N < k is SFFN_EINVAL.  The per-stage events are the same six
+ * stages; with k = 2 the ffn2 stage also holds the combine. */
+size_t switch_ffn_workspace_bytes_topk(int64_t T, int64_t d, int64_t F, int64_t N, double CF,
+                                       int k, int dtype);
+int switch_ffn_forward_topk(const void* x, const float* Wr, const void* W1, const void* b1,
+                            const void* W2, const void* b2, int64_t T, int64_t d, int64_t F,
+                            int64_t N, double CF, int k, int dtype, void* y, int32_t* expert_idx,
+                            int32_t* slot, float* gate, float* aux_loss, void* workspace,
+                            size_t workspace_bytes, void* stream, uint32_t flags,
+                            const sffn_stats* stats, void* const* stage_events);
+
 /* Number of stages forward_ex reports events around, and their names
  * ("router_logits", "softmax_route", ...); NULL for an index out of range. */
 int switch_ffn_num_stages(void);

@@ -21,8 +21,10 @@ from .binding import (  # noqa: F401
     switch_ffn_capacity,
     switch_ffn_forward,
     switch_ffn_forward_ex,
+    switch_ffn_forward_topk,
     switch_ffn_num_stages,
     switch_ffn_stage_name,
     switch_ffn_status_string,
     switch_ffn_workspace_bytes,
+    switch_ffn_workspace_bytes_topk,
 )

@@ -55,6 +55,12 @@ def load_library(path: str = LIB_PATH):
     L.switch_ffn_forward_ex.restype = ctypes.c_int
     L.switch_ffn_forward_ex.argtypes = _FWD_ARGS + [ctypes.c_uint32, ctypes.POINTER(sffn_stats),
                                                     _P]
+    L.switch_ffn_workspace_bytes_topk.restype = ctypes.c_size_t
+    L.switch_ffn_workspace_bytes_topk.argtypes = [_I64, _I64, _I64, _I64, ctypes.c_double,
+                                                  ctypes.c_int, ctypes.c_int]
+    L.switch_ffn_forward_topk.restype = ctypes.c_int
+    L.switch_ffn_forward_topk.argtypes = (_FWD_ARGS[:11] + [ctypes.c_int] + _FWD_ARGS[11:] +
+                                          [ctypes.c_uint32, ctypes.POINTER(sffn_stats), _P])
     L.switch_ffn_num_stages.restype = ctypes.c_int
     L.switch_ffn_num_stages.argtypes = []
     L.switch_ffn_stage_name.restype = ctypes.c_char_p
@@ -87,6 +93,10 @@ def switch_ffn_workspace_bytes(T, d, F, N, CF, dtype) -> int:
     return lib().switch_ffn_workspace_bytes(T, d, F, N, CF, dtype)
 
 
+def switch_ffn_workspace_bytes_topk(T, d, F, N, CF, k, dtype) -> int:
+    return lib().switch_ffn_workspace_bytes_topk(T, d, F, N, CF, k, dtype)
+
+
 def switch_ffn_num_stages() -> int:
     return lib().switch_ffn_num_stages()
 
@@ -115,10 +125,12 @@ def _dtype_code(t) -> int:
 
 def switch_ffn_forward(x, Wr, W1, b1, W2, b2, CF: float, *, y=None, expert_idx=None, slot=None,
                        gate=None, aux_loss=None, workspace=None, stream=None, flags: int = 0,
-                       stats=None, stage_events=None, check: bool = True) -> dict:
+                       stats=None, stage_events=None, check: bool = True, k: int = 1) -> dict:
     """Run the layer on device tensors; returns the output tensors (allocated when not given).
 
     x [T, d], Wr [N, d] fp32, W1 [N, F, d], b1 [N, F] | None, W2 [N, d, F], b2 [N, d] | None.
+    k: experts per token (1, or 2 for top-2 routing through switch_ffn_forward_topk; then
+    expert_idx, slot and gate are [T, 2]).
     stats: optional dict of int32 device tensors 'expert_count' [N], 'accepted_count' [N],
     'n_dropped' [1].  stage_events: optional list of torch.cuda.Event (already recorded once
     so that the handle exists), switch_ffn_num_stages()+1 of them.
@@ -132,15 +144,16 @@ def switch_ffn_forward(x, Wr, W1, b1, W2, b2, CF: float, *, y=None, expert_idx=N
     dev = x.device
     if y is None:
         y = torch.empty_like(x)
+    shape = (T,) if k == 1 else (T, k)
     if expert_idx is None:
-        expert_idx = torch.empty(T, dtype=torch.int32, device=dev)
+        expert_idx = torch.empty(shape, dtype=torch.int32, device=dev)
     if slot is None:
-        slot = torch.empty(T, dtype=torch.int32, device=dev)
+        slot = torch.empty(shape, dtype=torch.int32, device=dev)
     if gate is None:
-        gate = torch.empty(T, dtype=torch.float32, device=dev)
+        gate = torch.empty(shape, dtype=torch.float32, device=dev)
     if aux_loss is None:
         aux_loss = torch.empty(1, dtype=torch.float32, device=dev)
-    nbytes = switch_ffn_workspace_bytes(T, d, F, N, CF, dt)
+    nbytes = switch_ffn_workspace_bytes_topk(T, d, F, N, CF, k, dt)
     if workspace is None and nbytes > 0:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     if stream is None:
@@ -159,7 +172,12 @@ def switch_ffn_forward(x, Wr, W1, b1, W2, b2, CF: float, *, y=None, expert_idx=N
     args = (_ptr(x), _ptr(Wr), _ptr(W1), _ptr(b1), _ptr(W2), _ptr(b2), T, d, F, N, CF, dt,
             _ptr(y), _ptr(expert_idx), _ptr(slot), _ptr(gate), _ptr(aux_loss), _ptr(workspace),
             ws_bytes, stream)
-    if flags == 0 and st is None and ev is None:
+    if k != 1:
+        name = "switch_ffn_forward_topk"
+        rc = lib().switch_ffn_forward_topk(*args[:11], k, *args[11:], flags,
+                                           None if st is None else ctypes.byref(st),
+                                           None if ev is None else ctypes.cast(ev, ctypes.c_void_p))
+    elif flags == 0 and st is None and ev is None:
         name = "switch_ffn_forward"
         rc = lib().switch_ffn_forward(*args)
     else:
@@ -172,5 +190,6 @@ def switch_ffn_forward(x, Wr, W1, b1, W2, b2, CF: float, *, y=None, expert_idx=N
             "aux_loss": aux_loss, "workspace": workspace}
 
 
-# forward_ex's extra arguments are keyword arguments of switch_ffn_forward.
+# forward_ex's and forward_topk's extra arguments are keyword arguments of switch_ffn_forward.
 switch_ffn_forward_ex = switch_ffn_forward
+switch_ffn_forward_topk = switch_ffn_forward

@@ -40,16 +40,20 @@ size_t workspace_layout(const Shape& s, Workspace* ws, char* base) {
   Workspace w;
   w.logits = (float*)take(T * N * sizeof(float));
   w.ppart = (float*)take(nb * N * sizeof(float));
+  const size_t K = (size_t)s.k;
   w.cnt = (int*)take(nb * N * sizeof(int));
+  w.cnt1 = (int*)take(K == 2 ? nb * N * sizeof(int) : 0);
   w.base = (int*)take(nb * N * sizeof(int));
-  w.lrank = (int*)take(T * sizeof(int));
+  w.lrank = (int*)take(T * K * sizeof(int));
   w.hist = (int*)take(N * sizeof(int));
+  w.hist1 = (int*)take(K == 2 ? N * sizeof(int) : 0);
   w.acc = (int*)take(N * sizeof(int));
   w.offset = (int*)take((N + 1) * sizeof(int));
   w.psum = (double*)take(N * sizeof(double));
   w.row2tok = (int*)take((size_t)s.max_rows * sizeof(int) + 4);
   w.rowgate = (float*)take((size_t)s.max_rows * sizeof(float) + 4);
   w.H = (void*)take((size_t)s.max_rows * (size_t)s.F * esize + 16);
+  w.Y2 = (void*)take(K == 2 ? (size_t)s.max_rows * (size_t)s.d * esize + 16 : 0);
   w.planes = (uint16_t*)take(sffn::router_planes_bytes(s));
   if (ws) *ws = w;
   return off;
@@ -58,9 +62,10 @@ size_t workspace_layout(const Shape& s, Workspace* ws, char* base) {
 }  // namespace sffn
 
 // Shape checks shared by workspace sizing and the forward pass.
-static int make_shape(int64_t T, int64_t d, int64_t F, int64_t N, double CF, int dtype,
+static int make_shape(int64_t T, int64_t d, int64_t F, int64_t N, double CF, int dtype, int k,
                       sffn::Shape* s) {
   if (T <= 0 || d <= 0 || F <= 0 || N <= 0 || !isfinite(CF) || CF < 0) return SFFN_EINVAL;
+  if ((k != 1 && k != 2) || N < k) return SFFN_EINVAL;
   if (dtype != SFFN_FP32 && dtype != SFFN_BF16) return SFFN_EDTYPE;
   if (N > SFFN_MAX_EXPERTS) return SFFN_EUNSUPPORTED;
   const int64_t widest = N > d ? (N > F ? N : F) : (d > F ? d : F);
@@ -68,17 +73,21 @@ static int make_shape(int64_t T, int64_t d, int64_t F, int64_t N, double CF, int
   if (T > ((int64_t)1 << 30) / widest - 1) return SFFN_EUNSUPPORTED;
   if (d * F >= ((int64_t)1 << 30)) return SFFN_EUNSUPPORTED;
   if (dtype == SFFN_BF16 && ((d % 8) != 0 || (F % 8) != 0)) return SFFN_EUNSUPPORTED;
-  const int64_t C = switch_ffn_capacity(T, N, CF);
-  const int64_t Ce = C < T ? C : T;  // a rank never reaches T
+  const int64_t C = switch_ffn_capacity(k * T, N, CF);
+  const int64_t Ce = C < T ? C : T;  // a rank never reaches T (one position per token and expert)
   s->T = (int)T;
   s->d = (int)d;
   s->F = (int)F;
   s->N = (int)N;
   s->C = (int)Ce;
   s->dtype = dtype;
+  s->k = k;
   s->n_route_blocks = (int)((T + sffn::kRouteTokens - 1) / sffn::kRouteTokens);
   const int64_t cap_rows = N * Ce;
-  s->max_rows = (int)(cap_rows < T ? cap_rows : T);
+  s->max_rows = (int)(cap_rows < k * T ? cap_rows : k * T);
+  // k = 2: the expert buffers hold up to 2T rows; their byte offsets stay below 2^31.
+  if (k == 2 && (int64_t)s->max_rows * (d > F ? d : F) * 4 >= ((int64_t)1 << 31))
+    return SFFN_EUNSUPPORTED;
   return SFFN_OK;
 }
 
@@ -91,11 +100,16 @@ int64_t switch_ffn_capacity(int64_t T, int64_t N, double CF) {
   return (int64_t)c;
 }
 
+size_t switch_ffn_workspace_bytes_topk(int64_t T, int64_t d, int64_t F, int64_t N, double CF,
+                                       int k, int dtype) {
+  sffn::Shape s;
+  if (make_shape(T, d, F, N, CF, dtype, k, &s) != SFFN_OK) return 0;
+  return sffn::workspace_layout(s, nullptr, nullptr);
+}
+
 size_t switch_ffn_workspace_bytes(int64_t T, int64_t d, int64_t F, int64_t N, double CF,
                                   int dtype) {
-  sffn::Shape s;
-  if (make_shape(T, d, F, N, CF, dtype, &s) != SFFN_OK) return 0;
-  return sffn::workspace_layout(s, nullptr, nullptr);
+  return switch_ffn_workspace_bytes_topk(T, d, F, N, CF, 1, dtype);
 }
 
 int switch_ffn_num_stages(void) { return kNumStages; }
@@ -119,17 +133,17 @@ const char* switch_ffn_status_string(int status) {
   }
 }
 
-int switch_ffn_forward_ex(const void* x, const float* Wr, const void* W1, const void* b1,
-                          const void* W2, const void* b2, int64_t T, int64_t d, int64_t F,
-                          int64_t N, double CF, int dtype, void* y, int32_t* expert_idx,
-                          int32_t* slot, float* gate, float* aux_loss, void* workspace,
-                          size_t workspace_bytes, void* stream, uint32_t flags,
-                          const sffn_stats* stats, void* const* stage_events) {
+int switch_ffn_forward_topk(const void* x, const float* Wr, const void* W1, const void* b1,
+                            const void* W2, const void* b2, int64_t T, int64_t d, int64_t F,
+                            int64_t N, double CF, int k, int dtype, void* y, int32_t* expert_idx,
+                            int32_t* slot, float* gate, float* aux_loss, void* workspace,
+                            size_t workspace_bytes, void* stream, uint32_t flags,
+                            const sffn_stats* stats, void* const* stage_events) {
   if (!x || !Wr || !W1 || !W2 || !y || !expert_idx || !slot || !gate || !aux_loss)
     return SFFN_EINVAL;
   if (flags & ~(uint32_t)SFFN_NO_RESIDUAL) return SFFN_EINVAL;
   sffn::Shape s;
-  const int rc = make_shape(T, d, F, N, CF, dtype, &s);
+  const int rc = make_shape(T, d, F, N, CF, dtype, k, &s);
   if (rc != SFFN_OK) return rc;
   if (dtype == SFFN_BF16 &&
       !(aligned16(x) && aligned16(Wr) && aligned16(W1) && aligned16(W2) && aligned16(y)))
@@ -175,8 +189,21 @@ int switch_ffn_forward_ex(const void* x, const float* Wr, const void* W1, const 
   if ((e = mark(5)) != hipSuccess) return record_hip_error(e, "event record");
   if ((e = sffn::launch_ffn2(s, in, ws, out, no_res, st)) != hipSuccess)
     return record_hip_error(e, kStageNames[5]);
+  if (s.k == 2 && (e = sffn::launch_combine(s, in, ws, out, no_res, st)) != hipSuccess)
+    return record_hip_error(e, "combine");
   if ((e = mark(6)) != hipSuccess) return record_hip_error(e, "event record");
   return SFFN_OK;
+}
+
+int switch_ffn_forward_ex(const void* x, const float* Wr, const void* W1, const void* b1,
+                          const void* W2, const void* b2, int64_t T, int64_t d, int64_t F,
+                          int64_t N, double CF, int dtype, void* y, int32_t* expert_idx,
+                          int32_t* slot, float* gate, float* aux_loss, void* workspace,
+                          size_t workspace_bytes, void* stream, uint32_t flags,
+                          const sffn_stats* stats, void* const* stage_events) {
+  return switch_ffn_forward_topk(x, Wr, W1, b1, W2, b2, T, d, F, N, CF, 1, dtype, y, expert_idx,
+                                 slot, gate, aux_loss, workspace, workspace_bytes, stream, flags,
+                                 stats, stage_events);
 }
 
 int switch_ffn_forward(const void* x, const float* Wr, const void* W1, const void* b1,

@@ -29,8 +29,10 @@ constexpr int kScanSegs = 32;
 __global__ void __launch_bounds__(32 * kScanSegs)
 dispatch_scan_kernel(const int* __restrict__ cnt, const float* __restrict__ ppart, int nblk,
                      int N, int C, int* __restrict__ base, int* __restrict__ hist,
-                     int* __restrict__ acc, double* __restrict__ psum) {
+                     int* __restrict__ acc, double* __restrict__ psum,
+                     const int* __restrict__ cnt1, int* __restrict__ hist1) {
   __shared__ int part[kScanSegs][33];
+  __shared__ int part1[kScanSegs][33];
   __shared__ double ppart_s[kScanSegs][33];
   const int el = threadIdx.x & 31;
   const int seg = threadIdx.x >> 5;
@@ -38,7 +40,7 @@ dispatch_scan_kernel(const int* __restrict__ cnt, const float* __restrict__ ppar
   const int per = (nblk + kScanSegs - 1) / kScanSegs;
   const int c0 = min(nblk, seg * per);
   const int c1 = min(nblk, c0 + per);
-  int s = 0;
+  int s = 0, s1 = 0;
   double ps = 0.0;
   if (e < N) {
 #pragma unroll 4
@@ -46,8 +48,11 @@ dispatch_scan_kernel(const int* __restrict__ cnt, const float* __restrict__ ppar
       s += cnt[(size_t)c * N + e];
       ps += (double)ppart[(size_t)c * N + e];
     }
+    if (cnt1)
+      for (int c = c0; c < c1; ++c) s1 += cnt1[(size_t)c * N + e];
   }
   part[seg][el] = s;
+  part1[seg][el] = s1;
   ppart_s[seg][el] = ps;
   __syncthreads();
   if (e >= N) return;
@@ -60,22 +65,25 @@ dispatch_scan_kernel(const int* __restrict__ cnt, const float* __restrict__ ppar
     run += v;
   }
   if (seg == 0) {
-    int total = 0;
+    int total = 0, total1 = 0;
     double ptot = 0.0;
     for (int q = 0; q < kScanSegs; ++q) {
       total += part[q][el];
+      total1 += part1[q][el];
       ptot += ppart_s[q][el];
     }
     hist[e] = total;
     acc[e] = min(total, C);
     psum[e] = ptot;
+    if (hist1) hist1[e] = total1;
   }
 }
 
 hipError_t launch_dispatch_scan(const Shape& s, const Workspace& ws, hipStream_t st) {
   const dim3 grid((unsigned)((s.N + 31) / 32)), block(32 * kScanSegs);
   hipLaunchKernelGGL(dispatch_scan_kernel, grid, block, 0, st, ws.cnt, ws.ppart,
-                     s.n_route_blocks, s.N, s.C, ws.base, ws.hist, ws.acc, ws.psum);
+                     s.n_route_blocks, s.N, s.C, ws.base, ws.hist, ws.acc, ws.psum,
+                     s.k == 2 ? ws.cnt1 : nullptr, s.k == 2 ? ws.hist1 : nullptr);
   return hipGetLastError();
 }
 
@@ -202,9 +210,84 @@ dispatch_scatter_kernel(const int32_t* __restrict__ expert_idx, const int* __res
   }
 }
 
+// ---------------------------------------------------------------------------
+// Top-2 dispatch: slots and the row maps of both choices of every token (each
+// expert column in token order).  The residual path is left to the combine,
+// which writes every y row.  Block 0 also writes the expert offsets, the aux
+// loss (f from the top-1 counts) and the optional statistics.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256)
+dispatch_scatter_top2_kernel(const int32_t* __restrict__ expert_idx, const int* __restrict__ base,
+                             const int* __restrict__ lrank, const int* __restrict__ hist,
+                             const int* __restrict__ hist1, const int* __restrict__ acc,
+                             const double* __restrict__ psum, int T, int N, int C,
+                             const float* __restrict__ gate, int32_t* __restrict__ slot,
+                             int* __restrict__ row2tok, float* __restrict__ rowgate,
+                             int* __restrict__ offset, float* __restrict__ aux_loss,
+                             int32_t* __restrict__ stat_count, int32_t* __restrict__ stat_accepted,
+                             int32_t* __restrict__ stat_dropped) {
+  __shared__ int off_s[SFFN_MAX_EXPERTS + 1];
+  __shared__ int tsum[256];
+  __shared__ double red[256];
+
+  block_offsets(acc, N, off_s, tsum);
+
+  const int b = blockIdx.x;
+  const int tb = b * kRouteTokens;
+  if (threadIdx.x < 2 * kRouteTokens) {
+    const int t = tb + (threadIdx.x >> 1);
+    const size_t i = 2 * (size_t)t + (threadIdx.x & 1);
+    if (t < T) {
+      const int e = expert_idx[i];
+      const int r = base[(size_t)b * N + e] + lrank[i];
+      if (r < C) {
+        slot[i] = r;
+        row2tok[off_s[e] + r] = t;
+        rowgate[off_s[e] + r] = gate[i];
+      } else {
+        slot[i] = -1;
+      }
+    }
+  }
+
+  if (b != 0) return;
+  for (int i = threadIdx.x; i <= N; i += 256) offset[i] = off_s[i];
+  // aux = N * sum_i (hist1_i / T) * (psum_i / T), summed in a fixed tree order.
+  double part = 0.0;
+  int accepted = 0;
+  for (int i = threadIdx.x; i < N; i += 256) {
+    part += (double)hist1[i] * psum[i];
+    accepted += acc[i];
+    if (stat_count) stat_count[i] = hist[i];
+    if (stat_accepted) stat_accepted[i] = acc[i];
+  }
+  red[threadIdx.x] = part;
+  tsum[threadIdx.x] = accepted;
+  __syncthreads();
+  for (int w = 128; w >= 1; w >>= 1) {
+    if (threadIdx.x < w) {
+      red[threadIdx.x] += red[threadIdx.x + w];
+      tsum[threadIdx.x] += tsum[threadIdx.x + w];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const double Td = (double)T;
+    aux_loss[0] = (float)((double)N * red[0] / (Td * Td));
+    if (stat_dropped) stat_dropped[0] = 2 * T - tsum[0];
+  }
+}
+
 hipError_t launch_dispatch_scatter(const Shape& s, const Inputs& in, const Workspace& ws,
                                    const Outputs& out, bool no_residual, hipStream_t st) {
   const dim3 grid((unsigned)s.n_route_blocks), block(256);
+  if (s.k == 2) {
+    hipLaunchKernelGGL(dispatch_scatter_top2_kernel, grid, block, 0, st, out.expert_idx, ws.base,
+                       ws.lrank, ws.hist, ws.hist1, ws.acc, ws.psum, s.T, s.N, s.C, out.gate,
+                       out.slot, ws.row2tok, ws.rowgate, ws.offset, out.aux_loss,
+                       out.stat_count, out.stat_accepted, out.stat_dropped);
+    return hipGetLastError();
+  }
   const int esize = s.dtype == SFFN_BF16 ? 2 : 4;
   hipLaunchKernelGGL(dispatch_scatter_kernel, grid, block, 0, st, out.expert_idx, ws.base,
                      ws.lrank, ws.hist, ws.acc, ws.psum, s.T, s.N, s.C, s.d, esize, in.x, out.y,

@@ -159,14 +159,8 @@ __device__ __forceinline__ int find_tile(int t, int stride, int n_tiles, int n_n
     const int rest = t / n_ntiles;
     const int mc = rest % n_mchunks;
     const int e = rest / n_mchunks;
-    // The expert's rows split evenly over the chunks it needs, so that its
-    // chunks (which read the same weights, at the same time on one XCD) stream
-    // in step and the second reader of a weight line finds it in L2.
-    const int n_e = offset[e + 1] - offset[e];
-    const int used = (n_e + ROWS - 1) / ROWS;
-    const int per = used > 0 ? (n_e + used - 1) / used : 0;
-    const int rbeg = offset[e] + mc * per;
-    const int nrows = mc < used ? min(n_e - mc * per, per) : 0;
+    const int rbeg = offset[e] + mc * ROWS;
+    const int nrows = min(offset[e + 1] - rbeg, ROWS);
     if (nrows > 0) {
       d = FfnTile{e, nt, rbeg, nrows};
       return t;
@@ -225,7 +219,10 @@ ffn_bf16_kernel(const uint16_t* __restrict__ act, uint32_t act_bytes,
   const __amdgpu_buffer_rsrc_t gate_src = make_rsrc(rowgate, SECOND ? (uint32_t)max_rows * 4u : 0u);
   const __amdgpu_buffer_rsrc_t out_src = make_rsrc(out, out_bytes);
   const __amdgpu_buffer_rsrc_t x_src =
-      make_rsrc(xres, (SECOND && !no_residual) ? (uint32_t)T * (uint32_t)d_model * 2u : 0u);
+      make_rsrc(xres, (SECOND && !(no_residual & 1)) ? (uint32_t)T * (uint32_t)d_model * 2u : 0u);
+  // FFN2 output rows: the tokens' rows of y, or (bit 1 of no_residual, top-2
+  // routing) the expert buffer's own rows, gate-scaled without the residual.
+  const bool rowout = SECOND && (no_residual & 2) != 0;
 
   // Per-tile lookups: row token and gate (thread r: row r) and the tile's
   // bias (thread i: 16-byte chunk i, staged in LDS for the epilogue).
@@ -528,7 +525,9 @@ ffn_bf16_kernel(const uint16_t* __restrict__ act, uint32_t act_bytes,
           }
           __builtin_amdgcn_raw_buffer_store_b128(
               yr, out_src,
-              (int)(ok ? ((uint32_t)tok_s[rr] * (uint32_t)d_model + (uint32_t)col) * 2u : kOob), 0,
+              (int)(ok ? ((uint32_t)(rowout ? cur.rbeg + rr : tok_s[rr]) * (uint32_t)d_model + (uint32_t)col) * 2u
+                       : kOob),
+              0,
               kCpolNonTemporal);
         }
       }
@@ -703,6 +702,8 @@ static int rows_tiles(int C) {
 // fp32 experts: one thread per output element, fp32 FMA in k order.  Used for
 // the fp32 variant of the layer (small parity shapes).
 // ---------------------------------------------------------------------------
+// FFN2 with bit 1 of no_residual (top-2 routing): out is the expert buffer's
+// rows, gate the per-row gate, and no residual is added.
 template <bool SECOND>
 __global__ void __launch_bounds__(256)
 ffn_f32_kernel(const float* __restrict__ act, const float* __restrict__ W,
@@ -724,10 +725,12 @@ ffn_f32_kernel(const float* __restrict__ act, const float* __restrict__ W,
   if (bias) s += bias[(size_t)e * Nout + n];
   if (!SECOND) {
     out[(size_t)row * Nout + n] = fmaxf(s, 0.f);
+  } else if (no_residual & 2) {
+    out[(size_t)row * d_model + n] = gate[row] * s;
   } else {
     const size_t o = (size_t)tok * d_model + n;
     float yv = gate[tok] * s;
-    if (!no_residual) yv += xres[o];
+    if (!(no_residual & 1)) yv += xres[o];
     out[o] = yv;
   }
 }
@@ -782,9 +785,15 @@ hipError_t launch_ffn2(const Shape& s, const Inputs& in, const Workspace& ws, co
   if (s.C <= 0) return hipSuccess;
   if (s.dtype == SFFN_FP32) {
     const dim3 grid((unsigned)((s.d + 15) / 16), (unsigned)((s.C + 15) / 16), (unsigned)s.N);
-    hipLaunchKernelGGL(ffn_f32_kernel<true>, grid, dim3(256), 0, st, (const float*)ws.H,
-                       (const float*)in.W2, (const float*)in.b2, ws.offset, ws.row2tok, out.gate,
-                       (const float*)in.x, (float*)out.y, s.F, s.d, s.d, no_residual ? 1 : 0);
+    if (s.k == 2)
+      hipLaunchKernelGGL(ffn_f32_kernel<true>, grid, dim3(256), 0, st, (const float*)ws.H,
+                         (const float*)in.W2, (const float*)in.b2, ws.offset, ws.row2tok,
+                         ws.rowgate, (const float*)nullptr, (float*)ws.Y2, s.F, s.d, s.d, 3);
+    else
+      hipLaunchKernelGGL(ffn_f32_kernel<true>, grid, dim3(256), 0, st, (const float*)ws.H,
+                         (const float*)in.W2, (const float*)in.b2, ws.offset, ws.row2tok,
+                         out.gate, (const float*)in.x, (float*)out.y, s.F, s.d, s.d,
+                         no_residual ? 1 : 0);
     return hipGetLastError();
   }
   FfnArgs a{};
@@ -801,7 +810,78 @@ hipError_t launch_ffn2(const Shape& s, const Inputs& in, const Workspace& ws, co
   a.K = s.F;
   a.Nout = s.d;
   a.no_residual = no_residual ? 1 : 0;
+  if (s.k == 2) {  // gate-scaled rows of the expert buffer; the combine adds them up
+    a.out = (uint16_t*)ws.Y2;
+    a.out_bytes = (uint32_t)((size_t)s.max_rows * s.d * 2);
+    a.no_residual = 3;
+  }
   launch_ffn_bf16<true>(a, s, st);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Top-2 combine: y_t = x_t + Y2[row of choice 0] + Y2[row of choice 1], over
+// the accepted choices, summed in fp32 in that order and rounded once (Y2
+// holds gate-scaled expert outputs).  One wave per token row; bf16: 8
+// elements per lane and step (16-byte accesses), fp32: one.
+// ---------------------------------------------------------------------------
+template <bool BF16>
+__global__ void __launch_bounds__(256)
+combine_top2_kernel(const void* __restrict__ xv, const void* __restrict__ Y2v,
+                    const int32_t* __restrict__ expert_idx, const int32_t* __restrict__ slot,
+                    const int* __restrict__ offset, int T, int d, int no_residual,
+                    void* __restrict__ yv) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (t >= T) return;
+  int row[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int sl = slot[2 * (size_t)t + c];
+    row[c] = sl >= 0 ? offset[expert_idx[2 * (size_t)t + c]] + sl : -1;
+  }
+  if constexpr (BF16) {
+    const uint16_t* x = (const uint16_t*)xv + (size_t)t * d;
+    const uint16_t* Y2 = (const uint16_t*)Y2v;
+    uint16_t* y = (uint16_t*)yv + (size_t)t * d;
+    for (int i = lane * 8; i < d; i += 64 * 8) {  // d % 8 == 0
+      float acc[8];
+      const u32x4 xq = no_residual ? u32x4{0, 0, 0, 0} : load16(x + i);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[j] = bf16_bits_to_f32(j & 1 ? xq[j / 2] >> 16 : xq[j / 2] & 0xffffu);
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        if (row[c] < 0) continue;
+        const u32x4 v = load16(Y2 + (size_t)row[c] * d + i);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] += bf16_bits_to_f32(j & 1 ? v[j / 2] >> 16 : v[j / 2] & 0xffffu);
+      }
+      store16(y + i, u32x4{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+                           pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7])});
+    }
+  } else {
+    const float* x = (const float*)xv + (size_t)t * d;
+    const float* Y2 = (const float*)Y2v;
+    float* y = (float*)yv + (size_t)t * d;
+    for (int i = lane; i < d; i += 64) {
+      float acc = no_residual ? 0.f : x[i];
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+        if (row[c] >= 0) acc += Y2[(size_t)row[c] * d + i];
+      y[i] = acc;
+    }
+  }
+}
+
+hipError_t launch_combine(const Shape& s, const Inputs& in, const Workspace& ws,
+                          const Outputs& out, bool no_residual, hipStream_t st) {
+  const dim3 grid((unsigned)((s.T + 3) / 4)), block(256);
+  if (s.dtype == SFFN_BF16)
+    hipLaunchKernelGGL(combine_top2_kernel<true>, grid, block, 0, st, in.x, ws.Y2, out.expert_idx,
+                       out.slot, ws.offset, s.T, s.d, no_residual ? 1 : 0, out.y);
+  else
+    hipLaunchKernelGGL(combine_top2_kernel<false>, grid, block, 0, st, in.x, ws.Y2, out.expert_idx,
+                       out.slot, ws.offset, s.T, s.d, no_residual ? 1 : 0, out.y);
   return hipGetLastError();
 }
 

@@ -611,11 +611,12 @@ static bool logits_fit_offsets(const Shape& s) {
 static bool router_is_tiled(const Shape& s) {
   return s.dtype == SFFN_BF16 && s.N % 4 == 0 && logits_fit_offsets(s) &&
          tiled_planes_bytes(s) < ((size_t)1 << 31) - ((size_t)8 << 20) &&
-         (s.N > 128 || (s.N > 64 && s.T >= 256 * 128));
+         (s.k == 2 || s.N > 128 || (s.N > 64 && s.T >= 256 * 128));
 }
 
+// Top-2 routing always stages the logits (the fused epilogue is top-1 only).
 bool router_is_fused(const Shape& s) {
-  return s.dtype == SFFN_BF16 && s.N <= 128 && !router_is_tiled(s);
+  return s.dtype == SFFN_BF16 && s.k == 1 && s.N <= 128 && !router_is_tiled(s);
 }
 
 hipError_t launch_router_logits(const Shape& s, const Inputs& in, const Workspace& ws,
@@ -783,6 +784,128 @@ softmax_route_kernel(const float* __restrict__ logits, int T, int N,
 }
 
 // ---------------------------------------------------------------------------
+// Top-2 routing over staged logits.  One block per routing block of
+// kRouteTokens tokens, each wave every 4th token; lane l holds experts
+// l, l+64, ... (NPL of them).
+//   m = max z, e0 = lowest index with z = m, e1 = lowest index of the largest
+//   logit other than e0 (fp32), S = sum exp(z - m): gate0 = 1/S = p[t, e0],
+//   gate1 = exp(z[e1] - m)/S = p[t, e1] (raw gates);
+//   ppart[b, i] = sum of p over the block, cnt[b, i] = tokens of the block
+//   holding i among their two choices, cnt1[b, i] = tokens whose top-1 is i,
+//   lrank[2t + c] = earlier tokens of the block holding e_c among their choices.
+// Sums run in fixed orders, so results are bitwise reproducible.
+// ---------------------------------------------------------------------------
+template <int NPL>
+__global__ void __launch_bounds__(256)
+softmax_route_top2_kernel(const float* __restrict__ logits, int T, int N,
+                          int32_t* __restrict__ expert_idx, float* __restrict__ gate,
+                          float* __restrict__ ppart, int* __restrict__ cnt,
+                          int* __restrict__ cnt1, int* __restrict__ lrank) {
+  constexpr int WAVES = 4;
+  __shared__ float pacc[WAVES][NPL * 64];
+  __shared__ int eid_s[kRouteTokens][2];
+  __shared__ int cnt_s[NPL * 64], cnt1_s[NPL * 64];
+
+  const int b = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int tb = b * kRouteTokens;
+
+  for (int i = threadIdx.x; i < NPL * 64; i += 256) {
+    cnt_s[i] = 0;
+    cnt1_s[i] = 0;
+  }
+  float acc[NPL];
+#pragma unroll
+  for (int q = 0; q < NPL; ++q) acc[q] = 0.f;
+
+  // Lane-local then cross-lane maximum with the lowest index on ties, skipping `skip`.
+  auto argmax = [&](const float (&v)[NPL], int skip, float& m, int& arg) {
+    m = -INFINITY;
+    arg = 0x7fffffff;
+#pragma unroll
+    for (int q = 0; q < NPL; ++q) {
+      const int i = lane + 64 * q;
+      if (i < N && i != skip && (v[q] > m || (v[q] == m && i < arg))) {
+        m = v[q];
+        arg = i;
+      }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float om = __shfl_xor(m, off);
+      const int oa = __shfl_xor(arg, off);
+      if (om > m || (om == m && oa < arg)) {
+        m = om;
+        arg = oa;
+      }
+    }
+  };
+  for (int j = wave; j < kRouteTokens; j += WAVES) {
+    const int t = tb + j;
+    if (t >= T) {
+      if (lane == 0) eid_s[j][0] = eid_s[j][1] = -1;
+      continue;
+    }
+    float v[NPL];
+#pragma unroll
+    for (int q = 0; q < NPL; ++q) {
+      const int i = lane + 64 * q;
+      v[q] = i < N ? logits[(size_t)t * N + i] : -INFINITY;
+    }
+    float m, m1;
+    int e0, e1;
+    argmax(v, -1, m, e0);
+    argmax(v, e0, m1, e1);
+    float s = 0.f;
+#pragma unroll
+    for (int q = 0; q < NPL; ++q) {
+      v[q] = (lane + 64 * q < N) ? expf(v[q] - m) : 0.f;
+      s += v[q];
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+    const float inv = 1.0f / s;
+#pragma unroll
+    for (int q = 0; q < NPL; ++q) acc[q] += v[q] * inv;
+    if (lane == 0) {
+      expert_idx[2 * (size_t)t] = e0;
+      expert_idx[2 * (size_t)t + 1] = e1;
+      gate[2 * (size_t)t] = inv;
+      gate[2 * (size_t)t + 1] = expf(m1 - m) * inv;
+      eid_s[j][0] = e0;
+      eid_s[j][1] = e1;
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < NPL; ++q) pacc[wave][lane + 64 * q] = acc[q];
+  __syncthreads();
+
+  for (int i = threadIdx.x; i < N; i += 256) {
+    float p = 0.f;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) p += pacc[w][i];
+    ppart[(size_t)b * N + i] = p;
+  }
+  if (threadIdx.x < 2 * kRouteTokens) {
+    const int j = threadIdx.x >> 1, c = threadIdx.x & 1;
+    const int e = eid_s[j][c];
+    if (e >= 0) {
+      int r = 0;
+      for (int s2 = 0; s2 < j; ++s2) r += (eid_s[s2][0] == e) + (eid_s[s2][1] == e);
+      lrank[2 * (size_t)(tb + j) + c] = r;
+      atomicAdd(&cnt_s[e], 1);
+      if (c == 0) atomicAdd(&cnt1_s[e], 1);
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < N; i += 256) {
+    cnt[(size_t)b * N + i] = cnt_s[i];
+    cnt1[(size_t)b * N + i] = cnt1_s[i];
+  }
+}
+
+// ---------------------------------------------------------------------------
 // The same for N % 4 == 0 with 16-byte loads: lane l of a wave holds experts
 // 4 (64 q + l) + c, c = 0..3, q = 0..NQ-1, so one load instruction of a wave
 // covers 1 KB of a logit row.  A wave routes every 4th token of the block and
@@ -939,6 +1062,21 @@ hipError_t launch_softmax_route(const Shape& s, const Inputs& in, const Workspac
                                 const Outputs& out, hipStream_t st) {
   if (router_is_fused(s)) return launch_router_fused(s, in, ws, out, st);
   const dim3 grid((unsigned)s.n_route_blocks), block(256);
+  if (s.k == 2) {
+    const int npl = (s.N + 63) / 64;
+#define SFFN_TOP2(K)                                                                             \
+  hipLaunchKernelGGL(softmax_route_top2_kernel<K>, grid, block, 0, st, ws.logits, s.T, s.N,      \
+                     out.expert_idx, out.gate, ws.ppart, ws.cnt, ws.cnt1, ws.lrank)
+    if (npl <= 1) SFFN_TOP2(1);
+    else if (npl <= 2) SFFN_TOP2(2);
+    else if (npl <= 4) SFFN_TOP2(4);
+    else if (npl <= 8) SFFN_TOP2(8);
+    else if (npl <= 16) SFFN_TOP2(16);
+    else if (npl <= 32) SFFN_TOP2(32);
+    else SFFN_TOP2(64);
+#undef SFFN_TOP2
+    return hipGetLastError();
+  }
   if (s.N % 4 == 0 && logits_fit_offsets(s)) {
     const int nq = (s.N + 255) / 256;
 #define SFFN_SOFTMAX_VEC(K)                                                                      \

@@ -14,9 +14,10 @@ constexpr int kRouteTokens = 32;
 
 struct Shape {
   int T, d, F, N, C;
+  int k;                // experts per token (1: Switch routing, 2: top-2)
   int dtype;            // SFFN_FP32 / SFFN_BF16
   int n_route_blocks;   // ceil(T / kRouteTokens)
-  int max_rows;         // min(T, N*C): rows the expert buffers can hold
+  int max_rows;         // min(k*T, N*C): rows the expert buffers can hold
 };
 
 struct Workspace {
@@ -24,14 +25,17 @@ struct Workspace {
   float* ppart;    // [n_route_blocks, N] sum of p[t,i] over a block's tokens
   int* cnt;        // [n_route_blocks, N] top-1 counts per block
   int* base;       // [n_route_blocks, N] tokens of expert i in earlier blocks
-  int* lrank;      // [T] rank of a token among its block's tokens of the same expert
-  int* hist;       // [N] top-1 counts (before capacity)
+  int* cnt1;       // [n_route_blocks, N] top-1 counts per block (k = 2; the aux loss)
+  int* lrank;      // [T, k] rank of a choice among its block's tokens holding the same expert
+  int* hist;       // [N] tokens holding each expert among their k choices (before capacity)
+  int* hist1;      // [N] top-1 counts (k = 2; for k = 1 the aux loss uses hist)
   int* acc;        // [N] accepted counts min(hist, C)
   int* offset;     // [N+1] exclusive scan of acc: start row of each expert
   double* psum;    // [N] sum over all tokens of p[t,i]
   int* row2tok;    // [max_rows] token of each expert-buffer row
   float* rowgate;  // [max_rows] gate of each expert-buffer row's token
   void* H;         // [max_rows, F] expert hidden activations (dtype)
+  void* Y2;        // [max_rows, d] gate-scaled expert outputs per buffer row (k = 2, dtype)
   uint16_t* planes;  // router weights split into three bf16 planes, fragment order (fused router)
 };
 
@@ -73,5 +77,8 @@ hipError_t launch_dispatch_scatter(const Shape& s, const Inputs& in, const Works
 hipError_t launch_ffn1(const Shape& s, const Inputs& in, const Workspace& ws, hipStream_t st);
 hipError_t launch_ffn2(const Shape& s, const Inputs& in, const Workspace& ws, const Outputs& out,
                        bool no_residual, hipStream_t st);
+// k = 2: y_t = x_t (or 0) + the gate-scaled expert rows of t's accepted choices.
+hipError_t launch_combine(const Shape& s, const Inputs& in, const Workspace& ws,
+                          const Outputs& out, bool no_residual, hipStream_t st);
 
 }  // namespace sffn

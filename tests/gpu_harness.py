@@ -17,7 +17,7 @@ def announce(msg: str) -> None:
     print(f"[case] {msg}", flush=True)
 
 
-def run_gpu(w, dev_in, flags: int = 0):
+def run_gpu(w, dev_in, flags: int = 0, k: int = 1):
     import torch
 
     import sparse_mixture_experts_switchffn_amd as sffn
@@ -27,7 +27,8 @@ def run_gpu(w, dev_in, flags: int = 0):
              "accepted_count": torch.full((w.N,), -7, dtype=torch.int32, device=dev),
              "n_dropped": torch.full((1,), -7, dtype=torch.int32, device=dev)}
     out = sffn.switch_ffn_forward(dev_in["x"], dev_in["Wr"], dev_in["W1"], dev_in["b1"],
-                                  dev_in["W2"], dev_in["b2"], w.CF, flags=flags, stats=stats)
+                                  dev_in["W2"], dev_in["b2"], w.CF, flags=flags, stats=stats,
+                                  k=k)
     torch.cuda.synchronize(dev)
     y = out["y"]
     if y.dtype == torch.bfloat16:
@@ -55,7 +56,7 @@ def host_x(w):
 
 
 def oracle_ref(w, x_raw, Wr_raw, expert_idx, only_experts=None, no_residual=False,
-               experts=None):
+               experts=None, k=1):
     """The oracle on the same inputs, replaying the GPU's routing for dispatch and y."""
     x64 = synth.decode(x_raw)
     Wr64 = synth.decode(Wr_raw)
@@ -65,7 +66,7 @@ def oracle_ref(w, x_raw, Wr_raw, expert_idx, only_experts=None, no_residual=Fals
             return (synth.decode(ew["W1"]), synth.decode(ew["b1"]), synth.decode(ew["W2"]),
                     synth.decode(ew["b2"]))
     return oracle.forward(x64, Wr64, experts, w.CF, w.dtype, no_residual=no_residual,
-                          expert_idx=expert_idx, only_experts=only_experts)
+                          expert_idx=expert_idx, only_experts=only_experts, k=k)
 
 
 def rel_l2(a, b):
@@ -73,11 +74,35 @@ def rel_l2(a, b):
     return float(np.linalg.norm(a - b) / (nb if nb > 0 else 1.0))
 
 
+def near_tie_second(z, tol=TIE_TOL):
+    """Tokens whose 2nd and 3rd largest logits differ by at most tol (top-2 routing)."""
+    if z.shape[1] < 3:
+        return np.zeros(z.shape[0], dtype=bool)
+    part = np.sort(z, axis=1)
+    return (part[:, -2] - part[:, -3]) <= tol
+
+
 def check_routing(gpu, ref):
     """expert_idx, slot, gate, aux and stats.  Returns the near-tie count."""
     z = ref["logits"]
     tie = oracle.near_tie_tokens(z, TIE_TOL)
     eg = gpu["expert_idx"]
+    if eg.ndim == 2:  # top-2: both choices; a near-tie of either makes the token ambiguous
+        tie2 = tie | near_tie_second(z)
+        bad = np.nonzero(np.any(eg != ref["router_expert_idx"], axis=1) & ~tie2)[0]
+        assert bad.size == 0, f"expert_idx differs at {bad[:10]} (outside near-ties)"
+        srt = -np.sort(-z, axis=1)
+        for t in np.nonzero(tie2)[0]:  # each choice within tolerance of its rank's logit
+            assert z[t, eg[t, 0]] >= srt[t, 0] - TIE_TOL and z[t, eg[t, 1]] >= srt[t, 1] - TIE_TOL
+        assert np.array_equal(gpu["slot"], ref["slot"]), \
+            f"slot differs at {np.nonzero(np.any(gpu['slot'] != ref['slot'], axis=1))[0][:10]}"
+        gerr = np.max(np.abs(gpu["gate"] - ref["gate"]))
+        assert gerr <= GATE_TOL, f"gate error {gerr:.3e}"
+        assert abs(gpu["aux_loss"] - ref["aux_loss"]) <= AUX_TOL, (gpu["aux_loss"], ref["aux_loss"])
+        assert np.array_equal(gpu["expert_count"], ref["hist"])
+        assert np.array_equal(gpu["accepted_count"], ref["accepted"])
+        assert gpu["n_dropped"] == int(np.sum(ref["slot"] < 0))
+        return int(tie2.sum())
     bad = np.nonzero((eg != ref["router_expert_idx"]) & ~tie)[0]
     assert bad.size == 0, f"expert_idx differs at {bad[:10]} (outside near-ties)"
     if tie.any():
@@ -98,6 +123,8 @@ def check_routing(gpu, ref):
 def check_y(w, gpu, ref, x_bits, rows=None, no_residual=False):
     """Dropped rows bit-exact (x, or 0 without the residual); accepted rows to tolerance."""
     dropped = ref["slot"] < 0
+    if dropped.ndim == 2:  # top-2: a token passes through unchanged only when both are dropped
+        dropped = np.all(dropped, axis=1)
     if no_residual:
         assert np.all(gpu["y"][dropped] == 0.0), "dropped rows not zero"
     else:

@@ -91,3 +91,35 @@ def test_status_strings():
     for c in (S.SFFN_OK, S.SFFN_EINVAL, S.SFFN_EDTYPE, S.SFFN_EWORKSPACE, S.SFFN_EUNSUPPORTED,
               S.SFFN_EHIP, -99):
         assert isinstance(S.switch_ffn_status_string(c), str)
+
+
+def _call_topk(k, **over):
+    fake = 0x100000
+    a = dict(x=fake, Wr=fake, W1=fake, b1=None, W2=fake, b2=None, T=64, d=32, F=64, N=4, CF=1.0,
+             dtype=S.SFFN_BF16, y=fake, expert_idx=fake, slot=fake, gate=fake, aux=fake,
+             ws=fake, ws_bytes=1 << 40, stream=None, flags=0)
+    a.update(over)
+    return B.lib().switch_ffn_forward_topk(
+        a["x"], a["Wr"], a["W1"], a["b1"], a["W2"], a["b2"], a["T"], a["d"], a["F"], a["N"],
+        a["CF"], k, a["dtype"], a["y"], a["expert_idx"], a["slot"], a["gate"], a["aux"], a["ws"],
+        a["ws_bytes"], a["stream"], a["flags"], None, None)
+
+
+@pytest.mark.parametrize("k,over,code", [
+    (0, {}, S.SFFN_EINVAL), (3, {}, S.SFFN_EINVAL), (2, dict(N=1), S.SFFN_EINVAL),
+    (2, dict(x=None), S.SFFN_EINVAL), (2, dict(dtype=3), S.SFFN_EDTYPE),
+    (2, dict(d=36), S.SFFN_EUNSUPPORTED), (2, dict(ws_bytes=1000), S.SFFN_EWORKSPACE),
+    (2, dict(T=1 << 20, d=512, F=512, N=2, CF=1.0), S.SFFN_EUNSUPPORTED),  # 2T rows x F x 4 >= 2^31
+])
+def test_forward_topk_rejects_before_launch(k, over, code):
+    assert _call_topk(k, **over) == code
+
+
+def test_workspace_bytes_topk():
+    one = S.switch_ffn_workspace_bytes(8192, 768, 3072, 64, 1.25, S.SFFN_BF16)
+    assert S.switch_ffn_workspace_bytes_topk(8192, 768, 3072, 64, 1.25, 1, S.SFFN_BF16) == one
+    two = S.switch_ffn_workspace_bytes_topk(8192, 768, 3072, 64, 1.25, 2, S.SFFN_BF16)
+    # twice the expert rows (H and the per-row outputs), top-1 counts, two ranks per token
+    assert two > one + 8192 * 3072 * 2 + 2 * 8192 * 768 * 2 - 8192 * 768 * 2
+    assert S.switch_ffn_workspace_bytes_topk(8192, 768, 3072, 1, 1.25, 2, S.SFFN_BF16) == 0
+    assert S.switch_ffn_workspace_bytes_topk(8192, 768, 3072, 64, 1.25, 3, S.SFFN_BF16) == 0
