@@ -53,6 +53,8 @@ def parse():
     p.add_argument("--graph", type=int, default=10,
                    help="forward calls per captured HIP graph in the timed region (0 = eager launches)")
     p.add_argument("--quiet", action="store_true", help="only the JSON line on stdout")
+    p.add_argument("--topk", type=int, default=1, choices=(1, 2),
+                   help="experts per token: 1 (Switch routing, the headline) or 2 (top-2)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="run only a plain device copy of 1 GiB three times (calibrates the "
                         "rocprofv3 FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -139,7 +141,7 @@ def measured_traffic(kernel: str, workload: str):
         return None
 
 
-def algorithmic_bytes(w, stage, accepted, active, esize, dropped=0):
+def algorithmic_bytes(w, stage, accepted, active, esize, dropped=0, k=1):
     """Bytes a stage must move at minimum, from what it reads and writes once.
 
     The router runs one of two ways (the library's choice, mirrored here):
@@ -158,20 +160,27 @@ def algorithmic_bytes(w, stage, accepted, active, esize, dropped=0):
           written + b1 + the row-to-token map.
     ffn2: W2 of active experts + H rows + the x rows of the residual + the y rows
           written + b2 + gate and row-to-token entries.
+    Top-2 (k = 2): A counts accepted choices; the router always stages the logits and
+    writes two choices, gates and ranks per token; dispatch_scatter copies no rows;
+    ffn2 writes the gate-scaled expert rows and its stage also holds the combine
+    (x and those rows read once, y written).
     """
     A = accepted
     T, N, d = w.T, w.N, w.d
     nblk = (T + 31) // 32
     bf16 = w.dtype == "bf16"
-    tiled = bf16 and N % 4 == 0 and (N > 128 or (N > 64 and T >= 256 * 128))
-    fused = bf16 and N <= 128 and not tiled
+    tiled = bf16 and N % 4 == 0 and (k == 2 or N > 128 or (N > 64 and T >= 256 * 128))
+    fused = bf16 and k == 1 and N <= 128 and not tiled
     wbytes = active * w.F * w.d * esize
     bias1 = active * w.F * esize if w.has_bias else 0
     bias2 = active * w.d * esize if w.has_bias else 0
-    outs = T * 12 + nblk * N * 8
+    outs = T * 12 * k + nblk * N * (8 + 4 * (k - 1))
     if stage == "ffn1":
         return wbytes + A * w.d * esize + A * w.F * esize + bias1 + A * 4
     if stage == "ffn2":
+        if k == 2:
+            return (wbytes + A * w.F * esize + A * w.d * esize + bias2 + A * 8
+                    + 2 * T * d * esize + A * d * esize)
         return wbytes + A * w.F * esize + 2 * A * w.d * esize + bias2 + A * 8
     if stage == "router_logits":
         if fused:
@@ -184,6 +193,8 @@ def algorithmic_bytes(w, stage, accepted, active, esize, dropped=0):
     if stage == "dispatch_scan":
         return nblk * N * 12 + N * 16
     if stage == "dispatch_scatter":
+        if k == 2:
+            return T * 40 + A * 8
         return T * 20 + A * 8 + 2 * dropped * d * esize
     return None
 
@@ -206,7 +217,7 @@ def cpu_baseline(w, budget_s, args):
     experts = (dec["W1"], dec["b1"], dec["W2"], dec["b2"])
     passes, t0 = 0, time.perf_counter()
     while True:
-        oracle.forward(dec["x"], dec["Wr"], experts, w.CF, w.dtype)
+        oracle.forward(dec["x"], dec["Wr"], experts, w.CF, w.dtype, k=getattr(args, "topk", 1))
         passes += 1
         el = time.perf_counter() - t0
         if el >= budget_s or passes >= 1000:
@@ -243,8 +254,9 @@ def main():
     stats = {"expert_count": torch.zeros(N, dtype=torch.int32, device=dev),
              "accepted_count": torch.zeros(N, dtype=torch.int32, device=dev),
              "n_dropped": torch.zeros(1, dtype=torch.int32, device=dev)}
+    K = args.topk
     out = sffn.switch_ffn_forward(inp["x"], inp["Wr"], inp["W1"], inp["b1"], inp["W2"], inp["b2"],
-                                  w.CF, stats=stats)
+                                  w.CF, stats=stats, k=K)
     bufs = {k: out[k] for k in ("y", "expert_idx", "slot", "gate", "aux_loss", "workspace")}
     nst = sffn.switch_ffn_num_stages()
     names = [sffn.switch_ffn_stage_name(i) for i in range(nst)]
@@ -252,7 +264,7 @@ def main():
 
     def step(events=None):
         sffn.switch_ffn_forward(inp["x"], inp["Wr"], inp["W1"], inp["b1"], inp["W2"], inp["b2"],
-                                w.CF, stats=stats, stage_events=events, **bufs)
+                                w.CF, stats=stats, stage_events=events, k=K, **bufs)
 
     for _ in range(args.warmup):
         step()
@@ -346,17 +358,18 @@ def main():
     active = int((acc > 0).sum())
     dropped = int(stats["n_dropped"].cpu()[0])
     dominant = max(stage_ms, key=stage_ms.get)
-    alg = algorithmic_bytes(w, dominant, accepted, active, esize, dropped)
+    alg = algorithmic_bytes(w, dominant, accepted, active, esize, dropped, K)
     stage_table = {}
     for name, ms in stage_ms.items():
-        b = algorithmic_bytes(w, name, accepted, active, esize, dropped)
+        b = algorithmic_bytes(w, name, accepted, active, esize, dropped, K)
         gbs = b / (ms * 1e-3) / 1e9 if (b and ms > 0) else None
         stage_table[name] = {"ms": ms, "algorithmic_bytes": b, "GB_per_s": gbs,
                              "hbm_frac": gbs / HBM_PEAK_GBS if gbs else None}
     achieved = alg / (stage_ms[dominant] * 1e-3) / 1e9 if alg else None
     gemm_flops = 4.0 * accepted * w.d * w.F
     gemm_ms = stage_ms.get("ffn1", 0.0) + stage_ms.get("ffn2", 0.0)
-    traffic = measured_traffic(dominant, w.name)
+    wname = w.name + ("_top2" if K == 2 else "")
+    traffic = measured_traffic(dominant, wname)
 
     result = {
         "metric": "SwitchFFN fwd tokens/s",
@@ -371,8 +384,9 @@ def main():
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic (seeded counter-based generator; x ~ N(0,1), W ~ N(0,0.02^2))",
-        "config": {"workload": w.name, "tokens": T, "d_model": w.d, "d_ff": w.F, "experts": N,
-                   "capacity_factor": w.CF, "capacity": sffn.switch_ffn_capacity(T, N, w.CF),
+        "config": {"workload": wname, "tokens": T, "d_model": w.d, "d_ff": w.F, "experts": N,
+                   "capacity_factor": w.CF, "capacity": sffn.switch_ffn_capacity(K * T, N, w.CF),
+                   "experts_per_token": K,
                    "router_dtype": "fp32", "accepted_tokens": accepted, "dropped_tokens": dropped,
                    "active_experts": active, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": achieved,
