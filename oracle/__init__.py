@@ -11,10 +11,12 @@ from .switchffn_oracle import (  # noqa: F401
     dispatch_topk,
     expert_ffn,
     forward,
+    forward_reroute,
     near_tie_tokens,
     round_to_bf16,
     round_to_dtype,
     router,
+    reroute_overflow,
     router_logits,
     second_choice,
     softmax,

@@ -36,6 +36,16 @@ expert column is filled in token order (a token holds at most one position
 per expert, so both choices of a token are ranked by token); f_i of the aux
 loss stays the top-1 (argmax) share.
 
+No-Token-Left-Behind rerouting ([Switch summary] "Distributed Implementation
+and Expert Capacity", the No-Token-Left-Behind experiment, and section 5 on
+Appendix B / Figure 11): tokens that overflow their first choice are sent to
+their second choice.  Reading: two stages (the figure's two-stage process);
+stage 1 is the top-1 dispatch; stage 2 takes the overflowed tokens in token
+order and fills each expert's slots left after stage 1 (positions
+accepted_1[e] ..  C-1) with those whose second choice it is; a token accepted
+in stage 2 uses that expert and its gate p[t, e2]; a token refused twice
+passes through (y = x) and reports its first choice.
+
 Pins (tests/test_oracle_pins.py): the worked aux-loss example of the
 Math-LLMs card (1.15), the uniform-routing closed forms (aux = 1), the
 one-expert limit (aux -> N, closed form), N = 1 dense-FFN reduction, the x = 0
@@ -279,6 +289,86 @@ def forward(x, Wr, experts, CF: float, dtype: str = "fp32", *, no_residual: bool
     return {
         "C": C, "logits": r["logits"], "probs": r["probs"], "expert_idx": eidx,
         "router_expert_idx": r["expert_idx"], "gate": gate, "aux_loss": aux,
+        "y64": y, "y": round_to_dtype(y, dtype), **dp,
+    }
+
+
+def reroute_overflow(first: np.ndarray, second: np.ndarray, N: int, C: int) -> dict:
+    """Two-stage dispatch: top-1 first, then overflowed tokens to their second choice."""
+    T = len(first)
+    d1 = dispatch(first, N, C)
+    used = d1["accepted"].copy()            # stage-1 rows of each expert
+    expert = first.copy()
+    slot = d1["slot"].copy()
+    count2 = np.zeros(N, dtype=np.int64)
+    for t in range(T):                      # stage 2, token order
+        if slot[t] >= 0:
+            continue
+        e = int(second[t])
+        pos = used[e] + count2[e]           # next free position after stage 1
+        count2[e] += 1
+        if pos < C:
+            slot[t] = pos
+            expert[t] = e
+    accepted = np.minimum(used + count2, C)
+    offset = np.zeros(N + 1, dtype=np.int64)
+    offset[1:] = np.cumsum(accepted)
+    row2tok = np.empty(int(offset[-1]), dtype=np.int64)
+    for t in range(T):
+        if slot[t] >= 0:
+            row2tok[offset[int(expert[t])] + slot[t]] = t
+    return {"hist": d1["hist"], "rank": d1["rank"], "slot": slot, "accepted": accepted,
+            "offset": offset, "row2tok": row2tok, "expert": expert, "rerouted": count2}
+
+
+def forward_reroute(x, Wr, experts, CF: float, dtype: str = "fp32", *, no_residual: bool = False,
+                    expert_idx: Optional[np.ndarray] = None,
+                    only_experts: Optional[Iterable[int]] = None) -> dict:
+    """The top-1 layer with No-Token-Left-Behind rerouting (see the header).
+
+    expert_idx: replay a given pair of choices [T, 2] (first, second) instead of the
+    oracle's own; the returned expert_idx is the expert each token ends in.
+    """
+    x = np.asarray(x, np.float64)
+    T = x.shape[0]
+    N = np.asarray(Wr).shape[0]
+    if N < 2:
+        raise ValueError("rerouting needs N >= 2")
+    C = capacity(T, N, CF)
+    r = router(x, Wr)
+    first = r["expert_idx"]
+    own = np.stack([first, second_choice(r["logits"], first)], axis=1)
+    choices = own if expert_idx is None else np.asarray(expert_idx, np.int64).reshape(T, 2)
+    dp = reroute_overflow(choices[:, 0], choices[:, 1], N, C)
+    eidx = dp.pop("expert")
+    gate = r["probs"][np.arange(T), eidx]
+    aux = aux_loss(choices[:, 0], r["probs"])
+
+    if callable(experts):
+        get = experts
+    else:
+        W1, b1, W2, b2 = experts
+        def get(e):
+            return (W1[e], None if b1 is None else b1[e], W2[e], None if b2 is None else b2[e])
+
+    y = np.zeros_like(x) if no_residual else x.copy()
+    todo = range(N) if only_experts is None else sorted(set(int(e) for e in only_experts))
+    if only_experts is not None:
+        for e in range(N):
+            if e not in todo:
+                y[dp["row2tok"][dp["offset"][e]:dp["offset"][e + 1]]] = np.nan
+    for e in todo:
+        rows = dp["row2tok"][dp["offset"][e]:dp["offset"][e + 1]]
+        if len(rows) == 0:
+            continue
+        W1e, b1e, W2e, b2e = get(e)
+        o = expert_ffn(x[rows], W1e, b1e, W2e, b2e)
+        contrib = gate[rows, None] * o
+        y[rows] = contrib if no_residual else x[rows] + contrib
+
+    return {
+        "C": C, "logits": r["logits"], "probs": r["probs"], "expert_idx": eidx,
+        "choices": choices, "router_choices": own, "gate": gate, "aux_loss": aux,
         "y64": y, "y": round_to_dtype(y, dtype), **dp,
     }
 

@@ -130,3 +130,76 @@ def brute_forward_top2(x, Wr, W1, b1, W2, b2, CF, no_residual=False):
     aux *= N
     return {"C": C, "expert_idx": [list(c) for c in choices], "slot": slot, "gate": gate,
             "aux_loss": aux, "y": y, "probs": probs}
+
+
+def brute_forward_reroute(x, Wr, W1, b1, W2, b2, CF, no_residual=False):
+    """Top-1 routing with No-Token-Left-Behind rerouting, one token at a time: a token
+    refused by its first choice (rank >= C) takes the next free position of its second
+    choice after that expert's first-stage tokens, if one is left."""
+    T = len(x)
+    N = len(Wr)
+    d = len(x[0]) if T else len(Wr[0])
+    F = len(W1[0])
+    C = math.floor(CF * T / N)
+    choices, probs = [], []
+    for t in range(T):
+        z = [dot(x[t], Wr[i]) for i in range(N)]
+        z32 = [to_f32(v) for v in z]
+        first = 0
+        for i in range(1, N):
+            if z32[i] > z32[first]:
+                first = i
+        second = 1 if first == 0 else 0
+        for i in range(N):
+            if i != first and z32[i] > z32[second]:
+                second = i
+        m = max(z)
+        ex = [math.exp(v - m) for v in z]
+        s = math.fsum(ex)
+        choices.append((first, second))
+        probs.append([v / s for v in ex])
+
+    first_rank = [sum(1 for s_ in range(t) if choices[s_][0] == choices[t][0]) for t in range(T)]
+    stage1 = [first_rank[t] < C for t in range(T)]
+    used = [min(C, sum(1 for t in range(T) if choices[t][0] == e)) for e in range(N)]
+    expert, slot = [], []
+    for t in range(T):
+        if stage1[t]:
+            expert.append(choices[t][0])
+            slot.append(first_rank[t])
+            continue
+        e = choices[t][1]
+        before = sum(1 for s_ in range(t) if not stage1[s_] and choices[s_][1] == e)
+        pos = used[e] + before
+        if pos < C:
+            expert.append(e)
+            slot.append(pos)
+        else:
+            expert.append(choices[t][0])
+            slot.append(-1)
+
+    y, gate = [], []
+    for t in range(T):
+        e = expert[t]
+        g = probs[t][e]
+        gate.append(g)
+        if slot[t] < 0:
+            y.append([0.0] * d if no_residual else list(x[t]))
+            continue
+        h = []
+        for j in range(F):
+            a = dot(W1[e][j], x[t]) + (b1[e][j] if b1 is not None else 0.0)
+            h.append(a if a > 0.0 else 0.0)
+        row = []
+        for i in range(d):
+            o = dot(W2[e][i], h) + (b2[e][i] if b2 is not None else 0.0)
+            row.append(g * o if no_residual else x[t][i] + g * o)
+        y.append(row)
+
+    aux = 0.0
+    for i in range(N):
+        f_i = sum(1 for t in range(T) if choices[t][0] == i) / T
+        P_i = math.fsum(probs[t][i] for t in range(T)) / T
+        aux += f_i * P_i
+    aux *= N
+    return {"C": C, "expert_idx": expert, "slot": slot, "gate": gate, "aux_loss": aux, "y": y}

@@ -13,7 +13,7 @@ import os
 import numpy as np
 
 import oracle.switchffn_oracle as O
-from bruteforce import brute_forward, brute_forward_top2
+from bruteforce import brute_forward, brute_forward_reroute, brute_forward_top2
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
@@ -347,6 +347,73 @@ def pin_top2_capacity_and_aux():
     assert np.array_equal(acc, np.minimum(r2["hist"], 18))
     r0 = O.forward(x, Wr, (W1, b1, W2, b2), CF=0.0, k=2)
     assert np.all(r0["slot"] == -1) and np.array_equal(r0["y64"], x)
+
+
+# ---------------------------------------------------------------------------
+# No-Token-Left-Behind rerouting (overflow tokens to their second choice).
+# ---------------------------------------------------------------------------
+def pin_reroute_bruteforce_agreement():
+    cases = [
+        dict(seed=51, T=12, d=4, F=5, N=3, CF=0.5, bias=True),
+        dict(seed=52, T=40, d=5, F=6, N=4, CF=1.0, bias=False),
+        dict(seed=53, T=60, d=6, F=4, N=6, CF=0.75, bias=True),
+        dict(seed=54, T=33, d=3, F=7, N=2, CF=0.6, bias=True),
+    ]
+    for c in cases:
+        x, Wr, W1, b1, W2, b2 = random_case(c["seed"], c["T"], c["d"], c["F"], c["N"], c["bias"])
+        for nr in (False, True):
+            r = O.forward_reroute(x, Wr, (W1, b1, W2, b2), CF=c["CF"], no_residual=nr)
+            b = brute_forward_reroute(_tolist(x), _tolist(Wr), _tolist(W1), _tolist(b1),
+                                      _tolist(W2), _tolist(b2), c["CF"], no_residual=nr)
+            assert r["C"] == b["C"]
+            assert list(r["expert_idx"]) == b["expert_idx"]
+            assert list(r["slot"]) == b["slot"]
+            _close(r["gate"], b["gate"], 1e-12)
+            assert abs(r["aux_loss"] - b["aux_loss"]) < 1e-12
+            _close(r["y64"], b["y"], 1e-12)
+
+
+def pin_reroute_without_overflow_is_top1():
+    # CF = N: nothing overflows, so rerouting changes nothing.
+    x, Wr, W1, b1, W2, b2 = random_case(55, 30, 5, 6, 4, bias=True)
+    r0 = O.forward(x, Wr, (W1, b1, W2, b2), CF=4.0)
+    r1 = O.forward_reroute(x, Wr, (W1, b1, W2, b2), CF=4.0)
+    assert np.array_equal(r0["slot"], r1["slot"]) and np.array_equal(r0["expert_idx"], r1["expert_idx"])
+    assert np.array_equal(r0["y64"], r1["y64"]) and r0["aux_loss"] == r1["aux_loss"]
+
+
+def pin_reroute_router_zero():
+    # Wr = 0: every token picks expert 0 then expert 1 (ties), gate 1/N.  Tokens 0..C-1
+    # stay with expert 0, tokens C..2C-1 are rerouted into expert 1's empty buffer at
+    # positions 0..C-1, the rest pass through.
+    N, T = 4, 20
+    x, _, W1, b1, W2, b2 = random_case(57, T, 5, 6, N, bias=True)
+    r = O.forward_reroute(x, np.zeros((N, 5)), (W1, b1, W2, b2), CF=1.0)
+    C = r["C"]
+    assert C == 5
+    for t in range(T):
+        e, want_slot = (0, t) if t < C else ((1, t - C) if t < 2 * C else (0, -1))
+        assert r["expert_idx"][t] == e and r["slot"][t] == want_slot, (t, r["expert_idx"][t], r["slot"][t])
+        want = x[t].copy()
+        if want_slot >= 0:
+            want += (np.maximum(W1[e] @ x[t] + b1[e], 0.0) @ W2[e].T + b2[e]) / N
+        _close(r["y64"][t], want, 1e-13)
+    assert np.array_equal(r["accepted"], [5, 5, 0, 0])
+
+
+def pin_reroute_fills_after_first_stage():
+    # Experts 0 and 1, C = 3.  Logits put tokens 0-4 first on expert 0 (second 1) and
+    # tokens 5-6 first on expert 1 (second 0): expert 0 takes 0, 1, 2 and refuses 3, 4;
+    # expert 1 takes 5, 6 in stage 1 and has one position left, which goes to token 3
+    # (the earlier of the two overflowed tokens); token 4 passes through.
+    x = np.array([[2.0, 1.0]] * 5 + [[1.0, 2.0]] * 2)
+    r = O.forward_reroute(x, np.eye(2), _zero_ffn(2, 3, 2), CF=1.0)
+    assert r["C"] == 3
+    assert list(r["expert_idx"]) == [0, 0, 0, 1, 0, 1, 1]
+    assert list(r["slot"]) == [0, 1, 2, 2, -1, 0, 1]
+    assert np.array_equal(r["accepted"], [3, 3])
+    p = np.exp(1.0) / (np.exp(1.0) + np.exp(2.0))   # token 3's gate on its second choice
+    assert abs(r["gate"][3] - p) < 1e-15
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

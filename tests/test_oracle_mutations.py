@@ -14,7 +14,8 @@ from oracle_pins import ALL_PINS
 
 _orig = {name: getattr(O, name) for name in
          ("capacity", "router_logits", "softmax", "top1", "dispatch", "aux_loss", "expert_ffn",
-          "round_to_bf16", "forward", "second_choice", "topk_gates", "dispatch_topk")}
+          "round_to_bf16", "forward", "second_choice", "topk_gates", "dispatch_topk",
+          "reroute_overflow")}
 
 
 def _ffn_no_b2(xe, W1e, b1e, W2e, b2e):
@@ -184,6 +185,46 @@ def _dispatch_topk_capacity_without_k(choices, N, C):
     return _orig["dispatch_topk"](choices, N, C // 2)
 
 
+def _reroute_ignores_first_stage(first, second, N, C):
+    # Stage 2 placed from position 0 instead of after the stage-1 tokens.
+    d1 = _orig["dispatch"](first, N, C)
+    r = _orig["reroute_overflow"](first, second, N, C)
+    slot = r["slot"].copy()
+    over = d1["slot"] < 0
+    slot[over & (slot >= 0)] -= d1["accepted"][r["expert"][over & (slot >= 0)]]
+    r["slot"] = slot
+    return r
+
+
+def _reroute_reverse_order(first, second, N, C):
+    T = len(first)
+    d1 = _orig["dispatch"](first, N, C)
+    r = _orig["reroute_overflow"](first, second, N, C)
+    # redo stage 2 from the last overflowed token to the first
+    used = d1["accepted"].copy()
+    count2 = np.zeros(N, dtype=np.int64)
+    slot = d1["slot"].copy()
+    expert = np.asarray(first).copy()
+    for t in reversed(range(T)):
+        if d1["slot"][t] >= 0:
+            continue
+        e = int(second[t])
+        pos = used[e] + count2[e]
+        count2[e] += 1
+        if pos < C:
+            slot[t], expert[t] = pos, e
+    r.update(slot=slot, expert=expert)
+    return r
+
+
+def _reroute_none(first, second, N, C):
+    r = _orig["reroute_overflow"](first, second, N, C)
+    d1 = _orig["dispatch"](first, N, C)
+    r.update(slot=d1["slot"], expert=np.asarray(first).copy(), accepted=d1["accepted"],
+             offset=d1["offset"], row2tok=d1["row2tok"])
+    return r
+
+
 MUTANTS = {
     "ffn_drops_b2": ("expert_ffn", _ffn_no_b2),
     "ffn_drops_b1": ("expert_ffn", _ffn_no_b1),
@@ -212,6 +253,9 @@ MUTANTS = {
     "top2_gates_renormalised": ("topk_gates", _gates_renormalised),
     "top2_first_choices_first": ("dispatch_topk", _dispatch_first_choices_first),
     "top2_capacity_without_k": ("dispatch_topk", _dispatch_topk_capacity_without_k),
+    "reroute_ignores_first_stage": ("reroute_overflow", _reroute_ignores_first_stage),
+    "reroute_reverse_order": ("reroute_overflow", _reroute_reverse_order),
+    "reroute_none": ("reroute_overflow", _reroute_none),
 }
 
 
