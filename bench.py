@@ -55,6 +55,9 @@ def parse():
     p.add_argument("--quiet", action="store_true", help="only the JSON line on stdout")
     p.add_argument("--topk", type=int, default=1, choices=(1, 2),
                    help="experts per token: 1 (Switch routing, the headline) or 2 (top-2)")
+    p.add_argument("--reroute", action="store_true",
+                   help="top-1 routing with No-Token-Left-Behind rerouting of overflowed tokens "
+                        "to their second choice")
     p.add_argument("--copy-calibration", action="store_true",
                    help="run only a plain device copy of 1 GiB three times (calibrates the "
                         "rocprofv3 FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -141,7 +144,7 @@ def measured_traffic(kernel: str, workload: str):
         return None
 
 
-def algorithmic_bytes(w, stage, accepted, active, esize, dropped=0, k=1):
+def algorithmic_bytes(w, stage, accepted, active, esize, dropped=0, k=1, reroute=False):
     """Bytes a stage must move at minimum, from what it reads and writes once.
 
     The router runs one of two ways (the library's choice, mirrored here):
@@ -164,17 +167,25 @@ def algorithmic_bytes(w, stage, accepted, active, esize, dropped=0, k=1):
     writes two choices, gates and ranks per token; dispatch_scatter copies no rows;
     ffn2 writes the gate-scaled expert rows and its stage also holds the combine
     (x and those rows read once, y written).
+    Rerouting (k = 1): the router stages the logits and writes both choices and gates
+    and the first-choice rank per token; dispatch_scan also reads the choices and
+    ranks again, writes the first-stage slot and the overflow ranks and scans the
+    overflow counts; dispatch_scatter reads both choices and gates, the first-stage
+    slot and the overflow rank, and writes expert, gate and slot per token.
     """
     A = accepted
     T, N, d = w.T, w.N, w.d
     nblk = (T + 31) // 32
     bf16 = w.dtype == "bf16"
-    tiled = bf16 and N % 4 == 0 and (k == 2 or N > 128 or (N > 64 and T >= 256 * 128))
-    fused = bf16 and k == 1 and N <= 128 and not tiled
+    two = k == 2 or reroute
+    tiled = bf16 and N % 4 == 0 and (two or N > 128 or (N > 64 and T >= 256 * 128))
+    fused = bf16 and not two and N <= 128 and not tiled
     wbytes = active * w.F * w.d * esize
     bias1 = active * w.F * esize if w.has_bias else 0
     bias2 = active * w.d * esize if w.has_bias else 0
     outs = T * 12 * k + nblk * N * (8 + 4 * (k - 1))
+    if reroute:
+        outs = T * 20 + nblk * N * 8
     if stage == "ffn1":
         return wbytes + A * w.d * esize + A * w.F * esize + bias1 + A * 4
     if stage == "ffn2":
@@ -191,8 +202,12 @@ def algorithmic_bytes(w, stage, accepted, active, esize, dropped=0, k=1):
             return T * d * 2 + N * d * 4 + 12 * N * d + outs
         return T * N * 4 + outs
     if stage == "dispatch_scan":
+        if reroute:
+            return 2 * (nblk * N * 12 + N * 16) + T * 24
         return nblk * N * 12 + N * 16
     if stage == "dispatch_scatter":
+        if reroute:
+            return T * 36 + A * 8 + 2 * dropped * d * esize
         if k == 2:
             return T * 40 + A * 8
         return T * 20 + A * 8 + 2 * dropped * d * esize
@@ -217,7 +232,11 @@ def cpu_baseline(w, budget_s, args):
     experts = (dec["W1"], dec["b1"], dec["W2"], dec["b2"])
     passes, t0 = 0, time.perf_counter()
     while True:
-        oracle.forward(dec["x"], dec["Wr"], experts, w.CF, w.dtype, k=getattr(args, "topk", 1))
+        if getattr(args, "reroute", False):
+            oracle.forward_reroute(dec["x"], dec["Wr"], experts, w.CF, w.dtype)
+        else:
+            oracle.forward(dec["x"], dec["Wr"], experts, w.CF, w.dtype,
+                           k=getattr(args, "topk", 1))
         passes += 1
         el = time.perf_counter() - t0
         if el >= budget_s or passes >= 1000:
@@ -255,8 +274,12 @@ def main():
              "accepted_count": torch.zeros(N, dtype=torch.int32, device=dev),
              "n_dropped": torch.zeros(1, dtype=torch.int32, device=dev)}
     K = args.topk
+    if args.reroute and K != 1:
+        sys.stderr.write("bench.py: --reroute is a top-1 form; it needs --topk 1\n")
+        return 2
+    FLAGS = sffn.SFFN_REROUTE_OVERFLOW if args.reroute else 0
     out = sffn.switch_ffn_forward(inp["x"], inp["Wr"], inp["W1"], inp["b1"], inp["W2"], inp["b2"],
-                                  w.CF, stats=stats, k=K)
+                                  w.CF, stats=stats, k=K, flags=FLAGS)
     bufs = {k: out[k] for k in ("y", "expert_idx", "slot", "gate", "aux_loss", "workspace")}
     nst = sffn.switch_ffn_num_stages()
     names = [sffn.switch_ffn_stage_name(i) for i in range(nst)]
@@ -264,7 +287,8 @@ def main():
 
     def step(events=None):
         sffn.switch_ffn_forward(inp["x"], inp["Wr"], inp["W1"], inp["b1"], inp["W2"], inp["b2"],
-                                w.CF, stats=stats, stage_events=events, k=K, **bufs)
+                                w.CF, stats=stats, stage_events=events, k=K, flags=FLAGS,
+                                **bufs)
 
     for _ in range(args.warmup):
         step()
@@ -358,17 +382,17 @@ def main():
     active = int((acc > 0).sum())
     dropped = int(stats["n_dropped"].cpu()[0])
     dominant = max(stage_ms, key=stage_ms.get)
-    alg = algorithmic_bytes(w, dominant, accepted, active, esize, dropped, K)
+    alg = algorithmic_bytes(w, dominant, accepted, active, esize, dropped, K, args.reroute)
     stage_table = {}
     for name, ms in stage_ms.items():
-        b = algorithmic_bytes(w, name, accepted, active, esize, dropped, K)
+        b = algorithmic_bytes(w, name, accepted, active, esize, dropped, K, args.reroute)
         gbs = b / (ms * 1e-3) / 1e9 if (b and ms > 0) else None
         stage_table[name] = {"ms": ms, "algorithmic_bytes": b, "GB_per_s": gbs,
                              "hbm_frac": gbs / HBM_PEAK_GBS if gbs else None}
     achieved = alg / (stage_ms[dominant] * 1e-3) / 1e9 if alg else None
     gemm_flops = 4.0 * accepted * w.d * w.F
     gemm_ms = stage_ms.get("ffn1", 0.0) + stage_ms.get("ffn2", 0.0)
-    wname = w.name + ("_top2" if K == 2 else "")
+    wname = w.name + ("_top2" if K == 2 else "") + ("_reroute" if args.reroute else "")
     traffic = measured_traffic(dominant, wname)
 
     result = {
@@ -386,7 +410,7 @@ def main():
         "data": "synthetic (seeded counter-based generator; x ~ N(0,1), W ~ N(0,0.02^2))",
         "config": {"workload": wname, "tokens": T, "d_model": w.d, "d_ff": w.F, "experts": N,
                    "capacity_factor": w.CF, "capacity": sffn.switch_ffn_capacity(K * T, N, w.CF),
-                   "experts_per_token": K,
+                   "experts_per_token": K, "reroute_overflow": bool(args.reroute),
                    "router_dtype": "fp32", "accepted_tokens": accepted, "dropped_tokens": dropped,
                    "active_experts": active, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": achieved,

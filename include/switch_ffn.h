@@ -73,6 +73,22 @@ extern "C" {
 
 /* forward_ex flags. */
 #define SFFN_NO_RESIDUAL 1u /* y = g*E(x) for accepted tokens and 0 for dropped ones */
+/* No-Token-Left-Behind rerouting ("Switch Transformers" summary, section 3.4,
+ * "Distributed Implementation and Expert Capacity": the No-Token-Left-Behind
+ * experiment of Appendix B, the two-stage process of Figure 11).  k = 1 only,
+ * N >= 2 (else SFFN_EINVAL).  Stage 1 is the plain top-1 dispatch.  Stage 2
+ * takes the tokens stage 1 refused, in token order, and places each in the
+ * next free position of its second choice e2 (the largest fp32 logit other
+ * than the first choice, ties -> lowest index) after e2's stage-1 tokens; a
+ * position below C is accepted, and the token then uses e2 with gate
+ * p[t, e2].  A token refused by both passes through (y = x).  Outputs:
+ * expert_idx[t] is the expert t ends in (its first choice if refused by both),
+ * gate[t] = p[t, expert_idx[t]], slot[t] its position or -1; the aux loss and
+ * stats.expert_count count first choices, accepted_count = rows each expert
+ * holds after both stages, n_dropped = tokens refused by both.  The
+ * dispatch_scan stage also holds the second stage's count and scan.  The
+ * workspace of switch_ffn_workspace_bytes() covers this flag. */
+#define SFFN_REROUTE_OVERFLOW 2u
 
 /* Limits of this library (SFFN_EUNSUPPORTED beyond them):
  *   N <= 4096;  T * max(N, d, F) < 2^30;  d * F < 2^30;
@@ -112,7 +128,8 @@ int switch_ffn_forward(const void* x, const float* Wr, const void* W1, const voi
                        size_t workspace_bytes, void* stream);
 
 /* switch_ffn_forward plus:
- *   flags         0 or SFFN_NO_RESIDUAL (a diagnostic: the bare expert term)
+ *   flags         0 or an OR of SFFN_NO_RESIDUAL (a diagnostic: the bare expert
+ *                 term) and SFFN_REROUTE_OVERFLOW (No-Token-Left-Behind)
  *   stats         optional routing statistics (NULL = none)
  *   stage_events  optional host array of switch_ffn_num_stages()+1 hipEvent_t
  *                 handles (created by the caller); event i is recorded on

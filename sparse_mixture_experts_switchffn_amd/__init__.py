@@ -14,6 +14,7 @@ from .binding import (  # noqa: F401
     SFFN_EWORKSPACE,
     SFFN_FP32,
     SFFN_NO_RESIDUAL,
+    SFFN_REROUTE_OVERFLOW,
     SFFN_OK,
     LIB_PATH,
     header_functions,

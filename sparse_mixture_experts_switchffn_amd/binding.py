@@ -24,6 +24,7 @@ SFFN_EHIP = -5
 SFFN_FP32 = 0
 SFFN_BF16 = 1
 SFFN_NO_RESIDUAL = 1
+SFFN_REROUTE_OVERFLOW = 2
 
 
 class sffn_stats(ctypes.Structure):

@@ -44,10 +44,15 @@ size_t workspace_layout(const Shape& s, Workspace* ws, char* base) {
   w.cnt = (int*)take(nb * N * sizeof(int));
   w.cnt1 = (int*)take(K == 2 ? nb * N * sizeof(int) : 0);
   w.base = (int*)take(nb * N * sizeof(int));
-  w.lrank = (int*)take(T * K * sizeof(int));
+  const size_t R = s.reroute ? 1 : 0;
+  w.lrank = (int*)take(T * (R ? 2 : K) * sizeof(int));
   w.hist = (int*)take(N * sizeof(int));
   w.hist1 = (int*)take(K == 2 ? N * sizeof(int) : 0);
   w.acc = (int*)take(N * sizeof(int));
+  w.acc2 = (int*)take(R * N * sizeof(int));
+  w.choice = (int32_t*)take(R * 2 * T * sizeof(int32_t));
+  w.gate2 = (float*)take(R * 2 * T * sizeof(float));
+  w.slot1 = (int32_t*)take(R * T * sizeof(int32_t));
   w.offset = (int*)take((N + 1) * sizeof(int));
   w.psum = (double*)take(N * sizeof(double));
   w.row2tok = (int*)take((size_t)s.max_rows * sizeof(int) + 4);
@@ -63,9 +68,10 @@ size_t workspace_layout(const Shape& s, Workspace* ws, char* base) {
 
 // Shape checks shared by workspace sizing and the forward pass.
 static int make_shape(int64_t T, int64_t d, int64_t F, int64_t N, double CF, int dtype, int k,
-                      sffn::Shape* s) {
+                      bool reroute, sffn::Shape* s) {
   if (T <= 0 || d <= 0 || F <= 0 || N <= 0 || !isfinite(CF) || CF < 0) return SFFN_EINVAL;
   if ((k != 1 && k != 2) || N < k) return SFFN_EINVAL;
+  if (reroute && (k != 1 || N < 2)) return SFFN_EINVAL;
   if (dtype != SFFN_FP32 && dtype != SFFN_BF16) return SFFN_EDTYPE;
   if (N > SFFN_MAX_EXPERTS) return SFFN_EUNSUPPORTED;
   const int64_t widest = N > d ? (N > F ? N : F) : (d > F ? d : F);
@@ -82,6 +88,7 @@ static int make_shape(int64_t T, int64_t d, int64_t F, int64_t N, double CF, int
   s->C = (int)Ce;
   s->dtype = dtype;
   s->k = k;
+  s->reroute = reroute ? 1 : 0;
   s->n_route_blocks = (int)((T + sffn::kRouteTokens - 1) / sffn::kRouteTokens);
   const int64_t cap_rows = N * Ce;
   s->max_rows = (int)(cap_rows < k * T ? cap_rows : k * T);
@@ -103,8 +110,15 @@ int64_t switch_ffn_capacity(int64_t T, int64_t N, double CF) {
 size_t switch_ffn_workspace_bytes_topk(int64_t T, int64_t d, int64_t F, int64_t N, double CF,
                                        int k, int dtype) {
   sffn::Shape s;
-  if (make_shape(T, d, F, N, CF, dtype, k, &s) != SFFN_OK) return 0;
-  return sffn::workspace_layout(s, nullptr, nullptr);
+  if (make_shape(T, d, F, N, CF, dtype, k, false, &s) != SFFN_OK) return 0;
+  size_t bytes = sffn::workspace_layout(s, nullptr, nullptr);
+  // k = 1: room for rerouting too, so one workspace serves both forms of the call.
+  sffn::Shape r;
+  if (k == 1 && make_shape(T, d, F, N, CF, dtype, k, true, &r) == SFFN_OK) {
+    const size_t rb = sffn::workspace_layout(r, nullptr, nullptr);
+    if (rb > bytes) bytes = rb;
+  }
+  return bytes;
 }
 
 size_t switch_ffn_workspace_bytes(int64_t T, int64_t d, int64_t F, int64_t N, double CF,
@@ -141,9 +155,9 @@ int switch_ffn_forward_topk(const void* x, const float* Wr, const void* W1, cons
                             const sffn_stats* stats, void* const* stage_events) {
   if (!x || !Wr || !W1 || !W2 || !y || !expert_idx || !slot || !gate || !aux_loss)
     return SFFN_EINVAL;
-  if (flags & ~(uint32_t)SFFN_NO_RESIDUAL) return SFFN_EINVAL;
+  if (flags & ~(uint32_t)(SFFN_NO_RESIDUAL | SFFN_REROUTE_OVERFLOW)) return SFFN_EINVAL;
   sffn::Shape s;
-  const int rc = make_shape(T, d, F, N, CF, dtype, k, &s);
+  const int rc = make_shape(T, d, F, N, CF, dtype, k, (flags & SFFN_REROUTE_OVERFLOW) != 0, &s);
   if (rc != SFFN_OK) return rc;
   if (dtype == SFFN_BF16 &&
       !(aligned16(x) && aligned16(Wr) && aligned16(W1) && aligned16(W2) && aligned16(y)))

@@ -20,9 +20,11 @@ namespace sffn {
 
 // ---------------------------------------------------------------------------
 // Column scan over routing blocks.  Block = 32 experts x 32 segments of routing
-// blocks (1024 threads).  Outputs base[b][e] (tokens of e in blocks < b),
-// hist[e], acc[e] = min(hist[e], C) and psum[e] = sum_b ppart[b][e] (float64,
-// segment partial sums combined in segment order).
+// blocks (1024 threads).  Outputs base[b][e] (start[e] + tokens of e in blocks
+// < b), hist[e], acc[e] = min(start[e] + hist[e], C) and psum[e] = sum_b
+// ppart[b][e] (float64, segment partial sums combined in segment order).
+// start (rerouting's second stage), ppart/psum, hist and cnt1/hist1 may be
+// null: start counts as 0 and the others are skipped.
 // ---------------------------------------------------------------------------
 constexpr int kScanSegs = 32;
 
@@ -30,7 +32,8 @@ __global__ void __launch_bounds__(32 * kScanSegs)
 dispatch_scan_kernel(const int* __restrict__ cnt, const float* __restrict__ ppart, int nblk,
                      int N, int C, int* __restrict__ base, int* __restrict__ hist,
                      int* __restrict__ acc, double* __restrict__ psum,
-                     const int* __restrict__ cnt1, int* __restrict__ hist1) {
+                     const int* __restrict__ cnt1, int* __restrict__ hist1,
+                     const int* __restrict__ start) {
   __shared__ int part[kScanSegs][33];
   __shared__ int part1[kScanSegs][33];
   __shared__ double ppart_s[kScanSegs][33];
@@ -40,14 +43,14 @@ dispatch_scan_kernel(const int* __restrict__ cnt, const float* __restrict__ ppar
   const int per = (nblk + kScanSegs - 1) / kScanSegs;
   const int c0 = min(nblk, seg * per);
   const int c1 = min(nblk, c0 + per);
-  int s = 0, s1 = 0;
+  int s = 0, s1 = 0, s0 = 0;
   double ps = 0.0;
   if (e < N) {
+    if (start) s0 = start[e];
 #pragma unroll 4
-    for (int c = c0; c < c1; ++c) {
-      s += cnt[(size_t)c * N + e];
-      ps += (double)ppart[(size_t)c * N + e];
-    }
+    for (int c = c0; c < c1; ++c) s += cnt[(size_t)c * N + e];
+    if (ppart)
+      for (int c = c0; c < c1; ++c) ps += (double)ppart[(size_t)c * N + e];
     if (cnt1)
       for (int c = c0; c < c1; ++c) s1 += cnt1[(size_t)c * N + e];
   }
@@ -56,7 +59,7 @@ dispatch_scan_kernel(const int* __restrict__ cnt, const float* __restrict__ ppar
   ppart_s[seg][el] = ps;
   __syncthreads();
   if (e >= N) return;
-  int run = 0;
+  int run = s0;
   for (int q = 0; q < seg; ++q) run += part[q][el];
 #pragma unroll 4
   for (int c = c0; c < c1; ++c) {
@@ -72,18 +75,74 @@ dispatch_scan_kernel(const int* __restrict__ cnt, const float* __restrict__ ppar
       total1 += part1[q][el];
       ptot += ppart_s[q][el];
     }
-    hist[e] = total;
-    acc[e] = min(total, C);
-    psum[e] = ptot;
+    if (hist) hist[e] = total;
+    acc[e] = min(s0 + total, C);
+    if (psum) psum[e] = ptot;
     if (hist1) hist1[e] = total1;
   }
+}
+
+// ---------------------------------------------------------------------------
+// No-Token-Left-Behind rerouting ("Switch Transformers" summary, section 3.4,
+// "Distributed Implementation and Expert Capacity", the No-Token-Left-Behind
+// experiment of Appendix B and its two-stage Figure 11), second stage, count
+// pass.  After the first stage's scan a token's position in its first choice is
+// base[b][e1] + lrank[2t]; the slot it takes there (or -1) goes to slot1[t].
+// Overflowed tokens are counted per block by second choice: cnt[b][e] (the
+// first stage's counts are spent by then) and their rank among the block's
+// overflowed tokens with the same second choice in lrank[2t + 1].
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256)
+reroute_count_kernel(const int32_t* __restrict__ choice, const int* __restrict__ base, int T,
+                     int N, int C, int* __restrict__ lrank, int32_t* __restrict__ slot1,
+                     int* __restrict__ cnt) {
+  __shared__ int cnt_s[SFFN_MAX_EXPERTS];
+  __shared__ int e2_s[kRouteTokens];
+  const int b = blockIdx.x;
+  const int tb = b * kRouteTokens;
+  for (int i = threadIdx.x; i < N; i += 256) cnt_s[i] = 0;
+  if (threadIdx.x < kRouteTokens) {
+    const int t = tb + threadIdx.x;
+    int e2 = -1;
+    if (t < T) {
+      const int r = base[(size_t)b * N + choice[2 * (size_t)t]] + lrank[2 * (size_t)t];
+      if (r < C) {
+        slot1[t] = r;
+      } else {
+        slot1[t] = -1;
+        e2 = choice[2 * (size_t)t + 1];
+      }
+    }
+    e2_s[threadIdx.x] = e2;
+  }
+  __syncthreads();
+  if (threadIdx.x < kRouteTokens) {
+    const int e = e2_s[threadIdx.x];
+    if (e >= 0) {
+      int r = 0;
+      for (int j = 0; j < (int)threadIdx.x; ++j) r += e2_s[j] == e;
+      lrank[2 * (size_t)(tb + threadIdx.x) + 1] = r;
+      atomicAdd(&cnt_s[e], 1);
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < N; i += 256) cnt[(size_t)b * N + i] = cnt_s[i];
 }
 
 hipError_t launch_dispatch_scan(const Shape& s, const Workspace& ws, hipStream_t st) {
   const dim3 grid((unsigned)((s.N + 31) / 32)), block(32 * kScanSegs);
   hipLaunchKernelGGL(dispatch_scan_kernel, grid, block, 0, st, ws.cnt, ws.ppart,
                      s.n_route_blocks, s.N, s.C, ws.base, ws.hist, ws.acc, ws.psum,
-                     s.k == 2 ? ws.cnt1 : nullptr, s.k == 2 ? ws.hist1 : nullptr);
+                     s.k == 2 ? ws.cnt1 : nullptr, s.k == 2 ? ws.hist1 : nullptr, nullptr);
+  if (!s.reroute) return hipGetLastError();
+  // Second stage: overflowed tokens by second choice, then their positions,
+  // which start after each expert's first-stage rows: base = acc + earlier
+  // blocks' overflowed tokens, acc2 = min(acc + overflowed tokens, C).
+  hipLaunchKernelGGL(reroute_count_kernel, dim3((unsigned)s.n_route_blocks), dim3(256), 0, st,
+                     ws.choice, ws.base, s.T, s.N, s.C, ws.lrank, ws.slot1, ws.cnt);
+  hipLaunchKernelGGL(dispatch_scan_kernel, grid, block, 0, st, ws.cnt, nullptr,
+                     s.n_route_blocks, s.N, s.C, ws.base, nullptr, ws.acc2, nullptr,
+                     nullptr, nullptr, ws.acc);
   return hipGetLastError();
 }
 
@@ -119,6 +178,65 @@ __device__ void block_offsets(const int* __restrict__ acc, int N, int* off_s, in
   }
   if (threadIdx.x == 255) off_s[N] = run;
   __syncthreads();
+}
+
+// Dropped tokens leave the layer unchanged (or as zero in the no-residual view):
+// the four waves of the block copy the rows of the block's flagged tokens.
+__device__ void pass_through_dropped(const int* dropped_s, int tb, int d, int esize,
+                                     const void* __restrict__ x, void* __restrict__ y,
+                                     int no_residual) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const size_t row_bytes = (size_t)d * esize;
+  for (int j = wave; j < kRouteTokens; j += 4) {
+    if (!dropped_s[j]) continue;
+    const size_t t = (size_t)(tb + j);
+    char* dst = (char*)y + t * row_bytes;
+    const char* src = (const char*)x + t * row_bytes;
+    if (((row_bytes | (size_t)x | (size_t)y) & 15) == 0) {
+      for (size_t c = (size_t)lane * 16; c < row_bytes; c += 64 * 16)
+        store16(dst + c, no_residual ? u32x4{0, 0, 0, 0} : load16(src + c));
+    } else {
+      for (size_t c = (size_t)lane * 4; c < row_bytes; c += 64 * 4)
+        *(uint32_t*)(dst + c) = no_residual ? 0u : *(const uint32_t*)(src + c);
+    }
+  }
+}
+
+// Block 0's share of a dispatch: the expert offsets, the aux loss
+// N * sum_i (f_count_i / T) * (psum_i / T) summed in a fixed tree order, and the
+// optional statistics (count[i], accepted = acc[i], dropped = slots - sum acc).
+__device__ void finish_dispatch(const int* __restrict__ f_count, const int* __restrict__ count,
+                                const int* __restrict__ acc, const double* __restrict__ psum,
+                                int T, int N, int slots, const int* off_s, int* tsum, double* red,
+                                int* __restrict__ offset, float* __restrict__ aux_loss,
+                                int32_t* __restrict__ stat_count,
+                                int32_t* __restrict__ stat_accepted,
+                                int32_t* __restrict__ stat_dropped) {
+  for (int i = threadIdx.x; i <= N; i += 256) offset[i] = off_s[i];
+  double part = 0.0;
+  int accepted = 0;
+  for (int i = threadIdx.x; i < N; i += 256) {
+    part += (double)f_count[i] * psum[i];
+    accepted += acc[i];
+    if (stat_count) stat_count[i] = count[i];
+    if (stat_accepted) stat_accepted[i] = acc[i];
+  }
+  red[threadIdx.x] = part;
+  tsum[threadIdx.x] = accepted;
+  __syncthreads();
+  for (int w = 128; w >= 1; w >>= 1) {
+    if (threadIdx.x < w) {
+      red[threadIdx.x] += red[threadIdx.x + w];
+      tsum[threadIdx.x] += tsum[threadIdx.x + w];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const double Td = (double)T;
+    aux_loss[0] = (float)((double)N * red[0] / (Td * Td));
+    if (stat_dropped) stat_dropped[0] = slots - tsum[0];
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -164,50 +282,10 @@ dispatch_scatter_kernel(const int32_t* __restrict__ expert_idx, const int* __res
   }
   __syncthreads();
 
-  // Dropped tokens leave the layer unchanged (or as zero in the no-residual view).
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const size_t row_bytes = (size_t)d * esize;
-  for (int j = wave; j < kRouteTokens; j += 4) {
-    if (!dropped_s[j]) continue;
-    const size_t t = (size_t)(tb + j);
-    char* dst = (char*)y + t * row_bytes;
-    const char* src = (const char*)x + t * row_bytes;
-    if (((row_bytes | (size_t)x | (size_t)y) & 15) == 0) {
-      for (size_t c = (size_t)lane * 16; c < row_bytes; c += 64 * 16)
-        store16(dst + c, no_residual ? u32x4{0, 0, 0, 0} : load16(src + c));
-    } else {
-      for (size_t c = (size_t)lane * 4; c < row_bytes; c += 64 * 4)
-        *(uint32_t*)(dst + c) = no_residual ? 0u : *(const uint32_t*)(src + c);
-    }
-  }
-
+  pass_through_dropped(dropped_s, tb, d, esize, x, y, no_residual);
   if (b != 0) return;
-  for (int i = threadIdx.x; i <= N; i += 256) offset[i] = off_s[i];
-  // aux = N * sum_i (hist_i / T) * (psum_i / T), summed in a fixed tree order.
-  double part = 0.0;
-  int accepted = 0;
-  for (int i = threadIdx.x; i < N; i += 256) {
-    part += (double)hist[i] * psum[i];
-    accepted += acc[i];
-    if (stat_count) stat_count[i] = hist[i];
-    if (stat_accepted) stat_accepted[i] = acc[i];
-  }
-  red[threadIdx.x] = part;
-  tsum[threadIdx.x] = accepted;
-  __syncthreads();
-  for (int w = 128; w >= 1; w >>= 1) {
-    if (threadIdx.x < w) {
-      red[threadIdx.x] += red[threadIdx.x + w];
-      tsum[threadIdx.x] += tsum[threadIdx.x + w];
-    }
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) {
-    const double Td = (double)T;
-    aux_loss[0] = (float)((double)N * red[0] / (Td * Td));
-    if (stat_dropped) stat_dropped[0] = T - tsum[0];
-  }
+  finish_dispatch(hist, hist, acc, psum, T, N, T, off_s, tsum, red, offset, aux_loss, stat_count,
+                  stat_accepted, stat_dropped);
 }
 
 // ---------------------------------------------------------------------------
@@ -251,31 +329,77 @@ dispatch_scatter_top2_kernel(const int32_t* __restrict__ expert_idx, const int* 
   }
 
   if (b != 0) return;
-  for (int i = threadIdx.x; i <= N; i += 256) offset[i] = off_s[i];
-  // aux = N * sum_i (hist1_i / T) * (psum_i / T), summed in a fixed tree order.
-  double part = 0.0;
-  int accepted = 0;
-  for (int i = threadIdx.x; i < N; i += 256) {
-    part += (double)hist1[i] * psum[i];
-    accepted += acc[i];
-    if (stat_count) stat_count[i] = hist[i];
-    if (stat_accepted) stat_accepted[i] = acc[i];
-  }
-  red[threadIdx.x] = part;
-  tsum[threadIdx.x] = accepted;
-  __syncthreads();
-  for (int w = 128; w >= 1; w >>= 1) {
-    if (threadIdx.x < w) {
-      red[threadIdx.x] += red[threadIdx.x + w];
-      tsum[threadIdx.x] += tsum[threadIdx.x + w];
+  finish_dispatch(hist1, hist, acc, psum, T, N, 2 * T, off_s, tsum, red, offset, aux_loss,
+                  stat_count, stat_accepted, stat_dropped);
+}
+
+// ---------------------------------------------------------------------------
+// Rerouting dispatch: each token's final expert, slot and gate, the row maps,
+// and the pass-through of tokens refused by both choices.  A token keeps its
+// first-stage slot if it has one; otherwise it takes position base[b][e2] +
+// lrank[2t + 1] of its second choice e2 (base already starts after e2's
+// first-stage rows) if that is below C, else it is dropped and reports its
+// first choice.  Offsets come from acc2; the aux loss and expert_count use the
+// first choices (hist), accepted_count is acc2.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256)
+dispatch_scatter_reroute_kernel(const int32_t* __restrict__ choice,
+                                const float* __restrict__ gate2, const int32_t* __restrict__ slot1,
+                                const int* __restrict__ base, const int* __restrict__ lrank,
+                                const int* __restrict__ hist, const int* __restrict__ acc2,
+                                const double* __restrict__ psum, int T, int N, int C, int d,
+                                int esize, const void* __restrict__ x, void* __restrict__ y,
+                                int no_residual, int32_t* __restrict__ expert_idx,
+                                float* __restrict__ gate, int32_t* __restrict__ slot,
+                                int* __restrict__ row2tok, float* __restrict__ rowgate,
+                                int* __restrict__ offset, float* __restrict__ aux_loss,
+                                int32_t* __restrict__ stat_count,
+                                int32_t* __restrict__ stat_accepted,
+                                int32_t* __restrict__ stat_dropped) {
+  __shared__ int off_s[SFFN_MAX_EXPERTS + 1];
+  __shared__ int tsum[256];
+  __shared__ int dropped_s[kRouteTokens];
+  __shared__ double red[256];
+
+  block_offsets(acc2, N, off_s, tsum);
+
+  const int b = blockIdx.x;
+  const int tb = b * kRouteTokens;
+  if (threadIdx.x < kRouteTokens) {
+    const int t = tb + threadIdx.x;
+    int dropped = 0;
+    if (t < T) {
+      const size_t i0 = 2 * (size_t)t;
+      int e = choice[i0], r = slot1[t];
+      float g = gate2[i0];
+      if (r < 0) {
+        const int e2 = choice[i0 + 1];
+        const int r2 = base[(size_t)b * N + e2] + lrank[i0 + 1];
+        if (r2 < C) {
+          e = e2;
+          r = r2;
+          g = gate2[i0 + 1];
+        }
+      }
+      expert_idx[t] = e;
+      gate[t] = g;
+      if (r >= 0) {
+        slot[t] = r;
+        row2tok[off_s[e] + r] = t;
+        rowgate[off_s[e] + r] = g;
+      } else {
+        slot[t] = -1;
+        dropped = 1;
+      }
     }
-    __syncthreads();
+    dropped_s[threadIdx.x] = dropped;
   }
-  if (threadIdx.x == 0) {
-    const double Td = (double)T;
-    aux_loss[0] = (float)((double)N * red[0] / (Td * Td));
-    if (stat_dropped) stat_dropped[0] = 2 * T - tsum[0];
-  }
+  __syncthreads();
+
+  pass_through_dropped(dropped_s, tb, d, esize, x, y, no_residual);
+  if (b != 0) return;
+  finish_dispatch(hist, hist, acc2, psum, T, N, T, off_s, tsum, red, offset, aux_loss,
+                  stat_count, stat_accepted, stat_dropped);
 }
 
 hipError_t launch_dispatch_scatter(const Shape& s, const Inputs& in, const Workspace& ws,
@@ -289,6 +413,14 @@ hipError_t launch_dispatch_scatter(const Shape& s, const Inputs& in, const Works
     return hipGetLastError();
   }
   const int esize = s.dtype == SFFN_BF16 ? 2 : 4;
+  if (s.reroute) {
+    hipLaunchKernelGGL(dispatch_scatter_reroute_kernel, grid, block, 0, st, ws.choice, ws.gate2,
+                       ws.slot1, ws.base, ws.lrank, ws.hist, ws.acc2, ws.psum, s.T, s.N, s.C,
+                       s.d, esize, in.x, out.y, no_residual ? 1 : 0, out.expert_idx, out.gate,
+                       out.slot, ws.row2tok, ws.rowgate, ws.offset, out.aux_loss,
+                       out.stat_count, out.stat_accepted, out.stat_dropped);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(dispatch_scatter_kernel, grid, block, 0, st, out.expert_idx, ws.base,
                      ws.lrank, ws.hist, ws.acc, ws.psum, s.T, s.N, s.C, s.d, esize, in.x, out.y,
                      no_residual ? 1 : 0, out.gate, out.slot, ws.row2tok, ws.rowgate,

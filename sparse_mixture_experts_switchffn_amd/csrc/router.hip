@@ -611,12 +611,13 @@ static bool logits_fit_offsets(const Shape& s) {
 static bool router_is_tiled(const Shape& s) {
   return s.dtype == SFFN_BF16 && s.N % 4 == 0 && logits_fit_offsets(s) &&
          tiled_planes_bytes(s) < ((size_t)1 << 31) - ((size_t)8 << 20) &&
-         (s.k == 2 || s.N > 128 || (s.N > 64 && s.T >= 256 * 128));
+         (two_choices(s) || s.N > 128 || (s.N > 64 && s.T >= 256 * 128));
 }
 
-// Top-2 routing always stages the logits (the fused epilogue is top-1 only).
+// Top-2 routing and rerouting always stage the logits (the fused epilogue is
+// top-1 only).
 bool router_is_fused(const Shape& s) {
-  return s.dtype == SFFN_BF16 && s.k == 1 && s.N <= 128 && !router_is_tiled(s);
+  return s.dtype == SFFN_BF16 && !two_choices(s) && s.N <= 128 && !router_is_tiled(s);
 }
 
 hipError_t launch_router_logits(const Shape& s, const Inputs& in, const Workspace& ws,
@@ -793,6 +794,9 @@ softmax_route_kernel(const float* __restrict__ logits, int T, int N,
 //   ppart[b, i] = sum of p over the block, cnt[b, i] = tokens of the block
 //   holding i among their two choices, cnt1[b, i] = tokens whose top-1 is i,
 //   lrank[2t + c] = earlier tokens of the block holding e_c among their choices.
+// With first_only (rerouting) cnt and lrank[2t] count the first choices alone,
+// cnt1 is not written and lrank[2t + 1] is left to the overflow count, which
+// needs the first stage's global ranks.
 // Sums run in fixed orders, so results are bitwise reproducible.
 // ---------------------------------------------------------------------------
 template <int NPL>
@@ -800,7 +804,7 @@ __global__ void __launch_bounds__(256)
 softmax_route_top2_kernel(const float* __restrict__ logits, int T, int N,
                           int32_t* __restrict__ expert_idx, float* __restrict__ gate,
                           float* __restrict__ ppart, int* __restrict__ cnt,
-                          int* __restrict__ cnt1, int* __restrict__ lrank) {
+                          int* __restrict__ cnt1, int* __restrict__ lrank, int first_only) {
   constexpr int WAVES = 4;
   __shared__ float pacc[WAVES][NPL * 64];
   __shared__ int eid_s[kRouteTokens][2];
@@ -890,9 +894,13 @@ softmax_route_top2_kernel(const float* __restrict__ logits, int T, int N,
   if (threadIdx.x < 2 * kRouteTokens) {
     const int j = threadIdx.x >> 1, c = threadIdx.x & 1;
     const int e = eid_s[j][c];
-    if (e >= 0) {
+    if (e >= 0 && !(first_only && c == 1)) {
       int r = 0;
-      for (int s2 = 0; s2 < j; ++s2) r += (eid_s[s2][0] == e) + (eid_s[s2][1] == e);
+      if (first_only) {
+        for (int s2 = 0; s2 < j; ++s2) r += eid_s[s2][0] == e;
+      } else {
+        for (int s2 = 0; s2 < j; ++s2) r += (eid_s[s2][0] == e) + (eid_s[s2][1] == e);
+      }
       lrank[2 * (size_t)(tb + j) + c] = r;
       atomicAdd(&cnt_s[e], 1);
       if (c == 0) atomicAdd(&cnt1_s[e], 1);
@@ -901,7 +909,7 @@ softmax_route_top2_kernel(const float* __restrict__ logits, int T, int N,
   __syncthreads();
   for (int i = threadIdx.x; i < N; i += 256) {
     cnt[(size_t)b * N + i] = cnt_s[i];
-    cnt1[(size_t)b * N + i] = cnt1_s[i];
+    if (cnt1) cnt1[(size_t)b * N + i] = cnt1_s[i];
   }
 }
 
@@ -1062,11 +1070,16 @@ hipError_t launch_softmax_route(const Shape& s, const Inputs& in, const Workspac
                                 const Outputs& out, hipStream_t st) {
   if (router_is_fused(s)) return launch_router_fused(s, in, ws, out, st);
   const dim3 grid((unsigned)s.n_route_blocks), block(256);
-  if (s.k == 2) {
+  if (two_choices(s)) {
+    // Rerouting keeps both choices in the workspace; the scatter writes the outputs.
+    const bool rr = s.reroute != 0;
+    int32_t* const eidx = rr ? ws.choice : out.expert_idx;
+    float* const g = rr ? ws.gate2 : out.gate;
+    int* const cnt1 = rr ? nullptr : ws.cnt1;
     const int npl = (s.N + 63) / 64;
 #define SFFN_TOP2(K)                                                                             \
   hipLaunchKernelGGL(softmax_route_top2_kernel<K>, grid, block, 0, st, ws.logits, s.T, s.N,      \
-                     out.expert_idx, out.gate, ws.ppart, ws.cnt, ws.cnt1, ws.lrank)
+                     eidx, g, ws.ppart, ws.cnt, cnt1, ws.lrank, rr ? 1 : 0)
     if (npl <= 1) SFFN_TOP2(1);
     else if (npl <= 2) SFFN_TOP2(2);
     else if (npl <= 4) SFFN_TOP2(4);

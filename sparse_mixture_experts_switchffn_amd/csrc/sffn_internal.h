@@ -15,21 +15,33 @@ constexpr int kRouteTokens = 32;
 struct Shape {
   int T, d, F, N, C;
   int k;                // experts per token (1: Switch routing, 2: top-2)
+  int reroute;          // k = 1 with overflow tokens rerouted to their second choice
   int dtype;            // SFFN_FP32 / SFFN_BF16
   int n_route_blocks;   // ceil(T / kRouteTokens)
   int max_rows;         // min(k*T, N*C): rows the expert buffers can hold
 };
 
+// The router ranks two experts per token (top-2 routing, or rerouting).
+inline bool two_choices(const Shape& s) { return s.k == 2 || s.reroute != 0; }
+
 struct Workspace {
   float* logits;   // [T, N] fp32 router logits
   float* ppart;    // [n_route_blocks, N] sum of p[t,i] over a block's tokens
-  int* cnt;        // [n_route_blocks, N] top-1 counts per block
-  int* base;       // [n_route_blocks, N] tokens of expert i in earlier blocks
+  int* cnt;        // [n_route_blocks, N] top-1 counts per block (rerouting: then the
+                   //   per-block counts of overflowed tokens by second choice)
+  int* base;       // [n_route_blocks, N] tokens of expert i in earlier blocks (rerouting:
+                   //   then acc[i] + overflowed tokens of second choice i in earlier blocks)
   int* cnt1;       // [n_route_blocks, N] top-1 counts per block (k = 2; the aux loss)
   int* lrank;      // [T, k] rank of a choice among its block's tokens holding the same expert
+                   //   (rerouting, [T, 2]: rank among the block's first choices, then among
+                   //   the block's overflowed tokens with the same second choice)
   int* hist;       // [N] tokens holding each expert among their k choices (before capacity)
   int* hist1;      // [N] top-1 counts (k = 2; for k = 1 the aux loss uses hist)
-  int* acc;        // [N] accepted counts min(hist, C)
+  int* acc;        // [N] accepted counts min(hist, C) (rerouting: after the first stage)
+  int* acc2;       // [N] rerouting: rows of each expert after both stages
+  int32_t* choice; // [T, 2] rerouting: first and second choice of each token
+  float* gate2;    // [T, 2] rerouting: p[t, choice] of both choices
+  int32_t* slot1;  // [T] rerouting: first-stage slot of each token, -1 if it overflowed
   int* offset;     // [N+1] exclusive scan of acc: start row of each expert
   double* psum;    // [N] sum over all tokens of p[t,i]
   int* row2tok;    // [max_rows] token of each expert-buffer row
@@ -71,6 +83,7 @@ hipError_t launch_softmax_route(const Shape& s, const Inputs& in, const Workspac
                                 const Outputs& out, hipStream_t st);
 bool router_is_fused(const Shape& s);
 size_t router_planes_bytes(const Shape& s);
+// Rerouting: also the overflow count of the second stage and its scan.
 hipError_t launch_dispatch_scan(const Shape& s, const Workspace& ws, hipStream_t st);
 hipError_t launch_dispatch_scatter(const Shape& s, const Inputs& in, const Workspace& ws,
                                    const Outputs& out, bool no_residual, hipStream_t st);

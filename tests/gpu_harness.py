@@ -56,8 +56,9 @@ def host_x(w):
 
 
 def oracle_ref(w, x_raw, Wr_raw, expert_idx, only_experts=None, no_residual=False,
-               experts=None, k=1):
-    """The oracle on the same inputs, replaying the GPU's routing for dispatch and y."""
+               experts=None, k=1, reroute=False):
+    """The oracle on the same inputs, replaying the GPU's routing for dispatch and y
+    (reroute: expert_idx is the GPU's [T, 2] first and second choices)."""
     x64 = synth.decode(x_raw)
     Wr64 = synth.decode(Wr_raw)
     if experts is None:
@@ -65,6 +66,9 @@ def oracle_ref(w, x_raw, Wr_raw, expert_idx, only_experts=None, no_residual=Fals
             ew = synth.expert_weights_host(w, e)
             return (synth.decode(ew["W1"]), synth.decode(ew["b1"]), synth.decode(ew["W2"]),
                     synth.decode(ew["b2"]))
+    if reroute:
+        return oracle.forward_reroute(x64, Wr64, experts, w.CF, w.dtype, no_residual=no_residual,
+                                      expert_idx=expert_idx, only_experts=only_experts)
     return oracle.forward(x64, Wr64, experts, w.CF, w.dtype, no_residual=no_residual,
                           expert_idx=expert_idx, only_experts=only_experts, k=k)
 

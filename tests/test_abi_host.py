@@ -115,6 +115,20 @@ def test_forward_topk_rejects_before_launch(k, over, code):
     assert _call_topk(k, **over) == code
 
 
+@pytest.mark.parametrize("k,over,code", [
+    (1, dict(N=1), S.SFFN_EINVAL),                 # rerouting needs a second choice
+    (2, {}, S.SFFN_EINVAL),                        # rerouting is a top-1 form
+    (1, dict(flags=S.SFFN_REROUTE_OVERFLOW | 4), S.SFFN_EINVAL),
+    (1, dict(ws_bytes=1000), S.SFFN_EWORKSPACE),
+])
+def test_reroute_rejects_before_launch(k, over, code):
+    over = dict(over)
+    over["flags"] = over.get("flags", S.SFFN_REROUTE_OVERFLOW)
+    assert _call_topk(k, **over) == code
+    if k == 1:
+        assert _call(**over) == code
+
+
 def test_workspace_bytes_topk():
     one = S.switch_ffn_workspace_bytes(8192, 768, 3072, 64, 1.25, S.SFFN_BF16)
     assert S.switch_ffn_workspace_bytes_topk(8192, 768, 3072, 64, 1.25, 1, S.SFFN_BF16) == one

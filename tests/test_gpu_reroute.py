@@ -1,0 +1,124 @@
+"""GPU parity of No-Token-Left-Behind rerouting (forward_ex with SFFN_REROUTE_OVERFLOW)
+against the CPU oracle on the same seeded inputs.
+
+The two choices of every token come from the library's own router: a top-2 call on the
+same inputs runs the same logits and softmax kernels.  They are checked against the
+oracle's choices outside near-ties, then replayed into the oracle, so that the final
+expert, slot, drop mask and statistics are compared bit-exact, gates within 1e-6, aux
+within 1e-5, y within the dtype's tolerance and dropped rows bit-exact."""
+import numpy as np
+import pytest
+
+import oracle
+import switchffn_synth as synth
+from gpu_harness import (AUX_TOL, GATE_TOL, TIE_TOL, announce, check_y, host_x,
+                         near_tie_second, oracle_ref, run_gpu)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _check_choices(choices, ref):
+    z = ref["logits"]
+    tie = oracle.near_tie_tokens(z, TIE_TOL) | near_tie_second(z)
+    bad = np.nonzero(np.any(choices != ref["router_choices"], axis=1) & ~tie)[0]
+    assert bad.size == 0, f"router choices differ at {bad[:10]} (outside near-ties)"
+    srt = -np.sort(-z, axis=1)
+    for t in np.nonzero(tie)[0]:
+        assert z[t, choices[t, 0]] >= srt[t, 0] - TIE_TOL
+        assert z[t, choices[t, 1]] >= srt[t, 1] - TIE_TOL
+    return int(tie.sum())
+
+
+def _check_routing(gpu, ref):
+    assert np.array_equal(gpu["expert_idx"], ref["expert_idx"]), \
+        f"expert differs at {np.nonzero(gpu['expert_idx'] != ref['expert_idx'])[0][:10]}"
+    assert np.array_equal(gpu["slot"], ref["slot"]), \
+        f"slot differs at {np.nonzero(gpu['slot'] != ref['slot'])[0][:10]}"
+    gerr = np.max(np.abs(gpu["gate"] - ref["gate"]))
+    assert gerr <= GATE_TOL, f"gate error {gerr:.3e}"
+    assert abs(gpu["aux_loss"] - ref["aux_loss"]) <= AUX_TOL, (gpu["aux_loss"], ref["aux_loss"])
+    assert np.array_equal(gpu["expert_count"], ref["hist"])
+    assert np.array_equal(gpu["accepted_count"], ref["accepted"])
+    assert gpu["n_dropped"] == int(np.sum(ref["slot"] < 0))
+
+
+def _case(w, full=True, want_rerouted=True):
+    from sparse_mixture_experts_switchffn_amd import SFFN_NO_RESIDUAL, SFFN_REROUTE_OVERFLOW
+
+    announce("reroute " + w.describe())
+    dev_in = synth.device_inputs(w, DEV)
+    x_raw = host_x(w)
+    Wr_raw = synth.host_array(w, "Wr").reshape(w.N, w.d)
+    gpu = run_gpu(w, dev_in, flags=SFFN_REROUTE_OVERFLOW)
+    assert gpu["expert_idx"].shape == (w.T,)
+    choices = run_gpu(w, dev_in, k=2)["expert_idx"]
+    C = oracle.capacity(w.T, w.N, w.CF)
+    experts = None
+    if not full:
+        dp = oracle.reroute_overflow(choices[:, 0], choices[:, 1], w.N, C)
+        live = np.nonzero(dp["accepted"] > 0)[0]
+        rer = np.nonzero(dp["rerouted"] > 0)[0]
+        experts = sorted({int(live[0]), int(live[-1]), int(np.argmax(dp["accepted"]))} |
+                         set(int(e) for e in np.random.default_rng(0).choice(live, 4)) |
+                         set(int(e) for e in rer[:2]))
+    ref = oracle_ref(w, x_raw, Wr_raw, choices, only_experts=experts, reroute=True)
+    ties = _check_choices(choices, ref)
+    _check_routing(gpu, ref)
+    rerouted = int(np.sum((ref["slot"] >= 0) & (ref["expert_idx"] != choices[:, 0])))
+    if want_rerouted:
+        assert rerouted > 0, "case meant to exercise the second stage reroutes nothing"
+    rows = None
+    if experts is not None:
+        rows = np.nonzero(np.all(np.isfinite(ref["y64"]), axis=1) & (ref["slot"] >= 0))[0]
+        assert rows.size > 0
+    err = check_y(w, gpu, ref, x_raw, rows=rows)
+    gnr = run_gpu(w, dev_in, flags=SFFN_REROUTE_OVERFLOW | SFFN_NO_RESIDUAL)
+    assert np.array_equal(gnr["slot"], gpu["slot"])
+    assert np.array_equal(gnr["expert_idx"], gpu["expert_idx"])
+    rnr = oracle_ref(w, x_raw, Wr_raw, choices, only_experts=experts, no_residual=True,
+                     reroute=True)
+    err_nr = check_y(w, gnr, rnr, x_raw, rows=rows, no_residual=True)
+    print(f"  C={C} ties={ties} rerouted={rerouted} dropped={int(np.sum(ref['slot'] < 0))} "
+          f"y_err={err:.2e} y_err_nr={err_nr:.2e}", flush=True)
+    return gpu, ref
+
+
+@pytest.mark.parametrize("case", [
+    dict(T=300, d=72, F=136, N=6, CF=1.0, bias_sigma=0.02, zipf_s=1.1),  # ragged tails
+    dict(T=257, d=64, F=128, N=2, CF=0.9, zipf_s=1.1),           # N = 2: the other expert
+    dict(T=640, d=256, F=512, N=16, CF=0.9, bias_sigma=0.05),    # most experts full after stage 2
+    dict(T=1000, d=128, F=256, N=130, CF=1.0, zipf_s=1.1),       # scalar logits path, N % 4 != 0
+    dict(T=1100, d=200, F=64, N=260, CF=1.0, bias_sigma=0.02, zipf_s=1.1),  # tiled logits
+    dict(T=4096, d=64, F=96, N=4, CF=1.0, zipf_s=1.1),           # several row chunks per expert
+])
+def test_reroute_bf16_shapes(case):
+    _case(synth.workload("switch_base").replace(**case))
+
+
+def test_reroute_capacity_zero():
+    """C = 0: both stages refuse every token; y = x bit-exact."""
+    _case(synth.workload("switch_base").replace(T=200, d=32, F=64, N=5, CF=0.0),
+          want_rerouted=False)
+
+
+def test_reroute_without_overflow():
+    """CF = N: nothing overflows and rerouting matches plain top-1 routing."""
+    w = synth.workload("switch_base").replace(T=512, d=64, F=128, N=8, CF=8.0)
+    gpu, ref = _case(w, want_rerouted=False)
+    assert np.all(gpu["slot"] >= 0)
+
+
+@pytest.mark.parametrize("case", [
+    dict(T=100, d=5, F=7, N=3, CF=0.7, bias_sigma=0.1, zipf_s=1.1),
+    dict(T=333, d=33, F=65, N=9, CF=1.0, bias_sigma=0.02, zipf_s=1.1),
+])
+def test_reroute_fp32_shapes(case):
+    _case(synth.workload("tiny").replace(**case))
+
+
+def test_reroute_skewed():
+    """The skewed workload (Zipf-popular experts, CF = 1), full size, in the benchmark's
+    launch configuration: every token's routing, slots, gates, aux; y on sampled experts."""
+    _case(synth.workload("skewed"), full=False)
