@@ -12,6 +12,7 @@ from .switchffn_oracle import (  # noqa: F401
     expert_ffn,
     forward,
     forward_reroute,
+    gelu,
     near_tie_tokens,
     round_to_bf16,
     round_to_dtype,

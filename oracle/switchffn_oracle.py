@@ -46,6 +46,11 @@ accepted_1[e] ..  C-1) with those whose second choice it is; a token accepted
 in stage 2 uses that expert and its gate p[t, e2]; a token refused twice
 passes through (y = x) and reports its first choice.
 
+GEGLU experts ([Switch summary] 3.2 "Expert FFNs" names GEGLU beside ReLU and
+gives no formula): the gated-GELU unit GELU(W x + b_W) * (V x + b_V) with the
+exact GELU a * Phi(a) (Phi the standard normal CDF); W1 then holds the two
+up-projections, W in rows 0..F-1 and V in rows F..2F-1, and b1 both biases.
+
 Pins (tests/test_oracle_pins.py): the worked aux-loss example of the
 Math-LLMs card (1.15), the uniform-routing closed forms (aux = 1), the
 one-expert limit (aux -> N, closed form), N = 1 dense-FFN reduction, the x = 0
@@ -60,6 +65,7 @@ import math
 from typing import Callable, Iterable, Optional
 
 import numpy as np
+from scipy.special import erf as scipy_erf
 
 
 # ----------------------------------------------------------------------------
@@ -189,11 +195,29 @@ def aux_loss(expert_idx: np.ndarray, probs: np.ndarray) -> float:
 # + b_{1,i}) + b_{2,i}; sigma = ReLU, [Switch summary] 3.2 "Expert FFNs").
 # W1 is stored [F, d] and W2 [d, F] per expert.
 # ----------------------------------------------------------------------------
-def expert_ffn(xe: np.ndarray, W1e: np.ndarray, b1e, W2e: np.ndarray, b2e) -> np.ndarray:
+def gelu(a: np.ndarray) -> np.ndarray:
+    """GELU(a) = a * Phi(a), Phi the standard normal CDF (the exact form, via erf)."""
+    return 0.5 * a * (1.0 + scipy_erf(a / math.sqrt(2.0)))
+
+
+def expert_ffn(xe: np.ndarray, W1e: np.ndarray, b1e, W2e: np.ndarray, b2e,
+               activation: str = "relu") -> np.ndarray:
+    """E(x) = W2 sigma(W1 x + b1) + b2 for the rows of xe.
+
+    activation "geglu" ([Switch summary] 3.2 names it beside ReLU): W1e holds
+    2F rows, the gate projection W (rows 0..F-1) then the linear projection V
+    (rows F..2F-1), b1e likewise, and h = GELU(W x + b_W) * (V x + b_V).
+    """
     a = xe @ np.asarray(W1e, np.float64).T
     if b1e is not None:
         a = a + np.asarray(b1e, np.float64)
-    h = np.maximum(a, 0.0)
+    if activation == "relu":
+        h = np.maximum(a, 0.0)
+    elif activation == "geglu":
+        F = a.shape[1] // 2
+        h = gelu(a[:, :F]) * a[:, F:]
+    else:
+        raise ValueError(activation)
     o = h @ np.asarray(W2e, np.float64).T
     if b2e is not None:
         o = o + np.asarray(b2e, np.float64)
@@ -235,7 +259,8 @@ ExpertSource = Callable[[int], tuple]
 
 def forward(x, Wr, experts, CF: float, dtype: str = "fp32", *, no_residual: bool = False,
             expert_idx: Optional[np.ndarray] = None,
-            only_experts: Optional[Iterable[int]] = None, k: int = 1) -> dict:
+            only_experts: Optional[Iterable[int]] = None, k: int = 1,
+            activation: str = "relu") -> dict:
     """Run the layer on float64 inputs.
 
     k: experts per token, 1 (Switch routing) or 2 (top-2 routing; expert_idx,
@@ -248,10 +273,12 @@ def forward(x, Wr, experts, CF: float, dtype: str = "fp32", *, no_residual: bool
     only_experts: compute expert outputs for these experts only; the y rows of
         other experts' accepted tokens are NaN.
     no_residual: y = g * E(x) for accepted tokens and 0 for dropped ones.
+    activation: "relu", or "geglu" (W1 [N, 2F, d] and b1 [N, 2F]; see expert_ffn).
     """
     if k == 2:
         return _forward_top2(x, Wr, experts, CF, dtype, no_residual=no_residual,
-                             expert_idx=expert_idx, only_experts=only_experts)
+                             expert_idx=expert_idx, only_experts=only_experts,
+                             activation=activation)
     if k != 1:
         raise ValueError("k must be 1 or 2")
     x = np.asarray(x, np.float64)
@@ -282,7 +309,7 @@ def forward(x, Wr, experts, CF: float, dtype: str = "fp32", *, no_residual: bool
         if len(rows) == 0:
             continue
         W1e, b1e, W2e, b2e = get(e)
-        o = expert_ffn(x[rows], W1e, b1e, W2e, b2e)
+        o = expert_ffn(x[rows], W1e, b1e, W2e, b2e, activation)
         contrib = gate[rows, None] * o
         y[rows] = contrib if no_residual else x[rows] + contrib
 
@@ -323,7 +350,8 @@ def reroute_overflow(first: np.ndarray, second: np.ndarray, N: int, C: int) -> d
 
 def forward_reroute(x, Wr, experts, CF: float, dtype: str = "fp32", *, no_residual: bool = False,
                     expert_idx: Optional[np.ndarray] = None,
-                    only_experts: Optional[Iterable[int]] = None) -> dict:
+                    only_experts: Optional[Iterable[int]] = None,
+                    activation: str = "relu") -> dict:
     """The top-1 layer with No-Token-Left-Behind rerouting (see the header).
 
     expert_idx: replay a given pair of choices [T, 2] (first, second) instead of the
@@ -362,7 +390,7 @@ def forward_reroute(x, Wr, experts, CF: float, dtype: str = "fp32", *, no_residu
         if len(rows) == 0:
             continue
         W1e, b1e, W2e, b2e = get(e)
-        o = expert_ffn(x[rows], W1e, b1e, W2e, b2e)
+        o = expert_ffn(x[rows], W1e, b1e, W2e, b2e, activation)
         contrib = gate[rows, None] * o
         y[rows] = contrib if no_residual else x[rows] + contrib
 
@@ -373,7 +401,8 @@ def forward_reroute(x, Wr, experts, CF: float, dtype: str = "fp32", *, no_residu
     }
 
 
-def _forward_top2(x, Wr, experts, CF, dtype, *, no_residual, expert_idx, only_experts) -> dict:
+def _forward_top2(x, Wr, experts, CF, dtype, *, no_residual, expert_idx, only_experts,
+                  activation) -> dict:
     """Top-2 routing: y_t = x_t + sum_c [accepted] p_{t,e_c} E_{e_c}(x_t) (see the header)."""
     x = np.asarray(x, np.float64)
     T = x.shape[0]
@@ -408,7 +437,7 @@ def _forward_top2(x, Wr, experts, CF, dtype, *, no_residual, expert_idx, only_ex
         if len(rows) == 0:
             continue
         W1e, b1e, W2e, b2e = get(e)
-        o = expert_ffn(x[rows], W1e, b1e, W2e, b2e)
+        o = expert_ffn(x[rows], W1e, b1e, W2e, b2e, activation)
         y[rows] += gate[rows, dp["row2choice"][lo:hi], None] * o   # distinct rows per expert
 
     return {

@@ -19,12 +19,25 @@ def dot(a, b) -> float:
     return math.fsum(ai * bi for ai, bi in zip(a, b))
 
 
-def brute_forward(x, Wr, W1, b1, W2, b2, CF, no_residual=False):
+def brute_gelu(a: float) -> float:
+    return a * 0.5 * math.erfc(-a / math.sqrt(2.0))
+
+
+def brute_hidden(xt, W1e, b1e, F, activation):
+    """Hidden activations of one token: ReLU of F pre-activations, or (geglu) GELU of
+    the first F times the next F."""
+    pre = [dot(W1e[j], xt) + (b1e[j] if b1e is not None else 0.0) for j in range(len(W1e))]
+    if activation == "relu":
+        return [a if a > 0.0 else 0.0 for a in pre]
+    return [brute_gelu(pre[j]) * pre[F + j] for j in range(F)]
+
+
+def brute_forward(x, Wr, W1, b1, W2, b2, CF, no_residual=False, activation="relu"):
     """All arguments are nested lists of floats (b1/b2 may be None)."""
     T = len(x)
     N = len(Wr)
     d = len(x[0]) if T else len(Wr[0])
-    F = len(W1[0])
+    F = len(W2[0][0])
     C = math.floor(CF * T / N)
 
     choice, probs = [], []
@@ -51,10 +64,7 @@ def brute_forward(x, Wr, W1, b1, W2, b2, CF, no_residual=False):
             y.append([0.0] * d if no_residual else list(x[t]))
             continue
         g = probs[t][e]
-        h = []
-        for j in range(F):
-            a = dot(W1[e][j], x[t]) + (b1[e][j] if b1 is not None else 0.0)
-            h.append(a if a > 0.0 else 0.0)
+        h = brute_hidden(x[t], W1[e], None if b1 is None else b1[e], F, activation)
         row = []
         for i in range(d):
             o = dot(W2[e][i], h) + (b2[e][i] if b2 is not None else 0.0)

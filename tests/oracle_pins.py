@@ -416,4 +416,57 @@ def pin_reroute_fills_after_first_stage():
     assert abs(r["gate"][3] - p) < 1e-15
 
 
+# ---------------------------------------------------------------------------
+# GEGLU experts.
+# ---------------------------------------------------------------------------
+# Standard normal CDF values from the printed tables: Phi(1), Phi(2), Phi(3).
+PHI_1, PHI_2, PHI_3 = 0.8413447460685429, 0.9772498680518208, 0.9986501019683699
+
+
+def pin_gelu_closed_forms():
+    a = np.array([0.0, 1.0, -1.0, 2.0, -2.0, 3.0, -3.0, 12.0, -12.0])
+    want = np.array([0.0, PHI_1, -(1 - PHI_1), 2 * PHI_2, -2 * (1 - PHI_2), 3 * PHI_3,
+                     -3 * (1 - PHI_3), 12.0, 0.0])
+    got = O.gelu(a)
+    assert np.all(np.abs(got - want) <= 1e-15 * np.maximum(1.0, np.abs(want)) + 1e-30), got - want
+    # GELU(a) - GELU(-a) = a (Phi(a) + Phi(-a) = 1), at any a
+    b = np.linspace(-7, 7, 57)
+    assert np.max(np.abs(O.gelu(b) - O.gelu(-b) - b)) < 1e-14
+
+
+def pin_geglu_expert_hand_example():
+    # d = 2, F = 1: W = [1, 0], V = [0, 1], b_W = 0, b_V = 0.5, W2 = [[2], [-1]], b2 = 0.
+    # x = (1, 1.5): GELU(1) * (1.5 + 0.5) = 2 Phi(1); o = (4 Phi(1), -2 Phi(1)).
+    W1e = np.array([[1.0, 0.0], [0.0, 1.0]])
+    b1e = np.array([0.0, 0.5])
+    W2e = np.array([[2.0], [-1.0]])
+    o = O.expert_ffn(np.array([[1.0, 1.5]]), W1e, b1e, W2e, None, "geglu")
+    _close(o, [[4 * PHI_1, -2 * PHI_1]], 1e-15)
+
+
+def pin_geglu_bruteforce_agreement():
+    for seed, T, d, F, N, CF, bias in ((61, 20, 4, 3, 3, 1.0, True), (62, 33, 6, 5, 2, 0.7, False),
+                                       (63, 48, 5, 8, 4, 1.5, True)):
+        x, Wr, W1, b1, _, _ = random_case(seed, T, d, 2 * F, N, bias)
+        rng = np.random.default_rng(seed + 100)
+        W2 = rng.normal(0, 0.5, (N, d, F))
+        b2 = rng.normal(0, 0.1, (N, d)) if bias else None
+        for nr in (False, True):
+            r = O.forward(x, Wr, (W1, b1, W2, b2), CF=CF, no_residual=nr, activation="geglu")
+            b = brute_forward(_tolist(x), _tolist(Wr), _tolist(W1), _tolist(b1), _tolist(W2),
+                              _tolist(b2), CF, no_residual=nr, activation="geglu")
+            assert list(r["slot"]) == b["slot"]
+            _close(r["y64"], b["y"], 1e-12)
+
+
+def pin_geglu_linear_branch_identity():
+    # V = 0 and b_V = 1: h = GELU(W x + b_W), so E(x) matches a one-expert GELU FFN
+    # evaluated through the Phi table at pre-activations 1, -1, 2 (x = e_i, W = diag).
+    W1e = np.vstack([np.diag([1.0, -1.0, 2.0]), np.zeros((3, 3))])
+    b1e = np.concatenate([np.zeros(3), np.ones(3)])
+    o = O.expert_ffn(np.eye(3), W1e, b1e, np.eye(3), None, "geglu")
+    _close(np.diag(o), [PHI_1, -(1 - PHI_1), 2 * PHI_2], 1e-15)
+    assert np.all(o[~np.eye(3, dtype=bool)] == 0.0)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

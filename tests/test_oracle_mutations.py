@@ -15,29 +15,29 @@ from oracle_pins import ALL_PINS
 _orig = {name: getattr(O, name) for name in
          ("capacity", "router_logits", "softmax", "top1", "dispatch", "aux_loss", "expert_ffn",
           "round_to_bf16", "forward", "second_choice", "topk_gates", "dispatch_topk",
-          "reroute_overflow")}
+          "reroute_overflow", "gelu")}
 
 
-def _ffn_no_b2(xe, W1e, b1e, W2e, b2e):
-    return _orig["expert_ffn"](xe, W1e, b1e, W2e, None)
+def _ffn_no_b2(xe, W1e, b1e, W2e, b2e, activation="relu"):
+    return _orig["expert_ffn"](xe, W1e, b1e, W2e, None, activation)
 
 
-def _ffn_no_b1(xe, W1e, b1e, W2e, b2e):
-    return _orig["expert_ffn"](xe, W1e, None, W2e, b2e)
+def _ffn_no_b1(xe, W1e, b1e, W2e, b2e, activation="relu"):
+    return _orig["expert_ffn"](xe, W1e, None, W2e, b2e, activation)
 
 
-def _ffn_no_relu(xe, W1e, b1e, W2e, b2e):
+def _ffn_no_relu(xe, W1e, b1e, W2e, b2e, activation="relu"):
     a = xe @ np.asarray(W1e).T + (0 if b1e is None else b1e)
     return a @ np.asarray(W2e).T + (0 if b2e is None else b2e)
 
 
-def _ffn_relu_after(xe, W1e, b1e, W2e, b2e):
+def _ffn_relu_after(xe, W1e, b1e, W2e, b2e, activation="relu"):
     return np.maximum(_ffn_no_relu(xe, W1e, b1e, W2e, b2e), 0.0)
 
 
-def _ffn_transposed_w1(xe, W1e, b1e, W2e, b2e):
+def _ffn_transposed_w1(xe, W1e, b1e, W2e, b2e, activation="relu"):
     W1e = np.asarray(W1e)
-    return _orig["expert_ffn"](xe, W1e.reshape(W1e.shape[::-1]), b1e, W2e, b2e)
+    return _orig["expert_ffn"](xe, W1e.reshape(W1e.shape[::-1]), b1e, W2e, b2e, activation)
 
 
 def _logits_sign(x, Wr):
@@ -225,6 +225,29 @@ def _reroute_none(first, second, N, C):
     return r
 
 
+def _gelu_tanh(a):
+    # the tanh approximation instead of the exact a * Phi(a)
+    return 0.5 * a * (1.0 + np.tanh(math.sqrt(2.0 / math.pi) * (a + 0.044715 * a ** 3)))
+
+
+def _geglu_halves_swapped(xe, W1e, b1e, W2e, b2e, activation="relu"):
+    if activation != "geglu":
+        return _orig["expert_ffn"](xe, W1e, b1e, W2e, b2e, activation)
+    F = np.asarray(W1e).shape[0] // 2
+    W1s = np.concatenate([np.asarray(W1e)[F:], np.asarray(W1e)[:F]])
+    b1s = None if b1e is None else np.concatenate([np.asarray(b1e)[F:], np.asarray(b1e)[:F]])
+    return _orig["expert_ffn"](xe, W1s, b1s, W2e, b2e, activation)
+
+
+def _geglu_relu_gate(xe, W1e, b1e, W2e, b2e, activation="relu"):
+    if activation != "geglu":
+        return _orig["expert_ffn"](xe, W1e, b1e, W2e, b2e, activation)
+    a = xe @ np.asarray(W1e).T + (0 if b1e is None else b1e)
+    F = a.shape[1] // 2
+    h = np.maximum(a[:, :F], 0.0) * a[:, F:]
+    return h @ np.asarray(W2e).T + (0 if b2e is None else b2e)
+
+
 MUTANTS = {
     "ffn_drops_b2": ("expert_ffn", _ffn_no_b2),
     "ffn_drops_b1": ("expert_ffn", _ffn_no_b1),
@@ -256,6 +279,9 @@ MUTANTS = {
     "reroute_ignores_first_stage": ("reroute_overflow", _reroute_ignores_first_stage),
     "reroute_reverse_order": ("reroute_overflow", _reroute_reverse_order),
     "reroute_none": ("reroute_overflow", _reroute_none),
+    "gelu_tanh_approximation": ("gelu", _gelu_tanh),
+    "geglu_halves_swapped": ("expert_ffn", _geglu_halves_swapped),
+    "geglu_relu_gate": ("expert_ffn", _geglu_relu_gate),
 }
 
 
