@@ -58,6 +58,8 @@ def parse():
     p.add_argument("--reroute", action="store_true",
                    help="top-1 routing with No-Token-Left-Behind rerouting of overflowed tokens "
                         "to their second choice")
+    p.add_argument("--geglu", action="store_true",
+                   help="GEGLU experts (two up-projections, W1 [N, 2F, d])")
     p.add_argument("--copy-calibration", action="store_true",
                    help="run only a plain device copy of 1 GiB three times (calibrates the "
                         "rocprofv3 FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -167,6 +169,7 @@ def algorithmic_bytes(w, stage, accepted, active, esize, dropped=0, k=1, reroute
     writes two choices, gates and ranks per token; dispatch_scatter copies no rows;
     ffn2 writes the gate-scaled expert rows and its stage also holds the combine
     (x and those rows read once, y written).
+    GEGLU experts: ffn1 reads both up-projections (2F rows of W1 and of b1).
     Rerouting (k = 1): the router stages the logits and writes both choices and gates
     and the first-choice rank per token; dispatch_scan also reads the choices and
     ranks again, writes the first-stage slot and the overflow ranks and scans the
@@ -181,13 +184,14 @@ def algorithmic_bytes(w, stage, accepted, active, esize, dropped=0, k=1, reroute
     tiled = bf16 and N % 4 == 0 and (two or N > 128 or (N > 64 and T >= 256 * 128))
     fused = bf16 and not two and N <= 128 and not tiled
     wbytes = active * w.F * w.d * esize
-    bias1 = active * w.F * esize if w.has_bias else 0
+    w1mul = 2 if w.glu else 1  # GEGLU: two up-projections (W1 and b1 of 2F rows)
+    bias1 = w1mul * active * w.F * esize if w.has_bias else 0
     bias2 = active * w.d * esize if w.has_bias else 0
     outs = T * 12 * k + nblk * N * (8 + 4 * (k - 1))
     if reroute:
         outs = T * 20 + nblk * N * 8
     if stage == "ffn1":
-        return wbytes + A * w.d * esize + A * w.F * esize + bias1 + A * 4
+        return w1mul * wbytes + A * w.d * esize + A * w.F * esize + bias1 + A * 4
     if stage == "ffn2":
         if k == 2:
             return (wbytes + A * w.F * esize + A * w.d * esize + bias2 + A * 8
@@ -232,11 +236,12 @@ def cpu_baseline(w, budget_s, args):
     experts = (dec["W1"], dec["b1"], dec["W2"], dec["b2"])
     passes, t0 = 0, time.perf_counter()
     while True:
+        act = "geglu" if w.glu else "relu"
         if getattr(args, "reroute", False):
-            oracle.forward_reroute(dec["x"], dec["Wr"], experts, w.CF, w.dtype)
+            oracle.forward_reroute(dec["x"], dec["Wr"], experts, w.CF, w.dtype, activation=act)
         else:
             oracle.forward(dec["x"], dec["Wr"], experts, w.CF, w.dtype,
-                           k=getattr(args, "topk", 1))
+                           k=getattr(args, "topk", 1), activation=act)
         passes += 1
         el = time.perf_counter() - t0
         if el >= budget_s or passes >= 1000:
@@ -264,6 +269,8 @@ def main():
     import switchffn_synth as synth
 
     w = synth.workload(args.config)
+    if args.geglu:
+        w = w.replace(glu=True)
     dev = "cuda:0"
     torch.cuda.set_device(0)
     log(args, f"bench: {w.describe()}")
@@ -277,7 +284,7 @@ def main():
     if args.reroute and K != 1:
         sys.stderr.write("bench.py: --reroute is a top-1 form; it needs --topk 1\n")
         return 2
-    FLAGS = sffn.SFFN_REROUTE_OVERFLOW if args.reroute else 0
+    FLAGS = (sffn.SFFN_REROUTE_OVERFLOW if args.reroute else 0) | (sffn.SFFN_GEGLU if w.glu else 0)
     out = sffn.switch_ffn_forward(inp["x"], inp["Wr"], inp["W1"], inp["b1"], inp["W2"], inp["b2"],
                                   w.CF, stats=stats, k=K, flags=FLAGS)
     bufs = {k: out[k] for k in ("y", "expert_idx", "slot", "gate", "aux_loss", "workspace")}
@@ -390,9 +397,10 @@ def main():
         stage_table[name] = {"ms": ms, "algorithmic_bytes": b, "GB_per_s": gbs,
                              "hbm_frac": gbs / HBM_PEAK_GBS if gbs else None}
     achieved = alg / (stage_ms[dominant] * 1e-3) / 1e9 if alg else None
-    gemm_flops = 4.0 * accepted * w.d * w.F
+    gemm_flops = (6.0 if w.glu else 4.0) * accepted * w.d * w.F
     gemm_ms = stage_ms.get("ffn1", 0.0) + stage_ms.get("ffn2", 0.0)
-    wname = w.name + ("_top2" if K == 2 else "") + ("_reroute" if args.reroute else "")
+    wname = (w.name + ("_top2" if K == 2 else "") + ("_reroute" if args.reroute else "")
+             + ("_geglu" if w.glu else ""))
     traffic = measured_traffic(dominant, wname)
 
     result = {
@@ -411,6 +419,7 @@ def main():
         "config": {"workload": wname, "tokens": T, "d_model": w.d, "d_ff": w.F, "experts": N,
                    "capacity_factor": w.CF, "capacity": sffn.switch_ffn_capacity(K * T, N, w.CF),
                    "experts_per_token": K, "reroute_overflow": bool(args.reroute),
+                   "expert_activation": "geglu" if w.glu else "relu",
                    "router_dtype": "fp32", "accepted_tokens": accepted, "dropped_tokens": dropped,
                    "active_experts": active, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": achieved,

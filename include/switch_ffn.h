@@ -89,6 +89,15 @@ extern "C" {
  * dispatch_scan stage also holds the second stage's count and scan.  The
  * workspace of switch_ffn_workspace_bytes() covers this flag. */
 #define SFFN_REROUTE_OVERFLOW 2u
+/* GEGLU experts ("Switch Transformers" summary, section 3.2, "Expert FFNs",
+ * which names GEGLU beside ReLU): W1 is [N, 2F, d] and b1 [N, 2F]; rows
+ * 0..F-1 of W1[e] are the gate projection W, rows F..2F-1 the linear
+ * projection V, and the hidden activation is
+ *   h = GELU(W x + b1[0..F)) * (V x + b1[F..2F)),  GELU(a) = a Phi(a)
+ * (the exact GELU, Phi the standard normal CDF).  W2, b2, the workspace and
+ * every other argument keep their meaning.  Any k, with or without the other
+ * flags. */
+#define SFFN_GEGLU 4u
 
 /* Limits of this library (SFFN_EUNSUPPORTED beyond them):
  *   N <= 4096;  T * max(N, d, F) < 2^30;  d * F < 2^30;
@@ -129,7 +138,8 @@ int switch_ffn_forward(const void* x, const float* Wr, const void* W1, const voi
 
 /* switch_ffn_forward plus:
  *   flags         0 or an OR of SFFN_NO_RESIDUAL (a diagnostic: the bare expert
- *                 term) and SFFN_REROUTE_OVERFLOW (No-Token-Left-Behind)
+ *                 term), SFFN_REROUTE_OVERFLOW (No-Token-Left-Behind) and
+ *                 SFFN_GEGLU (GEGLU experts)
  *   stats         optional routing statistics (NULL = none)
  *   stage_events  optional host array of switch_ffn_num_stages()+1 hipEvent_t
  *                 handles (created by the caller); event i is recorded on

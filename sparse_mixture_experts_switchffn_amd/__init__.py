@@ -15,6 +15,7 @@ from .binding import (  # noqa: F401
     SFFN_FP32,
     SFFN_NO_RESIDUAL,
     SFFN_REROUTE_OVERFLOW,
+    SFFN_GEGLU,
     SFFN_OK,
     LIB_PATH,
     header_functions,

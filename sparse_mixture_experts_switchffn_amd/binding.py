@@ -25,6 +25,7 @@ SFFN_FP32 = 0
 SFFN_BF16 = 1
 SFFN_NO_RESIDUAL = 1
 SFFN_REROUTE_OVERFLOW = 2
+SFFN_GEGLU = 4
 
 
 class sffn_stats(ctypes.Structure):
@@ -129,7 +130,8 @@ def switch_ffn_forward(x, Wr, W1, b1, W2, b2, CF: float, *, y=None, expert_idx=N
                        stats=None, stage_events=None, check: bool = True, k: int = 1) -> dict:
     """Run the layer on device tensors; returns the output tensors (allocated when not given).
 
-    x [T, d], Wr [N, d] fp32, W1 [N, F, d], b1 [N, F] | None, W2 [N, d, F], b2 [N, d] | None.
+    x [T, d], Wr [N, d] fp32, W1 [N, F, d], b1 [N, F] | None, W2 [N, d, F], b2 [N, d] | None
+    (flags with SFFN_GEGLU: W1 [N, 2F, d], b1 [N, 2F]).
     k: experts per token (1, or 2 for top-2 routing through switch_ffn_forward_topk; then
     expert_idx, slot and gate are [T, 2]).
     stats: optional dict of int32 device tensors 'expert_count' [N], 'accepted_count' [N],
@@ -140,7 +142,7 @@ def switch_ffn_forward(x, Wr, W1, b1, W2, b2, CF: float, *, y=None, expert_idx=N
 
     T, d = x.shape
     N = Wr.shape[0]
-    F = W1.shape[1]
+    F = W2.shape[2]  # W1 has 2F rows with SFFN_GEGLU
     dt = _dtype_code(x)
     dev = x.device
     if y is None:

@@ -68,7 +68,7 @@ size_t workspace_layout(const Shape& s, Workspace* ws, char* base) {
 
 // Shape checks shared by workspace sizing and the forward pass.
 static int make_shape(int64_t T, int64_t d, int64_t F, int64_t N, double CF, int dtype, int k,
-                      bool reroute, sffn::Shape* s) {
+                      bool reroute, sffn::Shape* s, bool glu = false) {
   if (T <= 0 || d <= 0 || F <= 0 || N <= 0 || !isfinite(CF) || CF < 0) return SFFN_EINVAL;
   if ((k != 1 && k != 2) || N < k) return SFFN_EINVAL;
   if (reroute && (k != 1 || N < 2)) return SFFN_EINVAL;
@@ -89,6 +89,7 @@ static int make_shape(int64_t T, int64_t d, int64_t F, int64_t N, double CF, int
   s->dtype = dtype;
   s->k = k;
   s->reroute = reroute ? 1 : 0;
+  s->glu = glu ? 1 : 0;
   s->n_route_blocks = (int)((T + sffn::kRouteTokens - 1) / sffn::kRouteTokens);
   const int64_t cap_rows = N * Ce;
   s->max_rows = (int)(cap_rows < k * T ? cap_rows : k * T);
@@ -155,9 +156,11 @@ int switch_ffn_forward_topk(const void* x, const float* Wr, const void* W1, cons
                             const sffn_stats* stats, void* const* stage_events) {
   if (!x || !Wr || !W1 || !W2 || !y || !expert_idx || !slot || !gate || !aux_loss)
     return SFFN_EINVAL;
-  if (flags & ~(uint32_t)(SFFN_NO_RESIDUAL | SFFN_REROUTE_OVERFLOW)) return SFFN_EINVAL;
+  if (flags & ~(uint32_t)(SFFN_NO_RESIDUAL | SFFN_REROUTE_OVERFLOW | SFFN_GEGLU))
+    return SFFN_EINVAL;
   sffn::Shape s;
-  const int rc = make_shape(T, d, F, N, CF, dtype, k, (flags & SFFN_REROUTE_OVERFLOW) != 0, &s);
+  const int rc = make_shape(T, d, F, N, CF, dtype, k, (flags & SFFN_REROUTE_OVERFLOW) != 0, &s,
+                            (flags & SFFN_GEGLU) != 0);
   if (rc != SFFN_OK) return rc;
   if (dtype == SFFN_BF16 &&
       !(aligned16(x) && aligned16(Wr) && aligned16(W1) && aligned16(W2) && aligned16(y)))

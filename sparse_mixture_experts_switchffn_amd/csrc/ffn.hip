@@ -10,6 +10,11 @@
 //
 //   FFN1: H[r, :] = ReLU(x[row2tok[r], :] W1[e]^T + b1[e])   (bf16 H)
 //   FFN2: y[t, :] = x[t, :] + gate[t] (H[r, :] W2[e]^T + b2[e]),  t = row2tok[r]
+//
+// GEGLU experts (named beside ReLU in the same paper's section 3.2): W1[e]
+// holds 2F rows, the gate projection W (rows 0..F-1) and the linear
+// projection V (rows F..2F-1), b1[e] both biases, and
+//   FFN1: H[r, f] = GELU(x W^T + b_W)[f] * (x V^T + b_V)[f],  GELU(a) = a Phi(a).
 #include "sffn_device.h"
 #include "sffn_internal.h"
 #include "../../include/switch_ffn.h"
@@ -81,8 +86,19 @@ constexpr int kLdsBytes = 160 * 1024;
 // the last (whose loads fetch the next tile; it may also be the first).
 enum : int { kRoundFirst = 0, kRoundMid = 1, kRoundLast = 2 };
 
-template <int MT, int FW, int WN, bool SECOND>
+// GELU(a) = a Phi(a) = a (1 + erf(a / sqrt 2)) / 2, fp32.
+__device__ __forceinline__ float gelu_f32(float a) {
+  return 0.5f * a * (1.0f + erff(a * 0.7071067811865476f));
+}
+
+template <int MT, int FW, int WN, bool SECOND, bool GLU = false>
 struct FfnGeom {
+  // GEGLU (FFN1 only): a tile's COLS weight rows are its "virtual columns": in
+  // each epilogue part of PCOLS of them, the first half are gate rows and the
+  // second half the linear rows of the same PCOLS/2 features, so a part holds
+  // both factors of its outputs.  The stage is fp32 then, as for FFN2.
+  static_assert(!(SECOND && GLU), "GEGLU is an FFN1 form");
+  static constexpr bool F32STAGE = SECOND || GLU;
   static constexpr int ROWS = MT * 32;
   static constexpr int NTHR = FW * 64;
   static constexpr int WCOLS = WN * 32;               // output columns per wave
@@ -94,7 +110,7 @@ struct FfnGeom {
   static constexpr int B_BYTES = COLS * FLDS * 2;     // the waves' weight slots
   static constexpr int FREE = A_BYTES + B_BYTES;      // LDS the epilogue may use
   static constexpr int part_bytes(int wpp) {
-    return SECOND ? ROWS * (wpp * WCOLS + 4) * 4 : ROWS * (wpp * WCOLS + 8) * 2;
+    return F32STAGE ? ROWS * (wpp * WCOLS + 4) * 4 : ROWS * (wpp * WCOLS + 8) * 2;
   }
   static constexpr int pick_wpp() {
     for (int w = FW; w > 1; --w)
@@ -105,8 +121,10 @@ struct FfnGeom {
   static constexpr int WPP = pick_wpp();
   static constexpr int NPARTS = FW / WPP;
   static constexpr int PCOLS = WPP * WCOLS;
-  static constexpr int CPR = PCOLS / 8;                           // 16-byte chunks per part row
-  static constexpr int CST = SECOND ? PCOLS + 4 : PCOLS + 8;      // staged elements per row
+  static constexpr int OPC = GLU ? PCOLS / 2 : PCOLS;             // output columns per part
+  static constexpr int OCOLS = GLU ? COLS / 2 : COLS;             // output columns per tile
+  static constexpr int CPR = OPC / 8;                             // 16-byte chunks per part row
+  static constexpr int CST = F32STAGE ? PCOLS + 4 : PCOLS + 8;    // staged elements per row
   static constexpr int XPT = (ROWS * CPR + NTHR - 1) / NTHR;      // chunks per thread and part
   // Vector-memory operations per thread, in issue order:
   static constexpr int G = AL + BL;                 // per step of a first/middle round
@@ -171,7 +189,7 @@ __device__ __forceinline__ int find_tile(int t, int stride, int n_tiles, int n_n
 
 #define SFFN_LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
-template <int MT, int FW, int WN, bool SECOND, int WPOL>
+template <int MT, int FW, int WN, bool SECOND, int WPOL, bool GLU = false>
 __global__ void __launch_bounds__(FW * 64)
 ffn_bf16_kernel(const uint16_t* __restrict__ act, uint32_t act_bytes,
                 const uint16_t* __restrict__ W, const uint16_t* __restrict__ bias,
@@ -180,11 +198,12 @@ ffn_bf16_kernel(const uint16_t* __restrict__ act, uint32_t act_bytes,
                 uint16_t* __restrict__ out, uint32_t out_bytes, int K, int Nout,
                 int n_mchunks, int n_experts, int max_rows, int T, int d_model,
                 int no_residual) {
-  using Geo = FfnGeom<MT, FW, WN, SECOND>;
+  using Geo = FfnGeom<MT, FW, WN, SECOND, GLU>;
   constexpr int ROWS = Geo::ROWS, NTHR = Geo::NTHR, AL = Geo::AL, A_BYTES = Geo::A_BYTES;
   constexpr int NPARTS = Geo::NPARTS, WPP = Geo::WPP, PCOLS = Geo::PCOLS, CPR = Geo::CPR;
   constexpr int CST = Geo::CST, XPT = Geo::XPT, BL = Geo::BL, WCOLS = Geo::WCOLS;
-  constexpr int COLS = Geo::COLS;
+  constexpr int COLS = Geo::COLS, OPC = Geo::OPC, OCOLS = Geo::OCOLS;
+  constexpr int WMUL = GLU ? 2 : 1;  // weight rows per output column
   static_assert(ROWS <= NTHR, "one thread per row for the row lookups");
   static_assert(Geo::fits, "LDS budget");
   // [activation ring (FNB tiles) | weight slots | 1 KB sink for idle loads].
@@ -198,7 +217,7 @@ ffn_bf16_kernel(const uint16_t* __restrict__ act, uint32_t act_bytes,
   char* const sink = smem + FNB * A_BYTES + Geo::B_BYTES;
   char* const stage = smem + FP * A_BYTES;
 
-  const int n_ntiles = (Nout + COLS - 1) / COLS;
+  const int n_ntiles = (Nout + OCOLS - 1) / OCOLS;
   const int n_tiles = n_ntiles * n_mchunks * n_experts;
   const int stride = gridDim.x;
   FfnTile cur;
@@ -233,11 +252,27 @@ ffn_bf16_kernel(const uint16_t* __restrict__ act, uint32_t act_bytes,
     return __uint_as_float(
         buffer_load4(gate_src, tid < dt.nrows ? (uint32_t)(dt.rbeg + tid) * 4u : kOob));
   };
+  // Weight row (and bias entry) of virtual column v of column tile nt; -1 past
+  // the last output column.
+  auto phys_row = [&](int nt, int v) -> int {
+    if constexpr (!GLU) {
+      const int n = nt * COLS + v;
+      return n < Nout ? n : -1;
+    } else {
+      constexpr int H = PCOLS / 2;
+      const int j = v % PCOLS;
+      const int f = nt * OCOLS + (v / PCOLS) * H + j % H;
+      return f < Nout ? (j >= H ? Nout + f : f) : -1;
+    }
+  };
   auto load_bias = [&](const FfnTile& dt) -> u32x4 {
     const __amdgpu_buffer_rsrc_t src =
-        make_rsrc(bias ? bias + (size_t)dt.e * Nout : bias, bias ? (uint32_t)Nout * 2u : 0u);
-    const int n = dt.nt * COLS + tid * 8;  // Nout % 8 == 0: a chunk is all in or all out
-    return buffer_load16(src, (dt.nrows > 0 && tid < COLS / 8 && n < Nout) ? (uint32_t)n * 2u : kOob);
+        make_rsrc(bias ? bias + (size_t)dt.e * WMUL * Nout : bias,
+                  bias ? (uint32_t)(WMUL * Nout) * 2u : 0u);
+    // Nout % 8 == 0 and 8-column chunks never straddle a half: a chunk is all
+    // in or all out, and contiguous in the bias.
+    const int n = tid < COLS / 8 ? phys_row(dt.nt, tid * 8) : -1;
+    return buffer_load16(src, (dt.nrows > 0 && n >= 0) ? (uint32_t)n * 2u : kOob);
   };
   // Weights: load i of a step brings rows wrow(i) of the wave's WCOLS (8i +
   // lane/8, or grouped by parity for kCpolSplitRows), 16-byte chunk lane%8 of
@@ -246,12 +281,11 @@ ffn_bf16_kernel(const uint16_t* __restrict__ act, uint32_t act_bytes,
     return WPOL == kCpolSplitRows ? 2 * (8 * (i / 2) + (lane >> 3)) + (i & 1) : i * 8 + (lane >> 3);
   };
   auto setup_b = [&](const FfnTile& dt, __amdgpu_buffer_rsrc_t& src, uint32_t (&off)[BL]) {
-    src = make_rsrc(W + (size_t)dt.e * Nout * K, (uint32_t)((size_t)Nout * K * 2));
-    const int n0 = dt.nt * COLS + wave * WCOLS;
+    src = make_rsrc(W + (size_t)dt.e * WMUL * Nout * K, (uint32_t)((size_t)WMUL * Nout * K * 2));
 #pragma unroll
     for (int i = 0; i < BL; ++i) {
-      const int nr = n0 + wrow(i);
-      off[i] = (dt.nrows > 0 && nr < Nout)
+      const int nr = phys_row(dt.nt, wave * WCOLS + wrow(i));
+      off[i] = (dt.nrows > 0 && nr >= 0)
                    ? ((uint32_t)nr * (uint32_t)K + (uint32_t)(lane & 7) * 8u) * 2u : kOob;
     }
   };
@@ -483,7 +517,7 @@ ffn_bf16_kernel(const uint16_t* __restrict__ act, uint32_t act_bytes,
             for (int m = 0; m < MT; ++m) {
               const f32x16& a = acc[m * WN + w];
               const int r = m * 32 + er;
-              if (SECOND) {
+              if (Geo::F32STAGE) {
                 *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(stage) + r * CST + pc) =
                     f32x4{a[4 * g] + b0, a[4 * g + 1] + b1, a[4 * g + 2] + b2, a[4 * g + 3] + b3};
               } else {  // H: bias, ReLU, one rounding to bf16
@@ -500,10 +534,25 @@ ffn_bf16_kernel(const uint16_t* __restrict__ act, uint32_t act_bytes,
       for (int i = 0; i < XPT; ++i) {
         const int idx = etid + i * NTHR;
         const int r = idx / CPR, c = idx % CPR;
-        const int col = cur.nt * COLS + p * PCOLS + c * 8;
+        const int col = cur.nt * OCOLS + p * OPC + c * 8;
         const bool ok = r < cur.nrows && col < Nout;
         const int rr = ok ? r : 0;
-        if (!SECOND) {
+        if (GLU) {
+          // H = GELU(gate half) * linear half, one rounding to bf16.
+          const float* srow = reinterpret_cast<const float*>(stage) + rr * CST + c * 8;
+          const f32x4 g0 = *reinterpret_cast<const f32x4*>(srow);
+          const f32x4 g1 = *reinterpret_cast<const f32x4*>(srow + 4);
+          const f32x4 l0 = *reinterpret_cast<const f32x4*>(srow + PCOLS / 2);
+          const f32x4 l1 = *reinterpret_cast<const f32x4*>(srow + PCOLS / 2 + 4);
+          const u32x4 v{pack_bf16x2(gelu_f32(g0[0]) * l0[0], gelu_f32(g0[1]) * l0[1]),
+                        pack_bf16x2(gelu_f32(g0[2]) * l0[2], gelu_f32(g0[3]) * l0[3]),
+                        pack_bf16x2(gelu_f32(g1[0]) * l1[0], gelu_f32(g1[1]) * l1[1]),
+                        pack_bf16x2(gelu_f32(g1[2]) * l1[2], gelu_f32(g1[3]) * l1[3])};
+          __builtin_amdgcn_raw_buffer_store_b128(
+              v, out_src,
+              (int)(ok ? ((uint32_t)(cur.rbeg + r) * (uint32_t)Nout + (uint32_t)col) * 2u : kOob), 0,
+              kCpolNonTemporal);
+        } else if (!SECOND) {
           const u32x4 v = load16(reinterpret_cast<const uint16_t*>(stage) + rr * CST + c * 8);
           __builtin_amdgcn_raw_buffer_store_b128(
               v, out_src,
@@ -559,15 +608,15 @@ ffn_bf16_kernel(const uint16_t* __restrict__ act, uint32_t act_bytes,
 
 #undef SFFN_LDS_PTR
 
-template <int MT, int FW, int WN, bool SECOND>
+template <int MT, int FW, int WN, bool SECOND, bool GLU>
 static int ffn_resident_blocks() {
   // Blocks of this kernel the device holds at once (a persistent grid's size).
   static const int n = [] {
     int dev = 0, cus = 0, per_cu = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, ffn_bf16_kernel<MT, FW, WN, SECOND, 0>,
-                                                     FW * 64, 0) != hipSuccess)
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu, ffn_bf16_kernel<MT, FW, WN, SECOND, 0, GLU>, FW * 64, 0) != hipSuccess)
       return 256;
     return (cus > 0 ? cus : 256) * (per_cu > 0 ? per_cu : 1);
   }();
@@ -594,48 +643,55 @@ struct FfnShape {
 };
 constexpr FfnShape kFfnShapes[] = {{4, 2}, {3, 2}, {8, 1}, {6, 1}, {4, 1}};
 
-template <int MT, int FW, int WN, bool SECOND>
+template <int MT, int FW, int WN, bool SECOND, bool GLU>
 static constexpr bool ffn_shape_ok() {
   // Two column tiles per wave only for up to 2 row tiles: beyond that the
   // registers allow one wave per SIMD, which leaves too little latency
   // hiding.  Blocks of more than 4 waves (2 per SIMD) only up to 6 row tiles
   // (registers).  One thread per row for the row lookups; the LDS budget holds.
   return (WN == 1 || MT <= 2) && (FW <= 4 || MT <= 6) && MT * 32 <= FW * 64 &&
-         FfnGeom<MT, FW, WN, SECOND>::fits;
+         FfnGeom<MT, FW, WN, SECOND, GLU>::fits;
 }
 
-template <int MT, int FW, int WN, bool SECOND>
+template <int MT, int FW, int WN, bool SECOND, bool GLU>
 static long ffn_resident_if_ok() {
-  if constexpr (ffn_shape_ok<MT, FW, WN, SECOND>()) return ffn_resident_blocks<MT, FW, WN, SECOND>();
+  if constexpr (ffn_shape_ok<MT, FW, WN, SECOND, GLU>())
+    return ffn_resident_blocks<MT, FW, WN, SECOND, GLU>();
   else return 0;
 }
 
-template <int MT, int FW, int WN, bool SECOND>
+// Column tiles of a launch: each covers FW*WN*32 weight rows, which are as many
+// output columns (GEGLU: half as many).
+static long ffn_col_tiles(const FfnArgs& a, long rows_per_tile, bool glu) {
+  const long ocols = glu ? rows_per_tile / 2 : rows_per_tile;
+  return (a.Nout + ocols - 1) / ocols;
+}
+
+template <int MT, int FW, int WN, bool SECOND, bool GLU>
 static long ffn_grid(const FfnArgs& a) {
-  const long cols = FW * WN * 32;
-  const long n_tiles = (a.Nout + cols - 1) / cols * a.n_mchunks * a.n_experts;
-  const long resident = ffn_resident_blocks<MT, FW, WN, SECOND>();
+  const long n_tiles = ffn_col_tiles(a, FW * WN * 32, GLU) * a.n_mchunks * a.n_experts;
+  const long resident = ffn_resident_blocks<MT, FW, WN, SECOND, GLU>();
   return n_tiles < resident ? n_tiles : resident;
 }
 
-template <int MT, int FW, int WN, bool SECOND>
+template <int MT, int FW, int WN, bool SECOND, bool GLU>
 static void launch_ffn_bf16_t(const FfnArgs& a, hipStream_t st) {
-  if constexpr (ffn_shape_ok<MT, FW, WN, SECOND>()) {
-    const dim3 grid((unsigned)ffn_grid<MT, FW, WN, SECOND>(a)), block(FW * 64);
+  if constexpr (ffn_shape_ok<MT, FW, WN, SECOND, GLU>()) {
+    const dim3 grid((unsigned)ffn_grid<MT, FW, WN, SECOND, GLU>(a)), block(FW * 64);
     // Weights are streamed past the caches when nothing re-reads their lines
     // (with rows off the line grid: only the rows on it).
     if (a.n_mchunks == 1 && (a.K * 2) % 128 == 64 && ((size_t)a.W & 127) == 0 && a.Nout % 2 == 0)
-      hipLaunchKernelGGL((ffn_bf16_kernel<MT, FW, WN, SECOND, kCpolSplitRows>), grid, block, 0, st,
-                         a.act, a.act_bytes, a.W, a.bias, a.offset, a.row2tok, a.rowgate, a.xres,
-                         a.out, a.out_bytes, a.K, a.Nout, a.n_mchunks, a.n_experts, a.max_rows,
-                         a.T, a.d_model, a.no_residual);
+      hipLaunchKernelGGL((ffn_bf16_kernel<MT, FW, WN, SECOND, kCpolSplitRows, GLU>), grid, block,
+                         0, st, a.act, a.act_bytes, a.W, a.bias, a.offset, a.row2tok, a.rowgate,
+                         a.xres, a.out, a.out_bytes, a.K, a.Nout, a.n_mchunks, a.n_experts,
+                         a.max_rows, a.T, a.d_model, a.no_residual);
     else if (a.n_mchunks == 1 && (a.K * 2) % 128 == 0)
-      hipLaunchKernelGGL((ffn_bf16_kernel<MT, FW, WN, SECOND, kCpolNonTemporal>), grid, block, 0, st,
-                         a.act, a.act_bytes, a.W, a.bias, a.offset, a.row2tok, a.rowgate, a.xres,
-                         a.out, a.out_bytes, a.K, a.Nout, a.n_mchunks, a.n_experts, a.max_rows,
-                         a.T, a.d_model, a.no_residual);
+      hipLaunchKernelGGL((ffn_bf16_kernel<MT, FW, WN, SECOND, kCpolNonTemporal, GLU>), grid, block,
+                         0, st, a.act, a.act_bytes, a.W, a.bias, a.offset, a.row2tok, a.rowgate,
+                         a.xres, a.out, a.out_bytes, a.K, a.Nout, a.n_mchunks, a.n_experts,
+                         a.max_rows, a.T, a.d_model, a.no_residual);
     else
-      hipLaunchKernelGGL((ffn_bf16_kernel<MT, FW, WN, SECOND, 0>), grid, block, 0, st, a.act,
+      hipLaunchKernelGGL((ffn_bf16_kernel<MT, FW, WN, SECOND, 0, GLU>), grid, block, 0, st, a.act,
                          a.act_bytes, a.W, a.bias, a.offset, a.row2tok, a.rowgate, a.xres, a.out,
                          a.out_bytes, a.K, a.Nout, a.n_mchunks, a.n_experts, a.max_rows, a.T,
                          a.d_model, a.no_residual);
@@ -646,23 +702,23 @@ static void launch_ffn_bf16_t(const FfnArgs& a, hipStream_t st) {
 // streamed through a CU: each tile streams its COLS weight rows and re-reads
 // its activation rows (mostly L2 hits, weighted 0.6); tiles run in rounds of
 // the resident grid.  Returns a huge cost for shapes that cannot run.
-template <int MT, bool SECOND>
+template <int MT, bool SECOND, bool GLU>
 static double ffn_shape_cost(const FfnArgs& a, FfnShape sh, int cus) {
   long resident = 0;
-  if (sh.fw == 4 && sh.wn == 2) resident = ffn_resident_if_ok<MT, 4, 2, SECOND>();
-  if (sh.fw == 3 && sh.wn == 2) resident = ffn_resident_if_ok<MT, 3, 2, SECOND>();
-  if (sh.fw == 8 && sh.wn == 1) resident = ffn_resident_if_ok<MT, 8, 1, SECOND>();
-  if (sh.fw == 6 && sh.wn == 1) resident = ffn_resident_if_ok<MT, 6, 1, SECOND>();
-  if (sh.fw == 4 && sh.wn == 1) resident = ffn_resident_if_ok<MT, 4, 1, SECOND>();
+  if (sh.fw == 4 && sh.wn == 2) resident = ffn_resident_if_ok<MT, 4, 2, SECOND, GLU>();
+  if (sh.fw == 3 && sh.wn == 2) resident = ffn_resident_if_ok<MT, 3, 2, SECOND, GLU>();
+  if (sh.fw == 8 && sh.wn == 1) resident = ffn_resident_if_ok<MT, 8, 1, SECOND, GLU>();
+  if (sh.fw == 6 && sh.wn == 1) resident = ffn_resident_if_ok<MT, 6, 1, SECOND, GLU>();
+  if (sh.fw == 4 && sh.wn == 1) resident = ffn_resident_if_ok<MT, 4, 1, SECOND, GLU>();
   if (resident <= 0) return 1e300;
   const long cols = sh.fw * sh.wn * 32;
-  const long n_tiles = (a.Nout + cols - 1) / cols * a.n_mchunks * a.n_experts;
+  const long n_tiles = ffn_col_tiles(a, cols, GLU) * a.n_mchunks * a.n_experts;
   const long rounds = (n_tiles + resident - 1) / resident;
   const double tile = (double)cols + 0.6 * MT * 32;
   return (double)rounds * (double)resident / (double)cus * tile;
 }
 
-template <int MT, bool SECOND>
+template <int MT, bool SECOND, bool GLU>
 static void launch_ffn_bf16_mt(const FfnArgs& a, hipStream_t st) {
   static const int cus = [] {
     int dev = 0, n = 0;
@@ -677,17 +733,17 @@ static void launch_ffn_bf16_mt(const FfnArgs& a, hipStream_t st) {
 #ifdef SFFN_FFN_ONLY_WN  // tuning builds: restrict the choice to one wave width
     if (sh.wn != SFFN_FFN_ONLY_WN) continue;
 #endif
-    const double c = ffn_shape_cost<MT, SECOND>(a, sh, cus);
+    const double c = ffn_shape_cost<MT, SECOND, GLU>(a, sh, cus);
     if (c < best_cost) {
       best_cost = c;
       best = sh;
     }
   }
-  if (best.fw == 4 && best.wn == 2) launch_ffn_bf16_t<MT, 4, 2, SECOND>(a, st);
-  else if (best.fw == 3 && best.wn == 2) launch_ffn_bf16_t<MT, 3, 2, SECOND>(a, st);
-  else if (best.fw == 8) launch_ffn_bf16_t<MT, 8, 1, SECOND>(a, st);
-  else if (best.fw == 6) launch_ffn_bf16_t<MT, 6, 1, SECOND>(a, st);
-  else launch_ffn_bf16_t<MT, 4, 1, SECOND>(a, st);
+  if (best.fw == 4 && best.wn == 2) launch_ffn_bf16_t<MT, 4, 2, SECOND, GLU>(a, st);
+  else if (best.fw == 3 && best.wn == 2) launch_ffn_bf16_t<MT, 3, 2, SECOND, GLU>(a, st);
+  else if (best.fw == 8) launch_ffn_bf16_t<MT, 8, 1, SECOND, GLU>(a, st);
+  else if (best.fw == 6) launch_ffn_bf16_t<MT, 6, 1, SECOND, GLU>(a, st);
+  else launch_ffn_bf16_t<MT, 4, 1, SECOND, GLU>(a, st);
 }
 
 // Row tiles per block: the capacity's 32-row tiles split into as few chunks of at
@@ -710,7 +766,7 @@ ffn_f32_kernel(const float* __restrict__ act, const float* __restrict__ W,
                const float* __restrict__ bias, const int* __restrict__ offset,
                const int* __restrict__ row2tok, const float* __restrict__ gate,
                const float* __restrict__ xres, float* __restrict__ out, int K, int Nout,
-               int d_model, int no_residual) {
+               int d_model, int no_residual, int glu) {
   const int e = blockIdx.z;
   const int r = blockIdx.y * 16 + (threadIdx.x >> 4);
   const int n = blockIdx.x * 16 + (threadIdx.x & 15);
@@ -719,11 +775,18 @@ ffn_f32_kernel(const float* __restrict__ act, const float* __restrict__ W,
   const int row = rbeg + r;
   const int tok = row2tok[row];
   const float* a = SECOND ? act + (size_t)row * K : act + (size_t)tok * K;
-  const float* w = W + ((size_t)e * Nout + n) * K;
+  const int wm = (!SECOND && glu) ? 2 : 1;  // GEGLU: gate row n, linear row Nout + n
+  const float* w = W + ((size_t)e * wm * Nout + n) * K;
   float s = 0.f;
   for (int k = 0; k < K; ++k) s = fmaf(a[k], w[k], s);
-  if (bias) s += bias[(size_t)e * Nout + n];
-  if (!SECOND) {
+  if (bias) s += bias[(size_t)e * wm * Nout + n];
+  if (!SECOND && glu) {
+    const float* v = w + (size_t)Nout * K;
+    float l = 0.f;
+    for (int k = 0; k < K; ++k) l = fmaf(a[k], v[k], l);
+    if (bias) l += bias[(size_t)e * wm * Nout + Nout + n];
+    out[(size_t)row * Nout + n] = gelu_f32(s) * l;
+  } else if (!SECOND) {
     out[(size_t)row * Nout + n] = fmaxf(s, 0.f);
   } else if (no_residual & 2) {
     out[(size_t)row * d_model + n] = gate[row] * s;
@@ -735,7 +798,7 @@ ffn_f32_kernel(const float* __restrict__ act, const float* __restrict__ W,
   }
 }
 
-template <bool SECOND>
+template <bool SECOND, bool GLU = false>
 static void launch_ffn_bf16(FfnArgs a, const Shape& s, hipStream_t st) {
   const int mt = rows_tiles(s.C);
   a.n_mchunks = (s.C + mt * 32 - 1) / (mt * 32);
@@ -744,14 +807,14 @@ static void launch_ffn_bf16(FfnArgs a, const Shape& s, hipStream_t st) {
   a.T = s.T;
   a.d_model = s.d;
   switch (mt) {
-    case 1: launch_ffn_bf16_mt<1, SECOND>(a, st); break;
-    case 2: launch_ffn_bf16_mt<2, SECOND>(a, st); break;
-    case 3: launch_ffn_bf16_mt<3, SECOND>(a, st); break;
-    case 4: launch_ffn_bf16_mt<4, SECOND>(a, st); break;
-    case 5: launch_ffn_bf16_mt<5, SECOND>(a, st); break;
-    case 6: launch_ffn_bf16_mt<6, SECOND>(a, st); break;
-    case 7: launch_ffn_bf16_mt<7, SECOND>(a, st); break;
-    default: launch_ffn_bf16_mt<8, SECOND>(a, st); break;
+    case 1: launch_ffn_bf16_mt<1, SECOND, GLU>(a, st); break;
+    case 2: launch_ffn_bf16_mt<2, SECOND, GLU>(a, st); break;
+    case 3: launch_ffn_bf16_mt<3, SECOND, GLU>(a, st); break;
+    case 4: launch_ffn_bf16_mt<4, SECOND, GLU>(a, st); break;
+    case 5: launch_ffn_bf16_mt<5, SECOND, GLU>(a, st); break;
+    case 6: launch_ffn_bf16_mt<6, SECOND, GLU>(a, st); break;
+    case 7: launch_ffn_bf16_mt<7, SECOND, GLU>(a, st); break;
+    default: launch_ffn_bf16_mt<8, SECOND, GLU>(a, st); break;
   }
 }
 
@@ -762,7 +825,7 @@ hipError_t launch_ffn1(const Shape& s, const Inputs& in, const Workspace& ws, hi
     hipLaunchKernelGGL(ffn_f32_kernel<false>, grid, dim3(256), 0, st, (const float*)in.x,
                        (const float*)in.W1, (const float*)in.b1, ws.offset, ws.row2tok,
                        (const float*)nullptr, (const float*)nullptr, (float*)ws.H, s.d, s.F, s.d,
-                       0);
+                       0, s.glu);
     return hipGetLastError();
   }
   FfnArgs a{};
@@ -776,7 +839,8 @@ hipError_t launch_ffn1(const Shape& s, const Inputs& in, const Workspace& ws, hi
   a.out_bytes = (uint32_t)((size_t)s.max_rows * s.F * 2);
   a.K = s.d;
   a.Nout = s.F;
-  launch_ffn_bf16<false>(a, s, st);
+  if (s.glu) launch_ffn_bf16<false, true>(a, s, st);
+  else launch_ffn_bf16<false>(a, s, st);
   return hipGetLastError();
 }
 
@@ -788,12 +852,12 @@ hipError_t launch_ffn2(const Shape& s, const Inputs& in, const Workspace& ws, co
     if (s.k == 2)
       hipLaunchKernelGGL(ffn_f32_kernel<true>, grid, dim3(256), 0, st, (const float*)ws.H,
                          (const float*)in.W2, (const float*)in.b2, ws.offset, ws.row2tok,
-                         ws.rowgate, (const float*)nullptr, (float*)ws.Y2, s.F, s.d, s.d, 3);
+                         ws.rowgate, (const float*)nullptr, (float*)ws.Y2, s.F, s.d, s.d, 3, 0);
     else
       hipLaunchKernelGGL(ffn_f32_kernel<true>, grid, dim3(256), 0, st, (const float*)ws.H,
                          (const float*)in.W2, (const float*)in.b2, ws.offset, ws.row2tok,
                          out.gate, (const float*)in.x, (float*)out.y, s.F, s.d, s.d,
-                         no_residual ? 1 : 0);
+                         no_residual ? 1 : 0, 0);
     return hipGetLastError();
   }
   FfnArgs a{};

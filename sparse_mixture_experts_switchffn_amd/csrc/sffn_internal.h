@@ -16,6 +16,7 @@ struct Shape {
   int T, d, F, N, C;
   int k;                // experts per token (1: Switch routing, 2: top-2)
   int reroute;          // k = 1 with overflow tokens rerouted to their second choice
+  int glu;              // GEGLU experts: W1 [N, 2F, d], b1 [N, 2F]
   int dtype;            // SFFN_FP32 / SFFN_BF16
   int n_route_blocks;   // ceil(T / kRouteTokens)
   int max_rows;         // min(k*T, N*C): rows the expert buffers can hold

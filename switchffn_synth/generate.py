@@ -6,6 +6,7 @@ matrix, which is uploaded), the device one for the large expert tensors and x.
 
 Tensor layouts (row-major):
   x  [T, d]     Wr [N, d]     W1 [N, F, d]   b1 [N, F]   W2 [N, d, F]   b2 [N, d]
+  (GEGLU experts: W1 [N, 2F, d] and b1 [N, 2F])
 bf16 tensors travel as uint16 bit patterns on the host.
 """
 from __future__ import annotations
@@ -26,8 +27,8 @@ def shape_of(w: Workload, name: str) -> tuple:
     return {
         "x": (w.T, w.d),
         "Wr": (w.N, w.d),
-        "W1": (w.N, w.F, w.d),
-        "b1": (w.N, w.F),
+        "W1": (w.N, 2 * w.F if w.glu else w.F, w.d),
+        "b1": (w.N, 2 * w.F if w.glu else w.F),
         "W2": (w.N, w.d, w.F),
         "b2": (w.N, w.d),
     }[name]
@@ -116,16 +117,18 @@ def host_rows(w: Workload, name: str, rows: np.ndarray) -> np.ndarray:
 
 
 def expert_weights_host(w: Workload, e: int) -> dict:
-    """Expert e's W1 [F, d], b1 [F], W2 [d, F], b2 [d] (None when absent)."""
+    """Expert e's W1 [F1, d], b1 [F1], W2 [d, F], b2 [d] (None when absent); F1 = F, or
+    2F for GEGLU experts."""
+    F1 = 2 * w.F if w.glu else w.F
     Fd = w.F * w.d
     out = {
-        "W1": host_array(w, "W1", e * Fd, Fd).reshape(w.F, w.d),
+        "W1": host_array(w, "W1", e * F1 * w.d, F1 * w.d).reshape(F1, w.d),
         "W2": host_array(w, "W2", e * Fd, Fd).reshape(w.d, w.F),
         "b1": None,
         "b2": None,
     }
     if w.has_bias:
-        out["b1"] = host_array(w, "b1", e * w.F, w.F)
+        out["b1"] = host_array(w, "b1", e * F1, F1)
         out["b2"] = host_array(w, "b2", e * w.d, w.d)
     return out
 

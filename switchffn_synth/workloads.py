@@ -33,6 +33,7 @@ class Workload:
     bias_sigma: float = 0.0       # 0 -> biases are absent (zero)
     zipf_s: Optional[float] = None  # expert popularity ~ (i+1)^-s via a router bias
     zipf_beta: float = 0.5          # strength of that bias, in units of the logit std
+    glu: bool = False               # GEGLU experts: W1 [N, 2F, d] and b1 [N, 2F]
 
     @property
     def elem_bytes(self) -> int:
@@ -47,7 +48,7 @@ class Workload:
 
     def describe(self) -> str:
         return (f"{self.name}: T={self.T} d={self.d} F={self.F} N={self.N} CF={self.CF} "
-                f"dtype={self.dtype} seed={self.seed}")
+                f"dtype={self.dtype} seed={self.seed}" + (" geglu" if self.glu else ""))
 
 
 WORKLOADS = {

@@ -22,6 +22,9 @@ def run_gpu(w, dev_in, flags: int = 0, k: int = 1):
 
     import sparse_mixture_experts_switchffn_amd as sffn
 
+    if w.glu:
+        flags |= sffn.SFFN_GEGLU
+
     dev = dev_in["x"].device
     stats = {"expert_count": torch.full((w.N,), -7, dtype=torch.int32, device=dev),
              "accepted_count": torch.full((w.N,), -7, dtype=torch.int32, device=dev),
@@ -59,6 +62,7 @@ def oracle_ref(w, x_raw, Wr_raw, expert_idx, only_experts=None, no_residual=Fals
                experts=None, k=1, reroute=False):
     """The oracle on the same inputs, replaying the GPU's routing for dispatch and y
     (reroute: expert_idx is the GPU's [T, 2] first and second choices)."""
+    act = "geglu" if w.glu else "relu"
     x64 = synth.decode(x_raw)
     Wr64 = synth.decode(Wr_raw)
     if experts is None:
@@ -68,9 +72,10 @@ def oracle_ref(w, x_raw, Wr_raw, expert_idx, only_experts=None, no_residual=Fals
                     synth.decode(ew["b2"]))
     if reroute:
         return oracle.forward_reroute(x64, Wr64, experts, w.CF, w.dtype, no_residual=no_residual,
-                                      expert_idx=expert_idx, only_experts=only_experts)
+                                      expert_idx=expert_idx, only_experts=only_experts,
+                                      activation=act)
     return oracle.forward(x64, Wr64, experts, w.CF, w.dtype, no_residual=no_residual,
-                          expert_idx=expert_idx, only_experts=only_experts, k=k)
+                          expert_idx=expert_idx, only_experts=only_experts, k=k, activation=act)
 
 
 def rel_l2(a, b):

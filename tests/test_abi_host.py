@@ -118,7 +118,7 @@ def test_forward_topk_rejects_before_launch(k, over, code):
 @pytest.mark.parametrize("k,over,code", [
     (1, dict(N=1), S.SFFN_EINVAL),                 # rerouting needs a second choice
     (2, {}, S.SFFN_EINVAL),                        # rerouting is a top-1 form
-    (1, dict(flags=S.SFFN_REROUTE_OVERFLOW | 4), S.SFFN_EINVAL),
+    (1, dict(flags=S.SFFN_REROUTE_OVERFLOW | 8), S.SFFN_EINVAL),  # unknown flag bit
     (1, dict(ws_bytes=1000), S.SFFN_EWORKSPACE),
 ])
 def test_reroute_rejects_before_launch(k, over, code):

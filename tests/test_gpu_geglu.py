@@ -1,0 +1,94 @@
+"""GPU parity of GEGLU experts (flag SFFN_GEGLU: W1 [N, 2F, d] holding the gate and the
+linear up-projections) against the CPU oracle on the same seeded inputs, with top-1,
+top-2 and rerouted dispatch: routing bit-exact outside near-ties, y within the dtype's
+tolerance, dropped rows bit-exact."""
+import numpy as np
+import pytest
+
+import oracle
+import switchffn_synth as synth
+from gpu_harness import (announce, check_routing, check_y, host_x, oracle_ref, rows_of, run_gpu,
+                         sample_experts)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _case(w, k=1, sampled=False):
+    announce(f"geglu k={k} " + w.describe())
+    assert w.glu
+    dev_in = synth.device_inputs(w, DEV)
+    assert dev_in["W1"].shape == (w.N, 2 * w.F, w.d)
+    x_raw = host_x(w)
+    Wr_raw = synth.host_array(w, "Wr").reshape(w.N, w.d)
+    gpu = run_gpu(w, dev_in, k=k)
+    experts, rows = None, None
+    if sampled:
+        C = oracle.capacity(w.T, w.N, w.CF)
+        experts = sample_experts(oracle.dispatch(gpu["expert_idx"], w.N, C), 8)
+    ref = oracle_ref(w, x_raw, Wr_raw, gpu["expert_idx"], only_experts=experts, k=k)
+    ties = check_routing(gpu, ref)
+    if sampled:
+        rows = rows_of(ref, experts)
+    err = check_y(w, gpu, ref, x_raw, rows=rows)
+    from sparse_mixture_experts_switchffn_amd import SFFN_NO_RESIDUAL
+    gnr = run_gpu(w, dev_in, flags=SFFN_NO_RESIDUAL, k=k)
+    rnr = oracle_ref(w, x_raw, Wr_raw, gnr["expert_idx"], only_experts=experts, no_residual=True,
+                     k=k)
+    err_nr = check_y(w, gnr, rnr, x_raw, rows=rows, no_residual=True)
+    print(f"  ties={ties} dropped={int(np.sum(ref['slot'] < 0))} y_err={err:.2e} "
+          f"y_err_nr={err_nr:.2e}", flush=True)
+    return err
+
+
+@pytest.mark.parametrize("case", [
+    dict(T=300, d=72, F=136, N=6, CF=1.0, bias_sigma=0.02),     # ragged T, K and columns
+    dict(T=257, d=64, F=64, N=2, CF=1.25, bias_sigma=0.05),     # one partial column tile
+    dict(T=640, d=256, F=200, N=16, CF=0.5),                    # F off every tile width
+    dict(T=4096, d=64, F=96, N=4, CF=1.25, bias_sigma=0.02),    # several row chunks per expert
+    dict(T=1100, d=200, F=64, N=260, CF=2.0),                   # many experts, tiled logits
+])
+def test_geglu_bf16_shapes(case):
+    _case(synth.workload("switch_base").replace(glu=True, **case))
+
+
+@pytest.mark.parametrize("case", [
+    dict(T=100, d=5, F=7, N=3, CF=1.0, bias_sigma=0.1),
+    dict(T=333, d=33, F=65, N=9, CF=1.25, bias_sigma=0.02),
+])
+def test_geglu_fp32_shapes(case):
+    err = _case(synth.workload("tiny").replace(glu=True, **case))
+    assert err <= 1e-6
+
+
+def test_geglu_top2():
+    _case(synth.workload("switch_base").replace(glu=True, T=700, d=96, F=160, N=8, CF=1.0,
+                                                bias_sigma=0.02), k=2)
+
+
+def test_geglu_reroute():
+    """Rerouting and GEGLU together: routing as in the rerouting tests, y of every row."""
+    from sparse_mixture_experts_switchffn_amd import SFFN_REROUTE_OVERFLOW
+    w = synth.workload("switch_base").replace(glu=True, T=600, d=64, F=128, N=6, CF=1.0,
+                                              zipf_s=1.1)
+    announce("geglu reroute " + w.describe())
+    dev_in = synth.device_inputs(w, DEV)
+    x_raw = host_x(w)
+    Wr_raw = synth.host_array(w, "Wr").reshape(w.N, w.d)
+    gpu = run_gpu(w, dev_in, flags=SFFN_REROUTE_OVERFLOW)
+    choices = run_gpu(w, dev_in, k=2)["expert_idx"]
+    ref = oracle_ref(w, x_raw, Wr_raw, choices, reroute=True)
+    assert np.array_equal(gpu["expert_idx"], ref["expert_idx"])
+    assert np.array_equal(gpu["slot"], ref["slot"])
+    assert int(np.sum((ref["slot"] >= 0) & (ref["expert_idx"] != choices[:, 0]))) > 0
+    err = check_y(w, gpu, ref, x_raw)
+    print(f"  y_err={err:.2e}", flush=True)
+
+
+def test_geglu_switch_base():
+    """The Switch-Base-like workload with GEGLU experts at full size, in the benchmark's
+    launch configuration: every token's routing; y of sampled experts."""
+    import torch
+    _case(synth.workload("switch_base").replace(glu=True), sampled=True)
+    torch.cuda.empty_cache()
