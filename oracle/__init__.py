@@ -5,6 +5,7 @@ this package.  The HIP product path never does.
 """
 from .switchffn_oracle import (  # noqa: F401
     aux_loss,
+    backward,
     bf16_bits,
     capacity,
     dispatch,

@@ -51,6 +51,11 @@ gives no formula): the gated-GELU unit GELU(W x + b_W) * (V x + b_V) with the
 exact GELU a * Phi(a) (Phi the standard normal CDF); W1 then holds the two
 up-projections, W in rows 0..F-1 and V in rows F..2F-1, and b1 both biases.
 
+Backward pass (top-1, ReLU experts): the chain rule through the gate and
+through P_i of the aux loss, f_i and the routing carrying no gradient (see
+backward() for the readings); pinned against central finite differences of
+forward() and the closed forms below.
+
 Pins (tests/test_oracle_pins.py): the worked aux-loss example of the
 Math-LLMs card (1.15), the uniform-routing closed forms (aux = 1), the
 one-expert limit (aux -> N, closed form), N = 1 dense-FFN reduction, the x = 0
@@ -445,6 +450,118 @@ def _forward_top2(x, Wr, experts, CF, dtype, *, no_residual, expert_idx, only_ex
         "router_expert_idx": own, "gate": gate, "aux_loss": aux,
         "y64": y, "y": round_to_dtype(y, dtype), **dp,
     }
+
+
+# ----------------------------------------------------------------------------
+# Backward pass of the top-1 ReLU layer.  The routing (argmax, capacity) is a
+# piecewise-constant choice and carries no gradient; the router learns through
+# the gate p_{t,e_t} that scales the expert output ([Switch summary] 3.4
+# "Switch Routing: The k=1 Simplification"; [Explainer] "Why one expert is
+# enough") and through P_i of the aux loss, f_i being a count with no gradient
+# ([Explainer] symbol list under "Why one expert is enough"; [Switch summary]
+# 3.4 "The Load-Balancing Auxiliary Loss").  Chain rule, for accepted t with
+# expert e, a_t = W1_e x_t + b1_e, h_t = ReLU(a_t), o_t = W2_e h_t + b2_e:
+#   dO_t = g_t dy_t,  dg_t = dy_t . o_t
+#   dW2_e = sum_t dO_t h_t^T,  db2_e = sum_t dO_t
+#   da_t = (W2_e^T dO_t) * [a_t > 0]          (ReLU'(0) taken as 0)
+#   dW1_e = sum_t da_t x_t^T,  db1_e = sum_t da_t
+#   u_{t,i} = d_aux N f_i / T + [t accepted][i = e_t] dg_t
+#   dz_t = p_t * (u_t - p_t . u_t)            (softmax Jacobian)
+#   dWr = sum_t dz_t x_t^T
+#   dx_t = dy_t + [t accepted] W1_e^T da_t + Wr^T dz_t
+# where d_aux is the gradient of the loss with respect to the aux value.
+# ----------------------------------------------------------------------------
+def expert_backward(xe, W1e, b1e, W2e, b2e, dye, ge) -> dict:
+    """One expert's rows: forward recomputed in float64, then the chain rule."""
+    W1e = np.asarray(W1e, np.float64)
+    W2e = np.asarray(W2e, np.float64)
+    a = xe @ W1e.T + (0.0 if b1e is None else np.asarray(b1e, np.float64))
+    h = np.maximum(a, 0.0)
+    o = h @ W2e.T + (0.0 if b2e is None else np.asarray(b2e, np.float64))
+    dO = ge[:, None] * dye
+    da = (dO @ W2e) * (a > 0.0)
+    return {"dW1": da.T @ xe, "db1": da.sum(axis=0), "dW2": dO.T @ h, "db2": dO.sum(axis=0),
+            "dx": da @ W1e, "dg": np.sum(dye * o, axis=1)}
+
+
+def aux_prob_grad(hist: np.ndarray, T: int, d_aux: float) -> np.ndarray:
+    """dL/dp_{t,i} from the aux term: d_aux * N * f_i / T (the same for every t)."""
+    N = len(hist)
+    return d_aux * N * (np.asarray(hist, np.float64) / T) / T
+
+
+def softmax_backward(p: np.ndarray, u: np.ndarray) -> np.ndarray:
+    """dz from dL/dp through p = softmax(z): p * (u - p . u), row by row."""
+    return p * (u - np.sum(p * u, axis=1, keepdims=True))
+
+
+def backward(x, Wr, experts, CF: float, dy, d_aux: float = 0.0, *,
+             expert_idx: Optional[np.ndarray] = None,
+             only_experts: Optional[Iterable[int]] = None) -> dict:
+    """Gradients of L(y, aux) given dy = dL/dy [T, d] and d_aux = dL/daux.
+
+    experts, expert_idx and only_experts as for forward (expert_idx replays a given
+    routing).  only_experts: the weight and bias gradients of the other experts are
+    NaN, and so are the dx rows of their accepted tokens; the router gradient needs
+    every accepted token's dg, so it is computed only when only_experts is None.
+    Returns dx [T, d], dWr [N, d], dW1 [N, F, d], db1 [N, F], dW2 [N, d, F],
+    db2 [N, d] (float64), and dg [T] and dz [T, N].
+    """
+    x = np.asarray(x, np.float64)
+    dy = np.asarray(dy, np.float64)
+    Wr = np.asarray(Wr, np.float64)
+    T, d = x.shape
+    N = Wr.shape[0]
+    C = capacity(T, N, CF)
+    r = router(x, Wr)
+    p = r["probs"]
+    eidx = r["expert_idx"] if expert_idx is None else np.asarray(expert_idx, np.int64)
+    gate = p[np.arange(T), eidx]
+    dp = dispatch(eidx, N, C)
+
+    if callable(experts):
+        get = experts
+    else:
+        W1, b1, W2, b2 = experts
+        def get(e):
+            return (W1[e], None if b1 is None else b1[e], W2[e], None if b2 is None else b2[e])
+
+    F = None
+    dx = dy.copy()
+    dg = np.zeros(T)
+    grads = {}
+    todo = range(N) if only_experts is None else sorted(set(int(e) for e in only_experts))
+    for e in todo:
+        W1e, b1e, W2e, b2e = get(e)
+        F = np.asarray(W1e).shape[0]
+        rows = dp["row2tok"][dp["offset"][e]:dp["offset"][e + 1]]
+        g = expert_backward(x[rows], W1e, b1e, W2e, b2e, dy[rows], gate[rows])
+        dg[rows] = g["dg"]
+        grads[e] = (g["dW1"], g["db1"], g["dW2"], g["db2"])
+        dx[rows] += g["dx"]
+    if F is None:
+        F = np.asarray(get(0)[0]).shape[0]
+    dW1 = np.full((N, F, d), np.nan)
+    db1 = np.full((N, F), np.nan)
+    dW2 = np.full((N, d, F), np.nan)
+    db2 = np.full((N, d), np.nan)
+    for e, (g1, gb1, g2, gb2) in grads.items():
+        dW1[e], db1[e], dW2[e], db2[e] = g1, gb1, g2, gb2
+
+    out = {"C": C, "expert_idx": eidx, "slot": dp["slot"], "gate": gate, "dg": dg,
+           "dW1": dW1, "db1": db1, "dW2": dW2, "db2": db2}
+    if only_experts is not None:
+        for e in range(N):
+            if e not in grads:
+                dx[dp["row2tok"][dp["offset"][e]:dp["offset"][e + 1]]] = np.nan
+        out["dx"] = dx
+        return out
+    u = np.broadcast_to(aux_prob_grad(dp["hist"], T, d_aux), (T, N)).copy()
+    acc = dp["slot"] >= 0
+    u[np.nonzero(acc)[0], eidx[acc]] += dg[acc]
+    dz = softmax_backward(p, u)
+    out.update(dz=dz, dWr=dz.T @ x, dx=dx + dz @ Wr)
+    return out
 
 
 def near_tie_tokens(logits: np.ndarray, tol: float = 1e-5) -> np.ndarray:

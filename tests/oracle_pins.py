@@ -469,4 +469,86 @@ def pin_geglu_linear_branch_identity():
     assert np.all(o[~np.eye(3, dtype=bool)] == 0.0)
 
 
+# ---------------------------------------------------------------------------
+# Backward pass.
+# ---------------------------------------------------------------------------
+def _fd_check(x, Wr, experts, CF, dy, d_aux, entries=5, eps=1e-6, tol=2e-8, seed=0):
+    """Central differences of L = sum(y * dy) + d_aux * aux, through forward(), at
+    sampled entries of every input; the routing must not move within +-eps."""
+    g = O.backward(x, Wr, experts, CF, dy, d_aux)
+    W1, b1, W2, b2 = experts
+    base = O.forward(x, Wr, experts, CF)
+    arrays = {"dx": x, "dWr": Wr, "dW1": W1, "db1": b1, "dW2": W2, "db2": b2}
+    rng = np.random.default_rng(seed)
+
+    def loss():
+        r = O.forward(x, Wr, experts, CF)
+        assert np.array_equal(r["slot"], base["slot"]) and \
+            np.array_equal(r["expert_idx"], base["expert_idx"]), "routing moved"
+        return float(np.sum(r["y64"] * dy) + d_aux * r["aux_loss"])
+
+    for key, arr in arrays.items():
+        if arr is None:
+            continue
+        for _ in range(entries):
+            idx = tuple(int(rng.integers(0, n)) for n in arr.shape)
+            old = arr[idx]
+            arr[idx] = old + eps
+            lp = loss()
+            arr[idx] = old - eps
+            lm = loss()
+            arr[idx] = old
+            fd = (lp - lm) / (2 * eps)
+            assert abs(fd - g[key][idx]) <= tol * max(1.0, abs(fd)), (key, idx, fd, g[key][idx])
+    return g
+
+
+def pin_backward_finite_differences():
+    cases = [dict(seed=71, T=24, d=5, F=6, N=3, CF=0.8, bias=True, d_aux=0.7),   # drops
+             dict(seed=72, T=16, d=4, F=3, N=4, CF=2.0, bias=False, d_aux=0.0),
+             dict(seed=73, T=30, d=6, F=5, N=2, CF=1.0, bias=True, d_aux=-1.3),
+             dict(seed=74, T=12, d=3, F=4, N=1, CF=1.0, bias=True, d_aux=2.0)]   # dense
+    for c in cases:
+        x, Wr, W1, b1, W2, b2 = random_case(c["seed"], c["T"], c["d"], c["F"], c["N"], c["bias"])
+        x, Wr, W1, W2 = (np.array(a, np.float64) for a in (x, Wr, W1, W2))
+        b1 = None if b1 is None else np.array(b1, np.float64)
+        b2 = None if b2 is None else np.array(b2, np.float64)
+        dy = np.random.default_rng(c["seed"] + 1).standard_normal((c["T"], c["d"]))
+        g = _fd_check(x, Wr, (W1, b1, W2, b2), c["CF"], dy, c["d_aux"], seed=c["seed"])
+        if c["N"] == 1:
+            assert np.all(g["dz"] == 0.0) and np.all(g["dWr"] == 0.0)
+
+
+def pin_backward_aux_only_router_zero():
+    # Wr = 0, dy = 0, d_aux = 1: every token picks expert 0 (ties), f = (1, 0, ..), p = 1/N,
+    # so dz_{t,0} = (N-1)/(N T), dz_{t,j} = -1/(N T) for j > 0; dWr_j = dz_j * sum_t x_t;
+    # dx = Wr^T dz = 0 and every expert gradient is 0.
+    N, T, d = 4, 10, 3
+    x, _, W1, b1, W2, b2 = random_case(75, T, d, 5, N, bias=True)
+    g = O.backward(x, np.zeros((N, d)), (W1, b1, W2, b2), 4.0, np.zeros((T, d)), 1.0)
+    sx = np.asarray(x, np.float64).sum(axis=0)
+    want = np.vstack([(N - 1) / (N * T) * sx] + [-1.0 / (N * T) * sx] * (N - 1))
+    _close(g["dWr"], want, 1e-15)
+    assert np.all(g["dx"] == 0.0)
+    for k in ("dW1", "db1", "dW2", "db2"):
+        assert np.all(g[k] == 0.0), k
+
+
+def pin_backward_dropped_token_passes_gradient():
+    # CF = 0: every token is dropped, y = x, so dx = dy + Wr^T dz with dz from the aux
+    # term alone, and the expert gradients vanish.
+    x, Wr, W1, b1, W2, b2 = random_case(76, 14, 4, 5, 3, bias=True)
+    dy = np.random.default_rng(9).standard_normal((14, 4))
+    g = O.backward(x, Wr, (W1, b1, W2, b2), 0.0, dy, 0.0)
+    _close(g["dx"], dy, 0.0)
+    assert np.all(g["dWr"] == 0.0)
+    g = O.backward(x, Wr, (W1, b1, W2, b2), 0.0, dy, 1.0)
+    r = O.forward(x, Wr, (W1, b1, W2, b2), 0.0)
+    f = np.bincount(r["expert_idx"], minlength=3) / 14
+    p = r["probs"]
+    c = 3 * f / 14
+    dz = p * (c - (p @ c)[:, None])
+    _close(g["dx"], dy + dz @ np.asarray(Wr, np.float64), 1e-14)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

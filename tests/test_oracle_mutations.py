@@ -15,7 +15,8 @@ from oracle_pins import ALL_PINS
 _orig = {name: getattr(O, name) for name in
          ("capacity", "router_logits", "softmax", "top1", "dispatch", "aux_loss", "expert_ffn",
           "round_to_bf16", "forward", "second_choice", "topk_gates", "dispatch_topk",
-          "reroute_overflow", "gelu")}
+          "reroute_overflow", "gelu", "expert_backward", "aux_prob_grad", "softmax_backward",
+          "backward")}
 
 
 def _ffn_no_b2(xe, W1e, b1e, W2e, b2e, activation="relu"):
@@ -248,6 +249,48 @@ def _geglu_relu_gate(xe, W1e, b1e, W2e, b2e, activation="relu"):
     return h @ np.asarray(W2e).T + (0 if b2e is None else b2e)
 
 
+def _eb_no_relu_mask(xe, W1e, b1e, W2e, b2e, dye, ge):
+    g = _orig["expert_backward"](xe, W1e, b1e, W2e, b2e, dye, ge)
+    da = (ge[:, None] * dye) @ np.asarray(W2e, np.float64)   # mask forgotten
+    g.update(dW1=da.T @ xe, db1=da.sum(axis=0), dx=da @ np.asarray(W1e, np.float64))
+    return g
+
+
+def _eb_no_gate(xe, W1e, b1e, W2e, b2e, dye, ge):
+    return _orig["expert_backward"](xe, W1e, b1e, W2e, b2e, dye, np.ones_like(ge))
+
+
+def _eb_dg_without_b2(xe, W1e, b1e, W2e, b2e, dye, ge):
+    g = _orig["expert_backward"](xe, W1e, b1e, W2e, b2e, dye, ge)
+    if b2e is not None:
+        g["dg"] = g["dg"] - dye @ np.asarray(b2e, np.float64)
+    return g
+
+
+def _eb_db2_ungated(xe, W1e, b1e, W2e, b2e, dye, ge):
+    g = _orig["expert_backward"](xe, W1e, b1e, W2e, b2e, dye, ge)
+    g["db2"] = dye.sum(axis=0)
+    return g
+
+
+def _aux_grad_without_n(hist, T, d_aux):
+    return _orig["aux_prob_grad"](hist, T, d_aux) / len(hist)
+
+
+def _softmax_bwd_uncentred(p, u):
+    return p * u
+
+
+def _softmax_bwd_sign(p, u):
+    return -_orig["softmax_backward"](p, u)
+
+
+def _bwd_no_residual(*a, **k):
+    g = _orig["backward"](*a, **k)
+    g["dx"] = g["dx"] - np.asarray(a[4], np.float64)
+    return g
+
+
 MUTANTS = {
     "ffn_drops_b2": ("expert_ffn", _ffn_no_b2),
     "ffn_drops_b1": ("expert_ffn", _ffn_no_b1),
@@ -282,6 +325,14 @@ MUTANTS = {
     "gelu_tanh_approximation": ("gelu", _gelu_tanh),
     "geglu_halves_swapped": ("expert_ffn", _geglu_halves_swapped),
     "geglu_relu_gate": ("expert_ffn", _geglu_relu_gate),
+    "bwd_no_relu_mask": ("expert_backward", _eb_no_relu_mask),
+    "bwd_no_gate": ("expert_backward", _eb_no_gate),
+    "bwd_dg_without_b2": ("expert_backward", _eb_dg_without_b2),
+    "bwd_db2_ungated": ("expert_backward", _eb_db2_ungated),
+    "bwd_aux_grad_without_n": ("aux_prob_grad", _aux_grad_without_n),
+    "bwd_softmax_uncentred": ("softmax_backward", _softmax_bwd_uncentred),
+    "bwd_softmax_sign": ("softmax_backward", _softmax_bwd_sign),
+    "bwd_dx_without_residual": ("backward", _bwd_no_residual),
 }
 
 
