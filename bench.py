@@ -58,6 +58,9 @@ def parse():
     p.add_argument("--reroute", action="store_true",
                    help="top-1 routing with No-Token-Left-Behind rerouting of overflowed tokens "
                         "to their second choice")
+    p.add_argument("--backward", action="store_true",
+                   help="a training step of the layer: forward then backward (dy ~ N(0, 1), "
+                        "d_aux = 0.01), top-1 ReLU experts")
     p.add_argument("--geglu", action="store_true",
                    help="GEGLU experts (two up-projections, W1 [N, 2F, d])")
     p.add_argument("--copy-calibration", action="store_true",
@@ -138,7 +141,9 @@ def measured_traffic(kernel: str, workload: str):
         if "=" in line and not line.lstrip().startswith("#"):
             k, v = line.split("=", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("source_sha256_16") != source_digest(KERNEL_SOURCES[kernel]):
+    srcs = KERNEL_SOURCES.get(kernel) or (("bwd.hip", "sffn_device.h") if kernel.startswith("bwd_")
+                                          else None)
+    if srcs is None or kv.get("source_sha256_16") != source_digest(srcs):
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])
@@ -218,6 +223,42 @@ def algorithmic_bytes(w, stage, accepted, active, esize, dropped=0, k=1, reroute
     return None
 
 
+def backward_bytes(w, stage, accepted, active, esize, parts):
+    """Bytes a backward stage must move at minimum (each operand read once, each
+    result written once; A accepted rows, `active` experts with rows):
+    router_logits: x, Wr (and the tiled router's planes) read, fp32 logits written;
+    expert_dgrad_hidden: W2 of active experts, dy and H rows read, dA rows and the
+        partial dg (one fp32 per row and 128-column tile) written;
+    router_grad: logits read, dz written, partial dg read (plus dy . b2);
+    expert_dgrad_input: W1 of active experts and dA rows read, fp32 dXe rows written;
+    dx: dz, Wr, dy and dXe read, dx written;
+    router_wgrad: dz and x read, per-part fp32 sums written, read back and summed;
+    expert_wgrad: dy, H, dA and x rows read, dW2 and dW1 of every expert written;
+    bias_grad: dy and dA rows read, db2 and db1 written.
+    """
+    A, T, N, d, F = accepted, w.T, w.N, w.d, w.F
+    n_dgp = (F + 127) // 128 if w.dtype == "bf16" else 1
+    tiled = w.dtype == "bf16" and N % 4 == 0
+    wb = active * d * F * esize
+    if stage == "router_logits":
+        return T * d * esize + N * d * 4 + (12 * N * d if tiled else 0) + T * N * 4
+    if stage == "expert_dgrad_hidden":
+        return wb + A * d * esize + 2 * A * F * esize + n_dgp * A * 4 + A * 8
+    if stage == "router_grad":
+        return 2 * T * N * 4 + n_dgp * A * 4 + (A * d * esize if w.has_bias else 0) + T * 8
+    if stage == "expert_dgrad_input":
+        return wb + A * F * esize + A * d * 4 + A * 4
+    if stage == "dx":
+        return T * N * 4 + N * d * 4 + 2 * T * d * esize + A * d * 4 + T * 4
+    if stage == "router_wgrad":
+        return T * N * 4 + T * d * esize + 2 * parts * N * d * 4 + N * d * 4
+    if stage == "expert_wgrad":
+        return 2 * N * d * F * esize + 2 * A * d * esize + 2 * A * F * esize + A * 8
+    if stage == "bias_grad":
+        return (A * d * esize + A * F * esize + N * (d + F) * esize) if w.has_bias else None
+    return None
+
+
 def cpu_baseline(w, budget_s, args):
     """The oracle as it stands on this host: full forward passes until the budget is used."""
     import numpy as np
@@ -237,7 +278,11 @@ def cpu_baseline(w, budget_s, args):
     passes, t0 = 0, time.perf_counter()
     while True:
         act = "geglu" if w.glu else "relu"
-        if getattr(args, "reroute", False):
+        if getattr(args, "backward", False):
+            dy = np.random.default_rng(1).standard_normal((w.T, w.d))
+            oracle.forward(dec["x"], dec["Wr"], experts, w.CF, w.dtype)
+            oracle.backward(dec["x"], dec["Wr"], experts, w.CF, dy, 0.01)
+        elif getattr(args, "reroute", False):
             oracle.forward_reroute(dec["x"], dec["Wr"], experts, w.CF, w.dtype, activation=act)
         else:
             oracle.forward(dec["x"], dec["Wr"], experts, w.CF, w.dtype,
@@ -285,22 +330,40 @@ def main():
         sys.stderr.write("bench.py: --reroute is a top-1 form; it needs --topk 1\n")
         return 2
     FLAGS = (sffn.SFFN_REROUTE_OVERFLOW if args.reroute else 0) | (sffn.SFFN_GEGLU if w.glu else 0)
+    BWD = bool(args.backward)
+    if BWD and (K != 1 or FLAGS):
+        sys.stderr.write("bench.py: --backward covers the top-1 ReLU layer only\n")
+        return 2
     out = sffn.switch_ffn_forward(inp["x"], inp["Wr"], inp["W1"], inp["b1"], inp["W2"], inp["b2"],
                                   w.CF, stats=stats, k=K, flags=FLAGS)
     bufs = {k: out[k] for k in ("y", "expert_idx", "slot", "gate", "aux_loss", "workspace")}
     nst = sffn.switch_ffn_num_stages()
     names = [sffn.switch_ffn_stage_name(i) for i in range(nst)]
+    nbs = sffn.switch_ffn_backward_num_stages() if BWD else 0
+    bnames = [sffn.switch_ffn_backward_stage_name(i) for i in range(nbs)]
     stream = torch.cuda.current_stream(dev)
+    grads = None
+    if BWD:
+        gen = torch.Generator(device=dev).manual_seed(1)
+        dy = torch.randn(T, w.d, generator=gen, device=dev).to(inp["x"].dtype)
+        grads = sffn.switch_ffn_backward(inp["x"], inp["Wr"], inp["W1"], inp["b1"], inp["W2"],
+                                         inp["b2"], w.CF, out, dy, 0.01)
+        gbufs = {k: grads[k] for k in ("dx", "dWr", "dW1", "db1", "dW2", "db2", "workspace")}
 
-    def step(events=None):
+    def step(events=None, bevents=None):
         sffn.switch_ffn_forward(inp["x"], inp["Wr"], inp["W1"], inp["b1"], inp["W2"], inp["b2"],
                                 w.CF, stats=stats, stage_events=events, k=K, flags=FLAGS,
                                 **bufs)
+        if BWD:
+            sffn.switch_ffn_backward(inp["x"], inp["Wr"], inp["W1"], inp["b1"], inp["W2"],
+                                     inp["b2"], w.CF, bufs, dy, 0.01, stage_events=bevents,
+                                     **gbufs)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize(dev)
     y_ref = bufs["y"].clone()
+    dx_ref = gbufs["dx"].clone() if BWD else None
 
     def timed(run, n_steps):
         t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -336,9 +399,13 @@ def main():
                     step()
             torch.cuda.synchronize(dev)
             bufs["y"].zero_()
+            if BWD:
+                gbufs["dx"].zero_()
             g.replay()
             torch.cuda.synchronize(dev)
             exact = bool(torch.equal(bufs["y"], y_ref))
+            if BWD:
+                exact = exact and bool(torch.equal(gbufs["dx"], dx_ref))
             graph_info = {"calls_per_graph": args.graph, "replay_matches_eager": exact,
                           "used": exact}
             if exact:
@@ -365,11 +432,18 @@ def main():
         for e in row:
             e.record(stream)
     torch.cuda.synchronize(dev)
+    bevs = [[torch.cuda.Event(enable_timing=True) for _ in range(nbs + 1)] for _ in range(args.steps)]
+    for row in bevs:
+        for e in row:
+            e.record(stream)
+    torch.cuda.synchronize(dev)
     for k in range(args.steps):
-        step(evs[k])
+        step(evs[k], bevs[k] if BWD else None)
     torch.cuda.synchronize(dev)
     stage_ms = {names[i]: sum(evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(args.steps))
                 / args.steps for i in range(nst)}
+    bwd_ms = {bnames[i]: sum(bevs[k][i].elapsed_time(bevs[k][i + 1]) for k in range(args.steps))
+              / args.steps for i in range(nbs)}
 
     # Per-call wall time on the stream: an event between consecutive eager calls.
     cev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
@@ -388,23 +462,35 @@ def main():
     accepted = int(acc.sum())
     active = int((acc > 0).sum())
     dropped = int(stats["n_dropped"].cpu()[0])
-    dominant = max(stage_ms, key=stage_ms.get)
-    alg = algorithmic_bytes(w, dominant, accepted, active, esize, dropped, K, args.reroute)
+    parts = None
+    if BWD:
+        tiles = ((N + 127) // 128) * ((w.d + 127) // 128)
+        parts = max(1, min((1024 + tiles - 1) // tiles, (T + 31) // 32))
+
+    def stage_bytes(name):
+        if name.startswith("bwd_"):
+            return backward_bytes(w, name[4:], accepted, active, esize, parts)
+        return algorithmic_bytes(w, name, accepted, active, esize, dropped, K, args.reroute)
+
+    all_ms = dict(stage_ms)
+    all_ms.update({"bwd_" + k: v for k, v in bwd_ms.items()})
+    dominant = max(all_ms, key=all_ms.get)
+    alg = stage_bytes(dominant)
     stage_table = {}
-    for name, ms in stage_ms.items():
-        b = algorithmic_bytes(w, name, accepted, active, esize, dropped, K, args.reroute)
+    for name, ms in all_ms.items():
+        b = stage_bytes(name)
         gbs = b / (ms * 1e-3) / 1e9 if (b and ms > 0) else None
         stage_table[name] = {"ms": ms, "algorithmic_bytes": b, "GB_per_s": gbs,
                              "hbm_frac": gbs / HBM_PEAK_GBS if gbs else None}
-    achieved = alg / (stage_ms[dominant] * 1e-3) / 1e9 if alg else None
+    achieved = alg / (all_ms[dominant] * 1e-3) / 1e9 if alg else None
     gemm_flops = (6.0 if w.glu else 4.0) * accepted * w.d * w.F
     gemm_ms = stage_ms.get("ffn1", 0.0) + stage_ms.get("ffn2", 0.0)
     wname = (w.name + ("_top2" if K == 2 else "") + ("_reroute" if args.reroute else "")
-             + ("_geglu" if w.glu else ""))
+             + ("_geglu" if w.glu else "") + ("_train" if BWD else ""))
     traffic = measured_traffic(dominant, wname)
 
     result = {
-        "metric": "SwitchFFN fwd tokens/s",
+        "metric": "SwitchFFN fwd+bwd tokens/s" if BWD else "SwitchFFN fwd tokens/s",
         "value": T / (ms_per_step * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -426,7 +512,7 @@ def main():
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": (achieved / HBM_PEAK_GBS) if achieved else None,
                      "traffic": traffic, "algorithmic_bytes": alg},
-        "stages_ms": stage_ms,
+        "stages_ms": all_ms,
         "stages": stage_table,
         "per_call_ms": {"median": pct(0.5), "p10": pct(0.1), "p90": pct(0.9),
                         "note": "eager calls with an event between consecutive calls"},

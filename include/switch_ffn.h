@@ -181,6 +181,50 @@ int switch_ffn_forward_topk(const void* x, const float* Wr, const void* W1, cons
                             size_t workspace_bytes, void* stream, uint32_t flags,
                             const sffn_stats* stats, void* const* stage_events);
 
+/* Backward pass of the top-1 layer with ReLU experts (forward flags 0: k = 1,
+ * residual on, no rerouting, no GEGLU).  The routing is a piecewise-constant
+ * choice without a gradient; the router learns through the gate p[t, e_t]
+ * ("Switch Transformers" summary, section 3.4, "Switch Routing: The k=1
+ * Simplification") and through P_i of the aux loss, f_i being a count with no
+ * gradient ("Switch Transformer, explained.", the symbols under "Why one
+ * expert is enough"; the summary's "The Load-Balancing Auxiliary Loss").
+ * For an accepted token t of expert e (a = W1 x + b1, h = ReLU(a),
+ * o = W2 h + b2, g = gate):
+ *   dW2_e += g dy h^T,  db2_e += g dy,  da = (W2^T g dy) * [h > 0],
+ *   dW1_e += da x^T,  db1_e += da,  dx_t = dy_t + W1^T da + Wr^T dz_t,
+ *   dz_t = p_t * (u_t - p_t . u_t),  u_{t,i} = d_aux N f_i / T + [i = e] dy . o
+ * (dropped tokens: dx_t = dy_t + Wr^T dz_t with the aux term of u alone);
+ * dWr = sum_t dz_t x_t^T.  ReLU'(0) = 0; the mask uses the forward's H.
+ * Arguments:
+ *   x, Wr, W1, b1, W2, b2, T, d, F, N, CF, dtype  exactly as in the forward call
+ *   expert_idx, slot  [T] the forward's outputs (device)
+ *   fwd_workspace     the forward's workspace (device), as that call left it:
+ *                     it holds the dispatch (offsets, row maps, gates, counts)
+ *                     and the hidden activations H; only read here
+ *   dy                [T, d] dL/dy (device, dtype)
+ *   d_aux             dL/d(aux_loss) (host value; the alpha factor goes here)
+ * Outputs (device, caller-allocated, overwritten): dx [T, d] (dtype),
+ * dWr [N, d] fp32, dW1 [N, F, d], dW2 [N, d, F] (dtype), db1 [N, F] and
+ * db2 [N, d] (dtype; each nullable: then not computed).  Experts without
+ * tokens get zero gradients.  `workspace`: a device buffer of at least
+ * switch_ffn_backward_workspace_bytes() bytes, 256-byte aligned, separate
+ * from fwd_workspace.  stage_events: NULL or switch_ffn_backward_num_stages()+1
+ * events, recorded like forward_ex's.  Returns SFFN_OK, SFFN_EINVAL (a null
+ * required pointer, d_aux not finite, or the shape checks of the forward),
+ * SFFN_EWORKSPACE (either workspace too small), SFFN_EUNSUPPORTED (alignment,
+ * limits) or SFFN_EHIP. */
+size_t switch_ffn_backward_workspace_bytes(int64_t T, int64_t d, int64_t F, int64_t N, double CF,
+                                           int dtype);
+int switch_ffn_backward(const void* x, const float* Wr, const void* W1, const void* b1,
+                        const void* W2, const void* b2, int64_t T, int64_t d, int64_t F,
+                        int64_t N, double CF, int dtype, const int32_t* expert_idx,
+                        const int32_t* slot, const void* fwd_workspace,
+                        size_t fwd_workspace_bytes, const void* dy, float d_aux, void* dx,
+                        float* dWr, void* dW1, void* db1, void* dW2, void* db2, void* workspace,
+                        size_t workspace_bytes, void* stream, void* const* stage_events);
+int switch_ffn_backward_num_stages(void);
+const char* switch_ffn_backward_stage_name(int stage);
+
 /* Number of stages forward_ex reports events around, and their names
  * ("router_logits", "softmax_route", ...); NULL for an index out of range. */
 int switch_ffn_num_stages(void);

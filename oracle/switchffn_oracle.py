@@ -502,8 +502,8 @@ def backward(x, Wr, experts, CF: float, dy, d_aux: float = 0.0, *,
 
     experts, expert_idx and only_experts as for forward (expert_idx replays a given
     routing).  only_experts: the weight and bias gradients of the other experts are
-    NaN, and so are the dx rows of their accepted tokens; the router gradient needs
-    every accepted token's dg, so it is computed only when only_experts is None.
+    NaN, and so are the dz and dx rows of their accepted tokens (whose dg is then
+    unknown); dWr, a sum over every token, is computed only when only_experts is None.
     Returns dx [T, d], dWr [N, d], dW1 [N, F, d], db1 [N, F], dW2 [N, d, F],
     db2 [N, d] (float64), and dg [T] and dz [T, N].
     """
@@ -550,17 +550,20 @@ def backward(x, Wr, experts, CF: float, dy, d_aux: float = 0.0, *,
 
     out = {"C": C, "expert_idx": eidx, "slot": dp["slot"], "gate": gate, "dg": dg,
            "dW1": dW1, "db1": db1, "dW2": dW2, "db2": db2}
-    if only_experts is not None:
-        for e in range(N):
-            if e not in grads:
-                dx[dp["row2tok"][dp["offset"][e]:dp["offset"][e + 1]]] = np.nan
-        out["dx"] = dx
-        return out
     u = np.broadcast_to(aux_prob_grad(dp["hist"], T, d_aux), (T, N)).copy()
     acc = dp["slot"] >= 0
     u[np.nonzero(acc)[0], eidx[acc]] += dg[acc]
     dz = softmax_backward(p, u)
-    out.update(dz=dz, dWr=dz.T @ x, dx=dx + dz @ Wr)
+    dx = dx + dz @ Wr
+    if only_experts is not None:
+        for e in range(N):
+            if e not in grads:
+                rows = dp["row2tok"][dp["offset"][e]:dp["offset"][e + 1]]
+                dz[rows] = np.nan
+                dx[rows] = np.nan
+        out.update(dz=dz, dx=dx)
+        return out
+    out.update(dz=dz, dWr=dz.T @ x, dx=dx)
     return out
 
 

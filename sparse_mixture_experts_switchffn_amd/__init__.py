@@ -20,6 +20,10 @@ from .binding import (  # noqa: F401
     LIB_PATH,
     header_functions,
     lib,
+    switch_ffn_backward,
+    switch_ffn_backward_num_stages,
+    switch_ffn_backward_stage_name,
+    switch_ffn_backward_workspace_bytes,
     switch_ffn_capacity,
     switch_ffn_forward,
     switch_ffn_forward_ex,

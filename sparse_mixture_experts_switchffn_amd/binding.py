@@ -63,6 +63,17 @@ def load_library(path: str = LIB_PATH):
     L.switch_ffn_forward_topk.restype = ctypes.c_int
     L.switch_ffn_forward_topk.argtypes = (_FWD_ARGS[:11] + [ctypes.c_int] + _FWD_ARGS[11:] +
                                           [ctypes.c_uint32, ctypes.POINTER(sffn_stats), _P])
+    L.switch_ffn_backward_workspace_bytes.restype = ctypes.c_size_t
+    L.switch_ffn_backward_workspace_bytes.argtypes = [_I64, _I64, _I64, _I64, ctypes.c_double,
+                                                      ctypes.c_int]
+    L.switch_ffn_backward.restype = ctypes.c_int
+    L.switch_ffn_backward.argtypes = (_FWD_ARGS[:12] + [_P, _P, _P, ctypes.c_size_t, _P,
+                                                        ctypes.c_float] + [_P] * 6 +
+                                      [_P, ctypes.c_size_t, _P, _P])
+    L.switch_ffn_backward_num_stages.restype = ctypes.c_int
+    L.switch_ffn_backward_num_stages.argtypes = []
+    L.switch_ffn_backward_stage_name.restype = ctypes.c_char_p
+    L.switch_ffn_backward_stage_name.argtypes = [ctypes.c_int]
     L.switch_ffn_num_stages.restype = ctypes.c_int
     L.switch_ffn_num_stages.argtypes = []
     L.switch_ffn_stage_name.restype = ctypes.c_char_p
@@ -97,6 +108,19 @@ def switch_ffn_workspace_bytes(T, d, F, N, CF, dtype) -> int:
 
 def switch_ffn_workspace_bytes_topk(T, d, F, N, CF, k, dtype) -> int:
     return lib().switch_ffn_workspace_bytes_topk(T, d, F, N, CF, k, dtype)
+
+
+def switch_ffn_backward_workspace_bytes(T, d, F, N, CF, dtype) -> int:
+    return lib().switch_ffn_backward_workspace_bytes(T, d, F, N, CF, dtype)
+
+
+def switch_ffn_backward_num_stages() -> int:
+    return lib().switch_ffn_backward_num_stages()
+
+
+def switch_ffn_backward_stage_name(i: int):
+    s = lib().switch_ffn_backward_stage_name(i)
+    return None if s is None else s.decode()
 
 
 def switch_ffn_num_stages() -> int:
@@ -196,3 +220,52 @@ def switch_ffn_forward(x, Wr, W1, b1, W2, b2, CF: float, *, y=None, expert_idx=N
 # forward_ex's and forward_topk's extra arguments are keyword arguments of switch_ffn_forward.
 switch_ffn_forward_ex = switch_ffn_forward
 switch_ffn_forward_topk = switch_ffn_forward
+
+
+def switch_ffn_backward(x, Wr, W1, b1, W2, b2, CF: float, fwd: dict, dy, d_aux: float = 0.0, *,
+                        dx=None, dWr=None, dW1=None, db1=None, dW2=None, db2=None,
+                        workspace=None, stream=None, stage_events=None,
+                        check: bool = True) -> dict:
+    """Gradients of the top-1 ReLU layer (switch_ffn_backward).
+
+    fwd: what switch_ffn_forward returned for the same inputs (its expert_idx, slot and
+    workspace, untouched since).  dy [T, d] like x; d_aux = dL/d(aux_loss).  Returns dx,
+    dWr (fp32), dW1, db1, dW2, db2 (db1/db2 None when the bias is absent).
+    """
+    import torch
+
+    T, d = x.shape
+    N = Wr.shape[0]
+    F = W2.shape[2]
+    dt = _dtype_code(x)
+    dev = x.device
+    dx = torch.empty_like(x) if dx is None else dx
+    dWr = torch.empty((N, d), dtype=torch.float32, device=dev) if dWr is None else dWr
+    dW1 = torch.empty_like(W1) if dW1 is None else dW1
+    dW2 = torch.empty_like(W2) if dW2 is None else dW2
+    if db1 is None and b1 is not None:
+        db1 = torch.empty_like(b1)
+    if db2 is None and b2 is not None:
+        db2 = torch.empty_like(b2)
+    nbytes = switch_ffn_backward_workspace_bytes(T, d, F, N, CF, dt)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    ev = None
+    if stage_events is not None:
+        handles = [e.cuda_event for e in stage_events]
+        if any(h == 0 for h in handles):
+            raise ValueError("stage events must be recorded once before use (handle is null)")
+        ev = (ctypes.c_void_p * len(handles))(*handles)
+    fws = fwd["workspace"]
+    rc = lib().switch_ffn_backward(
+        _ptr(x), _ptr(Wr), _ptr(W1), _ptr(b1), _ptr(W2), _ptr(b2), T, d, F, N, CF, dt,
+        _ptr(fwd["expert_idx"]), _ptr(fwd["slot"]), _ptr(fws), fws.numel() * fws.element_size(),
+        _ptr(dy), float(d_aux), _ptr(dx), _ptr(dWr), _ptr(dW1), _ptr(db1), _ptr(dW2), _ptr(db2),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), stream,
+        None if ev is None else ctypes.cast(ev, ctypes.c_void_p))
+    if check and rc != SFFN_OK:
+        raise RuntimeError(f"switch_ffn_backward failed ({rc}): {switch_ffn_status_string(rc)}")
+    return {"status": rc, "dx": dx, "dWr": dWr, "dW1": dW1, "db1": db1, "dW2": dW2, "db2": db2,
+            "workspace": workspace}

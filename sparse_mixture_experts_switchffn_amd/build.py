@@ -11,7 +11,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libswitchffn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["api.hip", "router.hip", "dispatch.hip", "ffn.hip"]
+SOURCES = ["api.hip", "router.hip", "dispatch.hip", "ffn.hip", "bwd.hip"]
 FLAGS = ["-O3", "--offload-arch=gfx950", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-result",
          # Packed fp32 instructions stay off: the compiler must not form them.
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

@@ -90,6 +90,7 @@ static int make_shape(int64_t T, int64_t d, int64_t F, int64_t N, double CF, int
   s->k = k;
   s->reroute = reroute ? 1 : 0;
   s->glu = glu ? 1 : 0;
+  s->stage_logits = 0;
   s->n_route_blocks = (int)((T + sffn::kRouteTokens - 1) / sffn::kRouteTokens);
   const int64_t cap_rows = N * Ce;
   s->max_rows = (int)(cap_rows < k * T ? cap_rows : k * T);
@@ -209,6 +210,103 @@ int switch_ffn_forward_topk(const void* x, const float* Wr, const void* W1, cons
   if (s.k == 2 && (e = sffn::launch_combine(s, in, ws, out, no_res, st)) != hipSuccess)
     return record_hip_error(e, "combine");
   if ((e = mark(6)) != hipSuccess) return record_hip_error(e, "event record");
+  return SFFN_OK;
+}
+
+namespace {
+const char* const kBwdStageNames[] = {"router_logits", "expert_dgrad_hidden", "router_grad",
+                                      "expert_dgrad_input", "dx", "router_wgrad",
+                                      "expert_wgrad", "bias_grad"};
+constexpr int kNumBwdStages = (int)(sizeof(kBwdStageNames) / sizeof(kBwdStageNames[0]));
+
+// Backward scratch: dz [T, N] fp32 | router planes | dA [max_rows, F] | partial dg |
+// dXe [T, d] fp32 | partial dWr.
+size_t bwd_layout(const sffn::Shape& s, char* base, sffn::BwdState* b) {
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    char* p = base ? base + off : nullptr;
+    off += align256(bytes);
+    return p;
+  };
+  const size_t T = (size_t)s.T, N = (size_t)s.N, esize = s.dtype == SFFN_BF16 ? 2 : 4;
+  sffn::Shape sr = s;
+  sr.stage_logits = 1;
+  const int n_dgp = sffn::bwd_dgp_tiles(s), parts = sffn::bwd_wr_parts(s);
+  float* dz = (float*)take(T * N * 4);
+  uint16_t* planes = (uint16_t*)take(sffn::router_planes_bytes(sr));
+  void* dA = take((size_t)s.max_rows * s.F * esize + 16);
+  float* dgp = (float*)take((size_t)n_dgp * s.max_rows * 4 + 4);
+  float* dxe = (float*)take(T * s.d * 4);
+  float* wrp = (float*)take((size_t)parts * N * s.d * 4);
+  if (b) {
+    b->dz = dz;
+    b->planes = planes;
+    b->dA = dA;
+    b->dgp = dgp;
+    b->n_dgp = n_dgp;
+    b->dxe = dxe;
+    b->wrp = wrp;
+    b->n_wr_parts = parts;
+  }
+  return off;
+}
+}  // namespace
+
+size_t switch_ffn_backward_workspace_bytes(int64_t T, int64_t d, int64_t F, int64_t N, double CF,
+                                           int dtype) {
+  sffn::Shape s;
+  if (make_shape(T, d, F, N, CF, dtype, 1, false, &s) != SFFN_OK) return 0;
+  return bwd_layout(s, nullptr, nullptr);
+}
+
+int switch_ffn_backward_num_stages(void) { return kNumBwdStages; }
+
+const char* switch_ffn_backward_stage_name(int stage) {
+  return (stage >= 0 && stage < kNumBwdStages) ? kBwdStageNames[stage] : nullptr;
+}
+
+int switch_ffn_backward(const void* x, const float* Wr, const void* W1, const void* b1,
+                        const void* W2, const void* b2, int64_t T, int64_t d, int64_t F,
+                        int64_t N, double CF, int dtype, const int32_t* expert_idx,
+                        const int32_t* slot, const void* fwd_workspace,
+                        size_t fwd_workspace_bytes, const void* dy, float d_aux, void* dx,
+                        float* dWr, void* dW1, void* db1, void* dW2, void* db2, void* workspace,
+                        size_t workspace_bytes, void* stream, void* const* stage_events) {
+  if (!x || !Wr || !W1 || !W2 || !expert_idx || !slot || !fwd_workspace || !dy || !dx || !dWr ||
+      !dW1 || !dW2 || !isfinite(d_aux))
+    return SFFN_EINVAL;
+  sffn::Shape s;
+  const int rc = make_shape(T, d, F, N, CF, dtype, 1, false, &s);
+  if (rc != SFFN_OK) return rc;
+  if (dtype == SFFN_BF16 && !(aligned16(x) && aligned16(Wr) && aligned16(W1) && aligned16(W2) &&
+                              aligned16(dy) && aligned16(dx) && aligned16(dW1) && aligned16(dW2)))
+    return SFFN_EUNSUPPORTED;
+  if (fwd_workspace_bytes < sffn::workspace_layout(s, nullptr, nullptr)) return SFFN_EWORKSPACE;
+  if (!workspace || workspace_bytes < bwd_layout(s, nullptr, nullptr)) return SFFN_EWORKSPACE;
+  if ((((uintptr_t)workspace | (uintptr_t)fwd_workspace) & 255) != 0) return SFFN_EUNSUPPORTED;
+
+  sffn::Workspace fw;
+  sffn::workspace_layout(s, &fw, (char*)const_cast<void*>(fwd_workspace));
+  sffn::BwdState b{};
+  bwd_layout(s, (char*)workspace, &b);
+  b.expert_idx = expert_idx;
+  b.slot = slot;
+  b.offset = fw.offset;
+  b.row2tok = fw.row2tok;
+  b.rowgate = fw.rowgate;
+  b.hist = fw.hist;
+  b.H = fw.H;
+  b.dy = dy;
+  b.d_aux = d_aux;
+  b.dx = dx;
+  b.dWr = dWr;
+  b.dW1 = dW1;
+  b.db1 = db1;
+  b.dW2 = dW2;
+  b.db2 = db2;
+  const sffn::Inputs in{x, Wr, W1, b1, W2, b2};
+  const hipError_t e = sffn::launch_backward(s, in, b, (hipStream_t)stream, stage_events);
+  if (e != hipSuccess) return record_hip_error(e, "backward");
   return SFFN_OK;
 }
 

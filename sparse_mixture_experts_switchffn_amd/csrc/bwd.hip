@@ -1,0 +1,792 @@
+// Backward pass of the Switch layer: top-1 routing, ReLU experts.
+//
+// The routing (argmax and capacity) is a piecewise-constant choice without a
+// gradient; the router learns through the gate p[t, e_t] that scales the
+// expert output ("Switch Transformers: Scaling to Trillion Parameter Models
+// with Simple and Efficient Sparsity", section 3.4, "Switch Routing: The k=1
+// Simplification") and through P_i of the aux loss, f_i being a count
+// ("Switch Transformer, explained.", the symbol list under "Why one expert is
+// enough").  With a = W1 x + b1, h = ReLU(a), o = W2 h + b2 for an accepted
+// token t of expert e:
+//   Q_t   = W2^T dy_t                         (E1: [rows, F] = dY_g W2_e)
+//   dA_t  = g_t Q_t * [h_t > 0],  dg_t = Q_t . h_t + dy_t . b2_e
+//   dXe_t = W1^T dA_t                         (E2: [rows, d] = dA W1_e)
+//   dW2_e = sum_t g_t dy_t h_t^T               (E3: [d, F], contraction over rows)
+//   dW1_e = sum_t dA_t x_t^T                   (E4: [F, d], contraction over rows)
+//   db2_e = sum_t g_t dy_t,  db1_e = sum_t dA_t
+//   u_{t,i} = d_aux N f_i / T + [t accepted][i = e_t] dg_t,  dz_t = p_t * (u_t - p_t . u_t)
+//   dWr = dz^T x,  dx = dy + dXe + dz Wr       (fp32 router)
+// h is the forward's bf16 H (its mask h > 0 is a > 0 up to rounding to zero).
+#include "sffn_device.h"
+#include "sffn_internal.h"
+#include "../../include/switch_ffn.h"
+
+namespace sffn {
+
+// ---------------------------------------------------------------------------
+// bf16 grouped GEMMs E1..E4 on the matrix cores.
+//
+// Block tile 128 x 128, k-steps of 32, four waves of 64 x 64 (2 x 2 MFMA
+// tiles of 32 x 32).  Both operands sit in LDS as [outer][k] rows (k
+// contiguous, 80-byte pitch), which is what a v_mfma_f32_32x32x16_bf16
+// operand fragment reads (8 consecutive k of one row per lane, one 16-byte
+// LDS read).  An operand that is k-contiguous in memory (E1 and E2's row
+// operand) is copied in 16-byte chunks.  The others hold k as their row index
+// in memory (the weights of E1/E2 are [k][n]; E3/E4 contract over the
+// expert's rows); a thread loads two consecutive k rows of one 8-element
+// chunk and writes the eight (k, k+1) pairs as 32-bit words into their
+// columns, which transposes the tile on its way into LDS.  Double-buffered:
+// the next step's loads are in flight during this step's matrix ops.
+//
+//   E1: rows x F,  K = d     A = dy[row2tok[r]]     B = W2_e [d][F]
+//   E2: rows x d,  K = F     A = dA[r]              B = W1_e [F][d]
+//   E3: d x F,     K = rows  A = g_r dy[row2tok[r]] B = H[r]          -> dW2_e
+//   E4: F x d,     K = rows  A = dA[r]              B = x[row2tok[r]] -> dW1_e
+// ---------------------------------------------------------------------------
+constexpr int GM = 128, GN = 128, GK = 32;
+constexpr int GP = GK + 8;  // LDS row pitch in bf16 (80 bytes: fragment reads spread over banks)
+
+struct BwdGemmArgs {
+  const uint16_t* a;
+  const uint16_t* b;
+  const int* offset;
+  const int* row2tok;
+  const float* rowgate;
+  const uint16_t* H;
+  void* out;
+  float* dgp;
+  int T, d, F, max_rows, mt_max;
+};
+
+template <int KIND>
+__global__ void __launch_bounds__(256)
+bwd_gemm_kernel(BwdGemmArgs g) {
+  constexpr bool ROWS_M = KIND <= 2;  // M runs over the expert's rows (else K does)
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][GM][GP];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][GN][GP];
+  __shared__ float red[GM];
+
+  const int Nn = (KIND == 1 || KIND == 3) ? g.F : g.d;
+  const int Mfix = KIND == 3 ? g.d : g.F;  // E3/E4
+  const int Kfix = KIND == 1 ? g.d : g.F;  // E1/E2
+  const int n_nt = (Nn + GN - 1) / GN;
+  const int n_mt = ROWS_M ? g.mt_max : (Mfix + GM - 1) / GM;
+  const int tile = xcd_contiguous_tile(blockIdx.x, gridDim.x);
+  const int e = tile / (n_nt * n_mt);
+  const int rest = tile % (n_nt * n_mt);
+  const int mt = rest / n_nt, nt = rest % n_nt;
+  const int rbeg = g.offset[e];
+  const int Ae = g.offset[e + 1] - rbeg;
+  const int M = ROWS_M ? Ae : Mfix;
+  const int K = ROWS_M ? Kfix : Ae;
+  const int m0 = mt * GM, n0 = nt * GN;
+  if (ROWS_M && m0 >= Ae) return;  // uniform over the block
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave & 1, wn = wave >> 1;
+
+  // ---- operand A ----
+  // k-contiguous rows (E1, E2): thread rows m0 + tid/4 + 64 i, chunk tid % 4.
+  const int ac = tid & 3;
+  uint32_t a_row_off[2];
+  __amdgpu_buffer_rsrc_t a_src;
+  // k as the row index (E3, E4) and every B: thread k rows 2*(tid%16) + {0,1},
+  // chunk tid/16 of the 128-wide inner range.
+  const int kp = tid & 15, pc = tid >> 4;
+  __amdgpu_buffer_rsrc_t b_src;
+  if constexpr (KIND == 1) {
+    a_src = make_rsrc(g.a, (uint32_t)g.T * (uint32_t)g.d * 2u);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r = m0 + (tid >> 2) + 64 * i;
+      a_row_off[i] = r < Ae ? (uint32_t)g.row2tok[rbeg + r] * (uint32_t)g.d * 2u : kOob;
+    }
+    b_src = make_rsrc(g.b + (size_t)e * g.d * g.F, (uint32_t)((size_t)g.d * g.F * 2));
+  } else if constexpr (KIND == 2) {
+    a_src = make_rsrc(g.a + (size_t)rbeg * g.F, (uint32_t)Ae * (uint32_t)g.F * 2u);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r = m0 + (tid >> 2) + 64 * i;
+      a_row_off[i] = r < Ae ? (uint32_t)r * (uint32_t)g.F * 2u : kOob;
+    }
+    b_src = make_rsrc(g.b + (size_t)e * g.F * g.d, (uint32_t)((size_t)g.F * g.d * 2));
+  } else if constexpr (KIND == 3) {
+    a_src = make_rsrc(g.a, (uint32_t)g.T * (uint32_t)g.d * 2u);
+    b_src = make_rsrc(g.b + (size_t)rbeg * g.F, (uint32_t)Ae * (uint32_t)g.F * 2u);
+  } else {
+    a_src = make_rsrc(g.a + (size_t)rbeg * g.F, (uint32_t)Ae * (uint32_t)g.F * 2u);
+    b_src = make_rsrc(g.b, (uint32_t)g.T * (uint32_t)g.d * 2u);
+  }
+  const int ldA = (KIND == 2 || KIND == 4) ? g.F : g.d;  // elements per memory row of A
+  const int ldB = (KIND == 1 || KIND == 3) ? g.F : g.d;  // ... and of B
+  const int nb_chunk = n0 + pc * 8;                      // B's inner chunk (n)
+  const int ma_chunk = m0 + pc * 8;                      // A's inner chunk (m) for E3/E4
+
+  // Memory row of k index kk for the operands that hold k as the row index:
+  // E1/E2 B: the weight row kk; E3 A and E4 B: the token of expert row kk;
+  // E3 B and E4 A: expert row kk.
+  auto tok_of = [&](int kk) -> int { return kk < Ae ? g.row2tok[rbeg + kk] : -1; };
+
+  u32x4 ra[2], rb[2];
+  float sc[2] = {1.f, 1.f};
+  // Index lookups of the k rows two steps ahead (E3/E4), so that the data
+  // loads of a step never wait for them.
+  int tk_next[2] = {-1, -1};
+  float gk_next[2] = {0.f, 0.f};
+  auto lookup = [&](int k0, int (&tk)[2], float (&gk)[2]) {
+    if constexpr (KIND == 3 || KIND == 4) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int kk = k0 + 2 * kp + q;
+        tk[q] = tok_of(kk);
+        if constexpr (KIND == 3) gk[q] = kk < Ae ? g.rowgate[rbeg + kk] : 0.f;
+      }
+    }
+  };
+  auto load = [&](int k0, const int (&tk)[2], const float (&gk)[2]) {
+    if constexpr (ROWS_M) {
+      const bool kin = k0 + ac * 8 < K;
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        ra[i] = buffer_load16(a_src, kin ? a_row_off[i] + (uint32_t)(k0 + ac * 8) * 2u : kOob);
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int kk = k0 + 2 * kp + q;
+        rb[q] = buffer_load16(b_src, (kk < K && nb_chunk < Nn)
+                                         ? ((uint32_t)kk * (uint32_t)ldB + (uint32_t)nb_chunk) * 2u
+                                         : kOob);
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int kk = k0 + 2 * kp + q;
+        const bool kin = kk < Ae;
+        // A: E3 gathered dy rows (scaled by the gate below), E4 expert rows of dA
+        const uint32_t arow = KIND == 3 ? (uint32_t)(tk[q] < 0 ? 0 : tk[q]) : (uint32_t)kk;
+        ra[q] = buffer_load16(a_src, (kin && ma_chunk < Mfix)
+                                         ? (arow * (uint32_t)ldA + (uint32_t)ma_chunk) * 2u
+                                         : kOob);
+        // B: E3 expert rows of H, E4 gathered x rows
+        const uint32_t brow = KIND == 4 ? (uint32_t)(tk[q] < 0 ? 0 : tk[q]) : (uint32_t)kk;
+        rb[q] = buffer_load16(b_src, (kin && nb_chunk < Nn)
+                                         ? (brow * (uint32_t)ldB + (uint32_t)nb_chunk) * 2u
+                                         : kOob);
+        if constexpr (KIND == 3) sc[q] = gk[q];
+      }
+    }
+  };
+  // Pairs (k, k+1) of the 8 inner elements of one chunk as 32-bit LDS words.
+  auto store_pairs = [&](uint16_t (*S)[GP], const u32x4 (&v)[2], int inner0, bool scale) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t lo = (v[0][j >> 1] >> (16 * (j & 1))) & 0xffffu;
+      const uint32_t hi = (v[1][j >> 1] >> (16 * (j & 1))) & 0xffffu;
+      uint32_t w;
+      if (scale)
+        w = pack_bf16x2(bf16_bits_to_f32(lo) * sc[0], bf16_bits_to_f32(hi) * sc[1]);
+      else
+        w = lo | (hi << 16);
+      *reinterpret_cast<uint32_t*>(&S[inner0 + j][2 * kp]) = w;
+    }
+  };
+  auto store = [&](int buf) {
+    if constexpr (ROWS_M) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) store16(&As[buf][(tid >> 2) + 64 * i][ac * 8], ra[i]);
+    } else {
+      store_pairs(As[buf], ra, pc * 8, KIND == 3);
+    }
+    store_pairs(Bs[buf], rb, pc * 8, false);
+  };
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+
+  const int khalf = lane >> 5;
+  auto compute = [&](int buf) {
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+      bf16x8 fa[2], fb[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        fa[i] = as_bf16x8(load16(&As[buf][wm * 64 + 32 * i + (lane & 31)][kh * 16 + khalf * 8]));
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        fb[j] = as_bf16x8(load16(&Bs[buf][wn * 64 + 32 * j + (lane & 31)][kh * 16 + khalf * 8]));
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma_32x32x16(fb[j], fa[i], acc[i][j]);
+    }
+  };
+
+  const int nk = (K + GK - 1) / GK;
+  int tk_cur[2] = {-1, -1};
+  float gk_cur[2] = {0.f, 0.f};
+  lookup(0, tk_cur, gk_cur);
+  lookup(GK, tk_next, gk_next);
+  load(0, tk_cur, gk_cur);
+  store(0);
+  __syncthreads();
+  for (int ks = 0; ks < nk; ++ks) {
+    const int cur = ks & 1;
+    const bool more = ks + 1 < nk;
+    if (more) {
+      load((ks + 1) * GK, tk_next, gk_next);
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        tk_cur[q] = tk_next[q];
+        gk_cur[q] = gk_next[q];
+      }
+      lookup((ks + 2) * GK, tk_next, gk_next);
+    }
+    compute(cur);
+    if (more) store(cur ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogues: lane holds row (l % 32) of each 32-row tile i and, for
+  // value 4 gq + q, column 8 gq + 4 (l / 32) + q of each 32-column tile j ----
+  const int lr = lane & 31;
+  if constexpr (KIND == 1) {
+    // dA = g Q [H > 0] (bf16) and the tile's partial dg = sum_n Q H per row.
+    const __amdgpu_buffer_rsrc_t h_src =
+        make_rsrc(g.H + (size_t)rbeg * g.F, (uint32_t)Ae * (uint32_t)g.F * 2u);
+    uint16_t* dA = reinterpret_cast<uint16_t*>(g.out);
+    const __amdgpu_buffer_rsrc_t o_src =
+        make_rsrc(dA + (size_t)rbeg * g.F, (uint32_t)Ae * (uint32_t)g.F * 2u);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r = m0 + wm * 64 + 32 * i + lr;
+      const bool rok = r < Ae;
+      const float gate = rok ? g.rowgate[rbeg + r] : 0.f;
+      float part = 0.f;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const int n = n0 + wn * 64 + 32 * j + 8 * gq + 4 * khalf;
+          const bool ok = rok && n < g.F;
+          const uint32_t off = ok ? ((uint32_t)r * (uint32_t)g.F + (uint32_t)n) * 2u : kOob;
+          const u32x2 hv{__builtin_amdgcn_raw_buffer_load_b32(h_src, (int)off, 0, 0),
+                         __builtin_amdgcn_raw_buffer_load_b32(h_src, (int)(ok ? off + 4u : kOob), 0, 0)};
+          float h[4], da[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            h[q] = bf16_bits_to_f32((hv[q >> 1] >> (16 * (q & 1))) & 0xffffu);
+            const float qv = acc[i][j][4 * gq + q];
+            part += qv * h[q];
+            da[q] = h[q] > 0.f ? gate * qv : 0.f;
+          }
+          __builtin_amdgcn_raw_buffer_store_b32(pack_bf16x2(da[0], da[1]), o_src, (int)off, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b32(pack_bf16x2(da[2], da[3]), o_src,
+                                                (int)(ok ? off + 4u : kOob), 0, 0);
+        }
+      }
+      part += __shfl_xor(part, 32);
+      // the two column halves of the tile (waves wn = 0, 1) meet in LDS
+      if (wn == 1 && khalf == 0) red[wm * 64 + 32 * i + lr] = part;
+      __syncthreads();
+      if (wn == 0 && khalf == 0 && rok)
+        g.dgp[(size_t)nt * g.max_rows + rbeg + r] = part + red[wm * 64 + 32 * i + lr];
+      __syncthreads();
+    }
+  } else if constexpr (KIND == 2) {
+    // expert part of dx, fp32, at the token's row
+    float* dxe = reinterpret_cast<float*>(g.out);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r = m0 + wm * 64 + 32 * i + lr;
+      if (r >= Ae) continue;
+      float* row = dxe + (size_t)g.row2tok[rbeg + r] * g.d;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const int n = n0 + wn * 64 + 32 * j + 8 * gq + 4 * khalf;
+          if (n < g.d)
+            *reinterpret_cast<f32x4*>(row + n) =
+                f32x4{acc[i][j][4 * gq], acc[i][j][4 * gq + 1], acc[i][j][4 * gq + 2],
+                      acc[i][j][4 * gq + 3]};
+        }
+      }
+    }
+  } else {
+    // dW2_e [d][F] (E3) or dW1_e [F][d] (E4), bf16
+    uint16_t* out = reinterpret_cast<uint16_t*>(g.out) + (size_t)e * g.d * g.F;
+    const __amdgpu_buffer_rsrc_t o_src = make_rsrc(out, (uint32_t)((size_t)g.d * g.F * 2));
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int m = m0 + wm * 64 + 32 * i + lr;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const int n = n0 + wn * 64 + 32 * j + 8 * gq + 4 * khalf;
+          const bool ok = m < M && n < Nn;
+          const uint32_t off = ok ? ((uint32_t)m * (uint32_t)Nn + (uint32_t)n) * 2u : kOob;
+          const f32x16& a = acc[i][j];
+          __builtin_amdgcn_raw_buffer_store_b32(pack_bf16x2(a[4 * gq], a[4 * gq + 1]), o_src,
+                                                (int)off, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b32(pack_bf16x2(a[4 * gq + 2], a[4 * gq + 3]), o_src,
+                                                (int)(ok ? off + 4u : kOob), 0, 0);
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 experts: one thread per output (or per row for E1), fp32 FMA in k
+// order.  The fp32 layer's backward (small parity shapes).
+// ---------------------------------------------------------------------------
+// E1: one thread per expert row: Q = W2^T dy, dA = g Q [H > 0], dg part = Q . H.
+__global__ void __launch_bounds__(256)
+bwd_e1_f32_kernel(const float* __restrict__ dy, const float* __restrict__ W2,
+                  const int* __restrict__ offset, const int* __restrict__ row2tok,
+                  const float* __restrict__ rowgate, const float* __restrict__ H, int n_rows,
+                  int N, int d, int F, float* __restrict__ dA, float* __restrict__ dgp) {
+  const int row = blockIdx.x * 256 + threadIdx.x;
+  if (row >= n_rows || row >= offset[N]) return;
+  int e = 0;
+  while (e + 1 < N && offset[e + 1] <= row) ++e;
+  const float* y = dy + (size_t)row2tok[row] * d;
+  const float* w = W2 + (size_t)e * d * F;
+  const float gate = rowgate[row];
+  float part = 0.f;
+  for (int n = 0; n < F; ++n) {
+    float q = 0.f;
+    for (int k = 0; k < d; ++k) q = fmaf(y[k], w[(size_t)k * F + n], q);
+    const float h = H[(size_t)row * F + n];
+    part = fmaf(q, h, part);
+    dA[(size_t)row * F + n] = h > 0.f ? gate * q : 0.f;
+  }
+  dgp[row] = part;
+}
+
+// E2: dXe[tok(row)][n] = sum_j dA[row][j] W1_e[j][n].
+__global__ void __launch_bounds__(256)
+bwd_e2_f32_kernel(const float* __restrict__ dA, const float* __restrict__ W1,
+                  const int* __restrict__ offset, const int* __restrict__ row2tok, int n_rows,
+                  int N, int d, int F, float* __restrict__ dxe) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (long)n_rows * d) return;
+  const int row = (int)(i / d), n = (int)(i % d);
+  if (row >= offset[N]) return;
+  int e = 0;
+  while (e + 1 < N && offset[e + 1] <= row) ++e;
+  const float* w = W1 + (size_t)e * F * d;
+  float s = 0.f;
+  for (int j = 0; j < F; ++j) s = fmaf(dA[(size_t)row * F + j], w[(size_t)j * d + n], s);
+  dxe[(size_t)row2tok[row] * d + n] = s;
+}
+
+// E3 (SECOND = false): dW2_e[m][n] = sum_r g_r dy[tok_r][m] H[r][n] over M = d, N = F.
+// E4 (SECOND = true):  dW1_e[m][n] = sum_r dA[r][m] x[tok_r][n]  over M = F, N = d.
+template <bool E4>
+__global__ void __launch_bounds__(256)
+bwd_wgrad_f32_kernel(const float* __restrict__ rowsA, const float* __restrict__ rowsB,
+                     const int* __restrict__ offset, const int* __restrict__ row2tok,
+                     const float* __restrict__ rowgate, int d, int F, float* __restrict__ out) {
+  const int e = blockIdx.y;
+  const int M = E4 ? F : d, Nn = E4 ? d : F;
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (long)M * Nn) return;
+  const int m = (int)(i / Nn), n = (int)(i % Nn);
+  float s = 0.f;
+  for (int r = offset[e]; r < offset[e + 1]; ++r) {
+    const int tok = row2tok[r];
+    const float a = E4 ? rowsA[(size_t)r * F + m] : rowgate[r] * rowsA[(size_t)tok * d + m];
+    const float b = E4 ? rowsB[(size_t)tok * d + n] : rowsB[(size_t)r * F + n];
+    s = fmaf(a, b, s);
+  }
+  out[(size_t)e * M * Nn + i] = s;
+}
+
+// ---------------------------------------------------------------------------
+// Router gradient, one wave per token: p from the staged fp32 logits, dg from
+// E1's partial sums plus dy . b2, then dz = p * (u - p . u) written over the
+// logits.  u_i = d_aux N hist_i / T^2 (+ dg at the token's expert).
+// ---------------------------------------------------------------------------
+template <bool BF16>
+__global__ void __launch_bounds__(256)
+bwd_router_grad_kernel(float* __restrict__ z, const int32_t* __restrict__ expert_idx,
+                       const int32_t* __restrict__ slot, const int* __restrict__ offset,
+                       const int* __restrict__ hist, const float* __restrict__ dgp, int n_dgp,
+                       int max_rows, const void* __restrict__ dyv, const void* __restrict__ b2v,
+                       int T, int d, int N, float d_aux) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (t >= T) return;
+  float* zr = z + (size_t)t * N;
+  float m = -INFINITY;
+  for (int i = lane; i < N; i += 64) m = fmaxf(m, zr[i]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  float S = 0.f;
+  for (int i = lane; i < N; i += 64) S += expf(zr[i] - m);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) S += __shfl_xor(S, off);
+  const float inv = 1.0f / S;
+
+  const int e = expert_idx[t];
+  const int sl = slot[t];
+  float dg = 0.f;
+  if (sl >= 0) {
+    const int row = offset[e] + sl;
+    for (int q = lane; q < n_dgp; q += 64) dg += dgp[(size_t)q * max_rows + row];
+    if (b2v) {
+      for (int k = lane; k < d; k += 64) {
+        const float yk = BF16 ? bf16_bits_to_f32(((const uint16_t*)dyv)[(size_t)t * d + k])
+                              : ((const float*)dyv)[(size_t)t * d + k];
+        const float bk = BF16 ? bf16_bits_to_f32(((const uint16_t*)b2v)[(size_t)e * d + k])
+                              : ((const float*)b2v)[(size_t)e * d + k];
+        dg = fmaf(yk, bk, dg);
+      }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) dg += __shfl_xor(dg, off);
+  }
+  const float caux = d_aux * (float)N / ((float)T * (float)T);
+  float pu = 0.f;
+  for (int i = lane; i < N; i += 64) {
+    const float p = expf(zr[i] - m) * inv;
+    const float u = caux * (float)hist[i] + (i == e && sl >= 0 ? dg : 0.f);
+    pu = fmaf(p, u, pu);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) pu += __shfl_xor(pu, off);
+  for (int i = lane; i < N; i += 64) {
+    const float p = expf(zr[i] - m) * inv;
+    const float u = caux * (float)hist[i] + (i == e && sl >= 0 ? dg : 0.f);
+    zr[i] = p * (u - pu);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 router GEMMs on the matrix cores (v_mfma_f32_32x32x2_f32: one k per
+// lane, so either operand layout loads directly).  Block tile 128 x 128, four
+// waves of 64 x 64, k-steps of 32.
+//   DX:  dx[t][n] = dy + [accepted] dXe + sum_j dz[t][j] Wr[j][n]   (K = N)
+//   DWR: part[p][j][n] = sum over the tokens of part p of dz[t][j] x[t][n]
+// ---------------------------------------------------------------------------
+constexpr int FK = 32;
+constexpr int FPA = FK + 1;   // [m][k] rows of dz (DX): odd pitch, conflict-free column reads
+constexpr int FPB = 128 + 32; // [k][n] rows: the two k of a fragment 32 banks apart
+
+__device__ __forceinline__ f32x16 mfma_f32_32x32x2(float a, float b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+template <bool DWR, bool BF16>
+__global__ void __launch_bounds__(256)
+bwd_router_gemm_kernel(const float* __restrict__ dz, const float* __restrict__ Wr,
+                       const void* __restrict__ xv, const void* __restrict__ dyv,
+                       const float* __restrict__ dxe, const int32_t* __restrict__ slot, int T,
+                       int d, int N, int tokens_per_part, void* __restrict__ outv) {
+  // DX: A = dz [T][N] kept as [m][k]; B = Wr [N][d] as [k][n].
+  // DWR: A = dz^T, kept as [k][m] (dz rows); B = x [T][d] as [k][n].
+  __shared__ float As[DWR ? FK * FPB : 128 * FPA];
+  __shared__ float Bs[FK * FPB];
+  const int Mdim = DWR ? N : T;
+  const int n_nt = (d + 127) / 128;
+  const int n_mt = (Mdim + 127) / 128;
+  const int bid = blockIdx.x;
+  const int part = bid / (n_mt * n_nt);
+  const int mt = (bid / n_nt) % n_mt, nt = bid % n_nt;
+  const int m0 = mt * 128, n0 = nt * 128;
+  const int kbeg = DWR ? part * tokens_per_part : 0;
+  const int kend = DWR ? min(T, kbeg + tokens_per_part) : N;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave & 1, wn = wave >> 1;
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+
+  for (int k0 = kbeg; k0 < kend; k0 += FK) {
+    // 32 x 128 elements per operand: 16 per thread, consecutive threads on
+    // consecutive addresses.
+#pragma unroll 4
+    for (int q = 0; q < 16; ++q) {
+      const int idx = tid + 256 * q;
+      if (DWR) {
+        const int kk = idx >> 7, mm = idx & 127;  // A[k][m] = dz[k0+kk][m0+mm]
+        const int k = k0 + kk, m = m0 + mm;
+        As[kk * FPB + mm] = (k < kend && m < N) ? dz[(size_t)k * N + m] : 0.f;
+      } else {
+        const int mm = idx >> 5, kk = idx & 31;   // A[m][k] = dz[m0+mm][k0+kk]
+        const int k = k0 + kk, m = m0 + mm;
+        As[mm * FPA + kk] = (k < kend && m < T) ? dz[(size_t)m * N + k] : 0.f;
+      }
+      const int kk = idx >> 7, nn = idx & 127;
+      const int k = k0 + kk, n = n0 + nn;
+      float bv = 0.f;
+      if (k < kend && n < d) {
+        if (DWR)
+          bv = BF16 ? bf16_bits_to_f32(((const uint16_t*)xv)[(size_t)k * d + n])
+                    : ((const float*)xv)[(size_t)k * d + n];
+        else
+          bv = Wr[(size_t)k * d + n];
+      }
+      Bs[kk * FPB + nn] = bv;
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int ks = 0; ks < FK; ks += 2) {
+      const int kk = ks + (lane >> 5);
+      float fa[2], fb[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int mm = wm * 64 + 32 * i + (lane & 31);
+        fa[i] = DWR ? As[kk * FPB + mm] : As[mm * FPA + kk];
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) fb[j] = Bs[kk * FPB + wn * 64 + 32 * j + (lane & 31)];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma_f32_32x32x2(fb[j], fa[i], acc[i][j]);
+    }
+    __syncthreads();
+  }
+
+  const int lr = lane & 31, khalf = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int m = m0 + wm * 64 + 32 * i + lr;
+    if (m >= Mdim) continue;
+    const bool accepted = !DWR && slot[m] >= 0;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int n = n0 + wn * 64 + 32 * j + 8 * (v >> 2) + 4 * khalf + (v & 3);
+        if (n >= d) continue;
+        const size_t o = (size_t)m * d + n;
+        if (DWR) {
+          ((float*)outv)[(size_t)part * N * d + o] = acc[i][j][v];
+        } else {
+          float val = acc[i][j][v] + (accepted ? dxe[o] : 0.f);
+          if (BF16) {
+            val += bf16_bits_to_f32(((const uint16_t*)dyv)[o]);
+            ((uint16_t*)outv)[o] = (uint16_t)f32_to_bf16_bits(val);
+          } else {
+            val += ((const float*)dyv)[o];
+            ((float*)outv)[o] = val;
+          }
+        }
+      }
+    }
+  }
+}
+
+// dWr = sum over parts, in part order.
+__global__ void __launch_bounds__(256)
+bwd_wr_reduce_kernel(const float* __restrict__ part, int parts, long n, float* __restrict__ out) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  float s = 0.f;
+  for (int p = 0; p < parts; ++p) s += part[(size_t)p * n + i];
+  out[i] = s;
+}
+
+// ---------------------------------------------------------------------------
+// Bias gradients, one thread per (expert, column): db2_e = sum_r g_r dy[tok_r],
+// db1_e = sum_r dA[r], rows in buffer order.
+// ---------------------------------------------------------------------------
+template <bool BF16>
+__global__ void __launch_bounds__(256)
+bwd_bias_kernel(const void* __restrict__ dyv, const void* __restrict__ dAv,
+                const int* __restrict__ offset, const int* __restrict__ row2tok,
+                const float* __restrict__ rowgate, int d, int F, void* __restrict__ db1v,
+                void* __restrict__ db2v) {
+  const int e = blockIdx.y;
+  const int c = blockIdx.x * 256 + threadIdx.x;  // columns of db2 then db1
+  const bool first = c < d;
+  const int col = first ? c : c - d;
+  if (col >= (first ? d : F) || (first ? db2v == nullptr : db1v == nullptr)) return;
+  float s = 0.f;
+  for (int r = offset[e]; r < offset[e + 1]; ++r) {
+    float v;
+    if (first) {
+      const size_t o = (size_t)row2tok[r] * d + col;
+      v = rowgate[r] * (BF16 ? bf16_bits_to_f32(((const uint16_t*)dyv)[o]) : ((const float*)dyv)[o]);
+    } else {
+      const size_t o = (size_t)r * F + col;
+      v = BF16 ? bf16_bits_to_f32(((const uint16_t*)dAv)[o]) : ((const float*)dAv)[o];
+    }
+    s += v;
+  }
+  const size_t o = first ? (size_t)e * d + col : (size_t)e * F + col;
+  void* out = first ? db2v : db1v;
+  if (BF16) ((uint16_t*)out)[o] = (uint16_t)f32_to_bf16_bits(s);
+  else ((float*)out)[o] = s;
+}
+
+// ---------------------------------------------------------------------------
+int bwd_dgp_tiles(const Shape& s) { return s.dtype == SFFN_BF16 ? (s.F + GN - 1) / GN : 1; }
+
+int bwd_wr_parts(const Shape& s) {
+  // Enough token parts for about 1024 blocks, each part a multiple of FK tokens.
+  const int tiles = ((s.N + 127) / 128) * ((s.d + 127) / 128);
+  int parts = (1024 + tiles - 1) / tiles;
+  const int max_parts = (s.T + FK - 1) / FK;
+  if (parts > max_parts) parts = max_parts;
+  return parts < 1 ? 1 : parts;
+}
+
+hipError_t launch_backward(const Shape& s, const Inputs& in, const BwdState& b, hipStream_t st,
+                           void* const* ev) {
+  int stage = 0;
+  auto mark = [&]() -> hipError_t {
+    if (!ev) return hipSuccess;
+    return hipEventRecord((hipEvent_t)ev[stage++], st);
+  };
+  hipError_t err;
+#define SFFN_CHECK(x)                      \
+  do {                                     \
+    if ((err = (x)) != hipSuccess) return err; \
+  } while (0)
+  const bool bf16 = s.dtype == SFFN_BF16;
+  const int n_rows = s.max_rows;  // rows beyond offset[N] are never read
+
+  // 1. router logits, staged (fp32)
+  SFFN_CHECK(mark());
+  Shape sr = s;
+  sr.stage_logits = 1;
+  Workspace wr{};
+  wr.logits = b.dz;
+  wr.planes = b.planes;
+  SFFN_CHECK(launch_router_logits(sr, in, wr, st));
+
+  // 2. E1: dA and partial dg
+  SFFN_CHECK(mark());
+  const int mt_max = (s.C + GM - 1) / GM;
+  if (s.C > 0) {
+    if (bf16) {
+      BwdGemmArgs g{(const uint16_t*)b.dy, (const uint16_t*)in.W2, b.offset, b.row2tok, b.rowgate,
+                    (const uint16_t*)b.H, b.dA, b.dgp, s.T, s.d, s.F, s.max_rows, mt_max};
+      const int blocks = s.N * mt_max * ((s.F + GN - 1) / GN);
+      hipLaunchKernelGGL(bwd_gemm_kernel<1>, dim3((unsigned)blocks), dim3(256), 0, st, g);
+    } else {
+      hipLaunchKernelGGL(bwd_e1_f32_kernel, dim3((unsigned)((n_rows + 255) / 256)), dim3(256), 0,
+                         st, (const float*)b.dy, (const float*)in.W2, b.offset, b.row2tok,
+                         b.rowgate, (const float*)b.H, n_rows, s.N, s.d, s.F, (float*)b.dA, b.dgp);
+    }
+    SFFN_CHECK(hipGetLastError());
+  }
+
+  // 3. router gradient dz (over the logits)
+  SFFN_CHECK(mark());
+  {
+    const dim3 grid((unsigned)((s.T + 3) / 4));
+    if (bf16)
+      hipLaunchKernelGGL(bwd_router_grad_kernel<true>, grid, dim3(256), 0, st, b.dz, b.expert_idx,
+                         b.slot, b.offset, b.hist, b.dgp, b.n_dgp, s.max_rows, b.dy, in.b2, s.T,
+                         s.d, s.N, b.d_aux);
+    else
+      hipLaunchKernelGGL(bwd_router_grad_kernel<false>, grid, dim3(256), 0, st, b.dz, b.expert_idx,
+                         b.slot, b.offset, b.hist, b.dgp, b.n_dgp, s.max_rows, b.dy, in.b2, s.T,
+                         s.d, s.N, b.d_aux);
+    SFFN_CHECK(hipGetLastError());
+  }
+
+  // 4. E2: expert part of dx
+  SFFN_CHECK(mark());
+  if (s.C > 0) {
+    if (bf16) {
+      BwdGemmArgs g{(const uint16_t*)b.dA, (const uint16_t*)in.W1, b.offset, b.row2tok, b.rowgate,
+                    nullptr, b.dxe, nullptr, s.T, s.d, s.F, s.max_rows, mt_max};
+      const int blocks = s.N * mt_max * ((s.d + GN - 1) / GN);
+      hipLaunchKernelGGL(bwd_gemm_kernel<2>, dim3((unsigned)blocks), dim3(256), 0, st, g);
+    } else {
+      const long n = (long)n_rows * s.d;
+      hipLaunchKernelGGL(bwd_e2_f32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                         (const float*)b.dA, (const float*)in.W1, b.offset, b.row2tok, n_rows,
+                         s.N, s.d, s.F, b.dxe);
+    }
+    SFFN_CHECK(hipGetLastError());
+  }
+
+  // 5. dx = dy + dXe + dz Wr
+  SFFN_CHECK(mark());
+  {
+    const int blocks = ((s.T + 127) / 128) * ((s.d + 127) / 128);
+    if (bf16)
+      hipLaunchKernelGGL((bwd_router_gemm_kernel<false, true>), dim3((unsigned)blocks), dim3(256),
+                         0, st, b.dz, in.Wr, in.x, b.dy, b.dxe, b.slot, s.T, s.d, s.N, 0, b.dx);
+    else
+      hipLaunchKernelGGL((bwd_router_gemm_kernel<false, false>), dim3((unsigned)blocks), dim3(256),
+                         0, st, b.dz, in.Wr, in.x, b.dy, b.dxe, b.slot, s.T, s.d, s.N, 0, b.dx);
+    SFFN_CHECK(hipGetLastError());
+  }
+
+  // 6. dWr = dz^T x, split over token parts, then summed in part order
+  SFFN_CHECK(mark());
+  {
+    const int parts = b.n_wr_parts;
+    const int per = ((s.T + parts - 1) / parts + FK - 1) / FK * FK;
+    const int blocks = parts * ((s.N + 127) / 128) * ((s.d + 127) / 128);
+    if (bf16)
+      hipLaunchKernelGGL((bwd_router_gemm_kernel<true, true>), dim3((unsigned)blocks), dim3(256),
+                         0, st, b.dz, in.Wr, in.x, b.dy, b.dxe, b.slot, s.T, s.d, s.N, per, b.wrp);
+    else
+      hipLaunchKernelGGL((bwd_router_gemm_kernel<true, false>), dim3((unsigned)blocks), dim3(256),
+                         0, st, b.dz, in.Wr, in.x, b.dy, b.dxe, b.slot, s.T, s.d, s.N, per, b.wrp);
+    SFFN_CHECK(hipGetLastError());
+    const long n = (long)s.N * s.d;
+    hipLaunchKernelGGL(bwd_wr_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                       b.wrp, parts, n, b.dWr);
+    SFFN_CHECK(hipGetLastError());
+  }
+
+  // 7. E3 and E4: dW2, dW1 (every expert; zero where no rows)
+  SFFN_CHECK(mark());
+  if (bf16) {
+    BwdGemmArgs g3{(const uint16_t*)b.dy, (const uint16_t*)b.H, b.offset, b.row2tok, b.rowgate,
+                   nullptr, b.dW2, nullptr, s.T, s.d, s.F, s.max_rows, 0};
+    const int t3 = ((s.d + GM - 1) / GM) * ((s.F + GN - 1) / GN);
+    hipLaunchKernelGGL(bwd_gemm_kernel<3>, dim3((unsigned)(s.N * t3)), dim3(256), 0, st, g3);
+    SFFN_CHECK(hipGetLastError());
+    BwdGemmArgs g4{(const uint16_t*)b.dA, (const uint16_t*)in.x, b.offset, b.row2tok, b.rowgate,
+                   nullptr, b.dW1, nullptr, s.T, s.d, s.F, s.max_rows, 0};
+    const int t4 = ((s.F + GM - 1) / GM) * ((s.d + GN - 1) / GN);
+    hipLaunchKernelGGL(bwd_gemm_kernel<4>, dim3((unsigned)(s.N * t4)), dim3(256), 0, st, g4);
+  } else {
+    const long n = (long)s.d * s.F;
+    const dim3 grid((unsigned)((n + 255) / 256), (unsigned)s.N);
+    hipLaunchKernelGGL(bwd_wgrad_f32_kernel<false>, grid, dim3(256), 0, st, (const float*)b.dy,
+                       (const float*)b.H, b.offset, b.row2tok, b.rowgate, s.d, s.F, (float*)b.dW2);
+    SFFN_CHECK(hipGetLastError());
+    hipLaunchKernelGGL(bwd_wgrad_f32_kernel<true>, grid, dim3(256), 0, st, (const float*)b.dA,
+                       (const float*)in.x, b.offset, b.row2tok, b.rowgate, s.d, s.F,
+                       (float*)b.dW1);
+  }
+  SFFN_CHECK(hipGetLastError());
+
+  // 8. bias gradients
+  SFFN_CHECK(mark());
+  if (b.db1 || b.db2) {
+    const dim3 grid((unsigned)((s.d + s.F + 255) / 256), (unsigned)s.N);
+    if (bf16)
+      hipLaunchKernelGGL(bwd_bias_kernel<true>, grid, dim3(256), 0, st, b.dy, b.dA, b.offset,
+                         b.row2tok, b.rowgate, s.d, s.F, b.db1, b.db2);
+    else
+      hipLaunchKernelGGL(bwd_bias_kernel<false>, grid, dim3(256), 0, st, b.dy, b.dA, b.offset,
+                         b.row2tok, b.rowgate, s.d, s.F, b.db1, b.db2);
+    SFFN_CHECK(hipGetLastError());
+  }
+  SFFN_CHECK(mark());
+#undef SFFN_CHECK
+  return hipSuccess;
+}
+
+}  // namespace sffn

@@ -611,13 +611,13 @@ static bool logits_fit_offsets(const Shape& s) {
 static bool router_is_tiled(const Shape& s) {
   return s.dtype == SFFN_BF16 && s.N % 4 == 0 && logits_fit_offsets(s) &&
          tiled_planes_bytes(s) < ((size_t)1 << 31) - ((size_t)8 << 20) &&
-         (two_choices(s) || s.N > 128 || (s.N > 64 && s.T >= 256 * 128));
+         (staged_router(s) || s.N > 128 || (s.N > 64 && s.T >= 256 * 128));
 }
 
 // Top-2 routing and rerouting always stage the logits (the fused epilogue is
 // top-1 only).
 bool router_is_fused(const Shape& s) {
-  return s.dtype == SFFN_BF16 && !two_choices(s) && s.N <= 128 && !router_is_tiled(s);
+  return s.dtype == SFFN_BF16 && !staged_router(s) && s.N <= 128 && !router_is_tiled(s);
 }
 
 hipError_t launch_router_logits(const Shape& s, const Inputs& in, const Workspace& ws,

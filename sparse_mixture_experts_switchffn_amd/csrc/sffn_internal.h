@@ -17,6 +17,7 @@ struct Shape {
   int k;                // experts per token (1: Switch routing, 2: top-2)
   int reroute;          // k = 1 with overflow tokens rerouted to their second choice
   int glu;              // GEGLU experts: W1 [N, 2F, d], b1 [N, 2F]
+  int stage_logits;     // the router writes its fp32 logits to the workspace (backward)
   int dtype;            // SFFN_FP32 / SFFN_BF16
   int n_route_blocks;   // ceil(T / kRouteTokens)
   int max_rows;         // min(k*T, N*C): rows the expert buffers can hold
@@ -24,6 +25,8 @@ struct Shape {
 
 // The router ranks two experts per token (top-2 routing, or rerouting).
 inline bool two_choices(const Shape& s) { return s.k == 2 || s.reroute != 0; }
+// The logits go through the workspace (no fused router).
+inline bool staged_router(const Shape& s) { return two_choices(s) || s.stage_logits != 0; }
 
 struct Workspace {
   float* logits;   // [T, N] fp32 router logits
@@ -94,5 +97,43 @@ hipError_t launch_ffn2(const Shape& s, const Inputs& in, const Workspace& ws, co
 // k = 2: y_t = x_t (or 0) + the gate-scaled expert rows of t's accepted choices.
 hipError_t launch_combine(const Shape& s, const Inputs& in, const Workspace& ws,
                           const Outputs& out, bool no_residual, hipStream_t st);
+
+// Backward pass (top-1, ReLU experts): the forward's dispatch state, the
+// backward's own scratch, and the gradients.
+struct BwdState {
+  // from the forward
+  const int32_t* expert_idx;  // [T]
+  const int32_t* slot;        // [T]
+  const int* offset;          // [N+1]
+  const int* row2tok;         // [max_rows]
+  const float* rowgate;       // [max_rows]
+  const int* hist;            // [N] top-1 counts
+  const void* H;              // [max_rows, F] hidden activations (dtype)
+  // upstream gradients
+  const void* dy;             // [T, d] (dtype)
+  float d_aux;
+  // scratch
+  float* dz;                  // [T, N]: logits, then dz
+  uint16_t* planes;           // router planes of the staged logits
+  void* dA;                   // [max_rows, F] (dtype)
+  float* dgp;                 // [n_dgp, max_rows] partial dg per column tile of F
+  int n_dgp;
+  float* dxe;                 // [T, d] expert part of dx (accepted tokens)
+  float* wrp;                 // [n_wr_parts, N, d] partial dWr
+  int n_wr_parts;
+  // gradients
+  void* dx;                   // [T, d] (dtype)
+  float* dWr;                 // [N, d]
+  void* dW1;                  // [N, F, d] (dtype)
+  void* db1;                  // [N, F] (dtype), nullable
+  void* dW2;                  // [N, d, F] (dtype)
+  void* db2;                  // [N, d] (dtype), nullable
+};
+// Column tiles of F in the backward's first expert GEMM (partial dg rows).
+int bwd_dgp_tiles(const Shape& s);
+// Token parts of the split router-weight gradient.
+int bwd_wr_parts(const Shape& s);
+hipError_t launch_backward(const Shape& s, const Inputs& in, const BwdState& b, hipStream_t st,
+                           void* const* stage_events);
 
 }  // namespace sffn
