@@ -465,7 +465,7 @@ def main():
     parts = None
     if BWD:
         tiles = ((N + 127) // 128) * ((w.d + 127) // 128)
-        parts = max(1, min((1024 + tiles - 1) // tiles, (T + 31) // 32))
+        parts = max(1, min((1024 + tiles - 1) // tiles, (T + 127) // 128))
 
     def stage_bytes(name):
         if name.startswith("bwd_"):

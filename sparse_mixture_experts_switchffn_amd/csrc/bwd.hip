@@ -35,8 +35,8 @@ namespace sffn {
 // in memory (the weights of E1/E2 are [k][n]; E3/E4 contract over the
 // expert's rows); a thread loads two consecutive k rows of one 8-element
 // chunk and writes the eight (k, k+1) pairs as 32-bit words into their
-// columns, which transposes the tile on its way into LDS.  Double-buffered:
-// the next step's loads are in flight during this step's matrix ops.
+// columns, which transposes the tile on its way into LDS.  The loads of the
+// next PD steps are in flight in registers; LDS is double-buffered.
 //
 //   E1: rows x F,  K = d     A = dy[row2tok[r]]     B = W2_e [d][F]
 //   E2: rows x d,  K = F     A = dA[r]              B = W1_e [F][d]
@@ -45,6 +45,14 @@ namespace sffn {
 // ---------------------------------------------------------------------------
 constexpr int GM = 128, GN = 128, GK = 32;
 constexpr int GP = GK + 8;  // LDS row pitch in bf16 (80 bytes: fragment reads spread over banks)
+// k-steps whose loads are in flight: E1/E2 (long k-loops over d or F) and
+// E3/E4 (k-loops over one expert's rows).
+#ifndef SFFN_BWD_PD_ROWS
+#define SFFN_BWD_PD_ROWS 1
+#endif
+#ifndef SFFN_BWD_PD_WGRAD
+#define SFFN_BWD_PD_WGRAD 1
+#endif
 
 struct BwdGemmArgs {
   const uint16_t* a;
@@ -58,13 +66,18 @@ struct BwdGemmArgs {
   int T, d, F, max_rows, mt_max;
 };
 
-template <int KIND>
+template <int KIND, int PD>
 __global__ void __launch_bounds__(256)
 bwd_gemm_kernel(BwdGemmArgs g) {
   constexpr bool ROWS_M = KIND <= 2;  // M runs over the expert's rows (else K does)
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][GM][GP];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][GN][GP];
+  // [A ring | B ring]; after the k-loop the epilogue stages its tile over it.
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * GM * GP + 2 * GN * GP];
   __shared__ float red[GM];
+  uint16_t (*As)[GM][GP] = reinterpret_cast<uint16_t (*)[GM][GP]>(lds);
+  uint16_t (*Bs)[GN][GP] = reinterpret_cast<uint16_t (*)[GN][GP]>(lds + 2 * GM * GP);
+  constexpr int SP = GN + 8;  // staged tile pitch (bf16): 272-byte rows
+  static_assert(GM * SP <= 2 * GM * GP + 2 * GN * GP, "staged tile fits the rings");
+  uint16_t* const stg = lds;
 
   const int Nn = (KIND == 1 || KIND == 3) ? g.F : g.d;
   const int Mfix = KIND == 3 ? g.d : g.F;  // E3/E4
@@ -129,34 +142,36 @@ bwd_gemm_kernel(BwdGemmArgs g) {
   // E3 B and E4 A: expert row kk.
   auto tok_of = [&](int kk) -> int { return kk < Ae ? g.row2tok[rbeg + kk] : -1; };
 
-  u32x4 ra[2], rb[2];
-  float sc[2] = {1.f, 1.f};
-  // Index lookups of the k rows two steps ahead (E3/E4), so that the data
-  // loads of a step never wait for them.
-  int tk_next[2] = {-1, -1};
-  float gk_next[2] = {0.f, 0.f};
-  auto lookup = [&](int k0, int (&tk)[2], float (&gk)[2]) {
+  // Register ring of PD k-steps in flight: slot s holds the loads of the steps
+  // k with k % PD == s.  E3/E4 look their k rows' tokens (and gates) up one
+  // ring ahead, so that no data load waits for its index.
+  u32x4 ra[PD][2], rb[PD][2];
+  float sc[PD][2];
+  int tk[PD][2];
+  float gk[PD][2];
+  auto lookup = [&](int k0, int (&t)[2], float (&gt)[2]) {
     if constexpr (KIND == 3 || KIND == 4) {
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
         const int kk = k0 + 2 * kp + q;
-        tk[q] = tok_of(kk);
-        if constexpr (KIND == 3) gk[q] = kk < Ae ? g.rowgate[rbeg + kk] : 0.f;
+        t[q] = tok_of(kk);
+        gt[q] = (KIND == 3 && kk < Ae) ? g.rowgate[rbeg + kk] : 0.f;
       }
     }
   };
-  auto load = [&](int k0, const int (&tk)[2], const float (&gk)[2]) {
+  auto load = [&](int k0, u32x4 (&a)[2], u32x4 (&b)[2], float (&scale)[2], const int (&t)[2],
+                  const float (&gt)[2]) {
     if constexpr (ROWS_M) {
       const bool kin = k0 + ac * 8 < K;
 #pragma unroll
       for (int i = 0; i < 2; ++i)
-        ra[i] = buffer_load16(a_src, kin ? a_row_off[i] + (uint32_t)(k0 + ac * 8) * 2u : kOob);
+        a[i] = buffer_load16(a_src, kin ? a_row_off[i] + (uint32_t)(k0 + ac * 8) * 2u : kOob);
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
         const int kk = k0 + 2 * kp + q;
-        rb[q] = buffer_load16(b_src, (kk < K && nb_chunk < Nn)
-                                         ? ((uint32_t)kk * (uint32_t)ldB + (uint32_t)nb_chunk) * 2u
-                                         : kOob);
+        b[q] = buffer_load16(b_src, (kk < K && nb_chunk < Nn)
+                                        ? ((uint32_t)kk * (uint32_t)ldB + (uint32_t)nb_chunk) * 2u
+                                        : kOob);
       }
     } else {
 #pragma unroll
@@ -164,41 +179,42 @@ bwd_gemm_kernel(BwdGemmArgs g) {
         const int kk = k0 + 2 * kp + q;
         const bool kin = kk < Ae;
         // A: E3 gathered dy rows (scaled by the gate below), E4 expert rows of dA
-        const uint32_t arow = KIND == 3 ? (uint32_t)(tk[q] < 0 ? 0 : tk[q]) : (uint32_t)kk;
-        ra[q] = buffer_load16(a_src, (kin && ma_chunk < Mfix)
-                                         ? (arow * (uint32_t)ldA + (uint32_t)ma_chunk) * 2u
-                                         : kOob);
+        const uint32_t arow = KIND == 3 ? (uint32_t)(t[q] < 0 ? 0 : t[q]) : (uint32_t)kk;
+        a[q] = buffer_load16(a_src, (kin && ma_chunk < Mfix)
+                                        ? (arow * (uint32_t)ldA + (uint32_t)ma_chunk) * 2u
+                                        : kOob);
         // B: E3 expert rows of H, E4 gathered x rows
-        const uint32_t brow = KIND == 4 ? (uint32_t)(tk[q] < 0 ? 0 : tk[q]) : (uint32_t)kk;
-        rb[q] = buffer_load16(b_src, (kin && nb_chunk < Nn)
-                                         ? (brow * (uint32_t)ldB + (uint32_t)nb_chunk) * 2u
-                                         : kOob);
-        if constexpr (KIND == 3) sc[q] = gk[q];
+        const uint32_t brow = KIND == 4 ? (uint32_t)(t[q] < 0 ? 0 : t[q]) : (uint32_t)kk;
+        b[q] = buffer_load16(b_src, (kin && nb_chunk < Nn)
+                                        ? (brow * (uint32_t)ldB + (uint32_t)nb_chunk) * 2u
+                                        : kOob);
+        scale[q] = gt[q];
       }
     }
   };
   // Pairs (k, k+1) of the 8 inner elements of one chunk as 32-bit LDS words.
-  auto store_pairs = [&](uint16_t (*S)[GP], const u32x4 (&v)[2], int inner0, bool scale) {
+  auto store_pairs = [&](uint16_t (*S)[GP], const u32x4 (&v)[2], int inner0, bool scale,
+                         const float (&sv)[2]) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const uint32_t lo = (v[0][j >> 1] >> (16 * (j & 1))) & 0xffffu;
       const uint32_t hi = (v[1][j >> 1] >> (16 * (j & 1))) & 0xffffu;
       uint32_t w;
       if (scale)
-        w = pack_bf16x2(bf16_bits_to_f32(lo) * sc[0], bf16_bits_to_f32(hi) * sc[1]);
+        w = pack_bf16x2(bf16_bits_to_f32(lo) * sv[0], bf16_bits_to_f32(hi) * sv[1]);
       else
         w = lo | (hi << 16);
       *reinterpret_cast<uint32_t*>(&S[inner0 + j][2 * kp]) = w;
     }
   };
-  auto store = [&](int buf) {
+  auto store = [&](int buf, const u32x4 (&a)[2], const u32x4 (&b)[2], const float (&sv)[2]) {
     if constexpr (ROWS_M) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i) store16(&As[buf][(tid >> 2) + 64 * i][ac * 8], ra[i]);
+      for (int i = 0; i < 2; ++i) store16(&As[buf][(tid >> 2) + 64 * i][ac * 8], a[i]);
     } else {
-      store_pairs(As[buf], ra, pc * 8, KIND == 3);
+      store_pairs(As[buf], a, pc * 8, KIND == 3, sv);
     }
-    store_pairs(Bs[buf], rb, pc * 8, false);
+    store_pairs(Bs[buf], b, pc * 8, false, sv);
   };
 
   f32x16 acc[2][2];
@@ -225,77 +241,95 @@ bwd_gemm_kernel(BwdGemmArgs g) {
     }
   };
 
+  // Step k: its loads were issued PD steps earlier into slot k % PD; LDS
+  // buffer k % 2 receives it one step before its matrix ops.
   const int nk = (K + GK - 1) / GK;
-  int tk_cur[2] = {-1, -1};
-  float gk_cur[2] = {0.f, 0.f};
-  lookup(0, tk_cur, gk_cur);
-  lookup(GK, tk_next, gk_next);
-  load(0, tk_cur, gk_cur);
-  store(0);
+  static_for<0, PD>([&](auto j) { lookup(j * GK, tk[j], gk[j]); });
+  static_for<0, PD>([&](auto j) {
+    if (j < nk) load(j * GK, ra[j], rb[j], sc[j], tk[j], gk[j]);
+    lookup((j + PD) * GK, tk[j], gk[j]);
+  });
+  if (nk > 0) store(0, ra[0], rb[0], sc[0]);
   __syncthreads();
-  for (int ks = 0; ks < nk; ++ks) {
-    const int cur = ks & 1;
-    const bool more = ks + 1 < nk;
-    if (more) {
-      load((ks + 1) * GK, tk_next, gk_next);
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        tk_cur[q] = tk_next[q];
-        gk_cur[q] = gk_next[q];
+  for (int k0 = 0; k0 < nk; k0 += PD) {
+    static_for<0, PD>([&](auto j) {
+      constexpr int J = decltype(j)::value;
+      const int k = k0 + J;
+      if (k < nk) {  // uniform over the block
+        if (k + PD < nk) {
+          load((k + PD) * GK, ra[J], rb[J], sc[J], tk[J], gk[J]);
+          lookup((k + 2 * PD) * GK, tk[J], gk[J]);
+        }
+        compute(k & 1);
+        constexpr int N1 = (J + 1) % PD;
+        if (k + 1 < nk) store((k + 1) & 1, ra[N1], rb[N1], sc[N1]);
+        __syncthreads();
       }
-      lookup((ks + 2) * GK, tk_next, gk_next);
-    }
-    compute(cur);
-    if (more) store(cur ^ 1);
-    __syncthreads();
+    });
   }
 
   // ---- epilogues: lane holds row (l % 32) of each 32-row tile i and, for
   // value 4 gq + q, column 8 gq + 4 (l / 32) + q of each 32-column tile j ----
   const int lr = lane & 31;
+  // Tile rows/columns of this lane's values: row wm*64 + 32 i + lr, columns
+  // wn*64 + 32 j + 8 gq + 4 khalf + q.
+  // Coalesced tile transfer between LDS (pitch SP) and global rows: 16-byte
+  // chunks, 16 per 128-column row, eight per thread.
+  auto tile_io = [&](auto&& fn) {
+#pragma unroll
+    for (int c = 0; c < (GM * GN / 8) / 256; ++c) {
+      const int idx = tid + 256 * c;
+      fn(idx >> 4, (idx & 15) * 8);
+    }
+  };
   if constexpr (KIND == 1) {
-    // dA = g Q [H > 0] (bf16) and the tile's partial dg = sum_n Q H per row.
+    // H tile into LDS; then dA = g Q [H > 0] in place of it and the tile's
+    // partial dg = sum_n Q H per row; then dA out in row chunks.
     const __amdgpu_buffer_rsrc_t h_src =
         make_rsrc(g.H + (size_t)rbeg * g.F, (uint32_t)Ae * (uint32_t)g.F * 2u);
-    uint16_t* dA = reinterpret_cast<uint16_t*>(g.out);
-    const __amdgpu_buffer_rsrc_t o_src =
-        make_rsrc(dA + (size_t)rbeg * g.F, (uint32_t)Ae * (uint32_t)g.F * 2u);
+    tile_io([&](int row, int col) {
+      const int r = m0 + row, n = n0 + col;
+      store16(&stg[row * SP + col],
+              buffer_load16(h_src, (r < Ae && n < g.F) ? ((uint32_t)r * (uint32_t)g.F + (uint32_t)n) * 2u
+                                                        : kOob));
+    });
+    __syncthreads();
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int r = m0 + wm * 64 + 32 * i + lr;
-      const bool rok = r < Ae;
-      const float gate = rok ? g.rowgate[rbeg + r] : 0.f;
+      const int ml = wm * 64 + 32 * i + lr;
+      const int r = m0 + ml;
+      const float gate = r < Ae ? g.rowgate[rbeg + r] : 0.f;
       float part = 0.f;
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
 #pragma unroll
         for (int gq = 0; gq < 4; ++gq) {
-          const int n = n0 + wn * 64 + 32 * j + 8 * gq + 4 * khalf;
-          const bool ok = rok && n < g.F;
-          const uint32_t off = ok ? ((uint32_t)r * (uint32_t)g.F + (uint32_t)n) * 2u : kOob;
-          const u32x2 hv{__builtin_amdgcn_raw_buffer_load_b32(h_src, (int)off, 0, 0),
-                         __builtin_amdgcn_raw_buffer_load_b32(h_src, (int)(ok ? off + 4u : kOob), 0, 0)};
-          float h[4], da[4];
+          u32x2* p = reinterpret_cast<u32x2*>(&stg[ml * SP + wn * 64 + 32 * j + 8 * gq + 4 * khalf]);
+          const u32x2 hv = *p;
+          float da[4];
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            h[q] = bf16_bits_to_f32((hv[q >> 1] >> (16 * (q & 1))) & 0xffffu);
+            const float h = bf16_bits_to_f32((hv[q >> 1] >> (16 * (q & 1))) & 0xffffu);
             const float qv = acc[i][j][4 * gq + q];
-            part += qv * h[q];
-            da[q] = h[q] > 0.f ? gate * qv : 0.f;
+            part += qv * h;
+            da[q] = h > 0.f ? gate * qv : 0.f;
           }
-          __builtin_amdgcn_raw_buffer_store_b32(pack_bf16x2(da[0], da[1]), o_src, (int)off, 0, 0);
-          __builtin_amdgcn_raw_buffer_store_b32(pack_bf16x2(da[2], da[3]), o_src,
-                                                (int)(ok ? off + 4u : kOob), 0, 0);
+          *p = u32x2{pack_bf16x2(da[0], da[1]), pack_bf16x2(da[2], da[3])};
         }
       }
       part += __shfl_xor(part, 32);
       // the two column halves of the tile (waves wn = 0, 1) meet in LDS
-      if (wn == 1 && khalf == 0) red[wm * 64 + 32 * i + lr] = part;
+      if (wn == 1 && khalf == 0) red[ml] = part;
       __syncthreads();
-      if (wn == 0 && khalf == 0 && rok)
-        g.dgp[(size_t)nt * g.max_rows + rbeg + r] = part + red[wm * 64 + 32 * i + lr];
-      __syncthreads();
+      if (wn == 0 && khalf == 0 && r < Ae)
+        g.dgp[(size_t)nt * g.max_rows + rbeg + r] = part + red[ml];
     }
+    __syncthreads();
+    uint16_t* dA = reinterpret_cast<uint16_t*>(g.out) + (size_t)rbeg * g.F;
+    tile_io([&](int row, int col) {
+      const int r = m0 + row, n = n0 + col;
+      if (r < Ae && n < g.F) store16(dA + (size_t)r * g.F + n, load16(&stg[row * SP + col]));
+    });
   } else if constexpr (KIND == 2) {
     // expert part of dx, fp32, at the token's row
     float* dxe = reinterpret_cast<float*>(g.out);
@@ -317,27 +351,26 @@ bwd_gemm_kernel(BwdGemmArgs g) {
       }
     }
   } else {
-    // dW2_e [d][F] (E3) or dW1_e [F][d] (E4), bf16
-    uint16_t* out = reinterpret_cast<uint16_t*>(g.out) + (size_t)e * g.d * g.F;
-    const __amdgpu_buffer_rsrc_t o_src = make_rsrc(out, (uint32_t)((size_t)g.d * g.F * 2));
+    // dW2_e [d][F] (E3) or dW1_e [F][d] (E4), bf16, staged and written in row chunks
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int m = m0 + wm * 64 + 32 * i + lr;
+      const int ml = wm * 64 + 32 * i + lr;
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
 #pragma unroll
         for (int gq = 0; gq < 4; ++gq) {
-          const int n = n0 + wn * 64 + 32 * j + 8 * gq + 4 * khalf;
-          const bool ok = m < M && n < Nn;
-          const uint32_t off = ok ? ((uint32_t)m * (uint32_t)Nn + (uint32_t)n) * 2u : kOob;
           const f32x16& a = acc[i][j];
-          __builtin_amdgcn_raw_buffer_store_b32(pack_bf16x2(a[4 * gq], a[4 * gq + 1]), o_src,
-                                                (int)off, 0, 0);
-          __builtin_amdgcn_raw_buffer_store_b32(pack_bf16x2(a[4 * gq + 2], a[4 * gq + 3]), o_src,
-                                                (int)(ok ? off + 4u : kOob), 0, 0);
+          *reinterpret_cast<u32x2*>(&stg[ml * SP + wn * 64 + 32 * j + 8 * gq + 4 * khalf]) =
+              u32x2{pack_bf16x2(a[4 * gq], a[4 * gq + 1]), pack_bf16x2(a[4 * gq + 2], a[4 * gq + 3])};
         }
       }
     }
+    __syncthreads();
+    uint16_t* out = reinterpret_cast<uint16_t*>(g.out) + (size_t)e * g.d * g.F;
+    tile_io([&](int row, int col) {
+      const int m = m0 + row, n = n0 + col;
+      if (m < M && n < Nn) store16(out + (size_t)m * Nn + n, load16(&stg[row * SP + col]));
+    });
   }
 }
 
@@ -511,23 +544,22 @@ bwd_router_gemm_kernel(const float* __restrict__ dz, const float* __restrict__ W
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
 
-  for (int k0 = kbeg; k0 < kend; k0 += FK) {
-    // 32 x 128 elements per operand: 16 per thread, consecutive threads on
-    // consecutive addresses.
-#pragma unroll 4
+  // 32 x 128 elements per operand and k-step: 16 per thread (consecutive
+  // threads on consecutive addresses), all loaded into registers at once; the
+  // next step's are in flight during this step's matrix ops.
+  float pa[16], pb[16];
+  auto gload = [&](int k0) {
+#pragma unroll
     for (int q = 0; q < 16; ++q) {
       const int idx = tid + 256 * q;
       if (DWR) {
-        const int kk = idx >> 7, mm = idx & 127;  // A[k][m] = dz[k0+kk][m0+mm]
-        const int k = k0 + kk, m = m0 + mm;
-        As[kk * FPB + mm] = (k < kend && m < N) ? dz[(size_t)k * N + m] : 0.f;
+        const int k = k0 + (idx >> 7), m = m0 + (idx & 127);  // A[k][m] = dz[k][m]
+        pa[q] = (k < kend && m < N) ? dz[(size_t)k * N + m] : 0.f;
       } else {
-        const int mm = idx >> 5, kk = idx & 31;   // A[m][k] = dz[m0+mm][k0+kk]
-        const int k = k0 + kk, m = m0 + mm;
-        As[mm * FPA + kk] = (k < kend && m < T) ? dz[(size_t)m * N + k] : 0.f;
+        const int m = m0 + (idx >> 5), k = k0 + (idx & 31);   // A[m][k] = dz[m][k]
+        pa[q] = (k < kend && m < T) ? dz[(size_t)m * N + k] : 0.f;
       }
-      const int kk = idx >> 7, nn = idx & 127;
-      const int k = k0 + kk, n = n0 + nn;
+      const int k = k0 + (idx >> 7), n = n0 + (idx & 127);
       float bv = 0.f;
       if (k < kend && n < d) {
         if (DWR)
@@ -536,9 +568,23 @@ bwd_router_gemm_kernel(const float* __restrict__ dz, const float* __restrict__ W
         else
           bv = Wr[(size_t)k * d + n];
       }
-      Bs[kk * FPB + nn] = bv;
+      pb[q] = bv;
     }
+  };
+  auto sstore = [&]() {
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int idx = tid + 256 * q;
+      if (DWR) As[(idx >> 7) * FPB + (idx & 127)] = pa[q];
+      else As[(idx >> 5) * FPA + (idx & 31)] = pa[q];
+      Bs[(idx >> 7) * FPB + (idx & 127)] = pb[q];
+    }
+  };
+  if (kbeg < kend) gload(kbeg);
+  for (int k0 = kbeg; k0 < kend; k0 += FK) {
+    sstore();
     __syncthreads();
+    if (k0 + FK < kend) gload(k0 + FK);
 #pragma unroll 4
     for (int ks = 0; ks < FK; ks += 2) {
       const int kk = ks + (lane >> 5);
@@ -558,7 +604,10 @@ bwd_router_gemm_kernel(const float* __restrict__ dz, const float* __restrict__ W
     __syncthreads();
   }
 
+  // Lane values: row m0 + wm*64 + 32 i + lr, four consecutive columns per gq.
+  // With d % 4 == 0 each group moves as one vector access.
   const int lr = lane & 31, khalf = lane >> 5;
+  const bool vec = (d & 3) == 0;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int m = m0 + wm * 64 + 32 * i + lr;
@@ -567,20 +616,50 @@ bwd_router_gemm_kernel(const float* __restrict__ dz, const float* __restrict__ W
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int n = n0 + wn * 64 + 32 * j + 8 * (v >> 2) + 4 * khalf + (v & 3);
+      for (int gq = 0; gq < 4; ++gq) {
+        const int n = n0 + wn * 64 + 32 * j + 8 * gq + 4 * khalf;
         if (n >= d) continue;
         const size_t o = (size_t)m * d + n;
-        if (DWR) {
-          ((float*)outv)[(size_t)part * N * d + o] = acc[i][j][v];
-        } else {
-          float val = acc[i][j][v] + (accepted ? dxe[o] : 0.f);
+        float v[4] = {acc[i][j][4 * gq], acc[i][j][4 * gq + 1], acc[i][j][4 * gq + 2],
+                      acc[i][j][4 * gq + 3]};
+        if (vec) {
+          if (DWR) {
+            *reinterpret_cast<f32x4*>((float*)outv + (size_t)part * N * d + o) =
+                f32x4{v[0], v[1], v[2], v[3]};
+            continue;
+          }
+          if (accepted) {
+            const f32x4 xe = *reinterpret_cast<const f32x4*>(dxe + o);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) v[q] += xe[q];
+          }
           if (BF16) {
-            val += bf16_bits_to_f32(((const uint16_t*)dyv)[o]);
-            ((uint16_t*)outv)[o] = (uint16_t)f32_to_bf16_bits(val);
+            const u32x2 yb = *reinterpret_cast<const u32x2*>((const uint16_t*)dyv + o);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) v[q] += bf16_bits_to_f32((yb[q >> 1] >> (16 * (q & 1))) & 0xffffu);
+            *reinterpret_cast<u32x2*>((uint16_t*)outv + o) =
+                u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
           } else {
-            val += ((const float*)dyv)[o];
-            ((float*)outv)[o] = val;
+            const f32x4 yf = *reinterpret_cast<const f32x4*>((const float*)dyv + o);
+            *reinterpret_cast<f32x4*>((float*)outv + o) =
+                f32x4{v[0] + yf[0], v[1] + yf[1], v[2] + yf[2], v[3] + yf[3]};
+          }
+          continue;
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (n + q >= d) break;
+          if (DWR) {
+            ((float*)outv)[(size_t)part * N * d + o + q] = v[q];
+          } else {
+            float val = v[q] + (accepted ? dxe[o + q] : 0.f);
+            if (BF16) {
+              val += bf16_bits_to_f32(((const uint16_t*)dyv)[o + q]);
+              ((uint16_t*)outv)[o + q] = (uint16_t)f32_to_bf16_bits(val);
+            } else {
+              val += ((const float*)dyv)[o + q];
+              ((float*)outv)[o + q] = val;
+            }
           }
         }
       }
@@ -635,10 +714,10 @@ bwd_bias_kernel(const void* __restrict__ dyv, const void* __restrict__ dAv,
 int bwd_dgp_tiles(const Shape& s) { return s.dtype == SFFN_BF16 ? (s.F + GN - 1) / GN : 1; }
 
 int bwd_wr_parts(const Shape& s) {
-  // Enough token parts for about 1024 blocks, each part a multiple of FK tokens.
+  // Enough token parts for about 1024 blocks, each part at least 128 tokens.
   const int tiles = ((s.N + 127) / 128) * ((s.d + 127) / 128);
   int parts = (1024 + tiles - 1) / tiles;
-  const int max_parts = (s.T + FK - 1) / FK;
+  const int max_parts = (s.T + 127) / 128;
   if (parts > max_parts) parts = max_parts;
   return parts < 1 ? 1 : parts;
 }
@@ -675,7 +754,8 @@ hipError_t launch_backward(const Shape& s, const Inputs& in, const BwdState& b, 
       BwdGemmArgs g{(const uint16_t*)b.dy, (const uint16_t*)in.W2, b.offset, b.row2tok, b.rowgate,
                     (const uint16_t*)b.H, b.dA, b.dgp, s.T, s.d, s.F, s.max_rows, mt_max};
       const int blocks = s.N * mt_max * ((s.F + GN - 1) / GN);
-      hipLaunchKernelGGL(bwd_gemm_kernel<1>, dim3((unsigned)blocks), dim3(256), 0, st, g);
+      hipLaunchKernelGGL((bwd_gemm_kernel<1, SFFN_BWD_PD_ROWS>), dim3((unsigned)blocks), dim3(256),
+                         0, st, g);
     } else {
       hipLaunchKernelGGL(bwd_e1_f32_kernel, dim3((unsigned)((n_rows + 255) / 256)), dim3(256), 0,
                          st, (const float*)b.dy, (const float*)in.W2, b.offset, b.row2tok,
@@ -706,7 +786,8 @@ hipError_t launch_backward(const Shape& s, const Inputs& in, const BwdState& b, 
       BwdGemmArgs g{(const uint16_t*)b.dA, (const uint16_t*)in.W1, b.offset, b.row2tok, b.rowgate,
                     nullptr, b.dxe, nullptr, s.T, s.d, s.F, s.max_rows, mt_max};
       const int blocks = s.N * mt_max * ((s.d + GN - 1) / GN);
-      hipLaunchKernelGGL(bwd_gemm_kernel<2>, dim3((unsigned)blocks), dim3(256), 0, st, g);
+      hipLaunchKernelGGL((bwd_gemm_kernel<2, SFFN_BWD_PD_ROWS>), dim3((unsigned)blocks), dim3(256),
+                         0, st, g);
     } else {
       const long n = (long)n_rows * s.d;
       hipLaunchKernelGGL(bwd_e2_f32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
@@ -754,12 +835,14 @@ hipError_t launch_backward(const Shape& s, const Inputs& in, const BwdState& b, 
     BwdGemmArgs g3{(const uint16_t*)b.dy, (const uint16_t*)b.H, b.offset, b.row2tok, b.rowgate,
                    nullptr, b.dW2, nullptr, s.T, s.d, s.F, s.max_rows, 0};
     const int t3 = ((s.d + GM - 1) / GM) * ((s.F + GN - 1) / GN);
-    hipLaunchKernelGGL(bwd_gemm_kernel<3>, dim3((unsigned)(s.N * t3)), dim3(256), 0, st, g3);
+    hipLaunchKernelGGL((bwd_gemm_kernel<3, SFFN_BWD_PD_WGRAD>), dim3((unsigned)(s.N * t3)),
+                       dim3(256), 0, st, g3);
     SFFN_CHECK(hipGetLastError());
     BwdGemmArgs g4{(const uint16_t*)b.dA, (const uint16_t*)in.x, b.offset, b.row2tok, b.rowgate,
                    nullptr, b.dW1, nullptr, s.T, s.d, s.F, s.max_rows, 0};
     const int t4 = ((s.F + GM - 1) / GM) * ((s.d + GN - 1) / GN);
-    hipLaunchKernelGGL(bwd_gemm_kernel<4>, dim3((unsigned)(s.N * t4)), dim3(256), 0, st, g4);
+    hipLaunchKernelGGL((bwd_gemm_kernel<4, SFFN_BWD_PD_WGRAD>), dim3((unsigned)(s.N * t4)),
+                       dim3(256), 0, st, g4);
   } else {
     const long n = (long)s.d * s.F;
     const dim3 grid((unsigned)((n + 255) / 256), (unsigned)s.N);
