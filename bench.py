@@ -17,7 +17,9 @@ inputs already resident in HBM.  Prints ONE JSON line:
   cpu_baseline the CPU oracle (float64 numpy) timed on this host on a bounded
               sample of the same workload
 Default workload: Switch-Base-like (T=8192 tokens, d_model 768, d_ff 3072, 64
-experts, CF 1.25, bf16 experts, fp32 router).
+experts, CF 1.25, bf16 experts, fp32 router).  Variants of the step: --topk 2 (top-2
+routing), --reroute (No-Token-Left-Behind), --geglu (GEGLU experts), --backward (a
+training step: forward then backward; metric "SwitchFFN fwd+bwd tokens/s").
 """
 from __future__ import annotations
 
