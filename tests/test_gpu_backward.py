@@ -116,6 +116,15 @@ def test_backward_bf16(case):
     _case(synth.workload("switch_base").replace(**case), twice=True)
 
 
+@pytest.mark.parametrize("case", [
+    dict(T=1, d=64, F=128, N=4, CF=4.0, bias_sigma=0.02),      # one token
+    dict(T=256, d=64, F=96, N=1, CF=1.0, bias_sigma=0.02),     # N = 1: dense FFN, dz = 0
+    dict(T=130, d=40, F=200, N=3, CF=1.0),                     # K tails of every GEMM
+])
+def test_backward_edges(case):
+    _case(synth.workload("switch_base").replace(**case), twice=True)
+
+
 def test_backward_capacity_zero():
     """C = 0: every token dropped; dx = dy + Wr^T dz from the aux term; dW = 0."""
     _case(synth.workload("switch_base").replace(T=200, d=32, F=64, N=5, CF=0.0, bias_sigma=0.02),

@@ -62,6 +62,12 @@ def test_geglu_fp32_shapes(case):
     assert err <= 1e-6
 
 
+def test_geglu_single_token_and_one_expert():
+    _case(synth.workload("switch_base").replace(glu=True, T=1, d=64, F=128, N=4, CF=4.0))
+    _case(synth.workload("switch_base").replace(glu=True, T=300, d=64, F=72, N=1, CF=1.0,
+                                                bias_sigma=0.05))
+
+
 def test_geglu_top2():
     _case(synth.workload("switch_base").replace(glu=True, T=700, d=96, F=160, N=8, CF=1.0,
                                                 bias_sigma=0.02), k=2)

@@ -97,6 +97,13 @@ def test_reroute_bf16_shapes(case):
     _case(synth.workload("switch_base").replace(**case))
 
 
+def test_reroute_single_token():
+    """T = 1: C = 0 at CF = 1 with four experts (both stages refuse it); with CF = 4 the
+    token is accepted by its first choice."""
+    _case(synth.workload("switch_base").replace(T=1, d=64, F=128, N=4, CF=1.0), want_rerouted=False)
+    _case(synth.workload("switch_base").replace(T=1, d=64, F=128, N=4, CF=4.0), want_rerouted=False)
+
+
 def test_reroute_capacity_zero():
     """C = 0: both stages refuse every token; y = x bit-exact."""
     _case(synth.workload("switch_base").replace(T=200, d=32, F=64, N=5, CF=0.0),
