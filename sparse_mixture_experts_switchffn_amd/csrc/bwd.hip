@@ -29,14 +29,17 @@ namespace sffn {
 // Block tile 128 x 128, k-steps of 32, four waves of 64 x 64 (2 x 2 MFMA
 // tiles of 32 x 32).  Both operands sit in LDS as [outer][k] rows (k
 // contiguous, 80-byte pitch), which is what a v_mfma_f32_32x32x16_bf16
-// operand fragment reads (8 consecutive k of one row per lane, one 16-byte
-// LDS read).  An operand that is k-contiguous in memory (E1 and E2's row
-// operand) is copied in 16-byte chunks.  The others hold k as their row index
-// in memory (the weights of E1/E2 are [k][n]; E3/E4 contract over the
-// expert's rows); a thread loads two consecutive k rows of one 8-element
-// chunk and writes the eight (k, k+1) pairs as 32-bit words into their
-// columns, which transposes the tile on its way into LDS.  The loads of the
-// next PD steps are in flight in registers; LDS is double-buffered.
+// operand fragment reads (8 consecutive k of one row per lane).  An operand
+// that is k-contiguous in memory (E1 and E2's row operand) sits in LDS as
+// [outer][k] rows (80-byte pitch) and a fragment is one 16-byte read.  The
+// others hold k as their row index in memory (the weights of E1/E2 are
+// [k][n]; E3/E4 contract over the expert's rows): they are copied into LDS as
+// they are, [k][inner] rows of 320 bytes, and a fragment is two transposing
+// reads (ds_read_b64_tr_b16: within each 16-lane group, lane i receives
+// element i % 4 of the 8-byte chunks that lanes i/4 + 4c address, c = 0..3,
+// so lanes addressing rows k..k+3 at columns 4 (j % 4) give each lane four
+// consecutive k of one column).  The loads of the next PD steps are in flight
+// in registers; LDS is double-buffered.
 //
 //   E1: rows x F,  K = d     A = dy[row2tok[r]]     B = W2_e [d][F]
 //   E2: rows x d,  K = F     A = dA[r]              B = W1_e [F][d]
@@ -45,6 +48,21 @@ namespace sffn {
 // ---------------------------------------------------------------------------
 constexpr int GM = 128, GN = 128, GK = 32;
 constexpr int GP = GK + 8;  // LDS row pitch in bf16 (80 bytes: fragment reads spread over banks)
+constexpr int RP = 160;     // [k][inner] LDS row pitch in bf16 (320 bytes), same tile size
+static_assert(GK * RP == GM * GP, "both LDS forms of an operand tile take the same space");
+
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+// Operand fragment (8 consecutive k of inner index mbase + lane % 32, from k0 +
+// 8 (lane / 32)) of a [k][inner] LDS tile, by two transposing reads.
+__device__ __forceinline__ bf16x8 tr_fragment(const uint16_t* S, int k0, int mbase, int lane) {
+  const int g = lane >> 4, j = lane & 15;
+  const uint16_t* p = S + (k0 + 8 * (g >> 1) + (j >> 2)) * RP + mbase + 16 * (g & 1) + 4 * (j & 3);
+  const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p);
+  const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p + 4 * RP));
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
 // k-steps whose loads are in flight: E1/E2 (long k-loops over d or F) and
 // E3/E4 (k-loops over one expert's rows).
 #ifndef SFFN_BWD_PD_ROWS
@@ -105,9 +123,9 @@ bwd_gemm_kernel(BwdGemmArgs g) {
   const int ac = tid & 3;
   uint32_t a_row_off[2];
   __amdgpu_buffer_rsrc_t a_src;
-  // k as the row index (E3, E4) and every B: thread k rows 2*(tid%16) + {0,1},
-  // chunk tid/16 of the 128-wide inner range.
-  const int kp = tid & 15, pc = tid >> 4;
+  // k as the row index (E3, E4) and every B: thread k rows tid/16 + {0, 16},
+  // chunk tid%16 of the 128-wide inner range.
+  const int kr = tid >> 4, pc = tid & 15;
   __amdgpu_buffer_rsrc_t b_src;
   if constexpr (KIND == 1) {
     a_src = make_rsrc(g.a, (uint32_t)g.T * (uint32_t)g.d * 2u);
@@ -153,7 +171,7 @@ bwd_gemm_kernel(BwdGemmArgs g) {
     if constexpr (KIND == 3 || KIND == 4) {
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
-        const int kk = k0 + 2 * kp + q;
+        const int kk = k0 + kr + 16 * q;
         t[q] = tok_of(kk);
         gt[q] = (KIND == 3 && kk < Ae) ? g.rowgate[rbeg + kk] : 0.f;
       }
@@ -168,7 +186,7 @@ bwd_gemm_kernel(BwdGemmArgs g) {
         a[i] = buffer_load16(a_src, kin ? a_row_off[i] + (uint32_t)(k0 + ac * 8) * 2u : kOob);
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
-        const int kk = k0 + 2 * kp + q;
+        const int kk = k0 + kr + 16 * q;
         b[q] = buffer_load16(b_src, (kk < K && nb_chunk < Nn)
                                         ? ((uint32_t)kk * (uint32_t)ldB + (uint32_t)nb_chunk) * 2u
                                         : kOob);
@@ -176,7 +194,7 @@ bwd_gemm_kernel(BwdGemmArgs g) {
     } else {
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
-        const int kk = k0 + 2 * kp + q;
+        const int kk = k0 + kr + 16 * q;
         const bool kin = kk < Ae;
         // A: E3 gathered dy rows (scaled by the gate below), E4 expert rows of dA
         const uint32_t arow = KIND == 3 ? (uint32_t)(t[q] < 0 ? 0 : t[q]) : (uint32_t)kk;
@@ -192,19 +210,22 @@ bwd_gemm_kernel(BwdGemmArgs g) {
       }
     }
   };
-  // Pairs (k, k+1) of the 8 inner elements of one chunk as 32-bit LDS words.
-  auto store_pairs = [&](uint16_t (*S)[GP], const u32x4 (&v)[2], int inner0, bool scale,
-                         const float (&sv)[2]) {
+  // [k][inner] tiles: a thread's two chunks go to their rows as they are (E3's
+  // A scaled by the row's gate, rounded once more to bf16).
+  auto raw_tile = [&](int buf, bool a_side) -> uint16_t* {
+    return a_side ? &As[buf][0][0] : &Bs[buf][0][0];
+  };
+  auto store_raw = [&](uint16_t* S, const u32x4 (&v)[2], bool scale, const float (&sv)[2]) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t lo = (v[0][j >> 1] >> (16 * (j & 1))) & 0xffffu;
-      const uint32_t hi = (v[1][j >> 1] >> (16 * (j & 1))) & 0xffffu;
-      uint32_t w;
-      if (scale)
-        w = pack_bf16x2(bf16_bits_to_f32(lo) * sv[0], bf16_bits_to_f32(hi) * sv[1]);
-      else
-        w = lo | (hi << 16);
-      *reinterpret_cast<uint32_t*>(&S[inner0 + j][2 * kp]) = w;
+    for (int q = 0; q < 2; ++q) {
+      u32x4 w = v[q];
+      if (scale) {
+#pragma unroll
+        for (int h = 0; h < 4; ++h)
+          w[h] = pack_bf16x2(bf16_bits_to_f32(v[q][h] & 0xffffu) * sv[q],
+                             bf16_bits_to_f32(v[q][h] >> 16) * sv[q]);
+      }
+      store16(S + (kr + 16 * q) * RP + pc * 8, w);
     }
   };
   auto store = [&](int buf, const u32x4 (&a)[2], const u32x4 (&b)[2], const float (&sv)[2]) {
@@ -212,9 +233,9 @@ bwd_gemm_kernel(BwdGemmArgs g) {
 #pragma unroll
       for (int i = 0; i < 2; ++i) store16(&As[buf][(tid >> 2) + 64 * i][ac * 8], a[i]);
     } else {
-      store_pairs(As[buf], a, pc * 8, KIND == 3, sv);
+      store_raw(raw_tile(buf, true), a, KIND == 3, sv);
     }
-    store_pairs(Bs[buf], b, pc * 8, false, sv);
+    store_raw(raw_tile(buf, false), b, false, sv);
   };
 
   f32x16 acc[2][2];
@@ -229,11 +250,14 @@ bwd_gemm_kernel(BwdGemmArgs g) {
     for (int kh = 0; kh < 2; ++kh) {
       bf16x8 fa[2], fb[2];
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        fa[i] = as_bf16x8(load16(&As[buf][wm * 64 + 32 * i + (lane & 31)][kh * 16 + khalf * 8]));
+      for (int i = 0; i < 2; ++i) {
+        if constexpr (ROWS_M)
+          fa[i] = as_bf16x8(load16(&As[buf][wm * 64 + 32 * i + (lane & 31)][kh * 16 + khalf * 8]));
+        else
+          fa[i] = tr_fragment(raw_tile(buf, true), kh * 16, wm * 64 + 32 * i, lane);
+      }
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        fb[j] = as_bf16x8(load16(&Bs[buf][wn * 64 + 32 * j + (lane & 31)][kh * 16 + khalf * 8]));
+      for (int j = 0; j < 2; ++j) fb[j] = tr_fragment(raw_tile(buf, false), kh * 16, wn * 64 + 32 * j, lane);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
