@@ -571,37 +571,64 @@ bwd_router_gemm_kernel(const float* __restrict__ dz, const float* __restrict__ W
   // 32 x 128 elements per operand and k-step: 16 per thread (consecutive
   // threads on consecutive addresses), all loaded into registers at once; the
   // next step's are in flight during this step's matrix ops.
+  // Both operands move in chunks of 4 consecutive elements along their
+  // contiguous axis (16-byte loads when the whole chunk is in range and aligned,
+  // else element by element), 4 chunks per thread and operand; the element at
+  // chunk position e of chunk q is tile element 4 (tid + 256 q) + e in the
+  // operand's row-major tile order.
+  //   DWR: A [32 k][128 m] from dz rows (m contiguous), B [32 k][128 n] from x.
+  //   DX:  A [128 m][32 k] from dz rows (k contiguous), B [32 k][128 n] from Wr.
   float pa[16], pb[16];
+  const bool a_vec = (N & 3) == 0;
+  const bool b_vec = (d & 3) == 0;
+  auto load4 = [&](const float* row, int j, int lim, bool vec, float* out4) {
+    if (vec && j + 3 < lim) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(row + j);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) out4[e] = v[e];
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) out4[e] = j + e < lim ? row[j + e] : 0.f;
+    }
+  };
   auto gload = [&](int k0) {
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int idx = tid + 256 * q;
+    for (int q = 0; q < 4; ++q) {
+      const int c = tid + 256 * q;
       if (DWR) {
-        const int k = k0 + (idx >> 7), m = m0 + (idx & 127);  // A[k][m] = dz[k][m]
-        pa[q] = (k < kend && m < N) ? dz[(size_t)k * N + m] : 0.f;
+        const int k = k0 + (c >> 5), m = m0 + 4 * (c & 31);
+        if (k < kend) load4(dz + (size_t)k * N, m, N, a_vec, &pa[4 * q]);
+        else for (int e = 0; e < 4; ++e) pa[4 * q + e] = 0.f;
       } else {
-        const int m = m0 + (idx >> 5), k = k0 + (idx & 31);   // A[m][k] = dz[m][k]
-        pa[q] = (k < kend && m < T) ? dz[(size_t)m * N + k] : 0.f;
+        const int m = m0 + (c >> 3), k = k0 + 4 * (c & 7);
+        if (m < T) load4(dz + (size_t)m * N, k, kend, a_vec, &pa[4 * q]);
+        else for (int e = 0; e < 4; ++e) pa[4 * q + e] = 0.f;
       }
-      const int k = k0 + (idx >> 7), n = n0 + (idx & 127);
-      float bv = 0.f;
-      if (k < kend && n < d) {
-        if (DWR)
-          bv = BF16 ? bf16_bits_to_f32(((const uint16_t*)xv)[(size_t)k * d + n])
-                    : ((const float*)xv)[(size_t)k * d + n];
-        else
-          bv = Wr[(size_t)k * d + n];
+      const int k = k0 + (c >> 5), n = n0 + 4 * (c & 31);
+      if (k >= kend) {
+        for (int e = 0; e < 4; ++e) pb[4 * q + e] = 0.f;
+      } else if (!DWR) {
+        load4(Wr + (size_t)k * d, n, d, b_vec, &pb[4 * q]);
+      } else if (!BF16) {
+        load4((const float*)xv + (size_t)k * d, n, d, b_vec, &pb[4 * q]);
+      } else {  // bf16 x: d % 8 == 0, so a 4-element chunk is in range as a whole
+        const uint16_t* xr = (const uint16_t*)xv + (size_t)k * d;
+        const u32x2 v = n < d ? *reinterpret_cast<const u32x2*>(xr + n) : u32x2{0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pb[4 * q + e] = bf16_bits_to_f32((v[e >> 1] >> (16 * (e & 1))) & 0xffffu);
       }
-      pb[q] = bv;
     }
   };
   auto sstore = [&]() {
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int idx = tid + 256 * q;
-      if (DWR) As[(idx >> 7) * FPB + (idx & 127)] = pa[q];
-      else As[(idx >> 5) * FPA + (idx & 31)] = pa[q];
-      Bs[(idx >> 7) * FPB + (idx & 127)] = pb[q];
+    for (int q = 0; q < 4; ++q) {
+      const int c = tid + 256 * q;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (DWR) As[(c >> 5) * FPB + 4 * (c & 31) + e] = pa[4 * q + e];
+        else As[(c >> 3) * FPA + 4 * (c & 7) + e] = pa[4 * q + e];
+        Bs[(c >> 5) * FPB + 4 * (c & 31) + e] = pb[4 * q + e];
+      }
     }
   };
   if (kbeg < kend) gload(kbeg);
