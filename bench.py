@@ -187,9 +187,8 @@ def algorithmic_bytes(w, stage, accepted, active, esize, dropped=0, k=1, reroute
     T, N, d = w.T, w.N, w.d
     nblk = (T + 31) // 32
     bf16 = w.dtype == "bf16"
-    two = k == 2 or reroute
-    tiled = bf16 and N % 4 == 0 and (two or N > 128 or (N > 64 and T >= 256 * 128))
-    fused = bf16 and not two and N <= 128 and not tiled
+    tiled = bf16 and N % 4 == 0 and (N > 128 or (N > 64 and T >= 256 * 128))
+    fused = bf16 and N <= 128 and not tiled
     wbytes = active * w.F * w.d * esize
     w1mul = 2 if w.glu else 1  # GEGLU: two up-projections (W1 and b1 of 2F rows)
     bias1 = w1mul * active * w.F * esize if w.has_bias else 0

@@ -232,24 +232,31 @@ router_planes_kernel(const float* __restrict__ Wr, int d, int N, int MT, int nks
 // finally one thread per expert sums p over the block's tokens in token order
 // (ppart[b, i]) and counts the tokens whose top-1 is i (cnt[b, i]), and one
 // thread per token counts the earlier tokens with its top-1 (lrank[t]).
+// MODE 1 (top-2) also takes the second choice (the largest other logit, lowest
+// index on ties) with gate exp(z2 - m)/S, writes both choices [T, 2], counts
+// memberships in cnt and first choices in cnt1, and ranks each choice among
+// the block's earlier choices of the same expert (lrank[2t + c]), as the
+// staged top-2 route does.  MODE 2 (rerouting) writes both choices and gates
+// [T, 2] to the workspace and counts and ranks the first choices only.
 // ---------------------------------------------------------------------------
 constexpr int FR_BK = 32;
 constexpr int FR_LD = FR_BK + 8;  // bf16 per LDS row of the token slot (80 B)
 constexpr int FR_KSPLIT = 4;      // waves per block, each a quarter of the k-steps
 static_assert(kRouteTokens == 32, "one block routes 32 tokens");
 
-template <int MT>
+template <int MT, int MODE>
 __global__ void __launch_bounds__(64 * FR_KSPLIT)
 router_fused_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ planes,
                     uint32_t planes_bytes, int T, int d, int N, int32_t* __restrict__ expert_idx,
                     float* __restrict__ gate, float* __restrict__ ppart, int* __restrict__ cnt,
-                    int* __restrict__ lrank) {
+                    int* __restrict__ lrank, int* __restrict__ cnt1) {
   constexpr int NE = MT * 32;       // expert rows of the tile
   constexpr int PST = 33;           // floats per staged expert row (32 tokens + 1: banks)
   constexpr int EPT = NE / 8;       // experts per thread in the softmax (8 threads a token)
   __shared__ __attribute__((aligned(16))) uint16_t Xs[FR_KSPLIT][32 * FR_LD];
   __shared__ float Ps[FR_KSPLIT][NE * PST];  // partial logits; then Ps[0] holds p
   __shared__ int ids_s[32];
+  __shared__ int ids2_s[MODE != 0 ? 32 : 1];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int b = blockIdx.x;
@@ -360,6 +367,27 @@ router_fused_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__
       arg = oa;
     }
   }
+  float mx2 = -INFINITY;
+  int arg2 = 0x7fffffff;
+  if constexpr (MODE != 0) {  // second choice: the largest other logit, lowest index on ties
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+      const int e = g + 8 * i;
+      if (e < N && e != arg && z[i] > mx2) {
+        mx2 = z[i];
+        arg2 = e;
+      }
+    }
+#pragma unroll
+    for (int off = 1; off < 8; off <<= 1) {
+      const float om = __shfl_xor(mx2, off);
+      const int oa = __shfl_xor(arg2, off);
+      if (om > mx2 || (om == mx2 && oa < arg2)) {
+        mx2 = om;
+        arg2 = oa;
+      }
+    }
+  }
   float ssum = 0.f;
 #pragma unroll
   for (int i = 0; i < EPT; ++i) {
@@ -371,9 +399,17 @@ router_fused_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__
   const float inv = 1.0f / ssum;
   if (g == 0) {
     ids_s[tt] = live ? arg : -1;
+    if constexpr (MODE != 0) ids2_s[tt] = live ? arg2 : -1;
     if (live) {
-      expert_idx[t] = arg;
-      gate[t] = inv;
+      if constexpr (MODE == 0) {
+        expert_idx[t] = arg;
+        gate[t] = inv;
+      } else {
+        expert_idx[2 * (size_t)t] = arg;
+        expert_idx[2 * (size_t)t + 1] = arg2;
+        gate[2 * (size_t)t] = inv;
+        gate[2 * (size_t)t + 1] = expf(mx2 - mx) * inv;
+      }
     }
   }
   lds_barrier();  // every wave is past its reads of the partial tiles
@@ -384,20 +420,30 @@ router_fused_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__
   // ---- per expert: block sum of p (token order) and top-1 count ----
   for (int e = threadIdx.x; e < N; e += 64 * FR_KSPLIT) {
     float ps = 0.f;
-    int c = 0;
+    int c = 0, c2 = 0;
     for (int j = 0; j < 32; ++j) {
       ps += Ps[0][e * PST + j];
       c += ids_s[j] == e;
+      if constexpr (MODE == 1) c2 += ids2_s[j] == e;
     }
     ppart[(size_t)b * N + e] = ps;
-    cnt[(size_t)b * N + e] = c;
+    cnt[(size_t)b * N + e] = c + c2;  // top-2: memberships
+    if constexpr (MODE == 1) cnt1[(size_t)b * N + e] = c;
   }
   // ---- per token: earlier tokens of the block with the same top-1 ----
-  if (threadIdx.x < 32 && t0 + (int)threadIdx.x < T) {
+  if constexpr (MODE == 1) {  // each choice among the earlier choices of its expert
+    const int j0 = threadIdx.x >> 1, c = threadIdx.x & 1;
+    if (threadIdx.x < 64 && t0 + j0 < T) {
+      const int me = c ? ids2_s[j0] : ids_s[j0];
+      int r = 0;
+      for (int j = 0; j < j0; ++j) r += (ids_s[j] == me) + (ids2_s[j] == me);
+      lrank[2 * (size_t)(t0 + j0) + c] = r;
+    }
+  } else if (threadIdx.x < 32 && t0 + (int)threadIdx.x < T) {
     const int me = ids_s[threadIdx.x];
     int r = 0;
     for (int j = 0; j < (int)threadIdx.x; ++j) r += ids_s[j] == me;
-    lrank[t0 + threadIdx.x] = r;
+    lrank[(MODE == 2 ? 2 : 1) * (size_t)(t0 + threadIdx.x)] = r;
   }
 }
 
@@ -611,13 +657,13 @@ static bool logits_fit_offsets(const Shape& s) {
 static bool router_is_tiled(const Shape& s) {
   return s.dtype == SFFN_BF16 && s.N % 4 == 0 && logits_fit_offsets(s) &&
          tiled_planes_bytes(s) < ((size_t)1 << 31) - ((size_t)8 << 20) &&
-         (staged_router(s) || s.N > 128 || (s.N > 64 && s.T >= 256 * 128));
+         (s.stage_logits != 0 || s.N > 128 || (s.N > 64 && s.T >= 256 * 128));
 }
 
-// Top-2 routing and rerouting always stage the logits (the fused epilogue is
-// top-1 only).
+// The backward stages the logits; the forward forms (top-1, top-2, rerouting)
+// all have a fused epilogue.
 bool router_is_fused(const Shape& s) {
-  return s.dtype == SFFN_BF16 && !staged_router(s) && s.N <= 128 && !router_is_tiled(s);
+  return s.dtype == SFFN_BF16 && s.stage_logits == 0 && s.N <= 128 && !router_is_tiled(s);
 }
 
 hipError_t launch_router_logits(const Shape& s, const Inputs& in, const Workspace& ws,
@@ -1053,15 +1099,24 @@ hipError_t launch_router_fused(const Shape& s, const Inputs& in, const Workspace
   const dim3 grid((unsigned)s.n_route_blocks), block(256);
   const uint16_t* x = (const uint16_t*)in.x;
   const uint32_t pbytes = (uint32_t)router_planes_bytes(s);
-#define SFFN_FUSED(M)                                                                            \
-  hipLaunchKernelGGL(router_fused_kernel<M>, grid, block, 0, st, x, ws.planes, pbytes, s.T, s.d, \
-                     s.N, out.expert_idx, out.gate, ws.ppart, ws.cnt, ws.lrank)
+  // Rerouting keeps both choices in the workspace; the scatter writes the outputs.
+  const int mode = s.k == 2 ? 1 : (s.reroute ? 2 : 0);
+  int32_t* const eidx = mode == 2 ? ws.choice : out.expert_idx;
+  float* const g = mode == 2 ? ws.gate2 : out.gate;
+#define SFFN_FUSED(M, MO)                                                                         \
+  hipLaunchKernelGGL((router_fused_kernel<M, MO>), grid, block, 0, st, x, ws.planes, pbytes, s.T, \
+                     s.d, s.N, eidx, g, ws.ppart, ws.cnt, ws.lrank, ws.cnt1)
+#define SFFN_FUSED_MODES(M)         \
+  if (mode == 0) SFFN_FUSED(M, 0);  \
+  else if (mode == 1) SFFN_FUSED(M, 1); \
+  else SFFN_FUSED(M, 2)
   switch (mt) {
-    case 1: SFFN_FUSED(1); break;
-    case 2: SFFN_FUSED(2); break;
-    case 3: SFFN_FUSED(3); break;
-    default: SFFN_FUSED(4); break;
+    case 1: SFFN_FUSED_MODES(1); break;
+    case 2: SFFN_FUSED_MODES(2); break;
+    case 3: SFFN_FUSED_MODES(3); break;
+    default: SFFN_FUSED_MODES(4); break;
   }
+#undef SFFN_FUSED_MODES
 #undef SFFN_FUSED
   return hipGetLastError();
 }
