@@ -159,8 +159,9 @@ def algorithmic_bytes(w, stage, accepted, active, esize, dropped=0, k=1, reroute
     The router runs one of two ways (the library's choice, mirrored here):
     fused (bf16, N <= 128, fewer than 32768 tokens when N > 64): the whole
           router is in the softmax_route stage (router_logits launches nothing):
-          Wr read, its three bf16 planes written and read once, x read, and
-          expert/gate/rank per token and the per-block p sums and counts written;
+          Wr read, its three bf16 planes written and read once, x read, and the
+          fp32 logits, expert/gate/rank per token and the per-block p sums and
+          counts written;
     tiled / staged (otherwise): router_logits reads x and Wr (and, tiled, writes
           and reads the planes once) and writes the fp32 logits; softmax_route
           reads the logits and writes the same per-token and per-block outputs.
@@ -209,7 +210,7 @@ def algorithmic_bytes(w, stage, accepted, active, esize, dropped=0, k=1, reroute
         return T * d * esize + N * d * 4 + (12 * N * d if tiled else 0) + T * N * 4
     if stage == "softmax_route":
         if fused:
-            return T * d * 2 + N * d * 4 + 12 * N * d + outs
+            return T * d * 2 + N * d * 4 + 12 * N * d + T * N * 4 + outs
         return T * N * 4 + outs
     if stage == "dispatch_scan":
         if reroute:
@@ -227,10 +228,9 @@ def algorithmic_bytes(w, stage, accepted, active, esize, dropped=0, k=1, reroute
 def backward_bytes(w, stage, accepted, active, esize, parts):
     """Bytes a backward stage must move at minimum (each operand read once, each
     result written once; A accepted rows, `active` experts with rows):
-    router_logits: x, Wr (and the tiled router's planes) read, fp32 logits written;
     expert_dgrad_hidden: W2 of active experts, dy and H rows read, dA rows and the
         partial dg (one fp32 per row and 128-column tile) written;
-    router_grad: logits read, dz written, partial dg read (plus dy . b2);
+    router_grad: the forward's logits read, dz written, partial dg read (plus dy . b2);
     expert_dgrad_input: W1 of active experts and dA rows read, fp32 dXe rows written;
     dx: dz, Wr, dy and dXe read, dx written;
     router_wgrad: dz and x read, per-part fp32 sums written, read back and summed;
@@ -239,10 +239,7 @@ def backward_bytes(w, stage, accepted, active, esize, parts):
     """
     A, T, N, d, F = accepted, w.T, w.N, w.d, w.F
     n_dgp = (F + 127) // 128 if w.dtype == "bf16" else 1
-    tiled = w.dtype == "bf16" and N % 4 == 0
     wb = active * d * F * esize
-    if stage == "router_logits":
-        return T * d * esize + N * d * 4 + (12 * N * d if tiled else 0) + T * N * 4
     if stage == "expert_dgrad_hidden":
         return wb + A * d * esize + 2 * A * F * esize + n_dgp * A * 4 + A * 8
     if stage == "router_grad":

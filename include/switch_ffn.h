@@ -199,8 +199,9 @@ int switch_ffn_forward_topk(const void* x, const float* Wr, const void* W1, cons
  *   x, Wr, W1, b1, W2, b2, T, d, F, N, CF, dtype  exactly as in the forward call
  *   expert_idx, slot  [T] the forward's outputs (device)
  *   fwd_workspace     the forward's workspace (device), as that call left it:
- *                     it holds the dispatch (offsets, row maps, gates, counts)
- *                     and the hidden activations H; only read here
+ *                     it holds the fp32 router logits, the dispatch (offsets,
+ *                     row maps, gates, counts) and the hidden activations H;
+ *                     only read here
  *   dy                [T, d] dL/dy (device, dtype)
  *   d_aux             dL/d(aux_loss) (host value; the alpha factor goes here)
  * Outputs (device, caller-allocated, overwritten): dx [T, d] (dtype),

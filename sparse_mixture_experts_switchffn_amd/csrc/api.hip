@@ -90,7 +90,6 @@ static int make_shape(int64_t T, int64_t d, int64_t F, int64_t N, double CF, int
   s->k = k;
   s->reroute = reroute ? 1 : 0;
   s->glu = glu ? 1 : 0;
-  s->stage_logits = 0;
   s->n_route_blocks = (int)((T + sffn::kRouteTokens - 1) / sffn::kRouteTokens);
   const int64_t cap_rows = N * Ce;
   s->max_rows = (int)(cap_rows < k * T ? cap_rows : k * T);
@@ -214,12 +213,12 @@ int switch_ffn_forward_topk(const void* x, const float* Wr, const void* W1, cons
 }
 
 namespace {
-const char* const kBwdStageNames[] = {"router_logits", "expert_dgrad_hidden", "router_grad",
+const char* const kBwdStageNames[] = {"expert_dgrad_hidden", "router_grad",
                                       "expert_dgrad_input", "dx", "router_wgrad",
                                       "expert_wgrad", "bias_grad"};
 constexpr int kNumBwdStages = (int)(sizeof(kBwdStageNames) / sizeof(kBwdStageNames[0]));
 
-// Backward scratch: dz [T, N] fp32 | router planes | dA [max_rows, F] | partial dg |
+// Backward scratch: dz [T, N] fp32 | dA [max_rows, F] | partial dg |
 // dXe [T, d] fp32 | partial dWr.
 size_t bwd_layout(const sffn::Shape& s, char* base, sffn::BwdState* b) {
   size_t off = 0;
@@ -229,18 +228,14 @@ size_t bwd_layout(const sffn::Shape& s, char* base, sffn::BwdState* b) {
     return p;
   };
   const size_t T = (size_t)s.T, N = (size_t)s.N, esize = s.dtype == SFFN_BF16 ? 2 : 4;
-  sffn::Shape sr = s;
-  sr.stage_logits = 1;
   const int n_dgp = sffn::bwd_dgp_tiles(s), parts = sffn::bwd_wr_parts(s);
   float* dz = (float*)take(T * N * 4);
-  uint16_t* planes = (uint16_t*)take(sffn::router_planes_bytes(sr));
   void* dA = take((size_t)s.max_rows * s.F * esize + 16);
   float* dgp = (float*)take((size_t)n_dgp * s.max_rows * 4 + 4);
   float* dxe = (float*)take(T * s.d * 4);
   float* wrp = (float*)take((size_t)parts * N * s.d * 4);
   if (b) {
     b->dz = dz;
-    b->planes = planes;
     b->dA = dA;
     b->dgp = dgp;
     b->n_dgp = n_dgp;
@@ -296,6 +291,7 @@ int switch_ffn_backward(const void* x, const float* Wr, const void* W1, const vo
   b.rowgate = fw.rowgate;
   b.hist = fw.hist;
   b.H = fw.H;
+  b.logits = fw.logits;
   b.dy = dy;
   b.d_aux = d_aux;
   b.dx = dx;

@@ -466,13 +466,13 @@ bwd_wgrad_f32_kernel(const float* __restrict__ rowsA, const float* __restrict__ 
 }
 
 // ---------------------------------------------------------------------------
-// Router gradient, one wave per token: p from the staged fp32 logits, dg from
+// Router gradient, one wave per token: p from the forward's fp32 logits, dg from
 // E1's partial sums plus dy . b2, then dz = p * (u - p . u) written over the
 // logits.  u_i = d_aux N hist_i / T^2 (+ dg at the token's expert).
 // ---------------------------------------------------------------------------
 template <bool BF16>
 __global__ void __launch_bounds__(256)
-bwd_router_grad_kernel(float* __restrict__ z, const int32_t* __restrict__ expert_idx,
+bwd_router_grad_kernel(const float* __restrict__ z, float* __restrict__ dz, const int32_t* __restrict__ expert_idx,
                        const int32_t* __restrict__ slot, const int* __restrict__ offset,
                        const int* __restrict__ hist, const float* __restrict__ dgp, int n_dgp,
                        int max_rows, const void* __restrict__ dyv, const void* __restrict__ b2v,
@@ -480,7 +480,8 @@ bwd_router_grad_kernel(float* __restrict__ z, const int32_t* __restrict__ expert
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (t >= T) return;
-  float* zr = z + (size_t)t * N;
+  const float* zr = z + (size_t)t * N;
+  float* dzr = dz + (size_t)t * N;
   float m = -INFINITY;
   for (int i = lane; i < N; i += 64) m = fmaxf(m, zr[i]);
 #pragma unroll
@@ -521,7 +522,7 @@ bwd_router_grad_kernel(float* __restrict__ z, const int32_t* __restrict__ expert
   for (int i = lane; i < N; i += 64) {
     const float p = expf(zr[i] - m) * inv;
     const float u = caux * (float)hist[i] + (i == e && sl >= 0 ? dg : 0.f);
-    zr[i] = p * (u - pu);
+    dzr[i] = p * (u - pu);
   }
 }
 
@@ -803,15 +804,6 @@ hipError_t launch_backward(const Shape& s, const Inputs& in, const BwdState& b, 
   const bool bf16 = s.dtype == SFFN_BF16;
   const int n_rows = s.max_rows;  // rows beyond offset[N] are never read
 
-  // 1. router logits, staged (fp32)
-  SFFN_CHECK(mark());
-  Shape sr = s;
-  sr.stage_logits = 1;
-  Workspace wr{};
-  wr.logits = b.dz;
-  wr.planes = b.planes;
-  SFFN_CHECK(launch_router_logits(sr, in, wr, st));
-
   // 2. E1: dA and partial dg
   SFFN_CHECK(mark());
   const int mt_max = (s.C + GM - 1) / GM;
@@ -830,16 +822,18 @@ hipError_t launch_backward(const Shape& s, const Inputs& in, const BwdState& b, 
     SFFN_CHECK(hipGetLastError());
   }
 
-  // 3. router gradient dz (over the logits)
+  // 3. router gradient dz
   SFFN_CHECK(mark());
   {
     const dim3 grid((unsigned)((s.T + 3) / 4));
     if (bf16)
-      hipLaunchKernelGGL(bwd_router_grad_kernel<true>, grid, dim3(256), 0, st, b.dz, b.expert_idx,
+      hipLaunchKernelGGL(bwd_router_grad_kernel<true>, grid, dim3(256), 0, st, b.logits, b.dz,
+                         b.expert_idx,
                          b.slot, b.offset, b.hist, b.dgp, b.n_dgp, s.max_rows, b.dy, in.b2, s.T,
                          s.d, s.N, b.d_aux);
     else
-      hipLaunchKernelGGL(bwd_router_grad_kernel<false>, grid, dim3(256), 0, st, b.dz, b.expert_idx,
+      hipLaunchKernelGGL(bwd_router_grad_kernel<false>, grid, dim3(256), 0, st, b.logits, b.dz,
+                         b.expert_idx,
                          b.slot, b.offset, b.hist, b.dgp, b.n_dgp, s.max_rows, b.dy, in.b2, s.T,
                          s.d, s.N, b.d_aux);
     SFFN_CHECK(hipGetLastError());

@@ -226,7 +226,8 @@ router_planes_kernel(const float* __restrict__ Wr, int d, int N, int MT, int nks
 // re-laid out through a private LDS slot into the operand layout).  32 k per
 // step, operands fetched 2-3 steps ahead.
 // Epilogue (all four waves): the partial logit tiles meet in LDS and are
-// summed in wave order; eight threads per token then take
+// summed in wave order (and the fp32 logits are written to the workspace, where
+// the backward pass reads them); eight threads per token then take
 //   m = max z, e = lowest index with z = m, S = sum exp(z - m), gate = 1/S,
 // each over an eighth of the experts, combined by three cross-lane steps;
 // finally one thread per expert sums p over the block's tokens in token order
@@ -249,7 +250,8 @@ __global__ void __launch_bounds__(64 * FR_KSPLIT)
 router_fused_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ planes,
                     uint32_t planes_bytes, int T, int d, int N, int32_t* __restrict__ expert_idx,
                     float* __restrict__ gate, float* __restrict__ ppart, int* __restrict__ cnt,
-                    int* __restrict__ lrank, int* __restrict__ cnt1) {
+                    int* __restrict__ lrank, int* __restrict__ cnt1,
+                    float* __restrict__ logits) {
   constexpr int NE = MT * 32;       // expert rows of the tile
   constexpr int PST = 33;           // floats per staged expert row (32 tokens + 1: banks)
   constexpr int EPT = NE / 8;       // experts per thread in the softmax (8 threads a token)
@@ -353,6 +355,7 @@ router_fused_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__
     const int e = g + 8 * i;
     const int o = e * PST + tt;
     z[i] = ((Ps[0][o] + Ps[1][o]) + Ps[2][o]) + Ps[3][o];  // waves in order
+    if (live && e < N) logits[(size_t)t * N + e] = z[i];  // kept for the backward pass
     if (e < N && z[i] > mx) {  // e rises with i: the first maximum is the lowest index
       mx = z[i];
       arg = e;
@@ -657,13 +660,12 @@ static bool logits_fit_offsets(const Shape& s) {
 static bool router_is_tiled(const Shape& s) {
   return s.dtype == SFFN_BF16 && s.N % 4 == 0 && logits_fit_offsets(s) &&
          tiled_planes_bytes(s) < ((size_t)1 << 31) - ((size_t)8 << 20) &&
-         (s.stage_logits != 0 || s.N > 128 || (s.N > 64 && s.T >= 256 * 128));
+         (s.N > 128 || (s.N > 64 && s.T >= 256 * 128));
 }
 
-// The backward stages the logits; the forward forms (top-1, top-2, rerouting)
-// all have a fused epilogue.
+// The forward forms (top-1, top-2, rerouting) all have a fused epilogue.
 bool router_is_fused(const Shape& s) {
-  return s.dtype == SFFN_BF16 && s.stage_logits == 0 && s.N <= 128 && !router_is_tiled(s);
+  return s.dtype == SFFN_BF16 && s.N <= 128 && !router_is_tiled(s);
 }
 
 hipError_t launch_router_logits(const Shape& s, const Inputs& in, const Workspace& ws,
@@ -1105,7 +1107,7 @@ hipError_t launch_router_fused(const Shape& s, const Inputs& in, const Workspace
   float* const g = mode == 2 ? ws.gate2 : out.gate;
 #define SFFN_FUSED(M, MO)                                                                         \
   hipLaunchKernelGGL((router_fused_kernel<M, MO>), grid, block, 0, st, x, ws.planes, pbytes, s.T, \
-                     s.d, s.N, eidx, g, ws.ppart, ws.cnt, ws.lrank, ws.cnt1)
+                     s.d, s.N, eidx, g, ws.ppart, ws.cnt, ws.lrank, ws.cnt1, ws.logits)
 #define SFFN_FUSED_MODES(M)         \
   if (mode == 0) SFFN_FUSED(M, 0);  \
   else if (mode == 1) SFFN_FUSED(M, 1); \

@@ -17,7 +17,6 @@ struct Shape {
   int k;                // experts per token (1: Switch routing, 2: top-2)
   int reroute;          // k = 1 with overflow tokens rerouted to their second choice
   int glu;              // GEGLU experts: W1 [N, 2F, d], b1 [N, 2F]
-  int stage_logits;     // the router writes its fp32 logits to the workspace (backward)
   int dtype;            // SFFN_FP32 / SFFN_BF16
   int n_route_blocks;   // ceil(T / kRouteTokens)
   int max_rows;         // min(k*T, N*C): rows the expert buffers can hold
@@ -26,7 +25,6 @@ struct Shape {
 // The router ranks two experts per token (top-2 routing, or rerouting).
 inline bool two_choices(const Shape& s) { return s.k == 2 || s.reroute != 0; }
 // The logits go through the workspace (no fused router).
-inline bool staged_router(const Shape& s) { return two_choices(s) || s.stage_logits != 0; }
 
 struct Workspace {
   float* logits;   // [T, N] fp32 router logits
@@ -109,12 +107,12 @@ struct BwdState {
   const float* rowgate;       // [max_rows]
   const int* hist;            // [N] top-1 counts
   const void* H;              // [max_rows, F] hidden activations (dtype)
+  const float* logits;        // [T, N] fp32 router logits
   // upstream gradients
   const void* dy;             // [T, d] (dtype)
   float d_aux;
   // scratch
-  float* dz;                  // [T, N]: logits, then dz
-  uint16_t* planes;           // router planes of the staged logits
+  float* dz;                  // [T, N] dL/dz
   void* dA;                   // [max_rows, F] (dtype)
   float* dgp;                 // [n_dgp, max_rows] partial dg per column tile of F
   int n_dgp;
