@@ -76,6 +76,14 @@ constexpr int kCpolNonTemporal = 2;
 // past the caches, the others stay cached for the next k-step, which reads
 // the other half of their last line.
 constexpr int kCpolSplitRows = -1;
+// FFN1 weight policy for the same rows: every load takes whole lines.  A load
+// of an odd row (which starts mid-line) takes the line holding the second half
+// of its k-step and the first half of the next step; that first half waits in
+// registers (one stash per load) until the next step, and each tile starts
+// with one extra load per odd row of its first 32 k.  Each weight line is then
+// requested once (the line two rows share, twice) and all of them stream past
+// the caches.
+constexpr int kCpolShiftOdd = -2;
 constexpr int FBK = 64;              // k per step (one 128-byte chunk row)
 constexpr int FLDS = FBK + 8;        // bf16 per row of a weight slot (144 B: rows 4 banks apart)
 constexpr int FP = SFFN_FFN_STAGES;  // k-steps in flight
@@ -204,6 +212,10 @@ ffn_bf16_kernel(const uint16_t* __restrict__ act, uint32_t act_bytes,
   constexpr int CST = Geo::CST, XPT = Geo::XPT, BL = Geo::BL, WCOLS = Geo::WCOLS;
   constexpr int COLS = Geo::COLS, OPC = Geo::OPC, OCOLS = Geo::OCOLS;
   constexpr int WMUL = GLU ? 2 : 1;  // weight rows per output column
+  constexpr bool SHIFT = WPOL == kCpolShiftOdd;
+  constexpr bool PARITY = SHIFT || WPOL == kCpolSplitRows;  // loads grouped by row parity
+  constexpr int HB = SHIFT ? BL / 2 : 1;                     // odd-row loads (stashes)
+  static_assert(!SHIFT || !Geo::LATE_B, "the stash is refilled before a tile's activations");
   static_assert(ROWS <= NTHR, "one thread per row for the row lookups");
   static_assert(Geo::fits, "LDS budget");
   // [activation ring (FNB tiles) | weight slots | 1 KB sink for idle loads].
@@ -275,34 +287,49 @@ ffn_bf16_kernel(const uint16_t* __restrict__ act, uint32_t act_bytes,
     return buffer_load16(src, (dt.nrows > 0 && n >= 0) ? (uint32_t)n * 2u : kOob);
   };
   // Weights: load i of a step brings rows wrow(i) of the wave's WCOLS (8i +
-  // lane/8, or grouped by parity for kCpolSplitRows), 16-byte chunk lane%8 of
-  // the k-step.
+  // lane/8, or grouped by parity: load i takes rows of parity i%2), 16-byte
+  // chunk lane%8 of the k-step (kCpolShiftOdd, odd rows: 32 k further on).
   auto wrow = [&](int i) {
-    return WPOL == kCpolSplitRows ? 2 * (8 * (i / 2) + (lane >> 3)) + (i & 1) : i * 8 + (lane >> 3);
+    return PARITY ? 2 * (8 * (i / 2) + (lane >> 3)) + (i & 1) : i * 8 + (lane >> 3);
   };
   auto setup_b = [&](const FfnTile& dt, __amdgpu_buffer_rsrc_t& src, uint32_t (&off)[BL]) {
     src = make_rsrc(W + (size_t)dt.e * WMUL * Nout * K, (uint32_t)((size_t)WMUL * Nout * K * 2));
 #pragma unroll
     for (int i = 0; i < BL; ++i) {
       const int nr = phys_row(dt.nt, wave * WCOLS + wrow(i));
+      const uint32_t shift = (SHIFT && (i & 1)) ? 32u : 0u;
       off[i] = (dt.nrows > 0 && nr >= 0)
-                   ? ((uint32_t)nr * (uint32_t)K + (uint32_t)(lane & 7) * 8u) * 2u : kOob;
+                   ? ((uint32_t)nr * (uint32_t)K + shift + (uint32_t)(lane & 7) * 8u) * 2u : kOob;
     }
   };
   auto load_b = [&](u32x4 (&rb)[BL], const __amdgpu_buffer_rsrc_t& src, const uint32_t (&off)[BL],
                     int ks) {
-    const bool kin = ks * FBK + (lane & 7) * 8 < K;
-    constexpr int P0 = WPOL == kCpolSplitRows ? kCpolNonTemporal : WPOL;  // even loads
-    constexpr int P1 = WPOL == kCpolSplitRows ? 0 : WPOL;                 // odd loads
+    const int kc = ks * FBK + (lane & 7) * 8;
+    const bool kin = kc < K;
+    const bool kin_odd = SHIFT ? kc + 32 < K : kin;
+    constexpr int P0 = PARITY ? kCpolNonTemporal : WPOL;                      // even loads
+    constexpr int P1 = SHIFT ? kCpolNonTemporal : (PARITY ? 0 : WPOL);        // odd loads
 #pragma unroll
     for (int i = 0; i < BL; ++i) {
       if (i & 1)
         rb[i] = __builtin_amdgcn_raw_buffer_load_b128(
-            src, (int)(kin ? off[i] + (uint32_t)ks * (FBK * 2) : kOob), 0, P1);
+            src, (int)(kin_odd ? off[i] + (uint32_t)ks * (FBK * 2) : kOob), 0, P1);
       else
         rb[i] = __builtin_amdgcn_raw_buffer_load_b128(
             src, (int)(kin ? off[i] + (uint32_t)ks * (FBK * 2) : kOob), 0, P0);
     }
+  };
+  // kCpolShiftOdd: the stash of a tile's first step, each odd row's first
+  // 32 k (k-step -1 of its loads: lanes 4..7 hold them).
+  auto load_head = [&](u32x4 (&h)[HB], const __amdgpu_buffer_rsrc_t& src,
+                       const uint32_t (&off)[BL]) {
+    const int kc = (lane & 7) * 8 - 32;
+    const bool kin = kc >= 0 && kc < K;
+#pragma unroll
+    for (int j = 0; j < HB; ++j)
+      h[j] = __builtin_amdgcn_raw_buffer_load_b128(
+          src, (int)((kin && off[2 * j + 1] != kOob) ? off[2 * j + 1] - (uint32_t)(FBK * 2) : kOob),
+          0, kCpolNonTemporal);
   };
 
   // Activations: load i of a step fills row group g = wave + i*FW (rows 8g ..
@@ -339,12 +366,26 @@ ffn_bf16_kernel(const uint16_t* __restrict__ act, uint32_t act_bytes,
   const int rsw = (lane & 7) ^ ((lane >> 3) & 1);  // swizzle of rows with these low bits
   const uint32_t a_rd = (uint32_t)(lane & 31) * 128u + (uint32_t)(((khalf * 4) ^ rsw) * 16);
   f32x16 acc[MT * WN];
+  u32x4 st[HB];  // kCpolShiftOdd: the next step's first half of each odd row
   uint16_t* bslot = Bs + wave * WCOLS * FLDS;
   auto compute = [&](int buf, const u32x4 (&rb)[BL]) {
     // Weight tile into the wave's LDS slot (row-major), back out in operand layout.
     // LDS accesses of one wave complete in order, so no barrier is needed.
 #pragma unroll
-    for (int i = 0; i < BL; ++i) store16(bslot + wrow(i) * FLDS + (lane & 7) * 8, rb[i]);
+    for (int i = 0; i < BL; ++i) {
+      if (SHIFT && (i & 1)) {
+        // Lanes 0..3 hold chunks 4..7 of this step; lanes 4..7 take chunks
+        // 0..3 from the stash and keep their own (the next step's) in it.
+        const bool lo = (lane & 7) < 4;
+        u32x4 v;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = lo ? rb[i][q] : st[i / 2][q];
+        store16(bslot + wrow(i) * FLDS + (((lane & 7) + 4) & 7) * 8, v);
+        st[i / 2] = rb[i];
+      } else {
+        store16(bslot + wrow(i) * FLDS + (lane & 7) * 8, rb[i]);
+      }
+    }
     const char* abase = As + buf * A_BYTES;
     const uint16_t* bbase = bslot + (lane & 31) * FLDS + khalf * 32;
     // Operand fragments of sub-step q (16 k): read one sub-step ahead of the
@@ -390,6 +431,7 @@ ffn_bf16_kernel(const uint16_t* __restrict__ act, uint32_t act_bytes,
     }
   };
   if (!Geo::LATE_B) prologue_b();
+  if constexpr (SHIFT) load_head(st, rb_src, b_off);
   if (!SECOND) {
     if (tid < ROWS) tok_s[tid] = my_tok;
     dma_barrier();
@@ -466,6 +508,8 @@ ffn_bf16_kernel(const uint16_t* __restrict__ act, uint32_t act_bytes,
           load_residual();
         }
       } else {
+        // kCpolShiftOdd: the stash is free after the tile's final compute.
+        if constexpr (SHIFT && J == FP - 1) load_head(st, rb_src_n, b_off_n);
         load_b(rb[J], rb_src_n, b_off_n, J);
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -608,7 +652,7 @@ ffn_bf16_kernel(const uint16_t* __restrict__ act, uint32_t act_bytes,
 
 #undef SFFN_LDS_PTR
 
-template <int MT, int FW, int WN, bool SECOND, bool GLU>
+template <int MT, int FW, int WN, bool SECOND, bool GLU, int WPOL = 0>
 static int ffn_resident_blocks() {
   // Blocks of this kernel the device holds at once (a persistent grid's size).
   static const int n = [] {
@@ -616,7 +660,7 @@ static int ffn_resident_blocks() {
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, ffn_bf16_kernel<MT, FW, WN, SECOND, 0, GLU>, FW * 64, 0) != hipSuccess)
+            &per_cu, ffn_bf16_kernel<MT, FW, WN, SECOND, WPOL, GLU>, FW * 64, 0) != hipSuccess)
       return 256;
     return (cus > 0 ? cus : 256) * (per_cu > 0 ? per_cu : 1);
   }();
@@ -667,34 +711,32 @@ static long ffn_col_tiles(const FfnArgs& a, long rows_per_tile, bool glu) {
   return (a.Nout + ocols - 1) / ocols;
 }
 
-template <int MT, int FW, int WN, bool SECOND, bool GLU>
-static long ffn_grid(const FfnArgs& a) {
+// One launch with weight policy WPOL: a persistent grid of as many blocks as
+// that kernel keeps resident, or fewer if there are fewer tiles.
+template <int MT, int FW, int WN, bool SECOND, int WPOL, bool GLU>
+static void launch_ffn_pol(const FfnArgs& a, hipStream_t st) {
   const long n_tiles = ffn_col_tiles(a, FW * WN * 32, GLU) * a.n_mchunks * a.n_experts;
-  const long resident = ffn_resident_blocks<MT, FW, WN, SECOND, GLU>();
-  return n_tiles < resident ? n_tiles : resident;
+  const long resident = ffn_resident_blocks<MT, FW, WN, SECOND, GLU, WPOL>();
+  const dim3 grid((unsigned)(n_tiles < resident ? n_tiles : resident)), block(FW * 64);
+  hipLaunchKernelGGL((ffn_bf16_kernel<MT, FW, WN, SECOND, WPOL, GLU>), grid, block, 0, st, a.act,
+                     a.act_bytes, a.W, a.bias, a.offset, a.row2tok, a.rowgate, a.xres, a.out,
+                     a.out_bytes, a.K, a.Nout, a.n_mchunks, a.n_experts, a.max_rows, a.T,
+                     a.d_model, a.no_residual);
 }
 
 template <int MT, int FW, int WN, bool SECOND, bool GLU>
 static void launch_ffn_bf16_t(const FfnArgs& a, hipStream_t st) {
   if constexpr (ffn_shape_ok<MT, FW, WN, SECOND, GLU>()) {
-    const dim3 grid((unsigned)ffn_grid<MT, FW, WN, SECOND, GLU>(a)), block(FW * 64);
     // Weights are streamed past the caches when nothing re-reads their lines
-    // (with rows off the line grid: only the rows on it).
-    if (a.n_mchunks == 1 && (a.K * 2) % 128 == 64 && ((size_t)a.W & 127) == 0 && a.Nout % 2 == 0)
-      hipLaunchKernelGGL((ffn_bf16_kernel<MT, FW, WN, SECOND, kCpolSplitRows, GLU>), grid, block,
-                         0, st, a.act, a.act_bytes, a.W, a.bias, a.offset, a.row2tok, a.rowgate,
-                         a.xres, a.out, a.out_bytes, a.K, a.Nout, a.n_mchunks, a.n_experts,
-                         a.max_rows, a.T, a.d_model, a.no_residual);
+    // (with rows off the line grid: FFN1 loads whole lines, FFN2 streams only
+    // the rows on the grid).
+    const bool odd_rows =
+        a.n_mchunks == 1 && (a.K * 2) % 128 == 64 && ((size_t)a.W & 127) == 0 && a.Nout % 2 == 0;
+    constexpr int kOddPol = SECOND ? kCpolSplitRows : kCpolShiftOdd;
+    if (odd_rows) launch_ffn_pol<MT, FW, WN, SECOND, kOddPol, GLU>(a, st);
     else if (a.n_mchunks == 1 && (a.K * 2) % 128 == 0)
-      hipLaunchKernelGGL((ffn_bf16_kernel<MT, FW, WN, SECOND, kCpolNonTemporal, GLU>), grid, block,
-                         0, st, a.act, a.act_bytes, a.W, a.bias, a.offset, a.row2tok, a.rowgate,
-                         a.xres, a.out, a.out_bytes, a.K, a.Nout, a.n_mchunks, a.n_experts,
-                         a.max_rows, a.T, a.d_model, a.no_residual);
-    else
-      hipLaunchKernelGGL((ffn_bf16_kernel<MT, FW, WN, SECOND, 0, GLU>), grid, block, 0, st, a.act,
-                         a.act_bytes, a.W, a.bias, a.offset, a.row2tok, a.rowgate, a.xres, a.out,
-                         a.out_bytes, a.K, a.Nout, a.n_mchunks, a.n_experts, a.max_rows, a.T,
-                         a.d_model, a.no_residual);
+      launch_ffn_pol<MT, FW, WN, SECOND, kCpolNonTemporal, GLU>(a, st);
+    else launch_ffn_pol<MT, FW, WN, SECOND, 0, GLU>(a, st);
   }
 }
 

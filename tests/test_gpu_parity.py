@@ -73,6 +73,8 @@ def test_tiny_fp32():
     dict(T=33000, d=64, F=32, N=128, CF=1.0, bias_sigma=0.02),   # tiled logits, 128-token blocks, ragged T
     dict(T=33000, d=40, F=16, N=68, CF=1.0),                     # tiled logits, partial expert group
     dict(T=700, d=2080, F=64, N=7, CF=1.0),                      # d = 2080 (32 x 65) K tail
+    dict(T=300, d=32, F=64, N=4, CF=1.0, bias_sigma=0.02),       # d = 32: half a k-step
+    dict(T=500, d=96, F=128, N=6, CF=1.25, bias_sigma=0.02),     # d = 96: rows off the line grid
     dict(T=640, d=256, F=512, N=16, CF=0.5, bias_sigma=0.05),    # heavy dropping
 ])
 def test_bf16_edge_shapes(case):
