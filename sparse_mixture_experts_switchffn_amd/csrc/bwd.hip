@@ -24,27 +24,26 @@
 namespace sffn {
 
 // ---------------------------------------------------------------------------
-// bf16 grouped GEMMs E1..E4 on the matrix cores.
+// bf16 grouped GEMMs E1..E4 on the matrix cores: k-steps of 32 on
+// v_mfma_f32_32x32x16_bf16, whose operand fragment is 8 consecutive k of one
+// row or column per lane.  An operand that is k-contiguous in memory (E1 and
+// E2's row operand) sits in LDS as [outer][k] rows (80-byte pitch) and a
+// fragment is one 16-byte read.  The others hold k as their row index in
+// memory (the weights of E1/E2 are [k][n]; E3/E4 contract over the expert's
+// rows): they are copied into LDS as they are, [k][inner] rows of 320 bytes,
+// and a fragment is two transposing reads (ds_read_b64_tr_b16: within each
+// 16-lane group, lane i receives element i % 4 of the 8-byte chunks that
+// lanes i/4 + 4c address, c = 0..3, so lanes addressing rows k..k+3 at
+// columns 4 (j % 4) give each lane four consecutive k of one column).  The
+// loads of the next PD steps are in flight in registers; LDS is
+// double-buffered.
 //
-// Block tile 128 x 128, k-steps of 32, four waves of 64 x 64 (2 x 2 MFMA
-// tiles of 32 x 32).  Both operands sit in LDS as [outer][k] rows (k
-// contiguous, 80-byte pitch), which is what a v_mfma_f32_32x32x16_bf16
-// operand fragment reads (8 consecutive k of one row per lane).  An operand
-// that is k-contiguous in memory (E1 and E2's row operand) sits in LDS as
-// [outer][k] rows (80-byte pitch) and a fragment is one 16-byte read.  The
-// others hold k as their row index in memory (the weights of E1/E2 are
-// [k][n]; E3/E4 contract over the expert's rows): they are copied into LDS as
-// they are, [k][inner] rows of 320 bytes, and a fragment is two transposing
-// reads (ds_read_b64_tr_b16: within each 16-lane group, lane i receives
-// element i % 4 of the 8-byte chunks that lanes i/4 + 4c address, c = 0..3,
-// so lanes addressing rows k..k+3 at columns 4 (j % 4) give each lane four
-// consecutive k of one column).  The loads of the next PD steps are in flight
-// in registers; LDS is double-buffered.
-//
-//   E1: rows x F,  K = d     A = dy[row2tok[r]]     B = W2_e [d][F]
-//   E2: rows x d,  K = F     A = dA[r]              B = W1_e [F][d]
+//   E1: rows x F,  K = d     A = dy[row2tok[r]]     B = W2_e [d][F]   (bwd_rows_kernel)
+//   E2: rows x d,  K = F     A = dA[r]              B = W1_e [F][d]   (bwd_rows_kernel)
 //   E3: d x F,     K = rows  A = g_r dy[row2tok[r]] B = H[r]          -> dW2_e
 //   E4: F x d,     K = rows  A = dA[r]              B = x[row2tok[r]] -> dW1_e
+// E3/E4 (bwd_gemm_kernel): block tile 128 x 128, four waves of 64 x 64 (2 x 2
+// MFMA tiles of 32 x 32), both operands [k][inner].
 // ---------------------------------------------------------------------------
 constexpr int GM = 128, GN = 128, GK = 32;
 constexpr int GP = GK + 8;  // LDS row pitch in bf16 (80 bytes: fragment reads spread over banks)
@@ -66,7 +65,7 @@ __device__ __forceinline__ bf16x8 tr_fragment(const uint16_t* S, int k0, int mba
 // k-steps whose loads are in flight: E1/E2 (long k-loops over d or F) and
 // E3/E4 (k-loops over one expert's rows).
 #ifndef SFFN_BWD_PD_ROWS
-#define SFFN_BWD_PD_ROWS 1
+#define SFFN_BWD_PD_ROWS 2
 #endif
 #ifndef SFFN_BWD_PD_WGRAD
 #define SFFN_BWD_PD_WGRAD 1
@@ -78,142 +77,96 @@ struct BwdGemmArgs {
   const int* offset;
   const int* row2tok;
   const float* rowgate;
-  const uint16_t* H;
   void* out;
-  float* dgp;
-  int T, d, F, max_rows, mt_max;
+  int T, d, F;
 };
 
 template <int KIND, int PD>
 __global__ void __launch_bounds__(256)
 bwd_gemm_kernel(BwdGemmArgs g) {
-  constexpr bool ROWS_M = KIND <= 2;  // M runs over the expert's rows (else K does)
+  static_assert(KIND == 3 || KIND == 4, "the weight gradients");
   // [A ring | B ring]; after the k-loop the epilogue stages its tile over it.
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * GM * GP + 2 * GN * GP];
-  __shared__ float red[GM];
-  uint16_t (*As)[GM][GP] = reinterpret_cast<uint16_t (*)[GM][GP]>(lds);
-  uint16_t (*Bs)[GN][GP] = reinterpret_cast<uint16_t (*)[GN][GP]>(lds + 2 * GM * GP);
+  __shared__ __attribute__((aligned(16))) uint16_t lds[4 * GK * RP];
   constexpr int SP = GN + 8;  // staged tile pitch (bf16): 272-byte rows
-  static_assert(GM * SP <= 2 * GM * GP + 2 * GN * GP, "staged tile fits the rings");
+  static_assert(GM * SP <= 4 * GK * RP, "staged tile fits the rings");
   uint16_t* const stg = lds;
 
-  const int Nn = (KIND == 1 || KIND == 3) ? g.F : g.d;
-  const int Mfix = KIND == 3 ? g.d : g.F;  // E3/E4
-  const int Kfix = KIND == 1 ? g.d : g.F;  // E1/E2
+  const int Nn = KIND == 3 ? g.F : g.d;
+  const int M = KIND == 3 ? g.d : g.F;
   const int n_nt = (Nn + GN - 1) / GN;
-  const int n_mt = ROWS_M ? g.mt_max : (Mfix + GM - 1) / GM;
+  const int n_mt = (M + GM - 1) / GM;
   const int tile = xcd_contiguous_tile(blockIdx.x, gridDim.x);
   const int e = tile / (n_nt * n_mt);
   const int rest = tile % (n_nt * n_mt);
   const int mt = rest / n_nt, nt = rest % n_nt;
   const int rbeg = g.offset[e];
   const int Ae = g.offset[e + 1] - rbeg;
-  const int M = ROWS_M ? Ae : Mfix;
-  const int K = ROWS_M ? Kfix : Ae;
+  const int K = Ae;
   const int m0 = mt * GM, n0 = nt * GN;
-  if (ROWS_M && m0 >= Ae) return;  // uniform over the block
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wm = wave & 1, wn = wave >> 1;
 
-  // ---- operand A ----
-  // k-contiguous rows (E1, E2): thread rows m0 + tid/4 + 64 i, chunk tid % 4.
-  const int ac = tid & 3;
-  uint32_t a_row_off[2];
-  __amdgpu_buffer_rsrc_t a_src;
-  // k as the row index (E3, E4) and every B: thread k rows tid/16 + {0, 16},
-  // chunk tid%16 of the 128-wide inner range.
+  // Both operands [k][inner]: thread k rows tid/16 + {0, 16}, 16-byte chunk
+  // tid % 16 of the 128-wide inner range.
   const int kr = tid >> 4, pc = tid & 15;
-  __amdgpu_buffer_rsrc_t b_src;
-  if constexpr (KIND == 1) {
-    a_src = make_rsrc(g.a, (uint32_t)g.T * (uint32_t)g.d * 2u);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int r = m0 + (tid >> 2) + 64 * i;
-      a_row_off[i] = r < Ae ? (uint32_t)g.row2tok[rbeg + r] * (uint32_t)g.d * 2u : kOob;
-    }
-    b_src = make_rsrc(g.b + (size_t)e * g.d * g.F, (uint32_t)((size_t)g.d * g.F * 2));
-  } else if constexpr (KIND == 2) {
-    a_src = make_rsrc(g.a + (size_t)rbeg * g.F, (uint32_t)Ae * (uint32_t)g.F * 2u);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int r = m0 + (tid >> 2) + 64 * i;
-      a_row_off[i] = r < Ae ? (uint32_t)r * (uint32_t)g.F * 2u : kOob;
-    }
-    b_src = make_rsrc(g.b + (size_t)e * g.F * g.d, (uint32_t)((size_t)g.F * g.d * 2));
-  } else if constexpr (KIND == 3) {
+  __amdgpu_buffer_rsrc_t a_src, b_src;
+  if constexpr (KIND == 3) {
     a_src = make_rsrc(g.a, (uint32_t)g.T * (uint32_t)g.d * 2u);
     b_src = make_rsrc(g.b + (size_t)rbeg * g.F, (uint32_t)Ae * (uint32_t)g.F * 2u);
   } else {
     a_src = make_rsrc(g.a + (size_t)rbeg * g.F, (uint32_t)Ae * (uint32_t)g.F * 2u);
     b_src = make_rsrc(g.b, (uint32_t)g.T * (uint32_t)g.d * 2u);
   }
-  const int ldA = (KIND == 2 || KIND == 4) ? g.F : g.d;  // elements per memory row of A
-  const int ldB = (KIND == 1 || KIND == 3) ? g.F : g.d;  // ... and of B
-  const int nb_chunk = n0 + pc * 8;                      // B's inner chunk (n)
-  const int ma_chunk = m0 + pc * 8;                      // A's inner chunk (m) for E3/E4
+  const int ldA = KIND == 4 ? g.F : g.d;  // elements per memory row of A
+  const int ldB = KIND == 3 ? g.F : g.d;  // ... and of B
+  const int nb_chunk = n0 + pc * 8;       // B's inner chunk (n)
+  const int ma_chunk = m0 + pc * 8;       // A's inner chunk (m)
 
-  // Memory row of k index kk for the operands that hold k as the row index:
-  // E1/E2 B: the weight row kk; E3 A and E4 B: the token of expert row kk;
-  // E3 B and E4 A: expert row kk.
+  // Memory row of k index kk: E3 A and E4 B, the token of expert row kk; E3 B
+  // and E4 A, expert row kk.
   auto tok_of = [&](int kk) -> int { return kk < Ae ? g.row2tok[rbeg + kk] : -1; };
 
   // Register ring of PD k-steps in flight: slot s holds the loads of the steps
-  // k with k % PD == s.  E3/E4 look their k rows' tokens (and gates) up one
-  // ring ahead, so that no data load waits for its index.
+  // k with k % PD == s.  The k rows' tokens (and gates) are looked up one ring
+  // ahead, so that no data load waits for its index.
   u32x4 ra[PD][2], rb[PD][2];
   float sc[PD][2];
   int tk[PD][2];
   float gk[PD][2];
   auto lookup = [&](int k0, int (&t)[2], float (&gt)[2]) {
-    if constexpr (KIND == 3 || KIND == 4) {
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int kk = k0 + kr + 16 * q;
-        t[q] = tok_of(kk);
-        gt[q] = (KIND == 3 && kk < Ae) ? g.rowgate[rbeg + kk] : 0.f;
-      }
+    for (int q = 0; q < 2; ++q) {
+      const int kk = k0 + kr + 16 * q;
+      t[q] = tok_of(kk);
+      gt[q] = (KIND == 3 && kk < Ae) ? g.rowgate[rbeg + kk] : 0.f;
     }
   };
   auto load = [&](int k0, u32x4 (&a)[2], u32x4 (&b)[2], float (&scale)[2], const int (&t)[2],
                   const float (&gt)[2]) {
-    if constexpr (ROWS_M) {
-      const bool kin = k0 + ac * 8 < K;
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        a[i] = buffer_load16(a_src, kin ? a_row_off[i] + (uint32_t)(k0 + ac * 8) * 2u : kOob);
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int kk = k0 + kr + 16 * q;
-        b[q] = buffer_load16(b_src, (kk < K && nb_chunk < Nn)
-                                        ? ((uint32_t)kk * (uint32_t)ldB + (uint32_t)nb_chunk) * 2u
-                                        : kOob);
-      }
-    } else {
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int kk = k0 + kr + 16 * q;
-        const bool kin = kk < Ae;
-        // A: E3 gathered dy rows (scaled by the gate below), E4 expert rows of dA
-        const uint32_t arow = KIND == 3 ? (uint32_t)(t[q] < 0 ? 0 : t[q]) : (uint32_t)kk;
-        a[q] = buffer_load16(a_src, (kin && ma_chunk < Mfix)
-                                        ? (arow * (uint32_t)ldA + (uint32_t)ma_chunk) * 2u
-                                        : kOob);
-        // B: E3 expert rows of H, E4 gathered x rows
-        const uint32_t brow = KIND == 4 ? (uint32_t)(t[q] < 0 ? 0 : t[q]) : (uint32_t)kk;
-        b[q] = buffer_load16(b_src, (kin && nb_chunk < Nn)
-                                        ? (brow * (uint32_t)ldB + (uint32_t)nb_chunk) * 2u
-                                        : kOob);
-        scale[q] = gt[q];
-      }
+    for (int q = 0; q < 2; ++q) {
+      const int kk = k0 + kr + 16 * q;
+      const bool kin = kk < Ae;
+      // A: E3 gathered dy rows (scaled by the gate below), E4 expert rows of dA
+      const uint32_t arow = KIND == 3 ? (uint32_t)(t[q] < 0 ? 0 : t[q]) : (uint32_t)kk;
+      a[q] = buffer_load16(a_src, (kin && ma_chunk < M)
+                                      ? (arow * (uint32_t)ldA + (uint32_t)ma_chunk) * 2u
+                                      : kOob);
+      // B: E3 expert rows of H, E4 gathered x rows
+      const uint32_t brow = KIND == 4 ? (uint32_t)(t[q] < 0 ? 0 : t[q]) : (uint32_t)kk;
+      b[q] = buffer_load16(b_src, (kin && nb_chunk < Nn)
+                                      ? (brow * (uint32_t)ldB + (uint32_t)nb_chunk) * 2u
+                                      : kOob);
+      scale[q] = gt[q];
     }
   };
   // [k][inner] tiles: a thread's two chunks go to their rows as they are (E3's
   // A scaled by the row's gate, rounded once more to bf16).
   auto raw_tile = [&](int buf, bool a_side) -> uint16_t* {
-    return a_side ? &As[buf][0][0] : &Bs[buf][0][0];
+    return lds + ((a_side ? 0 : 2) + buf) * GK * RP;
   };
   auto store_raw = [&](uint16_t* S, const u32x4 (&v)[2], bool scale, const float (&sv)[2]) {
 #pragma unroll
@@ -229,12 +182,7 @@ bwd_gemm_kernel(BwdGemmArgs g) {
     }
   };
   auto store = [&](int buf, const u32x4 (&a)[2], const u32x4 (&b)[2], const float (&sv)[2]) {
-    if constexpr (ROWS_M) {
-#pragma unroll
-      for (int i = 0; i < 2; ++i) store16(&As[buf][(tid >> 2) + 64 * i][ac * 8], a[i]);
-    } else {
-      store_raw(raw_tile(buf, true), a, KIND == 3, sv);
-    }
+    store_raw(raw_tile(buf, true), a, KIND == 3, sv);
     store_raw(raw_tile(buf, false), b, false, sv);
   };
 
@@ -250,12 +198,7 @@ bwd_gemm_kernel(BwdGemmArgs g) {
     for (int kh = 0; kh < 2; ++kh) {
       bf16x8 fa[2], fb[2];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        if constexpr (ROWS_M)
-          fa[i] = as_bf16x8(load16(&As[buf][wm * 64 + 32 * i + (lane & 31)][kh * 16 + khalf * 8]));
-        else
-          fa[i] = tr_fragment(raw_tile(buf, true), kh * 16, wm * 64 + 32 * i, lane);
-      }
+      for (int i = 0; i < 2; ++i) fa[i] = tr_fragment(raw_tile(buf, true), kh * 16, wm * 64 + 32 * i, lane);
 #pragma unroll
       for (int j = 0; j < 2; ++j) fb[j] = tr_fragment(raw_tile(buf, false), kh * 16, wn * 64 + 32 * j, lane);
 #pragma unroll
@@ -266,29 +209,30 @@ bwd_gemm_kernel(BwdGemmArgs g) {
   };
 
   // Step k: its loads were issued PD steps earlier into slot k % PD; LDS
-  // buffer k % 2 receives it one step before its matrix ops.
+  // buffer k % 2 receives it one step before its matrix ops.  The steps are
+  // rounded up to whole rounds of PD and every load is issued (past the end
+  // of K they read zeros): the loop body has no branches, so the compiler's
+  // waits for a slot's registers leave the later slots' loads in flight.
   const int nk = (K + GK - 1) / GK;
+  const int nkr = (nk + PD - 1) / PD * PD;
   static_for<0, PD>([&](auto j) { lookup(j * GK, tk[j], gk[j]); });
   static_for<0, PD>([&](auto j) {
-    if (j < nk) load(j * GK, ra[j], rb[j], sc[j], tk[j], gk[j]);
+    load(j * GK, ra[j], rb[j], sc[j], tk[j], gk[j]);
     lookup((j + PD) * GK, tk[j], gk[j]);
   });
-  if (nk > 0) store(0, ra[0], rb[0], sc[0]);
+  store(0, ra[0], rb[0], sc[0]);
   __syncthreads();
-  for (int k0 = 0; k0 < nk; k0 += PD) {
+  for (int k0 = 0; k0 < nkr; k0 += PD) {
     static_for<0, PD>([&](auto j) {
       constexpr int J = decltype(j)::value;
       const int k = k0 + J;
-      if (k < nk) {  // uniform over the block
-        if (k + PD < nk) {
-          load((k + PD) * GK, ra[J], rb[J], sc[J], tk[J], gk[J]);
-          lookup((k + 2 * PD) * GK, tk[J], gk[J]);
-        }
-        compute(k & 1);
-        constexpr int N1 = (J + 1) % PD;
-        if (k + 1 < nk) store((k + 1) & 1, ra[N1], rb[N1], sc[N1]);
-        __syncthreads();
-      }
+      load((k + PD) * GK, ra[J], rb[J], sc[J], tk[J], gk[J]);
+      lookup((k + 2 * PD) * GK, tk[J], gk[J]);
+      __builtin_amdgcn_sched_barrier(0);  // the loads go out before this step's work
+      compute(k & 1);
+      constexpr int N1 = (J + 1) % PD;
+      store((k + 1) & 1, ra[N1], rb[N1], sc[N1]);
+      lds_barrier();  // LDS only: the later steps' loads stay in flight
     });
   }
 
@@ -306,76 +250,8 @@ bwd_gemm_kernel(BwdGemmArgs g) {
       fn(idx >> 4, (idx & 15) * 8);
     }
   };
-  if constexpr (KIND == 1) {
-    // H tile into LDS; then dA = g Q [H > 0] in place of it and the tile's
-    // partial dg = sum_n Q H per row; then dA out in row chunks.
-    const __amdgpu_buffer_rsrc_t h_src =
-        make_rsrc(g.H + (size_t)rbeg * g.F, (uint32_t)Ae * (uint32_t)g.F * 2u);
-    tile_io([&](int row, int col) {
-      const int r = m0 + row, n = n0 + col;
-      store16(&stg[row * SP + col],
-              buffer_load16(h_src, (r < Ae && n < g.F) ? ((uint32_t)r * (uint32_t)g.F + (uint32_t)n) * 2u
-                                                        : kOob));
-    });
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int ml = wm * 64 + 32 * i + lr;
-      const int r = m0 + ml;
-      const float gate = r < Ae ? g.rowgate[rbeg + r] : 0.f;
-      float part = 0.f;
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-#pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          u32x2* p = reinterpret_cast<u32x2*>(&stg[ml * SP + wn * 64 + 32 * j + 8 * gq + 4 * khalf]);
-          const u32x2 hv = *p;
-          float da[4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float h = bf16_bits_to_f32((hv[q >> 1] >> (16 * (q & 1))) & 0xffffu);
-            const float qv = acc[i][j][4 * gq + q];
-            part += qv * h;
-            da[q] = h > 0.f ? gate * qv : 0.f;
-          }
-          *p = u32x2{pack_bf16x2(da[0], da[1]), pack_bf16x2(da[2], da[3])};
-        }
-      }
-      part += __shfl_xor(part, 32);
-      // the two column halves of the tile (waves wn = 0, 1) meet in LDS
-      if (wn == 1 && khalf == 0) red[ml] = part;
-      __syncthreads();
-      if (wn == 0 && khalf == 0 && r < Ae)
-        g.dgp[(size_t)nt * g.max_rows + rbeg + r] = part + red[ml];
-    }
-    __syncthreads();
-    uint16_t* dA = reinterpret_cast<uint16_t*>(g.out) + (size_t)rbeg * g.F;
-    tile_io([&](int row, int col) {
-      const int r = m0 + row, n = n0 + col;
-      if (r < Ae && n < g.F) store16(dA + (size_t)r * g.F + n, load16(&stg[row * SP + col]));
-    });
-  } else if constexpr (KIND == 2) {
-    // expert part of dx, fp32, at the token's row
-    float* dxe = reinterpret_cast<float*>(g.out);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int r = m0 + wm * 64 + 32 * i + lr;
-      if (r >= Ae) continue;
-      float* row = dxe + (size_t)g.row2tok[rbeg + r] * g.d;
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-#pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          const int n = n0 + wn * 64 + 32 * j + 8 * gq + 4 * khalf;
-          if (n < g.d)
-            *reinterpret_cast<f32x4*>(row + n) =
-                f32x4{acc[i][j][4 * gq], acc[i][j][4 * gq + 1], acc[i][j][4 * gq + 2],
-                      acc[i][j][4 * gq + 3]};
-        }
-      }
-    }
-  } else {
-    // dW2_e [d][F] (E3) or dW1_e [F][d] (E4), bf16, staged and written in row chunks
+  // dW2_e [d][F] (E3) or dW1_e [F][d] (E4), bf16, staged and written in row chunks
+  {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int ml = wm * 64 + 32 * i + lr;
@@ -395,6 +271,210 @@ bwd_gemm_kernel(BwdGemmArgs g) {
       const int m = m0 + row, n = n0 + col;
       if (m < M && n < Nn) store16(out + (size_t)m * Nn + n, load16(&stg[row * SP + col]));
     });
+  }
+}
+
+// ---------------------------------------------------------------------------
+// E1 and E2 with a whole row chunk per tile: a block computes R = 32 MT rows
+// of one expert (all of its rows when C <= 160) against 128 output columns,
+// wave w taking columns 32 w .. 32 w + 31 of every row.  A weight tile then
+// streams once per row chunk instead of once per 128 rows, and no tile is
+// mostly empty.  Operands as in bwd_gemm_kernel: A [rows][k] in LDS (one
+// 16-byte fragment read), the weights [k][n] read as fragments by transposing
+// reads.
+//   E1: Q = dY_g W2_e  (K = d),  epilogue dA = g Q [H > 0] and partial dg
+//   E2: dXe = dA W1_e  (K = F),  fp32 rows at the tokens
+// ---------------------------------------------------------------------------
+struct BwdRowsArgs {
+  const uint16_t* a;   // E1: dy [T][d] (rows through row2tok); E2: dA [max_rows][F]
+  const uint16_t* w;   // E1: W2 [N][d][F]; E2: W1 [N][F][d]
+  const int* offset;
+  const int* row2tok;
+  const float* rowgate;
+  const uint16_t* H;
+  void* out;           // E1: dA [max_rows][F]; E2: dXe [T][d] fp32
+  float* dgp;
+  int T, d, F, max_rows, n_mc;  // n_mc: row chunks per expert
+};
+
+template <int KIND, int MT, int PD>
+__global__ void __launch_bounds__(256)
+bwd_rows_kernel(BwdRowsArgs g) {
+  constexpr int R = 32 * MT;
+  constexpr int AI = (R * 4 + 255) / 256;  // A loads per thread and step (16 bytes each)
+  constexpr int SP = GN + 8;               // staged tile pitch (bf16)
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * R * GP + 2 * GK * RP];
+  __shared__ float red[4][R];
+  static_assert(R * SP <= 2 * R * GP + 2 * GK * RP, "staged tile fits the rings");
+  uint16_t (*As)[R][GP] = reinterpret_cast<uint16_t (*)[R][GP]>(lds);
+  uint16_t* const Bs = lds + 2 * R * GP;   // two [GK][RP] tiles
+  uint16_t* const stg = lds;
+
+  const int Nn = KIND == 1 ? g.F : g.d;
+  const int Kfull = KIND == 1 ? g.d : g.F;
+  const int n_nt = (Nn + GN - 1) / GN;
+  const int tile = xcd_contiguous_tile(blockIdx.x, gridDim.x);
+  const int nt = tile % n_nt;
+  const int mc = (tile / n_nt) % g.n_mc;
+  const int e = tile / (n_nt * g.n_mc);
+  const int rbeg = g.offset[e];
+  const int Ae = g.offset[e + 1] - rbeg;
+  const int m0 = mc * R, n0 = nt * GN;
+  if (m0 >= Ae) return;  // uniform over the block
+  const int kend = Kfull;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int khalf = lane >> 5;
+
+  // A: chunk c = tid + 256 i is 16-byte chunk c % 4 (of the k-step) of tile row c / 4.
+  __amdgpu_buffer_rsrc_t a_src;
+  uint32_t a_off[AI];
+  if constexpr (KIND == 1) a_src = make_rsrc(g.a, (uint32_t)g.T * (uint32_t)g.d * 2u);
+  else a_src = make_rsrc(g.a + (size_t)rbeg * g.F, (uint32_t)Ae * (uint32_t)g.F * 2u);
+#pragma unroll
+  for (int i = 0; i < AI; ++i) {
+    const int c = tid + 256 * i;
+    const int r = m0 + (c >> 2);
+    const bool ok = c < R * 4 && r < Ae;
+    const uint32_t row = KIND == 1 ? (ok ? (uint32_t)g.row2tok[rbeg + r] : 0u) : (uint32_t)r;
+    a_off[i] = ok ? row * (uint32_t)(KIND == 1 ? g.d : g.F) * 2u : kOob;  // the row's start
+  }
+  // B: k rows tid/16 + {0, 16} of the step, chunk tid % 16 of the 128 columns.
+  const int kr = tid >> 4, pc = tid & 15;
+  const int nb = n0 + pc * 8;
+  const __amdgpu_buffer_rsrc_t b_src =
+      make_rsrc(g.w + (size_t)e * g.d * g.F, (uint32_t)((size_t)g.d * g.F * 2));
+
+  u32x4 ra[PD][AI], rb[PD][2];
+  auto load = [&](int k0, u32x4 (&a)[AI], u32x4 (&b)[2]) {
+#pragma unroll
+    for (int i = 0; i < AI; ++i) {
+      const int kc = k0 + ((tid + 256 * i) & 3) * 8;
+      a[i] = buffer_load16(a_src, kc < kend ? a_off[i] + (uint32_t)kc * 2u : kOob);
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int kk = k0 + kr + 16 * q;
+      b[q] = buffer_load16(b_src, (kk < kend && nb < Nn)
+                                      ? ((uint32_t)kk * (uint32_t)Nn + (uint32_t)nb) * 2u : kOob);
+    }
+  };
+  auto store = [&](int buf, const u32x4 (&a)[AI], const u32x4 (&b)[2]) {
+#pragma unroll
+    for (int i = 0; i < AI; ++i) {
+      const int c = tid + 256 * i;
+      if (c < R * 4) store16(&As[buf][c >> 2][(c & 3) * 8], a[i]);
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q) store16(Bs + buf * GK * RP + (kr + 16 * q) * RP + pc * 8, b[q]);
+  };
+
+  f32x16 acc[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) acc[m] = f32x16{};
+  auto compute = [&](int buf) {
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+      const bf16x8 fb = tr_fragment(Bs + buf * GK * RP, kh * 16, 32 * wave, lane);
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        const bf16x8 fa = as_bf16x8(load16(&As[buf][32 * m + (lane & 31)][kh * 16 + khalf * 8]));
+        acc[m] = mfma_32x32x16(fb, fa, acc[m]);
+      }
+    }
+  };
+
+  // The k-loop as in bwd_gemm_kernel: PD steps in flight in registers, whole
+  // rounds, no branches (steps past the end of K read zeros).
+  const int nk = (kend + GK - 1) / GK;
+  const int nkr = (nk + PD - 1) / PD * PD;
+  static_for<0, PD>([&](auto j) { load(j * GK, ra[j], rb[j]); });
+  store(0, ra[0], rb[0]);
+  __syncthreads();
+  for (int k0 = 0; k0 < nkr; k0 += PD) {
+    static_for<0, PD>([&](auto j) {
+      constexpr int J = decltype(j)::value;
+      const int k = k0 + J;
+      load((k + PD) * GK, ra[J], rb[J]);
+      __builtin_amdgcn_sched_barrier(0);  // the loads go out before this step's work
+      compute(k & 1);
+      constexpr int N1 = (J + 1) % PD;
+      store((k + 1) & 1, ra[N1], rb[N1]);
+      lds_barrier();  // LDS only: the later steps' loads stay in flight
+    });
+  }
+
+  // Lane values: row 32 m + lane % 32 of the tile; for value 4 gq + q,
+  // column 32 wave + 8 gq + 4 khalf + q.
+  const int lr = lane & 31;
+  if constexpr (KIND == 1) {
+    // H tile into LDS; dA = g Q [H > 0] in place of it and each wave's partial
+    // dg (its 32 columns) per row; the four waves' partials summed in wave
+    // order; then dA out in row chunks.
+    const __amdgpu_buffer_rsrc_t h_src =
+        make_rsrc(g.H + (size_t)rbeg * g.F, (uint32_t)Ae * (uint32_t)g.F * 2u);
+#pragma unroll
+    for (int c = 0; c < 2 * MT; ++c) {
+      const int idx = tid + 256 * c;
+      const int row = idx >> 4, col = (idx & 15) * 8;
+      const int r = m0 + row, n = n0 + col;
+      store16(&stg[row * SP + col],
+              buffer_load16(h_src, (r < Ae && n < g.F) ? ((uint32_t)r * (uint32_t)g.F + (uint32_t)n) * 2u
+                                                        : kOob));
+    }
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      const int ml = 32 * m + lr;
+      const int r = m0 + ml;
+      const float gate = r < Ae ? g.rowgate[rbeg + r] : 0.f;
+      float part = 0.f;
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        u32x2* p = reinterpret_cast<u32x2*>(&stg[ml * SP + 32 * wave + 8 * gq + 4 * khalf]);
+        const u32x2 hv = *p;
+        float da[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float h = bf16_bits_to_f32((hv[q >> 1] >> (16 * (q & 1))) & 0xffffu);
+          const float qv = acc[m][4 * gq + q];
+          part += qv * h;
+          da[q] = h > 0.f ? gate * qv : 0.f;
+        }
+        *p = u32x2{pack_bf16x2(da[0], da[1]), pack_bf16x2(da[2], da[3])};
+      }
+      part += __shfl_xor(part, 32);
+      if (khalf == 0) red[wave][ml] = part;
+    }
+    __syncthreads();
+    if (tid < R && m0 + tid < Ae)
+      g.dgp[(size_t)nt * g.max_rows + rbeg + m0 + tid] =
+          ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
+    uint16_t* dA = reinterpret_cast<uint16_t*>(g.out) + (size_t)rbeg * g.F;
+#pragma unroll
+    for (int c = 0; c < 2 * MT; ++c) {
+      const int idx = tid + 256 * c;
+      const int row = idx >> 4, col = (idx & 15) * 8;
+      const int r = m0 + row, n = n0 + col;
+      if (r < Ae && n < g.F) store16(dA + (size_t)r * g.F + n, load16(&stg[row * SP + col]));
+    }
+  } else {
+    float* dxe = reinterpret_cast<float*>(g.out);
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      const int r = m0 + 32 * m + lr;
+      if (r >= Ae) continue;
+      float* row = dxe + (size_t)g.row2tok[rbeg + r] * g.d;
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const int n = n0 + 32 * wave + 8 * gq + 4 * khalf;
+        if (n < g.d)
+          *reinterpret_cast<f32x4*>(row + n) =
+              f32x4{acc[m][4 * gq], acc[m][4 * gq + 1], acc[m][4 * gq + 2], acc[m][4 * gq + 3]};
+      }
+    }
   }
 }
 
@@ -789,6 +869,27 @@ int bwd_wr_parts(const Shape& s) {
   return parts < 1 ? 1 : parts;
 }
 
+// Row tiles (of 32 rows) per E1/E2 block: the capacity's tiles split into as
+// few chunks of at most 5 as possible, evenly.
+static int bwd_rows_mt(int C) {
+  const int tiles = C <= 0 ? 1 : (C + 31) / 32;
+  const int chunks = (tiles + 4) / 5;
+  return (tiles + chunks - 1) / chunks;
+}
+
+template <int KIND>
+static hipError_t launch_rows(const BwdRowsArgs& g, int mt, int blocks, hipStream_t st) {
+  constexpr int PD = SFFN_BWD_PD_ROWS;
+  switch (mt) {
+    case 1: hipLaunchKernelGGL((bwd_rows_kernel<KIND, 1, PD>), dim3((unsigned)blocks), dim3(256), 0, st, g); break;
+    case 2: hipLaunchKernelGGL((bwd_rows_kernel<KIND, 2, PD>), dim3((unsigned)blocks), dim3(256), 0, st, g); break;
+    case 3: hipLaunchKernelGGL((bwd_rows_kernel<KIND, 3, PD>), dim3((unsigned)blocks), dim3(256), 0, st, g); break;
+    case 4: hipLaunchKernelGGL((bwd_rows_kernel<KIND, 4, PD>), dim3((unsigned)blocks), dim3(256), 0, st, g); break;
+    default: hipLaunchKernelGGL((bwd_rows_kernel<KIND, 5, PD>), dim3((unsigned)blocks), dim3(256), 0, st, g); break;
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_backward(const Shape& s, const Inputs& in, const BwdState& b, hipStream_t st,
                            void* const* ev) {
   int stage = 0;
@@ -806,14 +907,12 @@ hipError_t launch_backward(const Shape& s, const Inputs& in, const BwdState& b, 
 
   // 2. E1: dA and partial dg
   SFFN_CHECK(mark());
-  const int mt_max = (s.C + GM - 1) / GM;
+  const int mt = bwd_rows_mt(s.C), n_mc = (s.C + 32 * mt - 1) / (32 * mt);
   if (s.C > 0) {
     if (bf16) {
-      BwdGemmArgs g{(const uint16_t*)b.dy, (const uint16_t*)in.W2, b.offset, b.row2tok, b.rowgate,
-                    (const uint16_t*)b.H, b.dA, b.dgp, s.T, s.d, s.F, s.max_rows, mt_max};
-      const int blocks = s.N * mt_max * ((s.F + GN - 1) / GN);
-      hipLaunchKernelGGL((bwd_gemm_kernel<1, SFFN_BWD_PD_ROWS>), dim3((unsigned)blocks), dim3(256),
-                         0, st, g);
+      BwdRowsArgs g{(const uint16_t*)b.dy, (const uint16_t*)in.W2, b.offset, b.row2tok, b.rowgate,
+                    (const uint16_t*)b.H, b.dA, b.dgp, s.T, s.d, s.F, s.max_rows, n_mc};
+      SFFN_CHECK(launch_rows<1>(g, mt, s.N * n_mc * ((s.F + GN - 1) / GN), st));
     } else {
       hipLaunchKernelGGL(bwd_e1_f32_kernel, dim3((unsigned)((n_rows + 255) / 256)), dim3(256), 0,
                          st, (const float*)b.dy, (const float*)in.W2, b.offset, b.row2tok,
@@ -843,11 +942,9 @@ hipError_t launch_backward(const Shape& s, const Inputs& in, const BwdState& b, 
   SFFN_CHECK(mark());
   if (s.C > 0) {
     if (bf16) {
-      BwdGemmArgs g{(const uint16_t*)b.dA, (const uint16_t*)in.W1, b.offset, b.row2tok, b.rowgate,
-                    nullptr, b.dxe, nullptr, s.T, s.d, s.F, s.max_rows, mt_max};
-      const int blocks = s.N * mt_max * ((s.d + GN - 1) / GN);
-      hipLaunchKernelGGL((bwd_gemm_kernel<2, SFFN_BWD_PD_ROWS>), dim3((unsigned)blocks), dim3(256),
-                         0, st, g);
+      BwdRowsArgs g{(const uint16_t*)b.dA, (const uint16_t*)in.W1, b.offset, b.row2tok, b.rowgate,
+                    nullptr, b.dxe, nullptr, s.T, s.d, s.F, s.max_rows, n_mc};
+      SFFN_CHECK(launch_rows<2>(g, mt, s.N * n_mc * ((s.d + GN - 1) / GN), st));
     } else {
       const long n = (long)n_rows * s.d;
       hipLaunchKernelGGL(bwd_e2_f32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
@@ -894,13 +991,13 @@ hipError_t launch_backward(const Shape& s, const Inputs& in, const BwdState& b, 
   SFFN_CHECK(mark());
   if (bf16) {
     BwdGemmArgs g3{(const uint16_t*)b.dy, (const uint16_t*)b.H, b.offset, b.row2tok, b.rowgate,
-                   nullptr, b.dW2, nullptr, s.T, s.d, s.F, s.max_rows, 0};
+                   b.dW2, s.T, s.d, s.F};
     const int t3 = ((s.d + GM - 1) / GM) * ((s.F + GN - 1) / GN);
     hipLaunchKernelGGL((bwd_gemm_kernel<3, SFFN_BWD_PD_WGRAD>), dim3((unsigned)(s.N * t3)),
                        dim3(256), 0, st, g3);
     SFFN_CHECK(hipGetLastError());
     BwdGemmArgs g4{(const uint16_t*)b.dA, (const uint16_t*)in.x, b.offset, b.row2tok, b.rowgate,
-                   nullptr, b.dW1, nullptr, s.T, s.d, s.F, s.max_rows, 0};
+                   b.dW1, s.T, s.d, s.F};
     const int t4 = ((s.F + GM - 1) / GM) * ((s.d + GN - 1) / GN);
     hipLaunchKernelGGL((bwd_gemm_kernel<4, SFFN_BWD_PD_WGRAD>), dim3((unsigned)(s.N * t4)),
                        dim3(256), 0, st, g4);

@@ -33,7 +33,9 @@ def _host(t):
     return t.float().cpu().numpy().astype(np.float64)
 
 
-def _case(w, d_aux=0.37, sampled=False, twice=False):
+def _case(w, d_aux=0.37, sampled=False, twice=False, expert_dx=False):
+    """expert_dx: also hold dx - dy (the expert and router terms) to the tolerance; for
+    weights large enough that those terms are not lost in dy's rounding."""
     import torch
 
     import sparse_mixture_experts_switchffn_amd as sffn
@@ -79,6 +81,8 @@ def _case(w, d_aux=0.37, sampled=False, twice=False):
     rows = np.nonzero(np.all(np.isfinite(ref["dx"]), axis=1))[0]
     assert rows.size > 0
     errs["dx"] = rel_l2(_host(g["dx"])[rows], ref["dx"][rows])
+    if expert_dx:
+        errs["dx-dy"] = rel_l2(_host(g["dx"])[rows] - dy64[rows], ref["dx"][rows] - dy64[rows])
     todo = range(w.N) if only is None else only
     for k in ("dW1", "dW2", "db1", "db2"):
         if g[k] is None:
@@ -114,6 +118,17 @@ def test_backward_fp32(case):
 ])
 def test_backward_bf16(case):
     _case(synth.workload("switch_base").replace(**case), twice=True)
+
+
+@pytest.mark.parametrize("case", [
+    dict(T=300, d=72, F=136, N=6, CF=1.0, bias_sigma=0.02, w_sigma=0.2),   # ragged tails
+    dict(T=700, d=128, F=640, N=8, CF=1.0, bias_sigma=0.02, w_sigma=0.1),  # 20 k-steps of E2
+    dict(T=2000, d=64, F=520, N=4, CF=1.25, w_sigma=0.15),                 # 4 row chunks, K tail
+])
+def test_backward_expert_dx(case):
+    """Weights large enough that dx - dy (W1^T dA + Wr^T dz) is of the size of dy, so that
+    an error in the expert or router part of dx cannot hide in dy's rounding."""
+    _case(synth.workload("switch_base").replace(**case), twice=True, expert_dx=True)
 
 
 @pytest.mark.parametrize("case", [
