@@ -799,6 +799,159 @@ bwd_router_gemm_kernel(const float* __restrict__ dz, const float* __restrict__ W
   }
 }
 
+// ---------------------------------------------------------------------------
+// Partial dWr of the bf16 layer on the bf16 matrix cores: part p holds
+// sum over its tokens t of dz_t^T x_t.  dz is split exactly into three bf16
+// planes (dz = hi + mid + lo, each the round-to-nearest of what is left, as
+// the router splits Wr in the forward pass) and x is bf16, so every product
+// is exact and the sums run in fp32: an fp32 GEMM up to summation order, at
+// the bf16 rate (three bf16 products per fp32 one).  Block tile 128 experts
+// x 128 columns, four waves of 64 x 64; per k-step of 32 tokens the three dz
+// planes and x are [k][inner] LDS tiles read by transposing reads.
+// ---------------------------------------------------------------------------
+template <int PD>
+__global__ void __launch_bounds__(256)
+bwd_wr_bf16_kernel(const float* __restrict__ dz, const uint16_t* __restrict__ x, int T, int d,
+                   int N, int tokens_per_part, float* __restrict__ part_out) {
+  constexpr int TILE = GK * RP;                // one [GK][RP] bf16 tile
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * 4 * TILE];  // per buffer: 3 planes, x
+  const int n_nt = (d + 127) / 128, n_mt = (N + 127) / 128;
+  const int bid = blockIdx.x;
+  const int part = bid / (n_mt * n_nt);
+  const int mt = (bid / n_nt) % n_mt, nt = bid % n_nt;
+  const int m0 = mt * 128, n0 = nt * 128;
+  const int kbeg = part * tokens_per_part;
+  const int kend = min(T, kbeg + tokens_per_part);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave & 1, wn = wave >> 1, khalf = lane >> 5;
+
+  // dz: thread k row tid/8, experts m0 + 16 (tid % 8) .. +15 (four 4-float
+  // chunks).  x: k rows tid/16 + {0, 16}, 16-byte chunk tid % 16.
+  const int ak = tid >> 3, am = m0 + 16 * (tid & 7);
+  const int kr = tid >> 4, pc = tid & 15, nb = n0 + pc * 8;
+  const bool nvec = (N & 3) == 0;
+  const __amdgpu_buffer_rsrc_t z_src = make_rsrc(dz, (uint32_t)((size_t)T * N * 4));
+  const __amdgpu_buffer_rsrc_t x_src = make_rsrc(x, (uint32_t)((size_t)T * d * 2));
+
+  u32x4 ra[PD][4], rb[PD][2];
+  auto load = [&](int k0, u32x4 (&a)[4], u32x4 (&b)[2]) {
+    const int t = kbeg + k0 + ak;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int m = am + 4 * c;
+      const uint32_t off = ((uint32_t)t * (uint32_t)N + (uint32_t)m) * 4u;
+      if (nvec) {
+        a[c] = buffer_load16(z_src, (t < kend && m < N) ? off : kOob);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          a[c][e] = buffer_load4(z_src, (t < kend && m + e < N) ? off + 4u * (uint32_t)e : kOob);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int tt = kbeg + k0 + kr + 16 * q;
+      b[q] = buffer_load16(x_src, (tt < kend && nb < d) ? ((uint32_t)tt * (uint32_t)d + (uint32_t)nb) * 2u
+                                                         : kOob);
+    }
+  };
+  auto store = [&](int buf, const u32x4 (&a)[4], const u32x4 (&b)[2]) {
+    uint16_t* base = lds + buf * 4 * TILE;
+    uint32_t pl[3][8];  // packed bf16 pairs of each plane
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+#pragma unroll
+      for (int e = 0; e < 4; e += 2) {
+        uint32_t h[2], mi[2], lo[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const float w = __uint_as_float(a[c][e + u]);
+          h[u] = f32_to_bf16_bits(w);
+          const float r1 = w - bf16_bits_to_f32(h[u]);
+          mi[u] = f32_to_bf16_bits(r1);
+          lo[u] = f32_to_bf16_bits(r1 - bf16_bits_to_f32(mi[u]));
+        }
+        pl[0][2 * c + e / 2] = h[0] | (h[1] << 16);
+        pl[1][2 * c + e / 2] = mi[0] | (mi[1] << 16);
+        pl[2][2 * c + e / 2] = lo[0] | (lo[1] << 16);
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < 3; ++p) {
+      uint16_t* row = base + p * TILE + ak * RP + 16 * (tid & 7);
+      store16(row, u32x4{pl[p][0], pl[p][1], pl[p][2], pl[p][3]});
+      store16(row + 8, u32x4{pl[p][4], pl[p][5], pl[p][6], pl[p][7]});
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q) store16(base + 3 * TILE + (kr + 16 * q) * RP + pc * 8, b[q]);
+  };
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+  auto compute = [&](int buf) {
+    const uint16_t* base = lds + buf * 4 * TILE;
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+      bf16x8 fb[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) fb[j] = tr_fragment(base + 3 * TILE, kh * 16, wn * 64 + 32 * j, lane);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        if (m0 + wm * 64 + 32 * i >= N) continue;  // uniform over the wave: experts past N
+#pragma unroll
+        for (int p = 2; p >= 0; --p) {  // smallest plane first
+          const bf16x8 fa = tr_fragment(base + p * TILE, kh * 16, wm * 64 + 32 * i, lane);
+#pragma unroll
+          for (int j = 0; j < 2; ++j) acc[i][j] = mfma_32x32x16(fb[j], fa, acc[i][j]);
+        }
+      }
+    }
+  };
+
+  // k-loop as in bwd_gemm_kernel: PD steps in flight, whole rounds, no branches.
+  const int nk = (kend - kbeg + GK - 1) / GK;
+  const int nkr = nk <= 0 ? 0 : (nk + PD - 1) / PD * PD;
+  static_for<0, PD>([&](auto j) { load(j * GK, ra[j], rb[j]); });
+  store(0, ra[0], rb[0]);
+  __syncthreads();
+  for (int k0 = 0; k0 < nkr; k0 += PD) {
+    static_for<0, PD>([&](auto j) {
+      constexpr int J = decltype(j)::value;
+      const int k = k0 + J;
+      load((k + PD) * GK, ra[J], rb[J]);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(k & 1);
+      constexpr int N1 = (J + 1) % PD;
+      store((k + 1) & 1, ra[N1], rb[N1]);
+      lds_barrier();
+    });
+  }
+
+  // lane: expert m0 + wm*64 + 32 i + lane % 32; columns n0 + wn*64 + 32 j +
+  // 8 gq + 4 khalf + q (d % 8 == 0: a group of four is in range as a whole).
+  const int lr = lane & 31;
+  float* out = part_out + (size_t)part * N * d;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int m = m0 + wm * 64 + 32 * i + lr;
+    if (m >= N) continue;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const int n = n0 + wn * 64 + 32 * j + 8 * gq + 4 * khalf;
+        if (n < d)
+          *reinterpret_cast<f32x4*>(out + (size_t)m * d + n) =
+              f32x4{acc[i][j][4 * gq], acc[i][j][4 * gq + 1], acc[i][j][4 * gq + 2],
+                    acc[i][j][4 * gq + 3]};
+      }
+    }
+  }
+}
+
 // dWr = sum over parts, in part order.
 __global__ void __launch_bounds__(256)
 bwd_wr_reduce_kernel(const float* __restrict__ part, int parts, long n, float* __restrict__ out) {
@@ -973,7 +1126,12 @@ hipError_t launch_backward(const Shape& s, const Inputs& in, const BwdState& b, 
     const int parts = b.n_wr_parts;
     const int per = ((s.T + parts - 1) / parts + FK - 1) / FK * FK;
     const int blocks = parts * ((s.N + 127) / 128) * ((s.d + 127) / 128);
-    if (bf16)
+    // bf16 planes while dz's byte offsets stay below 2^31 (the out-of-range
+    // placeholder offset must lie past the buffer)
+    if (bf16 && (size_t)s.T * s.N * 4 < ((size_t)1 << 31))
+      hipLaunchKernelGGL((bwd_wr_bf16_kernel<2>), dim3((unsigned)blocks), dim3(256), 0, st, b.dz,
+                         (const uint16_t*)in.x, s.T, s.d, s.N, per, b.wrp);
+    else if (bf16)
       hipLaunchKernelGGL((bwd_router_gemm_kernel<true, true>), dim3((unsigned)blocks), dim3(256),
                          0, st, b.dz, in.Wr, in.x, b.dy, b.dxe, b.slot, s.T, s.d, s.N, per, b.wrp);
     else
