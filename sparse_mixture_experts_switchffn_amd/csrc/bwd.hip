@@ -629,8 +629,10 @@ bwd_router_gemm_kernel(const float* __restrict__ dz, const float* __restrict__ W
                        int d, int N, int tokens_per_part, void* __restrict__ outv) {
   // DX: A = dz [T][N] kept as [m][k]; B = Wr [N][d] as [k][n].
   // DWR: A = dz^T, kept as [k][m] (dz rows); B = x [T][d] as [k][n].
-  __shared__ float As[DWR ? FK * FPB : 128 * FPA];
-  __shared__ float Bs[FK * FPB];
+  // [A | B] operand tiles; the dx epilogue stages its tile over them.
+  __shared__ __attribute__((aligned(16))) float smem[(DWR ? FK * FPB : 128 * FPA) + FK * FPB];
+  float* const As = smem;
+  float* const Bs = smem + (DWR ? FK * FPB : 128 * FPA);
   const int Mdim = DWR ? N : T;
   const int n_nt = (d + 127) / 128;
   const int n_mt = (Mdim + 127) / 128;
@@ -737,8 +739,58 @@ bwd_router_gemm_kernel(const float* __restrict__ dz, const float* __restrict__ W
   }
 
   // Lane values: row m0 + wm*64 + 32 i + lr, four consecutive columns per gq.
-  // With d % 4 == 0 each group moves as one vector access.
   const int lr = lane & 31, khalf = lane >> 5;
+  if constexpr (BF16 && !DWR) {
+    // dx of the bf16 layer: the tile leaves through LDS in two halves of 64
+    // rows (over the operand tiles), then each thread takes 8-column row
+    // chunks, coalesced: dx = acc + dXe (accepted tokens) + dy, rounded once
+    // (d % 8 == 0: a chunk is in range as a whole).
+    constexpr int STP = 128 + 4;  // staged row pitch (floats)
+    static_assert(64 * STP <= 128 * FPA + FK * FPB, "staged half tile fits the operand tiles");
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if (wm == h) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq)
+              *reinterpret_cast<f32x4*>(smem + (32 * i + lr) * STP + wn * 64 + 32 * j + 8 * gq +
+                                        4 * khalf) =
+                  f32x4{acc[i][j][4 * gq], acc[i][j][4 * gq + 1], acc[i][j][4 * gq + 2],
+                        acc[i][j][4 * gq + 3]};
+      }
+      __syncthreads();
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int idx = tid + 256 * c;
+        const int row = idx >> 4, col = (idx & 15) * 8;
+        const int m = m0 + 64 * h + row, n = n0 + col;
+        if (m >= T || n >= d) continue;
+        const float* sp = smem + row * STP + col;
+        f32x4 v0 = *reinterpret_cast<const f32x4*>(sp);
+        f32x4 v1 = *reinterpret_cast<const f32x4*>(sp + 4);
+        const size_t o = (size_t)m * d + n;
+        if (slot[m] >= 0) {
+          const f32x4 e0 = *reinterpret_cast<const f32x4*>(dxe + o);
+          const f32x4 e1 = *reinterpret_cast<const f32x4*>(dxe + o + 4);
+          v0 = f32x4{v0[0] + e0[0], v0[1] + e0[1], v0[2] + e0[2], v0[3] + e0[3]};
+          v1 = f32x4{v1[0] + e1[0], v1[1] + e1[1], v1[2] + e1[2], v1[3] + e1[3]};
+        }
+        const u32x4 yb = *reinterpret_cast<const u32x4*>((const uint16_t*)dyv + o);
+        const float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+        u32x4 r;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          r[q] = pack_bf16x2(v[2 * q] + bf16_bits_to_f32(yb[q] & 0xffffu),
+                             v[2 * q + 1] + bf16_bits_to_f32(yb[q] >> 16));
+        *reinterpret_cast<u32x4*>((uint16_t*)outv + o) = r;
+      }
+      __syncthreads();
+    }
+    return;
+  }
   const bool vec = (d & 3) == 0;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
