@@ -269,7 +269,11 @@ bwd_gemm_kernel(BwdGemmArgs g) {
     uint16_t* out = reinterpret_cast<uint16_t*>(g.out) + (size_t)e * g.d * g.F;
     tile_io([&](int row, int col) {
       const int m = m0 + row, n = n0 + col;
-      if (m < M && n < Nn) store16(out + (size_t)m * Nn + n, load16(&stg[row * SP + col]));
+      // stored non-temporal: nothing here reads the gradients again, and their
+      // dirty lines would otherwise crowd the caches for the next kernels
+      if (m < M && n < Nn)
+        __builtin_nontemporal_store(load16(&stg[row * SP + col]),
+                                    reinterpret_cast<u32x4*>(out + (size_t)m * Nn + n));
     });
   }
 }
