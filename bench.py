@@ -290,8 +290,10 @@ def cpu_baseline(w, budget_s, args):
         if el >= budget_s or passes >= 1000:
             break
     log(args, f"cpu_baseline: {passes} passes in {el:.2f} s")
+    kind = "forward + backward" if getattr(args, "backward", False) else "forward"
+
     return {"value": w.T * passes / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{passes} full forward pass(es) of the {w.name} workload "
+            "sample": f"{passes} full {kind} pass(es) of the {w.name} workload "
                       f"(T={w.T}) in float64 numpy, {el:.1f} s"}
 
 
