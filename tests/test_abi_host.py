@@ -55,6 +55,15 @@ def test_stage_names():
     assert S.switch_ffn_stage_name(n) is None and S.switch_ffn_stage_name(-1) is None
 
 
+def test_backward_stage_names():
+    n = S.switch_ffn_backward_num_stages()
+    names = [S.switch_ffn_backward_stage_name(i) for i in range(n)]
+    assert names == ["expert_dgrad_hidden", "router_grad", "expert_dgrad_input", "dx",
+                     "router_wgrad", "expert_wgrad", "bias_grad"]
+    assert S.switch_ffn_backward_stage_name(n) is None
+    assert S.switch_ffn_backward_stage_name(-1) is None
+
+
 def _call(**over):
     # Fake, never-dereferenced addresses: every case below must be rejected before
     # anything touches a device.
