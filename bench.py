@@ -173,13 +173,13 @@ def algorithmic_bytes(w, stage, accepted, active, esize, dropped=0, k=1, reroute
           written + b1 + the row-to-token map.
     ffn2: W2 of active experts + H rows + the x rows of the residual + the y rows
           written + b2 + gate and row-to-token entries.
-    Top-2 (k = 2): A counts accepted choices; the router always stages the logits and
+    Top-2 (k = 2): A counts accepted choices; the router (fused or tiled as above)
     writes two choices, gates and ranks per token; dispatch_scatter copies no rows;
     ffn2 writes the gate-scaled expert rows and its stage also holds the combine
     (x and those rows read once, y written).
     GEGLU experts: ffn1 reads both up-projections (2F rows of W1 and of b1).
-    Rerouting (k = 1): the router stages the logits and writes both choices and gates
-    and the first-choice rank per token; dispatch_scan also reads the choices and
+    Rerouting (k = 1): the router writes both choices and gates and the first-choice
+    rank per token; dispatch_scan also reads the choices and
     ranks again, writes the first-stage slot and the overflow ranks and scans the
     overflow counts; dispatch_scatter reads both choices and gates, the first-stage
     slot and the overflow rank, and writes expert, gate and slot per token.
