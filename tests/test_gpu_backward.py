@@ -135,6 +135,7 @@ def test_backward_expert_dx(case):
     dict(T=1, d=64, F=128, N=4, CF=4.0, bias_sigma=0.02),      # one token
     dict(T=256, d=64, F=96, N=1, CF=1.0, bias_sigma=0.02),     # N = 1: dense FFN, dz = 0
     dict(T=130, d=40, F=200, N=3, CF=1.0),                     # K tails of every GEMM
+    dict(T=500, d=96, F=128, N=6, CF=1.25, bias_sigma=0.02),   # weight rows off the line grid
 ])
 def test_backward_edges(case):
     _case(synth.workload("switch_base").replace(**case), twice=True)
