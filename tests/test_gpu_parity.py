@@ -163,3 +163,37 @@ def test_deterministic():
     for k in ("expert_idx", "slot", "gate", "y_bits"):
         assert np.array_equal(a[k], b[k]), k
     assert a["aux_loss"] == b["aux_loss"]
+
+
+@pytest.mark.parametrize("case,k,reroute", [
+    (dict(T=300, d=72, F=64, N=6, CF=1.0), 1, False),             # fused router, top-1
+    (dict(T=300, d=72, F=64, N=6, CF=1.0), 2, False),             # fused router, top-2 mode
+    (dict(T=300, d=72, F=64, N=6, CF=0.6, zipf_s=1.1), 1, True),  # fused router, rerouting mode
+    (dict(T=1100, d=200, F=64, N=260, CF=2.0), 1, False),         # tiled logits
+    (dict(T=1000, d=128, F=64, N=130, CF=1.5), 1, False),         # N % 4 != 0: scalar logits
+    (dict(T=333, d=33, F=65, N=9, CF=1.25, dtype="fp32"), 1, False),  # fp32 layer
+])
+def test_stored_router_logits(case, k, reroute):
+    """Every router path leaves z = Wr x (fp32) at the start of the forward workspace, where
+    the backward pass reads it.  Bound: an fp32 sum of n exact products, in any order, is
+    within about n * 2^-24 * sum |products| of the exact sum.  The bf16 paths add 3d
+    products (bf16 x times the exact bf16 planes hi, mid, lo of Wr, each exact in fp32), the
+    fp32 path d fused multiply-adds; 3d * 2^-24 * 1.01 * sum_k |x_k Wr_ik| covers both."""
+    import torch
+
+    import sparse_mixture_experts_switchffn_amd as sffn
+    w = synth.workload("switch_base").replace(**case)
+    announce(f"stored logits k={k} reroute={reroute} " + w.describe())
+    dev_in = synth.device_inputs(w, DEV)
+    flags = sffn.SFFN_REROUTE_OVERFLOW if reroute else 0
+    out = sffn.switch_ffn_forward(dev_in["x"], dev_in["Wr"], dev_in["W1"], dev_in["b1"],
+                                  dev_in["W2"], dev_in["b2"], w.CF, flags=flags, k=k)
+    torch.cuda.synchronize()
+    z = out["workspace"][: w.T * w.N * 4].view(torch.float32).cpu().numpy().reshape(w.T, w.N)
+    x64 = synth.decode(host_x(w))
+    Wr64 = synth.decode(synth.host_array(w, "Wr").reshape(w.N, w.d))
+    ref = oracle.router_logits(x64, Wr64)
+    bound = 3 * w.d * 2.0 ** -24 * 1.01 * (np.abs(x64) @ np.abs(Wr64).T)
+    err = np.abs(z.astype(np.float64) - ref)
+    assert np.all(err <= bound), f"max excess {np.max(err - bound):.3e}"
+    print(f"  max |z - z64| = {err.max():.2e} (bound {bound.max():.2e})", flush=True)
