@@ -120,9 +120,11 @@ typedef struct sffn_stats {
 int64_t switch_ffn_capacity(int64_t T, int64_t N, double CF);
 
 /* Bytes of device workspace switch_ffn_forward needs for this shape (0 on bad
- * arguments).  Host only.  The workspace holds fp32 router logits [T, N],
- * per-block probability sums, dispatch counts and offsets, the row-to-token
- * map and the expert hidden activations [min(T, N*C), F]. */
+ * arguments).  Host only.  The workspace holds, from its start, the fp32 router
+ * logits z [T, N] (row-major; a forward call leaves them there for the
+ * backward pass), then per-block probability sums, dispatch counts and
+ * offsets, the row-to-token map and the expert hidden activations
+ * [min(T, N*C), F]. */
 size_t switch_ffn_workspace_bytes(int64_t T, int64_t d, int64_t F, int64_t N, double CF,
                                   int dtype);
 
