@@ -155,3 +155,11 @@ def test_backward_switch_base():
     """The Switch-Base-like workload at full size: gradients of sampled experts, dx of
     their tokens and of the dropped tokens."""
     _case(synth.workload("switch_base"), sampled=True)
+
+
+@pytest.mark.parametrize("name", ["skewed", "switch_large"])
+def test_backward_full_size_sampled(name):
+    """The skewed (many drops, C = 128) and Switch-Large-like (C = 320: two row chunks per
+    expert) workloads at full size: gradients of sampled experts, dx of their tokens and of
+    the dropped tokens."""
+    _case(synth.workload(name), sampled=True)
