@@ -6,7 +6,6 @@ this package.  The HIP product path never does.
 from .switchffn_oracle import (  # noqa: F401
     aux_loss,
     backward,
-    bf16_bits,
     capacity,
     dispatch,
     dispatch_topk,
@@ -14,6 +13,7 @@ from .switchffn_oracle import (  # noqa: F401
     forward,
     forward_reroute,
     gelu,
+    near_tie_second,
     near_tie_tokens,
     round_to_bf16,
     round_to_dtype,

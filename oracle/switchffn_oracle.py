@@ -104,9 +104,14 @@ def softmax(z: np.ndarray) -> np.ndarray:
 
 
 def top1(z: np.ndarray) -> np.ndarray:
-    """Lowest expert index among the largest fp32 logits of each token."""
+    """Lowest expert index among the largest fp32 logits of each token.
+
+    numpy's argmax order: the first maximum wins, and a NaN counts as larger than
+    every number (the pages never meet non-finite logits; this reading gives every
+    token an expert in [0, N) whatever its logits hold).
+    """
     z32 = z.astype(np.float32)
-    return np.argmax(z32, axis=1).astype(np.int64)  # argmax returns the first maximum
+    return np.argmax(z32, axis=1).astype(np.int64)
 
 
 def router(x: np.ndarray, Wr: np.ndarray) -> dict:
@@ -145,10 +150,17 @@ def dispatch(expert_idx: np.ndarray, N: int, C: int) -> dict:
 
 
 def second_choice(z: np.ndarray, first: np.ndarray) -> np.ndarray:
-    """Lowest expert index among the largest fp32 logits other than the first choice."""
-    z32 = z.astype(np.float32).copy()
-    z32[np.arange(z.shape[0]), first] = -np.inf
-    return np.argmax(z32, axis=1).astype(np.int64)
+    """Lowest expert index among the largest fp32 logits other than the first choice.
+
+    The first choice is removed from each row (not masked by -inf, which would tie
+    with a row of -inf logits); argmax over the remaining experts in index order.
+    """
+    z32 = z.astype(np.float32)
+    T, N = z32.shape
+    j = np.arange(N - 1)[None, :]
+    rest = j + (j >= np.asarray(first)[:, None])      # the other experts, increasing
+    pick = np.argmax(np.take_along_axis(z32, rest, axis=1), axis=1)
+    return rest[np.arange(T), pick].astype(np.int64)
 
 
 def topk_gates(probs: np.ndarray, choices: np.ndarray) -> np.ndarray:
@@ -238,11 +250,6 @@ def round_to_bf16(v: np.ndarray) -> np.ndarray:
     m, e = np.frexp(v)                 # v = m * 2^e, 0.5 <= |m| < 1
     q = np.rint(m * 256.0)             # 8 significant bits, round half to even
     return np.ldexp(q, e - 8)
-
-
-def bf16_bits(v: np.ndarray) -> np.ndarray:
-    """bfloat16 bit patterns of values that are already bf16-representable."""
-    return (np.asarray(v, np.float64).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
 
 
 def round_to_dtype(v: np.ndarray, dtype: str) -> np.ndarray:
@@ -567,9 +574,26 @@ def backward(x, Wr, experts, CF: float, dy, d_aux: float = 0.0, *,
     return out
 
 
+# ----------------------------------------------------------------------------
+# Where the routing choice is ambiguous.  The router decides on fp32 logits
+# ([Switch summary] 3.4 "Selective Precision Training"); two fp32 dot products
+# of the same operands summed in different orders can differ by a few fp32
+# ulps, so where the largest logits lie within tol of each other either choice
+# is a correct fp32 router.  Parity checks exempt these tokens from the
+# bit-exact expert comparison (and check the choice lies within tol instead).
+# ----------------------------------------------------------------------------
 def near_tie_tokens(logits: np.ndarray, tol: float = 1e-5) -> np.ndarray:
-    """Tokens whose top-1 and top-2 logits differ by at most tol (float64 logits)."""
+    """Tokens whose largest and second-largest logits differ by at most tol."""
     if logits.shape[1] < 2:
         return np.zeros(logits.shape[0], dtype=bool)
     part = np.partition(logits, -2, axis=1)
     return (part[:, -1] - part[:, -2]) <= tol
+
+
+def near_tie_second(logits: np.ndarray, tol: float = 1e-5) -> np.ndarray:
+    """Tokens whose second- and third-largest logits differ by at most tol (the
+    second choice of top-2 routing or rerouting is then ambiguous)."""
+    if logits.shape[1] < 3:
+        return np.zeros(logits.shape[0], dtype=bool)
+    srt = np.sort(logits, axis=1)
+    return (srt[:, -2] - srt[:, -3]) <= tol

@@ -83,21 +83,13 @@ def rel_l2(a, b):
     return float(np.linalg.norm(a - b) / (nb if nb > 0 else 1.0))
 
 
-def near_tie_second(z, tol=TIE_TOL):
-    """Tokens whose 2nd and 3rd largest logits differ by at most tol (top-2 routing)."""
-    if z.shape[1] < 3:
-        return np.zeros(z.shape[0], dtype=bool)
-    part = np.sort(z, axis=1)
-    return (part[:, -2] - part[:, -3]) <= tol
-
-
 def check_routing(gpu, ref):
     """expert_idx, slot, gate, aux and stats.  Returns the near-tie count."""
     z = ref["logits"]
     tie = oracle.near_tie_tokens(z, TIE_TOL)
     eg = gpu["expert_idx"]
     if eg.ndim == 2:  # top-2: both choices; a near-tie of either makes the token ambiguous
-        tie2 = tie | near_tie_second(z)
+        tie2 = tie | oracle.near_tie_second(z, TIE_TOL)
         bad = np.nonzero(np.any(eg != ref["router_expert_idx"], axis=1) & ~tie2)[0]
         assert bad.size == 0, f"expert_idx differs at {bad[:10]} (outside near-ties)"
         srt = -np.sort(-z, axis=1)

@@ -252,6 +252,65 @@ def pin_ties_lowest_index():
     assert list(r["expert_idx"]) == [0, 1, 0, 2]
 
 
+def pin_nan_logits_routing_order():
+    # numpy's argmax order: a NaN logit counts as the largest, the first one wins;
+    # the second choice is the same order over the other experts (a row of -inf
+    # logits still gets a second expert distinct from the first).
+    z = np.array([[1.0, np.nan, 3.0], [np.nan, np.nan, 0.0], [-np.inf, -np.inf, -np.inf],
+                  [0.0, -np.inf, np.nan]])
+    first = O.top1(z)
+    assert list(first) == [1, 0, 0, 2], first
+    assert list(O.second_choice(z, first)) == [2, 1, 1, 0]
+    # A NaN row of x: all its logits are NaN, so it goes to expert 0 with a NaN gate,
+    # the aux loss is NaN, and every other token routes and ranks as it would by itself.
+    rng = np.random.default_rng(5)
+    x = _f32(rng.standard_normal((6, 3)))
+    x[2] = np.nan
+    r = O.forward(x, np.eye(3), _zero_ffn(3, 2, 3), CF=3.0)
+    assert r["expert_idx"][2] == 0 and np.isnan(r["gate"][2]) and math.isnan(r["aux_loss"])
+    others = [0, 1, 3, 4, 5]
+    assert list(r["expert_idx"][others]) == list(np.argmax(x[others], axis=1))
+    assert np.all(np.isnan(r["y64"][2]))
+    ranks = [sum(1 for s in range(t) if r["expert_idx"][s] == r["expert_idx"][t]) for t in range(6)]
+    assert list(r["slot"]) == ranks
+
+
+def pin_near_tie_rule():
+    # The exemption set of the routing parity rule: largest minus second-largest logit
+    # <= tol (1e-5), wherever the two maxima sit; hand-checked rows.
+    z = np.array([
+        [0.3, 0.3, -1.0, -2.0],              # exact tie                       -> exempt
+        [1.0, 1.0 - 0.5e-5, 0.0, 0.5],       # gap 0.5e-5                      -> exempt
+        [0.0, -1e-5, -2.0, -3.0],            # gap exactly 1e-5 (0 - (-1e-5))  -> exempt
+        [2e-5, 0.0, -3.0, -4.0],             # gap 2e-5                        -> not
+        [-5.0, 0.0, 3e-6, -1.0],             # maxima in columns 2 and 1       -> exempt
+        [7.0, -2.0, 7.0 - 4e-5, 7.0 - 4e-5], # second and third tie, gap 4e-5  -> not
+        [5.0, 5.0, 5.0, 0.0],                # three-way tie                   -> exempt
+        [1.0, 4.0, 4.0 - 1e-6, 1.0],         # maxima in columns 1 and 2       -> exempt
+        [-3.0, -3.0 - 1e-6, -7.0, -9.0],     # negative logits, gap 1e-6       -> exempt
+        [5.0, 1.0, 1.0, 0.0],                # clear winner                    -> not
+        [np.nan, 1.0, 1.0, 0.0],             # NaN: the choice is fixed, never exempt
+    ])
+    want = [True, True, True, False, True, False, True, True, True, False, False]
+    assert list(O.near_tie_tokens(z, 1e-5)) == want
+    assert not O.near_tie_tokens(np.array([[3.0], [3.0]]), 1e-5).any()   # one expert: no tie
+    assert list(O.near_tie_tokens(np.array([[1.0, 1.0 + 2e-5]]), 3e-5)) == [True]
+
+
+def pin_near_tie_second_rule():
+    # Top-2 routing's extra exemption: second- minus third-largest logit <= tol.
+    z = np.array([
+        [5.0, 1.0, 1.0],                     # second and third tie            -> exempt
+        [5.0, 1.0, 1.0 - 2e-5],              # gap 2e-5                        -> not
+        [1.0, 1.0, 1.0],                     # three-way tie                   -> exempt
+        [0.0, 0.0, -1e-5],                   # gap exactly 1e-5                -> exempt
+        [3.0, 2.0 - 0.5e-5, 2.0],            # gap 0.5e-5, columns swapped     -> exempt
+        [9.0, 9.0, 1.0],                     # top-1/top-2 tie only            -> not
+    ])
+    assert list(O.near_tie_second(z, 1e-5)) == [True, False, True, True, True, False]
+    assert not O.near_tie_second(np.array([[1.0, 1.0]]), 1e-5).any()      # two experts
+
+
 def pin_round_to_bf16():
     ulp = 2.0 ** -7
     vals = np.array([1.0, 1.0 + ulp / 2, 1.0 + 1.5 * ulp, 1.0 + 0.75 * ulp, -1.0 - ulp / 2,

@@ -12,7 +12,7 @@ import pytest
 import oracle
 import switchffn_synth as synth
 from gpu_harness import (AUX_TOL, GATE_TOL, TIE_TOL, announce, check_y, host_x,
-                         near_tie_second, oracle_ref, run_gpu)
+                         oracle_ref, run_gpu)
 
 pytestmark = pytest.mark.gpu
 
@@ -21,7 +21,7 @@ DEV = "cuda:0"
 
 def _check_choices(choices, ref):
     z = ref["logits"]
-    tie = oracle.near_tie_tokens(z, TIE_TOL) | near_tie_second(z)
+    tie = oracle.near_tie_tokens(z, TIE_TOL) | oracle.near_tie_second(z, TIE_TOL)
     bad = np.nonzero(np.any(choices != ref["router_choices"], axis=1) & ~tie)[0]
     assert bad.size == 0, f"router choices differ at {bad[:10]} (outside near-ties)"
     srt = -np.sort(-z, axis=1)

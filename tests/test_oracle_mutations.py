@@ -16,7 +16,7 @@ _orig = {name: getattr(O, name) for name in
          ("capacity", "router_logits", "softmax", "top1", "dispatch", "aux_loss", "expert_ffn",
           "round_to_bf16", "forward", "second_choice", "topk_gates", "dispatch_topk",
           "reroute_overflow", "gelu", "expert_backward", "aux_prob_grad", "softmax_backward",
-          "backward")}
+          "backward", "near_tie_tokens", "near_tie_second")}
 
 
 def _ffn_no_b2(xe, W1e, b1e, W2e, b2e, activation="relu"):
@@ -291,7 +291,67 @@ def _bwd_no_residual(*a, **k):
     return g
 
 
+def _near_tie_strict(z, tol=1e-5):
+    if z.shape[1] < 2:
+        return np.zeros(z.shape[0], dtype=bool)
+    part = np.partition(z, -2, axis=1)
+    return (part[:, -1] - part[:, -2]) < tol
+
+
+def _near_tie_top1_top3(z, tol=1e-5):
+    if z.shape[1] < 3:
+        return _orig["near_tie_tokens"](z, tol)
+    srt = np.sort(z, axis=1)
+    return (srt[:, -1] - srt[:, -3]) <= tol
+
+
+def _near_tie_top2_top3(z, tol=1e-5):
+    if z.shape[1] < 3:
+        return _orig["near_tie_tokens"](z, tol)
+    srt = np.sort(z, axis=1)
+    return (srt[:, -2] - srt[:, -3]) <= tol
+
+
+def _near_tie_sign(z, tol=1e-5):
+    if z.shape[1] < 2:
+        return np.zeros(z.shape[0], dtype=bool)
+    part = np.partition(z, -2, axis=1)
+    return (part[:, -2] - part[:, -1]) <= tol
+
+
+def _near_tie_second_strict(z, tol=1e-5):
+    if z.shape[1] < 3:
+        return np.zeros(z.shape[0], dtype=bool)
+    srt = np.sort(z, axis=1)
+    return (srt[:, -2] - srt[:, -3]) < tol
+
+
+def _near_tie_second_top1_top2(z, tol=1e-5):
+    if z.shape[1] < 3:
+        return np.zeros(z.shape[0], dtype=bool)
+    srt = np.sort(z, axis=1)
+    return (srt[:, -1] - srt[:, -2]) <= tol
+
+
+def _top1_ignores_nan(z):
+    return np.nanargmax(z.astype(np.float32), axis=1).astype(np.int64)
+
+
+def _second_by_minus_inf(z, first):
+    z32 = z.astype(np.float32).copy()
+    z32[np.arange(z.shape[0]), first] = -np.inf
+    return np.argmax(z32, axis=1).astype(np.int64)
+
+
 MUTANTS = {
+    "near_tie_strict_inequality": ("near_tie_tokens", _near_tie_strict),
+    "near_tie_top1_top3_gap": ("near_tie_tokens", _near_tie_top1_top3),
+    "near_tie_top2_top3_gap": ("near_tie_tokens", _near_tie_top2_top3),
+    "near_tie_sign_flip": ("near_tie_tokens", _near_tie_sign),
+    "near_tie_second_strict_inequality": ("near_tie_second", _near_tie_second_strict),
+    "near_tie_second_top1_top2_gap": ("near_tie_second", _near_tie_second_top1_top2),
+    "top1_ignores_nan": ("top1", _top1_ignores_nan),
+    "second_choice_masks_by_minus_inf": ("second_choice", _second_by_minus_inf),
     "ffn_drops_b2": ("expert_ffn", _ffn_no_b2),
     "ffn_drops_b1": ("expert_ffn", _ffn_no_b1),
     "ffn_no_relu": ("expert_ffn", _ffn_no_relu),
