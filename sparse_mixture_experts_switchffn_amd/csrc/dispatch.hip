@@ -105,12 +105,15 @@ reroute_count_kernel(const int32_t* __restrict__ choice, const int* __restrict__
     const int t = tb + threadIdx.x;
     int e2 = -1;
     if (t < T) {
-      const int r = base[(size_t)b * N + choice[2 * (size_t)t]] + lrank[2 * (size_t)t];
+      const int e1 = choice[2 * (size_t)t];
+      const int r = (unsigned)e1 < (unsigned)N ? base[(size_t)b * N + e1] + lrank[2 * (size_t)t]
+                                               : C;
       if (r < C) {
         slot1[t] = r;
       } else {
         slot1[t] = -1;
         e2 = choice[2 * (size_t)t + 1];
+        if ((unsigned)e2 >= (unsigned)N) e2 = -1;  // refused by both stages
       }
     }
     e2_s[threadIdx.x] = e2;
@@ -212,7 +215,13 @@ __device__ void finish_dispatch(const int* __restrict__ f_count, const int* __re
                                 int* __restrict__ offset, float* __restrict__ aux_loss,
                                 int32_t* __restrict__ stat_count,
                                 int32_t* __restrict__ stat_accepted,
-                                int32_t* __restrict__ stat_dropped) {
+                                int32_t* __restrict__ stat_dropped, uint32_t* __restrict__ tag,
+                                const WsTag& tagv) {
+  if (threadIdx.x == 0) {  // the layout tag (constant indices: the words stay in registers)
+#pragma unroll
+    for (int i = 0; i < 16; i += 4)
+      store16(tag + i, u32x4{tagv.w[i], tagv.w[i + 1], tagv.w[i + 2], tagv.w[i + 3]});
+  }
   for (int i = threadIdx.x; i <= N; i += 256) offset[i] = off_s[i];
   double part = 0.0;
   int accepted = 0;
@@ -253,7 +262,8 @@ dispatch_scatter_kernel(const int32_t* __restrict__ expert_idx, const int* __res
                         int32_t* __restrict__ slot, int* __restrict__ row2tok,
                         float* __restrict__ rowgate, int* __restrict__ offset, float* __restrict__ aux_loss,
                         int32_t* __restrict__ stat_count, int32_t* __restrict__ stat_accepted,
-                        int32_t* __restrict__ stat_dropped) {
+                        int32_t* __restrict__ stat_dropped,
+    uint32_t* __restrict__ tag, const WsTag tagv) {
   __shared__ int off_s[SFFN_MAX_EXPERTS + 1];
   __shared__ int tsum[256];
   __shared__ int dropped_s[kRouteTokens];
@@ -267,8 +277,11 @@ dispatch_scatter_kernel(const int32_t* __restrict__ expert_idx, const int* __res
     const int t = tb + threadIdx.x;
     int dropped = 0;
     if (t < T) {
+      // The router gives every token an expert in [0, N); an index outside it
+      // (a corrupted input) drops the token instead of indexing past the tables.
       const int e = expert_idx[t];
-      const int r = base[(size_t)b * N + e] + lrank[t];
+      const bool ok = (unsigned)e < (unsigned)N;
+      const int r = ok ? base[(size_t)b * N + e] + lrank[t] : C;
       if (r < C) {
         slot[t] = r;
         row2tok[off_s[e] + r] = t;
@@ -285,7 +298,7 @@ dispatch_scatter_kernel(const int32_t* __restrict__ expert_idx, const int* __res
   pass_through_dropped(dropped_s, tb, d, esize, x, y, no_residual);
   if (b != 0) return;
   finish_dispatch(hist, hist, acc, psum, T, N, T, off_s, tsum, red, offset, aux_loss, stat_count,
-                  stat_accepted, stat_dropped);
+                  stat_accepted, stat_dropped, tag, tagv);
 }
 
 // ---------------------------------------------------------------------------
@@ -303,7 +316,8 @@ dispatch_scatter_top2_kernel(const int32_t* __restrict__ expert_idx, const int* 
                              int* __restrict__ row2tok, float* __restrict__ rowgate,
                              int* __restrict__ offset, float* __restrict__ aux_loss,
                              int32_t* __restrict__ stat_count, int32_t* __restrict__ stat_accepted,
-                             int32_t* __restrict__ stat_dropped) {
+                             int32_t* __restrict__ stat_dropped,
+    uint32_t* __restrict__ tag, const WsTag tagv) {
   __shared__ int off_s[SFFN_MAX_EXPERTS + 1];
   __shared__ int tsum[256];
   __shared__ double red[256];
@@ -317,7 +331,8 @@ dispatch_scatter_top2_kernel(const int32_t* __restrict__ expert_idx, const int* 
     const size_t i = 2 * (size_t)t + (threadIdx.x & 1);
     if (t < T) {
       const int e = expert_idx[i];
-      const int r = base[(size_t)b * N + e] + lrank[i];
+      const bool ok = (unsigned)e < (unsigned)N;  // as in the top-1 dispatch
+      const int r = ok ? base[(size_t)b * N + e] + lrank[i] : C;
       if (r < C) {
         slot[i] = r;
         row2tok[off_s[e] + r] = t;
@@ -330,7 +345,7 @@ dispatch_scatter_top2_kernel(const int32_t* __restrict__ expert_idx, const int* 
 
   if (b != 0) return;
   finish_dispatch(hist1, hist, acc, psum, T, N, 2 * T, off_s, tsum, red, offset, aux_loss,
-                  stat_count, stat_accepted, stat_dropped);
+                  stat_count, stat_accepted, stat_dropped, tag, tagv);
 }
 
 // ---------------------------------------------------------------------------
@@ -355,7 +370,8 @@ dispatch_scatter_reroute_kernel(const int32_t* __restrict__ choice,
                                 int* __restrict__ offset, float* __restrict__ aux_loss,
                                 int32_t* __restrict__ stat_count,
                                 int32_t* __restrict__ stat_accepted,
-                                int32_t* __restrict__ stat_dropped) {
+                                int32_t* __restrict__ stat_dropped,
+    uint32_t* __restrict__ tag, const WsTag tagv) {
   __shared__ int off_s[SFFN_MAX_EXPERTS + 1];
   __shared__ int tsum[256];
   __shared__ int dropped_s[kRouteTokens];
@@ -374,7 +390,8 @@ dispatch_scatter_reroute_kernel(const int32_t* __restrict__ choice,
       float g = gate2[i0];
       if (r < 0) {
         const int e2 = choice[i0 + 1];
-        const int r2 = base[(size_t)b * N + e2] + lrank[i0 + 1];
+        const bool ok = (unsigned)e2 < (unsigned)N;  // as in the top-1 dispatch
+        const int r2 = ok ? base[(size_t)b * N + e2] + lrank[i0 + 1] : C;
         if (r2 < C) {
           e = e2;
           r = r2;
@@ -399,17 +416,18 @@ dispatch_scatter_reroute_kernel(const int32_t* __restrict__ choice,
   pass_through_dropped(dropped_s, tb, d, esize, x, y, no_residual);
   if (b != 0) return;
   finish_dispatch(hist, hist, acc2, psum, T, N, T, off_s, tsum, red, offset, aux_loss,
-                  stat_count, stat_accepted, stat_dropped);
+                  stat_count, stat_accepted, stat_dropped, tag, tagv);
 }
 
 hipError_t launch_dispatch_scatter(const Shape& s, const Inputs& in, const Workspace& ws,
-                                   const Outputs& out, bool no_residual, hipStream_t st) {
+                                   const Outputs& out, bool no_residual, const WsTag& tag,
+                                   hipStream_t st) {
   const dim3 grid((unsigned)s.n_route_blocks), block(256);
   if (s.k == 2) {
     hipLaunchKernelGGL(dispatch_scatter_top2_kernel, grid, block, 0, st, out.expert_idx, ws.base,
                        ws.lrank, ws.hist, ws.hist1, ws.acc, ws.psum, s.T, s.N, s.C, out.gate,
                        out.slot, ws.row2tok, ws.rowgate, ws.offset, out.aux_loss,
-                       out.stat_count, out.stat_accepted, out.stat_dropped);
+                       out.stat_count, out.stat_accepted, out.stat_dropped, ws.tag, tag);
     return hipGetLastError();
   }
   const int esize = s.dtype == SFFN_BF16 ? 2 : 4;
@@ -418,14 +436,14 @@ hipError_t launch_dispatch_scatter(const Shape& s, const Inputs& in, const Works
                        ws.slot1, ws.base, ws.lrank, ws.hist, ws.acc2, ws.psum, s.T, s.N, s.C,
                        s.d, esize, in.x, out.y, no_residual ? 1 : 0, out.expert_idx, out.gate,
                        out.slot, ws.row2tok, ws.rowgate, ws.offset, out.aux_loss,
-                       out.stat_count, out.stat_accepted, out.stat_dropped);
+                       out.stat_count, out.stat_accepted, out.stat_dropped, ws.tag, tag);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(dispatch_scatter_kernel, grid, block, 0, st, out.expert_idx, ws.base,
                      ws.lrank, ws.hist, ws.acc, ws.psum, s.T, s.N, s.C, s.d, esize, in.x, out.y,
                      no_residual ? 1 : 0, out.gate, out.slot, ws.row2tok, ws.rowgate,
                      ws.offset, out.aux_loss,
-                     out.stat_count, out.stat_accepted, out.stat_dropped);
+                     out.stat_count, out.stat_accepted, out.stat_dropped, ws.tag, tag);
   return hipGetLastError();
 }
 

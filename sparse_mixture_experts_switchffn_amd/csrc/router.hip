@@ -356,7 +356,7 @@ router_fused_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__
     const int o = e * PST + tt;
     z[i] = ((Ps[0][o] + Ps[1][o]) + Ps[2][o]) + Ps[3][o];  // waves in order
     if (live && e < N) logits[(size_t)t * N + e] = z[i];  // kept for the backward pass
-    if (e < N && z[i] > mx) {  // e rises with i: the first maximum is the lowest index
+    if (e < N && route_before(z[i], e, mx, arg)) {
       mx = z[i];
       arg = e;
     }
@@ -365,7 +365,7 @@ router_fused_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__
   for (int off = 1; off < 8; off <<= 1) {
     const float om = __shfl_xor(mx, off);
     const int oa = __shfl_xor(arg, off);
-    if (om > mx || (om == mx && oa < arg)) {
+    if (route_before(om, oa, mx, arg)) {
       mx = om;
       arg = oa;
     }
@@ -376,7 +376,7 @@ router_fused_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__
 #pragma unroll
     for (int i = 0; i < EPT; ++i) {
       const int e = g + 8 * i;
-      if (e < N && e != arg && z[i] > mx2) {
+      if (e < N && e != arg && route_before(z[i], e, mx2, arg2)) {
         mx2 = z[i];
         arg2 = e;
       }
@@ -385,7 +385,7 @@ router_fused_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__
     for (int off = 1; off < 8; off <<= 1) {
       const float om = __shfl_xor(mx2, off);
       const int oa = __shfl_xor(arg2, off);
-      if (om > mx2 || (om == mx2 && oa < arg2)) {
+      if (route_before(om, oa, mx2, arg2)) {
         mx2 = om;
         arg2 = oa;
       }
@@ -777,7 +777,7 @@ softmax_route_kernel(const float* __restrict__ logits, int T, int N,
 #pragma unroll
     for (int q = 0; q < NPL; ++q) {
       const int i = lane + 64 * q;
-      if (i < N && (v[q] > m || (v[q] == m && i < arg))) {
+      if (i < N && route_before(v[q], i, m, arg)) {
         m = v[q];
         arg = i;
       }
@@ -786,7 +786,7 @@ softmax_route_kernel(const float* __restrict__ logits, int T, int N,
     for (int off = 32; off >= 1; off >>= 1) {
       const float om = __shfl_xor(m, off);
       const int oa = __shfl_xor(arg, off);
-      if (om > m || (om == m && oa < arg)) {
+      if (route_before(om, oa, m, arg)) {
         m = om;
         arg = oa;
       }
@@ -878,7 +878,7 @@ softmax_route_top2_kernel(const float* __restrict__ logits, int T, int N,
 #pragma unroll
     for (int q = 0; q < NPL; ++q) {
       const int i = lane + 64 * q;
-      if (i < N && i != skip && (v[q] > m || (v[q] == m && i < arg))) {
+      if (i < N && i != skip && route_before(v[q], i, m, arg)) {
         m = v[q];
         arg = i;
       }
@@ -887,7 +887,7 @@ softmax_route_top2_kernel(const float* __restrict__ logits, int T, int N,
     for (int off = 32; off >= 1; off >>= 1) {
       const float om = __shfl_xor(m, off);
       const int oa = __shfl_xor(arg, off);
-      if (om > m || (om == m && oa < arg)) {
+      if (route_before(om, oa, m, arg)) {
         m = om;
         arg = oa;
       }
@@ -1019,7 +1019,7 @@ softmax_route_vec_kernel(const float* __restrict__ logits, int T, int N,
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const int i = 4 * (64 * q + lane) + c;
-        if (i < N && v[q][c] > m) {
+        if (i < N && route_before(v[q][c], i, m, arg)) {
           m = v[q][c];
           arg = i;
         }
@@ -1028,7 +1028,7 @@ softmax_route_vec_kernel(const float* __restrict__ logits, int T, int N,
     for (int off = 32; off >= 1; off >>= 1) {
       const float om = __shfl_xor(m, off);
       const int oa = __shfl_xor(arg, off);
-      if (om > m || (om == m && oa < arg)) {
+      if (route_before(om, oa, m, arg)) {
         m = om;
         arg = oa;
       }

@@ -30,6 +30,18 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+// Routing order of two candidate experts (logit a of expert ia against logit b
+// of expert ib): the larger fp32 logit goes first, a NaN counts as larger than
+// every number, and equal values (two NaNs included) go to the lower index.
+// This is numpy's argmax order, so an argmax that starts from (-inf, a
+// sentinel index above every expert) always ends on an expert in [0, N),
+// whatever a token's logits hold.
+__device__ __forceinline__ bool route_before(float a, int ia, float b, int ib) {
+  const bool an = __builtin_isnan(a), bn = __builtin_isnan(b);
+  if (an | bn) return an & (!bn | (ia < ib));
+  return (a > b) | ((a == b) & (ia < ib));
+}
+
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
