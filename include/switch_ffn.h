@@ -44,10 +44,15 @@
  * workspace and outputs.
  *
  * Errors: arguments are validated before anything is enqueued; on an error
- * nothing is launched and no output is touched.  NaN/Inf inputs are not
- * checked (undefined results).  SFFN_EHIP reports a launch failure; the HIP
- * error text is then available from switch_ffn_status_string(SFFN_EHIP) on
- * the same thread.
+ * nothing is launched and no output is touched.  SFFN_EHIP reports a launch
+ * failure; the HIP error text is then available from
+ * switch_ffn_status_string(SFFN_EHIP) on the same thread.
+ *
+ * Non-finite inputs are not checked and give non-finite results, but never an
+ * access outside the buffers: the routing order treats a NaN logit as larger
+ * than every number (ties and NaNs to the lowest index, numpy's argmax order),
+ * so every token is routed to an expert in [0, N); its gate and the aux loss
+ * then come out NaN.
  */
 #ifndef SWITCH_FFN_H
 #define SWITCH_FFN_H
@@ -120,11 +125,13 @@ typedef struct sffn_stats {
 int64_t switch_ffn_capacity(int64_t T, int64_t N, double CF);
 
 /* Bytes of device workspace switch_ffn_forward needs for this shape (0 on bad
- * arguments).  Host only.  The workspace holds, from its start, the fp32 router
- * logits z [T, N] (row-major; a forward call leaves them there for the
- * backward pass), then per-block probability sums, dispatch counts and
- * offsets, the row-to-token map and the expert hidden activations
- * [min(T, N*C), F]. */
+ * arguments).  Host only.  The workspace holds, from its start, a layout tag
+ * of 16 uint32 words (magic 0x4E464653, version 1, k, flags, T, d, F, N, C,
+ * dtype, then zeros) in a 256-byte region, so that the backward pass can tell
+ * which form of the layer wrote the rest; from byte 256 the fp32 router logits
+ * z [T, N] (row-major; a forward call leaves them there for the backward
+ * pass), then per-block probability sums, dispatch counts and offsets, the
+ * row-to-token map and the expert hidden activations [min(T, N*C), F]. */
 size_t switch_ffn_workspace_bytes(int64_t T, int64_t d, int64_t F, int64_t N, double CF,
                                   int dtype);
 
@@ -141,18 +148,15 @@ int switch_ffn_forward(const void* x, const float* Wr, const void* W1, const voi
 /* switch_ffn_forward plus:
  *   flags         0 or an OR of SFFN_NO_RESIDUAL (a diagnostic: the bare expert
  *                 term), SFFN_REROUTE_OVERFLOW (No-Token-Left-Behind) and
- *                 SFFN_GEGLU (GEGLU experts)
+ *                 SFFN_GEGLU (GEGLU experts); other bits: SFFN_EINVAL
  *   stats         optional routing statistics (NULL = none)
- *   stage_events  optional host array of switch_ffn_num_stages()+1 hipEvent_t
- *                 handles (created by the caller); event i is recorded on
- *                 `stream` before stage i and the last one after the final
- *                 stage, so the caller can time each stage.  NULL = none. */
+ * Per-stage timing events: switch_ffn_forward_topk with k = 1. */
 int switch_ffn_forward_ex(const void* x, const float* Wr, const void* W1, const void* b1,
                           const void* W2, const void* b2, int64_t T, int64_t d, int64_t F,
                           int64_t N, double CF, int dtype, void* y, int32_t* expert_idx,
                           int32_t* slot, float* gate, float* aux_loss, void* workspace,
                           size_t workspace_bytes, void* stream, uint32_t flags,
-                          const sffn_stats* stats, void* const* stage_events);
+                          const sffn_stats* stats);
 
 /* Top-k routing, k = 1 or 2 (k = 2: the MoE top-2 baseline the Switch summary
  * contrasts with, section "Why Top-1 Routing Matters" and its top-2 routing
@@ -172,8 +176,11 @@ int switch_ffn_forward_ex(const void* x, const float* Wr, const void* W1, const 
  *            accepted_count = min(expert_count, C), n_dropped = dropped choices.
  * k = 1 is exactly switch_ffn_forward_ex.  k = 2 needs N >= 2 and
  * min(2T, N*C) * max(d, F) * 4 < 2^31 (else SFFN_EUNSUPPORTED); k outside
- * {1, 2} or N < k is SFFN_EINVAL.  The per-stage events are the same six
- * stages; with k = 2 the ffn2 stage also holds the combine. */
+ * {1, 2} or N < k is SFFN_EINVAL.
+ * stage_events: NULL, or a host array of switch_ffn_num_stages()+1 hipEvent_t
+ * handles created by the caller; event i is recorded on `stream` before stage
+ * i and the last one after the final stage, so the caller can time each stage
+ * (with k = 2 the ffn2 stage also holds the combine). */
 size_t switch_ffn_workspace_bytes_topk(int64_t T, int64_t d, int64_t F, int64_t N, double CF,
                                        int k, int dtype);
 int switch_ffn_forward_topk(const void* x, const float* Wr, const void* W1, const void* b1,
@@ -201,9 +208,20 @@ int switch_ffn_forward_topk(const void* x, const float* Wr, const void* W1, cons
  *   x, Wr, W1, b1, W2, b2, T, d, F, N, CF, dtype  exactly as in the forward call
  *   expert_idx, slot  [T] the forward's outputs (device)
  *   fwd_workspace     the forward's workspace (device), as that call left it:
- *                     it holds the fp32 router logits, the dispatch (offsets,
- *                     row maps, gates, counts) and the hidden activations H;
- *                     only read here
+ *                     it holds the layout tag, the fp32 router logits, the
+ *                     dispatch (offsets, row maps, gates, counts) and the
+ *                     hidden activations H; only read here.  Its tag must name
+ *                     a forward with k = 1, without SFFN_REROUTE_OVERFLOW or
+ *                     SFFN_GEGLU, of the same T, d, F, N, C and dtype
+ *                     (SFFN_NO_RESIDUAL does not matter).  While `stream` is
+ *                     not being captured into a graph, the tag is read on the
+ *                     host before anything is enqueued (the call then waits
+ *                     for the stream's earlier work) and any other tag returns
+ *                     SFFN_EINVAL.  Under capture the forward has not run yet:
+ *                     the first kernel checks the tag on the device, together
+ *                     with the expert offsets, and on a mismatch the call
+ *                     reads none of the forward's row maps and every gradient
+ *                     comes out NaN.
  *   dy                [T, d] dL/dy (device, dtype)
  *   d_aux             dL/d(aux_loss) (host value; the alpha factor goes here)
  * Outputs (device, caller-allocated, overwritten): dx [T, d] (dtype),
@@ -212,8 +230,10 @@ int switch_ffn_forward_topk(const void* x, const float* Wr, const void* W1, cons
  * tokens get zero gradients.  `workspace`: a device buffer of at least
  * switch_ffn_backward_workspace_bytes() bytes, 256-byte aligned, separate
  * from fwd_workspace.  stage_events: NULL or switch_ffn_backward_num_stages()+1
- * events, recorded like forward_ex's.  Returns SFFN_OK, SFFN_EINVAL (a null
- * required pointer, d_aux not finite, or the shape checks of the forward),
+ * events, recorded like forward_topk's.  expert_idx[t] outside [0, N) or
+ * slot[t] >= C reads as a dropped token.  Returns SFFN_OK, SFFN_EINVAL (a null
+ * required pointer, d_aux not finite, the shape checks of the forward, or a
+ * forward workspace whose tag names another form of the layer),
  * SFFN_EWORKSPACE (either workspace too small), SFFN_EUNSUPPORTED (alignment,
  * limits) or SFFN_EHIP. */
 size_t switch_ffn_backward_workspace_bytes(int64_t T, int64_t d, int64_t F, int64_t N, double CF,

@@ -55,8 +55,7 @@ def load_library(path: str = LIB_PATH):
     L.switch_ffn_forward.restype = ctypes.c_int
     L.switch_ffn_forward.argtypes = _FWD_ARGS
     L.switch_ffn_forward_ex.restype = ctypes.c_int
-    L.switch_ffn_forward_ex.argtypes = _FWD_ARGS + [ctypes.c_uint32, ctypes.POINTER(sffn_stats),
-                                                    _P]
+    L.switch_ffn_forward_ex.argtypes = _FWD_ARGS + [ctypes.c_uint32, ctypes.POINTER(sffn_stats)]
     L.switch_ffn_workspace_bytes_topk.restype = ctypes.c_size_t
     L.switch_ffn_workspace_bytes_topk.argtypes = [_I64, _I64, _I64, _I64, ctypes.c_double,
                                                   ctypes.c_int, ctypes.c_int]
@@ -149,6 +148,53 @@ def _dtype_code(t) -> int:
     raise TypeError(f"x must be float32 or bfloat16, not {t.dtype}")
 
 
+def _check(name, t, shape, dtype, device, nullable=False):
+    """A tensor argument as the C-ABI reads it: this shape and dtype, contiguous, on the
+    layer's device (the library reads it through a raw pointer, so anything else would
+    make it read the wrong bytes or past the allocation)."""
+    if t is None:
+        if nullable:
+            return
+        raise ValueError(f"{name} is required")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, not {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, not {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the layer's tensors on {device}")
+
+
+def _check_workspace(name, ws, nbytes, device):
+    import torch
+    if ws.dtype != torch.uint8 or not ws.is_contiguous() or ws.device != device:
+        raise ValueError(f"{name} must be a contiguous uint8 tensor on {device}")
+    if ws.numel() < nbytes:
+        raise ValueError(f"{name} holds {ws.numel()} bytes, {nbytes} needed")
+
+
+def _check_layer(x, Wr, W1, b1, W2, b2, glu: bool):
+    """Shapes, dtypes, contiguity and device of the layer's inputs; returns T, d, F, N."""
+    import torch
+    if x.dim() != 2 or W2.dim() != 3 or Wr.dim() != 2:
+        raise ValueError("x must be [T, d], Wr [N, d], W2 [N, d, F]")
+    _dtype_code(x)
+    T, d = x.shape
+    N, F = Wr.shape[0], W2.shape[2]
+    F1 = 2 * F if glu else F
+    dev = x.device
+    _check("x", x, (T, d), x.dtype, dev)
+    _check("Wr", Wr, (N, d), torch.float32, dev)
+    _check("W1", W1, (N, F1, d), x.dtype, dev)
+    _check("b1", b1, (N, F1), x.dtype, dev, nullable=True)
+    _check("W2", W2, (N, d, F), x.dtype, dev)
+    _check("b2", b2, (N, d), x.dtype, dev, nullable=True)
+    if dev.type != "cuda":
+        raise ValueError(f"the layer's tensors must be GPU tensors, not on {dev}")
+    return T, d, F, N
+
+
 def switch_ffn_forward(x, Wr, W1, b1, W2, b2, CF: float, *, y=None, expert_idx=None, slot=None,
                        gate=None, aux_loss=None, workspace=None, stream=None, flags: int = 0,
                        stats=None, stage_events=None, check: bool = True, k: int = 1) -> dict:
@@ -164,14 +210,14 @@ def switch_ffn_forward(x, Wr, W1, b1, W2, b2, CF: float, *, y=None, expert_idx=N
     """
     import torch
 
-    T, d = x.shape
-    N = Wr.shape[0]
-    F = W2.shape[2]  # W1 has 2F rows with SFFN_GEGLU
+    if k not in (1, 2):
+        raise ValueError("k must be 1 or 2")
+    T, d, F, N = _check_layer(x, Wr, W1, b1, W2, b2, bool(flags & SFFN_GEGLU))
     dt = _dtype_code(x)
     dev = x.device
+    shape = (T,) if k == 1 else (T, k)
     if y is None:
         y = torch.empty_like(x)
-    shape = (T,) if k == 1 else (T, k)
     if expert_idx is None:
         expert_idx = torch.empty(shape, dtype=torch.int32, device=dev)
     if slot is None:
@@ -180,13 +226,22 @@ def switch_ffn_forward(x, Wr, W1, b1, W2, b2, CF: float, *, y=None, expert_idx=N
         gate = torch.empty(shape, dtype=torch.float32, device=dev)
     if aux_loss is None:
         aux_loss = torch.empty(1, dtype=torch.float32, device=dev)
+    _check("y", y, (T, d), x.dtype, dev)
+    _check("expert_idx", expert_idx, shape, torch.int32, dev)
+    _check("slot", slot, shape, torch.int32, dev)
+    _check("gate", gate, shape, torch.float32, dev)
+    _check("aux_loss", aux_loss, (1,), torch.float32, dev)
     nbytes = switch_ffn_workspace_bytes_topk(T, d, F, N, CF, k, dt)
     if workspace is None and nbytes > 0:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    if workspace is not None:
+        _check_workspace("workspace", workspace, nbytes, dev)
     if stream is None:
         stream = torch.cuda.current_stream(dev).cuda_stream
     st = None
     if stats is not None:
+        for key, n in (("expert_count", N), ("accepted_count", N), ("n_dropped", 1)):
+            _check(f"stats['{key}']", stats.get(key), (n,), torch.int32, dev, nullable=True)
         st = sffn_stats(_ptr(stats.get("expert_count")), _ptr(stats.get("accepted_count")),
                         _ptr(stats.get("n_dropped")))
     ev = None
@@ -199,22 +254,23 @@ def switch_ffn_forward(x, Wr, W1, b1, W2, b2, CF: float, *, y=None, expert_idx=N
     args = (_ptr(x), _ptr(Wr), _ptr(W1), _ptr(b1), _ptr(W2), _ptr(b2), T, d, F, N, CF, dt,
             _ptr(y), _ptr(expert_idx), _ptr(slot), _ptr(gate), _ptr(aux_loss), _ptr(workspace),
             ws_bytes, stream)
-    if k != 1:
+    if k != 1 or ev is not None:
         name = "switch_ffn_forward_topk"
         rc = lib().switch_ffn_forward_topk(*args[:11], k, *args[11:], flags,
                                            None if st is None else ctypes.byref(st),
                                            None if ev is None else ctypes.cast(ev, ctypes.c_void_p))
-    elif flags == 0 and st is None and ev is None:
+    elif flags == 0 and st is None:
         name = "switch_ffn_forward"
         rc = lib().switch_ffn_forward(*args)
     else:
         name = "switch_ffn_forward_ex"
-        rc = lib().switch_ffn_forward_ex(*args, flags, None if st is None else ctypes.byref(st),
-                                         None if ev is None else ctypes.cast(ev, ctypes.c_void_p))
+        rc = lib().switch_ffn_forward_ex(*args, flags, None if st is None else ctypes.byref(st))
     if check and rc != SFFN_OK:
         raise RuntimeError(f"{name} failed ({rc}): {switch_ffn_status_string(rc)}")
+    # k and flags travel with the workspace: the backward reads only a top-1 forward's
+    # workspace without rerouting or GEGLU experts (the library checks its tag as well).
     return {"status": rc, "y": y, "expert_idx": expert_idx, "slot": slot, "gate": gate,
-            "aux_loss": aux_loss, "workspace": workspace}
+            "aux_loss": aux_loss, "workspace": workspace, "k": k, "flags": flags}
 
 
 # forward_ex's and forward_topk's extra arguments are keyword arguments of switch_ffn_forward.
@@ -234,11 +290,15 @@ def switch_ffn_backward(x, Wr, W1, b1, W2, b2, CF: float, fwd: dict, dy, d_aux: 
     """
     import torch
 
-    T, d = x.shape
-    N = Wr.shape[0]
-    F = W2.shape[2]
+    if fwd.get("k", 1) != 1 or fwd.get("flags", 0) & (SFFN_REROUTE_OVERFLOW | SFFN_GEGLU):
+        raise ValueError("the backward pass covers the top-1 layer with ReLU experts: fwd must "
+                         "come from a k = 1 forward without SFFN_REROUTE_OVERFLOW or SFFN_GEGLU")
+    T, d, F, N = _check_layer(x, Wr, W1, b1, W2, b2, False)
     dt = _dtype_code(x)
     dev = x.device
+    _check("dy", dy, (T, d), x.dtype, dev)
+    _check("fwd['expert_idx']", fwd["expert_idx"], (T,), torch.int32, dev)
+    _check("fwd['slot']", fwd["slot"], (T,), torch.int32, dev)
     dx = torch.empty_like(x) if dx is None else dx
     dWr = torch.empty((N, d), dtype=torch.float32, device=dev) if dWr is None else dWr
     dW1 = torch.empty_like(W1) if dW1 is None else dW1
@@ -247,9 +307,18 @@ def switch_ffn_backward(x, Wr, W1, b1, W2, b2, CF: float, fwd: dict, dy, d_aux: 
         db1 = torch.empty_like(b1)
     if db2 is None and b2 is not None:
         db2 = torch.empty_like(b2)
+    _check("dx", dx, (T, d), x.dtype, dev)
+    _check("dWr", dWr, (N, d), torch.float32, dev)
+    _check("dW1", dW1, (N, F, d), x.dtype, dev)
+    _check("dW2", dW2, (N, d, F), x.dtype, dev)
+    _check("db1", db1, (N, F), x.dtype, dev, nullable=True)
+    _check("db2", db2, (N, d), x.dtype, dev, nullable=True)
+    _check_workspace("fwd['workspace']", fwd["workspace"],
+                     switch_ffn_workspace_bytes(T, d, F, N, CF, dt), dev)
     nbytes = switch_ffn_backward_workspace_bytes(T, d, F, N, CF, dt)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    _check_workspace("workspace", workspace, nbytes, dev)
     if stream is None:
         stream = torch.cuda.current_stream(dev).cuda_stream
     ev = None

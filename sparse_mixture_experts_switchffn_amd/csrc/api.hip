@@ -38,6 +38,7 @@ size_t workspace_layout(const Shape& s, Workspace* ws, char* base) {
   const size_t T = (size_t)s.T, N = (size_t)s.N, nb = (size_t)s.n_route_blocks;
   const size_t esize = s.dtype == SFFN_BF16 ? 2 : 4;
   Workspace w;
+  w.tag = (uint32_t*)take(kTagBytes);
   w.logits = (float*)take(T * N * sizeof(float));
   w.ppart = (float*)take(nb * N * sizeof(float));
   const size_t K = (size_t)s.k;
@@ -62,6 +63,21 @@ size_t workspace_layout(const Shape& s, Workspace* ws, char* base) {
   w.planes = (uint16_t*)take(sffn::router_planes_bytes(s));
   if (ws) *ws = w;
   return off;
+}
+
+WsTag make_tag(const Shape& s, uint32_t flags) {
+  WsTag t{};
+  t.w[kTagWMagic] = kTagMagic;
+  t.w[kTagWVersion] = kTagVersion;
+  t.w[kTagWK] = (uint32_t)s.k;
+  t.w[kTagWFlags] = flags;
+  t.w[kTagWT] = (uint32_t)s.T;
+  t.w[kTagWD] = (uint32_t)s.d;
+  t.w[kTagWF] = (uint32_t)s.F;
+  t.w[kTagWN] = (uint32_t)s.N;
+  t.w[kTagWC] = (uint32_t)s.C;
+  t.w[kTagWDtype] = (uint32_t)s.dtype;
+  return t;
 }
 
 }  // namespace sffn
@@ -198,7 +214,8 @@ int switch_ffn_forward_topk(const void* x, const float* Wr, const void* W1, cons
   if ((e = sffn::launch_dispatch_scan(s, ws, st)) != hipSuccess)
     return record_hip_error(e, kStageNames[2]);
   if ((e = mark(3)) != hipSuccess) return record_hip_error(e, "event record");
-  if ((e = sffn::launch_dispatch_scatter(s, in, ws, out, no_res, st)) != hipSuccess)
+  if ((e = sffn::launch_dispatch_scatter(s, in, ws, out, no_res, sffn::make_tag(s, flags), st)) !=
+      hipSuccess)
     return record_hip_error(e, kStageNames[3]);
   if ((e = mark(4)) != hipSuccess) return record_hip_error(e, "event record");
   if ((e = sffn::launch_ffn1(s, in, ws, st)) != hipSuccess)
@@ -218,8 +235,8 @@ const char* const kBwdStageNames[] = {"expert_dgrad_hidden", "router_grad",
                                       "expert_wgrad", "bias_grad"};
 constexpr int kNumBwdStages = (int)(sizeof(kBwdStageNames) / sizeof(kBwdStageNames[0]));
 
-// Backward scratch: dz [T, N] fp32 | dA [max_rows, F] | partial dg |
-// dXe [T, d] fp32 | partial dWr.
+// Backward scratch: checked offsets [N+1], counts [N] and the guard flag |
+// dz [T, N] fp32 | dA [max_rows, F] | partial dg | dXe [T, d] fp32 | partial dWr.
 size_t bwd_layout(const sffn::Shape& s, char* base, sffn::BwdState* b) {
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -229,12 +246,16 @@ size_t bwd_layout(const sffn::Shape& s, char* base, sffn::BwdState* b) {
   };
   const size_t T = (size_t)s.T, N = (size_t)s.N, esize = s.dtype == SFFN_BF16 ? 2 : 4;
   const int n_dgp = sffn::bwd_dgp_tiles(s), parts = sffn::bwd_wr_parts(s);
+  int* guard = (int*)take((2 * N + 2) * sizeof(int));
   float* dz = (float*)take(T * N * 4);
   void* dA = take((size_t)s.max_rows * s.F * esize + 16);
   float* dgp = (float*)take((size_t)n_dgp * s.max_rows * 4 + 4);
   float* dxe = (float*)take(T * s.d * 4);
   float* wrp = (float*)take((size_t)parts * N * s.d * 4);
   if (b) {
+    b->offset = guard;
+    b->hist = guard ? guard + N + 1 : nullptr;
+    b->bad = guard ? guard + 2 * N + 1 : nullptr;
     b->dz = dz;
     b->dA = dA;
     b->dgp = dgp;
@@ -280,16 +301,40 @@ int switch_ffn_backward(const void* x, const float* Wr, const void* W1, const vo
   if (!workspace || workspace_bytes < bwd_layout(s, nullptr, nullptr)) return SFFN_EWORKSPACE;
   if ((((uintptr_t)workspace | (uintptr_t)fwd_workspace) & 255) != 0) return SFFN_EUNSUPPORTED;
 
+  hipStream_t st = (hipStream_t)stream;
+  // The forward's layout tag (16 words at the start of its workspace) must name
+  // a top-1 forward without rerouting or GEGLU experts of this shape: the only
+  // form whose workspace this pass can read.  Read on the host while the
+  // stream is not being captured (it waits for the stream's earlier work);
+  // under capture the forward has not run yet, and the guard kernel checks the
+  // same tag on the device (see the header).
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  hipError_t he = hipStreamIsCapturing(st, &cap);
+  if (he != hipSuccess) return record_hip_error(he, "stream capture query");
+  if (cap == hipStreamCaptureStatusNone) {
+    uint32_t got[16];
+    he = hipMemcpyAsync(got, fwd_workspace, sizeof(got), hipMemcpyDeviceToHost, st);
+    if (he == hipSuccess) he = hipStreamSynchronize(st);
+    if (he != hipSuccess) return record_hip_error(he, "layout tag read");
+    const sffn::WsTag want = sffn::make_tag(s, 0u);
+    for (int i = 0; i < 16; ++i) {
+      const bool ok = i == sffn::kTagWFlags ? (got[i] & ~(uint32_t)SFFN_NO_RESIDUAL) == 0
+                                            : got[i] == want.w[i];
+      if (!ok) return SFFN_EINVAL;
+    }
+  }
+
   sffn::Workspace fw;
   sffn::workspace_layout(s, &fw, (char*)const_cast<void*>(fwd_workspace));
   sffn::BwdState b{};
   bwd_layout(s, (char*)workspace, &b);
+  b.fwd_tag = fw.tag;
+  b.fwd_offset = fw.offset;
+  b.fwd_hist = fw.hist;
   b.expert_idx = expert_idx;
   b.slot = slot;
-  b.offset = fw.offset;
   b.row2tok = fw.row2tok;
   b.rowgate = fw.rowgate;
-  b.hist = fw.hist;
   b.H = fw.H;
   b.logits = fw.logits;
   b.dy = dy;
@@ -301,7 +346,7 @@ int switch_ffn_backward(const void* x, const float* Wr, const void* W1, const vo
   b.dW2 = dW2;
   b.db2 = db2;
   const sffn::Inputs in{x, Wr, W1, b1, W2, b2};
-  const hipError_t e = sffn::launch_backward(s, in, b, (hipStream_t)stream, stage_events);
+  const hipError_t e = sffn::launch_backward(s, in, b, st, stage_events);
   if (e != hipSuccess) return record_hip_error(e, "backward");
   return SFFN_OK;
 }
@@ -311,10 +356,10 @@ int switch_ffn_forward_ex(const void* x, const float* Wr, const void* W1, const 
                           int64_t N, double CF, int dtype, void* y, int32_t* expert_idx,
                           int32_t* slot, float* gate, float* aux_loss, void* workspace,
                           size_t workspace_bytes, void* stream, uint32_t flags,
-                          const sffn_stats* stats, void* const* stage_events) {
+                          const sffn_stats* stats) {
   return switch_ffn_forward_topk(x, Wr, W1, b1, W2, b2, T, d, F, N, CF, 1, dtype, y, expert_idx,
                                  slot, gate, aux_loss, workspace, workspace_bytes, stream, flags,
-                                 stats, stage_events);
+                                 stats, nullptr);
 }
 
 int switch_ffn_forward(const void* x, const float* Wr, const void* W1, const void* b1,
@@ -323,8 +368,7 @@ int switch_ffn_forward(const void* x, const float* Wr, const void* W1, const voi
                        int32_t* slot, float* gate, float* aux_loss, void* workspace,
                        size_t workspace_bytes, void* stream) {
   return switch_ffn_forward_ex(x, Wr, W1, b1, W2, b2, T, d, F, N, CF, dtype, y, expert_idx, slot,
-                               gate, aux_loss, workspace, workspace_bytes, stream, 0u, nullptr,
-                               nullptr);
+                               gate, aux_loss, workspace, workspace_bytes, stream, 0u, nullptr);
 }
 
 }  // extern "C"

@@ -563,10 +563,14 @@ bwd_router_grad_kernel(const float* __restrict__ z, float* __restrict__ dz, cons
                        const int32_t* __restrict__ slot, const int* __restrict__ offset,
                        const int* __restrict__ hist, const float* __restrict__ dgp, int n_dgp,
                        int max_rows, const void* __restrict__ dyv, const void* __restrict__ b2v,
-                       int T, int d, int N, float d_aux) {
+                       int T, int d, int N, int C, float d_aux, const int* __restrict__ bad) {
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (t >= T) return;
+  if (*bad) {  // the forward's workspace failed the guard: every dz is NaN
+    for (int i = lane; i < N; i += 64) dz[(size_t)t * N + i] = __builtin_nanf("");
+    return;
+  }
   const float* zr = z + (size_t)t * N;
   float* dzr = dz + (size_t)t * N;
   float m = -INFINITY;
@@ -579,8 +583,10 @@ bwd_router_grad_kernel(const float* __restrict__ z, float* __restrict__ dz, cons
   for (int off = 32; off >= 1; off >>= 1) S += __shfl_xor(S, off);
   const float inv = 1.0f / S;
 
+  // A slot is accepted only below C for an expert in range (the caller's
+  // expert_idx and slot from the forward; anything else reads as dropped).
   const int e = expert_idx[t];
-  const int sl = slot[t];
+  const int sl = ((unsigned)e < (unsigned)N && slot[t] < C) ? slot[t] : -1;
   float dg = 0.f;
   if (sl >= 0) {
     const int row = offset[e] + sl;
@@ -1070,6 +1076,62 @@ bwd_bias_kernel(const void* __restrict__ dyv, const void* __restrict__ dAv,
 }
 
 // ---------------------------------------------------------------------------
+// Guard of the forward's workspace.  The pass reads the forward's dispatch maps
+// and H, which only a top-1 forward without rerouting or GEGLU experts, of this
+// very shape, lays out as read here; that forward leaves a layout tag at the
+// start of its workspace.  One block checks the tag and the expert offsets
+// (from 0, non-decreasing, at most max_rows rows; counts not negative) and
+// copies offsets and counts into the backward's own workspace, where every
+// later kernel reads them.  On a mismatch it writes empty experts there
+// instead, so that no later kernel indexes the forward's maps, and raises
+// `bad`: dz, and through it dx and dWr, comes out NaN, and the last kernel
+// fills the weight and bias gradients with NaN.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256)
+bwd_guard_kernel(const uint32_t* __restrict__ tag, const WsTag want, uint32_t flags_allowed,
+                 const int* __restrict__ offset, const int* __restrict__ hist, int N,
+                 int max_rows, int* __restrict__ offset_out, int* __restrict__ hist_out,
+                 int* __restrict__ bad) {
+  bool ok = true;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const uint32_t v = tag[i];
+    ok &= i == kTagWFlags ? (v & ~flags_allowed) == 0 : v == want.w[i];
+  }
+  if (ok) {
+    ok = offset[0] == 0 && offset[N] <= max_rows;
+    for (int i = threadIdx.x; i < N; i += 256) ok &= offset[i] <= offset[i + 1] && hist[i] >= 0;
+  }
+  ok = __syncthreads_and(ok);
+  for (int i = threadIdx.x; i <= N; i += 256) {
+    offset_out[i] = ok ? offset[i] : 0;
+    if (i < N) hist_out[i] = ok ? hist[i] : 0;
+  }
+  if (threadIdx.x == 0) *bad = ok ? 0 : 1;
+}
+
+// The weight and bias gradients as NaN after a failed guard (nothing otherwise).
+__global__ void __launch_bounds__(256)
+bwd_poison_kernel(const int* __restrict__ bad, void* __restrict__ dW1, void* __restrict__ dW2,
+                  void* __restrict__ db1, void* __restrict__ db2, size_t n_w, size_t n_b1,
+                  size_t n_b2, int esize) {
+  if (*bad == 0) return;
+  const size_t stride = (size_t)gridDim.x * 256;
+  const size_t i0 = (size_t)blockIdx.x * 256 + threadIdx.x;
+  auto fill = [&](void* p, size_t n) {
+    if (!p) return;
+    for (size_t i = i0; i < n; i += stride) {
+      if (esize == 2) ((uint16_t*)p)[i] = 0x7fc0u;
+      else ((uint32_t*)p)[i] = 0x7fc00000u;
+    }
+  };
+  fill(dW1, n_w);
+  fill(dW2, n_w);
+  fill(db1, n_b1);
+  fill(db2, n_b2);
+}
+
+// ---------------------------------------------------------------------------
 int bwd_dgp_tiles(const Shape& s) { return s.dtype == SFFN_BF16 ? (s.F + GN - 1) / GN : 1; }
 
 int bwd_wr_parts(const Shape& s) {
@@ -1117,6 +1179,12 @@ hipError_t launch_backward(const Shape& s, const Inputs& in, const BwdState& b, 
   const bool bf16 = s.dtype == SFFN_BF16;
   const int n_rows = s.max_rows;  // rows beyond offset[N] are never read
 
+  // 1. the guard: checked copies of the forward's offsets and counts
+  hipLaunchKernelGGL(bwd_guard_kernel, dim3(1), dim3(256), 0, st, b.fwd_tag, make_tag(s, 0u),
+                     (uint32_t)SFFN_NO_RESIDUAL, b.fwd_offset, b.fwd_hist, s.N, s.max_rows,
+                     b.offset, b.hist, b.bad);
+  SFFN_CHECK(hipGetLastError());
+
   // 2. E1: dA and partial dg
   SFFN_CHECK(mark());
   const int mt = bwd_rows_mt(s.C), n_mc = (s.C + 32 * mt - 1) / (32 * mt);
@@ -1141,12 +1209,12 @@ hipError_t launch_backward(const Shape& s, const Inputs& in, const BwdState& b, 
       hipLaunchKernelGGL(bwd_router_grad_kernel<true>, grid, dim3(256), 0, st, b.logits, b.dz,
                          b.expert_idx,
                          b.slot, b.offset, b.hist, b.dgp, b.n_dgp, s.max_rows, b.dy, in.b2, s.T,
-                         s.d, s.N, b.d_aux);
+                         s.d, s.N, s.C, b.d_aux, b.bad);
     else
       hipLaunchKernelGGL(bwd_router_grad_kernel<false>, grid, dim3(256), 0, st, b.logits, b.dz,
                          b.expert_idx,
                          b.slot, b.offset, b.hist, b.dgp, b.n_dgp, s.max_rows, b.dy, in.b2, s.T,
-                         s.d, s.N, b.d_aux);
+                         s.d, s.N, s.C, b.d_aux, b.bad);
     SFFN_CHECK(hipGetLastError());
   }
 
@@ -1242,6 +1310,10 @@ hipError_t launch_backward(const Shape& s, const Inputs& in, const BwdState& b, 
                          b.row2tok, b.rowgate, s.d, s.F, b.db1, b.db2);
     SFFN_CHECK(hipGetLastError());
   }
+  hipLaunchKernelGGL(bwd_poison_kernel, dim3(256), dim3(256), 0, st, b.bad, b.dW1, b.dW2, b.db1,
+                     b.db2, (size_t)s.N * s.d * s.F, (size_t)s.N * s.F, (size_t)s.N * s.d,
+                     bf16 ? 2 : 4);
+  SFFN_CHECK(hipGetLastError());
   SFFN_CHECK(mark());
 #undef SFFN_CHECK
   return hipSuccess;

@@ -26,7 +26,21 @@ struct Shape {
 inline bool two_choices(const Shape& s) { return s.k == 2 || s.reroute != 0; }
 // The logits go through the workspace (no fused router).
 
+// Layout tag: 16 words a forward call leaves at the start of its workspace, so
+// that a later call reading the workspace (the backward pass) can tell which
+// form of the layer carved it up and for which shape.
+constexpr uint32_t kTagMagic = 0x4E464653u;  // "SFFN" in little-endian bytes
+constexpr uint32_t kTagVersion = 1u;
+constexpr size_t kTagBytes = 256;  // the tag's region (16 words used)
+struct WsTag {
+  uint32_t w[16];  // magic, version, k, flags, T, d, F, N, C, dtype, rest 0
+};
+enum TagWord { kTagWMagic = 0, kTagWVersion, kTagWK, kTagWFlags, kTagWT, kTagWD, kTagWF,
+               kTagWN, kTagWC, kTagWDtype };
+WsTag make_tag(const Shape& s, uint32_t flags);
+
 struct Workspace {
+  uint32_t* tag;   // [16] layout tag (kTagBytes region)
   float* logits;   // [T, N] fp32 router logits
   float* ppart;    // [n_route_blocks, N] sum of p[t,i] over a block's tokens
   int* cnt;        // [n_route_blocks, N] top-1 counts per block (rerouting: then the
@@ -87,8 +101,10 @@ bool router_is_fused(const Shape& s);
 size_t router_planes_bytes(const Shape& s);
 // Rerouting: also the overflow count of the second stage and its scan.
 hipError_t launch_dispatch_scan(const Shape& s, const Workspace& ws, hipStream_t st);
+// Also writes the layout tag `tag` into ws.tag (block 0).
 hipError_t launch_dispatch_scatter(const Shape& s, const Inputs& in, const Workspace& ws,
-                                   const Outputs& out, bool no_residual, hipStream_t st);
+                                   const Outputs& out, bool no_residual, const WsTag& tag,
+                                   hipStream_t st);
 hipError_t launch_ffn1(const Shape& s, const Inputs& in, const Workspace& ws, hipStream_t st);
 hipError_t launch_ffn2(const Shape& s, const Inputs& in, const Workspace& ws, const Outputs& out,
                        bool no_residual, hipStream_t st);
@@ -100,12 +116,16 @@ hipError_t launch_combine(const Shape& s, const Inputs& in, const Workspace& ws,
 // backward's own scratch, and the gradients.
 struct BwdState {
   // from the forward
+  const uint32_t* fwd_tag;    // [16] the forward workspace's layout tag
+  const int* fwd_offset;      // [N+1] as the forward left them (read by the guard only)
+  const int* fwd_hist;        // [N]
   const int32_t* expert_idx;  // [T]
   const int32_t* slot;        // [T]
-  const int* offset;          // [N+1]
+  int* offset;                // [N+1] the guard's checked copy (backward workspace)
   const int* row2tok;         // [max_rows]
   const float* rowgate;       // [max_rows]
-  const int* hist;            // [N] top-1 counts
+  int* hist;                  // [N] top-1 counts, the guard's checked copy
+  int* bad;                   // [1] set by the guard when the forward workspace fails it
   const void* H;              // [max_rows, F] hidden activations (dtype)
   const float* logits;        // [T, N] fp32 router logits
   // upstream gradients

@@ -75,7 +75,14 @@ def _call(**over):
     return B.lib().switch_ffn_forward_ex(
         a["x"], a["Wr"], a["W1"], a["b1"], a["W2"], a["b2"], a["T"], a["d"], a["F"], a["N"],
         a["CF"], a["dtype"], a["y"], a["expert_idx"], a["slot"], a["gate"], a["aux"], a["ws"],
-        a["ws_bytes"], a["stream"], a["flags"], None, None)
+        a["ws_bytes"], a["stream"], a["flags"], None)
+
+
+def test_forward_ex_signature_is_forward_plus_flags_and_stats():
+    # switch_ffn_forward's 20 arguments, then flags and the nullable stats pointer.
+    assert len(B.lib().switch_ffn_forward.argtypes) == 20
+    assert len(B.lib().switch_ffn_forward_ex.argtypes) == 22
+    assert B.lib().switch_ffn_forward_ex.argtypes[:20] == B.lib().switch_ffn_forward.argtypes
 
 
 @pytest.mark.parametrize("over,code", [
@@ -146,3 +153,116 @@ def test_workspace_bytes_topk():
     assert two > one + 8192 * 3072 * 2 + 2 * 8192 * 768 * 2 - 8192 * 768 * 2
     assert S.switch_ffn_workspace_bytes_topk(8192, 768, 3072, 1, 1.25, 2, S.SFFN_BF16) == 0
     assert S.switch_ffn_workspace_bytes_topk(8192, 768, 3072, 64, 1.25, 3, S.SFFN_BF16) == 0
+
+
+def _call_bwd(**over):
+    # Fake, never-dereferenced addresses: every case below is rejected before the
+    # layout tag is read or anything is enqueued.
+    fake = 0x100000
+    T, d, F, N, CF, dt = 64, 32, 64, 4, 1.0, S.SFFN_BF16
+    fwd_need = S.switch_ffn_workspace_bytes(T, d, F, N, CF, dt)
+    bwd_need = S.switch_ffn_backward_workspace_bytes(T, d, F, N, CF, dt)
+    a = dict(x=fake, Wr=fake, W1=fake, b1=None, W2=fake, b2=None, T=T, d=d, F=F, N=N, CF=CF,
+             dtype=dt, expert_idx=fake, slot=fake, fws=fake, fws_bytes=fwd_need, dy=fake,
+             d_aux=0.01, dx=fake, dWr=fake, dW1=fake, db1=None, dW2=fake, db2=None, ws=fake,
+             ws_bytes=bwd_need, stream=None)
+    a.update(over)
+    return B.lib().switch_ffn_backward(
+        a["x"], a["Wr"], a["W1"], a["b1"], a["W2"], a["b2"], a["T"], a["d"], a["F"], a["N"],
+        a["CF"], a["dtype"], a["expert_idx"], a["slot"], a["fws"], a["fws_bytes"], a["dy"],
+        a["d_aux"], a["dx"], a["dWr"], a["dW1"], a["db1"], a["dW2"], a["db2"], a["ws"],
+        a["ws_bytes"], a["stream"], None)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(x=None), S.SFFN_EINVAL), (dict(Wr=None), S.SFFN_EINVAL), (dict(W1=None), S.SFFN_EINVAL),
+    (dict(W2=None), S.SFFN_EINVAL), (dict(expert_idx=None), S.SFFN_EINVAL),
+    (dict(slot=None), S.SFFN_EINVAL), (dict(fws=None), S.SFFN_EINVAL),
+    (dict(dy=None), S.SFFN_EINVAL), (dict(dx=None), S.SFFN_EINVAL),
+    (dict(dWr=None), S.SFFN_EINVAL), (dict(dW1=None), S.SFFN_EINVAL),
+    (dict(dW2=None), S.SFFN_EINVAL), (dict(d_aux=math.nan), S.SFFN_EINVAL),
+    (dict(d_aux=math.inf), S.SFFN_EINVAL), (dict(T=0), S.SFFN_EINVAL), (dict(N=0), S.SFFN_EINVAL),
+    (dict(CF=-1.0), S.SFFN_EINVAL), (dict(dtype=5), S.SFFN_EDTYPE),
+    (dict(N=5000), S.SFFN_EUNSUPPORTED), (dict(d=36), S.SFFN_EUNSUPPORTED),
+    (dict(dy=0x100004), S.SFFN_EUNSUPPORTED), (dict(dx=0x100008), S.SFFN_EUNSUPPORTED),
+    (dict(dW1=0x100002), S.SFFN_EUNSUPPORTED), (dict(dW2=0x100002), S.SFFN_EUNSUPPORTED),
+    (dict(fws_bytes=1000), S.SFFN_EWORKSPACE), (dict(ws=None), S.SFFN_EWORKSPACE),
+    (dict(ws_bytes=1000), S.SFFN_EWORKSPACE), (dict(ws=0x100010), S.SFFN_EUNSUPPORTED),
+    (dict(fws=0x100010), S.SFFN_EUNSUPPORTED),
+])
+def test_backward_rejects_before_launch(over, code):
+    assert _call_bwd(**over) == code
+
+
+def test_backward_workspace_bytes():
+    one = S.switch_ffn_backward_workspace_bytes(8192, 768, 3072, 64, 1.25, S.SFFN_BF16)
+    # dz [T, N] fp32, dA [rows, F] bf16 and the expert part of dx [T, d] fp32 at least
+    assert one > 8192 * 64 * 4 + 8192 * 3072 * 2 + 8192 * 768 * 4
+    assert S.switch_ffn_backward_workspace_bytes(8192, 768, 3072, 64, 1.25, 9) == 0
+    assert S.switch_ffn_backward_workspace_bytes(0, 768, 3072, 64, 1.25, S.SFFN_BF16) == 0
+
+
+# ---------------------------------------------------------------------------
+# The binding refuses tensors the C-ABI would read wrongly (CPU tensors stand in:
+# every check below fires before anything reaches the library).
+# ---------------------------------------------------------------------------
+def _layer(T=16, d=8, F=16, N=4, dtype=None, device="cpu"):
+    import torch
+    dt = torch.bfloat16 if dtype is None else dtype
+    return dict(x=torch.zeros(T, d, dtype=dt, device=device),
+                Wr=torch.zeros(N, d, dtype=torch.float32, device=device),
+                W1=torch.zeros(N, F, d, dtype=dt, device=device), b1=None,
+                W2=torch.zeros(N, d, F, dtype=dt, device=device), b2=None)
+
+
+def _fwd(L, **kw):
+    return B.switch_ffn_forward(L["x"], L["Wr"], L["W1"], L["b1"], L["W2"], L["b2"], 1.0, **kw)
+
+
+def test_binding_rejects_wrong_dtypes_and_shapes():
+    import torch
+    L = _layer()
+    with pytest.raises(TypeError):
+        _fwd(dict(L, x=L["x"].to(torch.float16)))
+    with pytest.raises(TypeError):
+        _fwd(dict(L, Wr=L["Wr"].to(torch.bfloat16)))          # the router is fp32
+    with pytest.raises(TypeError):
+        _fwd(dict(L, W1=L["W1"].float()))                      # experts share x's dtype
+    with pytest.raises(TypeError):
+        _fwd(dict(L, W2=L["W2"].float()))
+    with pytest.raises(TypeError):
+        _fwd(dict(L, b1=torch.zeros(4, 16, dtype=torch.float32)))
+    with pytest.raises(ValueError):
+        _fwd(dict(L, W1=torch.zeros(4, 8, 16, dtype=torch.bfloat16)))   # [N, d, F]: transposed
+    with pytest.raises(ValueError):
+        _fwd(dict(L, W2=torch.zeros(4, 16, 16, dtype=torch.bfloat16)))
+    with pytest.raises(ValueError):
+        _fwd(dict(L, Wr=torch.zeros(4, 9, dtype=torch.float32)))
+    with pytest.raises(ValueError):
+        _fwd(dict(L, b2=torch.zeros(4, 16, dtype=torch.bfloat16)))
+    with pytest.raises(ValueError):
+        _fwd(dict(L, x=L["x"][:, None]))                        # not [T, d]
+    with pytest.raises(ValueError):
+        _fwd(L, flags=B.SFFN_GEGLU)                             # GEGLU needs W1 [N, 2F, d]
+    with pytest.raises(ValueError):
+        _fwd(L, k=3)
+
+
+def test_binding_rejects_strided_and_host_tensors():
+    import torch
+    L = _layer()
+    with pytest.raises(ValueError):
+        _fwd(dict(L, x=torch.zeros(8, 16, dtype=torch.bfloat16).t()))   # a transposed view
+    with pytest.raises(ValueError):
+        _fwd(dict(L, W1=torch.zeros(4, 8, 16, dtype=torch.bfloat16).transpose(1, 2)))
+    with pytest.raises(ValueError, match="GPU"):
+        _fwd(L)                                                 # host memory
+
+
+def test_binding_backward_refuses_other_forward_forms():
+    L = _layer()
+    for fwd in (dict(k=2, flags=0), dict(k=1, flags=B.SFFN_REROUTE_OVERFLOW),
+                dict(k=1, flags=B.SFFN_GEGLU)):
+        with pytest.raises(ValueError, match="top-1"):
+            B.switch_ffn_backward(L["x"], L["Wr"], L["W1"], L["b1"], L["W2"], L["b2"], 1.0, fwd,
+                                  L["x"], 0.0)

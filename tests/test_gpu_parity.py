@@ -189,7 +189,14 @@ def test_stored_router_logits(case, k, reroute):
     out = sffn.switch_ffn_forward(dev_in["x"], dev_in["Wr"], dev_in["W1"], dev_in["b1"],
                                   dev_in["W2"], dev_in["b2"], w.CF, flags=flags, k=k)
     torch.cuda.synchronize()
-    z = out["workspace"][: w.T * w.N * 4].view(torch.float32).cpu().numpy().reshape(w.T, w.N)
+    # the header: a 16-word layout tag in the first 256 bytes, the logits from byte 256
+    tag = out["workspace"][:64].view(torch.int32).cpu().numpy().view(np.uint32)
+    C = sffn.switch_ffn_capacity(k * w.T, w.N, w.CF)
+    want = [0x4E464653, 1, k, flags, w.T, w.d, w.F, w.N, min(C, w.T),
+            sffn.SFFN_BF16 if w.dtype == "bf16" else sffn.SFFN_FP32] + [0] * 6
+    assert list(tag) == want, list(tag)
+    z = out["workspace"][256: 256 + w.T * w.N * 4].view(torch.float32).cpu().numpy().reshape(
+        w.T, w.N)
     x64 = synth.decode(host_x(w))
     Wr64 = synth.decode(synth.host_array(w, "Wr").reshape(w.N, w.d))
     ref = oracle.router_logits(x64, Wr64)
