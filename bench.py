@@ -16,10 +16,16 @@ inputs already resident in HBM.  Prints ONE JSON line:
               when the kernel source changed since it was measured
   cpu_baseline the CPU oracle (float64 numpy) timed on this host on a bounded
               sample of the same workload
-Default workload: Switch-Base-like (T=8192 tokens, d_model 768, d_ff 3072, 64
-experts, CF 1.25, bf16 experts, fp32 router).  Variants of the step: --topk 2 (top-2
-routing), --reroute (No-Token-Left-Behind), --geglu (GEGLU experts), --backward (a
-training step: forward then backward; metric "SwitchFFN fwd+bwd tokens/s").
+              (many_expert: the bounded sample described in cpu_baseline_extrapolated),
+              with the host's CPUs and one-thread rates of Tiny and Switch-Base-like
+  roofline.layer  the whole layer's minimum HBM bytes (the weights of experts with
+              accepted tokens, Wr, x read once, y written once) / ms_per_step
+Default workload: the many-expert Switch-C-shaped layer, the largest configuration
+that fits one GPU (T=65536 tokens, d_model 2080, d_ff 6144, 2048 experts, CF 1.0,
+105 GB of bf16 expert weights, fp32 router).  --config picks another (tiny,
+switch_base, skewed, switch_large).  Variants of the step: --topk 2 (top-2 routing),
+--reroute (No-Token-Left-Behind), --geglu (GEGLU experts), --backward (a training
+step: forward then backward; metric "SwitchFFN fwd+bwd tokens/s").
 """
 from __future__ import annotations
 
@@ -48,7 +54,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--config", default="switch_base",
+    p.add_argument("--config", default="many_expert",
                    help="workload: tiny, switch_base, skewed, switch_large, many_expert")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="CPU work budget of the oracle baseline (0 = skip)")
@@ -257,18 +263,129 @@ def backward_bytes(w, stage, accepted, active, esize, parts):
     return None
 
 
-def cpu_baseline(w, budget_s, args):
-    """The oracle as it stands on this host: full forward passes until the budget is used."""
+def host_cpu():
+    """The host the oracle runs on: logical CPUs, the ones this process may use, the CPU
+    model and the BLAS thread count numpy's matmuls use."""
+    info = {"nproc": os.cpu_count()}
+    try:
+        info["affinity_cpus"] = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        pass
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                info["model"] = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    info["omp_num_threads"] = os.environ.get("OMP_NUM_THREADS")
+    try:
+        from threadpoolctl import threadpool_info
+        info["blas_threads"] = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        info["blas_threads"] = int(os.environ.get("OMP_NUM_THREADS", "1"))
+    return info
+
+
+def one_thread_rates(args):
+    """The oracle's forward on Tiny and Switch-Base-like with numpy's BLAS on one thread
+    (tokens/s; Tiny repeated for about a second, Switch-Base-like one pass)."""
+    import oracle
+    import switchffn_synth as synth
+    from threadpoolctl import threadpool_limits
+
+    out = {}
+    for name, min_s in (("tiny", 1.0), ("switch_base", 0.0)):
+        w = synth.workload(name)
+        dec = {k: synth.decode(v) for k, v in synth.host_inputs(w).items()}
+        experts = (dec["W1"], dec["b1"], dec["W2"], dec["b2"])
+        with threadpool_limits(limits=1):
+            passes, t0 = 0, time.perf_counter()
+            while True:
+                oracle.forward(dec["x"], dec["Wr"], experts, w.CF, w.dtype)
+                passes += 1
+                el = time.perf_counter() - t0
+                if el >= min_s or passes >= 10000:
+                    break
+        out[name] = {"tokens_per_s": w.T * passes / el, "passes": passes, "seconds": el}
+        log(args, f"cpu_baseline: {name} on one thread, {passes} passes in {el:.2f} s")
+    return out
+
+
+def cpu_baseline_extrapolated(w, args):
+    """The many-expert oracle, bounded: the router (logits, softmax, top-1), dispatch and
+    aux loss over every token, and the expert FFNs of 64 experts stratified by load;
+    the FFN time is scaled by A / A_subset (accepted rows) to the whole layer."""
     import numpy as np
 
     import oracle
     import switchffn_synth as synth
 
+    log(args, f"cpu_baseline: drawing x and Wr for {w.name}")
+    x = synth.decode(synth.host_array(w, "x").reshape(w.T, w.d))
+    Wr = synth.decode(synth.host_array(w, "Wr").reshape(w.N, w.d))
+    C = oracle.capacity(w.T, w.N, w.CF)
+    # routing only (no expert computed): the router, dispatch and aux loss in full
+    t0 = time.perf_counter()
+    r0 = oracle.forward(x, Wr, lambda e: None, w.CF, w.dtype, only_experts=[])
+    t_route = time.perf_counter() - t0
+    acc = r0["accepted"]
+    order = np.argsort(acc, kind="stable")
+    pick = sorted(int(order[i]) for i in np.linspace(0, w.N - 1, 64).round().astype(int))
+    A, A_sub = int(acc.sum()), int(acc[pick].sum())
+    log(args, f"cpu_baseline: routing {t_route:.1f} s; drawing 64 experts' weights "
+              f"({A_sub} of {A} accepted rows)")
+    raw = {e: synth.expert_weights_host(w, e) for e in pick}
+
+    def experts(e):
+        ew = raw[e]
+        return (synth.decode(ew["W1"]), synth.decode(ew["b1"]), synth.decode(ew["W2"]),
+                synth.decode(ew["b2"]))
+
+    t0 = time.perf_counter()
+    oracle.forward(x, Wr, experts, w.CF, w.dtype, only_experts=pick)
+    t_sub = time.perf_counter() - t0
+    t_ffn = max(t_sub - t_route, 0.0) * A / max(A_sub, 1)
+    total = t_route + t_ffn
+    log(args, f"cpu_baseline: routing + 64 experts {t_sub:.1f} s; extrapolated layer "
+              f"{total:.1f} s")
+    return {"value": w.T / total, "unit": "tokens/s", "kind": "oracle",
+            "extrapolated": True,
+            "sample": (f"{w.name}: router, softmax, top-1, dispatch and aux loss of all "
+                       f"{w.T} tokens in full ({t_route:.1f} s, float64 numpy); expert FFNs of "
+                       f"64 of {w.N} experts stratified by load ({A_sub} of {A} accepted rows, "
+                       f"{t_sub - t_route:.1f} s), extrapolated by A/A_subset to "
+                       f"{t_ffn:.1f} s: layer {total:.1f} s (extrapolated)"),
+            "seconds": {"routing": t_route, "ffn_subset": t_sub - t_route,
+                        "ffn_extrapolated": t_ffn}, "capacity": C}
+
+
+def cpu_baseline(w, budget_s, args):
+    """The oracle as it stands on this host: full forward passes until the budget is used
+    (many_expert: the bounded, extrapolated sample of cpu_baseline_extrapolated), with the
+    host's description and one-thread rates of the two small workloads beside it."""
+    host = host_cpu()
+    if w.name == "many_expert" and not (args.backward or args.reroute or args.topk != 1
+                                        or w.glu):
+        out = cpu_baseline_extrapolated(w, args)
+    else:
+        out = cpu_baseline_full(w, budget_s, args)
+    out["cores"] = host["blas_threads"]
+    out["host"] = host
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # noqa: BLE001
-        threads = int(os.environ.get("OMP_NUM_THREADS", "1"))
+        out["one_thread"] = one_thread_rates(args)
+    except Exception as exc:  # noqa: BLE001 -- a reference figure only
+        out["one_thread"] = {"error": str(exc)[:200]}
+    return out
+
+
+def cpu_baseline_full(w, budget_s, args):
+    """Full forward (or training-step) passes of the oracle until the budget is used."""
+    import numpy as np
+
+    import oracle
+    import switchffn_synth as synth
+
     log(args, f"cpu_baseline: drawing inputs for {w.name}")
     host = synth.host_inputs(w, max_elems=1 << 31)
     dec = {k: synth.decode(v) for k, v in host.items()}
@@ -292,7 +409,8 @@ def cpu_baseline(w, budget_s, args):
     log(args, f"cpu_baseline: {passes} passes in {el:.2f} s")
     kind = "forward + backward" if getattr(args, "backward", False) else "forward"
 
-    return {"value": w.T * passes / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+    return {"value": w.T * passes / el, "unit": "tokens/s", "kind": "oracle",
+            "extrapolated": False,
             "sample": f"{passes} full {kind} pass(es) of the {w.name} workload "
                       f"(T={w.T}) in float64 numpy, {el:.1f} s"}
 
@@ -488,6 +606,9 @@ def main():
     wname = (w.name + ("_top2" if K == 2 else "") + ("_reroute" if args.reroute else "")
              + ("_geglu" if w.glu else "") + ("_train" if BWD else ""))
     traffic = measured_traffic(dominant, wname)
+    w1mul = 2 if w.glu else 1
+    layer_bytes = (active * (w1mul + 1) * w.F * w.d * esize + N * w.d * 4 + 2 * T * w.d * esize
+                   + (active * (w1mul * w.F + w.d) * esize if w.has_bias else 0))
 
     result = {
         "metric": "SwitchFFN fwd+bwd tokens/s" if BWD else "SwitchFFN fwd tokens/s",
@@ -511,7 +632,12 @@ def main():
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": (achieved / HBM_PEAK_GBS) if achieved else None,
-                     "traffic": traffic, "algorithmic_bytes": alg},
+                     "traffic": traffic, "algorithmic_bytes": alg,
+                     "layer": {"bytes": layer_bytes, "ms_per_step": ms_per_step,
+                               "GB_per_s": layer_bytes / (ms_per_step * 1e-3) / 1e9,
+                               "frac": layer_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                               "note": "weights of experts with accepted tokens (W1, W2, "
+                                       "biases), Wr, x read once and y written once"}},
         "stages_ms": all_ms,
         "stages": stage_table,
         "per_call_ms": {"median": pct(0.5), "p10": pct(0.1), "p90": pct(0.9),
@@ -527,7 +653,8 @@ def main():
     }
     del inp, bufs, out
     torch.cuda.empty_cache()
-    if args.cpu_seconds > 0 and w.name != "many_expert":
+    if args.cpu_seconds > 0 and (w.name != "many_expert" or not (BWD or args.reroute or K != 1
+                                                                  or w.glu)):
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, args)
     else:
         result["cpu_baseline"] = None
