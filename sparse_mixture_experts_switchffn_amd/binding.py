@@ -46,6 +46,12 @@ def load_library(path: str = LIB_PATH):
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: the HIP library must be built "
                            "(__graft_entry__.build()); there is no fallback path")
+    # One HIP runtime per process: torch ships its own libamdhip64 (soname
+    # libamdhip64.so.7) and asks for it by another name, so if this library
+    # loaded the system's copy first, torch would load a second runtime beside
+    # it and the two would not share the device.  With torch loaded first, the
+    # library's libamdhip64.so.7 resolves to torch's copy.
+    import torch  # noqa: F401
     L = ctypes.CDLL(path)
     L.switch_ffn_capacity.restype = ctypes.c_int64
     L.switch_ffn_capacity.argtypes = [_I64, _I64, ctypes.c_double]

@@ -33,7 +33,12 @@ def _load_dev():
     if _dev is None:
         if not os.path.exists(DEV_LIB):
             raise RuntimeError(f"{DEV_LIB} is missing; run __graft_entry__.build() first")
+        # torch first, so that this library binds to torch's HIP runtime rather than
+        # loading a second one (torch bundles libamdhip64 under the same soname).
+        import torch  # noqa: F401
         lib = ctypes.CDLL(DEV_LIB)
+        lib.synth_error_string.restype = ctypes.c_char_p
+        lib.synth_error_string.argtypes = [ctypes.c_int]
         lib.synth_fill_device.restype = ctypes.c_int
         lib.synth_fill_device.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
                                           ctypes.c_uint64, ctypes.c_uint64, ctypes.c_float,
@@ -53,6 +58,8 @@ def fill_host(out: np.ndarray, start: int, seed: int, stream: int, sigma: float,
 
 def fill_device(ptr: int, n: int, start: int, seed: int, stream: int, sigma: float, bf16: bool,
                 hip_stream: int) -> None:
-    rc = _load_dev().synth_fill_device(ptr, n, start, seed, stream, sigma, int(bf16), hip_stream)
+    lib = _load_dev()
+    rc = lib.synth_fill_device(ptr, n, start, seed, stream, sigma, int(bf16), hip_stream)
     if rc != 0:
-        raise RuntimeError(f"synth_fill_device failed ({rc})")
+        why = lib.synth_error_string(rc).decode() if rc > 0 else "bad arguments"
+        raise RuntimeError(f"synth_fill_device failed ({rc}: {why})")

@@ -28,5 +28,10 @@ extern "C" int synth_fill_device(void* out, int64_t n, int64_t start, uint64_t s
   if (blocks > 65536) blocks = 65536;
   hipLaunchKernelGGL(synth_fill_kernel, dim3((unsigned)blocks), dim3(256), 0,
                      (hipStream_t)stream, out, n, start, key, sigma, as_bf16);
-  return hipGetLastError() == hipSuccess ? 0 : -2;
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? 0 : (int)e;  // the HIP error code (positive)
+}
+
+extern "C" const char* synth_error_string(int code) {
+  return hipGetErrorString((hipError_t)code);
 }
