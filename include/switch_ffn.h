@@ -71,6 +71,7 @@ extern "C" {
 #define SFFN_EWORKSPACE (-3)   /* workspace NULL or smaller than switch_ffn_workspace_bytes() */
 #define SFFN_EUNSUPPORTED (-4) /* shape or alignment outside this library's limits (see below) */
 #define SFFN_EHIP (-5)         /* a HIP launch failed */
+#define SFFN_ESCRATCH (-6)     /* switch_ffn_forward_noalloc: the shape needs more than its scratch */
 
 /* Element types of x, W1, b1, W2, b2 and y. */
 #define SFFN_FP32 0
@@ -252,6 +253,29 @@ const char* switch_ffn_backward_stage_name(int stage);
  * ("router_logits", "softmax_route", ...); NULL for an index out of range. */
 int switch_ffn_num_stages(void);
 const char* switch_ffn_stage_name(int stage);
+
+/* Allocation-free forward, for callers that cannot allocate device memory
+ * (code under stream capture, tight serving loops, harnesses that forbid
+ * allocation).  switch_ffn_forward with the same arguments minus the
+ * workspace: the workspace is a file-scope device array of
+ * SFFN_NOALLOC_SCRATCH_MIB MiB inside the library (each GPU the library runs
+ * on holds its own copy from the first call there until the process ends),
+ * looked up once per device with that device current.  The call allocates
+ * nothing.  Shapes whose switch_ffn_workspace_bytes() exceeds
+ * switch_ffn_noalloc_scratch_bytes() return SFFN_ESCRATCH before anything is
+ * enqueued (64 MiB covers the Switch-Base-like layer: T = 8192, d = 768,
+ * F = 3072, N = 64); other errors are switch_ffn_forward's.  Every call on one
+ * GPU uses that GPU's one array, which keeps the last call's contents (the
+ * forward needs nothing cleared): calls that overlap on one GPU -- on
+ * different streams, or from different threads, without ordering between
+ * them -- race on it, and a backward pass cannot use this forward's
+ * workspace.  Outputs as switch_ffn_forward's. */
+#define SFFN_NOALLOC_SCRATCH_MIB 64
+size_t switch_ffn_noalloc_scratch_bytes(void);
+int switch_ffn_forward_noalloc(const void* x, const float* Wr, const void* W1, const void* b1,
+                               const void* W2, const void* b2, int64_t T, int64_t d, int64_t F,
+                               int64_t N, double CF, int dtype, void* y, int32_t* expert_idx,
+                               int32_t* slot, float* gate, float* aux_loss, void* stream);
 
 /* Static description of a status code; for SFFN_EHIP, the text of the last
  * HIP error seen on this thread. */

@@ -9,6 +9,7 @@ from .binding import (  # noqa: F401
     SFFN_BF16,
     SFFN_EDTYPE,
     SFFN_EHIP,
+    SFFN_ESCRATCH,
     SFFN_EINVAL,
     SFFN_EUNSUPPORTED,
     SFFN_EWORKSPACE,
@@ -27,7 +28,9 @@ from .binding import (  # noqa: F401
     switch_ffn_capacity,
     switch_ffn_forward,
     switch_ffn_forward_ex,
+    switch_ffn_forward_noalloc,
     switch_ffn_forward_topk,
+    switch_ffn_noalloc_scratch_bytes,
     switch_ffn_num_stages,
     switch_ffn_stage_name,
     switch_ffn_status_string,

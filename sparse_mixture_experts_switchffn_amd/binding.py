@@ -21,6 +21,7 @@ SFFN_EDTYPE = -2
 SFFN_EWORKSPACE = -3
 SFFN_EUNSUPPORTED = -4
 SFFN_EHIP = -5
+SFFN_ESCRATCH = -6
 SFFN_FP32 = 0
 SFFN_BF16 = 1
 SFFN_NO_RESIDUAL = 1
@@ -83,6 +84,10 @@ def load_library(path: str = LIB_PATH):
     L.switch_ffn_num_stages.argtypes = []
     L.switch_ffn_stage_name.restype = ctypes.c_char_p
     L.switch_ffn_stage_name.argtypes = [ctypes.c_int]
+    L.switch_ffn_noalloc_scratch_bytes.restype = ctypes.c_size_t
+    L.switch_ffn_noalloc_scratch_bytes.argtypes = []
+    L.switch_ffn_forward_noalloc.restype = ctypes.c_int
+    L.switch_ffn_forward_noalloc.argtypes = _FWD_ARGS[:17] + [_P]
     L.switch_ffn_status_string.restype = ctypes.c_char_p
     L.switch_ffn_status_string.argtypes = [ctypes.c_int]
     return L
@@ -135,6 +140,35 @@ def switch_ffn_num_stages() -> int:
 def switch_ffn_stage_name(i: int):
     s = lib().switch_ffn_stage_name(i)
     return None if s is None else s.decode()
+
+
+def switch_ffn_noalloc_scratch_bytes() -> int:
+    return lib().switch_ffn_noalloc_scratch_bytes()
+
+
+def switch_ffn_forward_noalloc(x, Wr, W1, b1, W2, b2, CF: float, *, y, expert_idx, slot, gate,
+                               aux_loss, stream=None, check: bool = True) -> int:
+    """The allocation-free forward into caller-given outputs (no workspace argument: the
+    library's built-in scratch).  Allocates nothing; returns the status."""
+    import torch
+
+    T, d, F, N = _check_layer(x, Wr, W1, b1, W2, b2, False)
+    dev = x.device
+    _check("y", y, (T, d), x.dtype, dev)
+    _check("expert_idx", expert_idx, (T,), torch.int32, dev)
+    _check("slot", slot, (T,), torch.int32, dev)
+    _check("gate", gate, (T,), torch.float32, dev)
+    _check("aux_loss", aux_loss, (1,), torch.float32, dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = lib().switch_ffn_forward_noalloc(
+        _ptr(x), _ptr(Wr), _ptr(W1), _ptr(b1), _ptr(W2), _ptr(b2), T, d, F, N, CF,
+        _dtype_code(x), _ptr(y), _ptr(expert_idx), _ptr(slot), _ptr(gate), _ptr(aux_loss),
+        stream)
+    if check and rc != SFFN_OK:
+        raise RuntimeError(f"switch_ffn_forward_noalloc failed ({rc}): "
+                           f"{switch_ffn_status_string(rc)}")
+    return rc
 
 
 def switch_ffn_status_string(status: int) -> str:

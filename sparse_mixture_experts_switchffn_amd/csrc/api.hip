@@ -19,12 +19,14 @@ size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 bool aligned16(const void* p) { return p == nullptr || ((uintptr_t)p & 15) == 0; }
 
-int record_hip_error(hipError_t e, const char* what) {
+}  // namespace
+
+int sffn::record_hip_error(hipError_t e, const char* what) {
   snprintf(g_hip_error, sizeof(g_hip_error), "%s: %s", what, hipGetErrorString(e));
   return SFFN_EHIP;
 }
 
-}  // namespace
+using sffn::record_hip_error;
 
 namespace sffn {
 
@@ -160,6 +162,9 @@ const char* switch_ffn_status_string(int status) {
              "needs d, F "
              "multiples of 8 and 16-byte aligned x, Wr, W1, W2, y; workspace 256-byte aligned)";
     case SFFN_EHIP: return g_hip_error;
+    case SFFN_ESCRATCH:
+      return "the shape needs more workspace than switch_ffn_forward_noalloc's built-in scratch "
+             "(switch_ffn_noalloc_scratch_bytes())";
     default: return "unknown status";
   }
 }

@@ -67,6 +67,9 @@ struct Workspace {
   uint16_t* planes;  // router weights split into three bf16 planes, fragment order (fused router)
 };
 
+// Records the HIP error text for switch_ffn_status_string and returns SFFN_EHIP.
+int record_hip_error(hipError_t e, const char* what);
+
 // Bytes of each region, in order, 256-byte aligned; returns the total.
 size_t workspace_layout(const Shape& s, Workspace* ws, char* base);
 

@@ -266,3 +266,20 @@ def test_binding_backward_refuses_other_forward_forms():
         with pytest.raises(ValueError, match="top-1"):
             B.switch_ffn_backward(L["x"], L["Wr"], L["W1"], L["b1"], L["W2"], L["b2"], 1.0, fwd,
                                   L["x"], 0.0)
+
+
+def test_noalloc_rejects_before_any_device_call():
+    fake = 0x100000
+    L = B.lib()
+    assert L.switch_ffn_noalloc_scratch_bytes() == 64 << 20
+
+    def call(T=8192, d=768, F=3072, N=64, CF=1.25, dtype=S.SFFN_BF16, x=fake):
+        return L.switch_ffn_forward_noalloc(x, fake, fake, None, fake, None, T, d, F, N, CF, dtype,
+                                            fake, fake, fake, fake, fake, None)
+    assert call(T=65536, d=2080, F=6144, N=2048, CF=1.0) == S.SFFN_ESCRATCH
+    assert call(T=32768, d=1024, F=4096, N=128) == S.SFFN_ESCRATCH
+    assert call(T=0) == S.SFFN_EINVAL
+    assert call(x=None) == S.SFFN_EINVAL
+    assert call(dtype=4) == S.SFFN_EDTYPE
+    assert call(d=36) == S.SFFN_EUNSUPPORTED
+    assert "scratch" in S.switch_ffn_status_string(S.SFFN_ESCRATCH)
