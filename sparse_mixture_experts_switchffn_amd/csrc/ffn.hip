@@ -86,8 +86,7 @@ constexpr int kCpolSplitRows = -1;
 constexpr int kCpolShiftOdd = -2;
 constexpr int FBK = 64;              // k per step (one 128-byte chunk row)
 constexpr int FLDS = FBK + 8;        // bf16 per row of a weight slot (144 B: rows 4 banks apart)
-constexpr int FP = SFFN_FFN_STAGES;  // k-steps in flight
-constexpr int FNB = FP + 1;          // activation tiles in the LDS ring
+constexpr int kFfnStages = SFFN_FFN_STAGES;  // k-steps in flight (two for split-row tiles)
 constexpr int kLdsBytes = 160 * 1024;
 
 // Kinds of pipeline round (FP steps): the first of a tile, a middle one, and
@@ -99,35 +98,47 @@ __device__ __forceinline__ float gelu_f32(float a) {
   return 0.5f * a * (1.0f + erff(a * 0.7071067811865476f));
 }
 
-template <int MT, int FW, int WN, bool SECOND, bool GLU = false>
+template <int MT, int FW, int WN, bool SECOND, bool GLU = false, int HV = 1>
 struct FfnGeom {
   // GEGLU (FFN1 only): a tile's COLS weight rows are its "virtual columns": in
   // each epilogue part of PCOLS of them, the first half are gate rows and the
   // second half the linear rows of the same PCOLS/2 features, so a part holds
   // both factors of its outputs.  The stage is fp32 then, as for FFN2.
   static_assert(!(SECOND && GLU), "GEGLU is an FFN1 form");
+  // Split rows (HV = 2): the waves form HV row parts of FW/HV column groups;
+  // the two waves of a column group (one per part) each load half of the
+  // group's weight rows into a slot they share, and each computes its own
+  // MT row tiles against the whole slot, so a tile of HV*MT*32 rows streams
+  // each weight byte once.  The shared slots are double-buffered and the
+  // step's barrier publishes them; two k-steps stay in flight (the 320-row
+  // activation tiles of 40 KB fill the LDS).
+  static_assert(HV == 1 || HV == 2, "one or two row parts");
   static constexpr bool F32STAGE = SECOND || GLU;
-  static constexpr int ROWS = MT * 32;
+  static constexpr int FP = HV == 2 ? 2 : kFfnStages;  // k-steps in flight
+  static constexpr int FNB = FP + 1;                   // activation tiles in the LDS ring
+  static constexpr int CG = FW / HV;                   // column groups (waves per row part)
+  static constexpr int WROWS = MT * 32;                // rows per wave
+  static constexpr int ROWS = WROWS * HV;              // rows per tile
   static constexpr int NTHR = FW * 64;
   static constexpr int WCOLS = WN * 32;               // output columns per wave
-  static constexpr int COLS = FW * WCOLS;             // output columns per tile
+  static constexpr int COLS = CG * WCOLS;             // output columns per tile
   static constexpr int GROUPS = ROWS / 8;             // 8-row groups: one LDS-writing load each
   static constexpr int AL = (GROUPS + FW - 1) / FW;   // such loads per wave and step
-  static constexpr int BL = 4 * WN;                   // weight loads per wave and step
+  static constexpr int BL = 4 * WN / HV;              // weight loads per wave and step
   static constexpr int A_BYTES = ROWS * 128;          // one activation tile
-  static constexpr int B_BYTES = COLS * FLDS * 2;     // the waves' weight slots
+  static constexpr int B_BYTES = HV * COLS * FLDS * 2;  // the weight slots (HV buffers)
   static constexpr int FREE = A_BYTES + B_BYTES;      // LDS the epilogue may use
   static constexpr int part_bytes(int wpp) {
     return F32STAGE ? ROWS * (wpp * WCOLS + 4) * 4 : ROWS * (wpp * WCOLS + 8) * 2;
   }
   static constexpr int pick_wpp() {
-    for (int w = FW; w > 1; --w)
-      if (FW % w == 0 && part_bytes(w) <= FREE) return w;
+    for (int w = CG; w > 1; --w)
+      if (CG % w == 0 && part_bytes(w) <= FREE) return w;
     return 1;
   }
-  // Epilogue: the result leaves through LDS in column parts of WPP waves.
+  // Epilogue: the result leaves through LDS in column parts of WPP column groups.
   static constexpr int WPP = pick_wpp();
-  static constexpr int NPARTS = FW / WPP;
+  static constexpr int NPARTS = CG / WPP;
   static constexpr int PCOLS = WPP * WCOLS;
   static constexpr int OPC = GLU ? PCOLS / 2 : PCOLS;             // output columns per part
   static constexpr int OCOLS = GLU ? COLS / 2 : COLS;             // output columns per tile
@@ -197,7 +208,7 @@ __device__ __forceinline__ int find_tile(int t, int stride, int n_tiles, int n_n
 
 #define SFFN_LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
-template <int MT, int FW, int WN, bool SECOND, int WPOL, bool GLU = false>
+template <int MT, int FW, int WN, bool SECOND, int WPOL, bool GLU = false, int HV = 1>
 __global__ void __launch_bounds__(FW * 64)
 ffn_bf16_kernel(const uint16_t* __restrict__ act, uint32_t act_bytes,
                 const uint16_t* __restrict__ W, const uint16_t* __restrict__ bias,
@@ -206,7 +217,8 @@ ffn_bf16_kernel(const uint16_t* __restrict__ act, uint32_t act_bytes,
                 uint16_t* __restrict__ out, uint32_t out_bytes, int K, int Nout,
                 int n_mchunks, int n_experts, int max_rows, int T, int d_model,
                 int no_residual) {
-  using Geo = FfnGeom<MT, FW, WN, SECOND, GLU>;
+  using Geo = FfnGeom<MT, FW, WN, SECOND, GLU, HV>;
+  constexpr int FP = Geo::FP, FNB = Geo::FNB, CG = Geo::CG, WROWS = Geo::WROWS;
   constexpr int ROWS = Geo::ROWS, NTHR = Geo::NTHR, AL = Geo::AL, A_BYTES = Geo::A_BYTES;
   constexpr int NPARTS = Geo::NPARTS, WPP = Geo::WPP, PCOLS = Geo::PCOLS, CPR = Geo::CPR;
   constexpr int CST = Geo::CST, XPT = Geo::XPT, BL = Geo::BL, WCOLS = Geo::WCOLS;
@@ -216,6 +228,7 @@ ffn_bf16_kernel(const uint16_t* __restrict__ act, uint32_t act_bytes,
   constexpr bool PARITY = SHIFT || WPOL == kCpolSplitRows;  // loads grouped by row parity
   constexpr int HB = SHIFT ? BL / 2 : 1;                     // odd-row loads (stashes)
   static_assert(!SHIFT || !Geo::LATE_B, "the stash is refilled before a tile's activations");
+  static_assert(HV == 1 || (!PARITY && !GLU), "split rows: weight rows on the line grid, ReLU");
   static_assert(ROWS <= NTHR, "one thread per row for the row lookups");
   static_assert(Geo::fits, "LDS budget");
   // [activation ring (FNB tiles) | weight slots | 1 KB sink for idle loads].
@@ -240,6 +253,8 @@ ffn_bf16_kernel(const uint16_t* __restrict__ act, uint32_t act_bytes,
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int cgrp = wave % CG;   // column group: output columns cgrp*WCOLS ..
+  const int rpart = wave / CG;  // row part: rows rpart*WROWS ..
   const int khalf = lane >> 5;
   // Steps rounded up to whole pipeline rounds: the loop body is then free of
   // branches (extra steps load zeros).
@@ -296,7 +311,7 @@ ffn_bf16_kernel(const uint16_t* __restrict__ act, uint32_t act_bytes,
     src = make_rsrc(W + (size_t)dt.e * WMUL * Nout * K, (uint32_t)((size_t)WMUL * Nout * K * 2));
 #pragma unroll
     for (int i = 0; i < BL; ++i) {
-      const int nr = phys_row(dt.nt, wave * WCOLS + wrow(i));
+      const int nr = phys_row(dt.nt, cgrp * WCOLS + wrow(rpart * BL + i));
       const uint32_t shift = (SHIFT && (i & 1)) ? 32u : 0u;
       off[i] = (dt.nrows > 0 && nr >= 0)
                    ? ((uint32_t)nr * (uint32_t)K + shift + (uint32_t)(lane & 7) * 8u) * 2u : kOob;
@@ -367,10 +382,10 @@ ffn_bf16_kernel(const uint16_t* __restrict__ act, uint32_t act_bytes,
   const uint32_t a_rd = (uint32_t)(lane & 31) * 128u + (uint32_t)(((khalf * 4) ^ rsw) * 16);
   f32x16 acc[MT * WN];
   u32x4 st[HB];  // kCpolShiftOdd: the next step's first half of each odd row
-  uint16_t* bslot = Bs + wave * WCOLS * FLDS;
-  auto compute = [&](int buf, const u32x4 (&rb)[BL]) {
-    // Weight tile into the wave's LDS slot (row-major), back out in operand layout.
-    // LDS accesses of one wave complete in order, so no barrier is needed.
+  // The weight slot of the wave's column group (HV = 2: buffer b of two).
+  auto slot_of = [&](int b) { return Bs + ((HV == 2 ? b * CG : 0) + cgrp) * WCOLS * FLDS; };
+  // This wave's weight rows of a step into a slot (row-major).
+  auto write_slot = [&](uint16_t* bslot, const u32x4 (&rb)[BL]) {
 #pragma unroll
     for (int i = 0; i < BL; ++i) {
       if (SHIFT && (i & 1)) {
@@ -383,10 +398,14 @@ ffn_bf16_kernel(const uint16_t* __restrict__ act, uint32_t act_bytes,
         store16(bslot + wrow(i) * FLDS + (((lane & 7) + 4) & 7) * 8, v);
         st[i / 2] = rb[i];
       } else {
-        store16(bslot + wrow(i) * FLDS + (lane & 7) * 8, rb[i]);
+        store16(bslot + wrow(rpart * BL + i) * FLDS + (lane & 7) * 8, rb[i]);
       }
     }
-    const char* abase = As + buf * A_BYTES;
+  };
+  // The matrix-core work of a step: activation ring tile `buf` (this wave's
+  // row part) against a weight slot, in operand layout.
+  auto mma = [&](int buf, const uint16_t* bslot) {
+    const char* abase = As + buf * A_BYTES + rpart * WROWS * 128;
     const uint16_t* bbase = bslot + (lane & 31) * FLDS + khalf * 32;
     // Operand fragments of sub-step q (16 k): read one sub-step ahead of the
     // matrix-core ops that use them; the scheduling fence per sub-step keeps
@@ -411,6 +430,12 @@ ffn_bf16_kernel(const uint16_t* __restrict__ act, uint32_t act_bytes,
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+  };
+  // One wave per slot: the wave writes its slot and reads it back (LDS
+  // accesses of one wave complete in order, so no barrier is needed).
+  auto compute = [&](int buf, const u32x4 (&rb)[BL]) {
+    write_slot(slot_of(0), rb);
+    mma(buf, slot_of(0));
   };
 
   // First tile: its lookups, then the weights (independent of the routing)
@@ -497,8 +522,18 @@ ffn_bf16_kernel(const uint16_t* __restrict__ act, uint32_t act_bytes,
       constexpr int J = decltype(j_c)::value;
       const int k = ks + J;
       wait_vmcnt<Geo::template step_wait<KIND, J>()>();  // this wave's A(k) is in LDS
-      dma_barrier();                                      // everyone's; ring tile k-1 is free
-      compute(k % FNB, rb[J]);
+      if constexpr (HV == 2) {
+        // This wave's half of the group's weights of step k (its own loads:
+        // the compiler waits for them) into slot buffer k % 2; the barrier
+        // publishes both halves.  Buffer k % 2 was last read in step k - 2,
+        // which every wave finished before the previous barrier.
+        write_slot(slot_of(k & 1), rb[J]);
+        dma_barrier();  // everyone's activations and slot halves; ring tile k-1 is free
+        mma(k % FNB, slot_of(k & 1));
+      } else {
+        dma_barrier();  // everyone's activations; ring tile k-1 is free
+        compute(k % FNB, rb[J]);
+      }
       if constexpr (KIND == kRoundFirst || KIND == kRoundMid) {
         dma_a((k + FP) % FNB, k + FP);  // zero past the end of K
         load_b(rb[J], rb_src, b_off, k + FP);
@@ -539,7 +574,7 @@ ffn_bf16_kernel(const uint16_t* __restrict__ act, uint32_t act_bytes,
     // 16-byte row chunks.
 #pragma unroll
     for (int p = 0; p < NPARTS; ++p) {
-      if (wave / WPP == p) {
+      if (cgrp / WPP == p) {
         // The matrix-core result is C^T: lane l holds row l%32 of row tile m
         // and, for value 4g + j, column 8g + 4*(l/32) + j of column tile w --
         // four consecutive columns per g, staged as one 8- or 16-byte write.
@@ -552,7 +587,7 @@ ffn_bf16_kernel(const uint16_t* __restrict__ act, uint32_t act_bytes,
         for (int w = 0; w < WN; ++w) {
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
-            const int cw = wave * WCOLS + w * 32 + 8 * g + 4 * ekh;  // column within the tile
+            const int cw = cgrp * WCOLS + w * 32 + 8 * g + 4 * ekh;  // column within the tile
             const u32x2 bb = *reinterpret_cast<const u32x2*>(bias_s + cw);
             const float b0 = bf16_bits_to_f32(bb[0] & 0xffffu), b1 = bf16_bits_to_f32(bb[0] >> 16);
             const float b2 = bf16_bits_to_f32(bb[1] & 0xffffu), b3 = bf16_bits_to_f32(bb[1] >> 16);
@@ -560,7 +595,7 @@ ffn_bf16_kernel(const uint16_t* __restrict__ act, uint32_t act_bytes,
 #pragma unroll
             for (int m = 0; m < MT; ++m) {
               const f32x16& a = acc[m * WN + w];
-              const int r = m * 32 + er;
+              const int r = rpart * WROWS + m * 32 + er;
               if (Geo::F32STAGE) {
                 *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(stage) + r * CST + pc) =
                     f32x4{a[4 * g] + b0, a[4 * g + 1] + b1, a[4 * g + 2] + b2, a[4 * g + 3] + b3};
@@ -652,7 +687,7 @@ ffn_bf16_kernel(const uint16_t* __restrict__ act, uint32_t act_bytes,
 
 #undef SFFN_LDS_PTR
 
-template <int MT, int FW, int WN, bool SECOND, bool GLU, int WPOL = 0>
+template <int MT, int FW, int WN, bool SECOND, bool GLU, int WPOL = 0, int HV = 1>
 static int ffn_resident_blocks() {
   // Blocks of this kernel the device holds at once (a persistent grid's size).
   static const int n = [] {
@@ -660,7 +695,7 @@ static int ffn_resident_blocks() {
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, ffn_bf16_kernel<MT, FW, WN, SECOND, WPOL, GLU>, FW * 64, 0) != hipSuccess)
+            &per_cu, ffn_bf16_kernel<MT, FW, WN, SECOND, WPOL, GLU, HV>, FW * 64, 0) != hipSuccess)
       return 256;
     return (cus > 0 ? cus : 256) * (per_cu > 0 ? per_cu : 1);
   }();
@@ -713,12 +748,12 @@ static long ffn_col_tiles(const FfnArgs& a, long rows_per_tile, bool glu) {
 
 // One launch with weight policy WPOL: a persistent grid of as many blocks as
 // that kernel keeps resident, or fewer if there are fewer tiles.
-template <int MT, int FW, int WN, bool SECOND, int WPOL, bool GLU>
+template <int MT, int FW, int WN, bool SECOND, int WPOL, bool GLU, int HV = 1>
 static void launch_ffn_pol(const FfnArgs& a, hipStream_t st) {
-  const long n_tiles = ffn_col_tiles(a, FW * WN * 32, GLU) * a.n_mchunks * a.n_experts;
-  const long resident = ffn_resident_blocks<MT, FW, WN, SECOND, GLU, WPOL>();
+  const long n_tiles = ffn_col_tiles(a, FW / HV * WN * 32, GLU) * a.n_mchunks * a.n_experts;
+  const long resident = ffn_resident_blocks<MT, FW, WN, SECOND, GLU, WPOL, HV>();
   const dim3 grid((unsigned)(n_tiles < resident ? n_tiles : resident)), block(FW * 64);
-  hipLaunchKernelGGL((ffn_bf16_kernel<MT, FW, WN, SECOND, WPOL, GLU>), grid, block, 0, st, a.act,
+  hipLaunchKernelGGL((ffn_bf16_kernel<MT, FW, WN, SECOND, WPOL, GLU, HV>), grid, block, 0, st, a.act,
                      a.act_bytes, a.W, a.bias, a.offset, a.row2tok, a.rowgate, a.xres, a.out,
                      a.out_bytes, a.K, a.Nout, a.n_mchunks, a.n_experts, a.max_rows, a.T,
                      a.d_model, a.no_residual);
@@ -842,6 +877,31 @@ ffn_f32_kernel(const float* __restrict__ act, const float* __restrict__ W,
 
 template <bool SECOND, bool GLU = false>
 static void launch_ffn_bf16(FfnArgs a, const Shape& s, hipStream_t st) {
+  a.n_experts = s.N;
+  a.max_rows = s.max_rows;
+  a.T = s.T;
+  a.d_model = s.d;
+  // Experts of 9 or 10 row tiles (capacity 257 .. 320 rows: Switch-Large-like,
+  // top-2 Switch-Base-like) as one tile of two row parts: 8 waves, 5 row tiles
+  // each, 128 columns, each weight byte streamed once (weight rows on the
+  // 128-byte line grid, ReLU experts).
+  // The grid is one block per CU (LDS), so the split tiles run only where
+  // they make at least four rounds of the grid: with fewer, the last round
+  // leaves CUs idle and two row chunks of wider tiles balance better.
+  const int tiles = (s.C + 31) / 32;
+#ifndef SFFN_FFN_NO_SPLIT  // tuning builds: the two-chunk path only
+  if constexpr (!GLU) {
+    if ((tiles == 9 || tiles == 10) && (a.K * 2) % 128 == 0) {
+      a.n_mchunks = 1;
+      const long n_split = ffn_col_tiles(a, 128, false) * a.n_experts;
+      const long resident = ffn_resident_blocks<5, 8, 1, SECOND, false, kCpolNonTemporal, 2>();
+      if (n_split >= 4 * resident) {
+        launch_ffn_pol<5, 8, 1, SECOND, kCpolNonTemporal, false, 2>(a, st);
+        return;
+      }
+    }
+  }
+#endif
   const int mt = rows_tiles(s.C);
   a.n_mchunks = (s.C + mt * 32 - 1) / (mt * 32);
   a.n_experts = s.N;

@@ -83,6 +83,43 @@ def test_bf16_edge_shapes(case):
 
 
 @pytest.mark.parametrize("case", [
+    dict(T=1200, d=128, F=192, N=4, CF=1.0, bias_sigma=0.02),    # C = 300: both GEMMs in two row parts
+    dict(T=1100, d=64, F=136, N=4, CF=1.0),                      # C = 275: FFN1 split, column tail
+    dict(T=1290, d=64, F=128, N=4, CF=1.0, bias_sigma=0.02),     # C = 322: 11 row tiles, two chunks
+    dict(T=1030, d=192, F=64, N=4, CF=1.0),                      # C = 257: 9 row tiles, one row
+])
+def test_tall_expert_tiles(case):
+    """Experts of 257..320 rows at small sizes: two row chunks (too few tiles to split)."""
+    w = synth.workload("switch_base").replace(**case)
+    _full_case(w)
+
+
+@pytest.mark.parametrize("case", [
+    dict(T=76800, d=64, F=512, N=256, CF=1.0, bias_sigma=0.02),   # FFN1 split: 1024 tiles
+    dict(T=76790, d=512, F=64, N=256, CF=1.0),                    # FFN2 split, ragged T
+])
+def test_split_row_tiles(case):
+    """C = 300 with enough column tiles (four rounds of the grid) for the split-row GEMM:
+    one tile of two row parts sharing each weight step, every weight byte read once."""
+    w = synth.workload("switch_base").replace(**case)
+    _full_case(w, no_residual_too=False)
+
+
+def test_split_row_tiles_top2():
+    """Top-2 routing with C = floor(1.0 * 2T / N) = 300: the split-row tiles with the
+    row-output FFN2 epilogue and the combine."""
+    w = synth.workload("switch_base").replace(T=600, d=128, F=192, N=4, CF=1.0, bias_sigma=0.02)
+    announce("split rows, top-2 " + w.describe())
+    dev_in = synth.device_inputs(w, DEV)
+    x_raw = host_x(w)
+    Wr_raw = synth.host_array(w, "Wr").reshape(w.N, w.d)
+    gpu = run_gpu(w, dev_in, k=2)
+    ref = oracle_ref(w, x_raw, Wr_raw, gpu["expert_idx"], k=2)
+    check_routing(gpu, ref)
+    check_y(w, gpu, ref, x_raw)
+
+
+@pytest.mark.parametrize("case", [
     dict(T=100, d=5, F=7, N=3, CF=1.0, bias_sigma=0.1),
     dict(T=333, d=33, F=65, N=9, CF=1.25, bias_sigma=0.02),
     dict(T=64, d=32, F=64, N=4, CF=0.0),
