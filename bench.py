@@ -159,6 +159,27 @@ def measured_traffic(kernel: str, workload: str):
         return None
 
 
+def measured_mfma(stage: str, workload: str):
+    """Matrix-core counters of a stage from the committed rocprofv3 summary, if still valid:
+    {mfma_flops, busy_frac} per launch (profiles/<stage>_<workload>_mfma.txt)."""
+    path = os.path.join(ROOT, "profiles", f"{stage}_{workload}_mfma.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if "=" in line and not line.lstrip().startswith("#"):
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    srcs = KERNEL_SOURCES.get(stage)
+    if srcs is None or kv.get("source_sha256_16") != source_digest(srcs):
+        return None
+    try:
+        return {"mfma_flops": float(kv["mfma_flops_per_launch"]), "busy_frac": float(kv["busy_frac"]),
+                "kernel": kv.get("kernel")}
+    except (KeyError, ValueError):
+        return None
+
+
 def algorithmic_bytes(w, stage, accepted, active, esize, dropped=0, k=1, reroute=False):
     """Bytes a stage must move at minimum, from what it reads and writes once.
 
@@ -606,6 +627,16 @@ def main():
     wname = (w.name + ("_top2" if K == 2 else "") + ("_reroute" if args.reroute else "")
              + ("_geglu" if w.glu else "") + ("_train" if BWD else ""))
     traffic = measured_traffic(dominant, wname)
+    counter_gemm = {}
+    for st in ("ffn1", "ffn2"):
+        mm = measured_mfma(st, wname)
+        if mm and stage_ms.get(st):
+            alg_flops = (2.0 * (2 if (w.glu and st == "ffn1") else 1)) * accepted * w.d * w.F
+            tf = mm["mfma_flops"] / (stage_ms[st] * 1e-3) / 1e12
+            counter_gemm[st] = {"kernel": mm["kernel"], "mfma_flops": mm["mfma_flops"],
+                                "tflops": tf, "frac_of_bf16_mfma_peak": tf / MFMA_BF16_PEAK_TFLOPS,
+                                "mfma_busy_frac": mm["busy_frac"],
+                                "padded_over_algorithmic": mm["mfma_flops"] / alg_flops}
     w1mul = 2 if w.glu else 1
     layer_bytes = (active * (w1mul + 1) * w.F * w.d * esize + N * w.d * 4 + 2 * T * w.d * esize
                    + (active * (w1mul * w.F + w.d) * esize if w.has_bias else 0))
@@ -646,7 +677,11 @@ def main():
         "measured_peaks": measured_peaks(dev),
         "expert_gemm": {"tflops": gemm_flops / (gemm_ms * 1e-3) / 1e12 if gemm_ms else None,
                         "frac_of_bf16_mfma_peak": (gemm_flops / (gemm_ms * 1e-3) / 1e12
-                                                   / MFMA_BF16_PEAK_TFLOPS) if gemm_ms else None},
+                                                   / MFMA_BF16_PEAK_TFLOPS) if gemm_ms else None,
+                        "note": "analytic: (4 or 6 for GEGLU) * accepted * d * F flops over the two "
+                                "stages' event times; counter: rocprofv3 bf16 MFMA flops per launch "
+                                "(padded tile rows included) over this run's stage time",
+                        "counter": counter_gemm},
         "wall_s_timed_region": wall,
         "launch": {"graph": graph_info, "eager_ms_per_step": eager_ms,
                    "eager_tokens_per_s": T / (eager_ms * 1e-3)},

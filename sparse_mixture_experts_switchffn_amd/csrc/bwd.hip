@@ -1179,14 +1179,14 @@ hipError_t launch_backward(const Shape& s, const Inputs& in, const BwdState& b, 
   const bool bf16 = s.dtype == SFFN_BF16;
   const int n_rows = s.max_rows;  // rows beyond offset[N] are never read
 
-  // 1. the guard: checked copies of the forward's offsets and counts
+  // 1. the guard: checked copies of the forward's offsets and counts (timed with E1)
+  SFFN_CHECK(mark());
   hipLaunchKernelGGL(bwd_guard_kernel, dim3(1), dim3(256), 0, st, b.fwd_tag, make_tag(s, 0u),
                      (uint32_t)SFFN_NO_RESIDUAL, b.fwd_offset, b.fwd_hist, s.N, s.max_rows,
                      b.offset, b.hist, b.bad);
   SFFN_CHECK(hipGetLastError());
 
   // 2. E1: dA and partial dg
-  SFFN_CHECK(mark());
   const int mt = bwd_rows_mt(s.C), n_mc = (s.C + 32 * mt - 1) / (32 * mt);
   if (s.C > 0) {
     if (bf16) {
