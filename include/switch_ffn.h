@@ -73,7 +73,12 @@ extern "C" {
 #define SFFN_EHIP (-5)         /* a HIP launch failed */
 #define SFFN_ESCRATCH (-6)     /* switch_ffn_forward_noalloc: the shape needs more than its scratch */
 
-/* Element types of x, W1, b1, W2, b2 and y. */
+/* Element types of x, W1, b1, W2, b2 and y.  SFFN_BF16 is the performance path
+ * (matrix-core GEMMs).  SFFN_FP32 computes the same layer in fp32 with
+ * fp32 FMA kernels of one thread per output element, made for exactness on
+ * small layers (the reference-precision check of the method): correct at
+ * every supported shape, but far below the bf16 path's throughput on large
+ * ones. */
 #define SFFN_FP32 0
 #define SFFN_BF16 1
 
