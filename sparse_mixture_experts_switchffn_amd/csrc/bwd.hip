@@ -42,13 +42,13 @@ namespace sffn {
 //   E2: rows x d,  K = F     A = dA[r]              B = W1_e [F][d]   (bwd_rows_kernel)
 //   E3: d x F,     K = rows  A = g_r dy[row2tok[r]] B = H[r]          -> dW2_e
 //   E4: F x d,     K = rows  A = dA[r]              B = x[row2tok[r]] -> dW1_e
-// E3/E4 (bwd_gemm_kernel): block tile 128 x 128, four waves of 64 x 64 (2 x 2
-// MFMA tiles of 32 x 32), both operands [k][inner].
+// E1/E2 (bwd_rows_kernel): a whole row chunk of one expert against 32 NW output
+// columns; E3/E4 (bwd_gemm_kernel): block tiles of (64 WMW) x (64 WNW), waves
+// of 64 x 64 (2 x 2 MFMA tiles of 32 x 32), both operands [k][inner].
 // ---------------------------------------------------------------------------
-constexpr int GM = 128, GN = 128, GK = 32;
-constexpr int GP = GK + 8;  // LDS row pitch in bf16 (80 bytes: fragment reads spread over banks)
-constexpr int RP = 160;     // [k][inner] LDS row pitch in bf16 (320 bytes), same tile size
-static_assert(GK * RP == GM * GP, "both LDS forms of an operand tile take the same space");
+constexpr int GK = 32;
+constexpr int GP = GK + 8;  // [outer][k] LDS row pitch in bf16 (80 bytes: fragment reads spread over banks)
+constexpr int RP = 160;     // [k][inner] LDS row pitch in bf16 (320 bytes) of 128-wide tiles
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
@@ -70,6 +70,19 @@ __device__ __forceinline__ bf16x8 tr_fragment(const uint16_t* S, int k0, int mba
 #ifndef SFFN_BWD_PD_WGRAD
 #define SFFN_BWD_PD_WGRAD 1
 #endif
+// Waves of E3/E4's block tile along its rows and columns (64 x 64 outputs each).
+#ifndef SFFN_BWD_WGRAD_WM
+#define SFFN_BWD_WGRAD_WM 2
+#endif
+#ifndef SFFN_BWD_WGRAD_WN
+#define SFFN_BWD_WGRAD_WN 4
+#endif
+constexpr int kWgradWm = SFFN_BWD_WGRAD_WM, kWgradWn = SFFN_BWD_WGRAD_WN;
+// Waves of E1/E2's block (32 output columns each).
+#ifndef SFFN_BWD_ROWS_NW
+#define SFFN_BWD_ROWS_NW 8
+#endif
+constexpr int kRowsWaves = SFFN_BWD_ROWS_NW, kRowsCols = 32 * kRowsWaves;
 
 struct BwdGemmArgs {
   const uint16_t* a;
@@ -81,20 +94,47 @@ struct BwdGemmArgs {
   int T, d, F;
 };
 
-template <int KIND, int PD>
-__global__ void __launch_bounds__(256)
+// A [k][inner] LDS tile's operand fragment as tr_fragment, for a tile of
+// `pitch` bf16 per k row.
+__device__ __forceinline__ bf16x8 tr_fragment_p(const uint16_t* S, int pitch, int k0, int mbase,
+                                                int lane) {
+  const int g = lane >> 4, j = lane & 15;
+  const uint16_t* p = S + (k0 + 8 * (g >> 1) + (j >> 2)) * pitch + mbase + 16 * (g & 1) + 4 * (j & 3);
+  const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p);
+  const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p + 4 * pitch));
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// E3/E4: a block tile of (64 WMW) x (64 WNW) outputs, WMW x WNW waves of 64 x 64
+// (2 x 2 matrix-core tiles each).  The contraction runs over the expert's rows
+// (about C of them), so a tile reads (64 WMW + 64 WNW) x rows operand values
+// and writes 64 WMW x 64 WNW results: wider tiles re-read the operands less per
+// result written.
+template <int KIND, int PD, int WMW, int WNW>
+__global__ void __launch_bounds__(64 * WMW * WNW)
 bwd_gemm_kernel(BwdGemmArgs g) {
   static_assert(KIND == 3 || KIND == 4, "the weight gradients");
-  // [A ring | B ring]; after the k-loop the epilogue stages its tile over it.
-  __shared__ __attribute__((aligned(16))) uint16_t lds[4 * GK * RP];
-  constexpr int SP = GN + 8;  // staged tile pitch (bf16): 272-byte rows
-  static_assert(GM * SP <= 4 * GK * RP, "staged tile fits the rings");
+  constexpr int NTHR = 64 * WMW * WNW;
+  constexpr int TM = 64 * WMW, TN = 64 * WNW;   // block tile
+  constexpr int RPA = TM + 32, RPB = TN + 32;   // [k][inner] LDS pitches (bf16): rows 16 banks apart
+  constexpr int A_EL = GK * RPA, B_EL = GK * RPB;
+  constexpr int SP = TN + 8;                    // staged tile pitch (bf16)
+  constexpr int RING = 2 * (A_EL + B_EL);
+  constexpr int LDS_EL = RING > TM * SP ? RING : TM * SP;
+  // [A ring | B ring] (two buffers each); after the k-loop the epilogue stages its tile over it.
+  __shared__ __attribute__((aligned(16))) uint16_t lds[LDS_EL];
   uint16_t* const stg = lds;
+  // Operand loads: CRx 16-byte chunks per k row, RPPx k rows per pass, NPx passes.
+  constexpr int CRA = TM / 8, RPPA = NTHR / CRA, NPA = GK / RPPA;
+  constexpr int CRB = TN / 8, RPPB = NTHR / CRB, NPB = GK / RPPB;
+  static_assert(NTHR % CRA == 0 && GK % RPPA == 0 && NTHR % CRB == 0 && GK % RPPB == 0,
+                "load mapping");
+  constexpr int NPG = KIND == 3 ? NPA : NPB;  // passes of the gathered operand
 
   const int Nn = KIND == 3 ? g.F : g.d;
   const int M = KIND == 3 ? g.d : g.F;
-  const int n_nt = (Nn + GN - 1) / GN;
-  const int n_mt = (M + GM - 1) / GM;
+  const int n_nt = (Nn + TN - 1) / TN;
+  const int n_mt = (M + TM - 1) / TM;
   const int tile = xcd_contiguous_tile(blockIdx.x, gridDim.x);
   const int e = tile / (n_nt * n_mt);
   const int rest = tile % (n_nt * n_mt);
@@ -102,16 +142,16 @@ bwd_gemm_kernel(BwdGemmArgs g) {
   const int rbeg = g.offset[e];
   const int Ae = g.offset[e + 1] - rbeg;
   const int K = Ae;
-  const int m0 = mt * GM, n0 = nt * GN;
+  const int m0 = mt * TM, n0 = nt * TN;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave % WMW, wn = wave / WMW;
 
-  // Both operands [k][inner]: thread k rows tid/16 + {0, 16}, 16-byte chunk
-  // tid % 16 of the 128-wide inner range.
-  const int kr = tid >> 4, pc = tid & 15;
+  // A: k row ar + RPPA q, chunk ac of the tile's TM-wide inner range; B likewise.
+  const int ar = tid / CRA, ac = tid % CRA;
+  const int br = tid / CRB, bc = tid % CRB;
   __amdgpu_buffer_rsrc_t a_src, b_src;
   if constexpr (KIND == 3) {
     a_src = make_rsrc(g.a, (uint32_t)g.T * (uint32_t)g.d * 2u);
@@ -122,68 +162,61 @@ bwd_gemm_kernel(BwdGemmArgs g) {
   }
   const int ldA = KIND == 4 ? g.F : g.d;  // elements per memory row of A
   const int ldB = KIND == 3 ? g.F : g.d;  // ... and of B
-  const int nb_chunk = n0 + pc * 8;       // B's inner chunk (n)
-  const int ma_chunk = m0 + pc * 8;       // A's inner chunk (m)
-
-  // Memory row of k index kk: E3 A and E4 B, the token of expert row kk; E3 B
-  // and E4 A, expert row kk.
-  auto tok_of = [&](int kk) -> int { return kk < Ae ? g.row2tok[rbeg + kk] : -1; };
+  const int ma_chunk = m0 + ac * 8;       // A's inner chunk (m)
+  const int nb_chunk = n0 + bc * 8;       // B's inner chunk (n)
+  // k row of pass q of the gathered operand (E3: A, E4: B).
+  auto grow = [&](int q) { return KIND == 3 ? ar + RPPA * q : br + RPPB * q; };
 
   // Register ring of PD k-steps in flight: slot s holds the loads of the steps
-  // k with k % PD == s.  The k rows' tokens (and gates) are looked up one ring
-  // ahead, so that no data load waits for its index.
-  u32x4 ra[PD][2], rb[PD][2];
-  float sc[PD][2];
-  int tk[PD][2];
-  float gk[PD][2];
-  auto lookup = [&](int k0, int (&t)[2], float (&gt)[2]) {
+  // k with k % PD == s.  The gathered rows' tokens (and gates) are looked up
+  // one ring ahead, so that no data load waits for its index.
+  u32x4 ra[PD][NPA], rb[PD][NPB];
+  int tk[PD][NPG];
+  float gk[PD][NPG];
+  auto lookup = [&](int k0, int (&t)[NPG], float (&gt)[NPG]) {
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int kk = k0 + kr + 16 * q;
-      t[q] = tok_of(kk);
+    for (int q = 0; q < NPG; ++q) {
+      const int kk = k0 + grow(q);
+      t[q] = kk < Ae ? g.row2tok[rbeg + kk] : -1;
       gt[q] = (KIND == 3 && kk < Ae) ? g.rowgate[rbeg + kk] : 0.f;
     }
   };
-  auto load = [&](int k0, u32x4 (&a)[2], u32x4 (&b)[2], float (&scale)[2], const int (&t)[2],
-                  const float (&gt)[2]) {
+  auto load = [&](int k0, u32x4 (&a)[NPA], u32x4 (&b)[NPB], const int (&t)[NPG]) {
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int kk = k0 + kr + 16 * q;
-      const bool kin = kk < Ae;
-      // A: E3 gathered dy rows (scaled by the gate below), E4 expert rows of dA
+    for (int q = 0; q < NPA; ++q) {
+      const int kk = k0 + ar + RPPA * q;
+      // A: E3 gathered dy rows (scaled by the gate when staged), E4 expert rows of dA
       const uint32_t arow = KIND == 3 ? (uint32_t)(t[q] < 0 ? 0 : t[q]) : (uint32_t)kk;
-      a[q] = buffer_load16(a_src, (kin && ma_chunk < M)
-                                      ? (arow * (uint32_t)ldA + (uint32_t)ma_chunk) * 2u
-                                      : kOob);
+      a[q] = buffer_load16(a_src, (kk < Ae && ma_chunk < M)
+                                      ? (arow * (uint32_t)ldA + (uint32_t)ma_chunk) * 2u : kOob);
+    }
+#pragma unroll
+    for (int q = 0; q < NPB; ++q) {
+      const int kk = k0 + br + RPPB * q;
       // B: E3 expert rows of H, E4 gathered x rows
       const uint32_t brow = KIND == 4 ? (uint32_t)(t[q] < 0 ? 0 : t[q]) : (uint32_t)kk;
-      b[q] = buffer_load16(b_src, (kin && nb_chunk < Nn)
-                                      ? (brow * (uint32_t)ldB + (uint32_t)nb_chunk) * 2u
-                                      : kOob);
-      scale[q] = gt[q];
+      b[q] = buffer_load16(b_src, (kk < Ae && nb_chunk < Nn)
+                                      ? (brow * (uint32_t)ldB + (uint32_t)nb_chunk) * 2u : kOob);
     }
   };
-  // [k][inner] tiles: a thread's two chunks go to their rows as they are (E3's
-  // A scaled by the row's gate, rounded once more to bf16).
-  auto raw_tile = [&](int buf, bool a_side) -> uint16_t* {
-    return lds + ((a_side ? 0 : 2) + buf) * GK * RP;
-  };
-  auto store_raw = [&](uint16_t* S, const u32x4 (&v)[2], bool scale, const float (&sv)[2]) {
+  auto a_tile = [&](int buf) { return lds + buf * A_EL; };
+  auto b_tile = [&](int buf) { return lds + 2 * A_EL + buf * B_EL; };
+  // [k][inner] tiles: each chunk goes to its row as it is (E3's A scaled by the
+  // row's gate, rounded once more to bf16).
+  auto store = [&](int buf, const u32x4 (&a)[NPA], const u32x4 (&b)[NPB], const float (&sv)[NPG]) {
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      u32x4 w = v[q];
-      if (scale) {
+    for (int q = 0; q < NPA; ++q) {
+      u32x4 w = a[q];
+      if constexpr (KIND == 3) {
 #pragma unroll
         for (int h = 0; h < 4; ++h)
-          w[h] = pack_bf16x2(bf16_bits_to_f32(v[q][h] & 0xffffu) * sv[q],
-                             bf16_bits_to_f32(v[q][h] >> 16) * sv[q]);
+          w[h] = pack_bf16x2(bf16_bits_to_f32(a[q][h] & 0xffffu) * sv[q],
+                             bf16_bits_to_f32(a[q][h] >> 16) * sv[q]);
       }
-      store16(S + (kr + 16 * q) * RP + pc * 8, w);
+      store16(a_tile(buf) + (ar + RPPA * q) * RPA + ac * 8, w);
     }
-  };
-  auto store = [&](int buf, const u32x4 (&a)[2], const u32x4 (&b)[2], const float (&sv)[2]) {
-    store_raw(raw_tile(buf, true), a, KIND == 3, sv);
-    store_raw(raw_tile(buf, false), b, false, sv);
+#pragma unroll
+    for (int q = 0; q < NPB; ++q) store16(b_tile(buf) + (br + RPPB * q) * RPB + bc * 8, b[q]);
   };
 
   f32x16 acc[2][2];
@@ -198,9 +231,11 @@ bwd_gemm_kernel(BwdGemmArgs g) {
     for (int kh = 0; kh < 2; ++kh) {
       bf16x8 fa[2], fb[2];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) fa[i] = tr_fragment(raw_tile(buf, true), kh * 16, wm * 64 + 32 * i, lane);
+      for (int i = 0; i < 2; ++i)
+        fa[i] = tr_fragment_p(a_tile(buf), RPA, kh * 16, wm * 64 + 32 * i, lane);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) fb[j] = tr_fragment(raw_tile(buf, false), kh * 16, wn * 64 + 32 * j, lane);
+      for (int j = 0; j < 2; ++j)
+        fb[j] = tr_fragment_p(b_tile(buf), RPB, kh * 16, wn * 64 + 32 * j, lane);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -213,11 +248,15 @@ bwd_gemm_kernel(BwdGemmArgs g) {
   // rounded up to whole rounds of PD and every load is issued (past the end
   // of K they read zeros): the loop body has no branches, so the compiler's
   // waits for a slot's registers leave the later slots' loads in flight.
+  // The gates of a slot's rows travel with it (sc) for the staging.
+  float sc[PD][NPG];
   const int nk = (K + GK - 1) / GK;
   const int nkr = (nk + PD - 1) / PD * PD;
   static_for<0, PD>([&](auto j) { lookup(j * GK, tk[j], gk[j]); });
   static_for<0, PD>([&](auto j) {
-    load(j * GK, ra[j], rb[j], sc[j], tk[j], gk[j]);
+    load(j * GK, ra[j], rb[j], tk[j]);
+#pragma unroll
+    for (int q = 0; q < NPG; ++q) sc[j][q] = gk[j][q];
     lookup((j + PD) * GK, tk[j], gk[j]);
   });
   store(0, ra[0], rb[0], sc[0]);
@@ -226,7 +265,9 @@ bwd_gemm_kernel(BwdGemmArgs g) {
     static_for<0, PD>([&](auto j) {
       constexpr int J = decltype(j)::value;
       const int k = k0 + J;
-      load((k + PD) * GK, ra[J], rb[J], sc[J], tk[J], gk[J]);
+      load((k + PD) * GK, ra[J], rb[J], tk[J]);
+#pragma unroll
+      for (int q = 0; q < NPG; ++q) sc[J][q] = gk[J][q];
       lookup((k + 2 * PD) * GK, tk[J], gk[J]);
       __builtin_amdgcn_sched_barrier(0);  // the loads go out before this step's work
       compute(k & 1);
@@ -236,45 +277,36 @@ bwd_gemm_kernel(BwdGemmArgs g) {
     });
   }
 
-  // ---- epilogues: lane holds row (l % 32) of each 32-row tile i and, for
+  // ---- epilogue: lane holds row (l % 32) of each 32-row tile i and, for
   // value 4 gq + q, column 8 gq + 4 (l / 32) + q of each 32-column tile j ----
   const int lr = lane & 31;
-  // Tile rows/columns of this lane's values: row wm*64 + 32 i + lr, columns
-  // wn*64 + 32 j + 8 gq + 4 khalf + q.
-  // Coalesced tile transfer between LDS (pitch SP) and global rows: 16-byte
-  // chunks, 16 per 128-column row, eight per thread.
-  auto tile_io = [&](auto&& fn) {
-#pragma unroll
-    for (int c = 0; c < (GM * GN / 8) / 256; ++c) {
-      const int idx = tid + 256 * c;
-      fn(idx >> 4, (idx & 15) * 8);
-    }
-  };
   // dW2_e [d][F] (E3) or dW1_e [F][d] (E4), bf16, staged and written in row chunks
-  {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int ml = wm * 64 + 32 * i + lr;
+  for (int i = 0; i < 2; ++i) {
+    const int ml = wm * 64 + 32 * i + lr;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < 2; ++j) {
 #pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          const f32x16& a = acc[i][j];
-          *reinterpret_cast<u32x2*>(&stg[ml * SP + wn * 64 + 32 * j + 8 * gq + 4 * khalf]) =
-              u32x2{pack_bf16x2(a[4 * gq], a[4 * gq + 1]), pack_bf16x2(a[4 * gq + 2], a[4 * gq + 3])};
-        }
+      for (int gq = 0; gq < 4; ++gq) {
+        const f32x16& a = acc[i][j];
+        *reinterpret_cast<u32x2*>(&stg[ml * SP + wn * 64 + 32 * j + 8 * gq + 4 * khalf]) =
+            u32x2{pack_bf16x2(a[4 * gq], a[4 * gq + 1]), pack_bf16x2(a[4 * gq + 2], a[4 * gq + 3])};
       }
     }
-    __syncthreads();
-    uint16_t* out = reinterpret_cast<uint16_t*>(g.out) + (size_t)e * g.d * g.F;
-    tile_io([&](int row, int col) {
-      const int m = m0 + row, n = n0 + col;
-      // stored non-temporal: nothing here reads the gradients again, and their
-      // dirty lines would otherwise crowd the caches for the next kernels
-      if (m < M && n < Nn)
-        __builtin_nontemporal_store(load16(&stg[row * SP + col]),
-                                    reinterpret_cast<u32x4*>(out + (size_t)m * Nn + n));
-    });
+  }
+  __syncthreads();
+  uint16_t* out = reinterpret_cast<uint16_t*>(g.out) + (size_t)e * g.d * g.F;
+  constexpr int CPR = TN / 8;  // 16-byte chunks per staged row
+#pragma unroll
+  for (int c = 0; c < TM * CPR / NTHR; ++c) {
+    const int idx = tid + NTHR * c;
+    const int row = idx / CPR, col = (idx % CPR) * 8;
+    const int m = m0 + row, n = n0 + col;
+    // stored non-temporal: nothing here reads the gradients again, and their
+    // dirty lines would otherwise crowd the caches for the next kernels
+    if (m < M && n < Nn)
+      __builtin_nontemporal_store(load16(&stg[row * SP + col]),
+                                  reinterpret_cast<u32x4*>(out + (size_t)m * Nn + n));
   }
 }
 
@@ -301,29 +333,37 @@ struct BwdRowsArgs {
   int T, d, F, max_rows, n_mc;  // n_mc: row chunks per expert
 };
 
-template <int KIND, int MT, int PD>
-__global__ void __launch_bounds__(256)
+template <int KIND, int MT, int PD, int NW>
+__global__ void __launch_bounds__(64 * NW)
 bwd_rows_kernel(BwdRowsArgs g) {
+  constexpr int NTHR = 64 * NW;
   constexpr int R = 32 * MT;
-  constexpr int AI = (R * 4 + 255) / 256;  // A loads per thread and step (16 bytes each)
-  constexpr int SP = GN + 8;               // staged tile pitch (bf16)
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * R * GP + 2 * GK * RP];
-  __shared__ float red[4][R];
-  static_assert(R * SP <= 2 * R * GP + 2 * GK * RP, "staged tile fits the rings");
+  constexpr int CW = 32 * NW;               // output columns per tile
+  constexpr int RPW = CW + 32;              // [k][n] weight tile pitch (bf16): rows 16 banks apart
+  constexpr int AI = (R * 4 + NTHR - 1) / NTHR;  // A loads per thread and step (16 bytes each)
+  constexpr int CRB = CW / 8;               // 16-byte chunks per weight row of the tile
+  constexpr int SPW = 128;                  // E1's epilogue works in parts of 128 columns
+  constexpr int SP = SPW + 8;               // staged part pitch (bf16)
+  constexpr int NPART = CW / SPW;
+  constexpr int RING = 2 * R * GP + 2 * GK * RPW;
+  static_assert(NTHR / CRB == 16 && CW % SPW == 0, "two weight passes of 16 k rows");
+  static_assert(R * SP <= RING, "a staged part fits the rings");
+  __shared__ __attribute__((aligned(16))) uint16_t lds[RING];
+  __shared__ float red[NW][R];
   uint16_t (*As)[R][GP] = reinterpret_cast<uint16_t (*)[R][GP]>(lds);
-  uint16_t* const Bs = lds + 2 * R * GP;   // two [GK][RP] tiles
+  uint16_t* const Bs = lds + 2 * R * GP;   // two [GK][RPW] tiles
   uint16_t* const stg = lds;
 
   const int Nn = KIND == 1 ? g.F : g.d;
   const int Kfull = KIND == 1 ? g.d : g.F;
-  const int n_nt = (Nn + GN - 1) / GN;
+  const int n_nt = (Nn + CW - 1) / CW;
   const int tile = xcd_contiguous_tile(blockIdx.x, gridDim.x);
   const int nt = tile % n_nt;
   const int mc = (tile / n_nt) % g.n_mc;
   const int e = tile / (n_nt * g.n_mc);
   const int rbeg = g.offset[e];
   const int Ae = g.offset[e + 1] - rbeg;
-  const int m0 = mc * R, n0 = nt * GN;
+  const int m0 = mc * R, n0 = nt * CW;
   if (m0 >= Ae) return;  // uniform over the block
   const int kend = Kfull;
 
@@ -332,21 +372,21 @@ bwd_rows_kernel(BwdRowsArgs g) {
   const int wave = tid >> 6;
   const int khalf = lane >> 5;
 
-  // A: chunk c = tid + 256 i is 16-byte chunk c % 4 (of the k-step) of tile row c / 4.
+  // A: chunk c = tid + NTHR i is 16-byte chunk c % 4 (of the k-step) of tile row c / 4.
   __amdgpu_buffer_rsrc_t a_src;
   uint32_t a_off[AI];
   if constexpr (KIND == 1) a_src = make_rsrc(g.a, (uint32_t)g.T * (uint32_t)g.d * 2u);
   else a_src = make_rsrc(g.a + (size_t)rbeg * g.F, (uint32_t)Ae * (uint32_t)g.F * 2u);
 #pragma unroll
   for (int i = 0; i < AI; ++i) {
-    const int c = tid + 256 * i;
+    const int c = tid + NTHR * i;
     const int r = m0 + (c >> 2);
     const bool ok = c < R * 4 && r < Ae;
     const uint32_t row = KIND == 1 ? (ok ? (uint32_t)g.row2tok[rbeg + r] : 0u) : (uint32_t)r;
     a_off[i] = ok ? row * (uint32_t)(KIND == 1 ? g.d : g.F) * 2u : kOob;  // the row's start
   }
-  // B: k rows tid/16 + {0, 16} of the step, chunk tid % 16 of the 128 columns.
-  const int kr = tid >> 4, pc = tid & 15;
+  // B: k rows tid/CRB + {0, 16} of the step, chunk tid % CRB of the CW columns.
+  const int kr = tid / CRB, pc = tid % CRB;
   const int nb = n0 + pc * 8;
   const __amdgpu_buffer_rsrc_t b_src =
       make_rsrc(g.w + (size_t)e * g.d * g.F, (uint32_t)((size_t)g.d * g.F * 2));
@@ -355,7 +395,7 @@ bwd_rows_kernel(BwdRowsArgs g) {
   auto load = [&](int k0, u32x4 (&a)[AI], u32x4 (&b)[2]) {
 #pragma unroll
     for (int i = 0; i < AI; ++i) {
-      const int kc = k0 + ((tid + 256 * i) & 3) * 8;
+      const int kc = k0 + ((tid + NTHR * i) & 3) * 8;
       a[i] = buffer_load16(a_src, kc < kend ? a_off[i] + (uint32_t)kc * 2u : kOob);
     }
 #pragma unroll
@@ -368,11 +408,11 @@ bwd_rows_kernel(BwdRowsArgs g) {
   auto store = [&](int buf, const u32x4 (&a)[AI], const u32x4 (&b)[2]) {
 #pragma unroll
     for (int i = 0; i < AI; ++i) {
-      const int c = tid + 256 * i;
+      const int c = tid + NTHR * i;
       if (c < R * 4) store16(&As[buf][c >> 2][(c & 3) * 8], a[i]);
     }
 #pragma unroll
-    for (int q = 0; q < 2; ++q) store16(Bs + buf * GK * RP + (kr + 16 * q) * RP + pc * 8, b[q]);
+    for (int q = 0; q < 2; ++q) store16(Bs + buf * GK * RPW + (kr + 16 * q) * RPW + pc * 8, b[q]);
   };
 
   f32x16 acc[MT];
@@ -381,7 +421,7 @@ bwd_rows_kernel(BwdRowsArgs g) {
   auto compute = [&](int buf) {
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh) {
-      const bf16x8 fb = tr_fragment(Bs + buf * GK * RP, kh * 16, 32 * wave, lane);
+      const bf16x8 fb = tr_fragment_p(Bs + buf * GK * RPW, RPW, kh * 16, 32 * wave, lane);
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
         const bf16x8 fa = as_bf16x8(load16(&As[buf][32 * m + (lane & 31)][kh * 16 + khalf * 8]));
@@ -414,58 +454,70 @@ bwd_rows_kernel(BwdRowsArgs g) {
   // column 32 wave + 8 gq + 4 khalf + q.
   const int lr = lane & 31;
   if constexpr (KIND == 1) {
-    // H tile into LDS; dA = g Q [H > 0] in place of it and each wave's partial
-    // dg (its 32 columns) per row; the four waves' partials summed in wave
-    // order; then dA out in row chunks.
+    // Per part of 128 columns (waves 4p .. 4p+3): the H part into LDS; dA =
+    // g Q [H > 0] in place of it and each wave's partial dg (its 32 columns)
+    // per row; then dA out in row chunks.  The waves' partials are summed in
+    // wave order at the end.
     const __amdgpu_buffer_rsrc_t h_src =
         make_rsrc(g.H + (size_t)rbeg * g.F, (uint32_t)Ae * (uint32_t)g.F * 2u);
-#pragma unroll
-    for (int c = 0; c < 2 * MT; ++c) {
-      const int idx = tid + 256 * c;
-      const int row = idx >> 4, col = (idx & 15) * 8;
-      const int r = m0 + row, n = n0 + col;
-      store16(&stg[row * SP + col],
-              buffer_load16(h_src, (r < Ae && n < g.F) ? ((uint32_t)r * (uint32_t)g.F + (uint32_t)n) * 2u
-                                                        : kOob));
-    }
-    __syncthreads();
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      const int ml = 32 * m + lr;
-      const int r = m0 + ml;
-      const float gate = r < Ae ? g.rowgate[rbeg + r] : 0.f;
-      float part = 0.f;
-#pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        u32x2* p = reinterpret_cast<u32x2*>(&stg[ml * SP + 32 * wave + 8 * gq + 4 * khalf]);
-        const u32x2 hv = *p;
-        float da[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float h = bf16_bits_to_f32((hv[q >> 1] >> (16 * (q & 1))) & 0xffffu);
-          const float qv = acc[m][4 * gq + q];
-          part += qv * h;
-          da[q] = h > 0.f ? gate * qv : 0.f;
-        }
-        *p = u32x2{pack_bf16x2(da[0], da[1]), pack_bf16x2(da[2], da[3])};
-      }
-      part += __shfl_xor(part, 32);
-      if (khalf == 0) red[wave][ml] = part;
-    }
-    __syncthreads();
-    if (tid < R && m0 + tid < Ae)
-      g.dgp[(size_t)nt * g.max_rows + rbeg + m0 + tid] =
-          ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
     uint16_t* dA = reinterpret_cast<uint16_t*>(g.out) + (size_t)rbeg * g.F;
+    constexpr int PCH = R * (SPW / 8) / NTHR;  // 16-byte chunks per thread of a part
 #pragma unroll
-    for (int c = 0; c < 2 * MT; ++c) {
-      const int idx = tid + 256 * c;
-      const int row = idx >> 4, col = (idx & 15) * 8;
-      const int r = m0 + row, n = n0 + col;
-      // non-temporal, as measured faster for the kernels after E1
-      if (r < Ae && n < g.F)
-        __builtin_nontemporal_store(load16(&stg[row * SP + col]),
-                                    reinterpret_cast<u32x4*>(dA + (size_t)r * g.F + n));
+    for (int p = 0; p < NPART; ++p) {
+      const int pn0 = n0 + p * SPW;
+#pragma unroll
+      for (int c = 0; c < PCH; ++c) {
+        const int idx = tid + NTHR * c;
+        const int row = idx >> 4, col = (idx & 15) * 8;
+        const int r = m0 + row, n = pn0 + col;
+        store16(&stg[row * SP + col],
+                buffer_load16(h_src, (r < Ae && n < g.F) ? ((uint32_t)r * (uint32_t)g.F + (uint32_t)n) * 2u
+                                                          : kOob));
+      }
+      __syncthreads();
+      if (wave / 4 == p) {
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          const int ml = 32 * m + lr;
+          const int r = m0 + ml;
+          const float gate = r < Ae ? g.rowgate[rbeg + r] : 0.f;
+          float part = 0.f;
+#pragma unroll
+          for (int gq = 0; gq < 4; ++gq) {
+            u32x2* ptr = reinterpret_cast<u32x2*>(&stg[ml * SP + 32 * (wave % 4) + 8 * gq + 4 * khalf]);
+            const u32x2 hv = *ptr;
+            float da[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const float h = bf16_bits_to_f32((hv[q >> 1] >> (16 * (q & 1))) & 0xffffu);
+              const float qv = acc[m][4 * gq + q];
+              part += qv * h;
+              da[q] = h > 0.f ? gate * qv : 0.f;
+            }
+            *ptr = u32x2{pack_bf16x2(da[0], da[1]), pack_bf16x2(da[2], da[3])};
+          }
+          part += __shfl_xor(part, 32);
+          if (khalf == 0) red[wave][ml] = part;
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int c = 0; c < PCH; ++c) {
+        const int idx = tid + NTHR * c;
+        const int row = idx >> 4, col = (idx & 15) * 8;
+        const int r = m0 + row, n = pn0 + col;
+        // non-temporal, as measured faster for the kernels after E1
+        if (r < Ae && n < g.F)
+          __builtin_nontemporal_store(load16(&stg[row * SP + col]),
+                                      reinterpret_cast<u32x4*>(dA + (size_t)r * g.F + n));
+      }
+      if (p + 1 < NPART) __syncthreads();  // the part is read out before the next one lands
+    }
+    if (tid < R && m0 + tid < Ae) {
+      float sum = red[0][tid];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) sum += red[w][tid];
+      g.dgp[(size_t)nt * g.max_rows + rbeg + m0 + tid] = sum;
     }
   } else {
     float* dxe = reinterpret_cast<float*>(g.out);
@@ -1132,7 +1184,9 @@ bwd_poison_kernel(const int* __restrict__ bad, void* __restrict__ dW1, void* __r
 }
 
 // ---------------------------------------------------------------------------
-int bwd_dgp_tiles(const Shape& s) { return s.dtype == SFFN_BF16 ? (s.F + GN - 1) / GN : 1; }
+int bwd_dgp_tiles(const Shape& s) {
+  return s.dtype == SFFN_BF16 ? (s.F + kRowsCols - 1) / kRowsCols : 1;
+}
 
 int bwd_wr_parts(const Shape& s) {
   // Enough token parts for about 1024 blocks, each part at least 128 tokens.
@@ -1153,13 +1207,14 @@ static int bwd_rows_mt(int C) {
 
 template <int KIND>
 static hipError_t launch_rows(const BwdRowsArgs& g, int mt, int blocks, hipStream_t st) {
-  constexpr int PD = SFFN_BWD_PD_ROWS;
+  constexpr int PD = SFFN_BWD_PD_ROWS, NW = kRowsWaves;
+  const dim3 grid((unsigned)blocks), block(64 * NW);
   switch (mt) {
-    case 1: hipLaunchKernelGGL((bwd_rows_kernel<KIND, 1, PD>), dim3((unsigned)blocks), dim3(256), 0, st, g); break;
-    case 2: hipLaunchKernelGGL((bwd_rows_kernel<KIND, 2, PD>), dim3((unsigned)blocks), dim3(256), 0, st, g); break;
-    case 3: hipLaunchKernelGGL((bwd_rows_kernel<KIND, 3, PD>), dim3((unsigned)blocks), dim3(256), 0, st, g); break;
-    case 4: hipLaunchKernelGGL((bwd_rows_kernel<KIND, 4, PD>), dim3((unsigned)blocks), dim3(256), 0, st, g); break;
-    default: hipLaunchKernelGGL((bwd_rows_kernel<KIND, 5, PD>), dim3((unsigned)blocks), dim3(256), 0, st, g); break;
+    case 1: hipLaunchKernelGGL((bwd_rows_kernel<KIND, 1, PD, NW>), grid, block, 0, st, g); break;
+    case 2: hipLaunchKernelGGL((bwd_rows_kernel<KIND, 2, PD, NW>), grid, block, 0, st, g); break;
+    case 3: hipLaunchKernelGGL((bwd_rows_kernel<KIND, 3, PD, NW>), grid, block, 0, st, g); break;
+    case 4: hipLaunchKernelGGL((bwd_rows_kernel<KIND, 4, PD, NW>), grid, block, 0, st, g); break;
+    default: hipLaunchKernelGGL((bwd_rows_kernel<KIND, 5, PD, NW>), grid, block, 0, st, g); break;
   }
   return hipGetLastError();
 }
@@ -1192,7 +1247,7 @@ hipError_t launch_backward(const Shape& s, const Inputs& in, const BwdState& b, 
     if (bf16) {
       BwdRowsArgs g{(const uint16_t*)b.dy, (const uint16_t*)in.W2, b.offset, b.row2tok, b.rowgate,
                     (const uint16_t*)b.H, b.dA, b.dgp, s.T, s.d, s.F, s.max_rows, n_mc};
-      SFFN_CHECK(launch_rows<1>(g, mt, s.N * n_mc * ((s.F + GN - 1) / GN), st));
+      SFFN_CHECK(launch_rows<1>(g, mt, s.N * n_mc * ((s.F + kRowsCols - 1) / kRowsCols), st));
     } else {
       hipLaunchKernelGGL(bwd_e1_f32_kernel, dim3((unsigned)((n_rows + 255) / 256)), dim3(256), 0,
                          st, (const float*)b.dy, (const float*)in.W2, b.offset, b.row2tok,
@@ -1224,7 +1279,7 @@ hipError_t launch_backward(const Shape& s, const Inputs& in, const BwdState& b, 
     if (bf16) {
       BwdRowsArgs g{(const uint16_t*)b.dA, (const uint16_t*)in.W1, b.offset, b.row2tok, b.rowgate,
                     nullptr, b.dxe, nullptr, s.T, s.d, s.F, s.max_rows, n_mc};
-      SFFN_CHECK(launch_rows<2>(g, mt, s.N * n_mc * ((s.d + GN - 1) / GN), st));
+      SFFN_CHECK(launch_rows<2>(g, mt, s.N * n_mc * ((s.d + kRowsCols - 1) / kRowsCols), st));
     } else {
       const long n = (long)n_rows * s.d;
       hipLaunchKernelGGL(bwd_e2_f32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
@@ -1277,15 +1332,16 @@ hipError_t launch_backward(const Shape& s, const Inputs& in, const BwdState& b, 
   if (bf16) {
     BwdGemmArgs g3{(const uint16_t*)b.dy, (const uint16_t*)b.H, b.offset, b.row2tok, b.rowgate,
                    b.dW2, s.T, s.d, s.F};
-    const int t3 = ((s.d + GM - 1) / GM) * ((s.F + GN - 1) / GN);
-    hipLaunchKernelGGL((bwd_gemm_kernel<3, SFFN_BWD_PD_WGRAD>), dim3((unsigned)(s.N * t3)),
-                       dim3(256), 0, st, g3);
+    constexpr int TM = 64 * kWgradWm, TN = 64 * kWgradWn;
+    const int t3 = ((s.d + TM - 1) / TM) * ((s.F + TN - 1) / TN);
+    hipLaunchKernelGGL((bwd_gemm_kernel<3, SFFN_BWD_PD_WGRAD, kWgradWm, kWgradWn>),
+                       dim3((unsigned)(s.N * t3)), dim3(64 * kWgradWm * kWgradWn), 0, st, g3);
     SFFN_CHECK(hipGetLastError());
     BwdGemmArgs g4{(const uint16_t*)b.dA, (const uint16_t*)in.x, b.offset, b.row2tok, b.rowgate,
                    b.dW1, s.T, s.d, s.F};
-    const int t4 = ((s.F + GM - 1) / GM) * ((s.d + GN - 1) / GN);
-    hipLaunchKernelGGL((bwd_gemm_kernel<4, SFFN_BWD_PD_WGRAD>), dim3((unsigned)(s.N * t4)),
-                       dim3(256), 0, st, g4);
+    const int t4 = ((s.F + TM - 1) / TM) * ((s.d + TN - 1) / TN);
+    hipLaunchKernelGGL((bwd_gemm_kernel<4, SFFN_BWD_PD_WGRAD, kWgradWm, kWgradWn>),
+                       dim3((unsigned)(s.N * t4)), dim3(64 * kWgradWm * kWgradWn), 0, st, g4);
   } else {
     const long n = (long)s.d * s.F;
     const dim3 grid((unsigned)((n + 255) / 256), (unsigned)s.N);

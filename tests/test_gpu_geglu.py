@@ -48,6 +48,7 @@ def _case(w, k=1, sampled=False):
     dict(T=640, d=256, F=200, N=16, CF=0.5),                    # F off every tile width
     dict(T=4096, d=64, F=96, N=4, CF=1.25, bias_sigma=0.02),    # several row chunks per expert
     dict(T=1100, d=200, F=64, N=260, CF=2.0),                   # many experts, tiled logits
+    dict(T=2000, d=96, F=128, N=64, CF=1.0, bias_sigma=0.02),   # rows off the line grid, C = 31
 ])
 def test_geglu_bf16_shapes(case):
     _case(synth.workload("switch_base").replace(glu=True, **case))

@@ -95,6 +95,35 @@ def test_tall_expert_tiles(case):
 
 
 @pytest.mark.parametrize("case", [
+    dict(T=2000, d=96, F=256, N=64, CF=1.0, bias_sigma=0.02),    # C = 31: one row tile, K tail of half a step
+    dict(T=3000, d=160, F=128, N=48, CF=1.0),                    # C = 62: two row tiles, three k-steps
+    dict(T=1500, d=2080, F=256, N=40, CF=1.0, bias_sigma=0.02),  # the many-expert row length, C = 37
+    dict(T=1000, d=32, F=128, N=32, CF=1.0),                     # K = 32: half a k-step
+])
+def test_rows_off_the_line_grid(case):
+    """Token rows of x and weight rows that start mid-line (2d % 128 == 64) in tiles of one
+    or two row tiles, the many-expert layer's tile shape."""
+    _full_case(synth.workload("switch_base").replace(**case))
+
+
+def test_rows_off_the_line_grid_offset_x():
+    """The same with x starting 64 bytes past a line (a view one row into a larger
+    buffer), so that the even tokens are the ones that start mid-line."""
+    import torch
+    w = synth.workload("switch_base").replace(T=2000, d=96, F=256, N=64, CF=1.0, bias_sigma=0.02)
+
+    def offset_x(dev_in, x_raw, Wr_raw):
+        x = dev_in["x"]
+        big = torch.zeros((w.T + 1, w.d), dtype=x.dtype, device=x.device)
+        big[1:] = x
+        dev_in["x"] = big[1:]
+        assert dev_in["x"].data_ptr() % 128 == 64
+        return x_raw, Wr_raw
+
+    _full_case(w, mutate=offset_x)
+
+
+@pytest.mark.parametrize("case", [
     dict(T=76800, d=64, F=512, N=256, CF=1.0, bias_sigma=0.02),   # FFN1 split: 1024 tiles
     dict(T=76790, d=512, F=64, N=256, CF=1.0),                    # FFN2 split, ragged T
 ])
