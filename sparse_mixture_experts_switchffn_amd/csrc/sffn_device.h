@@ -37,9 +37,11 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast
 // sentinel index above every expert) always ends on an expert in [0, N),
 // whatever a token's logits hold.
 __device__ __forceinline__ bool route_before(float a, int ia, float b, int ib) {
-  const bool an = __builtin_isnan(a), bn = __builtin_isnan(b);
-  if (an | bn) return an & (!bn | (ia < ib));
-  return (a > b) | ((a == b) & (ia < ib));
+  // Written without branches (selects only): it runs per candidate in the
+  // routing loops.
+  const bool an = __builtin_isnan(a), bn = __builtin_isnan(b), lt = ia < ib;
+  const bool num = (a > b) | ((a == b) & lt);
+  return (an & (!bn | lt)) | (!an & !bn & num);
 }
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
