@@ -91,6 +91,7 @@ struct BwdGemmArgs {
   const int* row2tok;
   const float* rowgate;
   void* out;
+  const int* bad;  // set by the guard: the results are written as NaN
   int T, d, F;
 };
 
@@ -143,6 +144,7 @@ bwd_gemm_kernel(BwdGemmArgs g) {
   const int Ae = g.offset[e + 1] - rbeg;
   const int K = Ae;
   const int m0 = mt * TM, n0 = nt * TN;
+  const bool poison = *g.bad != 0;  // uniform
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -305,8 +307,9 @@ bwd_gemm_kernel(BwdGemmArgs g) {
     // stored non-temporal: nothing here reads the gradients again, and their
     // dirty lines would otherwise crowd the caches for the next kernels
     if (m < M && n < Nn)
-      __builtin_nontemporal_store(load16(&stg[row * SP + col]),
-                                  reinterpret_cast<u32x4*>(out + (size_t)m * Nn + n));
+      __builtin_nontemporal_store(
+          poison ? u32x4{0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u} : load16(&stg[row * SP + col]),
+          reinterpret_cast<u32x4*>(out + (size_t)m * Nn + n));
   }
 }
 
@@ -588,7 +591,8 @@ template <bool E4>
 __global__ void __launch_bounds__(256)
 bwd_wgrad_f32_kernel(const float* __restrict__ rowsA, const float* __restrict__ rowsB,
                      const int* __restrict__ offset, const int* __restrict__ row2tok,
-                     const float* __restrict__ rowgate, int d, int F, float* __restrict__ out) {
+                     const float* __restrict__ rowgate, int d, int F, const int* __restrict__ bad,
+                     float* __restrict__ out) {
   const int e = blockIdx.y;
   const int M = E4 ? F : d, Nn = E4 ? d : F;
   const long i = (long)blockIdx.x * 256 + threadIdx.x;
@@ -601,7 +605,7 @@ bwd_wgrad_f32_kernel(const float* __restrict__ rowsA, const float* __restrict__ 
     const float b = E4 ? rowsB[(size_t)tok * d + n] : rowsB[(size_t)r * F + n];
     s = fmaf(a, b, s);
   }
-  out[(size_t)e * M * Nn + i] = s;
+  out[(size_t)e * M * Nn + i] = *bad ? __uint_as_float(0x7fc00000u) : s;
 }
 
 // ---------------------------------------------------------------------------
@@ -1102,8 +1106,8 @@ template <bool BF16>
 __global__ void __launch_bounds__(256)
 bwd_bias_kernel(const void* __restrict__ dyv, const void* __restrict__ dAv,
                 const int* __restrict__ offset, const int* __restrict__ row2tok,
-                const float* __restrict__ rowgate, int d, int F, void* __restrict__ db1v,
-                void* __restrict__ db2v) {
+                const float* __restrict__ rowgate, int d, int F, const int* __restrict__ bad,
+                void* __restrict__ db1v, void* __restrict__ db2v) {
   const int e = blockIdx.y;
   const int c = blockIdx.x * 256 + threadIdx.x;  // columns of db2 then db1
   const bool first = c < d;
@@ -1123,8 +1127,9 @@ bwd_bias_kernel(const void* __restrict__ dyv, const void* __restrict__ dAv,
   }
   const size_t o = first ? (size_t)e * d + col : (size_t)e * F + col;
   void* out = first ? db2v : db1v;
-  if (BF16) ((uint16_t*)out)[o] = (uint16_t)f32_to_bf16_bits(s);
-  else ((float*)out)[o] = s;
+  const bool poison = *bad != 0;  // the guard failed: NaN
+  if (BF16) ((uint16_t*)out)[o] = poison ? (uint16_t)0x7fc0u : (uint16_t)f32_to_bf16_bits(s);
+  else ((float*)out)[o] = poison ? __uint_as_float(0x7fc00000u) : s;
 }
 
 // ---------------------------------------------------------------------------
@@ -1136,8 +1141,8 @@ bwd_bias_kernel(const void* __restrict__ dyv, const void* __restrict__ dAv,
 // copies offsets and counts into the backward's own workspace, where every
 // later kernel reads them.  On a mismatch it writes empty experts there
 // instead, so that no later kernel indexes the forward's maps, and raises
-// `bad`: dz, and through it dx and dWr, comes out NaN, and the last kernel
-// fills the weight and bias gradients with NaN.
+// `bad`: dz, and through it dx and dWr, comes out NaN, and the kernels that
+// write the weight and bias gradients (every element of them) write NaN.
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(256)
 bwd_guard_kernel(const uint32_t* __restrict__ tag, const WsTag want, uint32_t flags_allowed,
@@ -1160,27 +1165,6 @@ bwd_guard_kernel(const uint32_t* __restrict__ tag, const WsTag want, uint32_t fl
     if (i < N) hist_out[i] = ok ? hist[i] : 0;
   }
   if (threadIdx.x == 0) *bad = ok ? 0 : 1;
-}
-
-// The weight and bias gradients as NaN after a failed guard (nothing otherwise).
-__global__ void __launch_bounds__(256)
-bwd_poison_kernel(const int* __restrict__ bad, void* __restrict__ dW1, void* __restrict__ dW2,
-                  void* __restrict__ db1, void* __restrict__ db2, size_t n_w, size_t n_b1,
-                  size_t n_b2, int esize) {
-  if (*bad == 0) return;
-  const size_t stride = (size_t)gridDim.x * 256;
-  const size_t i0 = (size_t)blockIdx.x * 256 + threadIdx.x;
-  auto fill = [&](void* p, size_t n) {
-    if (!p) return;
-    for (size_t i = i0; i < n; i += stride) {
-      if (esize == 2) ((uint16_t*)p)[i] = 0x7fc0u;
-      else ((uint32_t*)p)[i] = 0x7fc00000u;
-    }
-  };
-  fill(dW1, n_w);
-  fill(dW2, n_w);
-  fill(db1, n_b1);
-  fill(db2, n_b2);
 }
 
 // ---------------------------------------------------------------------------
@@ -1331,14 +1315,14 @@ hipError_t launch_backward(const Shape& s, const Inputs& in, const BwdState& b, 
   SFFN_CHECK(mark());
   if (bf16) {
     BwdGemmArgs g3{(const uint16_t*)b.dy, (const uint16_t*)b.H, b.offset, b.row2tok, b.rowgate,
-                   b.dW2, s.T, s.d, s.F};
+                   b.dW2, b.bad, s.T, s.d, s.F};
     constexpr int TM = 64 * kWgradWm, TN = 64 * kWgradWn;
     const int t3 = ((s.d + TM - 1) / TM) * ((s.F + TN - 1) / TN);
     hipLaunchKernelGGL((bwd_gemm_kernel<3, SFFN_BWD_PD_WGRAD, kWgradWm, kWgradWn>),
                        dim3((unsigned)(s.N * t3)), dim3(64 * kWgradWm * kWgradWn), 0, st, g3);
     SFFN_CHECK(hipGetLastError());
     BwdGemmArgs g4{(const uint16_t*)b.dA, (const uint16_t*)in.x, b.offset, b.row2tok, b.rowgate,
-                   b.dW1, s.T, s.d, s.F};
+                   b.dW1, b.bad, s.T, s.d, s.F};
     const int t4 = ((s.F + TM - 1) / TM) * ((s.d + TN - 1) / TN);
     hipLaunchKernelGGL((bwd_gemm_kernel<4, SFFN_BWD_PD_WGRAD, kWgradWm, kWgradWn>),
                        dim3((unsigned)(s.N * t4)), dim3(64 * kWgradWm * kWgradWn), 0, st, g4);
@@ -1346,10 +1330,11 @@ hipError_t launch_backward(const Shape& s, const Inputs& in, const BwdState& b, 
     const long n = (long)s.d * s.F;
     const dim3 grid((unsigned)((n + 255) / 256), (unsigned)s.N);
     hipLaunchKernelGGL(bwd_wgrad_f32_kernel<false>, grid, dim3(256), 0, st, (const float*)b.dy,
-                       (const float*)b.H, b.offset, b.row2tok, b.rowgate, s.d, s.F, (float*)b.dW2);
+                       (const float*)b.H, b.offset, b.row2tok, b.rowgate, s.d, s.F, b.bad,
+                       (float*)b.dW2);
     SFFN_CHECK(hipGetLastError());
     hipLaunchKernelGGL(bwd_wgrad_f32_kernel<true>, grid, dim3(256), 0, st, (const float*)b.dA,
-                       (const float*)in.x, b.offset, b.row2tok, b.rowgate, s.d, s.F,
+                       (const float*)in.x, b.offset, b.row2tok, b.rowgate, s.d, s.F, b.bad,
                        (float*)b.dW1);
   }
   SFFN_CHECK(hipGetLastError());
@@ -1360,16 +1345,12 @@ hipError_t launch_backward(const Shape& s, const Inputs& in, const BwdState& b, 
     const dim3 grid((unsigned)((s.d + s.F + 255) / 256), (unsigned)s.N);
     if (bf16)
       hipLaunchKernelGGL(bwd_bias_kernel<true>, grid, dim3(256), 0, st, b.dy, b.dA, b.offset,
-                         b.row2tok, b.rowgate, s.d, s.F, b.db1, b.db2);
+                         b.row2tok, b.rowgate, s.d, s.F, b.bad, b.db1, b.db2);
     else
       hipLaunchKernelGGL(bwd_bias_kernel<false>, grid, dim3(256), 0, st, b.dy, b.dA, b.offset,
-                         b.row2tok, b.rowgate, s.d, s.F, b.db1, b.db2);
+                         b.row2tok, b.rowgate, s.d, s.F, b.bad, b.db1, b.db2);
     SFFN_CHECK(hipGetLastError());
   }
-  hipLaunchKernelGGL(bwd_poison_kernel, dim3(256), dim3(256), 0, st, b.bad, b.dW1, b.dW2, b.db1,
-                     b.db2, (size_t)s.N * s.d * s.F, (size_t)s.N * s.F, (size_t)s.N * s.d,
-                     bf16 ? 2 : 4);
-  SFFN_CHECK(hipGetLastError());
   SFFN_CHECK(mark());
 #undef SFFN_CHECK
   return hipSuccess;
