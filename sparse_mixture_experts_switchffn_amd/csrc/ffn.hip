@@ -717,10 +717,12 @@ struct FfnArgs {
 };
 
 // Block shapes (waves, 32-column tiles per wave) the launcher chooses from.
+// {8, 2}: 512-column tiles (one block per CU) for one or two row tiles, where
+// the activation rows are re-read least and a launch has half as many tiles.
 struct FfnShape {
   int fw, wn;
 };
-constexpr FfnShape kFfnShapes[] = {{4, 2}, {3, 2}, {8, 1}, {6, 1}, {4, 1}};
+constexpr FfnShape kFfnShapes[] = {{8, 2}, {4, 2}, {3, 2}, {8, 1}, {6, 1}, {4, 1}};
 
 template <int MT, int FW, int WN, bool SECOND, bool GLU>
 static constexpr bool ffn_shape_ok() {
@@ -728,8 +730,10 @@ static constexpr bool ffn_shape_ok() {
   // registers allow one wave per SIMD, which leaves too little latency
   // hiding.  Blocks of more than 4 waves (2 per SIMD) only up to 6 row tiles
   // (registers).  One thread per row for the row lookups; the LDS budget holds.
+  // 512-column tiles (eight waves of two column tiles) for one row tile only
+  // (registers).
   return (WN == 1 || MT <= 2) && (FW <= 4 || MT <= 6) && MT * 32 <= FW * 64 &&
-         FfnGeom<MT, FW, WN, SECOND, GLU>::fits;
+         (FW * WN <= 8 || MT == 1) && FfnGeom<MT, FW, WN, SECOND, GLU>::fits;
 }
 
 template <int MT, int FW, int WN, bool SECOND, bool GLU>
@@ -782,6 +786,7 @@ static void launch_ffn_bf16_t(const FfnArgs& a, hipStream_t st) {
 template <int MT, bool SECOND, bool GLU>
 static double ffn_shape_cost(const FfnArgs& a, FfnShape sh, int cus) {
   long resident = 0;
+  if (sh.fw == 8 && sh.wn == 2) resident = ffn_resident_if_ok<MT, 8, 2, SECOND, GLU>();
   if (sh.fw == 4 && sh.wn == 2) resident = ffn_resident_if_ok<MT, 4, 2, SECOND, GLU>();
   if (sh.fw == 3 && sh.wn == 2) resident = ffn_resident_if_ok<MT, 3, 2, SECOND, GLU>();
   if (sh.fw == 8 && sh.wn == 1) resident = ffn_resident_if_ok<MT, 8, 1, SECOND, GLU>();
@@ -816,7 +821,8 @@ static void launch_ffn_bf16_mt(const FfnArgs& a, hipStream_t st) {
       best = sh;
     }
   }
-  if (best.fw == 4 && best.wn == 2) launch_ffn_bf16_t<MT, 4, 2, SECOND, GLU>(a, st);
+  if (best.fw == 8 && best.wn == 2) launch_ffn_bf16_t<MT, 8, 2, SECOND, GLU>(a, st);
+  else if (best.fw == 4 && best.wn == 2) launch_ffn_bf16_t<MT, 4, 2, SECOND, GLU>(a, st);
   else if (best.fw == 3 && best.wn == 2) launch_ffn_bf16_t<MT, 3, 2, SECOND, GLU>(a, st);
   else if (best.fw == 8) launch_ffn_bf16_t<MT, 8, 1, SECOND, GLU>(a, st);
   else if (best.fw == 6) launch_ffn_bf16_t<MT, 6, 1, SECOND, GLU>(a, st);
