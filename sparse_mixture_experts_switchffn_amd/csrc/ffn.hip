@@ -780,9 +780,11 @@ static void launch_ffn_bf16_t(const FfnArgs& a, hipStream_t st) {
 }
 
 // Estimated time of one launch with a block shape, in units of one row of K
-// streamed through a CU: each tile streams its COLS weight rows and re-reads
-// its activation rows (mostly L2 hits, weighted 0.6); tiles run in rounds of
-// the resident grid.  Returns a huge cost for shapes that cannot run.
+// streamed through a CU: each tile streams its weight rows (on average the
+// output columns over the column tiles: a ragged last tile streams only its
+// own rows) and re-reads its activation rows (mostly L2 hits, weighted 0.6);
+// tiles run in rounds of the resident grid.  Returns a huge cost for shapes
+// that cannot run.
 template <int MT, bool SECOND, bool GLU>
 static double ffn_shape_cost(const FfnArgs& a, FfnShape sh, int cus) {
   long resident = 0;
@@ -794,9 +796,10 @@ static double ffn_shape_cost(const FfnArgs& a, FfnShape sh, int cus) {
   if (sh.fw == 4 && sh.wn == 1) resident = ffn_resident_if_ok<MT, 4, 1, SECOND, GLU>();
   if (resident <= 0) return 1e300;
   const long cols = sh.fw * sh.wn * 32;
-  const long n_tiles = ffn_col_tiles(a, cols, GLU) * a.n_mchunks * a.n_experts;
+  const long n_ct = ffn_col_tiles(a, cols, GLU);
+  const long n_tiles = n_ct * a.n_mchunks * a.n_experts;
   const long rounds = (n_tiles + resident - 1) / resident;
-  const double tile = (double)cols + 0.6 * MT * 32;
+  const double tile = (double)(GLU ? 2 * a.Nout : a.Nout) / (double)n_ct + 0.6 * MT * 32;
   return (double)rounds * (double)resident / (double)cus * tile;
 }
 
@@ -814,6 +817,9 @@ static void launch_ffn_bf16_mt(const FfnArgs& a, hipStream_t st) {
   for (const FfnShape& sh : kFfnShapes) {  // first of equal cost wins (fewer LDS reads)
 #ifdef SFFN_FFN_ONLY_WN  // tuning builds: restrict the choice to one wave width
     if (sh.wn != SFFN_FFN_ONLY_WN) continue;
+#endif
+#ifdef SFFN_FFN2_ONLY_FW  // tuning builds: restrict the second GEMM to one block shape
+    if (SECOND && (sh.fw != SFFN_FFN2_ONLY_FW || sh.wn != 2)) continue;
 #endif
     const double c = ffn_shape_cost<MT, SECOND, GLU>(a, sh, cus);
     if (c < best_cost) {
