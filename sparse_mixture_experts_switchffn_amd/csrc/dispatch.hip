@@ -19,27 +19,30 @@
 namespace sffn {
 
 // ---------------------------------------------------------------------------
-// Column scan over routing blocks.  Block = 32 experts x 32 segments of routing
-// blocks (1024 threads).  Outputs base[b][e] (start[e] + tokens of e in blocks
-// < b), hist[e], acc[e] = min(start[e] + hist[e], C) and psum[e] = sum_b
-// ppart[b][e] (float64, segment partial sums combined in segment order).
-// start (rerouting's second stage), ppart/psum, hist and cnt1/hist1 may be
-// null: start counts as 0 and the others are skipped.
+// Column scan over routing blocks.  Block = EPB experts x 1024/EPB segments of
+// routing blocks (1024 threads; EPB = 8 gives four times the blocks of EPB =
+// 32, which the scan's short columns need to spread over the GPU).  Outputs
+// base[b][e] (start[e] + tokens of e in blocks < b), hist[e], acc[e] =
+// min(start[e] + hist[e], C) and psum[e] = sum_b ppart[b][e] (float64, segment
+// partial sums combined in segment order).  start (rerouting's second stage),
+// ppart/psum, hist and cnt1/hist1 may be null: start counts as 0 and the
+// others are skipped.
 // ---------------------------------------------------------------------------
-constexpr int kScanSegs = 32;
+constexpr int kScanEpb = 8;
+constexpr int kScanSegs = 1024 / kScanEpb;
 
-__global__ void __launch_bounds__(32 * kScanSegs)
+__global__ void __launch_bounds__(1024)
 dispatch_scan_kernel(const int* __restrict__ cnt, const float* __restrict__ ppart, int nblk,
                      int N, int C, int* __restrict__ base, int* __restrict__ hist,
                      int* __restrict__ acc, double* __restrict__ psum,
                      const int* __restrict__ cnt1, int* __restrict__ hist1,
                      const int* __restrict__ start) {
-  __shared__ int part[kScanSegs][33];
-  __shared__ int part1[kScanSegs][33];
-  __shared__ double ppart_s[kScanSegs][33];
-  const int el = threadIdx.x & 31;
-  const int seg = threadIdx.x >> 5;
-  const int e = blockIdx.x * 32 + el;
+  __shared__ int part[kScanSegs][kScanEpb + 1];
+  __shared__ int part1[kScanSegs][kScanEpb + 1];
+  __shared__ double ppart_s[kScanSegs][kScanEpb + 1];
+  const int el = threadIdx.x % kScanEpb;
+  const int seg = threadIdx.x / kScanEpb;
+  const int e = blockIdx.x * kScanEpb + el;
   const int per = (nblk + kScanSegs - 1) / kScanSegs;
   const int c0 = min(nblk, seg * per);
   const int c1 = min(nblk, c0 + per);
@@ -133,7 +136,7 @@ reroute_count_kernel(const int32_t* __restrict__ choice, const int* __restrict__
 }
 
 hipError_t launch_dispatch_scan(const Shape& s, const Workspace& ws, hipStream_t st) {
-  const dim3 grid((unsigned)((s.N + 31) / 32)), block(32 * kScanSegs);
+  const dim3 grid((unsigned)((s.N + kScanEpb - 1) / kScanEpb)), block(1024);
   hipLaunchKernelGGL(dispatch_scan_kernel, grid, block, 0, st, ws.cnt, ws.ppart,
                      s.n_route_blocks, s.N, s.C, ws.base, ws.hist, ws.acc, ws.psum,
                      s.k == 2 ? ws.cnt1 : nullptr, s.k == 2 ? ws.hist1 : nullptr, nullptr);
