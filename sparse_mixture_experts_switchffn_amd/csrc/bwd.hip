@@ -78,11 +78,17 @@ __device__ __forceinline__ bf16x8 tr_fragment(const uint16_t* S, int k0, int mba
 #define SFFN_BWD_WGRAD_WN 4
 #endif
 constexpr int kWgradWm = SFFN_BWD_WGRAD_WM, kWgradWn = SFFN_BWD_WGRAD_WN;
-// Waves of E1/E2's block (32 output columns each).
+// Waves of E1's and E2's blocks (32 output columns each).  E2 produces d columns, a quarter of
+// E1's F: 192-column tiles give it four column tiles at d = 768, so one block per CU with 64
+// experts, where 256-column tiles leave a quarter of the CUs idle.
 #ifndef SFFN_BWD_ROWS_NW
 #define SFFN_BWD_ROWS_NW 8
 #endif
-constexpr int kRowsWaves = SFFN_BWD_ROWS_NW, kRowsCols = 32 * kRowsWaves;
+#ifndef SFFN_BWD_E2_NW
+#define SFFN_BWD_E2_NW 6
+#endif
+constexpr int kRowsWaves = SFFN_BWD_ROWS_NW, kRowsCols = 32 * kRowsWaves;  // E1
+constexpr int kE2Waves = SFFN_BWD_E2_NW, kE2Cols = 32 * kE2Waves;          // E2
 
 struct BwdGemmArgs {
   const uint16_t* a;
@@ -349,7 +355,8 @@ bwd_rows_kernel(BwdRowsArgs g) {
   constexpr int SP = SPW + 8;               // staged part pitch (bf16)
   constexpr int NPART = CW / SPW;
   constexpr int RING = 2 * R * GP + 2 * GK * RPW;
-  static_assert(NTHR / CRB == 16 && CW % SPW == 0, "two weight passes of 16 k rows");
+  static_assert(NTHR / CRB == 16, "two weight passes of 16 k rows");
+  static_assert(KIND != 1 || CW % SPW == 0, "E1's epilogue parts");
   static_assert(R * SP <= RING, "a staged part fits the rings");
   __shared__ __attribute__((aligned(16))) uint16_t lds[RING];
   __shared__ float red[NW][R];
@@ -1191,7 +1198,7 @@ static int bwd_rows_mt(int C) {
 
 template <int KIND>
 static hipError_t launch_rows(const BwdRowsArgs& g, int mt, int blocks, hipStream_t st) {
-  constexpr int PD = SFFN_BWD_PD_ROWS, NW = kRowsWaves;
+  constexpr int PD = SFFN_BWD_PD_ROWS, NW = KIND == 1 ? kRowsWaves : kE2Waves;
   const dim3 grid((unsigned)blocks), block(64 * NW);
   switch (mt) {
     case 1: hipLaunchKernelGGL((bwd_rows_kernel<KIND, 1, PD, NW>), grid, block, 0, st, g); break;
@@ -1263,7 +1270,7 @@ hipError_t launch_backward(const Shape& s, const Inputs& in, const BwdState& b, 
     if (bf16) {
       BwdRowsArgs g{(const uint16_t*)b.dA, (const uint16_t*)in.W1, b.offset, b.row2tok, b.rowgate,
                     nullptr, b.dxe, nullptr, s.T, s.d, s.F, s.max_rows, n_mc};
-      SFFN_CHECK(launch_rows<2>(g, mt, s.N * n_mc * ((s.d + kRowsCols - 1) / kRowsCols), st));
+      SFFN_CHECK(launch_rows<2>(g, mt, s.N * n_mc * ((s.d + kE2Cols - 1) / kE2Cols), st));
     } else {
       const long n = (long)n_rows * s.d;
       hipLaunchKernelGGL(bwd_e2_f32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
