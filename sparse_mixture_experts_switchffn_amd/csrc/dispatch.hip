@@ -136,6 +136,7 @@ reroute_count_kernel(const int32_t* __restrict__ choice, const int* __restrict__
 }
 
 hipError_t launch_dispatch_scan(const Shape& s, const Workspace& ws, hipStream_t st) {
+  if (dispatch_scan_in_scatter(s)) return hipSuccess;  // done by dispatch_scatter_fold_kernel
   const dim3 grid((unsigned)((s.N + kScanEpb - 1) / kScanEpb)), block(1024);
   hipLaunchKernelGGL(dispatch_scan_kernel, grid, block, 0, st, ws.cnt, ws.ppart,
                      s.n_route_blocks, s.N, s.C, ws.base, ws.hist, ws.acc, ws.psum,
@@ -305,6 +306,130 @@ dispatch_scatter_kernel(const int32_t* __restrict__ expert_idx, const int* __res
 }
 
 // ---------------------------------------------------------------------------
+// Top-1 dispatch with the column scan folded in, for layers whose count table
+// cnt[nblk][N] is small: every block sums the table itself, so no scan pass
+// runs before it.  For each expert e, block b takes pre[e] = tokens of e in
+// routing blocks < b and tot[e] = tokens of e in all blocks (integer sums, the
+// same in any order), acc[e] = min(tot[e], C), and the offsets from acc.
+// Threads read 16-byte chunks of four experts' counts: chunk j of a row by the
+// threads of column j, routing blocks split into segments by thread row, the
+// segment partials combined in LDS.  Block 0 also takes psum[e] = sum_b
+// ppart[b][e] in float64 (each segment in block order, then the segments in
+// order) and writes hist = tot, the offsets, the aux loss and the statistics.
+// ---------------------------------------------------------------------------
+constexpr int kFoldMaxExperts = 256;
+constexpr int kFoldRowsPerThread = 16;  // all of a thread's table rows in flight at once
+
+bool dispatch_scan_in_scatter(const Shape& s) {
+  if (s.k != 1 || s.reroute || s.N % 4 != 0 || s.N > kFoldMaxExperts) return false;
+  const int segs = 256 / (s.N / 4) < s.n_route_blocks ? 256 / (s.N / 4) : s.n_route_blocks;
+  return (s.n_route_blocks + segs - 1) / segs <= kFoldRowsPerThread;
+}
+
+__global__ void __launch_bounds__(256)
+dispatch_scatter_fold_kernel(const int32_t* __restrict__ expert_idx, const int* __restrict__ cnt,
+                             const float* __restrict__ ppart, const int* __restrict__ lrank,
+                             int nblk, int T, int N, int C, int d, int esize,
+                             const void* __restrict__ x, void* __restrict__ y, int no_residual,
+                             const float* __restrict__ gate, int32_t* __restrict__ slot,
+                             int* __restrict__ row2tok, float* __restrict__ rowgate,
+                             int* __restrict__ hist, int* __restrict__ offset,
+                             float* __restrict__ aux_loss, int32_t* __restrict__ stat_count,
+                             int32_t* __restrict__ stat_accepted,
+                             int32_t* __restrict__ stat_dropped, uint32_t* __restrict__ tag,
+                             const WsTag tagv) {
+  __shared__ u32x4 part_pre[256], part_tot[256];
+  __shared__ double part_ps[256][4];
+  __shared__ int pre_s[kFoldMaxExperts], tot_s[kFoldMaxExperts], acc_s[kFoldMaxExperts];
+  __shared__ double psum_s[kFoldMaxExperts];
+  __shared__ int off_s[kFoldMaxExperts + 1];
+  __shared__ int tsum[256];
+  __shared__ int dropped_s[kRouteTokens];
+  __shared__ double red[256];
+
+  const int b = blockIdx.x;
+  const int cpr = N >> 2;            // 16-byte chunks per row of the table
+  const int segs = min(256 / cpr, nblk);  // segments of routing blocks
+  const int j = threadIdx.x % cpr, sg = threadIdx.x / cpr;
+  const int per = (nblk + segs - 1) / segs;  // at most kFoldRowsPerThread
+  const int c0 = sg < segs ? min(nblk, sg * per) : nblk;
+  const int c1 = min(nblk, c0 + per);
+  u32x4 pre{0, 0, 0, 0}, tot{0, 0, 0, 0};
+  double ps[4] = {0.0, 0.0, 0.0, 0.0};
+  {
+    u32x4 v[kFoldRowsPerThread];
+#pragma unroll
+    for (int r = 0; r < kFoldRowsPerThread; ++r)
+      v[r] = c0 + r < c1 ? load16(cnt + (size_t)(c0 + r) * N + 4 * j) : u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int r = 0; r < kFoldRowsPerThread; ++r) {
+      tot += v[r];
+      if (c0 + r < b) pre += v[r];
+    }
+  }
+  if (b == 0) {
+    u32x4 v[kFoldRowsPerThread];
+#pragma unroll
+    for (int r = 0; r < kFoldRowsPerThread; ++r)
+      v[r] = c0 + r < c1 ? load16(ppart + (size_t)(c0 + r) * N + 4 * j) : u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int r = 0; r < kFoldRowsPerThread; ++r)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) ps[q] += (double)__uint_as_float(v[r][q]);  // block order
+  }
+  part_pre[threadIdx.x] = pre;
+  part_tot[threadIdx.x] = tot;
+  if (b == 0) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) part_ps[threadIdx.x][q] = ps[q];
+  }
+  __syncthreads();
+  if ((int)threadIdx.x < N) {
+    const int e = threadIdx.x, jj = e >> 2, q = e & 3;
+    int p = 0, t = 0;
+    double sp = 0.0;
+    for (int g = 0; g < segs; ++g) {
+      p += (int)part_pre[g * cpr + jj][q];
+      t += (int)part_tot[g * cpr + jj][q];
+      if (b == 0) sp += part_ps[g * cpr + jj][q];
+    }
+    pre_s[e] = p;
+    tot_s[e] = t;
+    acc_s[e] = min(t, C);
+    psum_s[e] = sp;
+  }
+  __syncthreads();
+  block_offsets(acc_s, N, off_s, tsum);
+
+  const int tb = b * kRouteTokens;
+  if (threadIdx.x < kRouteTokens) {
+    const int t = tb + threadIdx.x;
+    int dropped = 0;
+    if (t < T) {
+      const int e = expert_idx[t];
+      const bool ok = (unsigned)e < (unsigned)N;  // as in dispatch_scatter_kernel
+      const int r = ok ? pre_s[e] + lrank[t] : C;
+      if (r < C) {
+        slot[t] = r;
+        row2tok[off_s[e] + r] = t;
+        rowgate[off_s[e] + r] = gate[t];
+      } else {
+        slot[t] = -1;
+        dropped = 1;
+      }
+    }
+    dropped_s[threadIdx.x] = dropped;
+  }
+  __syncthreads();
+
+  pass_through_dropped(dropped_s, tb, d, esize, x, y, no_residual);
+  if (b != 0) return;
+  for (int e = threadIdx.x; e < N; e += 256) hist[e] = tot_s[e];
+  finish_dispatch(tot_s, tot_s, acc_s, psum_s, T, N, T, off_s, tsum, red, offset, aux_loss,
+                  stat_count, stat_accepted, stat_dropped, tag, tagv);
+}
+
+// ---------------------------------------------------------------------------
 // Top-2 dispatch: slots and the row maps of both choices of every token (each
 // expert column in token order).  The residual path is left to the combine,
 // which writes every y row.  Block 0 also writes the expert offsets, the aux
@@ -440,6 +565,14 @@ hipError_t launch_dispatch_scatter(const Shape& s, const Inputs& in, const Works
                        s.d, esize, in.x, out.y, no_residual ? 1 : 0, out.expert_idx, out.gate,
                        out.slot, ws.row2tok, ws.rowgate, ws.offset, out.aux_loss,
                        out.stat_count, out.stat_accepted, out.stat_dropped, ws.tag, tag);
+    return hipGetLastError();
+  }
+  if (dispatch_scan_in_scatter(s)) {
+    hipLaunchKernelGGL(dispatch_scatter_fold_kernel, grid, block, 0, st, out.expert_idx, ws.cnt,
+                       ws.ppart, ws.lrank, s.n_route_blocks, s.T, s.N, s.C, s.d, esize, in.x,
+                       out.y, no_residual ? 1 : 0, out.gate, out.slot, ws.row2tok, ws.rowgate,
+                       ws.hist, ws.offset, out.aux_loss, out.stat_count, out.stat_accepted,
+                       out.stat_dropped, ws.tag, tag);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(dispatch_scatter_kernel, grid, block, 0, st, out.expert_idx, ws.base,

@@ -221,10 +221,16 @@ router_planes_kernel(const float* __restrict__ Wr, int d, int N, int MT, int nks
 // takes k-steps w, w+4, ...), which spreads the token stream over four times as
 // many blocks; the four partial logit tiles are summed in LDS in wave order.
 //
-// GEMM: rows = experts (the router planes, one coalesced fragment load each,
-// L2-resident), columns = tokens (four lanes per 64-byte row segment,
+// GEMM: rows = experts, columns = tokens (four lanes per 64-byte row segment,
 // re-laid out through a private LDS slot into the operand layout).  32 k per
-// step, operands fetched 2-3 steps ahead.
+// step, operands fetched 2-3 steps ahead.  The expert operand: for up to 64
+// experts (MT <= 2) straight from fp32 Wr (16-byte aligned rows, d % 8 == 0):
+// each lane loads the 16 consecutive weights of its row and k-half and splits
+// them into the three bf16 planes in registers, one hardware conversion per
+// pair and plane, so no planes pass runs first and Wr costs 4 bytes a weight
+// against the planes' 6.  For more experts the split's VALU work outweighs
+// that, and the block reads the router planes (one coalesced 1 KB fragment
+// load per plane and tile).
 // Epilogue (all four waves): the partial logit tiles meet in LDS and are
 // summed in wave order (and the fp32 logits are written to the workspace, where
 // the backward pass reads them); eight threads per token then take
@@ -247,8 +253,9 @@ static_assert(kRouteTokens == 32, "one block routes 32 tokens");
 
 template <int MT, int MODE>
 __global__ void __launch_bounds__(64 * FR_KSPLIT)
-router_fused_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ planes,
-                    uint32_t planes_bytes, int T, int d, int N, int32_t* __restrict__ expert_idx,
+router_fused_kernel(const uint16_t* __restrict__ x, const float* __restrict__ Wr,
+                    const uint16_t* __restrict__ planes, uint32_t planes_bytes, int T, int d, int N,
+                    int32_t* __restrict__ expert_idx,
                     float* __restrict__ gate, float* __restrict__ ppart, int* __restrict__ cnt,
                     int* __restrict__ lrank, int* __restrict__ cnt1,
                     float* __restrict__ logits) {
@@ -265,8 +272,17 @@ router_fused_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__
   const int t0 = b * kRouteTokens;
   const int khalf = lane >> 5;
 
-  const __amdgpu_buffer_rsrc_t rp_src = make_rsrc(planes, planes_bytes);
+  constexpr bool WF = MT <= 2;  // Wr split in registers, else the planes
+  const __amdgpu_buffer_rsrc_t rw_src =
+      WF ? make_rsrc(Wr, (uint32_t)((size_t)N * d * 4)) : make_rsrc(planes, planes_bytes);
   const __amdgpu_buffer_rsrc_t rx_src = make_rsrc(x, (uint32_t)((size_t)T * d * 2));
+  // Byte offset of Wr[32 m + lane%32][16 khalf] (kOob past the experts).
+  uint32_t w_row[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    const int row = 32 * m + (lane & 31);
+    w_row[m] = row < N ? ((uint32_t)row * (uint32_t)d + 16u * (uint32_t)khalf) * 4u : kOob;
+  }
   uint32_t x_off[2];
   bool x_ok[2];
 #pragma unroll
@@ -279,16 +295,30 @@ router_fused_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__
   const int nks = (d + FR_BK - 1) / FR_BK;
   const int nmine = (nks + FR_KSPLIT - 1) / FR_KSPLIT;      // this wave's steps, padded
   const int nk = (nmine + RFP - 1) / RFP * RFP;
-  const uint32_t step_bytes = 3u * MT * 2u * 1024u;
+  constexpr int NA = WF ? MT * 4 : 3 * MT * 2;  // 16-byte expert-operand loads a step
+  const uint32_t step_bytes = 3u * MT * 2u * 1024u;  // planes of one k-step
 
   // Local step j of this wave is global k-step wave + 4 j.
-  auto load_a = [&](u32x4 (&ra)[3 * MT * 2], int j) {
+  auto load_a = [&](u32x4 (&ra)[NA], int j) {
     const int ks = wave + FR_KSPLIT * j;
-    const bool kin = ks < nks;
+    if constexpr (WF) {
+      // Chunk c holds k = 32 ks + 16 khalf + 4 c + 0..3; d % 4 == 0, so a chunk is
+      // wholly inside or wholly past the row.
 #pragma unroll
-    for (int f = 0; f < 3 * MT * 2; ++f)
-      ra[f] = buffer_load16(rp_src, kin ? (uint32_t)ks * step_bytes + (uint32_t)f * 1024u +
-                                              (uint32_t)lane * 16u : kOob);
+      for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const bool kin = ks * FR_BK + 16 * khalf + 4 * c < d;
+          ra[m * 4 + c] = buffer_load16(
+              rw_src, kin ? w_row[m] + (uint32_t)ks * (FR_BK * 4) + 16u * c : kOob);
+        }
+    } else {
+      const bool kin = ks < nks;
+#pragma unroll
+      for (int f = 0; f < 3 * MT * 2; ++f)
+        ra[f] = buffer_load16(rw_src, kin ? (uint32_t)ks * step_bytes + (uint32_t)f * 1024u +
+                                                (uint32_t)lane * 16u : kOob);
+    }
   };
   auto load_x = [&](u32x4 (&rx)[2], int j) {
     const int ks = wave + FR_KSPLIT * j;
@@ -301,22 +331,44 @@ router_fused_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__
   f32x16 acc[MT];
 #pragma unroll
   for (int m = 0; m < MT; ++m) acc[m] = f32x16{};
-  auto compute = [&](const u32x4 (&ra)[3 * MT * 2], const u32x4 (&rx)[2]) {
+  auto compute = [&](const u32x4 (&ra)[NA], const u32x4 (&rx)[2]) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) store16(xslot + (i * 16 + (lane >> 2)) * FR_LD + (lane & 3) * 8, rx[i]);
     const uint16_t* xbase = xslot + (lane & 31) * FR_LD + khalf * 16;
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       const bf16x8 bv = as_bf16x8(load16(xbase + q * 8));
+      u32x4 pl[3][MT];  // the hi, mid and lo planes of this lane's 8 weights per tile
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        if constexpr (WF) {
+          // w = hi + mid + lo exactly: each plane is the round-to-nearest-even bf16 of
+          // what the earlier planes leave, and each remainder is exact in fp32.
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const u32x4& ch = ra[(m * 4 + 2 * q + (j >> 1)) % NA];
+            float w0 = __uint_as_float(ch[(2 * j) & 3]), w1 = __uint_as_float(ch[(2 * j + 1) & 3]);
+#pragma unroll
+            for (int p = 0; p < 3; ++p) {
+              const uint32_t h = pack_bf16x2(w0, w1);
+              pl[p][m][j] = h;
+              w0 -= __uint_as_float(h << 16);
+              w1 -= __uint_as_float(h & 0xffff0000u);
+            }
+          }
+        } else {
+#pragma unroll
+          for (int p = 0; p < 3; ++p) pl[p][m] = ra[(p * MT + m) * 2 + q];
+        }
+      }
 #pragma unroll
       for (int p = 0; p < 3; ++p)
 #pragma unroll
-        for (int m = 0; m < MT; ++m)
-          acc[m] = mfma_32x32x16(as_bf16x8(ra[(p * MT + m) * 2 + q]), bv, acc[m]);
+        for (int m = 0; m < MT; ++m) acc[m] = mfma_32x32x16(as_bf16x8(pl[p][m]), bv, acc[m]);
     }
   };
 
-  u32x4 ra[RFP][3 * MT * 2];
+  u32x4 ra[RFP][NA];
   u32x4 rx[RFP][2];
 #pragma unroll
   for (int st = 0; st < RFP; ++st) {
@@ -1087,9 +1139,11 @@ softmax_route_vec_kernel(const float* __restrict__ logits, int T, int N,
 
 int router_plane_tiles(int N) { return (N + 31) / 32; }
 
+// The tiled router, and the fused one for more than 64 experts, read planes;
+// the fused router for up to 64 experts splits Wr as it loads it.
 size_t router_planes_bytes(const Shape& s) {
   if (router_is_tiled(s)) return tiled_planes_bytes(s);
-  if (!router_is_fused(s)) return 0;
+  if (!router_is_fused(s) || router_plane_tiles(s.N) <= 2) return 0;
   const size_t nks = (size_t)(s.d + FR_BK - 1) / FR_BK;
   return nks * 3 * (size_t)router_plane_tiles(s.N) * 2 * 1024;
 }
@@ -1097,12 +1151,14 @@ size_t router_planes_bytes(const Shape& s) {
 hipError_t launch_router_fused(const Shape& s, const Inputs& in, const Workspace& ws,
                                const Outputs& out, hipStream_t st) {
   const int mt = router_plane_tiles(s.N);
-  const int nks = (s.d + FR_BK - 1) / FR_BK;
-  const int groups = nks * mt * 2 * 64;
-  hipLaunchKernelGGL(router_planes_kernel, dim3((unsigned)((groups + 255) / 256)), dim3(256), 0,
-                     st, in.Wr, s.d, s.N, mt, nks, ws.planes);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (mt > 2) {
+    const int nks = (s.d + FR_BK - 1) / FR_BK;
+    const int groups = nks * mt * 2 * 64;
+    hipLaunchKernelGGL(router_planes_kernel, dim3((unsigned)((groups + 255) / 256)), dim3(256), 0,
+                       st, in.Wr, s.d, s.N, mt, nks, ws.planes);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   const dim3 grid((unsigned)s.n_route_blocks), block(256);
   const uint16_t* x = (const uint16_t*)in.x;
   const uint32_t pbytes = (uint32_t)router_planes_bytes(s);
@@ -1110,9 +1166,10 @@ hipError_t launch_router_fused(const Shape& s, const Inputs& in, const Workspace
   const int mode = s.k == 2 ? 1 : (s.reroute ? 2 : 0);
   int32_t* const eidx = mode == 2 ? ws.choice : out.expert_idx;
   float* const g = mode == 2 ? ws.gate2 : out.gate;
-#define SFFN_FUSED(M, MO)                                                                         \
-  hipLaunchKernelGGL((router_fused_kernel<M, MO>), grid, block, 0, st, x, ws.planes, pbytes, s.T, \
-                     s.d, s.N, eidx, g, ws.ppart, ws.cnt, ws.lrank, ws.cnt1, ws.logits)
+#define SFFN_FUSED(M, MO)                                                                      \
+  hipLaunchKernelGGL((router_fused_kernel<M, MO>), grid, block, 0, st, x, in.Wr, ws.planes,     \
+                     pbytes, s.T, s.d, s.N, eidx, g, ws.ppart, ws.cnt, ws.lrank, ws.cnt1,       \
+                     ws.logits)
 #define SFFN_FUSED_MODES(M)         \
   if (mode == 0) SFFN_FUSED(M, 0);  \
   else if (mode == 1) SFFN_FUSED(M, 1); \

@@ -64,7 +64,7 @@ struct Workspace {
   float* rowgate;  // [max_rows] gate of each expert-buffer row's token
   void* H;         // [max_rows, F] expert hidden activations (dtype)
   void* Y2;        // [max_rows, d] gate-scaled expert outputs per buffer row (k = 2, dtype)
-  uint16_t* planes;  // router weights split into three bf16 planes, fragment order (fused router)
+  uint16_t* planes;  // router weights split into three bf16 planes, fragment order (tiled router; fused router for > 64 experts)
 };
 
 // Records the HIP error text for switch_ffn_status_string and returns SFFN_EHIP.
@@ -102,6 +102,7 @@ hipError_t launch_softmax_route(const Shape& s, const Inputs& in, const Workspac
                                 const Outputs& out, hipStream_t st);
 bool router_is_fused(const Shape& s);
 size_t router_planes_bytes(const Shape& s);
+bool dispatch_scan_in_scatter(const Shape& s);
 // Rerouting: also the overflow count of the second stage and its scan.
 hipError_t launch_dispatch_scan(const Shape& s, const Workspace& ws, hipStream_t st);
 // Also writes the layout tag `tag` into ws.tag (block 0).

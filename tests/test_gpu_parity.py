@@ -106,6 +106,19 @@ def test_rows_off_the_line_grid(case):
     _full_case(synth.workload("switch_base").replace(**case))
 
 
+@pytest.mark.parametrize("case", [
+    dict(T=8192, d=64, F=64, N=64, CF=1.0, bias_sigma=0.02),     # 256 blocks: the folded scan's limit
+    dict(T=8193, d=64, F=64, N=64, CF=1.0, bias_sigma=0.02),     # 257 blocks: the separate scan
+    dict(T=4000, d=64, F=64, N=128, CF=1.0),                     # 128 experts folded, router planes
+    dict(T=700, d=64, F=64, N=60, CF=1.0, bias_sigma=0.02),      # 15 chunks a row: idle threads
+    dict(T=3000, d=96, F=64, N=100, CF=1.0),                     # four partial expert tiles
+])
+def test_scan_fold_boundaries(case):
+    """Top-1 dispatch with the column scan in the scatter (the count table small enough)
+    and without it, and the fused router with and without the planes pass."""
+    _full_case(synth.workload("switch_base").replace(**case), no_residual_too=False)
+
+
 def test_rows_off_the_line_grid_offset_x():
     """The same with x starting 64 bytes past a line (a view one row into a larger
     buffer), so that the even tokens are the ones that start mid-line."""
