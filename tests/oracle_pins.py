@@ -229,6 +229,9 @@ def pin_bruteforce_agreement():
         dict(seed=25, T=40, d=4, F=3, N=3, CF=1.25, bias=True),
         dict(seed=26, T=30, d=7, F=5, N=5, CF=2.0, bias=False),
         dict(seed=27, T=25, d=3, F=2, N=4, CF=4.0, bias=True),
+        # larger layers: many route blocks, many experts with drops at CF = 1
+        dict(seed=28, T=1200, d=16, F=24, N=40, CF=1.0, bias=True),
+        dict(seed=29, T=1000, d=8, F=8, N=128, CF=1.0, bias=False),
     ]
     for c in cases:
         x, Wr, W1, b1, W2, b2 = random_case(c["seed"], c["T"], c["d"], c["F"], c["N"], c["bias"])
