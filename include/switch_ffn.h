@@ -111,7 +111,8 @@ extern "C" {
 #define SFFN_GEGLU 4u
 
 /* Limits of this library (SFFN_EUNSUPPORTED beyond them):
- *   N <= 4096;  T * max(N, d, F) < 2^30;  d * F < 2^30;
+ *   N <= 4096;  T * max(N, d, F) < 2^29;  d * F < 2^29 (byte offsets of every
+ *   fp32 and bf16 tensor, the fp32 router logits [T, N] included, below 2^31);
  *   SFFN_BF16: d % 8 == 0, F % 8 == 0, and x, W1, W2, y 16-byte aligned. */
 #define SFFN_MAX_EXPERTS 4096
 

@@ -93,9 +93,11 @@ static int make_shape(int64_t T, int64_t d, int64_t F, int64_t N, double CF, int
   if (dtype != SFFN_FP32 && dtype != SFFN_BF16) return SFFN_EDTYPE;
   if (N > SFFN_MAX_EXPERTS) return SFFN_EUNSUPPORTED;
   const int64_t widest = N > d ? (N > F ? N : F) : (d > F ? d : F);
-  // Element offsets of every tensor, and byte offsets of the bf16 ones, stay below 2^31.
-  if (T > ((int64_t)1 << 30) / widest - 1) return SFFN_EUNSUPPORTED;
-  if (d * F >= ((int64_t)1 << 30)) return SFFN_EUNSUPPORTED;
+  // Element offsets of every tensor (the fp32 router logits [T, N] included) and of one
+  // expert's weights stay below 2^29, so byte offsets of fp32 and bf16 tensors stay below
+  // 2^31: the offset the buffer accesses use for masked lanes (2^31) lies past them all.
+  if (T > ((int64_t)1 << 29) / widest - 1) return SFFN_EUNSUPPORTED;
+  if (d * F >= ((int64_t)1 << 29)) return SFFN_EUNSUPPORTED;
   if (dtype == SFFN_BF16 && ((d % 8) != 0 || (F % 8) != 0)) return SFFN_EUNSUPPORTED;
   const int64_t C = switch_ffn_capacity(k * T, N, CF);
   const int64_t Ce = C < T ? C : T;  // a rank never reaches T (one position per token and expert)

@@ -95,6 +95,8 @@ def test_forward_ex_signature_is_forward_plus_flags_and_stats():
     (dict(flags=8), S.SFFN_EINVAL), (dict(dtype=3), S.SFFN_EDTYPE),
     (dict(N=5000), S.SFFN_EUNSUPPORTED), (dict(d=36), S.SFFN_EUNSUPPORTED),
     (dict(F=70), S.SFFN_EUNSUPPORTED), (dict(T=1 << 25, d=64), S.SFFN_EUNSUPPORTED), (dict(d=32768, F=32768), S.SFFN_EUNSUPPORTED),
+    # fp32 logits of 2^29 elements (2 GiB) and an expert of 2^29 weights: past the limits
+    (dict(T=1 << 18, N=2048, d=64, F=64), S.SFFN_EUNSUPPORTED), (dict(d=16384, F=32768), S.SFFN_EUNSUPPORTED),
     (dict(x=0x100004), S.SFFN_EUNSUPPORTED), (dict(ws=None), S.SFFN_EWORKSPACE),
     (dict(ws_bytes=1000), S.SFFN_EWORKSPACE), (dict(ws=0x100010), S.SFFN_EUNSUPPORTED),
 ])
